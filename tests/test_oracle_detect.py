@@ -1,0 +1,110 @@
+"""Pins for the oracle vertical-line detector (CPU only).
+
+Pinned against: exact rational arithmetic (Python Fractions) on tiny grid
+inputs; the linearity identity colsum(Q K^T) == (sum of Q rows) K^T computed
+by a different route; a top-k written with Python's sorted(); the defining
+property of the selected set; the planted vertical lines of the synthetic
+workloads (a check of the data, not of the oracle).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import detect
+
+
+def _grid(rng, shape, scale=2.0):
+    return np.rint(rng.standard_normal(shape) * scale * 16) / 16
+
+
+def test_brute_force_fractions():
+    rng = np.random.default_rng(1)
+    Q = _grid(rng, (6, 8))
+    K = _grid(rng, (11, 8))
+    units = detect.to_units(detect.column_scores(Q, K))
+    for j in range(11):
+        c = sum(Fraction(float(Q[r, d])) * Fraction(float(K[j, d]))
+                for r in range(6) for d in range(8))
+        assert Fraction(int(units[j]), 1 << 16) == c
+
+
+def test_linearity_identity_exact():
+    w = synth.WORKLOADS["glm32k"]
+    rng = np.random.default_rng(2)
+    Q = synth.round_dtype(rng.standard_normal((1024, 128)) * 1.5 + 0.3, "bf16", grid=True)
+    K = synth.keys(w, 0, 0, 4096)
+    assert detect.on_grid(Q) and detect.on_grid(K) and detect.exact_bound_ok(Q, K)
+    via_matmul = detect.to_units(detect.column_scores(Q, K))
+    # different route: sum the query rows first (exact integers), then a GEMV in int64
+    qs = np.rint(np.asarray(Q, np.float64) * 16).astype(np.int64).sum(axis=0)
+    ki = np.rint(np.asarray(K, np.float64) * 16).astype(np.int64)
+    via_gemv = (ki @ qs) << 8            # units of 2**-8 -> 2**-16
+    assert np.array_equal(via_matmul, via_gemv)
+
+
+def _topk_sorted(scores, k):
+    order = sorted(range(len(scores)), key=lambda j: (-int(scores[j]), j))
+    return sorted(order[:k])
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_top_k_against_sorted_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 3000))
+    scores = rng.integers(-20, 20, n).astype(np.int64) * (1 << 12)   # heavy ties
+    k = int(rng.integers(0, n + 1))
+    got = detect.top_k(scores, k)
+    assert got.tolist() == _topk_sorted(scores, k)
+    # defining property: nothing outside beats anything inside, ties go low
+    sel = np.zeros(n, bool)
+    sel[got] = True
+    if 0 < k < n:
+        lo_in = scores[sel].min()
+        assert scores[~sel].max() <= lo_in
+        tied_out = np.nonzero(~sel & (scores == lo_in))[0]
+        tied_in = np.nonzero(sel & (scores == lo_in))[0]
+        if len(tied_out) and len(tied_in):
+            assert tied_in.max() < tied_out.min()
+
+
+def test_top_k_edge_cases():
+    assert detect.top_k(np.array([5, 5, 5], np.int64), 0).tolist() == []
+    assert detect.top_k(np.array([5, 5, 5], np.int64), 2).tolist() == [0, 1]
+    assert detect.top_k(np.array([1, 9, 9, 3], np.int64), 2).tolist() == [1, 2]
+    assert detect.top_k(np.array([-1, -2], np.int64), 2).tolist() == [0, 1]
+    with pytest.raises(ValueError):
+        detect.top_k(np.array([1], np.int64), 2)
+
+
+def test_units_rounding():
+    assert detect.to_units(np.array([1.0, -0.5, 2.0 ** -16, 1.5 * 2.0 ** -16])).tolist() == \
+        [65536, -32768, 1, 2]
+
+
+def test_detect_on_glm_workload_finds_planted_lines():
+    """Data check on a slice of the GLM-shaped detector workload: nearly all
+    planted positions are selected (alpha = beta = 7 puts a planted score about
+    3.5 noise deviations above the rest, so a few percent fall below the top-5 %
+    cut), and equal scores occur (so the tie rule is exercised)."""
+    wn = synth.WORKLOADS["glm32k"]
+    K = synth.all_keys(wn)
+    q = synth.all_query_histories(wn)
+    idx, sc = detect.detect(q, K, wn.T - wn.W, wn.k)
+    planted = synth.planted_positions(wn, 0)
+    for h in range(wn.Hkv):
+        recall = len(set(planted.tolist()) & set(idx[0, h].tolist())) / len(planted)
+        assert recall >= 0.85
+        assert np.all(np.diff(idx[0, h]) > 0)
+    vals, counts = np.unique(sc[0, 0], return_counts=True)
+    assert counts.max() > 1
+
+
+def test_rejects_non_grid_in_exact_mode():
+    q = np.full((1, 2, 1, 4), 0.1)
+    K = np.ones((1, 1, 8, 4))
+    with pytest.raises(ValueError):
+        detect.detect(q, K, 8, 2)
+    idx, _ = detect.detect(q, K, 8, 2, require_exact=False)
+    assert idx.tolist() == [[[0, 1]]]
