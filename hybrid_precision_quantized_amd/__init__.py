@@ -1,0 +1,200 @@
+"""Python binding of libhq.so, the HyQuant hybrid-precision attention library
+for AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every function forwards torch tensors' device
+pointers and plain sizes to the C ABI declared in include/hq.h (same names,
+same argument order apart from dtypes, which are taken from the tensors).
+PyTorch provides device memory and the current HIP stream; all computation
+runs in the library's HIP kernels. There is no fallback: if libhq.so is
+missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhq.so")
+
+HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP = range(5)
+HQ_F32, HQ_BF16, HQ_F16 = 0, 1, 2
+HQ_LAYOUT_ROWS, HQ_LAYOUT_TILE16 = 0, 1
+HQ_DETECT_MATMUL, HQ_DETECT_QSUM = 0, 1
+
+_DT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: HQ_F16}
+
+
+class HQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"hq status {status}: {message}")
+        self.status = status
+
+
+class HybridKV(ctypes.Structure):
+    """Mirror of hq_hybrid_kv (include/hq.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("Hkv", ctypes.c_int), ("D", ctypes.c_int), ("group", ctypes.c_int),
+        ("T", ctypes.c_int64), ("W", ctypes.c_int), ("k", ctypes.c_int), ("t_cap", ctypes.c_int64),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_sz", ctypes.c_void_p), ("v_sz", ctypes.c_void_p),
+        ("vl_bits", ctypes.c_void_p),
+        ("vl_k", ctypes.c_void_p), ("vl_v", ctypes.c_void_p),
+        ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
+        ("win_offset", ctypes.c_int), ("hp_dtype", ctypes.c_int),
+    ]
+
+
+_lib_handle = None
+
+_SIGS = {
+    "hq_quantize_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_void_p]),
+    "hq_gather_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+    "hq_vl_bitmap": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "hq_detect_vlines": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int), ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_detect_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
+    "hq_decode_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HybridKV), ctypes.c_int, ctypes.c_int]),
+    "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
+    "hq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "hq_last_error": (ctypes.c_char_p, []),
+    "hq_abi_version": (ctypes.c_int, []),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it is not built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m hybrid_precision_quantized_amd.build`")
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _check(status: int) -> None:
+    if status != HQ_OK:
+        msg = lib().hq_last_error().decode(errors="replace")
+        raise HQError(status, msg)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor or None")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+# ---------------------------------------------------------------- calls
+def hq_quantize_kv(x, n_heads, n_rows, D, x_head_stride, x_row_stride, codes, sz, layout,
+                   dst_head_rows, dst_row0, group=32, stream=None):
+    """Pack rows of x into INT4 codes and fp16 scale/zero (see include/hq.h)."""
+    if x.device.type != "cuda":
+        raise ValueError("x must live on the GPU")
+    _check(lib().hq_quantize_kv(x.data_ptr(), _dt(x), n_heads, n_rows, D, group, x_head_stride,
+                                x_row_stride, _ptr(codes), _ptr(sz), layout, dst_head_rows,
+                                dst_row0, _stream(stream)))
+
+
+def hq_gather_rows(src, n_heads, src_rows, D, idx, k, dst, stream=None):
+    _check(lib().hq_gather_rows(_ptr(src), _dt(src), n_heads, src_rows, D, _ptr(idx), k,
+                                _ptr(dst), _stream(stream)))
+
+
+def hq_vl_bitmap(vl_idx, n_heads, k, t_cap, bits, stream=None):
+    _check(lib().hq_vl_bitmap(_ptr(vl_idx), n_heads, k, t_cap, _ptr(bits), _stream(stream)))
+
+
+def hq_detect_workspace_size(B, Hkv, cand_end, k_top) -> int:
+    return int(lib().hq_detect_workspace_size(B, Hkv, cand_end, k_top))
+
+
+def hq_detect_vlines(q_new, q_acc, B, Hq, Hkv, D, R, step, force, k, k_rows, cand_end, k_top,
+                     method, idx_out, score_out=None, ws=None, stream=None) -> bool:
+    """Accumulate q_new into the ring q_acc and, on the last slot or when
+    forced, score and select the vertical lines. Returns True if detection
+    was enqueued."""
+    ran = ctypes.c_int(0)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hq_detect_vlines(_ptr(q_new), _ptr(q_acc), _dt(q_acc), B, Hq, Hkv, D, R, step,
+                                  int(force), _ptr(k), k_rows, cand_end, k_top, method,
+                                  _ptr(idx_out), _ptr(score_out), ctypes.byref(ran), _ptr(ws),
+                                  ws_bytes, _stream(stream)))
+    return bool(ran.value)
+
+
+def hq_decode_workspace_size(kv: HybridKV, Hq: int, n_splits: int = 0) -> int:
+    return int(lib().hq_decode_workspace_size(ctypes.byref(kv), Hq, n_splits))
+
+
+def hq_decode_auto_splits(kv: HybridKV, Hq: int) -> int:
+    return int(lib().hq_decode_auto_splits(ctypes.byref(kv), Hq))
+
+
+def hq_decode_attn(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, stream=None):
+    """One decode step over the hybrid cache described by kv (see include/hq.h)."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hq_decode_attn(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
+                                n_splits, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                _stream(stream)))
+
+
+def hq_status_string(s: int) -> str:
+    return lib().hq_status_string(s).decode()
+
+
+def hq_last_error() -> str:
+    return lib().hq_last_error().decode(errors="replace")
+
+
+def hq_abi_version() -> int:
+    return int(lib().hq_abi_version())
+
+
+from .cache import HybridCache  # noqa: E402,F401

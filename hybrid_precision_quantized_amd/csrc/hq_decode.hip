@@ -1,0 +1,845 @@
+// Decode-step attention over the hybrid KV cache, split over the context
+// with a log-sum-exp merge, plus the VL membership bitmap builder.
+//
+// What is computed: "HyQuant ... Explained for Beginners" (aifromscratch.in),
+// "How It Works" (three token sets: vertical lines and the last W tokens in
+// 16 bits, the rest INT4) and "The Technical Mechanics", Decode Stage (the
+// INT4 keys and values are dequantized inside the attention computation, on
+// the fly, instead of in a separate pass); kipquest.com paper page, "The
+// abstract" (decode fuses KV dequantization with attention). All three sets
+// feed one softmax.
+//
+// Kernel design (gfx950, wave64, VALU only):
+//  * One workgroup = 4 waves = one (sequence b, KV head h, head chunk of HB
+//    query heads, split) unit of work. A split is a contiguous range of INT4
+//    positions or of 16-bit rows (VL rows, then window rows).
+//  * INT4 keys, HQ_LAYOUT_ROWS: one 16-byte load = one 32-channel group of
+//    one token; LPT = D/32 lanes per token, 64/LPT tokens per wave step, so a
+//    wave reads one contiguous 1 KB block of codes per load.
+//  * q . k without dequantizing k: a nibble pair is turned into a 16-bit
+//    float pair (MAGIC + c0, MAGIC + c4) with one and-or (bf16 MAGIC = 128,
+//    fp16 MAGIC = 1024, both exact), multiplied by the matching query pair with
+//    v_dot2 (two products per lane op, fp32 accumulate), and
+//    logit = s * (sum q c) + z * (sum q) with the MAGIC offset folded into
+//    the accumulator's start value. Every unpacked key group is shared by the
+//    HB query heads of the GQA group.
+//  * softmax: per wave step, wave-wide max per head (lane shuffles), one
+//    rescale of the running state when the max grows, p = 2^(l - m) with the
+//    log2(e) and 1/sqrt(D) factors folded into the scale.
+//  * P . V without dequantizing v: values use HQ_LAYOUT_TILE16, so lane
+//    (channel pair j) loads 16 consecutive tokens of its two channels with
+//    one 16-byte load; token pairs become fp16 pairs (1024 + c_t, 1024 +
+//    c_t+1) and are multiplied by the fp16 pair (p_t s_t, p_t+1 s_t+1) with
+//    v_dot2. The 1024 offset and the zero point are added back once per split
+//    from per-group sums. No cross-lane reduction over tokens is needed.
+//  * Split partials (m, l, o) go to the workspace; the last workgroup of a
+//    unit to finish (atomic ticket) merges them in split order:
+//    m* = max m_s, L = sum 2^(m_s - m*) l_s, out = sum 2^(m_s - m*) o_s / L.
+//  * Blocks are numbered so that all splits of a unit run on the same XCD
+//    (dispatch is round-robin over the 8 XCDs), keeping the partials of a
+//    unit in one L2.
+#include <math.h>
+
+#include "hq_common.h"
+
+namespace hq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecodeParams {
+  const void *q;
+  const uint8_t *k_codes;
+  const uint8_t *v_codes;
+  const uint32_t *k_sz;     // {s, z} fp16 pairs as one word per (token, group)
+  const uint32_t *v_sz;
+  const uint32_t *vl_bits;
+  const void *vl_k, *vl_v, *win_k, *win_v;
+  float *out;
+  float *lse;
+  uint32_t *tickets;
+  float2 *part_ml;          // [B][Hq][S]
+  float *part_o;            // [B][Hq][S][D]
+  int64_t t_cap;            // rows per head of the INT4 planes
+  int64_t nq;               // T - W
+  int64_t bits_words;       // words per head of vl_bits
+  int k, W, win_offset;
+  int B, Hkv, Hq, G, nhc;   // nhc = head chunks per KV head
+  int S_q, S_fp, S;         // splits per unit
+  int64_t len_q;            // positions per INT4 split (multiple of the wave step)
+  int len_fp;               // rows per 16-bit split (multiple of the wave step)
+  int units;                // B * Hkv * nhc
+  int blocks_used;          // units * S
+  int blocks_per_xcd;
+  float cs;                 // sm_scale * log2(e)
+};
+
+// ---------------------------------------------------------------- lane helpers
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <int FROM>
+__device__ __forceinline__ float xor_max(float v) {
+#pragma unroll
+  for (int m = FROM; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+template <int FROM>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+  for (int m = FROM; m < 64; m <<= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a), __builtin_bit_cast(bf2, b),
+                                         c, false);
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+}
+template <int QT>
+__device__ __forceinline__ float dot2_q(uint32_t a, uint32_t b, float c) {
+  if constexpr (QT == HQ_BF16) return dot2_bf16(a, b, c);
+  else return dot2_f16(a, b, c);
+}
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
+  const uint32_t a = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lo));
+  const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hi));
+  return a | (b << 16);
+}
+__device__ __forceinline__ float lo_f16(uint32_t w) { return f16_to_f32(w & 0xFFFFu); }
+__device__ __forceinline__ float hi_f16(uint32_t w) { return f16_to_f32(w >> 16); }
+
+template <int DT>
+__device__ __forceinline__ uint32_t f32_bits_to_half(float x) {
+  if constexpr (DT == HQ_BF16) {
+    // q values are bf16 already; this only repacks them
+    return __float_as_uint(x) >> 16;
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Per-wave running state for HB heads. acc_e/acc_o hold the channel pair
+// (2*cp, 2*cp+1) of this lane; fix_off/fix_z are the per-(head, group)
+// constants subtracted/added at the end (INT4 pass only).
+template <int HB>
+struct WaveState {
+  float m[HB];
+  float l[HB];
+  float acc_e[HB];
+  float acc_o[HB];
+};
+
+struct SharedMem {
+  uint32_t ps[kWaves][4 * 4 * 16];      // [wave][h][g][pair]   (INT4 pass)
+  float p[kWaves][4 * 32];              // [wave][h][slot]      (16-bit pass)
+  float zo[kWaves][4][4][2];            // [wave][h][g]{off, z}
+  float bm[kWaves][4];
+  float bl[kWaves][4];
+  float bo[kWaves][4][128];
+  int last;
+};
+
+// ---------------------------------------------------------------- INT4 pass
+template <int D, int HB, int QT>
+__device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, int i0,
+                           int64_t r0, int64_t r1, WaveState<HB> &st) {
+  constexpr int LPT = D / 32;          // lanes per token (one group each)
+  constexpr int SLOTS = 64 / LPT;      // tokens per wave step
+  constexpr int CP = D / 2;            // channel pairs
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = lane / LPT;
+  const int g = lane % LPT;
+  const int cp = lane % CP;
+  const int sub = lane / CP;           // 16-token sub-tile for the P.V lanes
+  const int gp = cp / 16;
+  const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
+
+  // query pairs for this lane's group: qp[hh][j][m] = (q[8j+m], q[8j+m+4])
+  uint32_t qp[HB][4][4];
+  float qf[HB][32];
+  float qsum[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const int64_t qoff = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * D + g * 32;
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) v[c] = load_as_f32<QT>(P.q, qoff + c);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) s += v[c];
+    qsum[hh] = s;
+    if constexpr (QT == HQ_F32) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) qf[hh][c] = v[c];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          qp[hh][j][m] = f32_bits_to_half<QT>(v[8 * j + m]) |
+                         (f32_bits_to_half<QT>(v[8 * j + m + 4]) << 16);
+    }
+  }
+  constexpr uint32_t kMagic = (QT == HQ_BF16) ? 0x43004300u : 0x64006400u;
+  constexpr float kMagicVal = (QT == HQ_BF16) ? 128.f : 1024.f;
+
+  float offl[HB], zl[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) { offl[hh] = 0.f; zl[hh] = 0.f; }
+
+  const uint8_t *kc_base = P.k_codes + head * P.t_cap * (D / 2);
+  const uint32_t *ks_base = P.k_sz + head * P.t_cap * (D / 32);
+  const uint32_t *vs_base = P.v_sz + head * P.t_cap * (D / 32);
+  const uint8_t *vc_base = P.v_codes + head * P.t_cap * (D / 2);
+  const uint32_t *bits_base = P.vl_bits + head * P.bits_words;
+
+  const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
+  for (int64_t c = wave; c < nsteps; c += kWaves) {
+    const int64_t t0 = r0 + c * SLOTS;
+    const int64_t t = t0 + slot;
+    const bool tv = t < r1;
+    uint4 kc = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t ks = 0u, vs = 0u, bits = 0u;
+    if (tv) {
+      kc = *reinterpret_cast<const uint4 *>(kc_base + t * (D / 2) + g * 16);
+      ks = ks_base[t * (D / 32) + g];
+      vs = vs_base[t * (D / 32) + g];
+      bits = bits_base[t >> 5];
+    }
+    const int64_t vt = (t0 >> 4) + sub;          // 16-token tile for this P.V lane
+    uint4 vc = make_uint4(0u, 0u, 0u, 0u);
+    if (vt * 16 < r1) vc = *reinterpret_cast<const uint4 *>(vc_base + vt * (CP * 16) + cp * 16);
+
+    // ---- q . k
+    float part[HB];
+    const uint32_t w[4] = {kc.x, kc.y, kc.z, kc.w};
+    if constexpr (QT == HQ_F32) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float cv = static_cast<float>((w[j] >> (4 * e)) & 15u);
+#pragma unroll
+          for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(qf[hh][8 * j + e], cv, part[hh]);
+        }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) part[hh] = -kMagicVal * qsum[hh];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t x0 = (w[j] & 0x000F000Fu) | kMagic;
+        const uint32_t x1 = ((w[j] >> 4) & 0x000F000Fu) | kMagic;
+        const uint32_t x2 = ((w[j] >> 8) & 0x000F000Fu) | kMagic;
+        const uint32_t x3 = ((w[j] >> 12) & 0x000F000Fu) | kMagic;
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+          part[hh] = dot2_q<QT>(qp[hh][j][0], x0, part[hh]);
+          part[hh] = dot2_q<QT>(qp[hh][j][1], x1, part[hh]);
+          part[hh] = dot2_q<QT>(qp[hh][j][2], x2, part[hh]);
+          part[hh] = dot2_q<QT>(qp[hh][j][3], x3, part[hh]);
+        }
+      }
+    }
+    const float ssc = lo_f16(ks) * P.cs;
+    const float zsc = hi_f16(ks) * P.cs;
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(ssc, part[hh], zsc * qsum[hh]);
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1)
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) part[hh] += shfl_xor_f(part[hh], m);
+
+    const bool is_vl = (bits >> (t & 31)) & 1u;
+    const bool live = tv && !is_vl;
+
+    // ---- online softmax
+    float p[HB], alpha[HB];
+    bool rescale = false;
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const float lg = live ? part[hh] : kNegInf;
+      const float mx = xor_max<LPT>(lg);
+      const float mn = fmaxf(st.m[hh], mx);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      alpha[hh] = fast_exp2(st.m[hh] - mu);
+      rescale |= (mn != st.m[hh]);
+      st.m[hh] = mn;
+      p[hh] = fast_exp2(lg - mu);
+    }
+    const float sv = live ? lo_f16(vs) : 0.f;
+    const float zv = live ? hi_f16(vs) : 0.f;
+    const bool even = (slot & 1) == 0;
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      st.l[hh] = st.l[hh] * alpha[hh] + p[hh];
+      zl[hh] = fmaf(p[hh], zv, zl[hh] * alpha[hh]);
+      const float ps = p[hh] * sv;
+      const float nb = __shfl_down(ps, LPT, 64);
+      const uint32_t pair = pack_f16_rne(ps, nb);
+      const float add = dot2_f16(pair, 0x3C003C00u, 0.f);   // fp16 1.0 pair
+      offl[hh] = offl[hh] * alpha[hh] + (even ? add : 0.f);
+      if (even) sm.ps[wave][(hh * LPT + g) * 16 + (slot >> 1)] = pair;
+    }
+    wave_sync();
+
+    // ---- p . v
+    if (rescale) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        st.acc_e[hh] *= alpha[hh];
+        st.acc_o[hh] *= alpha[hh];
+      }
+    }
+    const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16 + 8 * sub]);
+      const uint4 pa = src[0], pb = src[1];
+      const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t x = __builtin_amdgcn_perm(0u, vw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
+        const uint32_t e = (x & 0x000F000Fu) | 0x64006400u;
+        const uint32_t o = (x & 0x00F000F0u) | 0x64006400u;
+        st.acc_e[hh] = dot2_f16(pr[i], e, st.acc_e[hh]);
+        st.acc_o[hh] = dot2_f16(pr[i], o, st.acc_o[hh]);
+      }
+    }
+    wave_sync();
+  }
+
+  // ---- per-(head, group) constants, then fold them into the accumulators
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const float off = xor_sum<LPT>(offl[hh]);
+    const float z = xor_sum<LPT>(zl[hh]);
+    if (slot == 0) {
+      sm.zo[wave][hh][g][0] = off;
+      sm.zo[wave][hh][g][1] = z;
+    }
+  }
+  wave_sync();
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    float ae = st.acc_e[hh], ao = st.acc_o[hh];
+    if constexpr (CP < 64) {       // D = 64: two 16-token sub-tiles share the channels
+      ae += shfl_xor_f(ae, 32);
+      ao += shfl_xor_f(ao, 32);
+    }
+    const float off = sm.zo[wave][hh][gp][0];
+    const float z = sm.zo[wave][hh][gp][1];
+    st.acc_e[hh] = (ae - 1024.f * off) + z;
+    st.acc_o[hh] = (ao - 1024.f * off) * 0.0625f + z;
+    st.l[hh] = xor_sum<1>(st.l[hh]) * (1.0f / LPT);
+  }
+}
+
+// ---------------------------------------------------------------- 16-bit pass
+template <int D, int HT>
+__device__ __forceinline__ int64_t fp_row_index(const DecodeParams &P, int64_t head, int64_t rr,
+                                                const void **kb, const void **vb) {
+  // returns the row index inside *kb / *vb
+  if (rr < P.k) {
+    *kb = P.vl_k;
+    *vb = P.vl_v;
+    return head * P.k + rr;
+  }
+  *kb = P.win_k;
+  *vb = P.win_v;
+  int64_t wi = (P.win_offset + (rr - P.k)) % P.W;
+  return head * P.W + wi;
+}
+
+template <int D, int HB, int HT>
+__device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int i0, int64_t r0,
+                         int64_t r1, WaveState<HB> &st) {
+  constexpr int LPT = D / 32;
+  constexpr int SLOTS = 64 / LPT;
+  constexpr int CP = D / 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = lane / LPT;
+  const int g = lane % LPT;
+  const int cp = lane % CP;
+  const int sub = lane / CP;
+  const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
+
+  // natural query pairs (q[2i], q[2i+1]) or fp32 values for this lane's group
+  uint32_t qn[HB][16];
+  float qf[HB][32];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const int64_t qoff = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * D + g * 32;
+    if constexpr (HT == HQ_F32) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) qf[hh][c] = load_as_f32<HQ_F32>(P.q, qoff + c);
+    } else {
+      const uint32_t *qq = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) qn[hh][c] = qq[c];
+    }
+  }
+
+  const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
+  for (int64_t c = wave; c < nsteps; c += kWaves) {
+    const int64_t f0 = r0 + c * SLOTS;
+    const int64_t rr = f0 + slot;
+    const bool tv = rr < r1;
+    float part[HB];
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
+    if (tv) {
+      const void *kb;
+      const void *vb;
+      const int64_t row = fp_row_index<D, HT>(P, head, rr, &kb, &vb);
+      if constexpr (HT == HQ_F32) {
+        const float4 *kp = reinterpret_cast<const float4 *>(static_cast<const float *>(kb) + row * D + g * 32);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 kv = kp[j];
+#pragma unroll
+          for (int hh = 0; hh < HB; ++hh) {
+            part[hh] = fmaf(qf[hh][4 * j + 0], kv.x, part[hh]);
+            part[hh] = fmaf(qf[hh][4 * j + 1], kv.y, part[hh]);
+            part[hh] = fmaf(qf[hh][4 * j + 2], kv.z, part[hh]);
+            part[hh] = fmaf(qf[hh][4 * j + 3], kv.w, part[hh]);
+          }
+        }
+      } else {
+        const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(kb) + row * D + g * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 kv = kp[j];
+          const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh) part[hh] = dot2_q<HT>(qn[hh][4 * j + e], kw[e], part[hh]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1)
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) part[hh] += shfl_xor_f(part[hh], m);
+
+    float alpha[HB];
+    bool rescale = false;
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const float lg = tv ? part[hh] * P.cs : kNegInf;
+      const float mx = xor_max<LPT>(lg);
+      const float mn = fmaxf(st.m[hh], mx);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      alpha[hh] = fast_exp2(st.m[hh] - mu);
+      rescale |= (mn != st.m[hh]);
+      st.m[hh] = mn;
+      const float p = fast_exp2(lg - mu);
+      st.l[hh] = st.l[hh] * alpha[hh] + p;
+      if (g == 0) sm.p[wave][hh * 32 + slot] = p;
+    }
+    wave_sync();
+    if (rescale) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        st.acc_e[hh] *= alpha[hh];
+        st.acc_o[hh] *= alpha[hh];
+      }
+    }
+    // lanes: channel pair cp over the 16 rows of sub-tile `sub`
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+      const int64_t rrow = f0 + 16 * sub + r;
+      if (rrow < r1) {
+        const void *kb;
+        const void *vb;
+        const int64_t row = fp_row_index<D, HT>(P, head, rrow, &kb, &vb);
+        float v0, v1;
+        if constexpr (HT == HQ_F32) {
+          const float2 vv = reinterpret_cast<const float2 *>(static_cast<const float *>(vb) + row * D)[cp];
+          v0 = vv.x;
+          v1 = vv.y;
+        } else {
+          const uint32_t vv = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(vb) + row * D)[cp];
+          if constexpr (HT == HQ_BF16) {
+            v0 = bf16_to_f32(vv & 0xFFFFu);
+            v1 = bf16_to_f32(vv >> 16);
+          } else {
+            v0 = lo_f16(vv);
+            v1 = hi_f16(vv);
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+          const float p = sm.p[wave][hh * 32 + 16 * sub + r];
+          st.acc_e[hh] = fmaf(p, v0, st.acc_e[hh]);
+          st.acc_o[hh] = fmaf(p, v1, st.acc_o[hh]);
+        }
+      }
+    }
+    wave_sync();
+  }
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    if constexpr (CP < 64) {
+      st.acc_e[hh] += shfl_xor_f(st.acc_e[hh], 32);
+      st.acc_o[hh] += shfl_xor_f(st.acc_o[hh], 32);
+    }
+    st.l[hh] = xor_sum<1>(st.l[hh]) * (1.0f / LPT);
+  }
+}
+
+// ---------------------------------------------------------------- the kernel
+template <int D, int HB, int QT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
+  __shared__ SharedMem sm;
+  constexpr int CP = D / 2;
+  // XCD-aware numbering: hardware block id -> (xcd, index on that xcd)
+  const int hw = blockIdx.x;
+  const int lin = (hw % kNumXcd) * P.blocks_per_xcd + hw / kNumXcd;
+  if (lin >= P.blocks_used) return;
+  const int unit = lin / P.S;
+  const int split = lin % P.S;
+  const int hc = unit % P.nhc;
+  const int bh = unit / P.nhc;
+  const int h = bh % P.Hkv;
+  const int b = bh / P.Hkv;
+  const int i0 = h * P.G + hc * HB;           // first query head of this block
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  WaveState<HB> st;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    st.m[hh] = kNegInf;
+    st.l[hh] = 0.f;
+    st.acc_e[hh] = 0.f;
+    st.acc_o[hh] = 0.f;
+  }
+  if (split < P.S_q) {
+    const int64_t r0 = static_cast<int64_t>(split) * P.len_q;
+    const int64_t r1 = r0 + P.len_q < P.nq ? r0 + P.len_q : P.nq;
+    int4_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
+  } else {
+    const int64_t nfp = static_cast<int64_t>(P.k) + P.W;
+    const int64_t r0 = static_cast<int64_t>(split - P.S_q) * P.len_fp;
+    const int64_t r1 = r0 + P.len_fp < nfp ? r0 + P.len_fp : nfp;
+    fp_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
+  }
+
+  // ---- combine the 4 waves
+  if (lane < CP) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      sm.bo[wave][hh][2 * lane] = st.acc_e[hh];
+      sm.bo[wave][hh][2 * lane + 1] = st.acc_o[hh];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      sm.bm[wave][hh] = st.m[hh];
+      sm.bl[wave][hh] = st.l[hh];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < HB * D; e += kThreads) {
+    const int hh = e / D;
+    const int d = e % D;
+    float mb = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mb = fmaxf(mb, sm.bm[w][hh]);
+    const float mu = (mb == kNegInf) ? 0.f : mb;
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(sm.bm[w][hh] - mu);
+      o = fmaf(f, sm.bo[w][hh][d], o);
+      l = fmaf(f, sm.bl[w][hh], l);
+    }
+    const int64_t pidx = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * P.S + split;
+    P.part_o[pidx * D + d] = o;
+    if (d == 0) P.part_ml[pidx] = make_float2(mb, l);
+  }
+
+  // ---- last block of the unit merges all splits
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&P.tickets[unit], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (prev == static_cast<uint32_t>(P.S - 1));
+    if (last) __hip_atomic_store(&P.tickets[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = last;
+  }
+  __syncthreads();
+  if (!sm.last) return;
+  __threadfence();
+  for (int e = threadIdx.x; e < HB * D; e += kThreads) {
+    const int hh = e / D;
+    const int d = e % D;
+    const int64_t base = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * P.S;
+    float mstar = kNegInf;
+    for (int s = 0; s < P.S; ++s) mstar = fmaxf(mstar, P.part_ml[base + s].x);
+    const float mu = (mstar == kNegInf) ? 0.f : mstar;
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < P.S; ++s) {
+      const float2 ml = P.part_ml[base + s];
+      const float f = fast_exp2(ml.x - mu);
+      L = fmaf(f, ml.y, L);
+      O = fmaf(f, P.part_o[(base + s) * D + d], O);
+    }
+    const int64_t oi = (static_cast<int64_t>(b) * P.Hq + i0 + hh);
+    P.out[oi * D + d] = O / L;
+    if (d == 0 && P.lse) P.lse[oi] = (mu + log2f(L)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------- VL bitmap
+// One block per (b, h): bits[h][w] has bit t%32 of word t/32 set iff t is in
+// vl_idx[h][0..k). Words are built in LDS segments of 8192 words.
+constexpr int kSegWords = 8192;
+__global__ __launch_bounds__(256) void vl_bitmap_kernel(const int32_t *__restrict__ idx, int k,
+                                                        int64_t words, uint32_t *__restrict__ bits) {
+  __shared__ uint32_t seg[kSegWords];
+  const int64_t h = blockIdx.x;
+  const int32_t *ih = idx + h * k;
+  uint32_t *bh = bits + h * words;
+  for (int64_t w0 = 0; w0 < words; w0 += kSegWords) {
+    const int64_t nw = (words - w0) < kSegWords ? (words - w0) : kSegWords;
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) seg[i] = 0u;
+    __syncthreads();
+    const int64_t lo = w0 * 32, hi = (w0 + nw) * 32;
+    for (int i = threadIdx.x; i < k; i += blockDim.x) {
+      const int64_t t = ih[i];
+      if (t >= lo && t < hi) atomicOr(&seg[(t - lo) >> 5], 1u << ((t - lo) & 31));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) bh[w0 + i] = seg[i];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- planning
+struct Plan {
+  int nhc, HB, units, S_q, S_fp, S;
+  int64_t len_q;
+  int len_fp;
+  int64_t nq;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
+  Plan pl{};
+  const int G = Hq / kv->Hkv;
+  pl.HB = G >= 4 ? 4 : G;
+  pl.nhc = G / pl.HB;
+  pl.units = kv->B * kv->Hkv * pl.nhc;
+  const int step = 64 / (kv->D / 32);
+  pl.nq = kv->T - kv->W;
+  const int64_t nfp = static_cast<int64_t>(kv->k) + kv->W;
+  const int hp_bytes = kv->hp_dtype == HQ_F32 ? 4 : 2;
+  const double bytes_q = static_cast<double>(pl.nq) * (kv->D + kv->D / 4);
+  const double bytes_fp = static_cast<double>(nfp) * 2.0 * kv->D * hp_bytes;
+  int S = n_splits;
+  if (S <= 0) {
+    const int target_blocks = 1024;
+    S = static_cast<int>(ceil_div(target_blocks, pl.units));
+    // at least ~4 wave steps of work per wave
+    const int64_t max_s = ceil_div(pl.nq + nfp, 16LL * step) ;
+    if (S > max_s) S = static_cast<int>(max_s > 0 ? max_s : 1);
+    if (S > 256) S = 256;
+    if (S < 1) S = 1;
+  }
+  int s_fp = 0;
+  if (nfp > 0) {
+    const double frac = bytes_fp / (bytes_q + bytes_fp);
+    s_fp = static_cast<int>(frac * S + 0.5);
+    if (s_fp < 1) s_fp = 1;
+    const int64_t mx = ceil_div(nfp, step);
+    if (s_fp > mx) s_fp = static_cast<int>(mx);
+  }
+  int s_q = 0;
+  if (pl.nq > 0) {
+    s_q = S - s_fp;
+    if (s_q < 1) s_q = 1;
+    // the VL bitmap and the ranges: at most 2^20 positions per split
+    const int64_t mn = ceil_div(pl.nq, 1LL << 20);
+    if (s_q < mn) s_q = static_cast<int>(mn);
+    const int64_t mx = ceil_div(pl.nq, step);
+    if (s_q > mx) s_q = static_cast<int>(mx);
+  }
+  pl.len_q = s_q > 0 ? ceil_div(ceil_div(pl.nq, s_q), step) * step : 0;
+  pl.S_q = s_q > 0 ? static_cast<int>(ceil_div(pl.nq, pl.len_q)) : 0;
+  pl.len_fp = s_fp > 0 ? static_cast<int>(ceil_div(ceil_div(nfp, s_fp), step) * step) : 0;
+  pl.S_fp = s_fp > 0 ? static_cast<int>(ceil_div(nfp, pl.len_fp)) : 0;
+  pl.S = pl.S_q + pl.S_fp;
+  return pl;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t tickets, ml, o, total;
+};
+WsLayout ws_layout(const hq_hybrid_kv *kv, int Hq, const Plan &pl) {
+  WsLayout L{};
+  L.tickets = 0;
+  L.ml = align_up(static_cast<size_t>(pl.units) * 4, 4096);
+  L.o = L.ml + align_up(static_cast<size_t>(kv->B) * Hq * pl.S * sizeof(float2), 256);
+  L.total = L.o + static_cast<size_t>(kv->B) * Hq * pl.S * kv->D * sizeof(float);
+  return L;
+}
+
+hq_status validate(const void *q, int q_dtype, int Hq, const hq_hybrid_kv *kv, float *out) {
+  if (!kv) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null descriptor");
+  if (kv->B < 1 || kv->Hkv < 1 || Hq < 1) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: B, Hkv, Hq must be >= 1");
+  if (Hq % kv->Hkv) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: Hq %% Hkv != 0");
+  const int G = Hq / kv->Hkv;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16))
+    return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn: G = %d not in {1,2,4,8,16}", G);
+  if (kv->D != 64 && kv->D != 128) return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn: D must be 64 or 128");
+  if (kv->group != 32) return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn: group must be 32");
+  if (!dtype_ok(q_dtype) || !dtype_ok(kv->hp_dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: bad dtype");
+  if (q_dtype != kv->hp_dtype)
+    return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn: q dtype must equal the 16-bit rows' dtype");
+  if (kv->T < 1) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: T must be >= 1");
+  if (kv->W < 0 || kv->W > kv->T) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: need 0 <= W <= T");
+  if (kv->k < 0 || kv->k > kv->T - kv->W) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: need 0 <= k <= T - W");
+  if (kv->t_cap < kv->T - kv->W || kv->t_cap % 32 != 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: t_cap must be >= T - W and a multiple of 32");
+  if (kv->W > 0 && (kv->win_offset < 0 || kv->win_offset >= kv->W))
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: win_offset out of range");
+  if (!q || !out) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null q or out");
+  if (kv->T - kv->W > 0 && (!kv->k_codes || !kv->v_codes || !kv->k_sz || !kv->v_sz || !kv->vl_bits))
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null INT4 plane or VL bitmap");
+  if (kv->k > 0 && (!kv->vl_k || !kv->vl_v)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null VL rows");
+  if (kv->W > 0 && (!kv->win_k || !kv->win_v)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null window rows");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(kv->k_codes) | reinterpret_cast<uintptr_t>(kv->v_codes) |
+                       reinterpret_cast<uintptr_t>(kv->vl_k) | reinterpret_cast<uintptr_t>(kv->vl_v) |
+                       reinterpret_cast<uintptr_t>(kv->win_k) | reinterpret_cast<uintptr_t>(kv->win_v) |
+                       reinterpret_cast<uintptr_t>(q);
+  if (al % 16) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: buffers must be 16-byte aligned");
+  return HQ_OK;
+}
+
+template <int D, int HB>
+void launch_hb(int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
+  switch (qdt) {
+    case HQ_F32: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_F32>), grid, dim3(kThreads), 0, st, P); break;
+    case HQ_BF16: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_BF16>), grid, dim3(kThreads), 0, st, P); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_F16>), grid, dim3(kThreads), 0, st, P); break;
+  }
+}
+template <int D>
+void launch_d(int HB, int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
+  switch (HB) {
+    case 1: launch_hb<D, 1>(qdt, grid, st, P); break;
+    case 2: launch_hb<D, 2>(qdt, grid, st, P); break;
+    default: launch_hb<D, 4>(qdt, grid, st, P); break;
+  }
+}
+
+}  // namespace
+}  // namespace hq
+
+using namespace hq;
+
+extern "C" int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq) {
+  if (!kv || kv->Hkv < 1 || Hq % kv->Hkv) return 0;
+  return make_plan(kv, Hq, 0).S;
+}
+
+extern "C" size_t hq_decode_workspace_size(const hq_hybrid_kv *kv, int Hq, int n_splits) {
+  if (!kv || kv->Hkv < 1 || Hq < 1 || Hq % kv->Hkv || kv->T < 1 || (kv->D != 64 && kv->D != 128))
+    return 0;
+  const Plan pl = make_plan(kv, Hq, n_splits);
+  return ws_layout(kv, Hq, pl).total;
+}
+
+extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                                    float sm_scale, int n_splits, float *out, float *lse, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  hq_status s = validate(q, q_dtype, Hq, kv, out);
+  if (s != HQ_OK) return s;
+  if (n_splits < 0) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: n_splits < 0");
+  const Plan pl = make_plan(kv, Hq, n_splits);
+  const WsLayout L = ws_layout(kv, Hq, pl);
+  if (!ws || ws_bytes < L.total)
+    return fail(HQ_ERR_WORKSPACE, "hq_decode_attn: workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: workspace must be 256-byte aligned");
+  DecodeParams P{};
+  P.q = q;
+  P.k_codes = kv->k_codes;
+  P.v_codes = kv->v_codes;
+  P.k_sz = reinterpret_cast<const uint32_t *>(kv->k_sz);
+  P.v_sz = reinterpret_cast<const uint32_t *>(kv->v_sz);
+  P.vl_bits = kv->vl_bits;
+  P.vl_k = kv->vl_k;
+  P.vl_v = kv->vl_v;
+  P.win_k = kv->win_k;
+  P.win_v = kv->win_v;
+  P.out = out;
+  P.lse = lse;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  P.tickets = reinterpret_cast<uint32_t *>(w8 + L.tickets);
+  P.part_ml = reinterpret_cast<float2 *>(w8 + L.ml);
+  P.part_o = reinterpret_cast<float *>(w8 + L.o);
+  P.t_cap = kv->t_cap;
+  P.nq = pl.nq;
+  P.bits_words = kv->t_cap / 32;
+  P.k = kv->k;
+  P.W = kv->W;
+  P.win_offset = kv->win_offset;
+  P.B = kv->B;
+  P.Hkv = kv->Hkv;
+  P.Hq = Hq;
+  P.G = Hq / kv->Hkv;
+  P.nhc = pl.nhc;
+  P.S_q = pl.S_q;
+  P.S_fp = pl.S_fp;
+  P.S = pl.S;
+  P.len_q = pl.len_q;
+  P.len_fp = pl.len_fp;
+  P.units = pl.units;
+  P.blocks_used = pl.units * pl.S;
+  const int blocks = static_cast<int>(ceil_div(P.blocks_used, kNumXcd) * kNumXcd);
+  P.blocks_per_xcd = blocks / kNumXcd;
+  const float scale = sm_scale == 0.f ? 1.0f / sqrtf(static_cast<float>(kv->D)) : sm_scale;
+  P.cs = scale * kLog2e;
+  hipStream_t st = as_stream(stream);
+  if (kv->D == 128) launch_d<128>(pl.HB, q_dtype, dim3(blocks), st, P);
+  else launch_d<64>(pl.HB, q_dtype, dim3(blocks), st, P);
+  return check_launch("hq_decode_attn");
+}
+
+extern "C" hq_status hq_vl_bitmap(const int32_t *vl_idx, int n_heads, int k, int64_t t_cap,
+                                  uint32_t *bits, void *stream) {
+  if (n_heads < 0 || k < 0 || t_cap < 0 || t_cap % 32)
+    return fail(HQ_ERR_INVALID_ARG, "hq_vl_bitmap: bad sizes (t_cap must be a multiple of 32)");
+  if (n_heads == 0 || t_cap == 0) { clear_error(); return HQ_OK; }
+  if (!bits || (k > 0 && !vl_idx)) return fail(HQ_ERR_INVALID_ARG, "hq_vl_bitmap: null pointer");
+  hipLaunchKernelGGL(vl_bitmap_kernel, dim3(n_heads), dim3(256), 0, as_stream(stream), vl_idx, k,
+                     t_cap / 32, bits);
+  return check_launch("hq_vl_bitmap");
+}

@@ -1,0 +1,217 @@
+// INT4 packing of keys/values and the vertical-line row gather.
+//
+// Quantizer: "HyQuant ... Explained for Beginners" (aifromscratch.in),
+// "How It Works: The Hybrid-Precision Strategy", item 3 -- the quantized
+// majority of keys and values is stored in 4 bits. Format (this library's
+// reading): per token, 32-channel groups, s = fp16((max - min) / 15),
+// z = fp16(min), c = clamp(rint_even((x - z) / s), 0, 15) in fp32 with
+// IEEE subtract and correctly rounded divide; s = 0 gives c = 0; a zero
+// scale or zero point is stored as +0.
+//
+// Gather: same page and section, item 1 -- vertical-line tokens keep their
+// full-precision keys and values; the gather copies those rows by index into
+// the compact 16-bit buffer read by the decode kernel.
+//
+// This file is compiled with -ffp-contract=off: the quantizer has no
+// multiply-add, and keeping contraction off makes the fp32 steps exactly the
+// IEEE operations above.
+#include <stdio.h>
+
+#include "hq_common.h"
+
+namespace hq {
+namespace {
+
+constexpr int kGroup = 32;
+
+// One thread per (head, row, 32-channel group).
+template <int DT, int LAYOUT>
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const void *__restrict__ x, int n_heads, int64_t n_rows, int D, int64_t x_head_stride,
+    int64_t x_row_stride, uint8_t *__restrict__ codes, uint16_t *__restrict__ sz,
+    int64_t dst_head_rows, int64_t dst_row0) {
+  const int ng = D / kGroup;
+  const int64_t total = static_cast<int64_t>(n_heads) * n_rows * ng;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int g = static_cast<int>(gid % ng);
+  const int64_t hr = gid / ng;
+  const int64_t r = hr % n_rows;
+  const int h = static_cast<int>(hr / n_rows);
+
+  const int64_t src = h * x_head_stride + r * x_row_stride + g * kGroup;
+  float v[kGroup];
+  if constexpr (DT == HQ_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + src);
+#pragma unroll
+    for (int i = 0; i < kGroup / 4; ++i) {
+      float4 f = p[i];
+      v[4 * i + 0] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + src);
+#pragma unroll
+    for (int i = 0; i < kGroup / 8; ++i) {
+      uint4 u = p[i];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (DT == HQ_BF16) {
+          v[8 * i + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+          v[8 * i + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
+        } else {
+          v[8 * i + 2 * j] = f16_to_f32(w[j] & 0xFFFFu);
+          v[8 * i + 2 * j + 1] = f16_to_f32(w[j] >> 16);
+        }
+      }
+    }
+  }
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < kGroup; ++i) {
+    mn = fminf(mn, v[i]);
+    mx = fmaxf(mx, v[i]);
+  }
+  // "+ 0.0f" turns a zero of either sign into +0 (IEEE: -0 + +0 = +0).
+  const float s32 = (mx - mn) / 15.0f + 0.0f;
+  const _Float16 s16 = static_cast<_Float16>(s32);
+  const _Float16 z16 = static_cast<_Float16>(mn + 0.0f);
+  const float s = static_cast<float>(s16);
+  const float z = static_cast<float>(z16);
+
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    uint32_t c = 0;
+    if (s != 0.0f) {
+      float t = __builtin_rintf((v[i] - z) / s);
+      t = fminf(fmaxf(t, 0.0f), 15.0f);
+      c = static_cast<uint32_t>(t);
+    }
+    packed[i >> 3] |= c << (4 * (i & 7));
+  }
+
+  const int64_t row = dst_row0 + r;
+  const int64_t head_row = static_cast<int64_t>(h) * dst_head_rows + row;
+  if constexpr (LAYOUT == HQ_LAYOUT_ROWS) {
+    uint4 *dst = reinterpret_cast<uint4 *>(codes + head_row * (D / 2) + g * (kGroup / 2));
+    *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  } else {
+    // tile u = row / 16 of head h; byte (j, row % 16) for channel pair j
+    const int64_t tile = static_cast<int64_t>(h) * (dst_head_rows / 16) + row / 16;
+    uint8_t *base = codes + tile * (D / 2) * 16 + (row % 16);
+#pragma unroll
+    for (int jj = 0; jj < kGroup / 2; ++jj) {
+      const int j = g * (kGroup / 2) + jj;
+      base[j * 16] = static_cast<uint8_t>((packed[jj >> 2] >> (8 * (jj & 3))) & 0xFFu);
+    }
+  }
+  const uint32_t szw = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+  reinterpret_cast<uint32_t *>(sz)[head_row * (D / kGroup) + g] = szw;
+}
+
+// One thread per 16-byte chunk of a destination row.
+__global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__ src,
+                                                     int64_t src_rows, int row_bytes,
+                                                     const int32_t *__restrict__ idx, int k,
+                                                     int n_heads, uint8_t *__restrict__ dst) {
+  const int chunks = row_bytes / 16;
+  const int64_t total = static_cast<int64_t>(n_heads) * k * chunks;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t hi = gid / chunks;          // h * k + i
+  const int64_t h = hi / k;
+  const int32_t j = idx[hi];
+  uint4 val = make_uint4(0u, 0u, 0u, 0u);
+  if (j >= 0 && j < src_rows) {
+    val = reinterpret_cast<const uint4 *>(src + (h * src_rows + j) * row_bytes)[c];
+  }
+  reinterpret_cast<uint4 *>(dst + hi * row_bytes)[c] = val;
+}
+
+template <int DT>
+void launch_quantize_dt(int layout, dim3 grid, hipStream_t st, const void *x, int n_heads,
+                        int64_t n_rows, int D, int64_t xh, int64_t xr, uint8_t *codes,
+                        uint16_t *sz, int64_t dhr, int64_t d0) {
+  if (layout == HQ_LAYOUT_ROWS) {
+    hipLaunchKernelGGL((quantize_kernel<DT, HQ_LAYOUT_ROWS>), grid, dim3(256), 0, st, x,
+                       n_heads, n_rows, D, xh, xr, codes, sz, dhr, d0);
+  } else {
+    hipLaunchKernelGGL((quantize_kernel<DT, HQ_LAYOUT_TILE16>), grid, dim3(256), 0, st, x,
+                       n_heads, n_rows, D, xh, xr, codes, sz, dhr, d0);
+  }
+}
+
+}  // namespace
+}  // namespace hq
+
+using namespace hq;
+
+extern "C" hq_status hq_quantize_kv(const void *x, hq_dtype x_dtype, int n_heads,
+                                    int64_t n_rows, int D, int group, int64_t x_head_stride,
+                                    int64_t x_row_stride, uint8_t *codes, uint16_t *sz,
+                                    hq_code_layout layout, int64_t dst_head_rows,
+                                    int64_t dst_row0, void *stream) {
+  if (!dtype_ok(x_dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: bad dtype %d", x_dtype);
+  if (layout != HQ_LAYOUT_ROWS && layout != HQ_LAYOUT_TILE16)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: bad layout %d", layout);
+  if (group != kGroup) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv: group must be 32");
+  if (D != 64 && D != 128) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv: D must be 64 or 128");
+  if (n_heads < 0 || n_rows < 0 || dst_row0 < 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: negative size");
+  if (dst_row0 + n_rows > dst_head_rows)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: rows [%lld, %lld) exceed dst_head_rows %lld",
+                (long long)dst_row0, (long long)(dst_row0 + n_rows), (long long)dst_head_rows);
+  if (layout == HQ_LAYOUT_TILE16 && dst_head_rows % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: TILE16 needs dst_head_rows %% 16 == 0");
+  if (n_heads == 0 || n_rows == 0) { clear_error(); return HQ_OK; }
+  if (!x || !codes || !sz) return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: null pointer");
+  const int eb = dtype_bytes(x_dtype);
+  if ((x_row_stride * eb) % 16 != 0 || (x_head_stride * eb) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(sz) % 4 != 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: x rows must be 16-byte aligned");
+  const int64_t threads = static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv: too many rows");
+  dim3 grid(static_cast<unsigned>(blocks));
+  hipStream_t st = as_stream(stream);
+  switch (x_dtype) {
+    case HQ_F32:
+      launch_quantize_dt<HQ_F32>(layout, grid, st, x, n_heads, n_rows, D, x_head_stride,
+                                 x_row_stride, codes, sz, dst_head_rows, dst_row0);
+      break;
+    case HQ_BF16:
+      launch_quantize_dt<HQ_BF16>(layout, grid, st, x, n_heads, n_rows, D, x_head_stride,
+                                  x_row_stride, codes, sz, dst_head_rows, dst_row0);
+      break;
+    default:
+      launch_quantize_dt<HQ_F16>(layout, grid, st, x, n_heads, n_rows, D, x_head_stride,
+                                 x_row_stride, codes, sz, dst_head_rows, dst_row0);
+      break;
+  }
+  return check_launch("hq_quantize_kv");
+}
+
+extern "C" hq_status hq_gather_rows(const void *src, hq_dtype dtype, int n_heads,
+                                    int64_t src_rows, int D, const int32_t *idx, int k, void *dst,
+                                    void *stream) {
+  if (!dtype_ok(dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_gather_rows: bad dtype %d", dtype);
+  if (n_heads < 0 || k < 0 || src_rows < 0 || D <= 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_gather_rows: negative size");
+  const int row_bytes = D * dtype_bytes(dtype);
+  if (row_bytes % 16 != 0) return fail(HQ_ERR_UNSUPPORTED, "hq_gather_rows: row bytes must be a multiple of 16");
+  if (n_heads == 0 || k == 0) { clear_error(); return HQ_OK; }
+  if (!src || !idx || !dst) return fail(HQ_ERR_INVALID_ARG, "hq_gather_rows: null pointer");
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
+    return fail(HQ_ERR_INVALID_ARG, "hq_gather_rows: buffers must be 16-byte aligned");
+  const int64_t threads = static_cast<int64_t>(n_heads) * k * (row_bytes / 16);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_gather_rows: too many rows");
+  hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     as_stream(stream), static_cast<const uint8_t *>(src), src_rows, row_bytes,
+                     idx, k, n_heads, static_cast<uint8_t *>(dst));
+  return check_launch("hq_gather_rows");
+}

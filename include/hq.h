@@ -1,0 +1,223 @@
+/*
+ * hq.h -- C ABI of the HyQuant hybrid-precision attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes (pages about "HyQuant: Hybrid-Precision
+ * Quantization for LLM Attention", cited by page and section):
+ *   [AFS] "HyQuant ... Explained for Beginners" (aifromscratch.in),
+ *         "How It Works: The Hybrid-Precision Strategy" and
+ *         "The Technical Mechanics: Two Operational Modes".
+ *   [WPN] "Hybrid-precision attention reduces compute cost with minimal
+ *         accuracy loss" (wpnews.pro), body paragraph 4.
+ *   [KQ]  kipquest.com paper page 2608.27875, "The abstract".
+ *   [HP]  hotpaper.ai paper page 2608.27875, technical-approach list.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless a comment says "host".
+ *  - The caller allocates and frees every buffer, workspaces included; the
+ *    library never allocates device memory and keeps no pointer after a call
+ *    returns.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *    work; buffers must stay alive until the stream has reached it.
+ *  - Every host-checkable precondition is validated before anything is
+ *    enqueued. On failure the call returns a non-zero hq_status, enqueues
+ *    nothing, and hq_last_error() gives a message (thread local). A failed
+ *    launch returns HQ_ERR_HIP. No C++ exception crosses this boundary.
+ *  - Device-side preconditions that are NOT checked: inputs are finite and
+ *    the fp16 scale/zero of every group is finite (|x| <= 65504); index lists
+ *    are strictly ascending where stated.
+ *  - Results are deterministic: same inputs, same sizes, same device =>
+ *    bitwise identical outputs (no floating-point atomics, fixed merge order).
+ *
+ * INT4 storage (the pages say only "4-bit keys and values" [AFS, How It
+ * Works, item 3]; the format is this library's reading): per token and per
+ * group of `group` = 32 consecutive channels, codes c in 0..15 with
+ * x_hat = c * s + z, s = fp16((max - min) / 15), z = fp16(min), c =
+ * clamp(rint_even((x - z) / s), 0, 15) in fp32, s = 0 and c = 0 for a
+ * constant group. Two planes per head:
+ *  - codes, HQ_LAYOUT_ROWS: [rows][D/2] bytes, byte j of a row holds channel
+ *    2j in its low nibble and channel 2j+1 in its high nibble (used for K).
+ *  - codes, HQ_LAYOUT_TILE16: rows grouped in tiles of 16; tile u is a
+ *    [D/2][16] byte block: byte (j, r) holds channels 2j (low nibble) and
+ *    2j+1 (high nibble) of row 16u + r (used for V: one 16-byte load gives one
+ *    channel pair of 16 consecutive tokens). The row capacity of a TILE16
+ *    plane is a multiple of 16.
+ *  - scale/zero: [rows][D/group][2] fp16 bit patterns {scale, zero}.
+ */
+#ifndef HQ_H_
+#define HQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HQ_ABI_VERSION 1
+
+typedef enum {
+  HQ_OK = 0,
+  HQ_ERR_INVALID_ARG = 1,   /* a null pointer, a size or range out of bounds */
+  HQ_ERR_UNSUPPORTED = 2,   /* a valid but unimplemented shape or dtype */
+  HQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  HQ_ERR_HIP = 4            /* the HIP runtime reported an error */
+} hq_status;
+
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1, HQ_F16 = 2 } hq_dtype;
+
+typedef enum { HQ_LAYOUT_ROWS = 0, HQ_LAYOUT_TILE16 = 1 } hq_code_layout;
+
+/* Detector forms: the pages' matrix multiplication (MFMA) followed by
+ * column sums, or the same scores through the sum of the query rows followed
+ * by one matrix-vector product (equal by linearity). */
+typedef enum { HQ_DETECT_MATMUL = 0, HQ_DETECT_QSUM = 1 } hq_detect_method;
+
+/*
+ * One layer's hybrid KV cache for a decode step [AFS, How It Works: the
+ * three token sets; Technical Mechanics, Decode Stage]. Caller owned.
+ * Positions [0, T) split into:
+ *   Win = [T - W, T)   local window (current token included), 16-bit rows;
+ *   VL  = a set of k positions inside [0, T - W), 16-bit rows;
+ *   the rest of [0, T - W), INT4 rows from the planes.
+ * The VL set is given twice, in the two forms the kernel reads: the compact
+ * rows vl_k / vl_v (row i = the i-th VL position in ascending order, built by
+ * hq_gather_rows) and the membership bitmap vl_bits (built by hq_vl_bitmap
+ * from the same index list). The INT4 planes cover at least [0, T - W); rows
+ * at VL positions may hold anything: they never reach the result.
+ */
+typedef struct {
+  int B, Hkv, D, group;       /* D in {64, 128}; group = 32 */
+  int64_t T;                  /* context length including the current token */
+  int W;                      /* window length, 0 <= W <= T */
+  int k;                      /* VL rows per (b, h), 0 <= k <= T - W */
+  int64_t t_cap;              /* row capacity of the INT4 planes: >= T - W and
+                                 a multiple of 32 */
+  const uint8_t *k_codes;     /* HQ_LAYOUT_ROWS   [B][Hkv][t_cap][D/2] */
+  const uint8_t *v_codes;     /* HQ_LAYOUT_TILE16 [B][Hkv][t_cap/16][D/2][16] */
+  const uint16_t *k_sz;       /* [B][Hkv][t_cap][D/group][2] fp16 {s, z} */
+  const uint16_t *v_sz;       /* [B][Hkv][t_cap][D/group][2] fp16 {s, z} */
+  const uint32_t *vl_bits;    /* [B][Hkv][t_cap/32]: bit t%32 of word t/32 set
+                                 iff position t is a VL position */
+  const void *vl_k, *vl_v;    /* [B][Hkv][k][D] hp_dtype, VL rows in ascending
+                                 position order */
+  const void *win_k, *win_v;  /* [B][Hkv][W][D] hp_dtype, ring buffer: position
+                                 T - W + i sits in row (win_offset + i) % W */
+  int win_offset;             /* 0 <= win_offset < W (0 when W == 0) */
+  hq_dtype hp_dtype;          /* dtype of the 16-bit rows: HQ_BF16, HQ_F16 or HQ_F32 */
+} hq_hybrid_kv;
+
+/*
+ * hq_quantize_kv -- pack rows into INT4 codes plus fp16 scale/zero
+ * [AFS, How It Works, item 3: keys and values of the quantized majority are
+ * 4-bit; KQ, The abstract: most attention states go to low-bit formats].
+ *
+ * Source row r of head h (0 <= h < n_heads, 0 <= r < n_rows) starts at
+ * element x + h * x_head_stride + r * x_row_stride (x_dtype elements, the D
+ * channels contiguous). It is written to row dst_row0 + r of head h in
+ * planes with dst_head_rows rows per head:
+ *   codes: [n_heads][dst_head_rows] rows in `layout` (TILE16 needs
+ *          dst_head_rows % 16 == 0),
+ *   sz:    [n_heads][dst_head_rows][D/group][2].
+ * Requires dst_row0 + n_rows <= dst_head_rows, D % group == 0, group == 32,
+ * D in {64, 128}. n_rows == 0 or n_heads == 0 is a no-op.
+ */
+hq_status hq_quantize_kv(const void *x, hq_dtype x_dtype, int n_heads, int64_t n_rows,
+                         int D, int group, int64_t x_head_stride, int64_t x_row_stride,
+                         uint8_t *codes, uint16_t *sz, hq_code_layout layout,
+                         int64_t dst_head_rows, int64_t dst_row0, void *stream);
+
+/*
+ * hq_gather_rows -- copy the vertical-line rows of K or V into the compact
+ * 16-bit buffer [AFS, How It Works, item 1: vertical-line tokens stay in full
+ * precision]. For each head h and i < k: dst[h][i][:] = src[h][idx[h][i]][:],
+ * src [n_heads][src_rows][D], dst [n_heads][k][D], both of dtype `dtype`,
+ * idx [n_heads][k] int32. An index outside [0, src_rows) yields a zero row
+ * (nothing outside src is read). k == 0 is a no-op.
+ */
+hq_status hq_gather_rows(const void *src, hq_dtype dtype, int n_heads, int64_t src_rows, int D,
+                         const int32_t *idx, int k, void *dst, void *stream);
+
+/*
+ * hq_vl_bitmap -- membership bitmap of the vertical-line set, the form in
+ * which the decode kernel skips the INT4 rows of VL positions [AFS, How It
+ * Works: the three token sets are disjoint; a VL token is read in 16 bits
+ * only]. bits [n_heads][t_cap/32] is overwritten: bit t%32 of word t/32 of
+ * head h is set iff t appears in vl_idx[h][0..k). Entries outside [0, t_cap)
+ * are ignored. Requires t_cap % 32 == 0.
+ */
+hq_status hq_vl_bitmap(const int32_t *vl_idx, int n_heads, int k, int64_t t_cap, uint32_t *bits,
+                       void *stream);
+
+/*
+ * hq_detect_vlines -- vertical-line detector [WPN, body paragraph 4: query
+ * vectors are accumulated, one matrix multiplication runs every 64 tokens and
+ * its columns are summed; HP: the tokens come from a column-wise attention
+ * score and are under 5 %].
+ *
+ * Accumulate: if q_new != NULL, q_new [B][Hq][D] is copied into slot
+ * (step mod R) of the ring q_acc [B][Hq][R][D].
+ * Detect: when step mod R == R - 1, or force != 0, for every (b, h) with
+ * query heads i in [h*G, (h+1)*G), G = Hq / Hkv:
+ *   c_j = sum over r < R and those i of q_acc[b][i][r] . k[b][h][j],
+ *   for candidates j in [0, cand_end);
+ *   idx_out[b][h] = the k_top positions with the largest c_j, equal scores
+ *   to the lower position, in ascending order.
+ * k [B][Hkv][k_rows][D] (k_rows >= cand_end). q_new, q_acc and k share
+ * `dtype` (HQ_BF16 or HQ_F16; HQ_F32 only with HQ_DETECT_QSUM).
+ * score_out (optional) [B][Hkv][cand_end] int64 receives c_j in units of
+ * 2^-16 (rounded to nearest even). With HQ_DETECT_MATMUL the product is formed
+ * by bf16/fp16 MFMA with fp32 accumulation: for each residue rho mod 32 the
+ * rows congruent to rho are accumulated in fp32, and the 32 sums are added in
+ * int64; when every input is a multiple of 2^-4 and every partial sum stays
+ * below 2^16 in magnitude the scores are exact. With HQ_DETECT_QSUM the query
+ * rows are summed in fp64 and multiplied with each key in fp64 (exact for the
+ * same inputs).
+ * *ran (host, optional) is set to 1 when detection was enqueued, else 0.
+ * Requires 0 <= k_top <= cand_end <= k_rows, 1 <= R <= 1024, D in {64, 128},
+ * Hq % Hkv == 0, ws_bytes >= hq_detect_workspace_size(...).
+ */
+hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype dtype, int B, int Hq,
+                           int Hkv, int D, int R, int64_t step, int force, const void *k,
+                           int64_t k_rows, int64_t cand_end, int k_top,
+                           hq_detect_method method, int32_t *idx_out, int64_t *score_out,
+                           int *ran, void *ws, size_t ws_bytes, void *stream);
+
+size_t hq_detect_workspace_size(int B, int Hkv, int64_t cand_end, int k_top);
+
+/*
+ * hq_decode_attn -- one decode step of attention over the hybrid KV cache
+ * [AFS, Technical Mechanics, Decode Stage: dequantization fused into the
+ * attention computation, decompressing on the fly; KQ, The abstract].
+ * For every b and query head i (KV head h = i / G, G = Hq / Hkv):
+ *   l_j = sm_scale * q[b][i] . key_j over all positions j in [0, T), key_j the
+ *   16-bit row on VL and Win and c * s + z elsewhere; one softmax over all
+ *   of them; out[b][i] = sum_j softmax_j * value_j (fp32);
+ *   lse[b][i] = log(sum_j exp(l_j)) (natural log, optional).
+ * q [B][Hq][D] of q_dtype (HQ_BF16, HQ_F16 or HQ_F32). sm_scale == 0 means
+ * 1/sqrt(D). The positions are split into n_splits ranges per (b, h)
+ * (0 = automatic), each producing a partial softmax state that the last
+ * finishing workgroup merges with the log-sum-exp rule in fixed order.
+ * ws: at least hq_decode_workspace_size(kv, Hq, n_splits) bytes; its first
+ * 4096 bytes (the merge tickets) must be zero before the first call with that
+ * workspace, and every call leaves them zero. Calls that share a workspace
+ * must not run concurrently. Requires Hq % Hkv == 0, G <= 16.
+ */
+hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                         float sm_scale, int n_splits, float *out, float *lse, void *ws,
+                         size_t ws_bytes, void *stream);
+
+size_t hq_decode_workspace_size(const hq_hybrid_kv *kv, int Hq, int n_splits);
+
+/* The split count hq_decode_attn uses for n_splits == 0. */
+int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
+
+const char *hq_status_string(hq_status s);
+const char *hq_last_error(void);
+int hq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H_ */

@@ -11,6 +11,8 @@ build) is:
   float32 with the fp16-rounded s and z (fp16 rounding may push the quotient
   slightly outside [0, 15], hence the clamp);
 * a constant group (max == min) stores s = 0 and codes 0;
+* signed zeros: the pages say nothing; a zero scale or a zero minimum is
+  stored as +0 (s and z are formed as ``value + 0.0`` in float32);
 * dequantized value x_hat = c * s + z;
 * packing: two codes per byte, the even channel in the low nibble.
 
@@ -43,10 +45,11 @@ def quantize_groups(x: np.ndarray, group: int = 32):
     g = xf.reshape(x.shape[:-1] + (D // group, group))
     mn = g.min(axis=-1)
     mx = g.max(axis=-1)
-    s32 = (mx - mn) / np.float32(LEVELS)          # float32 subtract, float32 divide
+    s32 = (mx - mn) / np.float32(LEVELS) + np.float32(0)   # float32 ops; -0 -> +0
+    mn0 = mn + np.float32(0)                               # -0 -> +0
     with np.errstate(over="ignore"):
         s16 = s32.astype(np.float16)
-        z16 = mn.astype(np.float16)
+        z16 = mn0.astype(np.float16)
     if not (np.all(np.isfinite(s16)) and np.all(np.isfinite(z16))):
         raise ValueError("group range or minimum outside the fp16 range")
     s = s16.astype(np.float32)[..., None]

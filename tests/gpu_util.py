@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU parity tests (no test cases here)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import synth
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x32: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Upload values exactly representable in `dtype`."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(device)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(x32)
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == "f16":
+        return torch.from_numpy(np.asarray(x32, dtype=np.float16)).to(device)
+    raise ValueError(dtype)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def rows_codes(plane: torch.Tensor) -> np.ndarray:
+    """HQ_LAYOUT_ROWS plane [..., rows, D/2] -> bytes per logical row."""
+    return plane.cpu().numpy()
+
+
+def tile16_codes(plane: torch.Tensor) -> np.ndarray:
+    """HQ_LAYOUT_TILE16 plane [..., rows/16, D/2, 16] -> [..., rows, D/2] bytes,
+    following the layout stated in include/hq.h."""
+    a = plane.cpu().numpy()
+    a = np.swapaxes(a, -1, -2)                     # [..., rows/16, 16, D/2]
+    return a.reshape(a.shape[:-3] + (a.shape[-3] * 16, a.shape[-1]))
+
+
+def sz_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def upload_kv(w: synth.Workload, n: int | None = None):
+    """K, V of every (b, KV head) on the device, streamed one sequence at a time."""
+    T = w.T if n is None else n
+    dt = TORCH_DT[w.dtype]
+    K = torch.empty((w.B, w.Hkv, T, w.D), dtype=dt, device="cuda")
+    V = torch.empty_like(K)
+    for b in range(w.B):
+        kb = np.stack(synth._parallel(lambda h: synth.keys(w, b, h, T), [(h,) for h in range(w.Hkv)]))
+        vb = np.stack(synth._parallel(lambda h: synth.values(w, b, h, T), [(h,) for h in range(w.Hkv)]))
+        K[b].copy_(to_dev(kb, w.dtype))
+        V[b].copy_(to_dev(vb, w.dtype))
+    return K, V
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    rms = float(np.sqrt(np.mean(np.square(ref))))
+    return float(np.max(np.abs(got - ref))) / rms

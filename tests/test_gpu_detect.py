@@ -1,0 +1,95 @@
+"""GPU parity of hq_detect_vlines against the oracle detector: query ring
+accumulation, exact int64 column scores and bit-exact index sets (both the
+MFMA matmul form and the summed-query form), on tie-heavy small cases and
+on the full GLM-4-9B-shaped (32 q / 2 kv heads, 32K) and
+Llama-3.1-8B-shaped (32 q / 8 kv heads, 32K) workloads."""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_precision_quantized_amd as hq
+import synth
+from oracle import detect
+from tests.gpu_util import TORCH_DT, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+METHODS = [hq.HQ_DETECT_MATMUL, hq.HQ_DETECT_QSUM]
+
+
+def _run(q_acc, K, cand_end, k_top, method, dtype):
+    B, Hq, R, D = q_acc.shape
+    Hkv, k_rows = K.shape[1], K.shape[2]
+    qd = to_dev(q_acc, dtype)
+    kd = to_dev(K, dtype)
+    idx = torch.full((B, Hkv, max(k_top, 1)), -1, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, Hkv, max(cand_end, 1)), dtype=torch.int64, device="cuda")
+    ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, cand_end, k_top), dtype=torch.uint8, device="cuda")
+    ran = hq.hq_detect_vlines(None, qd, B, Hq, Hkv, D, R, 0, True, kd, k_rows, cand_end, k_top,
+                              method, idx, sc, ws)
+    torch.cuda.synchronize()
+    assert ran
+    return idx.cpu().numpy()[..., :k_top], sc.cpu().numpy()[..., :cand_end]
+
+
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("B,Hq,Hkv,D,R,n,ce,k_top,dtype,spread", [
+    (2, 8, 2, 128, 64, 3000, 2900, 145, "bf16", 3.0),
+    (1, 4, 4, 128, 5, 1000, 999, 50, "bf16", 0.25),     # many equal scores
+    (1, 6, 2, 64, 33, 777, 700, 35, "bf16", 1.0),
+    (1, 8, 1, 128, 64, 2048, 1920, 1920, "f16", 1.0),   # k_top == cand_end
+    (1, 8, 2, 128, 64, 2048, 1920, 0, "bf16", 1.0),     # k_top == 0 (scores only)
+    (1, 8, 2, 128, 64, 1000, 1, 1, "bf16", 1.0),        # single candidate
+])
+def test_detect_small_exact(method, B, Hq, Hkv, D, R, n, ce, k_top, dtype, spread):
+    say(f"detect method={method} B={B} Hq={Hq} Hkv={Hkv} D={D} R={R} n={n} ce={ce} k={k_top} {dtype}")
+    rng = np.random.default_rng(n + R)
+    q = np.rint(rng.standard_normal((B, Hq, R, D)) * spread * 16) / 16
+    K = np.rint(rng.standard_normal((B, Hkv, n, D)) * spread * 16) / 16
+    if dtype == "bf16":
+        q, K = synth.round_dtype(q, "bf16"), synth.round_dtype(K, "bf16")
+    else:
+        q = q.astype(np.float16).astype(np.float32)
+        K = K.astype(np.float16).astype(np.float32)
+    want_idx, want_sc = detect.detect(q, K, ce, k_top)
+    got_idx, got_sc = _run(q, K, ce, k_top, method, dtype)
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+
+
+def test_accumulate_ring_and_cadence():
+    say("detect accumulate ring")
+    B, Hq, Hkv, D, R, n, ce, kt = 1, 4, 2, 128, 8, 300, 280, 14
+    rng = np.random.default_rng(9)
+    steps = synth.round_dtype(np.rint(rng.standard_normal((2 * R, B, Hq, D)) * 16) / 16, "bf16")
+    K = synth.round_dtype(np.rint(rng.standard_normal((B, Hkv, n, D)) * 16) / 16, "bf16")
+    q_acc = torch.zeros((B, Hq, R, D), dtype=torch.bfloat16, device="cuda")
+    kd = to_dev(K, "bf16")
+    idx = torch.zeros((B, Hkv, kt), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, ce, kt), dtype=torch.uint8, device="cuda")
+    ran_at = []
+    for s in range(2 * R):
+        if hq.hq_detect_vlines(to_dev(steps[s], "bf16"), q_acc, B, Hq, Hkv, D, R, s, False, kd, n, ce, kt,
+                               hq.HQ_DETECT_MATMUL, idx, None, ws):
+            ran_at.append(s)
+    torch.cuda.synchronize()
+    assert ran_at == [R - 1, 2 * R - 1]
+    ring = q_acc.float().cpu().numpy()
+    want_ring = np.moveaxis(steps[R:], 0, 2)              # [B][Hq][R][D], slot = step mod R
+    assert np.array_equal(ring, want_ring)
+    want_idx, _ = detect.detect(want_ring, K, ce, kt)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+
+
+@pytest.mark.parametrize("name", ["glm32k", "llama32k"])
+@pytest.mark.parametrize("method", METHODS)
+def test_detect_full_workload(name, method):
+    w = synth.WORKLOADS[name]
+    say(f"detect full workload {name} method={method}")
+    K = synth.all_keys(w)
+    q = synth.all_query_histories(w)
+    ce = w.T - w.W
+    want_idx, want_sc = detect.detect(q, K, ce, w.k)
+    got_idx, got_sc = _run(q, K, ce, w.k, method, w.dtype)
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)

@@ -138,3 +138,12 @@ def test_rejects_bad_inputs():
         quant.quantize_groups(np.array([[1e6] * 32], dtype=np.float32))
     with pytest.raises(ValueError):
         quant.quantize_groups(np.array([[0.1] * 32], dtype=np.float64))  # not exact in fp32
+
+
+def test_signed_zero_is_canonical():
+    x = np.zeros((2, 32), dtype=np.float32)
+    x[0, ::2] = -0.0
+    x[1, 5] = 0.5
+    x[1, 6] = -0.0
+    codes, s, z = quant.quantize_groups(x, 32)
+    assert s.view(np.uint16)[0, 0] == 0 and z.view(np.uint16).tolist() == [[0], [0]]
