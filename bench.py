@@ -1,0 +1,327 @@
+"""Benchmark of the HyQuant decode hot path on one MI355X.
+
+One step = one steady-state decode step of one attention layer over its
+hybrid KV cache:
+  1. hq_detect_vlines: the step's queries go into the 64-slot ring; every
+     64th step (step mod 64 == 63) the Q_acc . K^T column scores and the
+     top-k run, and the new VL set is installed (hq_vl_bitmap +
+     hq_gather_rows of the VL keys and values);
+  2. hq_quantize_kv: the token leaving the window is packed into INT4;
+  3. hq_decode_attn: attention over INT4 + VL + window with the split-K
+     LSE merge.
+Steps rotate over `--copies` independent layer caches (>= 1 GB in total) so
+that the 256 MB Infinity Cache cannot hold the working set: every step reads
+its cache from HBM as it would in a model with many layers. All inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line (rank 0). `value` is the algorithmic HBM bytes of a
+step divided by the measured step time (GB/s); `ms_per_step` is the step
+time. `roofline` is the decode kernel alone, timed per launch with HIP
+events on the launch stream. `cpu_baseline` is the CPU oracle on a bounded
+sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention µs/step and achieved HBM GB/s (% of peak) at 32K/128K ctx"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="llama32k", choices=["llama32k", "qwen128k", "glm32k"])
+    ap.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0 = auto, >= 1 GB)")
+    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum"])
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--kernel-launches", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hybrid_precision_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode attention shards by KV head or batch with no communication; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_precision_quantized_amd as hq
+    import synth
+
+    hq.lib()                                   # fail loudly if the library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS[args.workload]
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
+    R = 64
+    nq = T - W
+    method = hq.HQ_DETECT_MATMUL if args.detect_method == "matmul" else hq.HQ_DETECT_QSUM
+
+    # ------------------------------------------------------------ inputs
+    t_setup = time.time()
+
+    def to_dev(x32):
+        if w.dtype == "bf16":
+            return torch.from_numpy(synth.f32_to_bf16_bits(x32).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x32)).to(dev)
+
+    K0 = torch.empty((B, Hkv, T, D), dtype=dt, device=dev)
+    V0 = torch.empty_like(K0)
+    for b in range(B):
+        K0[b].copy_(to_dev(np.stack([synth.keys(w, b, h) for h in range(Hkv)])))
+        V0[b].copy_(to_dev(np.stack([synth.values(w, b, h) for h in range(Hkv)])))
+    q_steps = to_dev(np.stack([synth.all_queries(w.replace(seed=w.seed + 17 * s)) for s in range(4)]))
+    q_hist = to_dev(synth.all_query_histories(w))
+
+    layer_bytes = (2 * K0.numel() * K0.element_size()) + 2 * B * Hkv * T * (D // 2 + D // 16)
+    copies = args.copies or max(1, int(np.ceil(1.2e9 / layer_bytes)))
+    caches, Ks, Vs, qaccs = [], [], [], []
+    idx_new = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
+    det_ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, nq, k), dtype=torch.uint8, device=dev)
+    for c in range(copies):
+        Kc = K0 if c == 0 else K0.clone()
+        Vc = V0 if c == 0 else V0.clone()
+        qa = q_hist.clone()
+        cache = hq.HybridCache(B, Hkv, D, T, W, k, dt)
+        cache.quantize(Kc, Vc)
+        hq.hq_detect_vlines(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method, idx_new, None, det_ws)
+        cache.set_vl(Kc, Vc, idx_new)
+        cache.set_window(Kc, Vc)
+        caches.append(cache)
+        Ks.append(Kc)
+        Vs.append(Vc)
+        qaccs.append(qa)
+    descs = [c.descriptor() for c in caches]
+    dec_ws = [torch.zeros(hq.hq_decode_workspace_size(d, Hq, args.splits), dtype=torch.uint8, device=dev)
+              for d in descs]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    n_heads = B * Hkv
+
+    def step(s: int):
+        c = s % copies
+        cache, Kc, Vc = caches[c], Ks[c], Vs[c]
+        qn = q_steps[s % q_steps.shape[0]]
+        ran = hq.hq_detect_vlines(qn, qaccs[c], B, Hq, Hkv, D, R, s, False, Kc, T, nq, k, method,
+                                  idx_new, None, det_ws)
+        if ran:
+            hq.hq_vl_bitmap(idx_new, n_heads, k, cache.t_cap, cache.vl_bits)
+            hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
+            hq.hq_gather_rows(Vc, n_heads, T, D, idx_new, k, cache.vl_v)
+        # the token leaving the window goes to INT4 (static context: last INT4 row)
+        hq.hq_quantize_kv(Kc[:, :, nq - 1:], n_heads, 1, D, T * D, D, cache.k_codes, cache.k_sz,
+                          hq.HQ_LAYOUT_ROWS, cache.t_cap, nq - 1)
+        hq.hq_quantize_kv(Vc[:, :, nq - 1:], n_heads, 1, D, T * D, D, cache.v_codes, cache.v_sz,
+                          hq.HQ_LAYOUT_TILE16, cache.t_cap, nq - 1)
+        hq.hq_decode_attn(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
+
+    # ------------------------------------------------------------ timed steps
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    base = args.warmup
+    e0.record(stream)
+    for s in range(base, base + args.steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    n_detect = sum(1 for s in range(base, base + args.steps) if s % R == R - 1)
+
+    # ------------------------------------------------------------ decode kernel alone
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_launches)]
+    for i in range(args.kernel_launches):
+        c = i % copies
+        starts[i].record(stream)
+        hq.hq_decode_attn(q_steps[i % q_steps.shape[0]], Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])   # us
+    dec_us = float(np.mean(durs))
+
+    # ------------------------------------------------------------ detector alone (amortized share)
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    n_det = 20
+    d0.record(stream)
+    for i in range(n_det):
+        c = i % copies
+        hq.hq_detect_vlines(None, qaccs[c], B, Hq, Hkv, D, R, 0, True, Ks[c], T, nq, k, method, idx_new, None, det_ws)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    det_us = d0.elapsed_time(d1) * 1e3 / n_det
+
+    if args.calib_copy_mb:
+        a = torch.empty(args.calib_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ bytes
+    hp = K0.element_size()
+    units = B * Hkv
+    dec_bytes = (units * ((nq - k) * (D + (D // 32) * 8) + (k + W) * 2 * D * hp + (T - W + 31) // 32 * 4)
+                 + B * Hq * D * hp + B * Hq * D * 4 + B * Hq * 4)
+    det_bytes = units * nq * D * hp + B * Hq * R * D * hp + units * k * 4
+    gather_bytes = 2 * units * k * D * hp * 2 + units * (caches[0].t_cap // 32) * 4
+    evict_bytes = 2 * units * (D * hp + D // 2 + (D // 32) * 4)
+    acc_bytes = 2 * B * Hq * D * hp
+    step_bytes = dec_bytes + evict_bytes + acc_bytes + (det_bytes + gather_bytes) * n_detect / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_us * 1e-6) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            rec = tr.get(args.workload)
+            if rec and rec.get("source_hash") == source_hash("hq_decode.hip", "hq_common.h") \
+                    and rec.get("splits", 0) == args.splits:
+                traffic = rec["bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            traffic = None
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds, step_bytes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4+bf16 (fp32 accumulate)" if w.dtype == "bf16" else f"int4+{w.dtype}",
+        "data": "synthetic (seeded; shapes of the named model's attention layer, random-init values)",
+        "config": {
+            "workload": f"{args.workload}: one decode step of one attention layer, B {B}, "
+                        f"{Hq} q / {Hkv} kv heads, head_dim {D}, context {T}, window {W}, "
+                        f"VL budget {k}, INT4 group 32 with fp16 scale/zero",
+            "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
+            "layer_copies_rotated": copies, "detect_method": args.detect_method,
+            "decode_splits": hq.hq_decode_auto_splits(descs[0], Hq) if args.splits == 0 else args.splits,
+            "detect_every": R, "detections_in_timed_steps": n_detect,
+        },
+        "roofline": {
+            "kernel": "decode_kernel (hq_decode_attn)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+            "avg_launch_us": round(dec_us, 3),
+        },
+        "detector": {"us_per_detection": round(det_us, 2), "method": args.detect_method,
+                     "overhead_vs_64_decode_kernels": round(det_us / (64 * dec_us), 4)},
+        "step_bytes": int(step_bytes),
+        "setup_s": round(t_setup, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, seconds: float, step_bytes: float):
+    """The CPU oracle (unchanged) on a bounded sample of the same step: the
+    decode of whole (b, KV head) units over their cache, plus the amortized
+    detector share, repeated until `seconds` of work; scaled to one step."""
+    import synth
+    from oracle import attention, detect, quant
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    nq = w.T - w.W
+    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    prep = []
+    for (b, h) in units[:4]:
+        K = synth.keys(w, b, h)
+        V = synth.values(w, b, h)
+        kp, ks = quant.quantize_rows(K[:nq])
+        vp, vs = quant.quantize_rows(V[:nq])
+        vl = synth.random_vl_index(w, b, h)
+        q = np.stack([synth.query(w, b, i) for i in range(h * w.G, (h + 1) * w.G)])
+        qh = np.stack([synth.query_history(w, b, i) for i in range(h * w.G, (h + 1) * w.G)]).reshape(-1, w.D)
+        prep.append((q, K, V, kp, ks, vp, vs, vl, qh))
+    t0 = time.time()
+    n_units = 0
+    n_det = 0
+    while time.time() - t0 < seconds:
+        q, K, V, kp, ks, vp, vs, vl, qh = prep[n_units % len(prep)]
+        attention.decode_head(q, K, V, kp, ks, vp, vs, vl, w.W)
+        n_units += 1
+        if n_units % 16 == 0:
+            detect.detect_head(qh, K, nq, w.k)
+            n_det += 1
+        if n_units >= 200:
+            break
+    el = time.time() - t0
+    # per unit: decode + detect share (the detector runs once per 64 steps)
+    t_det_share = 0.0
+    per_unit = el / max(n_units, 1)
+    if n_det:
+        # separate the two: time one detection alone
+        q, K, V, kp, ks, vp, vs, vl, qh = prep[0]
+        t1 = time.time()
+        detect.detect_head(qh, K, nq, w.k)
+        t_det = time.time() - t1
+        per_unit = (el - n_det * t_det) / n_units
+        t_det_share = t_det / 64
+    s_per_step = (per_unit + t_det_share) * len(units)
+    return {"value": round(step_bytes / s_per_step / 1e9, 3), "unit": "GB/s",
+            "us_per_step": round(s_per_step * 1e6, 1), "cores": threads, "kind": "oracle",
+            "sample": f"{n_units} (b, kv-head) decode units of the {w.name} step over prebuilt INT4 "
+                      f"caches (+{n_det} detections), {el:.1f} s, scaled to all {len(units)} units "
+                      f"and the detector's 1/64 share"}
+
+
+if __name__ == "__main__":
+    main()

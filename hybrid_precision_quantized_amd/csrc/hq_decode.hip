@@ -28,10 +28,13 @@
 //    log2(e) and 1/sqrt(D) factors folded into the scale.
 //  * P . V without dequantizing v: values use HQ_LAYOUT_TILE16, so lane
 //    (channel pair j) loads 16 consecutive tokens of its two channels with
-//    one 16-byte load; token pairs become fp16 pairs (1024 + c_t, 1024 +
-//    c_t+1) and are multiplied by the fp16 pair (p_t s_t, p_t+1 s_t+1) with
-//    v_dot2. The 1024 offset and the zero point are added back once per split
-//    from per-group sums. No cross-lane reduction over tokens is needed.
+//    one 16-byte load; a token pair becomes the exact fp16 pair
+//    (c_t - 8, c_t+1 - 8) (one and-or onto 1024 and one packed fp16
+//    subtract) and is multiplied by the fp16 pair (p_t s_t, p_t+1 s_t+1) with
+//    v_dot2. Centring the codes keeps the fp16 rounding of p s from adding a
+//    bias proportional to the mean code; the zero point, as z + 8 s, is added
+//    once per split from per-group sums of p (z + 8 s). No cross-lane
+//    reduction over tokens is needed.
 //  * Split partials (m, l, o) go to the workspace; the last workgroup of a
 //    unit to finish (atomic ticket) merges them in split order:
 //    m* = max m_s, L = sum 2^(m_s - m*) l_s, out = sum 2^(m_s - m*) o_s / L.
@@ -114,6 +117,11 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
   const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hi));
   return a | (b << 16);
 }
+// packed fp16 add of two bit patterns (v_pk_add_f16)
+__device__ __forceinline__ uint32_t centre_f16x2(uint32_t a, uint32_t b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) + __builtin_bit_cast(h2, b));
+}
 __device__ __forceinline__ float lo_f16(uint32_t w) { return f16_to_f32(w & 0xFFFFu); }
 __device__ __forceinline__ float hi_f16(uint32_t w) { return f16_to_f32(w >> 16); }
 
@@ -134,8 +142,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Per-wave running state for HB heads. acc_e/acc_o hold the channel pair
-// (2*cp, 2*cp+1) of this lane; fix_off/fix_z are the per-(head, group)
-// constants subtracted/added at the end (INT4 pass only).
+// (2*cp, 2*cp+1) of this lane.
 template <int HB>
 struct WaveState {
   float m[HB];
@@ -147,7 +154,7 @@ struct WaveState {
 struct SharedMem {
   uint32_t ps[kWaves][4 * 4 * 16];      // [wave][h][g][pair]   (INT4 pass)
   float p[kWaves][4 * 32];              // [wave][h][slot]      (16-bit pass)
-  float zo[kWaves][4][4][2];            // [wave][h][g]{off, z}
+  float zo[kWaves][4][4];               // [wave][h][g] zero-point sums
   float bm[kWaves][4];
   float bl[kWaves][4];
   float bo[kWaves][4][128];
@@ -199,9 +206,9 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   constexpr uint32_t kMagic = (QT == HQ_BF16) ? 0x43004300u : 0x64006400u;
   constexpr float kMagicVal = (QT == HQ_BF16) ? 128.f : 1024.f;
 
-  float offl[HB], zl[HB];
+  float zl[HB];
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) { offl[hh] = 0.f; zl[hh] = 0.f; }
+  for (int hh = 0; hh < HB; ++hh) zl[hh] = 0.f;
 
   const uint8_t *kc_base = P.k_codes + head * P.t_cap * (D / 2);
   const uint32_t *ks_base = P.k_sz + head * P.t_cap * (D / 32);
@@ -284,8 +291,10 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
       st.m[hh] = mn;
       p[hh] = fast_exp2(lg - mu);
     }
+    // V scale and the zero point of the centred codes, z + 8 s; zero for
+    // masked tokens (their planes may hold anything, NaN included)
     const float sv = live ? lo_f16(vs) : 0.f;
-    const float zv = live ? hi_f16(vs) : 0.f;
+    const float zv = live ? fmaf(8.f, lo_f16(vs), hi_f16(vs)) : 0.f;
     const bool even = (slot & 1) == 0;
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
@@ -294,8 +303,6 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
       const float ps = p[hh] * sv;
       const float nb = __shfl_down(ps, LPT, 64);
       const uint32_t pair = pack_f16_rne(ps, nb);
-      const float add = dot2_f16(pair, 0x3C003C00u, 0.f);   // fp16 1.0 pair
-      offl[hh] = offl[hh] * alpha[hh] + (even ? add : 0.f);
       if (even) sm.ps[wave][(hh * LPT + g) * 16 + (slot >> 1)] = pair;
     }
     wave_sync();
@@ -317,8 +324,9 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t x = __builtin_amdgcn_perm(0u, vw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
-        const uint32_t e = (x & 0x000F000Fu) | 0x64006400u;
-        const uint32_t o = (x & 0x00F000F0u) | 0x64006400u;
+        // (1024 + c) - 1032 = c - 8 and (1024 + 16 c) - 1152 = 16 (c - 8), exact in fp16
+        const uint32_t e = centre_f16x2((x & 0x000F000Fu) | 0x64006400u, 0xE408E408u);
+        const uint32_t o = centre_f16x2((x & 0x00F000F0u) | 0x64006400u, 0xE480E480u);
         st.acc_e[hh] = dot2_f16(pr[i], e, st.acc_e[hh]);
         st.acc_o[hh] = dot2_f16(pr[i], o, st.acc_o[hh]);
       }
@@ -326,15 +334,11 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
     wave_sync();
   }
 
-  // ---- per-(head, group) constants, then fold them into the accumulators
+  // ---- per-(head, group) zero-point sums, then fold them into the accumulators
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    const float off = xor_sum<LPT>(offl[hh]);
     const float z = xor_sum<LPT>(zl[hh]);
-    if (slot == 0) {
-      sm.zo[wave][hh][g][0] = off;
-      sm.zo[wave][hh][g][1] = z;
-    }
+    if (slot == 0) sm.zo[wave][hh][g] = z;
   }
   wave_sync();
 #pragma unroll
@@ -344,10 +348,9 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
       ae += shfl_xor_f(ae, 32);
       ao += shfl_xor_f(ao, 32);
     }
-    const float off = sm.zo[wave][hh][gp][0];
-    const float z = sm.zo[wave][hh][gp][1];
-    st.acc_e[hh] = (ae - 1024.f * off) + z;
-    st.acc_o[hh] = (ao - 1024.f * off) * 0.0625f + z;
+    const float z = sm.zo[wave][hh][gp];
+    st.acc_e[hh] = ae + z;
+    st.acc_o[hh] = ao * 0.0625f + z;
     st.l[hh] = xor_sum<1>(st.l[hh]) * (1.0f / LPT);
   }
 }

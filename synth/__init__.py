@@ -46,7 +46,7 @@ class Workload:
     T: int
     W: int
     k: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     group: int = 32
     R: int = 64           # detector accumulation depth (decode steps)
     alpha: float = 7.0    # query component along u
@@ -129,6 +129,8 @@ def round_dtype(x: np.ndarray, dtype: str, grid: bool = False) -> np.ndarray:
         return x32
     if dtype == "bf16":
         return bf16_bits_to_f32(f32_to_bf16_bits(x32))
+    if dtype == "f16":
+        return x32.astype(np.float16).astype(np.float32)
     raise ValueError(dtype)
 
 
