@@ -35,12 +35,15 @@
 //    bias proportional to the mean code; the zero point, as z + 8 s, is added
 //    once per split from per-group sums of p (z + 8 s). No cross-lane
 //    reduction over tokens is needed.
-//  * Split partials (m, l, o) go to the workspace; the last workgroup of a
-//    unit to finish (atomic ticket) merges them in split order:
-//    m* = max m_s, L = sum 2^(m_s - m*) l_s, out = sum 2^(m_s - m*) o_s / L.
+//  * Split partials (m, l, o) go to the workspace; a second small kernel
+//    merges them per unit in split order: m* = max m_s,
+//    L = sum 2^(m_s - m*) l_s, out = sum 2^(m_s - m*) o_s / L. (A
+//    last-block merge inside the split kernel needs a device-scope release
+//    per block, which on gfx950 writes back the XCD's L2 each time and costs
+//    far more than one extra launch.)
 //  * Blocks are numbered so that all splits of a unit run on the same XCD
 //    (dispatch is round-robin over the 8 XCDs), keeping the partials of a
-//    unit in one L2.
+//    unit in one L2 for the merge.
 #include <math.h>
 
 #include "hq_common.h"
@@ -64,7 +67,6 @@ struct DecodeParams {
   const void *vl_k, *vl_v, *win_k, *win_v;
   float *out;
   float *lse;
-  uint32_t *tickets;
   float2 *part_ml;          // [B][Hq][S]
   float *part_o;            // [B][Hq][S][D]
   int64_t t_cap;            // rows per head of the INT4 planes
@@ -84,10 +86,36 @@ struct DecodeParams {
 // ---------------------------------------------------------------- lane helpers
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
-template <int FROM>
-__device__ __forceinline__ float xor_max(float v) {
+// DPP lane moves (bound_ctrl: lanes without a source read 0)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowShl = 0x100;      // + n: lane i reads lane i + n of its row of 16
+constexpr int kRowRor = 0x120;      // + n: rotate right by n within the row
+
+// sum over the LPT lanes of a token (consecutive lanes), result in all of them
+template <int LPT>
+__device__ __forceinline__ float token_sum(float v) {
+  v += dpp_f<kQuadXor1>(v);
+  if constexpr (LPT == 4) v += dpp_f<kQuadXor2>(v);
+  return v;
+}
+// max over the token slots of the wave (lanes with equal lane % LPT); every
+// lane of a token holds the same value, so this is the max over all lanes
+template <int LPT>
+__device__ __forceinline__ float slots_max(float v) {
 #pragma unroll
-  for (int m = FROM; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  for (int m = LPT; m < 16; m <<= 1) {
+    if (m == 2) v = fmaxf(v, dpp_f<kRowRor + 2>(v));
+    else if (m == 4) v = fmaxf(v, dpp_f<kRowRor + 4>(v));
+    else v = fmaxf(v, dpp_f<kRowRor + 8>(v));
+  }
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
   return v;
 }
 template <int FROM>
@@ -112,10 +140,11 @@ __device__ __forceinline__ float dot2_q(uint32_t a, uint32_t b, float c) {
   else return dot2_f16(a, b, c);
 }
 
+// two fp32 -> packed fp16, round to nearest even (v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lo));
-  const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hi));
-  return a | (b << 16);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 // packed fp16 add of two bit patterns (v_pk_add_f16)
 __device__ __forceinline__ uint32_t centre_f16x2(uint32_t a, uint32_t b) {
@@ -125,24 +154,30 @@ __device__ __forceinline__ uint32_t centre_f16x2(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float lo_f16(uint32_t w) { return f16_to_f32(w & 0xFFFFu); }
 __device__ __forceinline__ float hi_f16(uint32_t w) { return f16_to_f32(w >> 16); }
 
-template <int DT>
-__device__ __forceinline__ uint32_t f32_bits_to_half(float x) {
-  if constexpr (DT == HQ_BF16) {
-    // q values are bf16 already; this only repacks them
-    return __float_as_uint(x) >> 16;
-  } else {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-  }
-}
-
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
-// Per-wave running state for HB heads. acc_e/acc_o hold the channel pair
-// (2*cp, 2*cp+1) of this lane.
+// 32 channels of one query head starting at element `off`, as 16 raw pairs
+template <int QT>
+__device__ __forceinline__ void load_q32(const void *q, int64_t off, uint32_t (&w)[16]) {
+  const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + off);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = p[i];
+    w[4 * i + 0] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+  }
+}
+template <int QT>
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+  if constexpr (QT == HQ_BF16) return bf16_to_f32(h);
+  else return f16_to_f32(h);
+}
+
+// Per-wave running softmax state for HB heads. acc_e/acc_o hold the channel
+// pair (2*cp, 2*cp+1) of this lane (P . V accumulators, relative to m).
 template <int HB>
 struct WaveState {
   float m[HB];
@@ -151,6 +186,7 @@ struct WaveState {
   float acc_o[HB];
 };
 
+constexpr int kMaxSplits = 256;
 struct SharedMem {
   uint32_t ps[kWaves][4 * 4 * 16];      // [wave][h][g][pair]   (INT4 pass)
   float p[kWaves][4 * 32];              // [wave][h][slot]      (16-bit pass)
@@ -158,10 +194,59 @@ struct SharedMem {
   float bm[kWaves][4];
   float bl[kWaves][4];
   float bo[kWaves][4][128];
-  int last;
 };
 
+// Slow path of the online softmax: the wave max per head and the rescale of
+// every running quantity, taken only when some new logit exceeds the running
+// max (wave-uniform branch).
+template <int HB, int LPT>
+__device__ __forceinline__ void raise_max(const float (&lg)[HB], WaveState<HB> &st, float (&zl)[HB]) {
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const float mx = slots_max<LPT>(lg[hh]);
+    const float mn = fmaxf(st.m[hh], mx);
+    if (mn != st.m[hh]) {
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m[hh] - mu);
+      st.l[hh] *= alpha;
+      st.acc_e[hh] *= alpha;
+      st.acc_o[hh] *= alpha;
+      zl[hh] *= alpha;
+      st.m[hh] = mn;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- INT4 pass
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): loads past the end return 0,
+// so ragged tails need no branch, and offsets are 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+// (x & m) | o in one instruction; m is wave-uniform (SGPR), o in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+  return r;
+}
+
+template <int D>
+struct Int4Loads {
+  u32x4 kc;                 // 32 key codes of this lane's (token, group)
+  uint32_t ks, vs;          // {s, z} of the key / value group
+  uint32_t bits;            // VL bitmap word of this token
+  u32x4 vc;                 // 16 tokens of this lane's value channel pair
+};
+
 template <int D, int HB, int QT>
 __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, int i0,
                            int64_t r0, int64_t r1, WaveState<HB> &st) {
@@ -177,16 +262,39 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   const int gp = cp / 16;
   const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
 
-  // query pairs for this lane's group: qp[hh][j][m] = (q[8j+m], q[8j+m+4])
+  // query pairs of this lane's group: qp[hh][j][m] = (q[8j+m], q[8j+m+4])
   uint32_t qp[HB][4][4];
   float qf[HB][32];
-  float qsum[HB];
+  float qsum[HB], negmq[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const int64_t qoff = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * D + g * 32;
     float v[32];
+    if constexpr (QT == HQ_F32) {
+      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(P.q) + qoff);
 #pragma unroll
-    for (int c = 0; c < 32; ++c) v[c] = load_as_f32<QT>(P.q, qoff + c);
+      for (int i = 0; i < 8; ++i) {
+        const float4 f = p[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+      }
+    } else {
+      uint32_t raw[16];
+      load_q32<QT>(P.q, qoff, raw);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        v[2 * c] = half_bits_to_f32<QT>(raw[c] & 0xFFFFu);
+        v[2 * c + 1] = half_bits_to_f32<QT>(raw[c] >> 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int a = 8 * j + m, c = 8 * j + m + 4;
+          const uint32_t lo = (raw[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
+          const uint32_t hi = (raw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+          qp[hh][j][m] = lo | (hi << 16);
+        }
+    }
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < 32; ++c) s += v[c];
@@ -194,147 +302,144 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
     if constexpr (QT == HQ_F32) {
 #pragma unroll
       for (int c = 0; c < 32; ++c) qf[hh][c] = v[c];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          qp[hh][j][m] = f32_bits_to_half<QT>(v[8 * j + m]) |
-                         (f32_bits_to_half<QT>(v[8 * j + m + 4]) << 16);
     }
   }
   constexpr uint32_t kMagic = (QT == HQ_BF16) ? 0x43004300u : 0x64006400u;
   constexpr float kMagicVal = (QT == HQ_BF16) ? 128.f : 1024.f;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) negmq[hh] = -kMagicVal * qsum[hh];
+  const uint32_t magic = kMagic;           // held in a VGPR for v_and_or_b32
+  const uint32_t vmagic = 0x64006400u;
 
   float zl[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) zl[hh] = 0.f;
 
-  const uint8_t *kc_base = P.k_codes + head * P.t_cap * (D / 2);
-  const uint32_t *ks_base = P.k_sz + head * P.t_cap * (D / 32);
-  const uint32_t *vs_base = P.v_sz + head * P.t_cap * (D / 32);
-  const uint8_t *vc_base = P.v_codes + head * P.t_cap * (D / 2);
-  const uint32_t *bits_base = P.vl_bits + head * P.bits_words;
+  // buffer views of this split (loads past r1 return 0)
+  const uint32_t n = static_cast<uint32_t>(r1 - r0);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k_codes + (head * P.t_cap + r0) * (D / 2), n * (D / 2));
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(P.k_sz + (head * P.t_cap + r0) * (D / 32), n * (D / 8));
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(P.v_sz + (head * P.t_cap + r0) * (D / 32), n * (D / 8));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v_codes + (head * P.t_cap + r0) * (D / 2),
+                                              ((n + 15) / 16) * (CP * 16));
+  const uint32_t w_first = static_cast<uint32_t>(r0 >> 5);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(P.vl_bits + head * P.bits_words + w_first,
+                                              static_cast<uint32_t>(((r1 + 31) >> 5) - w_first) * 4);
+  const uint32_t r0_bit = static_cast<uint32_t>(r0 & 31);
 
+  auto issue = [&](int64_t c, Int4Loads<D> &L) {
+    const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;      // local token
+    L.kc = bload16(rk, tok * (D / 2) + g * 16);
+    L.ks = bload4(rks, tok * (D / 8) + g * 4);
+    L.vs = bload4(rvs, tok * (D / 8) + g * 4);
+    L.bits = bload4(rb, ((r0_bit + tok) >> 5) * 4);
+    const uint32_t vt = static_cast<uint32_t>(c) * (SLOTS / 16) + sub;  // local tile
+    L.vc = bload16(rv, vt * (CP * 16) + cp * 16);
+  };
+
+  // NPF-deep prefetch ring: while a wave works on one step, the loads of the
+  // next NPF - 1 steps of that wave are in flight (the ring is unrolled so
+  // every buffer stays in fixed registers).
+  constexpr int NPF = 3;
   const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
-  for (int64_t c = wave; c < nsteps; c += kWaves) {
-    const int64_t t0 = r0 + c * SLOTS;
-    const int64_t t = t0 + slot;
-    const bool tv = t < r1;
-    uint4 kc = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t ks = 0u, vs = 0u, bits = 0u;
-    if (tv) {
-      kc = *reinterpret_cast<const uint4 *>(kc_base + t * (D / 2) + g * 16);
-      ks = ks_base[t * (D / 32) + g];
-      vs = vs_base[t * (D / 32) + g];
-      bits = bits_base[t >> 5];
-    }
-    const int64_t vt = (t0 >> 4) + sub;          // 16-token tile for this P.V lane
-    uint4 vc = make_uint4(0u, 0u, 0u, 0u);
-    if (vt * 16 < r1) vc = *reinterpret_cast<const uint4 *>(vc_base + vt * (CP * 16) + cp * 16);
+  Int4Loads<D> ring[NPF];
+#pragma unroll
+  for (int jr = 0; jr < NPF; ++jr) issue(wave + jr * kWaves, ring[jr]);
+  for (int64_t cb = wave; cb < nsteps; cb += NPF * kWaves) {
+#pragma unroll
+    for (int jr = 0; jr < NPF; ++jr) {
+      const int64_t c = cb + jr * kWaves;
+      if (c >= nsteps) break;
+      Int4Loads<D> &cur = ring[jr];
+      const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
 
-    // ---- q . k
-    float part[HB];
-    const uint32_t w[4] = {kc.x, kc.y, kc.z, kc.w};
-    if constexpr (QT == HQ_F32) {
+      // ---- q . k (k never dequantized: s * sum(q c) + z * sum(q))
+      float part[HB];
+      const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+      if constexpr (QT == HQ_F32) {
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
+        for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float cv = static_cast<float>((w[j] >> (4 * e)) & 15u);
+          for (int e = 0; e < 8; ++e) {
+            const float cv = static_cast<float>((w[j] >> (4 * e)) & 15u);
 #pragma unroll
-          for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(qf[hh][8 * j + e], cv, part[hh]);
-        }
-    } else {
+            for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(qf[hh][8 * j + e], cv, part[hh]);
+          }
+      } else {
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) part[hh] = -kMagicVal * qsum[hh];
+        for (int hh = 0; hh < HB; ++hh) part[hh] = negmq[hh];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t x0 = (w[j] & 0x000F000Fu) | kMagic;
-        const uint32_t x1 = ((w[j] >> 4) & 0x000F000Fu) | kMagic;
-        const uint32_t x2 = ((w[j] >> 8) & 0x000F000Fu) | kMagic;
-        const uint32_t x3 = ((w[j] >> 12) & 0x000F000Fu) | kMagic;
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x0 = and_or(w[j], 0x000F000Fu, magic);
+          const uint32_t x1 = and_or(w[j] >> 4, 0x000F000Fu, magic);
+          const uint32_t x2 = and_or(w[j] >> 8, 0x000F000Fu, magic);
+          const uint32_t x3 = and_or(w[j] >> 12, 0x000F000Fu, magic);
 #pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-          part[hh] = dot2_q<QT>(qp[hh][j][0], x0, part[hh]);
-          part[hh] = dot2_q<QT>(qp[hh][j][1], x1, part[hh]);
-          part[hh] = dot2_q<QT>(qp[hh][j][2], x2, part[hh]);
-          part[hh] = dot2_q<QT>(qp[hh][j][3], x3, part[hh]);
+          for (int hh = 0; hh < HB; ++hh) {
+            part[hh] = dot2_q<QT>(qp[hh][j][0], x0, part[hh]);
+            part[hh] = dot2_q<QT>(qp[hh][j][1], x1, part[hh]);
+            part[hh] = dot2_q<QT>(qp[hh][j][2], x2, part[hh]);
+            part[hh] = dot2_q<QT>(qp[hh][j][3], x3, part[hh]);
+          }
         }
       }
-    }
-    const float ssc = lo_f16(ks) * P.cs;
-    const float zsc = hi_f16(ks) * P.cs;
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(ssc, part[hh], zsc * qsum[hh]);
-#pragma unroll
-    for (int m = 1; m < LPT; m <<= 1)
-#pragma unroll
-      for (int hh = 0; hh < HB; ++hh) part[hh] += shfl_xor_f(part[hh], m);
-
-    const bool is_vl = (bits >> (t & 31)) & 1u;
-    const bool live = tv && !is_vl;
-
-    // ---- online softmax
-    float p[HB], alpha[HB];
-    bool rescale = false;
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      const float lg = live ? part[hh] : kNegInf;
-      const float mx = xor_max<LPT>(lg);
-      const float mn = fmaxf(st.m[hh], mx);
-      const float mu = (mn == kNegInf) ? 0.f : mn;
-      alpha[hh] = fast_exp2(st.m[hh] - mu);
-      rescale |= (mn != st.m[hh]);
-      st.m[hh] = mn;
-      p[hh] = fast_exp2(lg - mu);
-    }
-    // V scale and the zero point of the centred codes, z + 8 s; zero for
-    // masked tokens (their planes may hold anything, NaN included)
-    const float sv = live ? lo_f16(vs) : 0.f;
-    const float zv = live ? fmaf(8.f, lo_f16(vs), hi_f16(vs)) : 0.f;
-    const bool even = (slot & 1) == 0;
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      st.l[hh] = st.l[hh] * alpha[hh] + p[hh];
-      zl[hh] = fmaf(p[hh], zv, zl[hh] * alpha[hh]);
-      const float ps = p[hh] * sv;
-      const float nb = __shfl_down(ps, LPT, 64);
-      const uint32_t pair = pack_f16_rne(ps, nb);
-      if (even) sm.ps[wave][(hh * LPT + g) * 16 + (slot >> 1)] = pair;
-    }
-    wave_sync();
-
-    // ---- p . v
-    if (rescale) {
+      const float ssc = lo_f16(cur.ks) * P.cs;
+      const float zsc = hi_f16(cur.ks) * P.cs;
+      const bool live = (tok < n) && !((cur.bits >> ((r0_bit + tok) & 31)) & 1u);
+      float lg[HB];
+      bool exceed = false;
 #pragma unroll
       for (int hh = 0; hh < HB; ++hh) {
-        st.acc_e[hh] *= alpha[hh];
-        st.acc_o[hh] *= alpha[hh];
+        const float v = token_sum<LPT>(fmaf(ssc, part[hh], zsc * qsum[hh]));
+        lg[hh] = live ? v : kNegInf;
+        exceed |= lg[hh] > st.m[hh];
       }
-    }
-    const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+      if (__ballot(exceed)) raise_max<HB, LPT>(lg, st, zl);
+
+      // V scale and the zero point of the centred codes, z + 8 s; zero for
+      // masked tokens (their planes may hold anything, NaN included)
+      const float sv = live ? lo_f16(cur.vs) : 0.f;
+      const float zv = live ? fmaf(8.f, lo_f16(cur.vs), hi_f16(cur.vs)) : 0.f;
+      _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
 #pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16 + 8 * sub]);
-      const uint4 pa = src[0], pb = src[1];
-      const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      for (int hh = 0; hh < HB; ++hh) {
+        const float mu = (st.m[hh] == kNegInf) ? 0.f : st.m[hh];
+        const float p = fast_exp2(lg[hh] - mu);
+        st.l[hh] += p;
+        zl[hh] = fmaf(p, zv, zl[hh]);
+        psh[(hh * LPT + g) * 32 + slot] = static_cast<_Float16>(p * sv);
+      }
+      wave_sync();
+
+      // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
+      const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
+      uint32_t e[8], o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t x = __builtin_amdgcn_perm(0u, vw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
         // (1024 + c) - 1032 = c - 8 and (1024 + 16 c) - 1152 = 16 (c - 8), exact in fp16
-        const uint32_t e = centre_f16x2((x & 0x000F000Fu) | 0x64006400u, 0xE408E408u);
-        const uint32_t o = centre_f16x2((x & 0x00F000F0u) | 0x64006400u, 0xE480E480u);
-        st.acc_e[hh] = dot2_f16(pr[i], e, st.acc_e[hh]);
-        st.acc_o[hh] = dot2_f16(pr[i], o, st.acc_o[hh]);
+        e[i] = centre_f16x2(and_or(x, 0x000F000Fu, vmagic), 0xE408E408u);
+        o[i] = centre_f16x2(and_or(x, 0x00F000F0u, vmagic), 0xE480E480u);
       }
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16 + 8 * sub]);
+        const uint4 pa = src[0], pb = src[1];
+        const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
+          st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
+        }
+      }
+      wave_sync();
+      if (c + NPF * kWaves < nsteps) issue(c + NPF * kWaves, ring[jr]);
     }
-    wave_sync();
   }
 
-  // ---- per-(head, group) zero-point sums, then fold them into the accumulators
+  // ---- per-(head, group) zero-point sums, folded into the accumulators
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const float z = xor_sum<LPT>(zl[hh]);
@@ -356,20 +461,27 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
 }
 
 // ---------------------------------------------------------------- 16-bit pass
-template <int D, int HT>
-__device__ __forceinline__ int64_t fp_row_index(const DecodeParams &P, int64_t head, int64_t rr,
-                                                const void **kb, const void **vb) {
-  // returns the row index inside *kb / *vb
-  if (rr < P.k) {
-    *kb = P.vl_k;
-    *vb = P.vl_v;
-    return head * P.k + rr;
-  }
-  *kb = P.win_k;
-  *vb = P.win_v;
-  int64_t wi = (P.win_offset + (rr - P.k)) % P.W;
-  return head * P.W + wi;
+// Element offset of row rr of the 16-bit list (VL rows first, then the window
+// in position order), clamped to the last valid row; rows past r1 are masked
+// by the caller.
+template <int D>
+__device__ __forceinline__ int64_t fp_row(const DecodeParams &P, int64_t head, int64_t rr,
+                                          int64_t r1, bool *in_vl) {
+  rr = rr < r1 ? rr : r1 - 1;
+  *in_vl = rr < P.k;
+  if (rr < P.k) return (head * P.k + rr) * D;
+  int wi = P.win_offset + static_cast<int>(rr - P.k);     // < 2 W
+  wi -= (wi >= P.W) ? P.W : 0;
+  return (head * P.W + wi) * D;
 }
+
+template <int HT>
+struct FpLoads {
+  static constexpr int KW = (HT == HQ_F32) ? 32 : 16;   // dwords of 32 K channels
+  static constexpr int VW = (HT == HQ_F32) ? 2 : 1;     // dwords of one V channel pair
+  uint32_t k[KW];
+  uint32_t v[16 * VW];
+};
 
 template <int D, int HB, int HT>
 __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int i0, int64_t r0,
@@ -377,6 +489,8 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
   constexpr int LPT = D / 32;
   constexpr int SLOTS = 64 / LPT;
   constexpr int CP = D / 2;
+  constexpr int EB = (HT == HQ_F32) ? 4 : 2;
+  using L = FpLoads<HT>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int slot = lane / LPT;
@@ -384,6 +498,10 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
   const int cp = lane % CP;
   const int sub = lane / CP;
   const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
+  const uint8_t *vlk = static_cast<const uint8_t *>(P.vl_k);
+  const uint8_t *vlv = static_cast<const uint8_t *>(P.vl_v);
+  const uint8_t *wk = static_cast<const uint8_t *>(P.win_k);
+  const uint8_t *wv = static_cast<const uint8_t *>(P.win_v);
 
   // natural query pairs (q[2i], q[2i+1]) or fp32 values for this lane's group
   uint32_t qn[HB][16];
@@ -392,113 +510,112 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
   for (int hh = 0; hh < HB; ++hh) {
     const int64_t qoff = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * D + g * 32;
     if constexpr (HT == HQ_F32) {
+      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(P.q) + qoff);
 #pragma unroll
-      for (int c = 0; c < 32; ++c) qf[hh][c] = load_as_f32<HQ_F32>(P.q, qoff + c);
+      for (int i = 0; i < 8; ++i) {
+        const float4 f = p[i];
+        qf[hh][4 * i] = f.x; qf[hh][4 * i + 1] = f.y; qf[hh][4 * i + 2] = f.z; qf[hh][4 * i + 3] = f.w;
+      }
     } else {
-      const uint32_t *qq = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(P.q) + qoff);
-#pragma unroll
-      for (int c = 0; c < 16; ++c) qn[hh][c] = qq[c];
+      load_q32<HT>(P.q, qoff, qn[hh]);
     }
   }
+  float zl[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) zl[hh] = 0.f;
+
+  // every load of one wave step, issued together (addresses clamped to valid rows)
+  auto issue = [&](int64_t c, L &ld) {
+    const int64_t f0 = r0 + c * SLOTS;
+    bool in_vl;
+    const int64_t ko = fp_row<D>(P, head, f0 + slot, r1, &in_vl) + g * 32;
+    const uint4 *kp = reinterpret_cast<const uint4 *>((in_vl ? vlk : wk) + ko * EB);
+#pragma unroll
+    for (int i = 0; i < L::KW / 4; ++i) {
+      const uint4 u = kp[i];
+      ld.k[4 * i] = u.x; ld.k[4 * i + 1] = u.y; ld.k[4 * i + 2] = u.z; ld.k[4 * i + 3] = u.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      bool vin;
+      const int64_t vo = fp_row<D>(P, head, f0 + 16 * sub + r, r1, &vin) + 2 * cp;
+      const uint8_t *vb = (vin ? vlv : wv) + vo * EB;
+      if constexpr (HT == HQ_F32) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(vb);
+        ld.v[2 * r] = u.x;
+        ld.v[2 * r + 1] = u.y;
+      } else {
+        ld.v[r] = *reinterpret_cast<const uint32_t *>(vb);
+      }
+    }
+  };
 
   const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
+  L cur, nxt;
+  if (wave < nsteps) issue(wave, cur);
   for (int64_t c = wave; c < nsteps; c += kWaves) {
+    if (c + kWaves < nsteps) issue(c + kWaves, nxt);
     const int64_t f0 = r0 + c * SLOTS;
-    const int64_t rr = f0 + slot;
-    const bool tv = rr < r1;
+    const bool tv = f0 + slot < r1;
     float part[HB];
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
-    if (tv) {
-      const void *kb;
-      const void *vb;
-      const int64_t row = fp_row_index<D, HT>(P, head, rr, &kb, &vb);
-      if constexpr (HT == HQ_F32) {
-        const float4 *kp = reinterpret_cast<const float4 *>(static_cast<const float *>(kb) + row * D + g * 32);
+    if constexpr (HT == HQ_F32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float4 kv = kp[j];
+      for (int e = 0; e < 32; ++e) {
+        const float kv = __uint_as_float(cur.k[e]);
 #pragma unroll
-          for (int hh = 0; hh < HB; ++hh) {
-            part[hh] = fmaf(qf[hh][4 * j + 0], kv.x, part[hh]);
-            part[hh] = fmaf(qf[hh][4 * j + 1], kv.y, part[hh]);
-            part[hh] = fmaf(qf[hh][4 * j + 2], kv.z, part[hh]);
-            part[hh] = fmaf(qf[hh][4 * j + 3], kv.w, part[hh]);
-          }
-        }
-      } else {
-        const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(kb) + row * D + g * 32);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 kv = kp[j];
-          const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int hh = 0; hh < HB; ++hh) part[hh] = dot2_q<HT>(qn[hh][4 * j + e], kw[e], part[hh]);
-        }
+        for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(qf[hh][e], kv, part[hh]);
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) part[hh] = dot2_q<HT>(qn[hh][e], cur.k[e], part[hh]);
     }
-#pragma unroll
-    for (int m = 1; m < LPT; m <<= 1)
-#pragma unroll
-      for (int hh = 0; hh < HB; ++hh) part[hh] += shfl_xor_f(part[hh], m);
-
-    float alpha[HB];
-    bool rescale = false;
+    float lg[HB];
+    bool exceed = false;
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
-      const float lg = tv ? part[hh] * P.cs : kNegInf;
-      const float mx = xor_max<LPT>(lg);
-      const float mn = fmaxf(st.m[hh], mx);
-      const float mu = (mn == kNegInf) ? 0.f : mn;
-      alpha[hh] = fast_exp2(st.m[hh] - mu);
-      rescale |= (mn != st.m[hh]);
-      st.m[hh] = mn;
-      const float p = fast_exp2(lg - mu);
-      st.l[hh] = st.l[hh] * alpha[hh] + p;
+      const float v = token_sum<LPT>(part[hh]) * P.cs;
+      lg[hh] = tv ? v : kNegInf;
+      exceed |= lg[hh] > st.m[hh];
+    }
+    if (__ballot(exceed)) raise_max<HB, LPT>(lg, st, zl);
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const float mu = (st.m[hh] == kNegInf) ? 0.f : st.m[hh];
+      const float p = fast_exp2(lg[hh] - mu);
+      st.l[hh] += p;
       if (g == 0) sm.p[wave][hh * 32 + slot] = p;
     }
     wave_sync();
-    if (rescale) {
+    // lanes: channel pair cp over the 16 rows of sub-tile `sub` (p = 0 past r1)
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        st.acc_e[hh] *= alpha[hh];
-        st.acc_o[hh] *= alpha[hh];
+    for (int hh = 0; hh < HB; ++hh) {
+      const float4 *pp = reinterpret_cast<const float4 *>(&sm.p[wave][hh * 32 + 16 * sub]);
+      float pr[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = pp[i];
+        pr[4 * i] = f.x; pr[4 * i + 1] = f.y; pr[4 * i + 2] = f.z; pr[4 * i + 3] = f.w;
       }
-    }
-    // lanes: channel pair cp over the 16 rows of sub-tile `sub`
-#pragma unroll 4
-    for (int r = 0; r < 16; ++r) {
-      const int64_t rrow = f0 + 16 * sub + r;
-      if (rrow < r1) {
-        const void *kb;
-        const void *vb;
-        const int64_t row = fp_row_index<D, HT>(P, head, rrow, &kb, &vb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
         float v0, v1;
         if constexpr (HT == HQ_F32) {
-          const float2 vv = reinterpret_cast<const float2 *>(static_cast<const float *>(vb) + row * D)[cp];
-          v0 = vv.x;
-          v1 = vv.y;
+          v0 = __uint_as_float(cur.v[2 * r]);
+          v1 = __uint_as_float(cur.v[2 * r + 1]);
         } else {
-          const uint32_t vv = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(vb) + row * D)[cp];
-          if constexpr (HT == HQ_BF16) {
-            v0 = bf16_to_f32(vv & 0xFFFFu);
-            v1 = bf16_to_f32(vv >> 16);
-          } else {
-            v0 = lo_f16(vv);
-            v1 = hi_f16(vv);
-          }
+          v0 = half_bits_to_f32<HT>(cur.v[r] & 0xFFFFu);
+          v1 = half_bits_to_f32<HT>(cur.v[r] >> 16);
         }
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-          const float p = sm.p[wave][hh * 32 + 16 * sub + r];
-          st.acc_e[hh] = fmaf(p, v0, st.acc_e[hh]);
-          st.acc_o[hh] = fmaf(p, v1, st.acc_o[hh]);
-        }
+        st.acc_e[hh] = fmaf(pr[r], v0, st.acc_e[hh]);
+        st.acc_o[hh] = fmaf(pr[r], v1, st.acc_o[hh]);
       }
     }
     wave_sync();
+    cur = nxt;
   }
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
@@ -584,36 +701,60 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     if (d == 0) P.part_ml[pidx] = make_float2(mb, l);
   }
 
-  // ---- last block of the unit merges all splits
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&P.tickets[unit], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (prev == static_cast<uint32_t>(P.S - 1));
-    if (last) __hip_atomic_store(&P.tickets[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = last;
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
-  for (int e = threadIdx.x; e < HB * D; e += kThreads) {
-    const int hh = e / D;
-    const int d = e % D;
-    const int64_t base = (static_cast<int64_t>(b) * P.Hq + i0 + hh) * P.S;
-    float mstar = kNegInf;
-    for (int s = 0; s < P.S; ++s) mstar = fmaxf(mstar, P.part_ml[base + s].x);
-    const float mu = (mstar == kNegInf) ? 0.f : mstar;
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < P.S; ++s) {
-      const float2 ml = P.part_ml[base + s];
-      const float f = fast_exp2(ml.x - mu);
-      L = fmaf(f, ml.y, L);
-      O = fmaf(f, P.part_o[(base + s) * D + d], O);
+}
+
+// ---------------------------------------------------------------- split merge
+// One block per (unit, query head): out = sum_s 2^(m_s - m*) o_s / L with
+// L = sum_s 2^(m_s - m*) l_s, in split order; lse = (m* + log2 L) ln 2.
+// A kernel of its own: the launch boundary makes every split's partial
+// visible without device-scope fences inside the split kernel. Partials are
+// staged through LDS 64 splits at a time, so each stage costs one memory
+// round trip.
+constexpr int kMergeStage = 64;
+template <int D, int HB>
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
+  __shared__ float4 so[kMergeStage * D / 4];
+  __shared__ float2 sml[kMergeStage];
+  const int unit = blockIdx.x / HB;
+  const int hh = blockIdx.x % HB;
+  const int hc = unit % P.nhc;
+  const int bh = unit / P.nhc;
+  const int h = bh % P.Hkv;
+  const int b = bh / P.Hkv;
+  const int64_t qi = static_cast<int64_t>(b) * P.Hq + h * P.G + hc * HB + hh;
+  const int S = P.S;
+  const float4 *po = reinterpret_cast<const float4 *>(P.part_o) + qi * S * (D / 4);
+  const float2 *pml = P.part_ml + qi * S;
+  float m_run = kNegInf, L = 0.f, o = 0.f;
+  const int d = threadIdx.x;
+  for (int s0 = 0; s0 < S; s0 += kMergeStage) {
+    const int ns = (S - s0) < kMergeStage ? (S - s0) : kMergeStage;
+    __syncthreads();
+    for (int e = threadIdx.x; e < ns * (D / 4); e += kThreads) so[e] = po[s0 * (D / 4) + e];
+    if (threadIdx.x < ns) sml[threadIdx.x] = pml[s0 + threadIdx.x];
+    __syncthreads();
+    if (d < D) {
+      float mx = m_run;
+      for (int s = 0; s < ns; ++s) mx = fmaxf(mx, sml[s].x);
+      const float mu = (mx == kNegInf) ? 0.f : mx;
+      const float a = fast_exp2(m_run - mu);
+      L *= a;
+      o *= a;
+      const float *sf = reinterpret_cast<const float *>(so);
+      for (int s = 0; s < ns; ++s) {
+        const float wgt = fast_exp2(sml[s].x - mu);
+        L = fmaf(wgt, sml[s].y, L);
+        o = fmaf(wgt, sf[s * D + d], o);
+      }
+      m_run = mx;
     }
-    const int64_t oi = (static_cast<int64_t>(b) * P.Hq + i0 + hh);
-    P.out[oi * D + d] = O / L;
-    if (d == 0 && P.lse) P.lse[oi] = (mu + log2f(L)) * kLn2;
+  }
+  if (d < D) {
+    P.out[qi * D + d] = o / L;
+    if (d == 0 && P.lse) {
+      const float mu = (m_run == kNegInf) ? 0.f : m_run;
+      P.lse[qi] = (mu + log2f(L)) * kLn2;
+    }
   }
 }
 
@@ -666,12 +807,12 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
   const double bytes_fp = static_cast<double>(nfp) * 2.0 * kv->D * hp_bytes;
   int S = n_splits;
   if (S <= 0) {
-    const int target_blocks = 1024;
+    const int target_blocks = 512;
     S = static_cast<int>(ceil_div(target_blocks, pl.units));
     // at least ~4 wave steps of work per wave
     const int64_t max_s = ceil_div(pl.nq + nfp, 16LL * step) ;
     if (S > max_s) S = static_cast<int>(max_s > 0 ? max_s : 1);
-    if (S > 256) S = 256;
+    if (S > kMaxSplits) S = kMaxSplits;
     if (S < 1) S = 1;
   }
   int s_fp = 0;
@@ -703,12 +844,11 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t tickets, ml, o, total;
+  size_t ml, o, total;
 };
 WsLayout ws_layout(const hq_hybrid_kv *kv, int Hq, const Plan &pl) {
   WsLayout L{};
-  L.tickets = 0;
-  L.ml = align_up(static_cast<size_t>(pl.units) * 4, 4096);
+  L.ml = 0;
   L.o = L.ml + align_up(static_cast<size_t>(kv->B) * Hq * pl.S * sizeof(float2), 256);
   L.total = L.o + static_cast<size_t>(kv->B) * Hq * pl.S * kv->D * sizeof(float);
   return L;
@@ -753,6 +893,7 @@ void launch_hb(int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
     case HQ_BF16: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_BF16>), grid, dim3(kThreads), 0, st, P); break;
     default: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_F16>), grid, dim3(kThreads), 0, st, P); break;
   }
+  hipLaunchKernelGGL((merge_kernel<D, HB>), dim3(P.units * HB), dim3(kThreads), 0, st, P);
 }
 template <int D>
 void launch_d(int HB, int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
@@ -787,6 +928,8 @@ extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, con
   if (s != HQ_OK) return s;
   if (n_splits < 0) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: n_splits < 0");
   const Plan pl = make_plan(kv, Hq, n_splits);
+  if (pl.S > kMaxSplits)
+    return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn: %d splits exceed the maximum %d", pl.S, kMaxSplits);
   const WsLayout L = ws_layout(kv, Hq, pl);
   if (!ws || ws_bytes < L.total)
     return fail(HQ_ERR_WORKSPACE, "hq_decode_attn: workspace needs %zu bytes, got %zu", L.total, ws_bytes);
@@ -805,7 +948,6 @@ extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, con
   P.out = out;
   P.lse = lse;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  P.tickets = reinterpret_cast<uint32_t *>(w8 + L.tickets);
   P.part_ml = reinterpret_cast<float2 *>(w8 + L.ml);
   P.part_o = reinterpret_cast<float *>(w8 + L.o);
   P.t_cap = kv->t_cap;

@@ -13,11 +13,11 @@
 // Kernels:
 //  * acc_kernel      copies this step's queries into the ring slot.
 //  * mfma_colsum     (HQ_DETECT_MATMUL) bf16/fp16 MFMA 32x32x16: each wave
-//    owns a 32-token column tile with its K fragments in registers and runs
-//    over all rows of the unit in 32-row chunks, accumulating every chunk
-//    into the same accumulator (so rows congruent mod 32 are summed by the
-//    matrix core itself); the 32 row sums of a column are then converted to
-//    int64 units of 2^-16 and added exactly.
+//    owns two 32-token column tiles with their K fragments in registers and
+//    runs over all rows of the unit (staged through LDS) in 32-row chunks,
+//    accumulating every chunk into the same accumulator (so rows congruent
+//    mod 32 are summed by the matrix core itself); the 32 row sums of a
+//    column are then converted to int64 units of 2^-16 and added exactly.
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
@@ -29,8 +29,6 @@
 
 namespace hq {
 namespace {
-
-constexpr int64_t kUnitsScale = 65536;   // scores in units of 2^-16
 
 // ---------------------------------------------------------------- accumulate
 __global__ __launch_bounds__(256) void acc_kernel(const uint8_t *__restrict__ q_new,
@@ -61,59 +59,106 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
   }
 }
 
-// Grid: units * ceil(cand_end / 128) blocks of 4 waves; wave w of a block owns
-// the 32-token column tile 4 * blockIdx_local + w.
+// Grid: units * ceil(tiles / 8) blocks of 4 waves; wave w of block cb owns the
+// 32-token column tiles 8 cb + 2 w and 8 cb + 2 w + 1 with their K fragments
+// in registers. The unit's query rows are staged through LDS 128 rows at a
+// time (double buffered; rows padded by 16 bytes so the 32 lanes reading 32
+// consecutive rows hit different banks) and every A fragment feeds the MFMAs
+// of both tiles.
+constexpr int kStageRows = 128;
+constexpr int kRowPad = 8;        // halves
 template <int D, int DT>
 __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__restrict__ q_acc,
                                                           const uint16_t *__restrict__ k, int Hq,
                                                           int Hkv, int R, int64_t k_rows,
                                                           int64_t cand_end, int tiles_per_unit,
                                                           int64_t *__restrict__ scores) {
-  constexpr int KC = D / 16;           // k-chunks of 16
+  constexpr int KC = D / 16;                       // k-chunks of 16
+  constexpr int ROWV = D / 8;                      // uint4 per row
+  constexpr int PER_T = kStageRows * ROWV / 256;   // uint4 per thread per stage
+  __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int blocks_per_unit = (tiles_per_unit + 3) / 4;
-  const int unit = blockIdx.x / blocks_per_unit;             // b * Hkv + h
-  const int tile = (blockIdx.x % blocks_per_unit) * 4 + wave;
-  if (tile >= tiles_per_unit) return;
+  const int blocks_per_unit = (tiles_per_unit + 7) / 8;
+  const int unit = blockIdx.x / blocks_per_unit;              // b * Hkv + h
+  const int cb = blockIdx.x % blocks_per_unit;
   const int G = Hq / Hkv;
   const int b = unit / Hkv;
   const int h = unit % Hkv;
   const int M = G * R;                                        // rows of this unit
   const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
-  const int64_t col = static_cast<int64_t>(tile) * 32 + (lane & 31);
   const int half = lane >> 5;
 
-  uint4 bfrag[KC];
-  const bool col_ok = col < cand_end;
-  const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok ? col : 0)) * D;
+  uint4 bfrag[2][KC];
+  int64_t col[2];
+  bool col_ok[2];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    bfrag[kc] = col_ok ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
-
-  f32x16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const int chunks = (M + 31) / 32;
-  for (int rc = 0; rc < chunks; ++rc) {
-    const int row = rc * 32 + (lane & 31);
-    const bool row_ok = row < M;
-    const uint16_t *qr = qrows + static_cast<int64_t>(row_ok ? row : 0) * D;
-    uint4 afrag[KC];
+  for (int t = 0; t < 2; ++t) {
+    const int tile = cb * 8 + wave * 2 + t;
+    col[t] = static_cast<int64_t>(tile) * 32 + (lane & 31);
+    col_ok[t] = col[t] < cand_end;
+    const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      afrag[kc] = row_ok ? *reinterpret_cast<const uint4 *>(qr + kc * 16 + half * 8)
-                         : make_uint4(0u, 0u, 0u, 0u);
+      bfrag[t][kc] = col_ok[t] ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  uint4 buf[PER_T];
+  auto load_stage = [&](int st) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) acc = mfma32<DT>(afrag[kc], bfrag[kc], acc);
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      const int grow = st * kStageRows + row;
+      buf[e] = grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_stage = [&](int slot) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      *reinterpret_cast<uint4 *>(&qs[slot][row][c8 * 8]) = buf[e];
+    }
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+
+  const int stages = (M + kStageRows - 1) / kStageRows;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < stages; ++st) {
+    if (st + 1 < stages) load_stage(st + 1);
+    const int slot = st & 1;
+#pragma unroll
+    for (int sub = 0; sub < kStageRows / 32; ++sub) {
+      const uint16_t *arow = &qs[slot][sub * 32 + (lane & 31)][half * 8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * 16);
+        acc[0] = mfma32<DT>(a, bfrag[0][kc], acc[0]);
+        acc[1] = mfma32<DT>(a, bfrag[1][kc], acc[1]);
+      }
+    }
+    if (st + 1 < stages) store_stage((st + 1) & 1);
+    __syncthreads();
   }
   // column = lane & 31; this lane holds 16 of the 32 row residues
-  long long s = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s += __double2ll_rn(static_cast<double>(acc[i]) * 65536.0);
-  const long long other = __shfl_xor(s, 32, 64);
-  if (half == 0 && col_ok) scores[static_cast<int64_t>(unit) * cand_end + col] = s + other;
+  for (int t = 0; t < 2; ++t) {
+    long long s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += __double2ll_rn(static_cast<double>(acc[t][i]) * 65536.0);
+    const long long other = __shfl_xor(s, 32, 64);
+    if (half == 0 && col_ok[t]) scores[static_cast<int64_t>(unit) * cand_end + col[t]] = s + other;
+  }
 }
 
 // ---------------------------------------------------------------- QSUM form
@@ -198,36 +243,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, c
 
 // ---------------------------------------------------------------- top-k
 constexpr int kTopkThreads = 1024;
+constexpr int kLdsKeys = 36864;          // keys kept in LDS up to this many candidates
 
-__device__ __forceinline__ unsigned long long block_reduce_min_max(long long v_min, long long v_max,
-                                                                   long long *sh, long long *out_min,
-                                                                   long long *out_max) {
-  // sh: 2 * 32 entries
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const long long a = __shfl_xor(v_min, m, 64);
-    const long long c = __shfl_xor(v_max, m, 64);
-    v_min = a < v_min ? a : v_min;
-    v_max = c > v_max ? c : v_max;
-  }
-  if (lane == 0) { sh[w] = v_min; sh[32 + w] = v_max; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    long long mn = sh[0], mx = sh[32];
-    for (int i = 1; i < kTopkThreads / 64; ++i) {
-      mn = sh[i] < mn ? sh[i] : mn;
-      mx = sh[32 + i] > mx ? sh[32 + i] : mx;
-    }
-    *out_min = mn;
-    *out_max = mx;
-  }
-  __syncthreads();
-  return 0;
+// Order-preserving 32-bit key of an int64 score: the bits of float(score)
+// (round to nearest is monotone non-decreasing) mapped so that unsigned order
+// equals float order.
+__device__ __forceinline__ uint32_t ordered_key(long long s) {
+  const uint32_t u = __float_as_uint(static_cast<float>(s));
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// exclusive scan of one int per thread over the block; returns the prefix
-// and writes the total to *total
+// exclusive scan of one int per thread over the block; *total gets the sum
 __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int inc = v;
@@ -254,118 +280,191 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) 
   return pre;
 }
 
-// Radix select over the 32-bit keys of the selected elements: finds the key
-// value kappa of the k_rem-th largest and how many with key == kappa to take.
-// key_of(j) returns (valid, key).
-template <typename KeyFn>
-__device__ void radix_select32(int64_t n, int k_rem, KeyFn key_of, unsigned *hist, int *sh_i,
-                               unsigned *kappa_out, int *take_out) {
-  unsigned prefix = 0, pmask = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
-    for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-      unsigned key;
-      if (key_of(j, &key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0, d = 255;
-      for (; d > 0; --d) {
-        if (cum + static_cast<int>(hist[d]) >= k_rem) break;
-        cum += hist[d];
-      }
-      sh_i[0] = d;
-      sh_i[1] = k_rem - cum;
-    }
-    __syncthreads();
-    prefix |= static_cast<unsigned>(sh_i[0]) << shift;
-    pmask |= 255u << shift;
-    k_rem = sh_i[1];
-    __syncthreads();
+struct TopkShared {
+  uint32_t hist[2048];
+  int scan[kTopkThreads / 64 + 2];
+  int sel[4];
+  unsigned long long mm[2 * kTopkThreads / 64];
+};
+
+// One radix pass: among elements with (key & pmask) == prefix, histogram the
+// digit (key >> shift) & (2^bits - 1) and find the digit holding the k_rem-th
+// largest. Returns the digit; *k_rem becomes the rank inside that digit.
+template <typename KeyAt>
+__device__ int radix_pass(int64_t n, KeyAt key_at, uint32_t prefix, uint32_t pmask, int shift,
+                          int bits, int *k_rem, int *eq_count, TopkShared &sh) {
+  const int nb = 1 << bits;
+  for (int i = threadIdx.x; i < 2048; i += kTopkThreads) sh.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll 4
+  for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
+    const uint32_t key = key_at(j);
+    if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
   }
-  *kappa_out = prefix;
-  *take_out = k_rem;
+  __syncthreads();
+  // bins in descending digit order: thread t holds digits nb-1-2t, nb-2-2t
+  const int dhi = nb - 1 - 2 * static_cast<int>(threadIdx.x);
+  const int dlo = dhi - 1;
+  const int chi = dhi >= 0 ? static_cast<int>(sh.hist[dhi]) : 0;
+  const int clo = dlo >= 0 ? static_cast<int>(sh.hist[dlo]) : 0;
+  int tot;
+  const int above = block_exclusive_scan(chi + clo, sh.scan, &tot);
+  const int kr = *k_rem;
+  if (dhi >= 0 && above < kr && kr <= above + chi) {
+    sh.sel[0] = dhi; sh.sel[1] = kr - above; sh.sel[2] = chi;
+  } else if (dlo >= 0 && above + chi < kr && kr <= above + chi + clo) {
+    sh.sel[0] = dlo; sh.sel[1] = kr - above - chi; sh.sel[2] = clo;
+  }
+  __syncthreads();
+  const int d = sh.sel[0];
+  *k_rem = sh.sel[1];
+  *eq_count = sh.sel[2];
+  __syncthreads();
+  return d;
 }
 
+template <bool IN_LDS>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__restrict__ scores,
-                                                            int64_t n, int k_top,
-                                                            int32_t *__restrict__ idx_out) {
-  __shared__ unsigned hist[256];
-  __shared__ long long shl[64];
-  __shared__ int shi[kTopkThreads / 64 + 2];
-  __shared__ long long s_min, s_max;
-  __shared__ unsigned s_kappa;
-  __shared__ int s_take;
+                                                            uint32_t *__restrict__ gkeys, int64_t n,
+                                                            int k_top, int32_t *__restrict__ idx_out) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t lkeys[IN_LDS ? kLdsKeys : 1];
   const int unit = blockIdx.x;
   const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
+  uint32_t *gk = gkeys + static_cast<int64_t>(unit) * n;
   int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
   if (k_top == 0) return;
 
-  // 1. min / max of the scores
-  long long mn = 0x7FFFFFFFFFFFFFFFLL, mx = -0x7FFFFFFFFFFFFFFFLL - 1;
+  // keys (one pass over the scores)
+#pragma unroll 4
   for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-    const long long v = sc[j];
-    mn = v < mn ? v : mn;
-    mx = v > mx ? v : mx;
+    const uint32_t key = ordered_key(sc[j]);
+    if constexpr (IN_LDS) lkeys[j] = key; else gk[j] = key;
   }
-  block_reduce_min_max(mn, mx, shl, &s_min, &s_max);
-  const long long smin = s_min;
-  const unsigned long long range = static_cast<unsigned long long>(s_max) - static_cast<unsigned long long>(smin);
-  const int bits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
-  const int shift = bits > 32 ? bits - 32 : 0;
-
-  // 2. radix select on key = (score - min) >> shift
-  auto key32 = [&](int64_t j, unsigned *key) -> bool {
-    *key = static_cast<unsigned>((static_cast<unsigned long long>(sc[j]) - static_cast<unsigned long long>(smin)) >> shift);
-    return true;
+  __syncthreads();
+  auto key_at = [&](int64_t j) -> uint32_t {
+    if constexpr (IN_LDS) return lkeys[j]; else return gk[j];
   };
-  radix_select32(n, k_top, key32, hist, shi, &s_kappa, &s_take);
-  const unsigned kappa = s_kappa;
-  int take = s_take;
 
-  // 3. refine the boundary bucket on the low `shift` bits of the score
-  unsigned long long tau = (static_cast<unsigned long long>(kappa) << shift);   // score - min
-  if (shift > 0) {
-    auto key_lo = [&](int64_t j, unsigned *key) -> bool {
-      const unsigned long long v = static_cast<unsigned long long>(sc[j]) - static_cast<unsigned long long>(smin);
-      *key = static_cast<unsigned>(v & ((1ull << shift) - 1ull));
-      return static_cast<unsigned>(v >> shift) == kappa;
-    };
-    radix_select32(n, take, key_lo, hist, shi, &s_kappa, &s_take);
-    tau |= s_kappa;
-    take = s_take;
+  // radix select on the 32-bit keys: 11 + 11 + 10 bits
+  int k_rem = k_top, eq = 0;
+  uint32_t prefix = 0, pmask = 0;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int p = 0; p < 3; ++p) {
+    const int d = radix_pass(n, key_at, prefix, pmask, shifts[p], widths[p], &k_rem, &eq, sh);
+    prefix |= static_cast<uint32_t>(d) << shifts[p];
+    pmask |= ((1u << widths[p]) - 1u) << shifts[p];
   }
-  const long long tau_s = static_cast<long long>(tau + static_cast<unsigned long long>(smin));
+  const uint32_t kappa = prefix;       // key of the k_top-th largest
+  int take = k_rem;                    // how many with key == kappa are taken
 
-  // 4. among scores == tau_s take the `take` lowest positions; then compact
+  // refine the kappa bucket on the exact int64 score (its members differ only
+  // in the bits float32 drops): radix over (score - min) of the bucket
+  long long tau = 0;
+  bool refine = eq > take;
+  if (refine) {
+    unsigned long long mn = ~0ull, mx = 0;
+#pragma unroll 4
+    for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
+      if (key_at(j) == kappa) {
+        const unsigned long long v = static_cast<unsigned long long>(sc[j]) ^ 0x8000000000000000ull;
+        mn = v < mn ? v : mn;
+        mx = v > mx ? v : mx;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sh.mm[w] = mn; sh.mm[kTopkThreads / 64 + w] = mx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int i = 1; i < kTopkThreads / 64; ++i) {
+        mn = sh.mm[i] < mn ? sh.mm[i] : mn;
+        mx = sh.mm[kTopkThreads / 64 + i] > mx ? sh.mm[kTopkThreads / 64 + i] : mx;
+      }
+      sh.mm[0] = mn; sh.mm[1] = mx;
+    }
+    __syncthreads();
+    const unsigned long long base = sh.mm[0];
+    const unsigned long long range = sh.mm[1] - base;
+    __syncthreads();
+    const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
+    unsigned long long lowpre = 0;
+    unsigned long long lowmask = 0;
+    for (int top = nbits; top > 0; top -= 11) {
+      const int bits = top >= 11 ? 11 : top;
+      const int shift = top - bits;
+      // histogram of this digit among the bucket members matching the higher digits
+      for (int i = threadIdx.x; i < 2048; i += kTopkThreads) sh.hist[i] = 0u;
+      __syncthreads();
+#pragma unroll 4
+      for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
+        if (key_at(j) == kappa) {
+          const unsigned long long v = (static_cast<unsigned long long>(sc[j]) ^ 0x8000000000000000ull) - base;
+          if ((v & lowmask) == lowpre) atomicAdd(&sh.hist[(v >> shift) & ((1u << bits) - 1u)], 1u);
+        }
+      }
+      __syncthreads();
+      const int nb = 1 << bits;
+      const int dhi = nb - 1 - 2 * static_cast<int>(threadIdx.x);
+      const int dlo = dhi - 1;
+      const int chi = dhi >= 0 ? static_cast<int>(sh.hist[dhi]) : 0;
+      const int clo = dlo >= 0 ? static_cast<int>(sh.hist[dlo]) : 0;
+      int tot;
+      const int above = block_exclusive_scan(chi + clo, sh.scan, &tot);
+      if (dhi >= 0 && above < take && take <= above + chi) {
+        sh.sel[0] = dhi; sh.sel[1] = take - above;
+      } else if (dlo >= 0 && above + chi < take && take <= above + chi + clo) {
+        sh.sel[0] = dlo; sh.sel[1] = take - above - chi;
+      }
+      __syncthreads();
+      lowpre |= static_cast<unsigned long long>(sh.sel[0]) << shift;
+      lowmask |= static_cast<unsigned long long>((1u << bits) - 1u) << shift;
+      take = sh.sel[1];
+      __syncthreads();
+    }
+    tau = static_cast<long long>((base + lowpre) ^ 0x8000000000000000ull);
+  }
+
+  // selected(j): key > kappa, or key == kappa and (not refining: one of the
+  // first `take` bucket members by position; refining: score > tau, or
+  // score == tau and one of the first `take` such members by position)
   const int64_t per = (n + kTopkThreads - 1) / kTopkThreads;
   const int64_t j0 = threadIdx.x * per;
   const int64_t j1 = (j0 + per) < n ? (j0 + per) : n;
-  int eq = 0, gt = 0;
+  auto is_tie = [&](int64_t j, uint32_t key) -> bool {
+    return key == kappa && (!refine || sc[j] == tau);
+  };
+  auto is_sure = [&](int64_t j, uint32_t key) -> bool {
+    return key > kappa || (refine && key == kappa && sc[j] > tau);
+  };
+  int ties = 0, sure = 0;
   for (int64_t j = j0; j < j1; ++j) {
-    const long long v = sc[j];
-    eq += (v == tau_s);
-    gt += (v > tau_s);
+    const uint32_t key = key_at(j);
+    ties += is_tie(j, key);
+    sure += is_sure(j, key);
   }
   int tot;
-  int eq_before = block_exclusive_scan(eq, shi, &tot);
-  // selected in this segment: all gt, and eq ones whose global rank < take
-  int sel = gt;
+  const int tie_before = block_exclusive_scan(ties, sh.scan, &tot);
+  int sel = sure;
   {
-    int r = eq_before;
+    int r = tie_before;
     for (int64_t j = j0; j < j1; ++j)
-      if (sc[j] == tau_s) { sel += (r < take); ++r; }
+      if (is_tie(j, key_at(j))) { sel += (r < take); ++r; }
   }
-  int pos = block_exclusive_scan(sel, shi, &tot);
+  int pos = block_exclusive_scan(sel, sh.scan, &tot);
   {
-    int r = eq_before;
+    int r = tie_before;
     for (int64_t j = j0; j < j1; ++j) {
-      const long long v = sc[j];
-      bool s = v > tau_s;
-      if (v == tau_s) { s = r < take; ++r; }
-      if (s && pos < k_top) out[pos++] = static_cast<int32_t>(j);
+      const uint32_t key = key_at(j);
+      bool sj = is_sure(j, key);
+      if (is_tie(j, key)) { sj = r < take; ++r; }
+      if (sj && pos < k_top) out[pos++] = static_cast<int32_t>(j);
     }
   }
 }
@@ -373,13 +472,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__res
 // ---------------------------------------------------------------- workspace
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct DetWs {
-  size_t scores, qs, total;
+  size_t scores, qs, keys, total;
 };
 DetWs det_ws(int B, int Hkv, int64_t cand_end) {
   DetWs L{};
   L.scores = 0;
   L.qs = align_up(static_cast<size_t>(B) * Hkv * cand_end * sizeof(int64_t), 256);
-  L.total = L.qs + static_cast<size_t>(B) * Hkv * 128 * sizeof(double);
+  L.keys = align_up(L.qs + static_cast<size_t>(B) * Hkv * 128 * sizeof(double), 256);
+  L.total = L.keys + (cand_end > kLdsKeys ? static_cast<size_t>(B) * Hkv * cand_end * 4 : 0);
   return L;
 }
 
@@ -420,8 +520,8 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
   if (detect) {
     if (!k || (k_top > 0 && !idx_out)) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines: null k or idx_out");
     const DetWs L = det_ws(B, Hkv, cand_end);
-    const bool need_ws_scores = (score_out == nullptr);
-    const size_t need = need_ws_scores || method == HQ_DETECT_QSUM ? L.total : 0;
+    const bool need_ws = score_out == nullptr || method == HQ_DETECT_QSUM || cand_end > kLdsKeys;
+    const size_t need = need_ws ? L.total : 0;
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(HQ_ERR_WORKSPACE, "hq_detect_vlines: workspace needs %zu bytes, got %zu", need, ws_bytes);
     if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(q_acc) % 16)
@@ -445,7 +545,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
   if (cand_end > 0) {
     if (method == HQ_DETECT_MATMUL) {
       const int tiles = static_cast<int>((cand_end + 31) / 32);
-      const int blocks = units * ((tiles + 3) / 4);
+      const int blocks = units * ((tiles + 7) / 8);
       const uint16_t *qa = static_cast<const uint16_t *>(q_acc);
       const uint16_t *kk = static_cast<const uint16_t *>(k);
       if (D == 128) {
@@ -480,7 +580,11 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
     if (s != HQ_OK) return s;
   }
   if (k_top > 0) {
-    hipLaunchKernelGGL(topk_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, cand_end, k_top, idx_out);
+    uint32_t *gkeys = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + L.keys);
+    if (cand_end <= kLdsKeys)
+      hipLaunchKernelGGL((topk_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    else
+      hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
     hq_status s = check_launch("hq_detect_vlines (top-k)");
     if (s != HQ_OK) return s;
   }

@@ -196,12 +196,12 @@ size_t hq_detect_workspace_size(int B, int Hkv, int64_t cand_end, int k_top);
  *   lse[b][i] = log(sum_j exp(l_j)) (natural log, optional).
  * q [B][Hq][D] of q_dtype (HQ_BF16, HQ_F16 or HQ_F32). sm_scale == 0 means
  * 1/sqrt(D). The positions are split into n_splits ranges per (b, h)
- * (0 = automatic), each producing a partial softmax state that the last
- * finishing workgroup merges with the log-sum-exp rule in fixed order.
- * ws: at least hq_decode_workspace_size(kv, Hq, n_splits) bytes; its first
- * 4096 bytes (the merge tickets) must be zero before the first call with that
- * workspace, and every call leaves them zero. Calls that share a workspace
- * must not run concurrently. Requires Hq % Hkv == 0, G <= 16.
+ * (0 = automatic, at most 256), each producing a partial softmax state; a
+ * second kernel merges them with the log-sum-exp rule in split order.
+ * ws: at least hq_decode_workspace_size(kv, Hq, n_splits) bytes (no
+ * initialisation needed). Calls that share a workspace and run concurrently
+ * on different streams race; calls on one stream do not.
+ * Requires Hq % Hkv == 0 and G in {1, 2, 4, 8, 16}.
  */
 hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
                          float sm_scale, int n_splits, float *out, float *lse, void *ws,

@@ -57,7 +57,8 @@ def _gpu_decode(w, K, V, q, vl, n_splits=0, win_offset=0, poison=False, repeat=1
                 for t in vl[b, h]:
                     vt[t // 16, :, t % 16] = 0xFF
     kv = cache.descriptor()
-    ws = torch.zeros(hq.hq_decode_workspace_size(kv, w.Hq, n_splits), dtype=torch.uint8, device="cuda")
+    # the workspace needs no initialisation: start from garbage
+    ws = torch.full((hq.hq_decode_workspace_size(kv, w.Hq, n_splits),), 0xFF, dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(repeat):
         out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
@@ -65,7 +66,6 @@ def _gpu_decode(w, K, V, q, vl, n_splits=0, win_offset=0, poison=False, repeat=1
         hq.hq_decode_attn(qd, w.Hq, kv, 0.0, n_splits, out, lse, ws)
         torch.cuda.synchronize()
         outs.append((out.cpu().numpy(), lse.cpu().numpy()))
-    assert int(ws[:4096].count_nonzero()) == 0, "merge tickets must be left zero"
     return outs if repeat > 1 else outs[0]
 
 

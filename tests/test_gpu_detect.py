@@ -40,6 +40,8 @@ def _run(q_acc, K, cand_end, k_top, method, dtype):
     (1, 8, 1, 128, 64, 2048, 1920, 1920, "f16", 1.0),   # k_top == cand_end
     (1, 8, 2, 128, 64, 2048, 1920, 0, "bf16", 1.0),     # k_top == 0 (scores only)
     (1, 8, 2, 128, 64, 1000, 1, 1, "bf16", 1.0),        # single candidate
+    (1, 8, 2, 128, 16, 40000, 39900, 1995, "bf16", 2.0),  # keys beyond the LDS-resident size
+    (1, 4, 1, 128, 2, 5000, 4900, 4000, "bf16", 0.0625),  # nearly all scores tied
 ])
 def test_detect_small_exact(method, B, Hq, Hkv, D, R, n, ce, k_top, dtype, spread):
     say(f"detect method={method} B={B} Hq={Hq} Hkv={Hkv} D={D} R={R} n={n} ce={ce} k={k_top} {dtype}")
