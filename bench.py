@@ -6,7 +6,8 @@ hybrid KV cache:
      64th step (step mod 64 == 63) the Q_acc . K^T column scores and the
      top-k run, and the new VL set is installed (hq_vl_bitmap +
      hq_gather_rows of the VL keys and values);
-  2. hq_quantize_kv: the token leaving the window is packed into INT4;
+  2. hq_quantize_kv_pair: the token leaving the window is packed into INT4
+     (keys and values in one launch);
   3. hq_decode_attn: attention over INT4 + VL + window with the split-K
      LSE merge.
 Steps rotate over `--copies` independent layer caches (>= 1 GB in total) so
@@ -144,10 +145,9 @@ def main():
             hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
             hq.hq_gather_rows(Vc, n_heads, T, D, idx_new, k, cache.vl_v)
         # the token leaving the window goes to INT4 (static context: last INT4 row)
-        hq.hq_quantize_kv(Kc[:, :, nq - 1:], n_heads, 1, D, T * D, D, cache.k_codes, cache.k_sz,
-                          hq.HQ_LAYOUT_ROWS, cache.t_cap, nq - 1)
-        hq.hq_quantize_kv(Vc[:, :, nq - 1:], n_heads, 1, D, T * D, D, cache.v_codes, cache.v_sz,
-                          hq.HQ_LAYOUT_TILE16, cache.t_cap, nq - 1)
+        hq.hq_quantize_kv_pair(Kc[:, :, nq - 1:], Vc[:, :, nq - 1:], n_heads, 1, D, T * D, D,
+                               cache.k_codes, cache.k_sz, cache.v_codes, cache.v_sz,
+                               cache.t_cap, nq - 1)
         hq.hq_decode_attn(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
 
     # ------------------------------------------------------------ timed steps

@@ -52,6 +52,11 @@ _SIGS = {
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_void_p]),
+    "hq_quantize_kv_pair": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_void_p]),
     "hq_gather_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p]),
@@ -140,6 +145,19 @@ def hq_quantize_kv(x, n_heads, n_rows, D, x_head_stride, x_row_stride, codes, sz
     _check(lib().hq_quantize_kv(x.data_ptr(), _dt(x), n_heads, n_rows, D, group, x_head_stride,
                                 x_row_stride, _ptr(codes), _ptr(sz), layout, dst_head_rows,
                                 dst_row0, _stream(stream)))
+
+
+def hq_quantize_kv_pair(xk, xv, n_heads, n_rows, D, x_head_stride, x_row_stride, k_codes, k_sz,
+                        v_codes, v_sz, dst_head_rows, dst_row0, group=32, stream=None):
+    """K rows (row layout) and V rows (16-token tiles) in one launch (see include/hq.h)."""
+    if xk.device.type != "cuda" or xv.device.type != "cuda":
+        raise ValueError("xk and xv must live on the GPU")
+    if xk.dtype != xv.dtype:
+        raise TypeError("xk and xv must share a dtype")
+    _check(lib().hq_quantize_kv_pair(xk.data_ptr(), xv.data_ptr(), _dt(xk), n_heads, n_rows, D, group,
+                                     x_head_stride, x_row_stride, _ptr(k_codes), _ptr(k_sz),
+                                     _ptr(v_codes), _ptr(v_sz), dst_head_rows, dst_row0,
+                                     _stream(stream)))
 
 
 def hq_gather_rows(src, n_heads, src_rows, D, idx, k, dst, stream=None):

@@ -460,6 +460,215 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   }
 }
 
+// ---------------------------------------------------------------- INT4 pass, D = 128, 4 heads
+// Specialisation of the INT4 pass for the common shape (head_dim 128, a GQA
+// chunk of 4 query heads, 16-bit queries). Lane (slot, g) keeps its four
+// per-head partial dots in a lane-dependent order -- register j holds head
+// g ^ j -- so two DPP exchanges (xor 2, then xor 1) leave the full logit of
+// head g in lane g of the token with three adds and no selects. The mask, the
+// max test, the subtraction and the exponential then run once per lane, and
+// the other heads' probabilities reach the P . V weights through DPP
+// broadcasts fused into the multiplies.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mul(float a, float b) {   // dpp(a) * b
+  return dpp_f<CTRL>(a) * b;
+}
+constexpr int kQuadBcast[4] = {0x00, 0x55, 0xAA, 0xFF};        // quad_perm [h,h,h,h]
+
+template <int QT>
+__device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int h, int i0,
+                                   int64_t r0, int64_t r1, WaveState<4> &st) {
+  constexpr int D = 128, HB = 4, LPT = 4, SLOTS = 16, CP = 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = lane >> 2;
+  const int g = lane & 3;
+  const int cp = lane;                 // P.V lane: channel pair
+  const int gp = cp >> 4;
+  const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
+
+  // query pairs of this lane's group for head g ^ j in register j
+  uint32_t qp[4][4][4];
+  float cqs[4];          // cs * sum of the group's query channels, head g ^ j
+  float negmq[4];        // -MAGIC * that sum (start of each dot chain)
+  constexpr uint32_t kMagic = (QT == HQ_BF16) ? 0x43004300u : 0x64006400u;
+  constexpr float kMagicVal = (QT == HQ_BF16) ? 128.f : 1024.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t qoff = (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32;
+    uint32_t raw[16];
+    load_q32<QT>(P.q, qoff, raw);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      s += half_bits_to_f32<QT>(raw[c] & 0xFFFFu) + half_bits_to_f32<QT>(raw[c] >> 16);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int a = 8 * w + m, c = 8 * w + m + 4;
+        const uint32_t lo = (raw[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
+        const uint32_t hi = (raw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+        qp[j][w][m] = lo | (hi << 16);
+      }
+    cqs[j] = P.cs * s;
+    negmq[j] = -kMagicVal * s;
+  }
+  const uint32_t magic = kMagic;
+  const uint32_t vmagic = 0x64006400u;
+  float zl[4] = {0.f, 0.f, 0.f, 0.f};   // sum p_h (z + 8 s) of this lane's group, head h
+  float lown = 0.f;                      // sum of p of head g (this lane's head)
+  float mown = kNegInf;                  // running max of head g
+
+  const uint32_t n = static_cast<uint32_t>(r1 - r0);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k_codes + (head * P.t_cap + r0) * (D / 2), n * (D / 2));
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(P.k_sz + (head * P.t_cap + r0) * (D / 32), n * (D / 8));
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(P.v_sz + (head * P.t_cap + r0) * (D / 32), n * (D / 8));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v_codes + (head * P.t_cap + r0) * (D / 2),
+                                              ((n + 15) / 16) * (CP * 16));
+  const uint32_t w_first = static_cast<uint32_t>(r0 >> 5);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(P.vl_bits + head * P.bits_words + w_first,
+                                              static_cast<uint32_t>(((r1 + 31) >> 5) - w_first) * 4);
+  const uint32_t r0_bit = static_cast<uint32_t>(r0 & 31);
+
+  auto issue = [&](int64_t c, Int4Loads<D> &L) {
+    const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
+    L.kc = bload16(rk, tok * (D / 2) + g * 16);
+    L.ks = bload4(rks, tok * (D / 8) + g * 4);
+    L.vs = bload4(rvs, tok * (D / 8) + g * 4);
+    L.bits = bload4(rb, ((r0_bit + tok) >> 5) * 4);
+    L.vc = bload16(rv, static_cast<uint32_t>(c) * (CP * 16) + cp * 16);
+  };
+
+  constexpr int NPF = 3;
+  const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
+  Int4Loads<D> ring[NPF];
+#pragma unroll
+  for (int jr = 0; jr < NPF; ++jr) issue(wave + jr * kWaves, ring[jr]);
+  _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
+  for (int64_t cb = wave; cb < nsteps; cb += NPF * kWaves) {
+#pragma unroll
+    for (int jr = 0; jr < NPF; ++jr) {
+      const int64_t c = cb + jr * kWaves;
+      if (c >= nsteps) break;
+      Int4Loads<D> &cur = ring[jr];
+      const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
+
+      // ---- q . k over this lane's group, head g ^ j in part[j]
+      float part[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[j] = negmq[j];
+      const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const uint32_t x0 = and_or(w[ww], 0x000F000Fu, magic);
+        const uint32_t x1 = and_or(w[ww] >> 4, 0x000F000Fu, magic);
+        const uint32_t x2 = and_or(w[ww] >> 8, 0x000F000Fu, magic);
+        const uint32_t x3 = and_or(w[ww] >> 12, 0x000F000Fu, magic);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          part[j] = dot2_q<QT>(qp[j][ww][0], x0, part[j]);
+          part[j] = dot2_q<QT>(qp[j][ww][1], x1, part[j]);
+          part[j] = dot2_q<QT>(qp[j][ww][2], x2, part[j]);
+          part[j] = dot2_q<QT>(qp[j][ww][3], x3, part[j]);
+        }
+      }
+      // scaled group partials: cs * (s * dot + z * sum q)
+      const float ssc = lo_f16(cur.ks) * P.cs;
+      const float zk = hi_f16(cur.ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[j] = fmaf(zk, cqs[j], part[j] * ssc);
+      // quad reduce-scatter: lane g ends with head g summed over the 4 groups
+      const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
+      const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
+      const float lgv = y0 + dpp_f<kQuadXor1>(y1);
+      const bool live = (tok < n) && !((cur.bits >> ((r0_bit + tok) & 31)) & 1u);
+      const float lg = live ? lgv : kNegInf;
+
+      if (__ballot(lg > mown)) {
+        // slow path: new wave max of head g; rescale every running quantity
+        const float mx = slots_max<LPT>(lg);
+        const float mn = fmaxf(mown, mx);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        const float alpha = fast_exp2(mown - mu);          // of head g
+        mown = mn;
+        lown *= alpha;
+        zl[0] = dpp_mul<kQuadBcast[0]>(alpha, zl[0]);
+        zl[1] = dpp_mul<kQuadBcast[1]>(alpha, zl[1]);
+        zl[2] = dpp_mul<kQuadBcast[2]>(alpha, zl[2]);
+        zl[3] = dpp_mul<kQuadBcast[3]>(alpha, zl[3]);
+        // the P.V lanes hold channels of every head: alpha of head hh from lane hh
+        const float a0 = __shfl(alpha, 0, 64), a1 = __shfl(alpha, 1, 64);
+        const float a2 = __shfl(alpha, 2, 64), a3 = __shfl(alpha, 3, 64);
+        st.acc_e[0] *= a0; st.acc_o[0] *= a0;
+        st.acc_e[1] *= a1; st.acc_o[1] *= a1;
+        st.acc_e[2] *= a2; st.acc_o[2] *= a2;
+        st.acc_e[3] *= a3; st.acc_o[3] *= a3;
+      }
+      const float p = fast_exp2(lg - ((mown == kNegInf) ? 0.f : mown));
+      lown += p;
+      // V scale and the zero point of the centred codes, z + 8 s; zero for
+      // masked tokens (their planes may hold anything, NaN included)
+      const float sv = live ? lo_f16(cur.vs) : 0.f;
+      const float zv = live ? fmaf(8.f, lo_f16(cur.vs), hi_f16(cur.vs)) : 0.f;
+      const float ps0 = dpp_mul<kQuadBcast[0]>(p, sv);
+      const float ps1 = dpp_mul<kQuadBcast[1]>(p, sv);
+      const float ps2 = dpp_mul<kQuadBcast[2]>(p, sv);
+      const float ps3 = dpp_mul<kQuadBcast[3]>(p, sv);
+      zl[0] = fmaf(dpp_f<kQuadBcast[0]>(p), zv, zl[0]);
+      zl[1] = fmaf(dpp_f<kQuadBcast[1]>(p), zv, zl[1]);
+      zl[2] = fmaf(dpp_f<kQuadBcast[2]>(p), zv, zl[2]);
+      zl[3] = fmaf(dpp_f<kQuadBcast[3]>(p), zv, zl[3]);
+      psh[(0 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps0);
+      psh[(1 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps1);
+      psh[(2 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps2);
+      psh[(3 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps3);
+      wave_sync();
+
+      // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
+      const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
+      uint32_t e[8], o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t x = __builtin_amdgcn_perm(0u, vw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
+        e[i] = centre_f16x2(and_or(x, 0x000F000Fu, vmagic), 0xE408E408u);
+        o[i] = centre_f16x2(and_or(x, 0x00F000F0u, vmagic), 0xE480E480u);
+      }
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16]);
+        const uint4 pa = src[0], pb = src[1];
+        const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
+          st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
+        }
+      }
+      wave_sync();
+      if (c + NPF * kWaves < nsteps) issue(c + NPF * kWaves, ring[jr]);
+    }
+  }
+
+  // ---- per-(head, group) zero-point sums, folded into the accumulators; the
+  // wave state of head hh lives in lane hh's quad position
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const float z = xor_sum<LPT>(zl[hh]);
+    if (slot == 0) sm.zo[wave][hh][g] = z;
+  }
+  const float lsum = xor_sum<LPT>(lown);                 // head g, over the slots
+  wave_sync();
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const float z = sm.zo[wave][hh][gp];
+    st.acc_e[hh] = st.acc_e[hh] + z;
+    st.acc_o[hh] = st.acc_o[hh] * 0.0625f + z;
+    st.m[hh] = __shfl(mown, hh, 64);
+    st.l[hh] = __shfl(lsum, hh, 64);
+  }
+}
+
 // ---------------------------------------------------------------- 16-bit pass
 // Element offset of row rr of the 16-bit list (VL rows first, then the window
 // in position order), clamped to the last valid row; rows past r1 are masked
@@ -658,7 +867,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   if (split < P.S_q) {
     const int64_t r0 = static_cast<int64_t>(split) * P.len_q;
     const int64_t r1 = r0 + P.len_q < P.nq ? r0 + P.len_q : P.nq;
-    int4_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
+    if constexpr (D == 128 && HB == 4 && QT != HQ_F32)
+      int4_split_d128_g4<QT>(P, sm, b, h, i0, r0, r1, st);
+    else
+      int4_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
   } else {
     const int64_t nfp = static_cast<int64_t>(P.k) + P.W;
     const int64_t r0 = static_cast<int64_t>(split - P.S_q) * P.len_fp;
@@ -730,8 +942,20 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
   for (int s0 = 0; s0 < S; s0 += kMergeStage) {
     const int ns = (S - s0) < kMergeStage ? (S - s0) : kMergeStage;
     __syncthreads();
-    for (int e = threadIdx.x; e < ns * (D / 4); e += kThreads) so[e] = po[s0 * (D / 4) + e];
-    if (threadIdx.x < ns) sml[threadIdx.x] = pml[s0 + threadIdx.x];
+    {
+      // every load of the stage first, then the LDS stores (one round trip)
+      constexpr int PER = kMergeStage * D / 4 / kThreads;
+      float4 v[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = i * kThreads + threadIdx.x;
+        v[i] = e < ns * (D / 4) ? po[s0 * (D / 4) + e] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      const float2 ml = threadIdx.x < ns ? pml[s0 + threadIdx.x] : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) so[i * kThreads + threadIdx.x] = v[i];
+      if (threadIdx.x < ns) sml[threadIdx.x] = ml;
+    }
     __syncthreads();
     if (d < D) {
       float mx = m_run;

@@ -21,9 +21,10 @@
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
-//  * topk_kernel     one workgroup per unit: radix select on a 32-bit
-//    order-preserving key (score - min) >> shift, refinement of the boundary
-//    bucket on the full int64 score, then an index cut for equal scores and an
+//  * topk_kernel     one workgroup per unit: radix select (8-bit digits,
+//    one histogram per wave so the waves never contend) on the 32-bit key
+//    (score - min) >> shift (held in LDS), refinement of the boundary bucket
+//    on the bits the shift dropped, then an index cut for equal scores and an
 //    in-order compaction, so the output is ascending by position.
 #include "hq_common.h"
 
@@ -243,15 +244,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, c
 
 // ---------------------------------------------------------------- top-k
 constexpr int kTopkThreads = 1024;
-constexpr int kLdsKeys = 36864;          // keys kept in LDS up to this many candidates
-
-// Order-preserving 32-bit key of an int64 score: the bits of float(score)
-// (round to nearest is monotone non-decreasing) mapped so that unsigned order
-// equals float order.
-__device__ __forceinline__ uint32_t ordered_key(long long s) {
-  const uint32_t u = __float_as_uint(static_cast<float>(s));
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int kLdsKeys = 33792;          // keys kept in LDS up to this many candidates
+// LDS slot of key j: one padding word per 32 keys, so both the strided passes
+// (consecutive j across lanes) and the per-thread runs of the compaction
+// (j = t * per + i, 33 * t mod 64 distinct) are free of bank conflicts
+__device__ __forceinline__ int64_t pad_slot(int64_t j) { return j + (j >> 5); }
+constexpr int kLdsKeySlots = kLdsKeys + kLdsKeys / 32;
 
 // exclusive scan of one int per thread over the block; *total gets the sum
 __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) {
@@ -280,29 +278,34 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) 
   return pre;
 }
 
+constexpr int kDigitBits = 8;            // radix digits of 8 bits, 256 bins
+constexpr int kBins = 1 << kDigitBits;
 struct TopkShared {
-  uint32_t hist[2048];
+  uint32_t whist[kTopkThreads / 64][kBins];   // one histogram per wave: no cross-wave contention
+  uint32_t hist[kBins];
   int scan[kTopkThreads / 64 + 2];
   int sel[4];
   unsigned long long mm[2 * kTopkThreads / 64];
 };
 
-// One radix pass: among elements with (key & pmask) == prefix, histogram the
-// digit (key >> shift) & (2^bits - 1) and find the digit holding the k_rem-th
-// largest. Returns the digit; *k_rem becomes the rank inside that digit.
-template <typename KeyAt>
-__device__ int radix_pass(int64_t n, KeyAt key_at, uint32_t prefix, uint32_t pmask, int shift,
-                          int bits, int *k_rem, int *eq_count, TopkShared &sh) {
-  const int nb = 1 << bits;
-  for (int i = threadIdx.x; i < 2048; i += kTopkThreads) sh.hist[i] = 0u;
-  __syncthreads();
-#pragma unroll 4
-  for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-    const uint32_t key = key_at(j);
-    if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+__device__ __forceinline__ void clear_whist(TopkShared &sh) {
+  uint32_t *h = &sh.whist[0][0];
+  for (int i = threadIdx.x; i < (kTopkThreads / 64) * kBins; i += kTopkThreads) h[i] = 0u;
+}
+// sum the per-wave histograms into sh.hist
+__device__ __forceinline__ void reduce_whist(TopkShared &sh) {
+  for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) t += sh.whist[w][b];
+    sh.hist[b] = t;
   }
-  __syncthreads();
-  // bins in descending digit order: thread t holds digits nb-1-2t, nb-2-2t
+}
+
+// Digit search after a histogram pass: the digit (bins in descending order)
+// holding the k_rem-th largest; returns it, *k_rem becomes the rank inside
+// the digit and *cnt the digit's population.
+__device__ int find_digit(int nb, int *k_rem, int *cnt, TopkShared &sh) {
   const int dhi = nb - 1 - 2 * static_cast<int>(threadIdx.x);
   const int dlo = dhi - 1;
   const int chi = dhi >= 0 ? static_cast<int>(sh.hist[dhi]) : 0;
@@ -318,131 +321,162 @@ __device__ int radix_pass(int64_t n, KeyAt key_at, uint32_t prefix, uint32_t pma
   __syncthreads();
   const int d = sh.sel[0];
   *k_rem = sh.sel[1];
-  *eq_count = sh.sel[2];
+  *cnt = sh.sel[2];
   __syncthreads();
   return d;
 }
 
+// One workgroup per (b, h). Keys (score - min) >> shift live in LDS (or, past
+// kLdsKeys candidates, in the workspace); scores are read from global memory
+// in the two key-building passes (8 independent loads per thread per step)
+// and again only for members of the boundary bucket.
 template <bool IN_LDS>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__restrict__ scores,
                                                             uint32_t *__restrict__ gkeys, int64_t n,
                                                             int k_top, int32_t *__restrict__ idx_out) {
   __shared__ TopkShared sh;
-  __shared__ uint32_t lkeys[IN_LDS ? kLdsKeys : 1];
+  __shared__ uint32_t lkeys[IN_LDS ? kLdsKeySlots : 1];
   const int unit = blockIdx.x;
   const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
   uint32_t *gk = gkeys + static_cast<int64_t>(unit) * n;
   int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
   if (k_top == 0) return;
+  constexpr int U = 8;
+  const int64_t stride = static_cast<int64_t>(kTopkThreads) * U;
 
-  // keys (one pass over the scores)
-#pragma unroll 4
-  for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-    const uint32_t key = ordered_key(sc[j]);
-    if constexpr (IN_LDS) lkeys[j] = key; else gk[j] = key;
+  // 1. range of the scores
+  unsigned long long mn = ~0ull, mx = 0;
+  for (int64_t j0 = threadIdx.x; j0 < n; j0 += stride) {
+    long long w[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t j = j0 + static_cast<int64_t>(i) * kTopkThreads;
+      w[i] = j < n ? sc[j] : sc[j0];
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const unsigned long long u = static_cast<unsigned long long>(w[i]) ^ 0x8000000000000000ull;
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+    mn = a < mn ? a : mn;
+    mx = c > mx ? c : mx;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sh.mm[threadIdx.x >> 6] = mn;
+    sh.mm[kTopkThreads / 64 + (threadIdx.x >> 6)] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kTopkThreads / 64; ++i) {
+      mn = sh.mm[i] < mn ? sh.mm[i] : mn;
+      mx = sh.mm[kTopkThreads / 64 + i] > mx ? sh.mm[kTopkThreads / 64 + i] : mx;
+    }
+    sh.mm[0] = mn;
+    sh.mm[1] = mx;
+  }
+  __syncthreads();
+  const unsigned long long base = sh.mm[0];
+  const unsigned long long range = sh.mm[1] - base;
+  __syncthreads();
+  const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
+  const int shift = nbits > 32 ? nbits - 32 : 0;
+  auto off = [&](long long sv) -> unsigned long long {
+    return (static_cast<unsigned long long>(sv) ^ 0x8000000000000000ull) - base;
+  };
+
+  // 2. keys
+  for (int64_t j0 = threadIdx.x; j0 < n; j0 += stride) {
+    long long w[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t j = j0 + static_cast<int64_t>(i) * kTopkThreads;
+      w[i] = j < n ? sc[j] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t j = j0 + static_cast<int64_t>(i) * kTopkThreads;
+      if (j < n) {
+        const uint32_t key = static_cast<uint32_t>(off(w[i]) >> shift);
+        if constexpr (IN_LDS) lkeys[pad_slot(j)] = key; else gk[j] = key;
+      }
+    }
   }
   __syncthreads();
   auto key_at = [&](int64_t j) -> uint32_t {
-    if constexpr (IN_LDS) return lkeys[j]; else return gk[j];
+    if constexpr (IN_LDS) return lkeys[pad_slot(j)]; else return gk[j];
   };
 
-  // radix select on the 32-bit keys: 11 + 11 + 10 bits
+  // 3. radix select on the keys: four 8-bit digits
   int k_rem = k_top, eq = 0;
   uint32_t prefix = 0, pmask = 0;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int p = 0; p < 3; ++p) {
-    const int d = radix_pass(n, key_at, prefix, pmask, shifts[p], widths[p], &k_rem, &eq, sh);
-    prefix |= static_cast<uint32_t>(d) << shifts[p];
-    pmask |= ((1u << widths[p]) - 1u) << shifts[p];
-  }
-  const uint32_t kappa = prefix;       // key of the k_top-th largest
-  int take = k_rem;                    // how many with key == kappa are taken
-
-  // refine the kappa bucket on the exact int64 score (its members differ only
-  // in the bits float32 drops): radix over (score - min) of the bucket
-  long long tau = 0;
-  bool refine = eq > take;
-  if (refine) {
-    unsigned long long mn = ~0ull, mx = 0;
+  uint32_t *wh = sh.whist[threadIdx.x >> 6];
+  for (int sft = 24; sft >= 0; sft -= kDigitBits) {
+    clear_whist(sh);
+    __syncthreads();
 #pragma unroll 4
     for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-      if (key_at(j) == kappa) {
-        const unsigned long long v = static_cast<unsigned long long>(sc[j]) ^ 0x8000000000000000ull;
-        mn = v < mn ? v : mn;
-        mx = v > mx ? v : mx;
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
-      mn = a < mn ? a : mn;
-      mx = c > mx ? c : mx;
-    }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { sh.mm[w] = mn; sh.mm[kTopkThreads / 64 + w] = mx; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int i = 1; i < kTopkThreads / 64; ++i) {
-        mn = sh.mm[i] < mn ? sh.mm[i] : mn;
-        mx = sh.mm[kTopkThreads / 64 + i] > mx ? sh.mm[kTopkThreads / 64 + i] : mx;
-      }
-      sh.mm[0] = mn; sh.mm[1] = mx;
+      const uint32_t key = key_at(j);
+      if ((key & pmask) == prefix) atomicAdd(&wh[(key >> sft) & (kBins - 1)], 1u);
     }
     __syncthreads();
-    const unsigned long long base = sh.mm[0];
-    const unsigned long long range = sh.mm[1] - base;
+    reduce_whist(sh);
     __syncthreads();
-    const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
-    unsigned long long lowpre = 0;
-    unsigned long long lowmask = 0;
-    for (int top = nbits; top > 0; top -= 11) {
-      const int bits = top >= 11 ? 11 : top;
-      const int shift = top - bits;
-      // histogram of this digit among the bucket members matching the higher digits
-      for (int i = threadIdx.x; i < 2048; i += kTopkThreads) sh.hist[i] = 0u;
+    const int d = find_digit(kBins, &k_rem, &eq, sh);
+    prefix |= static_cast<uint32_t>(d) << sft;
+    pmask |= static_cast<uint32_t>(kBins - 1) << sft;
+  }
+  const uint32_t kappa = prefix;   // key of the k_top-th largest
+  int take = k_rem;                // taken among key == kappa
+
+  // 4. members of the kappa bucket differ only in the low `shift` bits:
+  //    select on those bits when the bucket is not taken whole
+  const bool refine = eq > take && shift > 0;
+  unsigned long long low = 0;
+  if (refine) {
+    unsigned long long lowpre = 0, lowmask = 0;
+    const unsigned long long lbits = (shift >= 64) ? ~0ull : ((1ull << shift) - 1ull);
+    for (int top = shift; top > 0; top -= kDigitBits) {
+      const int bits = top >= kDigitBits ? kDigitBits : top;
+      const int sh2 = top - bits;
+      clear_whist(sh);
       __syncthreads();
-#pragma unroll 4
       for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
         if (key_at(j) == kappa) {
-          const unsigned long long v = (static_cast<unsigned long long>(sc[j]) ^ 0x8000000000000000ull) - base;
-          if ((v & lowmask) == lowpre) atomicAdd(&sh.hist[(v >> shift) & ((1u << bits) - 1u)], 1u);
+          const unsigned long long lo = off(sc[j]) & lbits;
+          if ((lo & lowmask) == lowpre) atomicAdd(&wh[(lo >> sh2) & ((1u << bits) - 1u)], 1u);
         }
       }
       __syncthreads();
-      const int nb = 1 << bits;
-      const int dhi = nb - 1 - 2 * static_cast<int>(threadIdx.x);
-      const int dlo = dhi - 1;
-      const int chi = dhi >= 0 ? static_cast<int>(sh.hist[dhi]) : 0;
-      const int clo = dlo >= 0 ? static_cast<int>(sh.hist[dlo]) : 0;
-      int tot;
-      const int above = block_exclusive_scan(chi + clo, sh.scan, &tot);
-      if (dhi >= 0 && above < take && take <= above + chi) {
-        sh.sel[0] = dhi; sh.sel[1] = take - above;
-      } else if (dlo >= 0 && above + chi < take && take <= above + chi + clo) {
-        sh.sel[0] = dlo; sh.sel[1] = take - above - chi;
-      }
+      reduce_whist(sh);
       __syncthreads();
-      lowpre |= static_cast<unsigned long long>(sh.sel[0]) << shift;
-      lowmask |= static_cast<unsigned long long>((1u << bits) - 1u) << shift;
-      take = sh.sel[1];
-      __syncthreads();
+      int cnt;
+      const int d = find_digit(1 << bits, &take, &cnt, sh);
+      lowpre |= static_cast<unsigned long long>(d) << sh2;
+      lowmask |= static_cast<unsigned long long>((1u << bits) - 1u) << sh2;
     }
-    tau = static_cast<long long>((base + lowpre) ^ 0x8000000000000000ull);
+    low = lowpre;
   }
-
-  // selected(j): key > kappa, or key == kappa and (not refining: one of the
-  // first `take` bucket members by position; refining: score > tau, or
-  // score == tau and one of the first `take` such members by position)
-  const int64_t per = (n + kTopkThreads - 1) / kTopkThreads;
-  const int64_t j0 = threadIdx.x * per;
-  const int64_t j1 = (j0 + per) < n ? (j0 + per) : n;
+  // every candidate above the threshold is taken; of those equal to it, the
+  // first `take` by position
+  const unsigned long long tau = (static_cast<unsigned long long>(kappa) << shift) + low;
   auto is_tie = [&](int64_t j, uint32_t key) -> bool {
-    return key == kappa && (!refine || sc[j] == tau);
+    if (key != kappa) return false;
+    return refine ? (off(sc[j]) == tau) : true;
   };
   auto is_sure = [&](int64_t j, uint32_t key) -> bool {
-    return key > kappa || (refine && key == kappa && sc[j] > tau);
+    if (key != kappa) return key > kappa;
+    return refine && off(sc[j]) > tau;
   };
+
+  // 5. in-order compaction over contiguous per-thread runs
+  const int64_t per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int64_t j0 = threadIdx.x * per < n ? threadIdx.x * per : n;
+  const int64_t j1 = (j0 + per) < n ? (j0 + per) : n;
   int ties = 0, sure = 0;
   for (int64_t j = j0; j < j1; ++j) {
     const uint32_t key = key_at(j);

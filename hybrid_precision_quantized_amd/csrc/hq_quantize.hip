@@ -24,16 +24,13 @@ namespace {
 
 constexpr int kGroup = 32;
 
-// One thread per (head, row, 32-channel group).
+// Quantizes one (head, row, 32-channel group) of x, thread index gid.
 template <int DT, int LAYOUT>
-__global__ __launch_bounds__(256) void quantize_kernel(
-    const void *__restrict__ x, int n_heads, int64_t n_rows, int D, int64_t x_head_stride,
+__device__ __forceinline__ void quantize_group(
+    int64_t gid, const void *__restrict__ x, int64_t n_rows, int D, int64_t x_head_stride,
     int64_t x_row_stride, uint8_t *__restrict__ codes, uint16_t *__restrict__ sz,
     int64_t dst_head_rows, int64_t dst_row0) {
   const int ng = D / kGroup;
-  const int64_t total = static_cast<int64_t>(n_heads) * n_rows * ng;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= total) return;
   const int g = static_cast<int>(gid % ng);
   const int64_t hr = gid / ng;
   const int64_t r = hr % n_rows;
@@ -109,6 +106,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const uint32_t szw = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
                        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
   reinterpret_cast<uint32_t *>(sz)[head_row * (D / kGroup) + g] = szw;
+}
+
+// One thread per (head, row, 32-channel group).
+template <int DT, int LAYOUT>
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const void *__restrict__ x, int n_heads, int64_t n_rows, int D, int64_t x_head_stride,
+    int64_t x_row_stride, uint8_t *__restrict__ codes, uint16_t *__restrict__ sz,
+    int64_t dst_head_rows, int64_t dst_row0) {
+  const int64_t total = static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  quantize_group<DT, LAYOUT>(gid, x, n_rows, D, x_head_stride, x_row_stride, codes, sz,
+                             dst_head_rows, dst_row0);
+}
+
+// Keys (row layout) and values (16-token tiles) of the same rows in one launch:
+// the first half of the threads packs K, the second half V.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_pair_kernel(
+    const void *__restrict__ xk, const void *__restrict__ xv, int n_heads, int64_t n_rows, int D,
+    int64_t x_head_stride, int64_t x_row_stride, uint8_t *__restrict__ k_codes,
+    uint16_t *__restrict__ k_sz, uint8_t *__restrict__ v_codes, uint16_t *__restrict__ v_sz,
+    int64_t dst_head_rows, int64_t dst_row0) {
+  const int64_t total = static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid < total) {
+    quantize_group<DT, HQ_LAYOUT_ROWS>(gid, xk, n_rows, D, x_head_stride, x_row_stride, k_codes,
+                                       k_sz, dst_head_rows, dst_row0);
+  } else if (gid < 2 * total) {
+    quantize_group<DT, HQ_LAYOUT_TILE16>(gid - total, xv, n_rows, D, x_head_stride, x_row_stride,
+                                         v_codes, v_sz, dst_head_rows, dst_row0);
+  }
 }
 
 // One thread per 16-byte chunk of a destination row.
@@ -214,4 +243,43 @@ extern "C" hq_status hq_gather_rows(const void *src, hq_dtype dtype, int n_heads
                      as_stream(stream), static_cast<const uint8_t *>(src), src_rows, row_bytes,
                      idx, k, n_heads, static_cast<uint8_t *>(dst));
   return check_launch("hq_gather_rows");
+}
+
+extern "C" hq_status hq_quantize_kv_pair(const void *xk, const void *xv, hq_dtype x_dtype,
+                                         int n_heads, int64_t n_rows, int D, int group,
+                                         int64_t x_head_stride, int64_t x_row_stride,
+                                         uint8_t *k_codes, uint16_t *k_sz, uint8_t *v_codes,
+                                         uint16_t *v_sz, int64_t dst_head_rows, int64_t dst_row0,
+                                         void *stream) {
+  if (!dtype_ok(x_dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: bad dtype %d", x_dtype);
+  if (group != kGroup) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv_pair: group must be 32");
+  if (D != 64 && D != 128) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv_pair: D must be 64 or 128");
+  if (n_heads < 0 || n_rows < 0 || dst_row0 < 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: negative size");
+  if (dst_row0 + n_rows > dst_head_rows)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: rows exceed dst_head_rows");
+  if (dst_head_rows % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: dst_head_rows must be a multiple of 16");
+  if (n_heads == 0 || n_rows == 0) { clear_error(); return HQ_OK; }
+  if (!xk || !xv || !k_codes || !k_sz || !v_codes || !v_sz)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: null pointer");
+  const int eb = dtype_bytes(x_dtype);
+  if ((x_row_stride * eb) % 16 != 0 || (x_head_stride * eb) % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(xk) | reinterpret_cast<uintptr_t>(xv) |
+       reinterpret_cast<uintptr_t>(k_codes)) % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(k_sz) | reinterpret_cast<uintptr_t>(v_sz)) % 4 != 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: rows must be 16-byte aligned");
+  const int64_t threads = 2 * static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv_pair: too many rows");
+  const dim3 grid(static_cast<unsigned>(blocks));
+  hipStream_t st = as_stream(stream);
+#define HQ_PAIR(DT_) hipLaunchKernelGGL(quantize_pair_kernel<DT_>, grid, dim3(256), 0, st, xk, xv, n_heads, n_rows, D, x_head_stride, x_row_stride, k_codes, k_sz, v_codes, v_sz, dst_head_rows, dst_row0)
+  switch (x_dtype) {
+    case HQ_F32: HQ_PAIR(HQ_F32); break;
+    case HQ_BF16: HQ_PAIR(HQ_BF16); break;
+    default: HQ_PAIR(HQ_F16); break;
+  }
+#undef HQ_PAIR
+  return check_launch("hq_quantize_kv_pair");
 }

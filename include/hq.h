@@ -128,6 +128,21 @@ hq_status hq_quantize_kv(const void *x, hq_dtype x_dtype, int n_heads, int64_t n
                          int64_t dst_head_rows, int64_t dst_row0, void *stream);
 
 /*
+ * hq_quantize_kv_pair -- hq_quantize_kv for the keys and the values of the
+ * same rows in one launch, in the layouts hq_decode_attn reads: K codes in
+ * HQ_LAYOUT_ROWS, V codes in HQ_LAYOUT_TILE16 (same page and section: both
+ * keys and values of the quantized majority are 4-bit). This is the per-step
+ * eviction of the token that leaves the local window. Arguments as in
+ * hq_quantize_kv, with xk/xv sharing dtype and strides; dst_head_rows must be
+ * a multiple of 16.
+ */
+hq_status hq_quantize_kv_pair(const void *xk, const void *xv, hq_dtype x_dtype, int n_heads,
+                              int64_t n_rows, int D, int group, int64_t x_head_stride,
+                              int64_t x_row_stride, uint8_t *k_codes, uint16_t *k_sz,
+                              uint8_t *v_codes, uint16_t *v_sz, int64_t dst_head_rows,
+                              int64_t dst_row0, void *stream);
+
+/*
  * hq_gather_rows -- copy the vertical-line rows of K or V into the compact
  * 16-bit buffer [AFS, How It Works, item 1: vertical-line tokens stay in full
  * precision]. For each head h and i < k: dst[h][i][:] = src[h][idx[h][i]][:],

@@ -104,3 +104,28 @@ def test_vl_bitmap_exact():
         for t in idx[h]:
             want[h, t // 32] |= np.uint32(1) << np.uint32(t % 32)
     assert np.array_equal(bits.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("dtype,D,n_heads,n_rows,row0", [("bf16", 128, 8, 1, 32639), ("bf16", 64, 3, 40, 8),
+                                                         ("f32", 64, 2, 17, 0), ("f16", 128, 4, 100, 28)])
+def test_quantize_pair_matches_oracle(dtype, D, n_heads, n_rows, row0):
+    say(f"quantize pair dtype={dtype} D={D} heads={n_heads} rows={n_rows} row0={row0}")
+    rng = np.random.default_rng(n_rows + D)
+    src_rows = n_rows + 5
+    xk = _values(rng, n_heads, src_rows, D, dtype)
+    xv = _values(rng, n_heads, src_rows, D, dtype)
+    cap = ((row0 + n_rows + 31) // 32) * 32
+    kc = torch.full((n_heads, cap, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    vc = torch.full((n_heads, cap // 16, D // 2, 16), 0x5A, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((n_heads, cap, D // 32, 2), dtype=torch.int16, device="cuda")
+    vs = torch.zeros_like(ks)
+    hq.hq_quantize_kv_pair(to_dev(xk, dtype), to_dev(xv, dtype), n_heads, n_rows, D, src_rows * D, D,
+                           kc, ks, vc, vs, cap, row0)
+    torch.cuda.synchronize()
+    kp, kz = quant.quantize_rows(xk[:, :n_rows], 32)
+    vp, vz = quant.quantize_rows(xv[:, :n_rows], 32)
+    assert np.array_equal(kc.cpu().numpy()[:, row0:row0 + n_rows], kp)
+    assert np.array_equal(tile16_codes(vc)[:, row0:row0 + n_rows], vp)
+    assert np.array_equal(sz_bits(ks)[:, row0:row0 + n_rows], kz)
+    assert np.array_equal(sz_bits(vs)[:, row0:row0 + n_rows], vz)
+    assert np.all(kc.cpu().numpy()[:, :row0] == 0x5A)
