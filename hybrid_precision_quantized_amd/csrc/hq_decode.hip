@@ -46,6 +46,8 @@
 //    unit in one L2 for the merge.
 #include <math.h>
 
+#include <cmath>
+
 #include "hq_common.h"
 
 namespace hq {
@@ -74,9 +76,9 @@ struct DecodeParams {
   int64_t bits_words;       // words per head of vl_bits
   int k, W, win_offset;
   int B, Hkv, Hq, G, nhc;   // nhc = head chunks per KV head
-  int S_q, S_fp, S;         // splits per unit
-  int64_t len_q;            // positions per INT4 split (multiple of the wave step)
-  int len_fp;               // rows per 16-bit split (multiple of the wave step)
+  int S_q, S_vl, S_win, S;  // splits per unit: INT4, VL rows, window rows
+  int64_t len_q;            // positions per INT4 split (multiple of 64)
+  int len_vl, len_win;      // rows per 16-bit split (multiples of the wave step)
   int units;                // B * Hkv * nhc
   int blocks_used;          // units * S
   int blocks_per_xcd;
@@ -226,6 +228,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
 }
+// The view [base + off, base + bytes), empty when off >= bytes. off is
+// wave-uniform and both are below 2^31, so the size is a signed max with 0,
+// which stays on the scalar unit (an unsigned saturating subtract would be a
+// vector instruction and put the descriptor in vector registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t view(const uint8_t *base, uint32_t bytes, uint32_t off) {
+  const int32_t rem = static_cast<int32_t>(bytes) - static_cast<int32_t>(off);
+  return make_rsrc(base + off, static_cast<uint32_t>(rem > 0 ? rem : 0));
+}
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -237,6 +247,24 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
   return r;
+}
+
+// The 16 tokens of one channel pair of a TILE16 value tile (4 words; word a
+// holds tokens 4a, 4a+2, 4a+1, 4a+3 in bytes 0..3) as centred fp16 pairs:
+// e[i] = (c - 8) of channel 2cp for tokens (2i, 2i+1), o[i] = 16 (c - 8) of
+// channel 2cp+1. A nibble ORed under the fp16 exponent of 1024 gives 1024 + c
+// (low nibble) or 1024 + 16 c (high nibble), and one packed subtract of 1032
+// or 1152 centres it exactly.
+__device__ __forceinline__ void unpack_v_tile(const uint32_t (&vw)[4], uint32_t vmagic, uint32_t (&e)[8],
+                                              uint32_t (&o)[8]) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t w0 = vw[a], w8 = vw[a] >> 8;
+    e[2 * a] = centre_f16x2(and_or(w0, 0x000F000Fu, vmagic), 0xE408E408u);
+    o[2 * a] = centre_f16x2(and_or(w0, 0x00F000F0u, vmagic), 0xE480E480u);
+    e[2 * a + 1] = centre_f16x2(and_or(w8, 0x000F000Fu, vmagic), 0xE408E408u);
+    o[2 * a + 1] = centre_f16x2(and_or(w8, 0x00F000F0u, vmagic), 0xE480E480u);
+  }
 }
 
 template <int D>
@@ -254,7 +282,7 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   constexpr int SLOTS = 64 / LPT;      // tokens per wave step
   constexpr int CP = D / 2;            // channel pairs
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int slot = lane / LPT;
   const int g = lane % LPT;
   const int cp = lane % CP;
@@ -327,7 +355,7 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
                                               static_cast<uint32_t>(((r1 + 31) >> 5) - w_first) * 4);
   const uint32_t r0_bit = static_cast<uint32_t>(r0 & 31);
 
-  auto issue = [&](int64_t c, Int4Loads<D> &L) {
+  auto issue = [&](uint32_t c, Int4Loads<D> &L) {
     const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;      // local token
     L.kc = bload16(rk, tok * (D / 2) + g * 16);
     L.ks = bload4(rks, tok * (D / 8) + g * 4);
@@ -341,103 +369,108 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   // next NPF - 1 steps of that wave are in flight (the ring is unrolled so
   // every buffer stays in fixed registers).
   constexpr int NPF = 3;
-  const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
+  const uint32_t nsteps = (n + SLOTS - 1) / SLOTS;
   Int4Loads<D> ring[NPF];
 #pragma unroll
-  for (int jr = 0; jr < NPF; ++jr) issue(wave + jr * kWaves, ring[jr]);
-  for (int64_t cb = wave; cb < nsteps; cb += NPF * kWaves) {
-#pragma unroll
-    for (int jr = 0; jr < NPF; ++jr) {
-      const int64_t c = cb + jr * kWaves;
-      if (c >= nsteps) break;
-      Int4Loads<D> &cur = ring[jr];
-      const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
+  for (int jr = 0; jr < NPF; ++jr) {
+    issue(wave + jr * kWaves, ring[jr]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: waits are counts
+  }
+  // one wave step over chunk c held in `cur`
+  auto step = [&](const uint32_t c, const Int4Loads<D> &cur) {
+    const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
 
-      // ---- q . k (k never dequantized: s * sum(q c) + z * sum(q))
-      float part[HB];
-      const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
-      if constexpr (QT == HQ_F32) {
+    // ---- q . k (k never dequantized: s * sum(q c) + z * sum(q))
+    float part[HB];
+    const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+    if constexpr (QT == HQ_F32) {
 #pragma unroll
-        for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
+      for (int hh = 0; hh < HB; ++hh) part[hh] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float cv = static_cast<float>((w[j] >> (4 * e)) & 15u);
+        for (int e = 0; e < 8; ++e) {
+          const float cv = static_cast<float>((w[j] >> (4 * e)) & 15u);
 #pragma unroll
-            for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(qf[hh][8 * j + e], cv, part[hh]);
-          }
-      } else {
+          for (int hh = 0; hh < HB; ++hh) part[hh] = fmaf(qf[hh][8 * j + e], cv, part[hh]);
+        }
+    } else {
 #pragma unroll
-        for (int hh = 0; hh < HB; ++hh) part[hh] = negmq[hh];
+      for (int hh = 0; hh < HB; ++hh) part[hh] = negmq[hh];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t x0 = and_or(w[j], 0x000F000Fu, magic);
-          const uint32_t x1 = and_or(w[j] >> 4, 0x000F000Fu, magic);
-          const uint32_t x2 = and_or(w[j] >> 8, 0x000F000Fu, magic);
-          const uint32_t x3 = and_or(w[j] >> 12, 0x000F000Fu, magic);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t x0 = and_or(w[j], 0x000F000Fu, magic);
+        const uint32_t x1 = and_or(w[j] >> 4, 0x000F000Fu, magic);
+        const uint32_t x2 = and_or(w[j] >> 8, 0x000F000Fu, magic);
+        const uint32_t x3 = and_or(w[j] >> 12, 0x000F000Fu, magic);
 #pragma unroll
-          for (int hh = 0; hh < HB; ++hh) {
-            part[hh] = dot2_q<QT>(qp[hh][j][0], x0, part[hh]);
-            part[hh] = dot2_q<QT>(qp[hh][j][1], x1, part[hh]);
-            part[hh] = dot2_q<QT>(qp[hh][j][2], x2, part[hh]);
-            part[hh] = dot2_q<QT>(qp[hh][j][3], x3, part[hh]);
-          }
+        for (int hh = 0; hh < HB; ++hh) {
+          part[hh] = dot2_q<QT>(qp[hh][j][0], x0, part[hh]);
+          part[hh] = dot2_q<QT>(qp[hh][j][1], x1, part[hh]);
+          part[hh] = dot2_q<QT>(qp[hh][j][2], x2, part[hh]);
+          part[hh] = dot2_q<QT>(qp[hh][j][3], x3, part[hh]);
         }
       }
-      const float ssc = lo_f16(cur.ks) * P.cs;
-      const float zsc = hi_f16(cur.ks) * P.cs;
-      const bool live = (tok < n) && !((cur.bits >> ((r0_bit + tok) & 31)) & 1u);
-      float lg[HB];
-      bool exceed = false;
+    }
+    const float ssc = lo_f16(cur.ks) * P.cs;
+    const float zsc = hi_f16(cur.ks) * P.cs;
+    const bool live = (tok < n) && !((cur.bits >> ((r0_bit + tok) & 31)) & 1u);
+    float lg[HB];
+    bool exceed = false;
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        const float v = token_sum<LPT>(fmaf(ssc, part[hh], zsc * qsum[hh]));
-        lg[hh] = live ? v : kNegInf;
-        exceed |= lg[hh] > st.m[hh];
-      }
-      if (__ballot(exceed)) raise_max<HB, LPT>(lg, st, zl);
+    for (int hh = 0; hh < HB; ++hh) {
+      const float v = token_sum<LPT>(fmaf(ssc, part[hh], zsc * qsum[hh]));
+      lg[hh] = live ? v : kNegInf;
+      exceed |= lg[hh] > st.m[hh];
+    }
+    if (__ballot(exceed)) raise_max<HB, LPT>(lg, st, zl);
 
-      // V scale and the zero point of the centred codes, z + 8 s; zero for
-      // masked tokens (their planes may hold anything, NaN included)
-      const float sv = live ? lo_f16(cur.vs) : 0.f;
-      const float zv = live ? fmaf(8.f, lo_f16(cur.vs), hi_f16(cur.vs)) : 0.f;
-      _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
+    // V scale and the zero point of the centred codes, z + 8 s; zero for
+    // masked tokens (their planes may hold anything, NaN included)
+    const float sv = live ? lo_f16(cur.vs) : 0.f;
+    const float zv = live ? fmaf(8.f, lo_f16(cur.vs), hi_f16(cur.vs)) : 0.f;
+    _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        const float mu = (st.m[hh] == kNegInf) ? 0.f : st.m[hh];
-        const float p = fast_exp2(lg[hh] - mu);
-        st.l[hh] += p;
-        zl[hh] = fmaf(p, zv, zl[hh]);
-        psh[(hh * LPT + g) * 32 + slot] = static_cast<_Float16>(p * sv);
-      }
-      wave_sync();
+    for (int hh = 0; hh < HB; ++hh) {
+      const float mu = (st.m[hh] == kNegInf) ? 0.f : st.m[hh];
+      const float p = fast_exp2(lg[hh] - mu);
+      st.l[hh] += p;
+      zl[hh] = fmaf(p, zv, zl[hh]);
+      psh[(hh * LPT + g) * 32 + slot] = static_cast<_Float16>(p * sv);
+    }
+    wave_sync();
 
-      // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
-      const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
-      uint32_t e[8], o[8];
+    // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
+    const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
+    uint32_t e[8], o[8];
+    unpack_v_tile(vw, vmagic, e, o);
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16 + 8 * sub]);
+      const uint4 pa = src[0], pb = src[1];
+      const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t x = __builtin_amdgcn_perm(0u, vw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
-        // (1024 + c) - 1032 = c - 8 and (1024 + 16 c) - 1152 = 16 (c - 8), exact in fp16
-        e[i] = centre_f16x2(and_or(x, 0x000F000Fu, vmagic), 0xE408E408u);
-        o[i] = centre_f16x2(and_or(x, 0x00F000F0u, vmagic), 0xE480E480u);
+        st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
+        st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
       }
+    }
+  };
+  // full groups of NPF steps: every refill is issued unconditionally (past
+  // the split the buffer loads return 0), so each wait for the oldest ring
+  // entry is a fixed count on every path into the loop
+  uint32_t cb = wave;
+  for (; cb + (NPF - 1) * kWaves < nsteps; cb += NPF * kWaves) {
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16 + 8 * sub]);
-        const uint4 pa = src[0], pb = src[1];
-        const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
-          st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
-        }
-      }
-      wave_sync();
-      if (c + NPF * kWaves < nsteps) issue(c + NPF * kWaves, ring[jr]);
+    for (int jr = 0; jr < NPF; ++jr) {
+      step(cb + jr * kWaves, ring[jr]);
+      issue(cb + jr * kWaves + NPF * kWaves, ring[jr]);
     }
   }
+  // the last NPF - 1 steps at most
+#pragma unroll
+  for (int jr = 0; jr < NPF - 1; ++jr)
+    if (cb + jr * kWaves < nsteps) step(cb + jr * kWaves, ring[jr]);
 
   // ---- per-(head, group) zero-point sums, folded into the accumulators
 #pragma unroll
@@ -480,24 +513,74 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
                                    int64_t r0, int64_t r1, WaveState<4> &st) {
   constexpr int D = 128, HB = 4, LPT = 4, SLOTS = 16, CP = 64;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int slot = lane >> 2;
   const int g = lane & 3;
   const int cp = lane;                 // P.V lane: channel pair
   const int gp = cp >> 4;
   const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
-
-  // query pairs of this lane's group for head g ^ j in register j
-  uint32_t qp[4][4][4];
-  float cqs[4];          // cs * sum of the group's query channels, head g ^ j
-  float negmq[4];        // -MAGIC * that sum (start of each dot chain)
   constexpr uint32_t kMagic = (QT == HQ_BF16) ? 0x43004300u : 0x64006400u;
   constexpr float kMagicVal = (QT == HQ_BF16) ? 128.f : 1024.f;
+
+  // raw query channels of this lane's group for head g ^ j, loaded before the
+  // ring so that their wait does not cover the ring's loads
+  uint32_t qraw[4][16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    load_q32<QT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32, qraw[j]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t magic = kMagic;
+  const uint32_t vmagic = 0x64006400u;
+  float zl[4] = {0.f, 0.f, 0.f, 0.f};   // sum p_h (z + 8 s) of this lane's group, head h
+  float lown = 0.f;                      // sum of p of head g (this lane's head)
+  // running max of head g; starts finite, so p = 2^(l - m) needs no guard
+  // (a live logit above it always takes the rescale first)
+  float mown = -__FLT_MAX__;
+
+  // Each chunk gets its own buffer views, built in SGPRs from wave-uniform
+  // offsets: the per-lane offsets below never change, so the loads need no
+  // vector address arithmetic, and a view past the end of the split is empty
+  // (its loads return 0). Splits start at multiples of 64 positions, so the
+  // VL bits of chunk c sit in word c / 2 at bit 16 (c % 2) + slot, and c % 2
+  // equals wave % 2 for every chunk of this wave.
+  const uint32_t n = static_cast<uint32_t>(r1 - r0);
+  const int64_t row0 = head * P.t_cap + r0;
+  const uint8_t *kb = P.k_codes + row0 * (D / 2);
+  const uint8_t *ksb = reinterpret_cast<const uint8_t *>(P.k_sz + row0 * (D / 32));
+  const uint8_t *vsb = reinterpret_cast<const uint8_t *>(P.v_sz + row0 * (D / 32));
+  const uint8_t *vb = P.v_codes + row0 * (D / 2);
+  const uint8_t *bb = reinterpret_cast<const uint8_t *>(P.vl_bits + head * P.bits_words + (r0 >> 5));
+  const uint32_t nk = n * (D / 2), ns = n * (D / 8), nv = ((n + 15) / 16) * (CP * 16);
+  const uint32_t nb = ((n + 31) >> 5) * 4;
+  const uint32_t lo_k = slot * (D / 2) + g * 16;
+  const uint32_t lo_s = slot * (D / 8) + g * 4;
+  const uint32_t lo_v = cp * 16;
+  const uint32_t bitpos = (wave & 1) * 16 + slot;
+
+  auto issue = [&](uint32_t c, Int4Loads<D> &L) {
+    const uint32_t os = c * (SLOTS * D / 8);
+    L.kc = bload16(view(kb, nk, c * (SLOTS * D / 2)), lo_k);
+    L.ks = bload4(view(ksb, ns, os), lo_s);
+    L.vs = bload4(view(vsb, ns, os), lo_s);
+    L.bits = bload4(view(bb, nb, (c >> 1) * 4), 0);
+    L.vc = bload16(view(vb, nv, c * (CP * 16)), lo_v);
+  };
+
+  constexpr int NPF = 6;
+  const uint32_t nsteps = (n + SLOTS - 1) / SLOTS;
+  Int4Loads<D> ring[NPF];
+#pragma unroll
+  for (int jr = 0; jr < NPF; ++jr) {
+    issue(wave + jr * kWaves, ring[jr]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: waits are counts
+  }
+  // query pairs (register j: head g ^ j) while the ring's first loads fly
+  uint32_t qp[4][4][4];
+  float cqs[4];          // cs * sum of the group's query channels, head g ^ j
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t qoff = (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32;
-    uint32_t raw[16];
-    load_q32<QT>(P.q, qoff, raw);
+    const uint32_t (&raw)[16] = qraw[j];
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < 16; ++c)
@@ -512,143 +595,115 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
         qp[j][w][m] = lo | (hi << 16);
       }
     cqs[j] = P.cs * s;
-    negmq[j] = -kMagicVal * s;
   }
-  const uint32_t magic = kMagic;
-  const uint32_t vmagic = 0x64006400u;
-  float zl[4] = {0.f, 0.f, 0.f, 0.f};   // sum p_h (z + 8 s) of this lane's group, head h
-  float lown = 0.f;                      // sum of p of head g (this lane's head)
-  float mown = kNegInf;                  // running max of head g
-
-  const uint32_t n = static_cast<uint32_t>(r1 - r0);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k_codes + (head * P.t_cap + r0) * (D / 2), n * (D / 2));
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(P.k_sz + (head * P.t_cap + r0) * (D / 32), n * (D / 8));
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(P.v_sz + (head * P.t_cap + r0) * (D / 32), n * (D / 8));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v_codes + (head * P.t_cap + r0) * (D / 2),
-                                              ((n + 15) / 16) * (CP * 16));
-  const uint32_t w_first = static_cast<uint32_t>(r0 >> 5);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(P.vl_bits + head * P.bits_words + w_first,
-                                              static_cast<uint32_t>(((r1 + 31) >> 5) - w_first) * 4);
-  const uint32_t r0_bit = static_cast<uint32_t>(r0 & 31);
-
-  auto issue = [&](int64_t c, Int4Loads<D> &L) {
-    const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
-    L.kc = bload16(rk, tok * (D / 2) + g * 16);
-    L.ks = bload4(rks, tok * (D / 8) + g * 4);
-    L.vs = bload4(rvs, tok * (D / 8) + g * 4);
-    L.bits = bload4(rb, ((r0_bit + tok) >> 5) * 4);
-    L.vc = bload16(rv, static_cast<uint32_t>(c) * (CP * 16) + cp * 16);
-  };
-
-  constexpr int NPF = 3;
-  const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
-  Int4Loads<D> ring[NPF];
-#pragma unroll
-  for (int jr = 0; jr < NPF; ++jr) issue(wave + jr * kWaves, ring[jr]);
   _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
-  for (int64_t cb = wave; cb < nsteps; cb += NPF * kWaves) {
-#pragma unroll
-    for (int jr = 0; jr < NPF; ++jr) {
-      const int64_t c = cb + jr * kWaves;
-      if (c >= nsteps) break;
-      Int4Loads<D> &cur = ring[jr];
-      const uint32_t tok = static_cast<uint32_t>(c) * SLOTS + slot;
+  // one wave step over chunk c held in `cur`
+  auto step = [&](const uint32_t c, const Int4Loads<D> &cur) {
 
-      // ---- q . k over this lane's group, head g ^ j in part[j]
-      float part[4];
+    // ---- q . k over this lane's group, head g ^ j in part[j]; the chains
+    // carry the MAGIC offset, MAGIC * sum q, which is removed with the zero point
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[j] = negmq[j];
-      const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+    for (int ww = 0; ww < 4; ++ww) {
+      const uint32_t x0 = and_or(w[ww], 0x000F000Fu, magic);
+      const uint32_t x1 = and_or(w[ww] >> 4, 0x000F000Fu, magic);
+      const uint32_t x2 = and_or(w[ww] >> 8, 0x000F000Fu, magic);
+      const uint32_t x3 = and_or(w[ww] >> 12, 0x000F000Fu, magic);
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const uint32_t x0 = and_or(w[ww], 0x000F000Fu, magic);
-        const uint32_t x1 = and_or(w[ww] >> 4, 0x000F000Fu, magic);
-        const uint32_t x2 = and_or(w[ww] >> 8, 0x000F000Fu, magic);
-        const uint32_t x3 = and_or(w[ww] >> 12, 0x000F000Fu, magic);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          part[j] = dot2_q<QT>(qp[j][ww][0], x0, part[j]);
-          part[j] = dot2_q<QT>(qp[j][ww][1], x1, part[j]);
-          part[j] = dot2_q<QT>(qp[j][ww][2], x2, part[j]);
-          part[j] = dot2_q<QT>(qp[j][ww][3], x3, part[j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        part[j] = dot2_q<QT>(qp[j][ww][0], x0, part[j]);
+        part[j] = dot2_q<QT>(qp[j][ww][1], x1, part[j]);
+        part[j] = dot2_q<QT>(qp[j][ww][2], x2, part[j]);
+        part[j] = dot2_q<QT>(qp[j][ww][3], x3, part[j]);
       }
-      // scaled group partials: cs * (s * dot + z * sum q)
-      const float ssc = lo_f16(cur.ks) * P.cs;
-      const float zk = hi_f16(cur.ks);
+    }
+    // scaled group partials: cs (s (dot - MAGIC sum q) + z sum q)
+    //                        = (cs s) dot + (cs sum q)(z - MAGIC s)
+    const float ssc = lo_f16(cur.ks) * P.cs;
+    const float zm = fmaf(-kMagicVal, lo_f16(cur.ks), hi_f16(cur.ks));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[j] = fmaf(zk, cqs[j], part[j] * ssc);
-      // quad reduce-scatter: lane g ends with head g summed over the 4 groups
-      const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
-      const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
-      const float lgv = y0 + dpp_f<kQuadXor1>(y1);
-      const bool live = (tok < n) && !((cur.bits >> ((r0_bit + tok) & 31)) & 1u);
-      const float lg = live ? lgv : kNegInf;
+    for (int j = 0; j < 4; ++j) part[j] = fmaf(ssc, part[j], cqs[j] * zm);
+    // quad reduce-scatter: lane g ends with head g summed over the 4 groups
+    const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
+    const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
+    const float lgv = y0 + dpp_f<kQuadXor1>(y1);
+    const bool live = (slot < n - c * SLOTS) && !((cur.bits >> bitpos) & 1u);
+    const float lg = live ? lgv : kNegInf;
 
-      if (__ballot(lg > mown)) {
-        // slow path: new wave max of head g; rescale every running quantity
-        const float mx = slots_max<LPT>(lg);
-        const float mn = fmaxf(mown, mx);
-        const float mu = (mn == kNegInf) ? 0.f : mn;
-        const float alpha = fast_exp2(mown - mu);          // of head g
-        mown = mn;
-        lown *= alpha;
-        zl[0] = dpp_mul<kQuadBcast[0]>(alpha, zl[0]);
-        zl[1] = dpp_mul<kQuadBcast[1]>(alpha, zl[1]);
-        zl[2] = dpp_mul<kQuadBcast[2]>(alpha, zl[2]);
-        zl[3] = dpp_mul<kQuadBcast[3]>(alpha, zl[3]);
-        // the P.V lanes hold channels of every head: alpha of head hh from lane hh
-        const float a0 = __shfl(alpha, 0, 64), a1 = __shfl(alpha, 1, 64);
-        const float a2 = __shfl(alpha, 2, 64), a3 = __shfl(alpha, 3, 64);
-        st.acc_e[0] *= a0; st.acc_o[0] *= a0;
-        st.acc_e[1] *= a1; st.acc_o[1] *= a1;
-        st.acc_e[2] *= a2; st.acc_o[2] *= a2;
-        st.acc_e[3] *= a3; st.acc_o[3] *= a3;
-      }
-      const float p = fast_exp2(lg - ((mown == kNegInf) ? 0.f : mown));
-      lown += p;
-      // V scale and the zero point of the centred codes, z + 8 s; zero for
-      // masked tokens (their planes may hold anything, NaN included)
-      const float sv = live ? lo_f16(cur.vs) : 0.f;
-      const float zv = live ? fmaf(8.f, lo_f16(cur.vs), hi_f16(cur.vs)) : 0.f;
-      const float ps0 = dpp_mul<kQuadBcast[0]>(p, sv);
-      const float ps1 = dpp_mul<kQuadBcast[1]>(p, sv);
-      const float ps2 = dpp_mul<kQuadBcast[2]>(p, sv);
-      const float ps3 = dpp_mul<kQuadBcast[3]>(p, sv);
-      zl[0] = fmaf(dpp_f<kQuadBcast[0]>(p), zv, zl[0]);
-      zl[1] = fmaf(dpp_f<kQuadBcast[1]>(p), zv, zl[1]);
-      zl[2] = fmaf(dpp_f<kQuadBcast[2]>(p), zv, zl[2]);
-      zl[3] = fmaf(dpp_f<kQuadBcast[3]>(p), zv, zl[3]);
-      psh[(0 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps0);
-      psh[(1 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps1);
-      psh[(2 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps2);
-      psh[(3 * LPT + g) * 32 + slot] = static_cast<_Float16>(ps3);
-      wave_sync();
+    if (__builtin_expect(__ballot(lg > mown) != 0, 0)) {
+      // slow path: new wave max of head g; rescale every running quantity
+      const float mx = slots_max<LPT>(lg);
+      const float mn = fmaxf(mown, mx);
+      const float alpha = fast_exp2(mown - mn);          // of head g
+      mown = mn;
+      lown *= alpha;
+      zl[0] = dpp_mul<kQuadBcast[0]>(alpha, zl[0]);
+      zl[1] = dpp_mul<kQuadBcast[1]>(alpha, zl[1]);
+      zl[2] = dpp_mul<kQuadBcast[2]>(alpha, zl[2]);
+      zl[3] = dpp_mul<kQuadBcast[3]>(alpha, zl[3]);
+      // the P.V lanes hold channels of every head: alpha of head hh from lane hh
+      const float a0 = __shfl(alpha, 0, 64), a1 = __shfl(alpha, 1, 64);
+      const float a2 = __shfl(alpha, 2, 64), a3 = __shfl(alpha, 3, 64);
+      st.acc_e[0] *= a0; st.acc_o[0] *= a0;
+      st.acc_e[1] *= a1; st.acc_o[1] *= a1;
+      st.acc_e[2] *= a2; st.acc_o[2] *= a2;
+      st.acc_e[3] *= a3; st.acc_o[3] *= a3;
+    }
+    const float p = fast_exp2(lg - mown);
+    lown += p;
+    // V scale and the zero point of the centred codes, z + 8 s; zero for
+    // masked tokens (their planes may hold anything, NaN included)
+    const uint32_t vsw = live ? cur.vs : 0u;
+    const float sv = lo_f16(vsw);
+    const float zv = fmaf(8.f, sv, hi_f16(vsw));
+    const float ps0 = dpp_mul<kQuadBcast[0]>(p, sv);
+    const float ps1 = dpp_mul<kQuadBcast[1]>(p, sv);
+    const float ps2 = dpp_mul<kQuadBcast[2]>(p, sv);
+    const float ps3 = dpp_mul<kQuadBcast[3]>(p, sv);
+    zl[0] = fmaf(dpp_f<kQuadBcast[0]>(p), zv, zl[0]);
+    zl[1] = fmaf(dpp_f<kQuadBcast[1]>(p), zv, zl[1]);
+    zl[2] = fmaf(dpp_f<kQuadBcast[2]>(p), zv, zl[2]);
+    zl[3] = fmaf(dpp_f<kQuadBcast[3]>(p), zv, zl[3]);
+    const uint32_t ps01 = pack_f16_rne(ps0, ps1), ps23 = pack_f16_rne(ps2, ps3);
+    uint16_t *psw = reinterpret_cast<uint16_t *>(psh);
+    psw[(0 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps01);
+    psw[(1 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps01 >> 16);
+    psw[(2 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps23);
+    psw[(3 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps23 >> 16);
+    wave_sync();
 
-      // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
-      const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
-      uint32_t e[8], o[8];
+    // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
+    const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
+    uint32_t e[8], o[8];
+    unpack_v_tile(vw, vmagic, e, o);
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16]);
+      const uint4 pa = src[0], pb = src[1];
+      const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t x = __builtin_amdgcn_perm(0u, vw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
-        e[i] = centre_f16x2(and_or(x, 0x000F000Fu, vmagic), 0xE408E408u);
-        o[i] = centre_f16x2(and_or(x, 0x00F000F0u, vmagic), 0xE480E480u);
+        st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
+        st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
       }
+    }
+  };
+  // full groups of NPF steps: every refill is issued unconditionally (past
+  // the split the buffer loads return 0), so each wait for the oldest ring
+  // entry is a fixed count on every path into the loop
+  uint32_t cb = wave;
+  for (; cb + (NPF - 1) * kWaves < nsteps; cb += NPF * kWaves) {
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16]);
-        const uint4 pa = src[0], pb = src[1];
-        const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
-          st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
-        }
-      }
-      wave_sync();
-      if (c + NPF * kWaves < nsteps) issue(c + NPF * kWaves, ring[jr]);
+    for (int jr = 0; jr < NPF; ++jr) {
+      step(cb + jr * kWaves, ring[jr]);
+      issue(cb + jr * kWaves + NPF * kWaves, ring[jr]);
     }
   }
+  // the last NPF - 1 steps at most
+#pragma unroll
+  for (int jr = 0; jr < NPF - 1; ++jr)
+    if (cb + jr * kWaves < nsteps) step(cb + jr * kWaves, ring[jr]);
 
   // ---- per-(head, group) zero-point sums, folded into the accumulators; the
   // wave state of head hh lives in lane hh's quad position
@@ -701,7 +756,7 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
   constexpr int EB = (HT == HQ_F32) ? 4 : 2;
   using L = FpLoads<HT>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int slot = lane / LPT;
   const int g = lane % LPT;
   const int cp = lane % CP;
@@ -761,9 +816,11 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
 
   const int64_t nsteps = (r1 - r0 + SLOTS - 1) / SLOTS;
   L cur, nxt;
-  if (wave < nsteps) issue(wave, cur);
+  // row indices are clamped to the split, so every issue is in bounds and
+  // needs no condition
+  issue(wave, cur);
   for (int64_t c = wave; c < nsteps; c += kWaves) {
-    if (c + kWaves < nsteps) issue(c + kWaves, nxt);
+    issue(c + kWaves, nxt);
     const int64_t f0 = r0 + c * SLOTS;
     const bool tv = f0 + slot < r1;
     float part[HB];
@@ -836,6 +893,164 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
   }
 }
 
+// ---------------------------------------------------------------- 16-bit pass, D = 128, 4 heads
+// Specialisation of the 16-bit pass for head_dim 128, a chunk of 4 query
+// heads and 16-bit rows. A split holds either VL rows (a contiguous block of
+// vl_k / vl_v) or window rows (the ring), never both, so the chunk type is
+// wave-uniform. Lane (slot, g) dots its row's 32 channels of group g with the
+// query of head g ^ j in register j; the quad reduce-scatter of the INT4 pass
+// then leaves head g's logit in lane g, so one exponential per lane suffices.
+// P . V: lane cp accumulates channels (2cp, 2cp+1) of all 4 heads over the 16
+// rows, weights read back from LDS in fp32 (these rows carry the largest
+// attention weights, so the weights are not rounded).
+struct FpRing {
+  u32x4 k[4];                 // 32 key channels of this lane's (row, group)
+  uint32_t v[16];             // value channel pair cp of the chunk's 16 rows
+};
+
+template <int HT, bool WIN>
+__device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int h, int i0,
+                                int64_t r0, int64_t r1, WaveState<4> &st) {
+  constexpr int D = 128, LPT = 4, SLOTS = 16, RB = D * 2;   // RB: bytes per row
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = lane >> 2;
+  const int g = lane & 3;
+  const int cp = lane;
+  const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
+
+  // natural query pairs (q[2i], q[2i+1]) of group g, head g ^ j in register j
+  uint32_t qn[4][16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    load_q32<HT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32, qn[j]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t n = static_cast<uint32_t>(r1 - r0);
+  const uint8_t *kbase, *vbase;
+  uint32_t kbytes;
+  int wrow0 = 0;
+  if constexpr (!WIN) {
+    // rows [r0, r1) of the head's VL block; views past r1 read as 0
+    kbase = static_cast<const uint8_t *>(P.vl_k) + (head * P.k + r0) * RB;
+    vbase = static_cast<const uint8_t *>(P.vl_v) + (head * P.k + r0) * RB;
+    kbytes = n * RB;
+  } else {
+    // the head's ring of W rows; list row k + w is ring row (win_offset + w) mod W
+    kbase = static_cast<const uint8_t *>(P.win_k) + head * P.W * RB;
+    vbase = static_cast<const uint8_t *>(P.win_v) + head * P.W * RB;
+    kbytes = static_cast<uint32_t>(P.W) * RB;
+    wrow0 = P.win_offset + static_cast<int>(r0 - P.k);      // ring row of the split's first row, < 2 W
+  }
+  auto ring_row = [&](int w) {                                // w < 3 W
+    w -= (w >= P.W) ? P.W : 0;
+    w -= (w >= P.W) ? P.W : 0;
+    return w;
+  };
+
+  auto issue = [&](uint32_t c, FpRing &L) {
+    const uint32_t f = c * SLOTS;                              // first row of the chunk in the split
+    if constexpr (!WIN) {
+      const __amdgpu_buffer_rsrc_t rk = view(kbase, kbytes, f * RB);
+      const __amdgpu_buffer_rsrc_t rv = view(vbase, kbytes, f * RB);
+      const uint32_t ko = slot * RB + g * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.k[i] = bload16(rk, ko + 16 * i);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) L.v[r] = bload4(rv, cp * 4 + r * RB);
+    } else {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, kbytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, kbytes);
+      const uint32_t ko = static_cast<uint32_t>(ring_row(wrow0 + static_cast<int>(f) + slot)) * RB + g * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.k[i] = bload16(rk, ko + 16 * i);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        L.v[r] = bload4(rv, cp * 4 + static_cast<uint32_t>(ring_row(wrow0 + static_cast<int>(f) + r)) * RB);
+    }
+  };
+
+  constexpr int NPF = 2;
+  const uint32_t nsteps = (n + SLOTS - 1) / SLOTS;
+  FpRing ring[NPF];
+#pragma unroll
+  for (int jr = 0; jr < NPF; ++jr) {
+    issue(wave + jr * kWaves, ring[jr]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float mown = -__FLT_MAX__;            // running max of head g (finite: see the INT4 pass)
+  float lown = 0.f;
+  float *pw = &sm.p[wave][0];           // [head][32] fp32 weights of the chunk
+
+  auto step = [&](const uint32_t c, const FpRing &cur) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t kw[16] = {cur.k[0].x, cur.k[0].y, cur.k[0].z, cur.k[0].w,
+                             cur.k[1].x, cur.k[1].y, cur.k[1].z, cur.k[1].w,
+                             cur.k[2].x, cur.k[2].y, cur.k[2].z, cur.k[2].w,
+                             cur.k[3].x, cur.k[3].y, cur.k[3].z, cur.k[3].w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[j] = dot2_q<HT>(qn[j][e], kw[e], part[j]);
+    const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
+    const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
+    const float lgv = (y0 + dpp_f<kQuadXor1>(y1)) * P.cs;
+    const bool live = slot < n - c * SLOTS;
+    const float lg = live ? lgv : kNegInf;
+    if (__builtin_expect(__ballot(lg > mown) != 0, 0)) {
+      const float mx = slots_max<LPT>(lg);
+      const float mn = fmaxf(mown, mx);
+      const float alpha = fast_exp2(mown - mn);
+      mown = mn;
+      lown *= alpha;
+      const float a0 = __shfl(alpha, 0, 64), a1 = __shfl(alpha, 1, 64);
+      const float a2 = __shfl(alpha, 2, 64), a3 = __shfl(alpha, 3, 64);
+      st.acc_e[0] *= a0; st.acc_o[0] *= a0;
+      st.acc_e[1] *= a1; st.acc_o[1] *= a1;
+      st.acc_e[2] *= a2; st.acc_o[2] *= a2;
+      st.acc_e[3] *= a3; st.acc_o[3] *= a3;
+    }
+    const float p = fast_exp2(lg - mown);
+    lown += p;
+    pw[g * 32 + slot] = p;
+    wave_sync();
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const float4 *pp = reinterpret_cast<const float4 *>(pw + hh * 32);
+      float pr[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f4 = pp[i];
+        pr[4 * i] = f4.x; pr[4 * i + 1] = f4.y; pr[4 * i + 2] = f4.z; pr[4 * i + 3] = f4.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.acc_e[hh] = fmaf(pr[r], half_bits_to_f32<HT>(cur.v[r] & 0xFFFFu), st.acc_e[hh]);
+        st.acc_o[hh] = fmaf(pr[r], half_bits_to_f32<HT>(cur.v[r] >> 16), st.acc_o[hh]);
+      }
+    }
+    wave_sync();
+  };
+  uint32_t cb = wave;
+  for (; cb + (NPF - 1) * kWaves < nsteps; cb += NPF * kWaves) {
+#pragma unroll
+    for (int jr = 0; jr < NPF; ++jr) {
+      step(cb + jr * kWaves, ring[jr]);
+      issue(cb + jr * kWaves + NPF * kWaves, ring[jr]);
+    }
+  }
+#pragma unroll
+  for (int jr = 0; jr < NPF - 1; ++jr)
+    if (cb + jr * kWaves < nsteps) step(cb + jr * kWaves, ring[jr]);
+
+  const float lsum = xor_sum<LPT>(lown);
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    st.m[hh] = __shfl(mown, hh, 64);
+    st.l[hh] = __shfl(lsum, hh, 64);
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
 template <int D, int HB, int QT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
@@ -854,7 +1069,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   const int i0 = h * P.G + hc * HB;           // first query head of this block
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
 
   WaveState<HB> st;
 #pragma unroll
@@ -872,10 +1087,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     else
       int4_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
   } else {
-    const int64_t nfp = static_cast<int64_t>(P.k) + P.W;
-    const int64_t r0 = static_cast<int64_t>(split - P.S_q) * P.len_fp;
-    const int64_t r1 = r0 + P.len_fp < nfp ? r0 + P.len_fp : nfp;
-    fp_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
+    // rows [r0, r1) of the 16-bit list (VL rows 0..k-1, then the W window
+    // rows); a split lies entirely in one of the two parts
+    int64_t r0, r1;
+    const bool win = split >= P.S_q + P.S_vl;
+    if (!win) {
+      r0 = static_cast<int64_t>(split - P.S_q) * P.len_vl;
+      r1 = r0 + P.len_vl < P.k ? r0 + P.len_vl : P.k;
+    } else {
+      r0 = P.k + static_cast<int64_t>(split - P.S_q - P.S_vl) * P.len_win;
+      r1 = r0 + P.len_win < static_cast<int64_t>(P.k) + P.W ? r0 + P.len_win : static_cast<int64_t>(P.k) + P.W;
+    }
+    if constexpr (D == 128 && HB == 4 && QT != HQ_F32) {
+      if (win) fp_rows_d128_g4<QT, true>(P, sm, b, h, i0, r0, r1, st);
+      else fp_rows_d128_g4<QT, false>(P, sm, b, h, i0, r0, r1, st);
+    } else {
+      fp_split<D, HB, QT>(P, sm, b, h, i0, r0, r1, st);
+    }
   }
 
   // ---- combine the 4 waves
@@ -1009,9 +1237,9 @@ __global__ __launch_bounds__(256) void vl_bitmap_kernel(const int32_t *__restric
 
 // ---------------------------------------------------------------- planning
 struct Plan {
-  int nhc, HB, units, S_q, S_fp, S;
+  int nhc, HB, units, S_q, S_vl, S_win, S;
   int64_t len_q;
-  int len_fp;
+  int len_vl, len_win;
   int64_t nq;
 };
 
@@ -1023,26 +1251,33 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
   pl.HB = G >= 4 ? 4 : G;
   pl.nhc = G / pl.HB;
   pl.units = kv->B * kv->Hkv * pl.nhc;
-  const int step = 64 / (kv->D / 32);
+  const int step = 64 / (kv->D / 32);                         // positions per wave step
+  const int64_t gran = static_cast<int64_t>(kWaves) * step;   // INT4 split granularity (64 or 128)
   pl.nq = kv->T - kv->W;
   const int64_t nfp = static_cast<int64_t>(kv->k) + kv->W;
-  const int hp_bytes = kv->hp_dtype == HQ_F32 ? 4 : 2;
-  const double bytes_q = static_cast<double>(pl.nq) * (kv->D + kv->D / 4);
-  const double bytes_fp = static_cast<double>(nfp) * 2.0 * kv->D * hp_bytes;
+  // Splits are sized by cost, not bytes: a 16-bit row costs about twice an
+  // INT4 position (fp32 P . V products and 3.2x the bytes, against the
+  // unpacking of the codes).
+  constexpr double kFpRowCost = 2.0;
+  const double cost_q = static_cast<double>(pl.nq);
+  const double cost_fp = kFpRowCost * static_cast<double>(nfp);
   int S = n_splits;
   if (S <= 0) {
-    const int target_blocks = 512;
+    // one generation of 512 blocks fills the chip; long contexts get four,
+    // so that blocks finishing early are replaced and the tail stays short
+    const double steps_per_wave = (cost_q + cost_fp) / step * pl.units / (512.0 * kWaves);
+    const int target_blocks = steps_per_wave >= 128.0 ? 2048 : 512;
     S = static_cast<int>(ceil_div(target_blocks, pl.units));
     // at least ~4 wave steps of work per wave
-    const int64_t max_s = ceil_div(pl.nq + nfp, 16LL * step) ;
+    const int64_t max_s = ceil_div(pl.nq + nfp, 16LL * step);
     if (S > max_s) S = static_cast<int>(max_s > 0 ? max_s : 1);
     if (S > kMaxSplits) S = kMaxSplits;
     if (S < 1) S = 1;
   }
+  // 16-bit splits: rounded up, so that none costs more than an average split
   int s_fp = 0;
   if (nfp > 0) {
-    const double frac = bytes_fp / (bytes_q + bytes_fp);
-    s_fp = static_cast<int>(frac * S + 0.5);
+    s_fp = static_cast<int>(std::ceil(cost_fp / (cost_q + cost_fp) * S - 1e-9));
     if (s_fp < 1) s_fp = 1;
     const int64_t mx = ceil_div(nfp, step);
     if (s_fp > mx) s_fp = static_cast<int>(mx);
@@ -1054,14 +1289,28 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
     // the VL bitmap and the ranges: at most 2^20 positions per split
     const int64_t mn = ceil_div(pl.nq, 1LL << 20);
     if (s_q < mn) s_q = static_cast<int>(mn);
-    const int64_t mx = ceil_div(pl.nq, step);
+    const int64_t mx = ceil_div(pl.nq, gran);
     if (s_q > mx) s_q = static_cast<int>(mx);
   }
-  pl.len_q = s_q > 0 ? ceil_div(ceil_div(pl.nq, s_q), step) * step : 0;
+  // INT4 splits start at multiples of gran (a multiple of 64): the kernel
+  // reads the VL bits of a chunk from one aligned bitmap word
+  pl.len_q = s_q > 0 ? ceil_div(ceil_div(pl.nq, s_q), gran) * gran : 0;
   pl.S_q = s_q > 0 ? static_cast<int>(ceil_div(pl.nq, pl.len_q)) : 0;
-  pl.len_fp = s_fp > 0 ? static_cast<int>(ceil_div(ceil_div(nfp, s_fp), step) * step) : 0;
-  pl.S_fp = s_fp > 0 ? static_cast<int>(ceil_div(nfp, pl.len_fp)) : 0;
-  pl.S = pl.S_q + pl.S_fp;
+  // the 16-bit splits divided between the VL rows and the window rows
+  int s_win = 0, s_vl = 0;
+  if (s_fp > 0) {
+    if (kv->W > 0) {
+      s_win = static_cast<int>(static_cast<double>(s_fp) * kv->W / nfp + 0.5);
+      if (s_win < 1) s_win = 1;
+    }
+    s_vl = kv->k > 0 ? s_fp - s_win : 0;
+    if (kv->k > 0 && s_vl < 1) s_vl = 1;
+  }
+  pl.len_vl = s_vl > 0 ? static_cast<int>(ceil_div(ceil_div(kv->k, s_vl), step) * step) : 0;
+  pl.S_vl = s_vl > 0 ? static_cast<int>(ceil_div(kv->k, pl.len_vl)) : 0;
+  pl.len_win = s_win > 0 ? static_cast<int>(ceil_div(ceil_div(kv->W, s_win), step) * step) : 0;
+  pl.S_win = s_win > 0 ? static_cast<int>(ceil_div(kv->W, pl.len_win)) : 0;
+  pl.S = pl.S_q + pl.S_vl + pl.S_win;
   return pl;
 }
 
@@ -1186,10 +1435,12 @@ extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, con
   P.G = Hq / kv->Hkv;
   P.nhc = pl.nhc;
   P.S_q = pl.S_q;
-  P.S_fp = pl.S_fp;
+  P.S_vl = pl.S_vl;
+  P.S_win = pl.S_win;
   P.S = pl.S;
   P.len_q = pl.len_q;
-  P.len_fp = pl.len_fp;
+  P.len_vl = pl.len_vl;
+  P.len_win = pl.len_win;
   P.units = pl.units;
   P.blocks_used = pl.units * pl.S;
   const int blocks = static_cast<int>(ceil_div(P.blocks_used, kNumXcd) * kNumXcd);

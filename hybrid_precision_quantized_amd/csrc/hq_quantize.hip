@@ -94,9 +94,12 @@ __device__ __forceinline__ void quantize_group(
     uint4 *dst = reinterpret_cast<uint4 *>(codes + head_row * (D / 2) + g * (kGroup / 2));
     *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   } else {
-    // tile u = row / 16 of head h; byte (j, row % 16) for channel pair j
+    // tile u = row / 16 of head h; byte (j, slot(row % 16)) for channel pair
+    // j, where each run of 4 rows is stored in the order 0, 2, 1, 3
     const int64_t tile = static_cast<int64_t>(h) * (dst_head_rows / 16) + row / 16;
-    uint8_t *base = codes + tile * (D / 2) * 16 + (row % 16);
+    const int r16 = static_cast<int>(row % 16);
+    const int slot16 = (r16 & ~3) | ((r16 & 1) << 1) | ((r16 >> 1) & 1);
+    uint8_t *base = codes + tile * (D / 2) * 16 + slot16;
 #pragma unroll
     for (int jj = 0; jj < kGroup / 2; ++jj) {
       const int j = g * (kGroup / 2) + jj;

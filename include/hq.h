@@ -38,10 +38,11 @@
  *  - codes, HQ_LAYOUT_ROWS: [rows][D/2] bytes, byte j of a row holds channel
  *    2j in its low nibble and channel 2j+1 in its high nibble (used for K).
  *  - codes, HQ_LAYOUT_TILE16: rows grouped in tiles of 16; tile u is a
- *    [D/2][16] byte block: byte (j, r) holds channels 2j (low nibble) and
- *    2j+1 (high nibble) of row 16u + r (used for V: one 16-byte load gives one
- *    channel pair of 16 consecutive tokens). The row capacity of a TILE16
- *    plane is a multiple of 16.
+ *    [D/2][16] byte block: byte (j, 4a + b) holds channels 2j (low nibble)
+ *    and 2j+1 (high nibble) of row 16u + 4a + (0, 2, 1, 3)[b] (used for V:
+ *    one 16-byte load gives one channel pair of 16 consecutive tokens, and
+ *    each 32-bit word holds rows (t, t+1) in its even bytes and (t+2, t+3) in
+ *    its odd bytes). The row capacity of a TILE16 plane is a multiple of 16.
  *  - scale/zero: [rows][D/group][2] fp16 bit patterns {scale, zero}.
  */
 #ifndef HQ_H_

@@ -41,8 +41,18 @@ def tile16_codes(plane: torch.Tensor) -> np.ndarray:
     """HQ_LAYOUT_TILE16 plane [..., rows/16, D/2, 16] -> [..., rows, D/2] bytes,
     following the layout stated in include/hq.h."""
     a = plane.cpu().numpy()
+    # byte slot 4a + b holds row 4a + (0, 2, 1, 3)[b]; that order is its own inverse
+    order = np.array([0, 2, 1, 3, 4, 6, 5, 7, 8, 10, 9, 11, 12, 14, 13, 15])
+    a = a[..., order]
     a = np.swapaxes(a, -1, -2)                     # [..., rows/16, 16, D/2]
     return a.reshape(a.shape[:-3] + (a.shape[-3] * 16, a.shape[-1]))
+
+
+def tile16_slot(r: int) -> int:
+    """Byte slot of row r % 16 inside its TILE16 tile (runs of 4 rows are
+    stored in the order 0, 2, 1, 3)."""
+    r %= 16
+    return (r & ~3) | ((r & 1) << 1) | ((r >> 1) & 1)
 
 
 def sz_bits(t: torch.Tensor) -> np.ndarray:

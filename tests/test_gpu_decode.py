@@ -15,7 +15,7 @@ import torch
 import hybrid_precision_quantized_amd as hq
 import synth
 from oracle import attention, detect, quant
-from tests.gpu_util import TORCH_DT, rel_err, say, to_dev, upload_kv
+from tests.gpu_util import TORCH_DT, rel_err, say, tile16_slot, to_dev, upload_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def _gpu_decode(w, K, V, q, vl, n_splits=0, win_offset=0, poison=False, repeat=1
                 cache.v_sz[b, h, rows] = torch.full((w.k, w.D // 32, 2), -1, dtype=torch.int16).cuda()
                 vt = cache.v_codes[b, h].view(-1, w.D // 2, 16)
                 for t in vl[b, h]:
-                    vt[t // 16, :, t % 16] = 0xFF
+                    vt[t // 16, :, tile16_slot(t)] = 0xFF
     kv = cache.descriptor()
     # the workspace needs no initialisation: start from garbage
     ws = torch.full((hq.hq_decode_workspace_size(kv, w.Hq, n_splits),), 0xFF, dtype=torch.uint8, device="cuda")
