@@ -256,6 +256,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
+            "traffic_unit": "bytes per hq_decode_attn call (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+            "traffic_over_algorithmic": (round(traffic / dec_bytes, 4) if traffic else None),
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "avg_launch_us": round(dec_us, 3),
         },
