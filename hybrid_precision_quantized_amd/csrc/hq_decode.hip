@@ -1144,17 +1144,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------- split merge
-// One block per (unit, query head): out = sum_s 2^(m_s - m*) o_s / L with
-// L = sum_s 2^(m_s - m*) l_s, in split order; lse = (m* + log2 L) ln 2.
+// One block per (unit, query head): out = sum_s w_s o_s / L with
+// w_s = 2^(m_s - m*), m* = max_s m_s and L = sum_s w_s l_s; lse = (m* + log2 L) ln 2.
 // A kernel of its own: the launch boundary makes every split's partial
-// visible without device-scope fences inside the split kernel. Partials are
-// staged through LDS 64 splits at a time, so each stage costs one memory
-// round trip.
+// visible without device-scope fences inside the split kernel. Thread s
+// computes the weight of split s once. The partial outputs go through LDS 64
+// splits at a time, every load of a stage issued before any is used (the
+// first stage's loads overlap the reductions), and kThreads / D threads per
+// channel sum interleaved splits; their sums are combined in a fixed order,
+// so the result is deterministic.
 constexpr int kMergeStage = 64;
 template <int D, int HB>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
+  static_assert(kThreads >= kMaxSplits, "one thread per split");
+  constexpr int TPD = kThreads / D;                      // threads per output channel
+  constexpr int PER = kMergeStage * D / 4 / kThreads;    // float4 per thread per stage
   __shared__ float4 so[kMergeStage * D / 4];
-  __shared__ float2 sml[kMergeStage];
+  __shared__ float sw[kMaxSplits];
+  __shared__ float red_m[kWaves], red_l[kWaves];
+  __shared__ float part[TPD][D];
   const int unit = blockIdx.x / HB;
   const int hh = blockIdx.x % HB;
   const int hc = unit % P.nhc;
@@ -1163,50 +1171,62 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
   const int b = bh / P.Hkv;
   const int64_t qi = static_cast<int64_t>(b) * P.Hq + h * P.G + hc * HB + hh;
   const int S = P.S;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const float4 *po = reinterpret_cast<const float4 *>(P.part_o) + qi * S * (D / 4);
-  const float2 *pml = P.part_ml + qi * S;
-  float m_run = kNegInf, L = 0.f, o = 0.f;
-  const int d = threadIdx.x;
+  const float2 ml = t < S ? P.part_ml[qi * S + t] : make_float2(kNegInf, 0.f);
+  float4 v[PER];
+  auto load_stage = [&](int s0) {
+    const int ne = ((S - s0) < kMergeStage ? (S - s0) : kMergeStage) * (D / 4);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = i * kThreads + t;
+      v[i] = e < ne ? po[static_cast<int64_t>(s0) * (D / 4) + e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_stage(0);
+  // m* over the splits, the weights and L
+  float mx = ml.x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+  if (lane == 0) red_m[wave] = mx;
+  __syncthreads();
+  mx = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red_m[w]);
+  const float mu = (mx == kNegInf) ? 0.f : mx;
+  const float wgt = t < S ? fast_exp2(ml.x - mu) : 0.f;
+  if (t < kMaxSplits) sw[t] = wgt;
+  float lw = wgt * ml.y;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lw += shfl_xor_f(lw, o);
+  if (lane == 0) red_l[wave] = lw;
+  // channel d, splits q, q + TPD, ... of each stage
+  const int d = t % D, q = t / D;
+  const float *sf = reinterpret_cast<const float *>(so);
+  float acc = 0.f;
   for (int s0 = 0; s0 < S; s0 += kMergeStage) {
+    if (s0) {
+      __syncthreads();          // the previous stage is consumed
+      load_stage(s0);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) so[i * kThreads + t] = v[i];
+    __syncthreads();
     const int ns = (S - s0) < kMergeStage ? (S - s0) : kMergeStage;
-    __syncthreads();
-    {
-      // every load of the stage first, then the LDS stores (one round trip)
-      constexpr int PER = kMergeStage * D / 4 / kThreads;
-      float4 v[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = i * kThreads + threadIdx.x;
-        v[i] = e < ns * (D / 4) ? po[s0 * (D / 4) + e] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      const float2 ml = threadIdx.x < ns ? pml[s0 + threadIdx.x] : make_float2(0.f, 0.f);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) so[i * kThreads + threadIdx.x] = v[i];
-      if (threadIdx.x < ns) sml[threadIdx.x] = ml;
-    }
-    __syncthreads();
-    if (d < D) {
-      float mx = m_run;
-      for (int s = 0; s < ns; ++s) mx = fmaxf(mx, sml[s].x);
-      const float mu = (mx == kNegInf) ? 0.f : mx;
-      const float a = fast_exp2(m_run - mu);
-      L *= a;
-      o *= a;
-      const float *sf = reinterpret_cast<const float *>(so);
-      for (int s = 0; s < ns; ++s) {
-        const float wgt = fast_exp2(sml[s].x - mu);
-        L = fmaf(wgt, sml[s].y, L);
-        o = fmaf(wgt, sf[s * D + d], o);
-      }
-      m_run = mx;
-    }
+    for (int s2 = q; s2 < ns; s2 += TPD) acc = fmaf(sw[s0 + s2], sf[s2 * D + d], acc);
   }
-  if (d < D) {
-    P.out[qi * D + d] = o / L;
-    if (d == 0 && P.lse) {
-      const float mu = (m_run == kNegInf) ? 0.f : m_run;
-      P.lse[qi] = (mu + log2f(L)) * kLn2;
-    }
+  part[q][d] = acc;
+  __syncthreads();
+  if (t < D) {
+    float o = part[0][t];
+#pragma unroll
+    for (int k = 1; k < TPD; ++k) o += part[k][t];
+    float L = red_l[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) L += red_l[w];
+    P.out[qi * D + t] = o / L;
+    if (t == 0 && P.lse) P.lse[qi] = (mu + log2f(L)) * kLn2;
   }
 }
 

@@ -24,51 +24,61 @@ namespace {
 
 constexpr int kGroup = 32;
 
-// Quantizes one (head, row, 32-channel group) of x, thread index gid.
+// Quantizes one quarter (8 channels) of one (head, row, 32-channel group) of
+// x; thread index gid = 4 * item + quarter, and the 4 threads of an item are
+// consecutive lanes (a DPP quad), which share the group's min and max. Every
+// lane then derives the same s and z from the same values with the same
+// instructions, and codes its own 8 channels: a 32-bit word of 8 nibbles.
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
 template <int DT, int LAYOUT>
-__device__ __forceinline__ void quantize_group(
-    int64_t gid, const void *__restrict__ x, int64_t n_rows, int D, int64_t x_head_stride,
+__device__ __forceinline__ void quantize_quarter(
+    uint32_t gid, const void *__restrict__ x, uint32_t n_rows, int D, int64_t x_head_stride,
     int64_t x_row_stride, uint8_t *__restrict__ codes, uint16_t *__restrict__ sz,
     int64_t dst_head_rows, int64_t dst_row0) {
-  const int ng = D / kGroup;
-  const int g = static_cast<int>(gid % ng);
-  const int64_t hr = gid / ng;
-  const int64_t r = hr % n_rows;
-  const int h = static_cast<int>(hr / n_rows);
+  const int ng = D / kGroup;                  // 2 or 4
+  const int q = static_cast<int>(gid & 3u);
+  const uint32_t item = gid >> 2;
+  const int g = static_cast<int>(item & static_cast<uint32_t>(ng - 1));
+  const uint32_t hr = ng == 4 ? (item >> 2) : (item >> 1);
+  const uint32_t r = hr % n_rows;
+  const uint32_t h = hr / n_rows;
 
-  const int64_t src = h * x_head_stride + r * x_row_stride + g * kGroup;
-  float v[kGroup];
+  const int64_t src = static_cast<int64_t>(h) * x_head_stride + static_cast<int64_t>(r) * x_row_stride +
+                      g * kGroup + q * 8;
+  float v[8];
   if constexpr (DT == HQ_F32) {
     const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + src);
-#pragma unroll
-    for (int i = 0; i < kGroup / 4; ++i) {
-      float4 f = p[i];
-      v[4 * i + 0] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-    }
+    const float4 f0 = p[0], f1 = p[1];
+    v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
+    v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
   } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + src);
+    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + src);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < kGroup / 8; ++i) {
-      uint4 u = p[i];
-      uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (DT == HQ_BF16) {
-          v[8 * i + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-          v[8 * i + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
-        } else {
-          v[8 * i + 2 * j] = f16_to_f32(w[j] & 0xFFFFu);
-          v[8 * i + 2 * j + 1] = f16_to_f32(w[j] >> 16);
-        }
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (DT == HQ_BF16) {
+        v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+      } else {
+        v[2 * j] = f16_to_f32(w[j] & 0xFFFFu);
+        v[2 * j + 1] = f16_to_f32(w[j] >> 16);
       }
     }
   }
   float mn = v[0], mx = v[0];
 #pragma unroll
-  for (int i = 1; i < kGroup; ++i) {
+  for (int i = 1; i < 8; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
+  mn = fminf(mn, quad_dpp<0xB1>(mn));         // quad_perm [1,0,3,2]
+  mx = fmaxf(mx, quad_dpp<0xB1>(mx));
+  mn = fminf(mn, quad_dpp<0x4E>(mn));         // quad_perm [2,3,0,1]
+  mx = fmaxf(mx, quad_dpp<0x4E>(mx));
   // "+ 0.0f" turns a zero of either sign into +0 (IEEE: -0 + +0 = +0).
   const float s32 = (mx - mn) / 15.0f + 0.0f;
   const _Float16 s16 = static_cast<_Float16>(s32);
@@ -76,23 +86,22 @@ __device__ __forceinline__ void quantize_group(
   const float s = static_cast<float>(s16);
   const float z = static_cast<float>(z16);
 
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  uint32_t packed = 0u;
 #pragma unroll
-  for (int i = 0; i < kGroup; ++i) {
+  for (int i = 0; i < 8; ++i) {
     uint32_t c = 0;
     if (s != 0.0f) {
       float t = __builtin_rintf((v[i] - z) / s);
       t = fminf(fmaxf(t, 0.0f), 15.0f);
       c = static_cast<uint32_t>(t);
     }
-    packed[i >> 3] |= c << (4 * (i & 7));
+    packed |= c << (4 * i);
   }
 
   const int64_t row = dst_row0 + r;
   const int64_t head_row = static_cast<int64_t>(h) * dst_head_rows + row;
   if constexpr (LAYOUT == HQ_LAYOUT_ROWS) {
-    uint4 *dst = reinterpret_cast<uint4 *>(codes + head_row * (D / 2) + g * (kGroup / 2));
-    *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    reinterpret_cast<uint32_t *>(codes + head_row * (D / 2) + g * (kGroup / 2))[q] = packed;
   } else {
     // tile u = row / 16 of head h; byte (j, slot(row % 16)) for channel pair
     // j, where each run of 4 rows is stored in the order 0, 2, 1, 3
@@ -101,27 +110,31 @@ __device__ __forceinline__ void quantize_group(
     const int slot16 = (r16 & ~3) | ((r16 & 1) << 1) | ((r16 >> 1) & 1);
     uint8_t *base = codes + tile * (D / 2) * 16 + slot16;
 #pragma unroll
-    for (int jj = 0; jj < kGroup / 2; ++jj) {
-      const int j = g * (kGroup / 2) + jj;
-      base[j * 16] = static_cast<uint8_t>((packed[jj >> 2] >> (8 * (jj & 3))) & 0xFFu);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = g * (kGroup / 2) + q * 4 + jj;
+      base[j * 16] = static_cast<uint8_t>((packed >> (8 * jj)) & 0xFFu);
     }
   }
-  const uint32_t szw = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
-                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
-  reinterpret_cast<uint32_t *>(sz)[head_row * (D / kGroup) + g] = szw;
+  if (q == 0) {
+    const uint32_t szw = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+    reinterpret_cast<uint32_t *>(sz)[head_row * (D / kGroup) + g] = szw;
+  }
 }
 
-// One thread per (head, row, 32-channel group).
+// Four threads per (head, row, 32-channel group); the host keeps the thread
+// count below 2^31. Items are whole quads, so a quad is either all in range
+// or all out.
 template <int DT, int LAYOUT>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const void *__restrict__ x, int n_heads, int64_t n_rows, int D, int64_t x_head_stride,
     int64_t x_row_stride, uint8_t *__restrict__ codes, uint16_t *__restrict__ sz,
     int64_t dst_head_rows, int64_t dst_row0) {
-  const int64_t total = static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const uint32_t total = static_cast<uint32_t>(n_heads) * static_cast<uint32_t>(n_rows) * (D / kGroup) * 4u;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
-  quantize_group<DT, LAYOUT>(gid, x, n_rows, D, x_head_stride, x_row_stride, codes, sz,
-                             dst_head_rows, dst_row0);
+  quantize_quarter<DT, LAYOUT>(gid, x, static_cast<uint32_t>(n_rows), D, x_head_stride, x_row_stride,
+                               codes, sz, dst_head_rows, dst_row0);
 }
 
 // Keys (row layout) and values (16-token tiles) of the same rows in one launch:
@@ -132,14 +145,15 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     int64_t x_head_stride, int64_t x_row_stride, uint8_t *__restrict__ k_codes,
     uint16_t *__restrict__ k_sz, uint8_t *__restrict__ v_codes, uint16_t *__restrict__ v_sz,
     int64_t dst_head_rows, int64_t dst_row0) {
-  const int64_t total = static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const uint32_t total = static_cast<uint32_t>(n_heads) * static_cast<uint32_t>(n_rows) * (D / kGroup) * 4u;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < total) {
-    quantize_group<DT, HQ_LAYOUT_ROWS>(gid, xk, n_rows, D, x_head_stride, x_row_stride, k_codes,
-                                       k_sz, dst_head_rows, dst_row0);
+    quantize_quarter<DT, HQ_LAYOUT_ROWS>(gid, xk, static_cast<uint32_t>(n_rows), D, x_head_stride,
+                                         x_row_stride, k_codes, k_sz, dst_head_rows, dst_row0);
   } else if (gid < 2 * total) {
-    quantize_group<DT, HQ_LAYOUT_TILE16>(gid - total, xv, n_rows, D, x_head_stride, x_row_stride,
-                                         v_codes, v_sz, dst_head_rows, dst_row0);
+    quantize_quarter<DT, HQ_LAYOUT_TILE16>(gid - total, xv, static_cast<uint32_t>(n_rows), D,
+                                           x_head_stride, x_row_stride, v_codes, v_sz, dst_head_rows,
+                                           dst_row0);
   }
 }
 
@@ -205,9 +219,9 @@ extern "C" hq_status hq_quantize_kv(const void *x, hq_dtype x_dtype, int n_heads
       reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(sz) % 4 != 0)
     return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv: x rows must be 16-byte aligned");
-  const int64_t threads = static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
+  const int64_t threads = 4 * static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
   const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv: too many rows");
+  if (threads > 0x7FFFFF00LL) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv: too many rows for one call");
   dim3 grid(static_cast<unsigned>(blocks));
   hipStream_t st = as_stream(stream);
   switch (x_dtype) {
@@ -272,9 +286,9 @@ extern "C" hq_status hq_quantize_kv_pair(const void *xk, const void *xv, hq_dtyp
        reinterpret_cast<uintptr_t>(k_codes)) % 16 != 0 ||
       (reinterpret_cast<uintptr_t>(k_sz) | reinterpret_cast<uintptr_t>(v_sz)) % 4 != 0)
     return fail(HQ_ERR_INVALID_ARG, "hq_quantize_kv_pair: rows must be 16-byte aligned");
-  const int64_t threads = 2 * static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
+  const int64_t threads = 8 * static_cast<int64_t>(n_heads) * n_rows * (D / kGroup);
   const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv_pair: too many rows");
+  if (threads > 0x7FFFFF00LL) return fail(HQ_ERR_UNSUPPORTED, "hq_quantize_kv_pair: too many rows for one call");
   const dim3 grid(static_cast<unsigned>(blocks));
   hipStream_t st = as_stream(stream);
 #define HQ_PAIR(DT_) hipLaunchKernelGGL(quantize_pair_kernel<DT_>, grid, dim3(256), 0, st, xk, xv, n_heads, n_rows, D, x_head_stride, x_row_stride, k_codes, k_sz, v_codes, v_sz, dst_head_rows, dst_row0)

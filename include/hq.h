@@ -121,7 +121,10 @@ typedef struct {
  *          dst_head_rows % 16 == 0),
  *   sz:    [n_heads][dst_head_rows][D/group][2].
  * Requires dst_row0 + n_rows <= dst_head_rows, D % group == 0, group == 32,
- * D in {64, 128}. n_rows == 0 or n_heads == 0 is a no-op.
+ * D in {64, 128}; x, its row and head strides (in bytes) and codes 16-byte
+ * aligned, sz 4-byte aligned. One call covers fewer than 2^31 / 4 groups
+ * (n_heads * n_rows * D / 32), else HQ_ERR_UNSUPPORTED: larger planes are
+ * quantized in several calls. n_rows == 0 or n_heads == 0 is a no-op.
  */
 hq_status hq_quantize_kv(const void *x, hq_dtype x_dtype, int n_heads, int64_t n_rows,
                          int D, int group, int64_t x_head_stride, int64_t x_row_stride,
@@ -135,7 +138,7 @@ hq_status hq_quantize_kv(const void *x, hq_dtype x_dtype, int n_heads, int64_t n
  * keys and values of the quantized majority are 4-bit). This is the per-step
  * eviction of the token that leaves the local window. Arguments as in
  * hq_quantize_kv, with xk/xv sharing dtype and strides; dst_head_rows must be
- * a multiple of 16.
+ * a multiple of 16, and one call covers fewer than 2^31 / 8 groups.
  */
 hq_status hq_quantize_kv_pair(const void *xk, const void *xv, hq_dtype x_dtype, int n_heads,
                               int64_t n_rows, int D, int group, int64_t x_head_stride,
