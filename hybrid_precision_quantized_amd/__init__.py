@@ -75,6 +75,13 @@ _SIGS = {
                                       ctypes.c_size_t, ctypes.c_void_p]),
     "hq_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HybridKV), ctypes.c_int, ctypes.c_int]),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
+    "hq_prefill_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int64, ctypes.c_int]),
     "hq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hq_last_error": (ctypes.c_char_p, []),
     "hq_abi_version": (ctypes.c_int, []),
@@ -201,6 +208,21 @@ def hq_decode_attn(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, stream
     _check(lib().hq_decode_attn(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
                                 n_splits, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream)))
+
+
+def hq_prefill_workspace_size(B, Hq, Hkv, T, D) -> int:
+    return int(lib().hq_prefill_workspace_size(B, Hq, Hkv, T, D))
+
+
+def hq_prefill_attn(q, k, v, B, Hq, Hkv, T, D, W, vl_idx, k_vl, sm_scale, out, lse, ws, group=32,
+                    stream=None):
+    """Causal hybrid-precision prefill attention (see include/hq.h)."""
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hq_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, T, D, group, W,
+                                 _ptr(vl_idx), k_vl, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                 ws_bytes, _stream(stream)))
 
 
 def hq_status_string(s: int) -> str:

@@ -1,0 +1,463 @@
+// Hybrid-precision prefill attention (causal), on MFMA.
+//
+// What is computed: "HyQuant ... explained simply" (aifromscratch.in), The
+// Technical Mechanics, Prefill Stage (the fused operator handles the
+// quantized majority first, then overlays the 16-bit vertical-line tokens and
+// the local window into the result); "Hybrid-precision attention reduces
+// compute cost ..." (wpnews.pro), summary (queries are quantized as well as
+// keys and values); kipquest.com paper page, The abstract (the prefill
+// operator keeps vertical-line tokens and a local sliding window in full
+// precision and quantizes the remaining context). For query position i of
+// query head qh (KV head h = qh / G) and key position j <= i:
+//   logit = q_i . k_j            if j is a VL position of h or i - W < j,
+//   logit = q_hat_i . k_hat_j    otherwise,
+// with q_hat, k_hat the INT4 round trip of the query and key rows in the KV
+// cache format (per token, 32-channel groups, fp16 scale and zero); one causal
+// softmax with scale sm_scale over all j <= i; P . V with the 16-bit V.
+//
+// Design (gfx950):
+//  * A pre-pass encodes every query and key row exactly as the quantizer does
+//    (hq_int4.h) and writes x_hat = s c + z (fp32) as two fp16 halves,
+//    hi = fp16(x_hat) and lo = fp16(x_hat - hi). q_hat . k_hat is then
+//    hi.hi + hi.lo + lo.hi on fp16 MFMA with fp32 accumulation, about 2^-21 from
+//    the exact product (lo . lo is below that). One fp16 rounding of x_hat
+//    (2^-11) would move the logits of the outlier channels far beyond the
+//    output tolerance; an INT8 MFMA over the codes would need each group's
+//    scale products applied per logit on the vector unit.
+//  * One workgroup = 4 waves = 128 query rows of one query head; wave w owns
+//    rows 32w..32w+31. Per 32-key tile S^T = K . Q^T (v_mfma_f32_32x32x16):
+//    lane l holds query l % 32 and 16 of the 32 keys, so the row softmax is
+//    16 registers plus one exchange with lane l ^ 32. The exponentiated tile,
+//    packed to fp16, is already the B operand of O^T += V^T . P^T: the
+//    contraction index follows the accumulator's key order, and V^T is read
+//    from LDS in that order (two 8-byte reads per fragment).
+//  * Three key streams share one online softmax per row: the quantized keys
+//    j <= i - W outside the VL set (split fp16 product), the window keys
+//    i - W < j <= i and the VL keys j <= i - W gathered by index (16-bit
+//    product). The three masks are disjoint and cover every j <= i once.
+//  * K tiles are staged row-major in LDS; V tiles are staged transposed,
+//    [d][key], in fp16 (16-bit inputs convert exactly inside the fp16 range;
+//    larger values are a precondition violation). The probabilities are
+//    rounded to fp16 for the P . V MFMA (relative 2^-12).
+//  * Query tiles are issued longest-first (the causal work grows with i).
+#include <math.h>
+
+#include <cmath>
+
+#include "hq_common.h"
+#include "hq_int4.h"
+
+extern "C" hq_status hq_vl_bitmap(const int32_t *vl_idx, int n_heads, int k, int64_t t_cap,
+                                  uint32_t *bits, void *stream);
+
+namespace hq {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 128;          // head_dim
+constexpr int kBM = 128;         // query rows per workgroup
+constexpr int kBN = 32;          // keys per tile
+constexpr int kThreads = 256;
+constexpr int kKPad = 8;         // halves of padding per K row in LDS
+constexpr int kVPad = 4;         // halves of padding per V^T row in LDS
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- pre-pass
+// Four threads per (row, 32-channel group) of x [rows][D]; writes the split
+// dequantized values of the same elements to hi and lo (fp16 bits).
+template <int DT>
+__global__ __launch_bounds__(256) void split_kernel(const void *__restrict__ x, uint32_t rows, int D,
+                                                    uint16_t *__restrict__ hi, uint16_t *__restrict__ lo) {
+  const int ng = D / 32;
+  const uint32_t total = rows * static_cast<uint32_t>(ng) * 4u;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;          // whole quads drop out together
+  const int q = static_cast<int>(gid & 3u);
+  const uint32_t item = gid >> 2;
+  const int g = static_cast<int>(item % static_cast<uint32_t>(ng));
+  const uint32_t r = item / static_cast<uint32_t>(ng);
+  const int64_t src = static_cast<int64_t>(r) * D + g * 32 + q * 8;
+  float v[8];
+  load8<DT>(x, src, v);
+  _Float16 s16, z16;
+  const uint32_t packed = encode_quarter(v, s16, z16);
+  const float s = static_cast<float>(s16), z = static_cast<float>(z16);
+  uint32_t wh[4], wl[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float x0 = fmaf(s, static_cast<float>((packed >> (4 * e)) & 15u), z);
+    const float x1 = fmaf(s, static_cast<float>((packed >> (4 * e + 4)) & 15u), z);
+    const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+    const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
+    const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
+    wh[e / 2] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+    wl[e / 2] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l0)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l1)) << 16);
+  }
+  *reinterpret_cast<uint4 *>(hi + src) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+  *reinterpret_cast<uint4 *>(lo + src) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+}
+
+// ---------------------------------------------------------------- attention
+struct PrefillParams {
+  const uint16_t *q, *k, *v;        // 16-bit [B][Hq or Hkv][T][D]
+  const uint16_t *q_hi, *q_lo;      // fp16 [B][Hq][T][D]
+  const uint16_t *k_hi, *k_lo;      // fp16 [B][Hkv][T][D]
+  const int32_t *vl_idx;            // [B][Hkv][k_vl], ascending
+  const uint32_t *vl_bits;          // [B][Hkv][words]
+  float *out;                       // [B][Hq][T][D]
+  float *lse;                       // [B][Hq][T] or null
+  int64_t T, words;
+  int B, Hq, Hkv, G, W, k_vl, n_qt;
+  float cs;                         // sm_scale * log2(e)
+};
+
+__device__ __forceinline__ f32x16 mfma_f16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                               c, 0, 0, 0);
+}
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_16bit(uint4 a, uint4 b, f32x16 c) {
+  if constexpr (DT == HQ_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  c, 0, 0, 0);
+  else
+    return mfma_f16(a, b, c);
+}
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// 16-bit pair -> fp16 pair (exact for values inside the fp16 range)
+template <int DT>
+__device__ __forceinline__ uint32_t to_f16x2(uint32_t w) {
+  if constexpr (DT == HQ_BF16) return pack2_f16(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
+  else return w;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
+  __shared__ __align__(16) uint16_t ka[kBN][kD + kKPad];   // K tile: hi, or the 16-bit rows
+  __shared__ __align__(16) uint16_t kb[kBN][kD + kKPad];   // K tile: lo
+  __shared__ __align__(16) uint16_t vt[kD][kBN + kVPad];   // V^T tile, fp16
+  __shared__ int32_t tpos[kBN];                            // key positions of a VL tile
+  __shared__ int s_nvl;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int bq = blockIdx.x % (P.B * P.Hq);
+  const int qt = P.n_qt - 1 - blockIdx.x / (P.B * P.Hq);     // longest rows first
+  const int b = bq / P.Hq;
+  const int qh = bq % P.Hq;
+  const int h = qh / P.G;
+  const int64_t q0 = static_cast<int64_t>(qt) * kBM;
+  const int64_t qi = q0 + wave * 32 + (lane & 31);           // this lane's query position
+  const bool q_ok = qi < P.T;
+  const int64_t qrow = (static_cast<int64_t>(b) * P.Hq + qh) * P.T + (q_ok ? qi : P.T - 1);
+  const int64_t krow0 = (static_cast<int64_t>(b) * P.Hkv + h) * P.T;   // first row of the KV head
+
+  // Q^T fragments (B operand): query lane % 32, channels 16 kc + 8 half .. + 7
+  uint4 fqh[8], fql[8], fqr[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    const int64_t off = qrow * kD + kc * 16 + half * 8;
+    fqh[kc] = *reinterpret_cast<const uint4 *>(P.q_hi + off);
+    fql[kc] = *reinterpret_cast<const uint4 *>(P.q_lo + off);
+    fqr[kc] = *reinterpret_cast<const uint4 *>(P.q + off);
+  }
+
+  float m_run = -__FLT_MAX__;        // running max (finite: the rescale runs first)
+  float l_run = 0.f;                 // this lane's share of the row sum
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+
+  // key of accumulator register r of this lane (a row of S^T)
+  auto key_of = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
+
+  // ---- staging: rows of K (one or two planes) and V^T for 32 keys; row(r)
+  // gives the key position of tile row r or -1 (zero row)
+  auto stage = [&](const uint16_t *ksrc_a, const uint16_t *ksrc_b, auto row) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = e * kThreads + threadIdx.x;     // 512 uint4 per plane
+      const int r = idx >> 4, c = idx & 15;
+      const int64_t pos = row(r);
+      uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
+      if (pos >= 0) {
+        va = *reinterpret_cast<const uint4 *>(ksrc_a + (krow0 + pos) * kD + c * 8);
+        if (ksrc_b) vb = *reinterpret_cast<const uint4 *>(ksrc_b + (krow0 + pos) * kD + c * 8);
+      }
+      *reinterpret_cast<uint4 *>(&ka[r][c * 8]) = va;
+      if (ksrc_b) *reinterpret_cast<uint4 *>(&kb[r][c * 8]) = vb;
+    }
+    {
+      const int r = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
+      const int64_t pos = row(r);
+      uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      if (pos >= 0) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(P.v + (krow0 + pos) * kD + d0);
+        const uint4 u0 = src[0], u1 = src[1];
+        w[0] = u0.x; w[1] = u0.y; w[2] = u0.z; w[3] = u0.w;
+        w[4] = u1.x; w[5] = u1.y; w[6] = u1.z; w[7] = u1.w;
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const uint32_t f = to_f16x2<DT>(w[x]);
+        vt[d0 + 2 * x][r] = static_cast<uint16_t>(f & 0xFFFFu);
+        vt[d0 + 2 * x + 1][r] = static_cast<uint16_t>(f >> 16);
+      }
+    }
+  };
+
+  // ---- one 32-key tile: mask, online softmax, P . V
+  auto consume = [&](f32x16 &s, auto valid) {
+    float tmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = q_ok && valid(key_of(r));
+      s[r] = ok ? s[r] * P.cs : kNegInf;
+      tmax = fmaxf(tmax, s[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    if (__builtin_expect(__ballot(tmax > m_run) != 0, 0)) {
+      const float mn = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    uint32_t pk[8];
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2f(s[r] - m_run), p1 = exp2f(s[r + 1] - m_run);
+      ls += p0 + p1;
+      pk[r / 2] = pack2_f16(p0, p1);
+    }
+    l_run += ls;
+    const uint4 pf[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint16_t *vrow = &vt[dt * 32 + (lane & 31)][0];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint2 a0 = *reinterpret_cast<const uint2 *>(vrow + 16 * c + 4 * half);
+        const uint2 a1 = *reinterpret_cast<const uint2 *>(vrow + 16 * c + 8 + 4 * half);
+        o[dt] = mfma_f16(make_uint4(a0.x, a0.y, a1.x, a1.y), pf[c], o[dt]);
+      }
+    }
+  };
+
+  const int64_t qlast = (q0 + kBM - 1 < P.T - 1) ? q0 + kBM - 1 : P.T - 1;   // last row of the tile
+  const uint32_t *bits = P.vl_bits + (static_cast<int64_t>(b) * P.Hkv + h) * P.words;
+
+  // ---- stream 1: quantized keys j <= i - W outside the VL set
+  {
+    const int64_t nkeys = qlast - P.W + 1;                    // keys 0 .. qlast - W
+    const int ntiles = nkeys > 0 ? static_cast<int>((nkeys + kBN - 1) / kBN) : 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const int64_t k0 = static_cast<int64_t>(t) * kBN;
+      __syncthreads();
+      stage(P.k_hi, P.k_lo, [&](int r) { return k0 + r < P.T ? k0 + r : int64_t(-1); });
+      __syncthreads();
+      const uint32_t word = bits[t];                          // VL bits of keys k0 .. k0 + 31
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        const uint4 ah = *reinterpret_cast<const uint4 *>(&ka[lane & 31][kc * 16 + half * 8]);
+        const uint4 al = *reinterpret_cast<const uint4 *>(&kb[lane & 31][kc * 16 + half * 8]);
+        s = mfma_f16(ah, fqh[kc], s);
+        s = mfma_f16(ah, fql[kc], s);
+        s = mfma_f16(al, fqh[kc], s);
+      }
+      consume(s, [&](int m) {
+        const int64_t j = k0 + m;
+        return j <= qi - P.W && !((word >> m) & 1u);
+      });
+    }
+  }
+  // ---- stream 2: window keys i - W < j <= i (16-bit)
+  if (P.W > 0) {
+    const int64_t jlo = (q0 - P.W + 1 > 0) ? q0 - P.W + 1 : 0;
+    const int t0 = static_cast<int>(jlo / kBN), t1 = static_cast<int>(qlast / kBN);
+    for (int t = t0; t <= t1; ++t) {
+      const int64_t k0 = static_cast<int64_t>(t) * kBN;
+      __syncthreads();
+      stage(P.k, nullptr, [&](int r) { return k0 + r < P.T ? k0 + r : int64_t(-1); });
+      __syncthreads();
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        s = mfma_16bit<DT>(*reinterpret_cast<const uint4 *>(&ka[lane & 31][kc * 16 + half * 8]), fqr[kc], s);
+      consume(s, [&](int m) {
+        const int64_t j = k0 + m;
+        return j > qi - P.W && j <= qi;
+      });
+    }
+  }
+  // ---- stream 3: VL keys j <= i - W (16-bit, gathered by index)
+  if (P.k_vl > 0) {
+    const int32_t *vl = P.vl_idx + (static_cast<int64_t>(b) * P.Hkv + h) * P.k_vl;
+    if (threadIdx.x == 0) {                 // VL positions <= qlast - W (ascending list)
+      int lo = 0, hi = P.k_vl;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (vl[mid] <= qlast - P.W) lo = mid + 1; else hi = mid;
+      }
+      s_nvl = lo;
+    }
+    __syncthreads();
+    const int nvl = s_nvl;
+    for (int t = 0; t * kBN < nvl; ++t) {
+      __syncthreads();
+      if (threadIdx.x < kBN) tpos[threadIdx.x] = (t * kBN + static_cast<int>(threadIdx.x) < nvl)
+                                                      ? vl[t * kBN + threadIdx.x] : -1;
+      __syncthreads();
+      stage(P.k, nullptr, [&](int r) { return static_cast<int64_t>(tpos[r]); });
+      __syncthreads();
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        s = mfma_16bit<DT>(*reinterpret_cast<const uint4 *>(&ka[lane & 31][kc * 16 + half * 8]), fqr[kc], s);
+      consume(s, [&](int m) {
+        const int64_t j = tpos[m];
+        return j >= 0 && j <= qi - P.W;
+      });
+    }
+  }
+
+  // ---- output: lane holds query lane % 32, channels dt * 32 + key_of(r)
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (q_ok) {
+    const float inv = 1.f / l_tot;
+    float *orow = P.out + qrow * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const int d = dt * 32 + key_of(r);
+        *reinterpret_cast<float4 *>(orow + d) =
+            make_float4(o[dt][r] * inv, o[dt][r + 1] * inv, o[dt][r + 2] * inv, o[dt][r + 3] * inv);
+      }
+    if (half == 0 && P.lse) P.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct PrefillWs {
+  size_t q_hi, q_lo, k_hi, k_lo, bits, total;
+};
+PrefillWs prefill_ws(int B, int Hq, int Hkv, int64_t T, int D) {
+  PrefillWs L{};
+  const size_t qn = static_cast<size_t>(B) * Hq * T * D * 2, kn = static_cast<size_t>(B) * Hkv * T * D * 2;
+  const size_t words = static_cast<size_t>((T + 31) / 32);
+  L.q_hi = 0;
+  L.q_lo = align_up(L.q_hi + qn, 256);
+  L.k_hi = align_up(L.q_lo + qn, 256);
+  L.k_lo = align_up(L.k_hi + kn, 256);
+  L.bits = align_up(L.k_lo + kn, 256);
+  L.total = L.bits + static_cast<size_t>(B) * Hkv * words * 4;
+  return L;
+}
+
+}  // namespace
+}  // namespace hq
+
+using namespace hq;
+
+extern "C" size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || D < 1) return 0;
+  return prefill_ws(B, Hq, Hkv, T, D).total;
+}
+
+extern "C" hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype dtype, int B,
+                                     int Hq, int Hkv, int64_t T, int D, int group, int W,
+                                     const int32_t *vl_idx, int k_vl, float sm_scale, float *out,
+                                     float *lse, void *ws, size_t ws_bytes, void *stream) {
+  if (dtype != HQ_BF16 && dtype != HQ_F16)
+    return fail(HQ_ERR_UNSUPPORTED, "hq_prefill_attn: dtype must be HQ_BF16 or HQ_F16");
+  if (D != kD) return fail(HQ_ERR_UNSUPPORTED, "hq_prefill_attn: D must be 128");
+  if (group != 32) return fail(HQ_ERR_UNSUPPORTED, "hq_prefill_attn: group must be 32");
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: sizes must be >= 1");
+  if (Hq % Hkv) return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: Hq %% Hkv != 0");
+  if (W < 0 || k_vl < 0) return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: W and k must be >= 0");
+  if (k_vl > T) return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: k exceeds T");
+  if (!q || !k || !v || !out || (k_vl > 0 && !vl_idx))
+    return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: null pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(out)) % 16)
+    return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: q, k, v and out must be 16-byte aligned");
+  // thread counts of the pre-pass and the row indices stay below 2^31
+  if (static_cast<double>(B) * Hq * T * (D / 32) * 4 > 2.0e9)
+    return fail(HQ_ERR_UNSUPPORTED, "hq_prefill_attn: too many query rows for one call");
+  const PrefillWs L = prefill_ws(B, Hq, Hkv, T, D);
+  if (!ws || ws_bytes < L.total)
+    return fail(HQ_ERR_WORKSPACE, "hq_prefill_attn: workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: workspace must be 256-byte aligned");
+  hipStream_t st = as_stream(stream);
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  PrefillParams P{};
+  P.q = static_cast<const uint16_t *>(q);
+  P.k = static_cast<const uint16_t *>(k);
+  P.v = static_cast<const uint16_t *>(v);
+  P.q_hi = reinterpret_cast<uint16_t *>(w8 + L.q_hi);
+  P.q_lo = reinterpret_cast<uint16_t *>(w8 + L.q_lo);
+  P.k_hi = reinterpret_cast<uint16_t *>(w8 + L.k_hi);
+  P.k_lo = reinterpret_cast<uint16_t *>(w8 + L.k_lo);
+  P.vl_idx = vl_idx;
+  P.vl_bits = reinterpret_cast<uint32_t *>(w8 + L.bits);
+  P.out = out;
+  P.lse = lse;
+  P.T = T;
+  P.words = (T + 31) / 32;
+  P.B = B; P.Hq = Hq; P.Hkv = Hkv; P.G = Hq / Hkv; P.W = W; P.k_vl = k_vl;
+  P.n_qt = static_cast<int>((T + kBM - 1) / kBM);
+  P.cs = (sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(D))) * kLog2e;
+
+  // pre-pass: split dequantized Q and K
+  const uint32_t qrows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hq * T);
+  const uint32_t krows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hkv * T);
+  const uint32_t qthreads = qrows * (D / 32) * 4, kthreads = krows * (D / 32) * 4;
+  uint16_t *qh = reinterpret_cast<uint16_t *>(w8 + L.q_hi), *ql = reinterpret_cast<uint16_t *>(w8 + L.q_lo);
+  uint16_t *kh = reinterpret_cast<uint16_t *>(w8 + L.k_hi), *kl = reinterpret_cast<uint16_t *>(w8 + L.k_lo);
+  if (dtype == HQ_BF16) {
+    hipLaunchKernelGGL(split_kernel<HQ_BF16>, dim3((qthreads + 255) / 256), dim3(256), 0, st, q, qrows, D, qh, ql);
+    hipLaunchKernelGGL(split_kernel<HQ_BF16>, dim3((kthreads + 255) / 256), dim3(256), 0, st, k, krows, D, kh, kl);
+  } else {
+    hipLaunchKernelGGL(split_kernel<HQ_F16>, dim3((qthreads + 255) / 256), dim3(256), 0, st, q, qrows, D, qh, ql);
+    hipLaunchKernelGGL(split_kernel<HQ_F16>, dim3((kthreads + 255) / 256), dim3(256), 0, st, k, krows, D, kh, kl);
+  }
+  hq_status s = check_launch("hq_prefill_attn (pre-pass)");
+  if (s != HQ_OK) return s;
+  // VL membership bitmap (no VL: an all-zero bitmap)
+  s = hq_vl_bitmap(vl_idx, B * Hkv, k_vl, P.words * 32, const_cast<uint32_t *>(P.vl_bits), stream);
+  if (s != HQ_OK) return s;
+  const unsigned blocks = static_cast<unsigned>(P.n_qt) * B * Hq;
+  if (dtype == HQ_BF16)
+    hipLaunchKernelGGL(prefill_kernel<HQ_BF16>, dim3(blocks), dim3(kThreads), 0, st, P);
+  else
+    hipLaunchKernelGGL(prefill_kernel<HQ_F16>, dim3(blocks), dim3(kThreads), 0, st, P);
+  return check_launch("hq_prefill_attn");
+}

@@ -18,6 +18,7 @@
 #include <stdio.h>
 
 #include "hq_common.h"
+#include "hq_int4.h"
 
 namespace hq {
 namespace {
@@ -26,14 +27,7 @@ constexpr int kGroup = 32;
 
 // Quantizes one quarter (8 channels) of one (head, row, 32-channel group) of
 // x; thread index gid = 4 * item + quarter, and the 4 threads of an item are
-// consecutive lanes (a DPP quad), which share the group's min and max. Every
-// lane then derives the same s and z from the same values with the same
-// instructions, and codes its own 8 channels: a 32-bit word of 8 nibbles.
-template <int CTRL>
-__device__ __forceinline__ float quad_dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, true));
-}
+// consecutive lanes (a DPP quad) that encode the group together (hq_int4.h).
 template <int DT, int LAYOUT>
 __device__ __forceinline__ void quantize_quarter(
     uint32_t gid, const void *__restrict__ x, uint32_t n_rows, int D, int64_t x_head_stride,
@@ -50,53 +44,9 @@ __device__ __forceinline__ void quantize_quarter(
   const int64_t src = static_cast<int64_t>(h) * x_head_stride + static_cast<int64_t>(r) * x_row_stride +
                       g * kGroup + q * 8;
   float v[8];
-  if constexpr (DT == HQ_F32) {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + src);
-    const float4 f0 = p[0], f1 = p[1];
-    v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
-    v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
-  } else {
-    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + src);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (DT == HQ_BF16) {
-        v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-        v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-      } else {
-        v[2 * j] = f16_to_f32(w[j] & 0xFFFFu);
-        v[2 * j + 1] = f16_to_f32(w[j] >> 16);
-      }
-    }
-  }
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = fminf(mn, v[i]);
-    mx = fmaxf(mx, v[i]);
-  }
-  mn = fminf(mn, quad_dpp<0xB1>(mn));         // quad_perm [1,0,3,2]
-  mx = fmaxf(mx, quad_dpp<0xB1>(mx));
-  mn = fminf(mn, quad_dpp<0x4E>(mn));         // quad_perm [2,3,0,1]
-  mx = fmaxf(mx, quad_dpp<0x4E>(mx));
-  // "+ 0.0f" turns a zero of either sign into +0 (IEEE: -0 + +0 = +0).
-  const float s32 = (mx - mn) / 15.0f + 0.0f;
-  const _Float16 s16 = static_cast<_Float16>(s32);
-  const _Float16 z16 = static_cast<_Float16>(mn + 0.0f);
-  const float s = static_cast<float>(s16);
-  const float z = static_cast<float>(z16);
-
-  uint32_t packed = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t c = 0;
-    if (s != 0.0f) {
-      float t = __builtin_rintf((v[i] - z) / s);
-      t = fminf(fmaxf(t, 0.0f), 15.0f);
-      c = static_cast<uint32_t>(t);
-    }
-    packed |= c << (4 * i);
-  }
+  load8<DT>(x, src, v);
+  _Float16 s16, z16;
+  const uint32_t packed = encode_quarter(v, s16, z16);
 
   const int64_t row = dst_row0 + r;
   const int64_t head_row = static_cast<int64_t>(h) * dst_head_rows + row;

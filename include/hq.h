@@ -231,6 +231,37 @@ size_t hq_decode_workspace_size(const hq_hybrid_kv *kv, int Hq, int n_splits);
 /* The split count hq_decode_attn uses for n_splits == 0. */
 int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
 
+/*
+ * hq_prefill_attn -- causal hybrid-precision prefill attention [AFS, The
+ * Technical Mechanics, Prefill Stage: the quantized majority is handled first
+ * and the 16-bit vertical lines and local window are overlaid into the
+ * result; WPN, summary: queries are quantized as well as keys and values;
+ * KQ, The abstract]. For every b, query head qh (KV head h = qh / G) and
+ * query position i, over key positions j <= i:
+ *   logit(i, j) = sm_scale * q_i . k_j          if j is in vl_idx[b][h] or
+ *                                                i - W < j,
+ *   logit(i, j) = sm_scale * q_hat_i . k_hat_j  otherwise,
+ * q_hat, k_hat being the INT4 round trip of the rows in the hq_quantize_kv
+ * format (per token, 32-channel groups, fp16 scale and zero); one causal
+ * softmax; out[b][qh][i] = sum_j softmax_j * v_j (fp32), lse[b][qh][i] its
+ * natural log-sum-exp (optional).
+ * q [B][Hq][T][D], k and v [B][Hkv][T][D], contiguous, of `dtype` (HQ_BF16 or
+ * HQ_F16), 16-byte aligned; vl_idx [B][Hkv][k_vl] strictly ascending
+ * positions in [0, T) (not checked on the device); out [B][Hq][T][D];
+ * sm_scale <= 0 means 1/sqrt(D). Requires D == 128, group == 32,
+ * Hq % Hkv == 0. ws: at least hq_prefill_workspace_size bytes, 256-byte
+ * aligned, no initialisation needed (it holds the split dequantized Q and K
+ * and the VL bitmap). Precision: the quantized logits are within about 2^-21
+ * (relative) of the exact q_hat . k_hat; the probabilities are rounded to
+ * fp16 for the P . V product.
+ */
+hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype dtype, int B, int Hq,
+                          int Hkv, int64_t T, int D, int group, int W, const int32_t *vl_idx, int k_vl,
+                          float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
+                          void *stream);
+
+size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D);
+
 const char *hq_status_string(hq_status s);
 const char *hq_last_error(void);
 int hq_abi_version(void);
