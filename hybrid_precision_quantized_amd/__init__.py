@@ -81,7 +81,7 @@ _SIGS = {
                                        ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "hq_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                                    ctypes.c_int64, ctypes.c_int]),
+                                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
     "hq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hq_last_error": (ctypes.c_char_p, []),
     "hq_abi_version": (ctypes.c_int, []),
@@ -210,8 +210,8 @@ def hq_decode_attn(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, stream
                                 _stream(stream)))
 
 
-def hq_prefill_workspace_size(B, Hq, Hkv, T, D) -> int:
-    return int(lib().hq_prefill_workspace_size(B, Hq, Hkv, T, D))
+def hq_prefill_workspace_size(B, Hq, Hkv, T, D, k_vl) -> int:
+    return int(lib().hq_prefill_workspace_size(B, Hq, Hkv, T, D, k_vl))
 
 
 def hq_prefill_attn(q, k, v, B, Hq, Hkv, T, D, W, vl_idx, k_vl, sm_scale, out, lse, ws, group=32,

@@ -104,17 +104,69 @@ __global__ __launch_bounds__(256) void split_kernel(const void *__restrict__ x, 
   *reinterpret_cast<uint4 *>(lo + src) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
 }
 
+// 32-key tiles for the attention kernel, one thread per (tile, key, 8-channel
+// chunk): row pos of src [heads][T][D] (16-bit) goes to V^T tile layout
+// vt [heads][tiles][D][32] in fp16 and, when krows is given, to the row-major
+// K tile layout krows [heads][tiles * 32][D] (16-bit). Key r of tile t is
+// position 32 t + r, or idx[head][32 t + r] when idx is given (n_keys
+// entries); keys past the end become zero rows.
+template <int DT>
+__global__ __launch_bounds__(256) void tile_kernel(const uint16_t *__restrict__ vsrc,
+                                                   const uint16_t *__restrict__ ksrc, int64_t T,
+                                                   const int32_t *__restrict__ idx, int n_keys, int tiles,
+                                                   int heads, uint16_t *__restrict__ vt,
+                                                   uint16_t *__restrict__ krows) {
+  const int64_t total = static_cast<int64_t>(heads) * tiles * 32 * (kD / 8);
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % (kD / 8));
+  const int64_t hr = gid / (kD / 8);             // (head, tile, key)
+  const int r = static_cast<int>(hr % 32);
+  const int64_t ht = hr / 32;                   // head * tiles + tile
+  const int t = static_cast<int>(ht % tiles);
+  const int64_t head = ht / tiles;
+  const int key = t * 32 + r;
+  int64_t pos = -1;
+  if (idx) pos = key < n_keys ? idx[head * n_keys + key] : -1;
+  else pos = key < T ? key : -1;
+  uint4 u = make_uint4(0u, 0u, 0u, 0u), uk = u;
+  if (pos >= 0) {
+    u = *reinterpret_cast<const uint4 *>(vsrc + (head * T + pos) * kD + c * 8);
+    if (krows) uk = *reinterpret_cast<const uint4 *>(ksrc + (head * T + pos) * kD + c * 8);
+  }
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint16_t *dst = vt + (ht * kD + c * 8) * 32 + r;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    uint32_t f;
+    if constexpr (DT == HQ_BF16) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      h2 v2 = {static_cast<_Float16>(bf16_to_f32(w[x] & 0xFFFFu)), static_cast<_Float16>(bf16_to_f32(w[x] >> 16))};
+      f = __builtin_bit_cast(uint32_t, v2);
+    } else {
+      f = w[x];
+    }
+    dst[(2 * x) * 32] = static_cast<uint16_t>(f & 0xFFFFu);
+    dst[(2 * x + 1) * 32] = static_cast<uint16_t>(f >> 16);
+  }
+  if (krows) *reinterpret_cast<uint4 *>(krows + (hr) * kD + c * 8) = uk;
+}
+
 // ---------------------------------------------------------------- attention
 struct PrefillParams {
-  const uint16_t *q, *k, *v;        // 16-bit [B][Hq or Hkv][T][D]
+  const uint16_t *q;                // 16-bit [B][Hq][T][D]
+  const uint16_t *k;                // 16-bit [B][Hkv][T][D]
   const uint16_t *q_hi, *q_lo;      // fp16 [B][Hq][T][D]
   const uint16_t *k_hi, *k_lo;      // fp16 [B][Hkv][T][D]
+  const uint16_t *vt;               // fp16 V^T tiles [B][Hkv][ntk][D][32]
+  const uint16_t *vl_k;             // 16-bit VL key rows [B][Hkv][nvt * 32][D]
+  const uint16_t *vl_vt;            // fp16 VL V^T tiles [B][Hkv][nvt][D][32]
   const int32_t *vl_idx;            // [B][Hkv][k_vl], ascending
   const uint32_t *vl_bits;          // [B][Hkv][words]
   float *out;                       // [B][Hq][T][D]
   float *lse;                       // [B][Hq][T] or null
   int64_t T, words;
-  int B, Hq, Hkv, G, W, k_vl, n_qt;
+  int B, Hq, Hkv, G, W, k_vl, n_qt, ntk, nvt;
   float cs;                         // sm_scale * log2(e)
 };
 
@@ -135,20 +187,23 @@ __device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
   h2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
 }
-// 16-bit pair -> fp16 pair (exact for values inside the fp16 range)
-template <int DT>
-__device__ __forceinline__ uint32_t to_f16x2(uint32_t w) {
-  if constexpr (DT == HQ_BF16) return pack2_f16(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
-  else return w;
-}
+
+// Stream kinds: quantized keys, window keys, VL keys.
+enum { kQuant = 0, kWin = 1, kVl = 2 };
+
+// The staged data of one 32-key tile: K rows (one or two planes, row-major,
+// padded) and the V^T tile ([d][key], padded); two LDS slots.
+struct PrefillShared {
+  uint16_t ka[2][kBN][kD + kKPad];
+  uint16_t kb[2][kBN][kD + kKPad];
+  uint16_t vt[2][kD][kBN + kVPad];
+  int32_t pos[2][kBN];
+  int nvl;
+};
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
-  __shared__ __align__(16) uint16_t ka[kBN][kD + kKPad];   // K tile: hi, or the 16-bit rows
-  __shared__ __align__(16) uint16_t kb[kBN][kD + kKPad];   // K tile: lo
-  __shared__ __align__(16) uint16_t vt[kD][kBN + kVPad];   // V^T tile, fp16
-  __shared__ int32_t tpos[kBN];                            // key positions of a VL tile
-  __shared__ int s_nvl;
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
+  __shared__ __align__(16) PrefillShared sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -158,21 +213,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
   const int b = bq / P.Hq;
   const int qh = bq % P.Hq;
   const int h = qh / P.G;
+  const int64_t bh = static_cast<int64_t>(b) * P.Hkv + h;
   const int64_t q0 = static_cast<int64_t>(qt) * kBM;
   const int64_t qi = q0 + wave * 32 + (lane & 31);           // this lane's query position
   const bool q_ok = qi < P.T;
   const int64_t qrow = (static_cast<int64_t>(b) * P.Hq + qh) * P.T + (q_ok ? qi : P.T - 1);
-  const int64_t krow0 = (static_cast<int64_t>(b) * P.Hkv + h) * P.T;   // first row of the KV head
-
-  // Q^T fragments (B operand): query lane % 32, channels 16 kc + 8 half .. + 7
-  uint4 fqh[8], fql[8], fqr[8];
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    const int64_t off = qrow * kD + kc * 16 + half * 8;
-    fqh[kc] = *reinterpret_cast<const uint4 *>(P.q_hi + off);
-    fql[kc] = *reinterpret_cast<const uint4 *>(P.q_lo + off);
-    fqr[kc] = *reinterpret_cast<const uint4 *>(P.q + off);
-  }
+  const int64_t krow0 = bh * P.T;                            // first K row of the KV head
+  const int64_t qlast = (q0 + kBM - 1 < P.T - 1) ? q0 + kBM - 1 : P.T - 1;
 
   float m_run = -__FLT_MAX__;        // running max (finite: the rescale runs first)
   float l_run = 0.f;                 // this lane's share of the row sum
@@ -182,46 +229,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
-  // key of accumulator register r of this lane (a row of S^T)
   auto key_of = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
 
-  // ---- staging: rows of K (one or two planes) and V^T for 32 keys; row(r)
-  // gives the key position of tile row r or -1 (zero row)
-  auto stage = [&](const uint16_t *ksrc_a, const uint16_t *ksrc_b, auto row) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = e * kThreads + threadIdx.x;     // 512 uint4 per plane
-      const int r = idx >> 4, c = idx & 15;
-      const int64_t pos = row(r);
-      uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
-      if (pos >= 0) {
-        va = *reinterpret_cast<const uint4 *>(ksrc_a + (krow0 + pos) * kD + c * 8);
-        if (ksrc_b) vb = *reinterpret_cast<const uint4 *>(ksrc_b + (krow0 + pos) * kD + c * 8);
-      }
-      *reinterpret_cast<uint4 *>(&ka[r][c * 8]) = va;
-      if (ksrc_b) *reinterpret_cast<uint4 *>(&kb[r][c * 8]) = vb;
-    }
-    {
-      const int r = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
-      const int64_t pos = row(r);
-      uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-      if (pos >= 0) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(P.v + (krow0 + pos) * kD + d0);
-        const uint4 u0 = src[0], u1 = src[1];
-        w[0] = u0.x; w[1] = u0.y; w[2] = u0.z; w[3] = u0.w;
-        w[4] = u1.x; w[5] = u1.y; w[6] = u1.z; w[7] = u1.w;
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const uint32_t f = to_f16x2<DT>(w[x]);
-        vt[d0 + 2 * x][r] = static_cast<uint16_t>(f & 0xFFFFu);
-        vt[d0 + 2 * x + 1][r] = static_cast<uint16_t>(f >> 16);
-      }
-    }
-  };
-
-  // ---- one 32-key tile: mask, online softmax, P . V
-  auto consume = [&](f32x16 &s, auto valid) {
+  // ---- one 32-key tile from LDS slot `sl`: mask, online softmax, P . V
+  auto consume = [&](f32x16 &s, int sl, auto valid) {
     float tmax = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -252,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
     const uint4 pf[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t *vrow = &vt[dt * 32 + (lane & 31)][0];
+      const uint16_t *vrow = &sm.vt[sl][dt * 32 + (lane & 31)][0];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const uint2 a0 = *reinterpret_cast<const uint2 *>(vrow + 16 * c + 4 * half);
@@ -262,87 +273,133 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
     }
   };
 
-  const int64_t qlast = (q0 + kBM - 1 < P.T - 1) ? q0 + kBM - 1 : P.T - 1;   // last row of the tile
-  const uint32_t *bits = P.vl_bits + (static_cast<int64_t>(b) * P.Hkv + h) * P.words;
-
-  // ---- stream 1: quantized keys j <= i - W outside the VL set
-  {
-    const int64_t nkeys = qlast - P.W + 1;                    // keys 0 .. qlast - W
-    const int ntiles = nkeys > 0 ? static_cast<int>((nkeys + kBN - 1) / kBN) : 0;
-    for (int t = 0; t < ntiles; ++t) {
-      const int64_t k0 = static_cast<int64_t>(t) * kBN;
-      __syncthreads();
-      stage(P.k_hi, P.k_lo, [&](int r) { return k0 + r < P.T ? k0 + r : int64_t(-1); });
-      __syncthreads();
-      const uint32_t word = bits[t];                          // VL bits of keys k0 .. k0 + 31
+  // ---- a stream of 32-key tiles t0 .. t1 - 1, staged through two LDS slots
+  // with the next tile's global loads in flight during each tile's MFMAs
+  struct Pre {
+    uint4 a[2], b[2], v[2];
+    int32_t pos;
+  };
+  auto run_stream = [&](const int kind, const int t0, const int t1, const uint4 (&fq0)[8],
+                        const uint4 (&fq1)[8]) {
+    if (t0 >= t1) return;
+    const bool two = kind == kQuant;
+    const uint16_t *kpa = kind == kQuant ? P.k_hi : (kind == kWin ? P.k : P.vl_k);
+    const uint16_t *kpb = P.k_lo;
+    const int64_t krows = kind == kVl ? static_cast<int64_t>(P.nvt) * kBN : P.T;   // rows per head
+    const uint16_t *vsrc = kind == kVl ? P.vl_vt : P.vt;
+    const int vtiles = kind == kVl ? P.nvt : P.ntk;
+    const int32_t *vl = P.vl_idx + bh * P.k_vl;
+    auto load = [&](int t, Pre &L) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int idx = e * kThreads + threadIdx.x;      // 512 uint4 per K plane
+        const int r = idx >> 4, c = idx & 15;
+        const int64_t row = static_cast<int64_t>(t) * kBN + r;
+        uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
+        if (row < krows) {
+          const int64_t off = (bh * krows + row) * kD + c * 8;
+          va = *reinterpret_cast<const uint4 *>(kpa + off);
+          if (two) vb = *reinterpret_cast<const uint4 *>(kpb + off);
+        }
+        L.a[e] = va;
+        L.b[e] = vb;
+        // V^T tile: 8 KB contiguous
+        L.v[e] = reinterpret_cast<const uint4 *>(vsrc + (bh * vtiles + t) * (kD * kBN))[idx];
+      }
+      L.pos = 0;
+      if (kind == kVl && threadIdx.x < kBN) {
+        const int j = t * kBN + static_cast<int>(threadIdx.x);
+        L.pos = j < sm.nvl ? vl[j] : -1;
+      }
+    };
+    auto store = [&](int sl, const Pre &L) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int idx = e * kThreads + threadIdx.x;
+        const int r = idx >> 4, c = idx & 15;
+        *reinterpret_cast<uint4 *>(&sm.ka[sl][r][c * 8]) = L.a[e];
+        if (two) *reinterpret_cast<uint4 *>(&sm.kb[sl][r][c * 8]) = L.b[e];
+        const int d = idx >> 2, k8 = (idx & 3) * 8;       // V^T: row d, keys k8 .. k8 + 7
+        *reinterpret_cast<uint4 *>(&sm.vt[sl][d][k8]) = L.v[e];
+      }
+      if (kind == kVl && threadIdx.x < kBN) sm.pos[sl][threadIdx.x] = L.pos;
+    };
+    Pre pre;
+    load(t0, pre);
+    store(0, pre);
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+      const int sl = (t - t0) & 1;
+      if (t + 1 < t1) load(t + 1, pre);
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        const uint4 ah = *reinterpret_cast<const uint4 *>(&ka[lane & 31][kc * 16 + half * 8]);
-        const uint4 al = *reinterpret_cast<const uint4 *>(&kb[lane & 31][kc * 16 + half * 8]);
-        s = mfma_f16(ah, fqh[kc], s);
-        s = mfma_f16(ah, fql[kc], s);
-        s = mfma_f16(al, fqh[kc], s);
+        const uint4 ah = *reinterpret_cast<const uint4 *>(&sm.ka[sl][lane & 31][kc * 16 + half * 8]);
+        if (kind == kQuant) {
+          const uint4 al = *reinterpret_cast<const uint4 *>(&sm.kb[sl][lane & 31][kc * 16 + half * 8]);
+          s = mfma_f16(ah, fq0[kc], s);
+          s = mfma_f16(ah, fq1[kc], s);
+          s = mfma_f16(al, fq0[kc], s);
+        } else {
+          s = mfma_16bit<DT>(ah, fq0[kc], s);
+        }
       }
-      consume(s, [&](int m) {
-        const int64_t j = k0 + m;
-        return j <= qi - P.W && !((word >> m) & 1u);
-      });
-    }
-  }
-  // ---- stream 2: window keys i - W < j <= i (16-bit)
-  if (P.W > 0) {
-    const int64_t jlo = (q0 - P.W + 1 > 0) ? q0 - P.W + 1 : 0;
-    const int t0 = static_cast<int>(jlo / kBN), t1 = static_cast<int>(qlast / kBN);
-    for (int t = t0; t <= t1; ++t) {
       const int64_t k0 = static_cast<int64_t>(t) * kBN;
-      __syncthreads();
-      stage(P.k, nullptr, [&](int r) { return k0 + r < P.T ? k0 + r : int64_t(-1); });
-      __syncthreads();
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        s = mfma_16bit<DT>(*reinterpret_cast<const uint4 *>(&ka[lane & 31][kc * 16 + half * 8]), fqr[kc], s);
-      consume(s, [&](int m) {
-        const int64_t j = k0 + m;
-        return j > qi - P.W && j <= qi;
-      });
-    }
-  }
-  // ---- stream 3: VL keys j <= i - W (16-bit, gathered by index)
-  if (P.k_vl > 0) {
-    const int32_t *vl = P.vl_idx + (static_cast<int64_t>(b) * P.Hkv + h) * P.k_vl;
-    if (threadIdx.x == 0) {                 // VL positions <= qlast - W (ascending list)
-      int lo = 0, hi = P.k_vl;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (vl[mid] <= qlast - P.W) lo = mid + 1; else hi = mid;
+      if (kind == kQuant) {
+        const uint32_t word = P.vl_bits[bh * P.words + t];          // VL bits of keys k0 .. k0 + 31
+        consume(s, sl, [&](int m) { return k0 + m <= qi - P.W && !((word >> m) & 1u); });
+      } else if (kind == kWin) {
+        consume(s, sl, [&](int m) { return k0 + m > qi - P.W && k0 + m <= qi; });
+      } else {
+        consume(s, sl, [&](int m) {
+          const int64_t j = sm.pos[sl][m];
+          return j >= 0 && j <= qi - P.W;
+        });
       }
-      s_nvl = lo;
+      if (t + 1 < t1) store(sl ^ 1, pre);
+      __syncthreads();
     }
-    __syncthreads();
-    const int nvl = s_nvl;
-    for (int t = 0; t * kBN < nvl; ++t) {
-      __syncthreads();
-      if (threadIdx.x < kBN) tpos[threadIdx.x] = (t * kBN + static_cast<int>(threadIdx.x) < nvl)
-                                                      ? vl[t * kBN + threadIdx.x] : -1;
-      __syncthreads();
-      stage(P.k, nullptr, [&](int r) { return static_cast<int64_t>(tpos[r]); });
-      __syncthreads();
-      f32x16 s;
+  };
+
+  // ---- stream 1: quantized keys j <= i - W outside the VL set
+  {
+    uint4 fqh[8], fql[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int kc = 0; kc < 8; ++kc) {
+      const int64_t off = qrow * kD + kc * 16 + half * 8;
+      fqh[kc] = *reinterpret_cast<const uint4 *>(P.q_hi + off);
+      fql[kc] = *reinterpret_cast<const uint4 *>(P.q_lo + off);
+    }
+    const int64_t nkeys = qlast - P.W + 1;                    // keys 0 .. qlast - W
+    const int ntiles = nkeys > 0 ? static_cast<int>((nkeys + kBN - 1) / kBN) : 0;
+    run_stream(kQuant, 0, ntiles, fqh, fql);
+  }
+  {
+    uint4 fqr[8];
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        s = mfma_16bit<DT>(*reinterpret_cast<const uint4 *>(&ka[lane & 31][kc * 16 + half * 8]), fqr[kc], s);
-      consume(s, [&](int m) {
-        const int64_t j = tpos[m];
-        return j >= 0 && j <= qi - P.W;
-      });
+    for (int kc = 0; kc < 8; ++kc)
+      fqr[kc] = *reinterpret_cast<const uint4 *>(P.q + qrow * kD + kc * 16 + half * 8);
+    // ---- stream 2: window keys i - W < j <= i (16-bit)
+    if (P.W > 0) {
+      const int64_t jlo = (q0 - P.W + 1 > 0) ? q0 - P.W + 1 : 0;
+      run_stream(kWin, static_cast<int>(jlo / kBN), static_cast<int>(qlast / kBN) + 1, fqr, fqr);
+    }
+    // ---- stream 3: VL keys j <= i - W (16-bit, gathered by index)
+    if (P.k_vl > 0) {
+      if (threadIdx.x == 0) {                 // VL positions <= qlast - W (ascending list)
+        const int32_t *vl = P.vl_idx + bh * P.k_vl;
+        int lo = 0, hi = P.k_vl;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (vl[mid] <= qlast - P.W) lo = mid + 1; else hi = mid;
+        }
+        sm.nvl = lo;
+      }
+      __syncthreads();
+      const int nvl = sm.nvl;
+      run_stream(kVl, 0, (nvl + kBN - 1) / kBN, fqr, fqr);
     }
   }
 
@@ -366,17 +423,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams P) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct PrefillWs {
-  size_t q_hi, q_lo, k_hi, k_lo, bits, total;
+  size_t q_hi, q_lo, k_hi, k_lo, vt, vl_k, vl_vt, bits, total;
+  int ntk, nvt;
 };
-PrefillWs prefill_ws(int B, int Hq, int Hkv, int64_t T, int D) {
+PrefillWs prefill_ws(int B, int Hq, int Hkv, int64_t T, int D, int k_vl) {
   PrefillWs L{};
+  L.ntk = static_cast<int>((T + kBN - 1) / kBN);
+  L.nvt = (k_vl + kBN - 1) / kBN;
   const size_t qn = static_cast<size_t>(B) * Hq * T * D * 2, kn = static_cast<size_t>(B) * Hkv * T * D * 2;
+  const size_t vtn = static_cast<size_t>(B) * Hkv * L.ntk * kBN * D * 2;
+  const size_t vln = static_cast<size_t>(B) * Hkv * L.nvt * kBN * D * 2;
   const size_t words = static_cast<size_t>((T + 31) / 32);
   L.q_hi = 0;
   L.q_lo = align_up(L.q_hi + qn, 256);
   L.k_hi = align_up(L.q_lo + qn, 256);
   L.k_lo = align_up(L.k_hi + kn, 256);
-  L.bits = align_up(L.k_lo + kn, 256);
+  L.vt = align_up(L.k_lo + kn, 256);
+  L.vl_k = align_up(L.vt + vtn, 256);
+  L.vl_vt = align_up(L.vl_k + vln, 256);
+  L.bits = align_up(L.vl_vt + vln, 256);
   L.total = L.bits + static_cast<size_t>(B) * Hkv * words * 4;
   return L;
 }
@@ -386,9 +451,9 @@ PrefillWs prefill_ws(int B, int Hq, int Hkv, int64_t T, int D) {
 
 using namespace hq;
 
-extern "C" size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || D < 1) return 0;
-  return prefill_ws(B, Hq, Hkv, T, D).total;
+extern "C" size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D, int k_vl) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || D < 1 || k_vl < 0) return 0;
+  return prefill_ws(B, Hq, Hkv, T, D, k_vl).total;
 }
 
 extern "C" hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype dtype, int B,
@@ -408,52 +473,65 @@ extern "C" hq_status hq_prefill_attn(const void *q, const void *k, const void *v
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
        reinterpret_cast<uintptr_t>(out)) % 16)
     return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: q, k, v and out must be 16-byte aligned");
-  // thread counts of the pre-pass and the row indices stay below 2^31
+  // thread counts of the pre-pass stay below 2^31
   if (static_cast<double>(B) * Hq * T * (D / 32) * 4 > 2.0e9)
     return fail(HQ_ERR_UNSUPPORTED, "hq_prefill_attn: too many query rows for one call");
-  const PrefillWs L = prefill_ws(B, Hq, Hkv, T, D);
+  const PrefillWs L = prefill_ws(B, Hq, Hkv, T, D, k_vl);
   if (!ws || ws_bytes < L.total)
     return fail(HQ_ERR_WORKSPACE, "hq_prefill_attn: workspace needs %zu bytes, got %zu", L.total, ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) % 256)
     return fail(HQ_ERR_INVALID_ARG, "hq_prefill_attn: workspace must be 256-byte aligned");
   hipStream_t st = as_stream(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
+  uint16_t *qh = reinterpret_cast<uint16_t *>(w8 + L.q_hi), *ql = reinterpret_cast<uint16_t *>(w8 + L.q_lo);
+  uint16_t *kh = reinterpret_cast<uint16_t *>(w8 + L.k_hi), *kl = reinterpret_cast<uint16_t *>(w8 + L.k_lo);
+  uint16_t *vt = reinterpret_cast<uint16_t *>(w8 + L.vt);
+  uint16_t *vlk = reinterpret_cast<uint16_t *>(w8 + L.vl_k), *vlvt = reinterpret_cast<uint16_t *>(w8 + L.vl_vt);
+  uint32_t *bits = reinterpret_cast<uint32_t *>(w8 + L.bits);
+  const uint16_t *q16 = static_cast<const uint16_t *>(q), *k16 = static_cast<const uint16_t *>(k);
+  const uint16_t *v16 = static_cast<const uint16_t *>(v);
+
+  // pre-pass: split dequantized Q and K; V^T tiles; VL K rows and V^T tiles
+  const uint32_t qrows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hq * T);
+  const uint32_t krows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hkv * T);
+  const uint32_t qthreads = qrows * (D / 32) * 4, kthreads = krows * (D / 32) * 4;
+  const int heads = B * Hkv;
+  const int64_t vthreads = static_cast<int64_t>(heads) * L.ntk * kBN * (kD / 8);
+  const int64_t lthreads = static_cast<int64_t>(heads) * L.nvt * kBN * (kD / 8);
+#define HQ_PRE(DT_)                                                                                        \
+  do {                                                                                                     \
+    hipLaunchKernelGGL(split_kernel<DT_>, dim3((qthreads + 255) / 256), dim3(256), 0, st, q, qrows, D, qh, ql); \
+    hipLaunchKernelGGL(split_kernel<DT_>, dim3((kthreads + 255) / 256), dim3(256), 0, st, k, krows, D, kh, kl); \
+    hipLaunchKernelGGL(tile_kernel<DT_>, dim3(static_cast<unsigned>((vthreads + 255) / 256)), dim3(256), 0, st,   \
+                       v16, nullptr, T, nullptr, 0, L.ntk, heads, vt, nullptr);                            \
+    if (L.nvt > 0)                                                                                         \
+      hipLaunchKernelGGL(tile_kernel<DT_>, dim3(static_cast<unsigned>((lthreads + 255) / 256)), dim3(256), 0, st, \
+                         v16, k16, T, vl_idx, k_vl, L.nvt, heads, vlvt, vlk);                              \
+  } while (0)
+  if (dtype == HQ_BF16) HQ_PRE(HQ_BF16);
+  else HQ_PRE(HQ_F16);
+#undef HQ_PRE
+  hq_status s = check_launch("hq_prefill_attn (pre-pass)");
+  if (s != HQ_OK) return s;
+  // VL membership bitmap (no VL: an all-zero bitmap)
+  s = hq_vl_bitmap(vl_idx, heads, k_vl, ((T + 31) / 32) * 32, bits, stream);
+  if (s != HQ_OK) return s;
+
   PrefillParams P{};
-  P.q = static_cast<const uint16_t *>(q);
-  P.k = static_cast<const uint16_t *>(k);
-  P.v = static_cast<const uint16_t *>(v);
-  P.q_hi = reinterpret_cast<uint16_t *>(w8 + L.q_hi);
-  P.q_lo = reinterpret_cast<uint16_t *>(w8 + L.q_lo);
-  P.k_hi = reinterpret_cast<uint16_t *>(w8 + L.k_hi);
-  P.k_lo = reinterpret_cast<uint16_t *>(w8 + L.k_lo);
+  P.q = q16;
+  P.k = k16;
+  P.q_hi = qh; P.q_lo = ql; P.k_hi = kh; P.k_lo = kl;
+  P.vt = vt; P.vl_k = vlk; P.vl_vt = vlvt;
   P.vl_idx = vl_idx;
-  P.vl_bits = reinterpret_cast<uint32_t *>(w8 + L.bits);
+  P.vl_bits = bits;
   P.out = out;
   P.lse = lse;
   P.T = T;
   P.words = (T + 31) / 32;
   P.B = B; P.Hq = Hq; P.Hkv = Hkv; P.G = Hq / Hkv; P.W = W; P.k_vl = k_vl;
   P.n_qt = static_cast<int>((T + kBM - 1) / kBM);
+  P.ntk = L.ntk; P.nvt = L.nvt;
   P.cs = (sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(D))) * kLog2e;
-
-  // pre-pass: split dequantized Q and K
-  const uint32_t qrows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hq * T);
-  const uint32_t krows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hkv * T);
-  const uint32_t qthreads = qrows * (D / 32) * 4, kthreads = krows * (D / 32) * 4;
-  uint16_t *qh = reinterpret_cast<uint16_t *>(w8 + L.q_hi), *ql = reinterpret_cast<uint16_t *>(w8 + L.q_lo);
-  uint16_t *kh = reinterpret_cast<uint16_t *>(w8 + L.k_hi), *kl = reinterpret_cast<uint16_t *>(w8 + L.k_lo);
-  if (dtype == HQ_BF16) {
-    hipLaunchKernelGGL(split_kernel<HQ_BF16>, dim3((qthreads + 255) / 256), dim3(256), 0, st, q, qrows, D, qh, ql);
-    hipLaunchKernelGGL(split_kernel<HQ_BF16>, dim3((kthreads + 255) / 256), dim3(256), 0, st, k, krows, D, kh, kl);
-  } else {
-    hipLaunchKernelGGL(split_kernel<HQ_F16>, dim3((qthreads + 255) / 256), dim3(256), 0, st, q, qrows, D, qh, ql);
-    hipLaunchKernelGGL(split_kernel<HQ_F16>, dim3((kthreads + 255) / 256), dim3(256), 0, st, k, krows, D, kh, kl);
-  }
-  hq_status s = check_launch("hq_prefill_attn (pre-pass)");
-  if (s != HQ_OK) return s;
-  // VL membership bitmap (no VL: an all-zero bitmap)
-  s = hq_vl_bitmap(vl_idx, B * Hkv, k_vl, P.words * 32, const_cast<uint32_t *>(P.vl_bits), stream);
-  if (s != HQ_OK) return s;
   const unsigned blocks = static_cast<unsigned>(P.n_qt) * B * Hq;
   if (dtype == HQ_BF16)
     hipLaunchKernelGGL(prefill_kernel<HQ_BF16>, dim3(blocks), dim3(kThreads), 0, st, P);

@@ -250,8 +250,8 @@ int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
  * positions in [0, T) (not checked on the device); out [B][Hq][T][D];
  * sm_scale <= 0 means 1/sqrt(D). Requires D == 128, group == 32,
  * Hq % Hkv == 0. ws: at least hq_prefill_workspace_size bytes, 256-byte
- * aligned, no initialisation needed (it holds the split dequantized Q and K
- * and the VL bitmap). Precision: the quantized logits are within about 2^-21
+ * aligned, no initialisation needed (it holds the split dequantized Q and K,
+ * V and the VL rows in 32-key tiles, and the VL bitmap). Precision: the quantized logits are within about 2^-21
  * (relative) of the exact q_hat . k_hat; the probabilities are rounded to
  * fp16 for the P . V product.
  */
@@ -260,7 +260,7 @@ hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype 
                           float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
                           void *stream);
 
-size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D);
+size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D, int k_vl);
 
 const char *hq_status_string(hq_status s);
 const char *hq_last_error(void);

@@ -35,7 +35,7 @@ def _run(w, q, K, V, vl):
     out = torch.full((B, Hq, T, D), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, Hq, T), float("nan"), dtype=torch.float32, device="cuda")
     # the workspace needs no initialisation: start from garbage
-    ws = torch.full((hq.hq_prefill_workspace_size(B, Hq, Hkv, T, D),), 0xFF, dtype=torch.uint8, device="cuda")
+    ws = torch.full((hq.hq_prefill_workspace_size(B, Hq, Hkv, T, D, k),), 0xFF, dtype=torch.uint8, device="cuda")
     hq.hq_prefill_attn(qd, kd, vd, B, Hq, Hkv, T, D, w.W, vld, k, 0.0, out, lse, ws)
     torch.cuda.synchronize()
     return out, lse
