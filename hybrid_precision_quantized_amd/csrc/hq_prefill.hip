@@ -56,6 +56,16 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer view [base + off, base + bytes), empty when off >= bytes (off is
+// wave-uniform and both are below 2^31: a signed max keeps it scalar); loads
+// past the end of the view return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t view(const uint8_t *base, uint32_t bytes, uint32_t off) {
+  const int32_t rem = static_cast<int32_t>(bytes) - static_cast<int32_t>(off);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base + off), static_cast<short>(0),
+                                           rem > 0 ? rem : 0, 0x00020000);
+}
 
 constexpr int kD = 128;          // head_dim
 constexpr int kBM = 128;         // query rows per workgroup
@@ -221,7 +231,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
   const int64_t krow0 = bh * P.T;                            // first K row of the KV head
   const int64_t qlast = (q0 + kBM - 1 < P.T - 1) ? q0 + kBM - 1 : P.T - 1;
 
-  float m_run = -__FLT_MAX__;        // running max (finite: the rescale runs first)
+  // running max of the raw logits; starts finite (the rescale runs before any
+  // finite logit is used) and small enough that -cs * m_run stays finite
+  float m_run = -1e30f;
   float l_run = 0.f;                 // this lane's share of the row sum
   f32x16 o[4];
 #pragma unroll
@@ -231,19 +243,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
 
   auto key_of = [&](int r) { return 8 * (r >> 2) + 4 * half + (r & 3); };
 
-  // ---- one 32-key tile from LDS slot `sl`: mask, online softmax, P . V
-  auto consume = [&](f32x16 &s, int sl, auto valid) {
+  // ---- one 32-key tile from LDS slot `sl`: mask, online softmax, P . V.
+  // okm: this lane's valid keys of the tile as a bit mask over the register
+  // key order c = 8 (r / 4) + (r % 4) (key 4 half + c); all_ok: the whole
+  // tile is valid for every lane of the wave (no per-element mask).
+  auto consume = [&](f32x16 &s, int sl, uint32_t okm, bool all_ok) {
+    if (!all_ok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        s[r] = ((okm >> c) & 1u) ? s[r] : kNegInf;
+      }
+    }
     float tmax = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok = q_ok && valid(key_of(r));
-      s[r] = ok ? s[r] * P.cs : kNegInf;
-      tmax = fmaxf(tmax, s[r]);
-    }
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // the running max m_run is kept in raw logit units (before sm_scale, which
+    // is positive); p = 2^(cs (s - m_run))
     if (__builtin_expect(__ballot(tmax > m_run) != 0, 0)) {
       const float mn = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - mn);
+      const float alpha = __builtin_amdgcn_exp2f(P.cs * (m_run - mn));
       m_run = mn;
       l_run *= alpha;
 #pragma unroll
@@ -251,11 +271,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
+    const float nm = -P.cs * m_run;
     uint32_t pk[8];
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2f(s[r] - m_run), p1 = exp2f(s[r + 1] - m_run);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], P.cs, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], P.cs, nm));
       ls += p0 + p1;
       pk[r / 2] = pack2_f16(p0, p1);
     }
@@ -272,11 +294,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
       }
     }
   };
+  // bits c of the register key order for which key 4 half + c lies in (lo, hi]
+  // (tile-relative keys; lo < hi)
+  auto range_mask = [&](int lo, int hi) {
+    lo -= 4 * half;
+    hi -= 4 * half;
+    const uint32_t upto = hi >= 31 ? 0xFFFFFFFFu : (hi < 0 ? 0u : ((2u << hi) - 1u));
+    const uint32_t below = lo >= 31 ? 0xFFFFFFFFu : (lo < 0 ? 0u : ((2u << lo) - 1u));
+    return upto & ~below;
+  };
+  // the first and last query rows of this wave
+  const int64_t wq0 = q0 + wave * 32;
+  const int64_t wq1 = (wq0 + 31 < P.T - 1) ? wq0 + 31 : P.T - 1;
 
   // ---- a stream of 32-key tiles t0 .. t1 - 1, staged through two LDS slots
   // with the next tile's global loads in flight during each tile's MFMAs
   struct Pre {
-    uint4 a[2], b[2], v[2];
+    u32x4 a[2], b[2], v[2];
     int32_t pos;
   };
   auto run_stream = [&](const int kind, const int t0, const int t1, const uint4 (&fq0)[8],
@@ -284,28 +318,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
     if (t0 >= t1) return;
     const bool two = kind == kQuant;
     const uint16_t *kpa = kind == kQuant ? P.k_hi : (kind == kWin ? P.k : P.vl_k);
-    const uint16_t *kpb = P.k_lo;
     const int64_t krows = kind == kVl ? static_cast<int64_t>(P.nvt) * kBN : P.T;   // rows per head
-    const uint16_t *vsrc = kind == kVl ? P.vl_vt : P.vt;
-    const int vtiles = kind == kVl ? P.nvt : P.ntk;
+    const uint8_t *ka_base = reinterpret_cast<const uint8_t *>(kpa + bh * krows * kD);
+    const uint8_t *kb_base = reinterpret_cast<const uint8_t *>(P.k_lo + bh * krows * kD);
+    const uint32_t kbytes = static_cast<uint32_t>(krows) * kD * 2;
+    const uint8_t *v_base = reinterpret_cast<const uint8_t *>(
+        (kind == kVl ? P.vl_vt : P.vt) + bh * (kind == kVl ? P.nvt : P.ntk) * (kD * kBN));
+    const uint32_t vbytes = static_cast<uint32_t>(kind == kVl ? P.nvt : P.ntk) * (kD * kBN) * 2;
     const int32_t *vl = P.vl_idx + bh * P.k_vl;
+    // per-thread byte offsets inside a tile (K rows past the end read as 0)
+    const uint32_t lk0 = threadIdx.x * 16, lk1 = (kThreads + threadIdx.x) * 16;
     auto load = [&](int t, Pre &L) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int idx = e * kThreads + threadIdx.x;      // 512 uint4 per K plane
-        const int r = idx >> 4, c = idx & 15;
-        const int64_t row = static_cast<int64_t>(t) * kBN + r;
-        uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
-        if (row < krows) {
-          const int64_t off = (bh * krows + row) * kD + c * 8;
-          va = *reinterpret_cast<const uint4 *>(kpa + off);
-          if (two) vb = *reinterpret_cast<const uint4 *>(kpb + off);
-        }
-        L.a[e] = va;
-        L.b[e] = vb;
-        // V^T tile: 8 KB contiguous
-        L.v[e] = reinterpret_cast<const uint4 *>(vsrc + (bh * vtiles + t) * (kD * kBN))[idx];
+      const uint32_t toff = static_cast<uint32_t>(t) * kBN * kD * 2;     // wave-uniform
+      const __amdgpu_buffer_rsrc_t rka = view(ka_base, kbytes, toff);
+      L.a[0] = __builtin_amdgcn_raw_buffer_load_b128(rka, lk0, 0, 0);
+      L.a[1] = __builtin_amdgcn_raw_buffer_load_b128(rka, lk1, 0, 0);
+      if (two) {
+        const __amdgpu_buffer_rsrc_t rkb = view(kb_base, kbytes, toff);
+        L.b[0] = __builtin_amdgcn_raw_buffer_load_b128(rkb, lk0, 0, 0);
+        L.b[1] = __builtin_amdgcn_raw_buffer_load_b128(rkb, lk1, 0, 0);
       }
+      const __amdgpu_buffer_rsrc_t rv = view(v_base, vbytes, toff);
+      L.v[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, lk0, 0, 0);
+      L.v[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, lk1, 0, 0);
       L.pos = 0;
       if (kind == kVl && threadIdx.x < kBN) {
         const int j = t * kBN + static_cast<int>(threadIdx.x);
@@ -317,10 +352,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
       for (int e = 0; e < 2; ++e) {
         const int idx = e * kThreads + threadIdx.x;
         const int r = idx >> 4, c = idx & 15;
-        *reinterpret_cast<uint4 *>(&sm.ka[sl][r][c * 8]) = L.a[e];
-        if (two) *reinterpret_cast<uint4 *>(&sm.kb[sl][r][c * 8]) = L.b[e];
+        *reinterpret_cast<u32x4 *>(&sm.ka[sl][r][c * 8]) = L.a[e];
+        if (two) *reinterpret_cast<u32x4 *>(&sm.kb[sl][r][c * 8]) = L.b[e];
         const int d = idx >> 2, k8 = (idx & 3) * 8;       // V^T: row d, keys k8 .. k8 + 7
-        *reinterpret_cast<uint4 *>(&sm.vt[sl][d][k8]) = L.v[e];
+        *reinterpret_cast<u32x4 *>(&sm.vt[sl][d][k8]) = L.v[e];
       }
       if (kind == kVl && threadIdx.x < kBN) sm.pos[sl][threadIdx.x] = L.pos;
     };
@@ -348,15 +383,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
       }
       const int64_t k0 = static_cast<int64_t>(t) * kBN;
       if (kind == kQuant) {
-        const uint32_t word = P.vl_bits[bh * P.words + t];          // VL bits of keys k0 .. k0 + 31
-        consume(s, sl, [&](int m) { return k0 + m <= qi - P.W && !((word >> m) & 1u); });
+        // keys k0 + m <= qi - W outside the VL set
+        const uint32_t word = P.vl_bits[bh * P.words + t];         // VL bits of keys k0 .. k0 + 31
+        const bool full = k0 + kBN - 1 <= wq0 - P.W && word == 0u;   // wave-uniform
+        const int hi = static_cast<int>(qi - P.W - k0 < 64 ? qi - P.W - k0 : 64);
+        // register key order: bit c <-> key 4 half + c, i.e. VL bit 4 half + c
+        const uint32_t vlr = word >> (4 * half);
+        consume(s, sl, range_mask(-1, hi) & ~vlr, full);
       } else if (kind == kWin) {
-        consume(s, sl, [&](int m) { return k0 + m > qi - P.W && k0 + m <= qi; });
+        // keys qi - W < k0 + m <= qi
+        const bool full = k0 > wq1 - P.W && k0 + kBN - 1 <= wq0;
+        const int64_t lo64 = qi - P.W - k0, hi64 = qi - k0;
+        const int lo = static_cast<int>(lo64 < -1 ? -1 : (lo64 > 64 ? 64 : lo64));
+        const int hi = static_cast<int>(hi64 < -1 ? -1 : (hi64 > 64 ? 64 : hi64));
+        consume(s, sl, range_mask(lo, hi), full);
       } else {
-        consume(s, sl, [&](int m) {
-          const int64_t j = sm.pos[sl][m];
-          return j >= 0 && j <= qi - P.W;
-        });
+        uint32_t okm = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          const int64_t j = sm.pos[sl][4 * half + c];
+          okm |= static_cast<uint32_t>(j >= 0 && j <= qi - P.W) << c;
+        }
+        consume(s, sl, okm, false);
       }
       if (t + 1 < t1) store(sl ^ 1, pre);
       __syncthreads();
@@ -416,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
         *reinterpret_cast<float4 *>(orow + d) =
             make_float4(o[dt][r] * inv, o[dt][r + 1] * inv, o[dt][r + 2] * inv, o[dt][r + 3] * inv);
       }
-    if (half == 0 && P.lse) P.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
+    if (half == 0 && P.lse) P.lse[qrow] = (P.cs * m_run + log2f(l_tot)) * kLn2;
   }
 }
 
