@@ -366,21 +366,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
     for (int t = t0; t < t1; ++t) {
       const int sl = (t - t0) & 1;
       if (t + 1 < t1) load(t + 1, pre);
-      f32x16 s;
+      // two independent accumulator chains (the hi . lo term in s2) so that
+      // consecutive MFMAs do not wait on each other's results
+      f32x16 s, s2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s2[r] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
         const uint4 ah = *reinterpret_cast<const uint4 *>(&sm.ka[sl][lane & 31][kc * 16 + half * 8]);
         if (kind == kQuant) {
           const uint4 al = *reinterpret_cast<const uint4 *>(&sm.kb[sl][lane & 31][kc * 16 + half * 8]);
           s = mfma_f16(ah, fq0[kc], s);
-          s = mfma_f16(ah, fq1[kc], s);
+          s2 = mfma_f16(ah, fq1[kc], s2);
           s = mfma_f16(al, fq0[kc], s);
+        } else if (kc & 1) {
+          s2 = mfma_16bit<DT>(ah, fq0[kc], s2);
         } else {
           s = mfma_16bit<DT>(ah, fq0[kc], s);
         }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] += s2[r];
       const int64_t k0 = static_cast<int64_t>(t) * kBN;
       if (kind == kQuant) {
         // keys k0 + m <= qi - W outside the VL set
