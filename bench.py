@@ -36,7 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode attention µs/step and achieved HBM GB/s (% of peak) at 32K/128K ctx"
+PREFILL_METRIC = "hybrid prefill attention ms/step and algorithmic TFLOP/s (causal 32K prompt)"
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0          # dense f16 / bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
@@ -45,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="llama32k", choices=["llama32k", "qwen128k", "glm32k"])
+    ap.add_argument("--workload", default="llama32k",
+                    choices=["llama32k", "qwen128k", "glm32k", "prefill32k"],
+                    help="decode workloads, or prefill32k: the causal hybrid prefill of a 32K prompt")
     ap.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0 = auto, >= 1 GB)")
     ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum"])
     ap.add_argument("--splits", type=int, default=0)
@@ -81,6 +85,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "prefill32k":
+        return main_prefill(args)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     w = synth.WORKLOADS[args.workload]
@@ -268,6 +274,150 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def main_prefill(args):
+    """One step = the prefill of one attention layer over a causal prompt:
+    the vertical lines are chosen from the prompt's last 64 queries
+    (hq_detect_vlines), then hq_prefill_attn computes every row's output and
+    log-sum-exp. `value` is the algorithmic flops of the attention (Q K^T
+    and P V over the causal triangle, 2 flops per multiply-add) divided by
+    the step time."""
+    import torch
+    import hybrid_precision_quantized_amd as hq
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS[args.workload]
+    B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
+    R = 64
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    t_setup = time.time()
+
+    def to_dev(x32):
+        if w.dtype == "bf16":
+            return torch.from_numpy(synth.f32_to_bf16_bits(x32).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float16)).to(dev)
+
+    q = torch.empty((B, Hq, T, D), dtype=dt, device=dev)
+    for b in range(B):
+        for i in range(Hq):
+            q[b, i].copy_(to_dev(synth.prefill_queries(w, b, i)))
+    K = to_dev(synth.all_keys(w))
+    V = to_dev(synth.all_values(w))
+    q_last = q[:, :, T - R:].contiguous()              # the detector's 64-query window
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
+    det_ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, T - W, k), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(hq.hq_prefill_workspace_size(B, Hq, Hkv, T, D, k), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    def detect():
+        hq.hq_detect_vlines(None, q_last, B, Hq, Hkv, D, R, 0, True, K, T, T - W, k,
+                            hq.HQ_DETECT_MATMUL, idx, None, det_ws)
+
+    def prefill():
+        hq.hq_prefill_attn(q, K, V, B, Hq, Hkv, T, D, W, idx, k, 0.0, out, lse, ws)
+
+    steps = max(1, min(args.steps, 20))
+    warm = max(1, min(args.warmup, 3))
+    for _ in range(warm):
+        detect()
+        prefill()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        detect()
+        prefill()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+
+    # hq_prefill_attn alone, per call (pre-pass + tiling + the attention kernel)
+    n_l = max(3, min(args.kernel_launches, 10))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_l)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_l)]
+    for i in range(n_l):
+        starts[i].record(stream)
+        prefill()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+
+    flops = 2.0 * 2.0 * B * Hq * D * (T * (T + 1) / 2.0)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_seconds, flops)
+    line = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 q/k (f16 hi+lo MFMA) + bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded; shapes of the named model's attention layer, random-init values)",
+        "config": {
+            "workload": f"prefill32k: causal prefill of one attention layer, B {B}, {Hq} q / {Hkv} kv heads, "
+                        f"head_dim {D}, prompt {T}, window {W}, VL budget {k} (detected from the last "
+                        f"{R} queries), INT4 group 32 for the quantized Q.K majority",
+            "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "prefill_kernel (hq_prefill_attn, timed per call incl. its pre-pass)",
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": int(flops),
+            "avg_launch_ms": round(call_ms, 4),
+        },
+        "setup_s": round(t_setup, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_prefill(w, seconds: float, flops: float):
+    """The CPU oracle prefill (unchanged) on a bounded sample: blocks of query
+    rows of KV head 0's group, repeated until `seconds` of work, scaled to
+    every row of every head (its cost per row does not depend on the row)."""
+    import synth
+    from oracle import prefill
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    q = np.stack([synth.prefill_queries(w, 0, i) for i in range(w.G)])
+    K = synth.keys(w, 0, 0)
+    V = synth.values(w, 0, 0)
+    vl = synth.random_vl_index(w, 0, 0)
+    rng = np.random.default_rng(5)
+    t0 = time.time()
+    n_rows = 0
+    while time.time() - t0 < seconds and n_rows < 4096:
+        rows = np.sort(rng.choice(w.T, size=32, replace=False))
+        prefill.prefill_rows(q, K, V, vl, w.W, rows)
+        n_rows += len(rows)
+    el = time.time() - t0
+    per_row_head = el / (n_rows * w.G)
+    s_total = per_row_head * w.T * w.Hq * w.B
+    return {"value": round(flops / s_total / 1e12, 6), "unit": "TFLOP/s", "ms_per_step": round(s_total * 1e3, 1),
+            "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} random query rows x {w.G} heads of KV head 0 ({el:.1f} s), "
+                      f"scaled to all {w.T} rows x {w.Hq} heads"}
 
 
 def cpu_baseline(w, seconds: float, step_bytes: float):

@@ -222,6 +222,20 @@ __device__ __forceinline__ void raise_max(const float (&lg)[HB], WaveState<HB> &
 // ---------------------------------------------------------------- INT4 pass
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Wave priority from the share of the split still to do (c of n chunks
+// done, both wave-uniform). The instruction arbiter of a SIMD prefers the
+// higher user priority and, among equals, the older wave; with equal
+// priorities the first block on a CU runs ahead and the second finishes
+// alone at low occupancy. Raising the priority of the wave that is further
+// behind keeps co-resident waves abreast, so they finish together.
+__device__ __forceinline__ void prio_by_remaining(uint32_t c, uint32_t n) {
+  const uint32_t rem = c < n ? n - c : 0u;
+  if (rem * 2u > n) __builtin_amdgcn_s_setprio(3);
+  else if (rem * 4u > n) __builtin_amdgcn_s_setprio(2);
+  else if (rem * 8u > n) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Buffer resource over [base, base + bytes): loads past the end return 0,
 // so ragged tails need no branch, and offsets are 32-bit.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -463,6 +477,7 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   for (; cb + (NPF - 1) * kWaves < nsteps; cb += NPF * kWaves) {
 #pragma unroll
     for (int jr = 0; jr < NPF; ++jr) {
+      prio_by_remaining(cb + jr * kWaves, nsteps);
       step(cb + jr * kWaves, ring[jr]);
       issue(cb + jr * kWaves + NPF * kWaves, ring[jr]);
     }
@@ -470,7 +485,10 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
   // the last NPF - 1 steps at most
 #pragma unroll
   for (int jr = 0; jr < NPF - 1; ++jr)
-    if (cb + jr * kWaves < nsteps) step(cb + jr * kWaves, ring[jr]);
+    if (cb + jr * kWaves < nsteps) {
+      prio_by_remaining(cb + jr * kWaves, nsteps);
+      step(cb + jr * kWaves, ring[jr]);
+    }
 
   // ---- per-(head, group) zero-point sums, folded into the accumulators
 #pragma unroll
@@ -696,6 +714,7 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
   for (; cb + (NPF - 1) * kWaves < nsteps; cb += NPF * kWaves) {
 #pragma unroll
     for (int jr = 0; jr < NPF; ++jr) {
+      prio_by_remaining(cb + jr * kWaves, nsteps);
       step(cb + jr * kWaves, ring[jr]);
       issue(cb + jr * kWaves + NPF * kWaves, ring[jr]);
     }
@@ -703,7 +722,10 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
   // the last NPF - 1 steps at most
 #pragma unroll
   for (int jr = 0; jr < NPF - 1; ++jr)
-    if (cb + jr * kWaves < nsteps) step(cb + jr * kWaves, ring[jr]);
+    if (cb + jr * kWaves < nsteps) {
+      prio_by_remaining(cb + jr * kWaves, nsteps);
+      step(cb + jr * kWaves, ring[jr]);
+    }
 
   // ---- per-(head, group) zero-point sums, folded into the accumulators; the
   // wave state of head hh lives in lane hh's quad position
@@ -820,6 +842,7 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
   // needs no condition
   issue(wave, cur);
   for (int64_t c = wave; c < nsteps; c += kWaves) {
+    prio_by_remaining(static_cast<uint32_t>(c), static_cast<uint32_t>(nsteps));
     issue(c + kWaves, nxt);
     const int64_t f0 = r0 + c * SLOTS;
     const bool tv = f0 + slot < r1;
@@ -1035,13 +1058,17 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
   for (; cb + (NPF - 1) * kWaves < nsteps; cb += NPF * kWaves) {
 #pragma unroll
     for (int jr = 0; jr < NPF; ++jr) {
+      prio_by_remaining(cb + jr * kWaves, nsteps);
       step(cb + jr * kWaves, ring[jr]);
       issue(cb + jr * kWaves + NPF * kWaves, ring[jr]);
     }
   }
 #pragma unroll
   for (int jr = 0; jr < NPF - 1; ++jr)
-    if (cb + jr * kWaves < nsteps) step(cb + jr * kWaves, ring[jr]);
+    if (cb + jr * kWaves < nsteps) {
+      prio_by_remaining(cb + jr * kWaves, nsteps);
+      step(cb + jr * kWaves, ring[jr]);
+    }
 
   const float lsum = xor_sum<LPT>(lown);
 #pragma unroll
@@ -1144,27 +1171,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------- split merge
-// One block per (unit, query head): out = sum_s w_s o_s / L with
-// w_s = 2^(m_s - m*), m* = max_s m_s and L = sum_s w_s l_s; lse = (m* + log2 L) ln 2.
-// A kernel of its own: the launch boundary makes every split's partial
-// visible without device-scope fences inside the split kernel. Thread s
-// computes the weight of split s once. The partial outputs go through LDS 64
-// splits at a time, every load of a stage issued before any is used (the
-// first stage's loads overlap the reductions), and kThreads / D threads per
-// channel sum interleaved splits; their sums are combined in a fixed order,
-// so the result is deterministic.
-constexpr int kMergeStage = 64;
+// One block per (unit, query head, 32-channel slice): out = sum_s w_s o_s / L
+// with w_s = 2^(m_s - m*), m* = max_s m_s and L = sum_s w_s l_s; lse = (m* +
+// log2 L) ln 2. A kernel of its own: the launch boundary makes every split's
+// partial visible without device-scope fences inside the split kernel. All
+// loads are issued first. Each wave finds m* and L over all splits by itself
+// (the same values in the same lanes and the same reduction order, so every
+// wave gets the same numbers); thread t weights float4 t % 8 of the slice for
+// the splits t / 8, t / 8 + 32, ..., and the 32 split groups are summed in a
+// fixed order, so the result is deterministic.
+constexpr int kMergeSlice = 32;
 template <int D, int HB>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
-  static_assert(kThreads >= kMaxSplits, "one thread per split");
-  constexpr int TPD = kThreads / D;                      // threads per output channel
-  constexpr int PER = kMergeStage * D / 4 / kThreads;    // float4 per thread per stage
-  __shared__ float4 so[kMergeStage * D / 4];
+  constexpr int NSL = D / kMergeSlice;            // slices per head
+  constexpr int F4 = kMergeSlice / 4;             // float4 per slice row
+  constexpr int SG = kThreads / F4;               // split groups
+  constexpr int MAXO = kMaxSplits / SG;           // partial rows per thread at most
+  constexpr int MAXM = kMaxSplits / 64;           // (m, l) pairs per lane at most
+  static_assert(kMaxSplits % SG == 0 && kMaxSplits % 64 == 0, "split tiling");
   __shared__ float sw[kMaxSplits];
-  __shared__ float red_m[kWaves], red_l[kWaves];
-  __shared__ float part[TPD][D];
-  const int unit = blockIdx.x / HB;
-  const int hh = blockIdx.x % HB;
+  __shared__ float4 red[SG][F4];
+  const int sl = blockIdx.x % NSL;
+  const int qh = blockIdx.x / NSL;
+  const int unit = qh / HB;
+  const int hh = qh % HB;
   const int hc = unit % P.nhc;
   const int bh = unit / P.nhc;
   const int h = bh % P.Hkv;
@@ -1173,60 +1203,58 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
   const int S = P.S;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const float4 *po = reinterpret_cast<const float4 *>(P.part_o) + qi * S * (D / 4);
-  const float2 ml = t < S ? P.part_ml[qi * S + t] : make_float2(kNegInf, 0.f);
-  float4 v[PER];
-  auto load_stage = [&](int s0) {
-    const int ne = ((S - s0) < kMergeStage ? (S - s0) : kMergeStage) * (D / 4);
+  const int f = t % F4, sg = t / F4;
+  const float4 *po = reinterpret_cast<const float4 *>(P.part_o) + qi * S * (D / 4) + sl * F4 + f;
+  float4 v[MAXO];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = i * kThreads + t;
-      v[i] = e < ne ? po[static_cast<int64_t>(s0) * (D / 4) + e] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  load_stage(0);
-  // m* over the splits, the weights and L
-  float mx = ml.x;
+  for (int i = 0; i < MAXO; ++i) {
+    const int sp = sg + i * SG;
+    v[i] = sp < S ? po[static_cast<int64_t>(sp) * (D / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float2 ml[MAXM];
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) {
+    const int sp = lane + 64 * i;
+    ml[i] = sp < S ? P.part_ml[qi * S + sp] : make_float2(kNegInf, 0.f);
+  }
+  float mx = ml[0].x;
+#pragma unroll
+  for (int i = 1; i < MAXM; ++i) mx = fmaxf(mx, ml[i].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
-  if (lane == 0) red_m[wave] = mx;
-  __syncthreads();
-  mx = red_m[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red_m[w]);
   const float mu = (mx == kNegInf) ? 0.f : mx;
-  const float wgt = t < S ? fast_exp2(ml.x - mu) : 0.f;
-  if (t < kMaxSplits) sw[t] = wgt;
-  float lw = wgt * ml.y;
+  float lw = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) {
+    const int sp = lane + 64 * i;
+    const float wgt = sp < S ? fast_exp2(ml[i].x - mu) : 0.f;
+    if (wave == 0 && sp < S) sw[sp] = wgt;
+    lw = fmaf(wgt, ml[i].y, lw);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) lw += shfl_xor_f(lw, o);
-  if (lane == 0) red_l[wave] = lw;
-  // channel d, splits q, q + TPD, ... of each stage
-  const int d = t % D, q = t / D;
-  const float *sf = reinterpret_cast<const float *>(so);
-  float acc = 0.f;
-  for (int s0 = 0; s0 < S; s0 += kMergeStage) {
-    if (s0) {
-      __syncthreads();          // the previous stage is consumed
-      load_stage(s0);
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) so[i * kThreads + t] = v[i];
-    __syncthreads();
-    const int ns = (S - s0) < kMergeStage ? (S - s0) : kMergeStage;
-    for (int s2 = q; s2 < ns; s2 += TPD) acc = fmaf(sw[s0 + s2], sf[s2 * D + d], acc);
-  }
-  part[q][d] = acc;
   __syncthreads();
-  if (t < D) {
-    float o = part[0][t];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 1; k < TPD; ++k) o += part[k][t];
-    float L = red_l[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) L += red_l[w];
-    P.out[qi * D + t] = o / L;
-    if (t == 0 && P.lse) P.lse[qi] = (mu + log2f(L)) * kLn2;
+  for (int i = 0; i < MAXO; ++i) {
+    const int sp = sg + i * SG;
+    if (sp < S) {
+      const float wgt = sw[sp];
+      acc.x = fmaf(wgt, v[i].x, acc.x);
+      acc.y = fmaf(wgt, v[i].y, acc.y);
+      acc.z = fmaf(wgt, v[i].z, acc.z);
+      acc.w = fmaf(wgt, v[i].w, acc.w);
+    }
+  }
+  red[sg][f] = acc;
+  __syncthreads();
+  if (t < kMergeSlice) {
+    const float *rf = reinterpret_cast<const float *>(&red[0][0]);
+    float o = 0.f;
+#pragma unroll 8
+    for (int g2 = 0; g2 < SG; ++g2) o += rf[g2 * kMergeSlice + t];
+    P.out[qi * D + sl * kMergeSlice + t] = o / lw;
+    if (t == 0 && sl == 0 && P.lse) P.lse[qi] = (mu + log2f(lw)) * kLn2;
   }
 }
 
@@ -1386,7 +1414,7 @@ void launch_hb(int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
     case HQ_BF16: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_BF16>), grid, dim3(kThreads), 0, st, P); break;
     default: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_F16>), grid, dim3(kThreads), 0, st, P); break;
   }
-  hipLaunchKernelGGL((merge_kernel<D, HB>), dim3(P.units * HB), dim3(kThreads), 0, st, P);
+  hipLaunchKernelGGL((merge_kernel<D, HB>), dim3(P.units * HB * (D / kMergeSlice)), dim3(kThreads), 0, st, P);
 }
 template <int D>
 void launch_d(int HB, int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
