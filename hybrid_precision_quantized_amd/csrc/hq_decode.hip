@@ -228,11 +228,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // priorities the first block on a CU runs ahead and the second finishes
 // alone at low occupancy. Raising the priority of the wave that is further
 // behind keeps co-resident waves abreast, so they finish together.
+// Signed arithmetic (n < 2^28) keeps it on the scalar unit.
 __device__ __forceinline__ void prio_by_remaining(uint32_t c, uint32_t n) {
-  const uint32_t rem = c < n ? n - c : 0u;
-  if (rem * 2u > n) __builtin_amdgcn_s_setprio(3);
-  else if (rem * 4u > n) __builtin_amdgcn_s_setprio(2);
-  else if (rem * 8u > n) __builtin_amdgcn_s_setprio(1);
+  const int32_t ni = static_cast<int32_t>(n);
+  const int32_t rem = ni - static_cast<int32_t>(c);
+  if (rem * 2 > ni) __builtin_amdgcn_s_setprio(3);
+  else if (rem * 4 > ni) __builtin_amdgcn_s_setprio(2);
+  else if (rem * 8 > ni) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
