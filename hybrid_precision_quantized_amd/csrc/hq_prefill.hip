@@ -36,9 +36,10 @@
 //    i - W < j <= i and the VL keys j <= i - W gathered by index (16-bit
 //    product). The three masks are disjoint and cover every j <= i once.
 //  * K tiles are staged row-major in LDS; V tiles are staged transposed,
-//    [d][key], in fp16 (16-bit inputs convert exactly inside the fp16 range;
-//    larger values are a precondition violation). The probabilities are
-//    rounded to fp16 for the P . V MFMA (relative 2^-12).
+//    [d][key], in fp16 (bf16 inputs convert exactly for magnitudes in
+//    [2^-17, 65504]; smaller ones round to the fp16 subnormal grid, absolute
+//    error below 2^-25; larger ones are a precondition violation). The
+//    probabilities are rounded to fp16 for the P . V MFMA (relative 2^-12).
 //  * Query tiles are issued longest-first (the causal work grows with i).
 #include <math.h>
 

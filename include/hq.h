@@ -251,15 +251,25 @@ int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
  * sm_scale <= 0 means 1/sqrt(D). Requires D == 128, group == 32,
  * Hq % Hkv == 0. ws: at least hq_prefill_workspace_size bytes, 256-byte
  * aligned, no initialisation needed (it holds the split dequantized Q and K,
- * V and the VL rows in 32-key tiles, and the VL bitmap). Precision: the quantized logits are within about 2^-21
- * (relative) of the exact q_hat . k_hat; the probabilities are rounded to
- * fp16 for the P . V product.
+ * V and the VL rows in 32-key tiles, and the VL bitmap).
+ * Precision: the quantized logits are within about 2^-21 (relative) of the
+ * exact q_hat . k_hat; the probabilities are rounded to fp16 for the P . V
+ * product and V is converted to fp16 (exact for bf16 magnitudes in
+ * [2^-17, 65504]; smaller ones round to the fp16 subnormal grid, absolute
+ * error below 2^-25; larger ones are a precondition violation).
+ * Errors: HQ_ERR_UNSUPPORTED for another dtype, D or group, or more than
+ * 5e8 query groups (B * Hq * T * D / 32) in one call; HQ_ERR_INVALID_ARG for
+ * sizes < 1, Hq % Hkv != 0, W or k_vl < 0, k_vl > T, null or misaligned
+ * pointers; HQ_ERR_WORKSPACE if ws_bytes is too small. Nothing is enqueued
+ * on error. The VL positions themselves are not checked on the device.
  */
 hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype dtype, int B, int Hq,
                           int Hkv, int64_t T, int D, int group, int W, const int32_t *vl_idx, int k_vl,
                           float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* Workspace bytes hq_prefill_attn needs for these sizes (0 if a size is
+ * out of range). */
 size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D, int k_vl);
 
 const char *hq_status_string(hq_status s);
