@@ -295,6 +295,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
       }
     }
   };
+  // VL keys of a tile whose keys are all in range, from the tile's VL word
+  // (wave-uniform): element r holds key c(r) in lanes 0-31 and key c(r) + 4 in
+  // lanes 32-63, so each element's valid lanes form a 64-bit mask built on the
+  // scalar unit and the select is a single v_cndmask per element.
+  const float ninf = kNegInf;
+  auto mask_vl_uniform = [&](f32x16 &s, uint32_t word) {
+    const uint32_t nw = ~word;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 8 * (r >> 2) + (r & 3);
+      const uint32_t lo = 0u - ((nw >> c) & 1u);
+      const uint32_t hi = 0u - ((nw >> (c + 4)) & 1u);
+      const uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
+      asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(s[r]) : "v"(ninf), "s"(m));
+    }
+  };
   // bits c of the register key order for which key 4 half + c lies in (lo, hi]
   // (tile-relative keys; lo < hi)
   auto range_mask = [&](int lo, int hi) {
@@ -394,11 +410,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
       if (kind == kQuant) {
         // keys k0 + m <= qi - W outside the VL set
         const uint32_t word = P.vl_bits[bh * P.words + t];         // VL bits of keys k0 .. k0 + 31
-        const bool full = k0 + kBN - 1 <= wq0 - P.W && word == 0u;   // wave-uniform
-        const int hi = static_cast<int>(qi - P.W - k0 < 64 ? qi - P.W - k0 : 64);
-        // register key order: bit c <-> key 4 half + c, i.e. VL bit 4 half + c
-        const uint32_t vlr = word >> (4 * half);
-        consume(s, sl, range_mask(-1, hi) & ~vlr, full);
+        // the VL keys: selects with scalar lane masks (all-ones when word == 0)
+        mask_vl_uniform(s, word);
+        // the range j <= i - W: a per-lane mask only on tiles that cross it
+        const bool in_range = k0 + kBN - 1 <= wq0 - P.W;           // wave-uniform
+        uint32_t okm = 0u;
+        if (!in_range) {
+          const int hi = static_cast<int>(qi - P.W - k0 < 64 ? qi - P.W - k0 : 64);
+          okm = range_mask(-1, hi);
+        }
+        consume(s, sl, okm, in_range);
       } else if (kind == kWin) {
         // keys qi - W < k0 + m <= qi
         const bool full = k0 > wq1 - P.W && k0 + kBN - 1 <= wq0;
