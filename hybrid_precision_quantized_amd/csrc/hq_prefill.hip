@@ -204,11 +204,12 @@ enum { kQuant = 0, kWin = 1, kVl = 2 };
 
 // The staged data of one 32-key tile: K rows (one or two planes, row-major,
 // padded) and the V^T tile ([d][key], padded); two LDS slots.
+// K tiles in two slots, V^T tiles and VL positions in three (see run_stream).
 struct PrefillShared {
   uint16_t ka[2][kBN][kD + kKPad];
   uint16_t kb[2][kBN][kD + kKPad];
-  uint16_t vt[2][kD][kBN + kVPad];
-  int32_t pos[2][kBN];
+  uint16_t vt[3][kD][kBN + kVPad];
+  int32_t pos[3][kBN];
   int nvl;
 };
 
@@ -219,10 +220,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
-  const int bq = blockIdx.x % (P.B * P.Hq);
-  const int qt = P.n_qt - 1 - blockIdx.x / (P.B * P.Hq);     // longest rows first
-  const int b = bq / P.Hq;
-  const int qh = bq % P.Hq;
+  // Block order: longest rows first. Workgroups go to the 8 XCDs round-robin
+  // (block id mod 8); when the KV heads divide evenly, XCD x takes the KV
+  // heads u = x, x + 8, ... with all their query heads, so every query head
+  // and query tile in flight on an XCD that streams a KV head's tiles shares
+  // them through that XCD's L2.
+  int b, qh, qt;
+  {
+    const int U = P.B * P.Hkv;
+    if (U % kNumXcd == 0) {
+      const int x = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
+      const int per = (U / kNumXcd) * P.G;              // (unit, query head) items per XCD and tile
+      const int rem = j % per;
+      const int unit = x + kNumXcd * (rem / P.G);
+      b = unit / P.Hkv;
+      qh = (unit % P.Hkv) * P.G + rem % P.G;
+      qt = P.n_qt - 1 - j / per;
+    } else {
+      const int bq = blockIdx.x % (P.B * P.Hq);
+      b = bq / P.Hq;
+      qh = bq % P.Hq;
+      qt = P.n_qt - 1 - blockIdx.x / (P.B * P.Hq);
+    }
+  }
   const int h = qh / P.G;
   const int64_t bh = static_cast<int64_t>(b) * P.Hkv + h;
   const int64_t q0 = static_cast<int64_t>(qt) * kBM;
@@ -364,54 +384,65 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
         L.pos = j < sm.nvl ? vl[j] : -1;
       }
     };
-    auto store = [&](int sl, const Pre &L) {
+    auto store = [&](int ks, int vs, const Pre &L) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int idx = e * kThreads + threadIdx.x;
         const int r = idx >> 4, c = idx & 15;
-        *reinterpret_cast<u32x4 *>(&sm.ka[sl][r][c * 8]) = L.a[e];
-        if (two) *reinterpret_cast<u32x4 *>(&sm.kb[sl][r][c * 8]) = L.b[e];
+        *reinterpret_cast<u32x4 *>(&sm.ka[ks][r][c * 8]) = L.a[e];
+        if (two) *reinterpret_cast<u32x4 *>(&sm.kb[ks][r][c * 8]) = L.b[e];
         const int d = idx >> 2, k8 = (idx & 3) * 8;       // V^T: row d, keys k8 .. k8 + 7
-        *reinterpret_cast<u32x4 *>(&sm.vt[sl][d][k8]) = L.v[e];
+        *reinterpret_cast<u32x4 *>(&sm.vt[vs][d][k8]) = L.v[e];
       }
-      if (kind == kVl && threadIdx.x < kBN) sm.pos[sl][threadIdx.x] = L.pos;
+      if (kind == kVl && threadIdx.x < kBN) sm.pos[vs][threadIdx.x] = L.pos;
     };
-    Pre pre;
-    load(t0, pre);
-    store(0, pre);
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-      const int sl = (t - t0) & 1;
-      if (t + 1 < t1) load(t + 1, pre);
-      // two independent accumulator chains (the hi . lo term in s2) so that
-      // consecutive MFMAs do not wait on each other's results
-      f32x16 s, s2;
+    // S^T of the tile in K slot ks
+    auto qk = [&](int ks) {
+      f32x16 sc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s2[r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        const uint4 ah = *reinterpret_cast<const uint4 *>(&sm.ka[sl][lane & 31][kc * 16 + half * 8]);
+        const uint4 ah = *reinterpret_cast<const uint4 *>(&sm.ka[ks][lane & 31][kc * 16 + half * 8]);
         if (kind == kQuant) {
-          const uint4 al = *reinterpret_cast<const uint4 *>(&sm.kb[sl][lane & 31][kc * 16 + half * 8]);
-          s = mfma_f16(ah, fq0[kc], s);
-          s2 = mfma_f16(ah, fq1[kc], s2);
-          s = mfma_f16(al, fq0[kc], s);
-        } else if (kc & 1) {
-          s2 = mfma_16bit<DT>(ah, fq0[kc], s2);
+          const uint4 al = *reinterpret_cast<const uint4 *>(&sm.kb[ks][lane & 31][kc * 16 + half * 8]);
+          sc = mfma_f16(ah, fq0[kc], sc);
+          sc = mfma_f16(ah, fq1[kc], sc);
+          sc = mfma_f16(al, fq0[kc], sc);
         } else {
-          s = mfma_16bit<DT>(ah, fq0[kc], s);
+          sc = mfma_16bit<DT>(ah, fq0[kc], sc);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += s2[r];
+      return sc;
+    };
+    // Software pipeline, one barrier per tile: iteration i (tile t = t0 + i)
+    // issues the score MFMAs of tile t + 1 (K slot (i + 1) % 2) before the
+    // softmax and P . V of tile t (V slot i % 3), so the matrix core works
+    // while the vector unit runs the softmax, and stores tile t + 2 into K slot
+    // i % 2 and V slot (i + 2) % 3, which no wave reads during iteration i
+    // (their last readers finished before the previous barrier).
+    Pre pre;
+    load(t0, pre);
+    store(0, 0, pre);
+    __syncthreads();
+    if (t0 + 1 < t1) load(t0 + 1, pre);
+    f32x16 s_cur = qk(0);
+    if (t0 + 1 < t1) store(1, 1, pre);
+    __syncthreads();
+    int vs = 0;                                  // V slot of tile t: i % 3
+    for (int t = t0; t < t1; ++t) {
+      const int i = t - t0;
+      const int vs2 = vs == 0 ? 2 : vs - 1;      // (i + 2) % 3
+      if (t + 2 < t1) load(t + 2, pre);
+      f32x16 s_next;
+      if (t + 1 < t1) s_next = qk((i + 1) & 1);
+      f32x16 &sv = s_cur;
       const int64_t k0 = static_cast<int64_t>(t) * kBN;
       if (kind == kQuant) {
         // keys k0 + m <= qi - W outside the VL set
         const uint32_t word = P.vl_bits[bh * P.words + t];         // VL bits of keys k0 .. k0 + 31
         // the VL keys: selects with scalar lane masks (all-ones when word == 0)
-        mask_vl_uniform(s, word);
+        mask_vl_uniform(sv, word);
         // the range j <= i - W: a per-lane mask only on tiles that cross it
         const bool in_range = k0 + kBN - 1 <= wq0 - P.W;           // wave-uniform
         uint32_t okm = 0u;
@@ -419,26 +450,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
           const int hi = static_cast<int>(qi - P.W - k0 < 64 ? qi - P.W - k0 : 64);
           okm = range_mask(-1, hi);
         }
-        consume(s, sl, okm, in_range);
+        consume(sv, vs, okm, in_range);
       } else if (kind == kWin) {
         // keys qi - W < k0 + m <= qi
         const bool full = k0 > wq1 - P.W && k0 + kBN - 1 <= wq0;
         const int64_t lo64 = qi - P.W - k0, hi64 = qi - k0;
         const int lo = static_cast<int>(lo64 < -1 ? -1 : (lo64 > 64 ? 64 : lo64));
         const int hi = static_cast<int>(hi64 < -1 ? -1 : (hi64 > 64 ? 64 : hi64));
-        consume(s, sl, range_mask(lo, hi), full);
+        consume(sv, vs, range_mask(lo, hi), full);
       } else {
         uint32_t okm = 0u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int c = 8 * (r >> 2) + (r & 3);
-          const int64_t j = sm.pos[sl][4 * half + c];
+          const int64_t j = sm.pos[vs][4 * half + c];
           okm |= static_cast<uint32_t>(j >= 0 && j <= qi - P.W) << c;
         }
-        consume(s, sl, okm, false);
+        consume(sv, vs, okm, false);
       }
-      if (t + 1 < t1) store(sl ^ 1, pre);
+      if (t + 2 < t1) store(i & 1, vs2, pre);
       __syncthreads();
+      s_cur = s_next;
+      vs = vs == 2 ? 0 : vs + 1;
     }
   };
 
