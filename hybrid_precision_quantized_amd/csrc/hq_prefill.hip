@@ -421,19 +421,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
     // while the vector unit runs the softmax, and stores tile t + 2 into K slot
     // i % 2 and V slot (i + 2) % 3, which no wave reads during iteration i
     // (their last readers finished before the previous barrier).
-    Pre pre;
-    load(t0, pre);
-    store(0, 0, pre);
+    Pre pa, pb;
+    load(t0, pa);
+    store(0, 0, pa);
     __syncthreads();
-    if (t0 + 1 < t1) load(t0 + 1, pre);
+    if (t0 + 1 < t1) load(t0 + 1, pb);
     f32x16 s_cur = qk(0);
-    if (t0 + 1 < t1) store(1, 1, pre);
+    if (t0 + 1 < t1) store(1, 1, pb);
+    if (t0 + 2 < t1) load(t0 + 2, pa);
     __syncthreads();
     int vs = 0;                                  // V slot of tile t: i % 3
-    for (int t = t0; t < t1; ++t) {
+    // one tile; `st` holds tile t + 2 (loaded an iteration earlier), tile t + 3
+    // goes into `ld`, so each tile's loads have a whole iteration to land
+    auto iter = [&](const int t, const Pre &st, Pre &ld) {
       const int i = t - t0;
       const int vs2 = vs == 0 ? 2 : vs - 1;      // (i + 2) % 3
-      if (t + 2 < t1) load(t + 2, pre);
+      if (t + 3 < t1) load(t + 3, ld);
       f32x16 s_next;
       if (t + 1 < t1) s_next = qk((i + 1) & 1);
       f32x16 &sv = s_cur;
@@ -468,10 +471,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
         }
         consume(sv, vs, okm, false);
       }
-      if (t + 2 < t1) store(i & 1, vs2, pre);
+      if (t + 2 < t1) store(i & 1, vs2, st);
       __syncthreads();
       s_cur = s_next;
       vs = vs == 2 ? 0 : vs + 1;
+    };
+    for (int t = t0; t < t1; t += 2) {
+      iter(t, pa, pb);
+      if (t + 1 < t1) iter(t + 1, pb, pa);
     }
   };
 
