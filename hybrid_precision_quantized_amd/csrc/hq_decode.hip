@@ -522,6 +522,21 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
 // max test, the subtraction and the exponential then run once per lane, and
 // the other heads' probabilities reach the P . V weights through DPP
 // broadcasts fused into the multiplies.
+//
+// Key codes become fp16 pairs at two nibble positions without shifts: the
+// low nibble of each byte under the magic 1024 (ulp 1, so 1024 + c) and the
+// high nibble in place under the magic 64 (ulp 1/16 at bits 4-7, so 64 + c);
+// one shift by 8 serves the other two nibbles. The queries are rounded to
+// fp16 once (exact for bf16 magnitudes in [2^-17, 65504]; the fast path
+// requires |q| < 65504), and each dot chain starts from minus its offset,
+// -(1024 sum of the even channels + 64 sum of the odd ones), so the chain
+// ends at q . c itself.
+__device__ __forceinline__ float dot2_f16_from(uint32_t a, uint32_t b, float c) {
+  // the VOP3P form: the accumulator input need not be the destination
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_mul(float a, float b) {   // dpp(a) * b
   return dpp_f<CTRL>(a) * b;
@@ -539,8 +554,6 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
   const int cp = lane;                 // P.V lane: channel pair
   const int gp = cp >> 4;
   const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
-  constexpr uint32_t kMagic = (QT == HQ_BF16) ? 0x43004300u : 0x64006400u;
-  constexpr float kMagicVal = (QT == HQ_BF16) ? 128.f : 1024.f;
 
   // raw query channels of this lane's group for head g ^ j, loaded before the
   // ring so that their wait does not cover the ring's loads
@@ -550,7 +563,6 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
     load_q32<QT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32, qraw[j]);
   __builtin_amdgcn_sched_barrier(0);
 
-  const uint32_t magic = kMagic;
   const uint32_t vmagic = 0x64006400u;
   float zl[4] = {0.f, 0.f, 0.f, 0.f};   // sum p_h (z + 8 s) of this lane's group, head h
   float lown = 0.f;                      // sum of p of head g (this lane's head)
@@ -595,55 +607,60 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
     issue(wave + jr * kWaves, ring[jr]);
     __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: waits are counts
   }
-  // query pairs (register j: head g ^ j) while the ring's first loads fly
+  // fp16 query pairs (register j: head g ^ j) while the ring's first loads fly
   uint32_t qp[4][4][4];
   float cqs[4];          // cs * sum of the group's query channels, head g ^ j
+  float nof[4];          // minus the chain offset, head g ^ j
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t (&raw)[16] = qraw[j];
-    float s = 0.f;
+    uint32_t hb[32];
+    float se = 0.f, so = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-      s += half_bits_to_f32<QT>(raw[c] & 0xFFFFu) + half_bits_to_f32<QT>(raw[c] >> 16);
+    for (int c = 0; c < 32; ++c) {
+      const uint32_t bits = (raw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+      _Float16 q16;
+      if constexpr (QT == HQ_BF16) q16 = static_cast<_Float16>(bf16_to_f32(bits));
+      else q16 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits));
+      hb[c] = __builtin_bit_cast(uint16_t, q16);
+      if (c & 1) so += static_cast<float>(q16);
+      else se += static_cast<float>(q16);
+    }
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int a = 8 * w + m, c = 8 * w + m + 4;
-        const uint32_t lo = (raw[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
-        const uint32_t hi = (raw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
-        qp[j][w][m] = lo | (hi << 16);
-      }
-    cqs[j] = P.cs * s;
+      for (int m = 0; m < 4; ++m) qp[j][w][m] = hb[8 * w + m] | (hb[8 * w + m + 4] << 16);
+    cqs[j] = P.cs * (se + so);
+    nof[j] = -fmaf(1024.f, se, 64.f * so);
   }
   _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
   // one wave step over chunk c held in `cur`
   auto step = [&](const uint32_t c, const Int4Loads<D> &cur) {
 
-    // ---- q . k over this lane's group, head g ^ j in part[j]; the chains
-    // carry the MAGIC offset, MAGIC * sum q, which is removed with the zero point
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- q . c over this lane's group, head g ^ j in part[j] (each chain
+    // starts at minus its magic offset)
+    float part[4];
     const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const uint32_t x0 = and_or(w[ww], 0x000F000Fu, magic);
-      const uint32_t x1 = and_or(w[ww] >> 4, 0x000F000Fu, magic);
-      const uint32_t x2 = and_or(w[ww] >> 8, 0x000F000Fu, magic);
-      const uint32_t x3 = and_or(w[ww] >> 12, 0x000F000Fu, magic);
+      const uint32_t w8 = w[ww] >> 8;
+      const uint32_t x0 = and_or(w[ww], 0x000F000Fu, 0x64006400u);   // channels 8ww, 8ww + 4
+      const uint32_t x1 = and_or(w[ww], 0x00F000F0u, 0x54005400u);   // 8ww + 1, 8ww + 5
+      const uint32_t x2 = and_or(w8, 0x000F000Fu, 0x64006400u);      // 8ww + 2, 8ww + 6
+      const uint32_t x3 = and_or(w8, 0x00F000F0u, 0x54005400u);      // 8ww + 3, 8ww + 7
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        part[j] = dot2_q<QT>(qp[j][ww][0], x0, part[j]);
-        part[j] = dot2_q<QT>(qp[j][ww][1], x1, part[j]);
-        part[j] = dot2_q<QT>(qp[j][ww][2], x2, part[j]);
-        part[j] = dot2_q<QT>(qp[j][ww][3], x3, part[j]);
+        part[j] = ww == 0 ? dot2_f16_from(qp[j][0][0], x0, nof[j]) : dot2_f16(qp[j][ww][0], x0, part[j]);
+        part[j] = dot2_f16(qp[j][ww][1], x1, part[j]);
+        part[j] = dot2_f16(qp[j][ww][2], x2, part[j]);
+        part[j] = dot2_f16(qp[j][ww][3], x3, part[j]);
       }
     }
-    // scaled group partials: cs (s (dot - MAGIC sum q) + z sum q)
-    //                        = (cs s) dot + (cs sum q)(z - MAGIC s)
+    // scaled group partials: cs (s q.c + z sum q) = (cs s) q.c + (cs sum q) z
     const float ssc = lo_f16(cur.ks) * P.cs;
-    const float zm = fmaf(-kMagicVal, lo_f16(cur.ks), hi_f16(cur.ks));
+    const float zk = hi_f16(cur.ks);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) part[j] = fmaf(ssc, part[j], cqs[j] * zm);
+    for (int j = 0; j < 4; ++j) part[j] = fmaf(ssc, part[j], cqs[j] * zk);
     // quad reduce-scatter: lane g ends with head g summed over the 4 groups
     const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
     const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
