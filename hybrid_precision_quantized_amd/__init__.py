@@ -73,6 +73,11 @@ _SIGS = {
                                       ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_decode_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p]),
     "hq_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HybridKV), ctypes.c_int, ctypes.c_int]),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
     "hq_prefill_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -207,6 +212,17 @@ def hq_decode_attn(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, stream
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hq_decode_attn(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
                                 n_splits, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                _stream(stream)))
+
+
+def hq_decode_step(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, q_acc=None, R=64, step=0,
+                   evict=False, stream=None):
+    """hq_decode_attn plus the step's upkeep: q into the detector ring and the
+    window's oldest row into INT4 row T - W (see include/hq.h)."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hq_decode_step(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
+                                n_splits, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                _ptr(q_acc), int(R), int(step), 1 if evict else 0,
                                 _stream(stream)))
 
 

@@ -49,6 +49,7 @@
 #include <cmath>
 
 #include "hq_common.h"
+#include "hq_int4.h"
 
 namespace hq {
 namespace {
@@ -83,6 +84,14 @@ struct DecodeParams {
   int blocks_used;          // units * S
   int blocks_per_xcd;
   float cs;                 // sm_scale * log2(e)
+  // per-step upkeep (hq_decode_step), run by extra blocks of the merge launch
+  int merge_blocks;         // blocks of the merge itself
+  int up_q;                 // 1: one block copies q into the detector's query ring
+  uint8_t *q_ring;          // [B][Hq][R][D] of the query dtype
+  int R, ring_slot;
+  int evict;                // 1: pack the window's oldest row into INT4 row T - W
+  uint8_t *ek_codes, *ev_codes;
+  uint32_t *ek_sz, *ev_sz;
 };
 
 // ---------------------------------------------------------------- lane helpers
@@ -1200,8 +1209,70 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 // the splits t / 8, t / 8 + 32, ..., and the 32 split groups are summed in a
 // fixed order, so the result is deterministic.
 constexpr int kMergeSlice = 32;
-template <int D, int HB>
+
+// Per-step upkeep of hq_decode_step. It runs in the merge launch, after every
+// split has read the cache, so writing INT4 row T - W (outside this step's
+// INT4 range [0, T - W)) cannot race with them.
+//  * block 0 (if up_q): q [B][Hq][D] into slot ring_slot of q_ring;
+//  * the next blocks (if evict): the window's oldest row (position T - W, ring
+//    row win_offset) of every (b, KV head) packed like hq_quantize_kv_pair:
+//    four lanes (a DPP quad) per 32-channel group, K in rows, V in TILE16.
+template <int D, int QT>
+__device__ void upkeep(const DecodeParams &P, int ub) {
+  constexpr int EB = QT == HQ_F32 ? 4 : 2;
+  constexpr int NG = D / 32;
+  if (ub < P.up_q) {
+    constexpr int CH = D * EB / 16;                         // 16-byte chunks per q row
+    const int rows = P.B * P.Hq;
+    for (int c = threadIdx.x; c < rows * CH; c += kThreads) {
+      const int r = c / CH, cc = c % CH;
+      const uint4 v = reinterpret_cast<const uint4 *>(P.q)[c];
+      reinterpret_cast<uint4 *>(P.q_ring + (static_cast<int64_t>(r) * P.R + P.ring_slot) * (D * EB))[cc] = v;
+    }
+    return;
+  }
+  const uint32_t per = 4u * static_cast<uint32_t>(P.B * P.Hkv) * NG;    // threads per tensor
+  const uint32_t gid = static_cast<uint32_t>(ub - P.up_q) * kThreads + threadIdx.x;
+  if (gid >= 2u * per) return;                             // whole quads: per is a multiple of 4
+  const bool is_v = gid >= per;
+  const uint32_t lg = is_v ? gid - per : gid;
+  const int qq = static_cast<int>(lg & 3u);
+  const uint32_t item = lg >> 2;
+  const int g = static_cast<int>(item % NG);
+  const int64_t hd = item / NG;                             // b * Hkv + h
+  const void *src = is_v ? P.win_v : P.win_k;
+  float v[8];
+  load8<QT>(src, (hd * P.W + P.win_offset) * D + g * 32 + qq * 8, v);
+  _Float16 s16, z16;
+  const uint32_t packed = encode_quarter(v, s16, z16);
+  const int64_t row = P.nq;                                 // position T - W
+  const int64_t head_row = hd * P.t_cap + row;
+  if (!is_v) {
+    reinterpret_cast<uint32_t *>(P.ek_codes + head_row * (D / 2) + g * 16)[qq] = packed;
+  } else {
+    // tile row / 16 of the head; byte (j, slot16(row % 16)), each run of 4
+    // rows stored in the order 0, 2, 1, 3
+    const int64_t tile = hd * (P.t_cap / 16) + row / 16;
+    const int r16 = static_cast<int>(row % 16);
+    const int slot16 = (r16 & ~3) | ((r16 & 1) << 1) | ((r16 >> 1) & 1);
+    uint8_t *base = P.ev_codes + tile * (D / 2) * 16 + slot16;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      base[(g * 16 + qq * 4 + jj) * 16] = static_cast<uint8_t>((packed >> (8 * jj)) & 0xFFu);
+  }
+  if (qq == 0) {
+    const uint32_t szw = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+    (is_v ? P.ev_sz : P.ek_sz)[head_row * NG + g] = szw;
+  }
+}
+
+template <int D, int HB, int QT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
+  if (static_cast<int>(blockIdx.x) >= P.merge_blocks) {    // block-uniform
+    upkeep<D, QT>(P, static_cast<int>(blockIdx.x) - P.merge_blocks);
+    return;
+  }
   constexpr int NSL = D / kMergeSlice;            // slices per head
   constexpr int F4 = kMergeSlice / 4;             // float4 per slice row
   constexpr int SG = kThreads / F4;               // split groups
@@ -1426,14 +1497,20 @@ hq_status validate(const void *q, int q_dtype, int Hq, const hq_hybrid_kv *kv, f
   return HQ_OK;
 }
 
+template <int D, int HB, int QT>
+void launch_qt(dim3 grid, dim3 mgrid, hipStream_t st, const DecodeParams &P) {
+  hipLaunchKernelGGL((decode_kernel<D, HB, QT>), grid, dim3(kThreads), 0, st, P);
+  hipLaunchKernelGGL((merge_kernel<D, HB, QT>), mgrid, dim3(kThreads), 0, st, P);
+}
 template <int D, int HB>
 void launch_hb(int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
+  const dim3 mgrid(static_cast<unsigned>(P.merge_blocks + P.up_q) +
+                   (P.evict ? static_cast<unsigned>((8 * P.B * P.Hkv * (D / 32) + kThreads - 1) / kThreads) : 0u));
   switch (qdt) {
-    case HQ_F32: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_F32>), grid, dim3(kThreads), 0, st, P); break;
-    case HQ_BF16: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_BF16>), grid, dim3(kThreads), 0, st, P); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, HB, HQ_F16>), grid, dim3(kThreads), 0, st, P); break;
+    case HQ_F32: launch_qt<D, HB, HQ_F32>(grid, mgrid, st, P); break;
+    case HQ_BF16: launch_qt<D, HB, HQ_BF16>(grid, mgrid, st, P); break;
+    default: launch_qt<D, HB, HQ_F16>(grid, mgrid, st, P); break;
   }
-  hipLaunchKernelGGL((merge_kernel<D, HB>), dim3(P.units * HB * (D / kMergeSlice)), dim3(kThreads), 0, st, P);
 }
 template <int D>
 void launch_d(int HB, int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
@@ -1461,10 +1538,17 @@ extern "C" size_t hq_decode_workspace_size(const hq_hybrid_kv *kv, int Hq, int n
   return ws_layout(kv, Hq, pl).total;
 }
 
-extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
-                                    float sm_scale, int n_splits, float *out, float *lse, void *ws,
-                                    size_t ws_bytes, void *stream) {
-  hq_status s = validate(q, q_dtype, Hq, kv, out);
+namespace hq {
+namespace {
+struct Upkeep {
+  void *q_ring = nullptr;
+  int R = 0, slot = 0;
+  bool evict = false;
+};
+hq_status decode_common(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv, float sm_scale,
+                        int n_splits, float *out, float *lse, void *ws, size_t ws_bytes, const Upkeep &up,
+                        void *stream) {
+  const hq_status s = validate(q, q_dtype, Hq, kv, out);
   if (s != HQ_OK) return s;
   if (n_splits < 0) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: n_splits < 0");
   const Plan pl = make_plan(kv, Hq, n_splits);
@@ -1514,10 +1598,57 @@ extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, con
   P.blocks_per_xcd = blocks / kNumXcd;
   const float scale = sm_scale == 0.f ? 1.0f / sqrtf(static_cast<float>(kv->D)) : sm_scale;
   P.cs = scale * kLog2e;
+  P.merge_blocks = pl.units * pl.HB * (kv->D / kMergeSlice);
+  P.up_q = up.q_ring ? 1 : 0;
+  P.q_ring = static_cast<uint8_t *>(up.q_ring);
+  P.R = up.R;
+  P.ring_slot = up.slot;
+  P.evict = up.evict ? 1 : 0;
+  P.ek_codes = const_cast<uint8_t *>(kv->k_codes);
+  P.ev_codes = const_cast<uint8_t *>(kv->v_codes);
+  P.ek_sz = reinterpret_cast<uint32_t *>(const_cast<uint16_t *>(kv->k_sz));
+  P.ev_sz = reinterpret_cast<uint32_t *>(const_cast<uint16_t *>(kv->v_sz));
   hipStream_t st = as_stream(stream);
   if (kv->D == 128) launch_d<128>(pl.HB, q_dtype, dim3(blocks), st, P);
   else launch_d<64>(pl.HB, q_dtype, dim3(blocks), st, P);
+  return HQ_OK;
+}
+}  // namespace
+}  // namespace hq
+
+extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                                    float sm_scale, int n_splits, float *out, float *lse, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  const hq_status s = decode_common(q, q_dtype, Hq, kv, sm_scale, n_splits, out, lse, ws, ws_bytes, Upkeep{},
+                                    stream);
+  if (s != HQ_OK) return s;
   return check_launch("hq_decode_attn");
+}
+
+extern "C" hq_status hq_decode_step(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                                    float sm_scale, int n_splits, float *out, float *lse, void *ws,
+                                    size_t ws_bytes, void *q_acc, int R, int64_t step, int evict,
+                                    void *stream) {
+  if (q_acc && (R < 1 || R > 1024)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_step: need 1 <= R <= 1024");
+  if (step < 0) return fail(HQ_ERR_INVALID_ARG, "hq_decode_step: step < 0");
+  if (q_acc && reinterpret_cast<uintptr_t>(q_acc) % 16)
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_step: q_acc must be 16-byte aligned");
+  Upkeep up;
+  up.q_ring = q_acc;
+  up.R = q_acc ? R : 0;
+  up.slot = q_acc ? static_cast<int>(step % R) : 0;
+  up.evict = evict != 0 && kv && kv->W > 0;
+  if (up.evict) {
+    if (kv->t_cap < kv->T - kv->W + 1)
+      return fail(HQ_ERR_INVALID_ARG, "hq_decode_step: eviction needs t_cap >= T - W + 1");
+    if (!kv->k_codes || !kv->v_codes || !kv->k_sz || !kv->v_sz)
+      return fail(HQ_ERR_INVALID_ARG, "hq_decode_step: null INT4 plane");
+    if ((reinterpret_cast<uintptr_t>(kv->k_sz) | reinterpret_cast<uintptr_t>(kv->v_sz)) % 4)
+      return fail(HQ_ERR_INVALID_ARG, "hq_decode_step: scale planes must be 4-byte aligned");
+  }
+  const hq_status s = decode_common(q, q_dtype, Hq, kv, sm_scale, n_splits, out, lse, ws, ws_bytes, up, stream);
+  if (s != HQ_OK) return s;
+  return check_launch("hq_decode_step");
 }
 
 extern "C" hq_status hq_vl_bitmap(const int32_t *vl_idx, int n_heads, int k, int64_t t_cap,

@@ -226,6 +226,34 @@ hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybri
                          float sm_scale, int n_splits, float *out, float *lse, void *ws,
                          size_t ws_bytes, void *stream);
 
+/*
+ * hq_decode_step -- hq_decode_attn plus the per-step upkeep of the cache, in
+ * the same two kernel launches [AFS, How It Works: a local window of recent
+ * tokens stays 16-bit while older tokens are kept in 4 bits; WPN, body
+ * paragraph 4: the detector accumulates the decode queries and scores them
+ * every 64 tokens]. Same arguments and outputs as hq_decode_attn (out and lse
+ * are bitwise the same), and:
+ *   q_acc, R, step: if q_acc != NULL, q is copied into slot step % R of the
+ *     detector's query ring q_acc [B][Hq][R][D] (q_dtype), exactly as
+ *     hq_detect_vlines(q_new = q, ...) would; a following hq_detect_vlines
+ *     call then passes q_new = NULL. 1 <= R <= 1024, q_acc 16-byte aligned.
+ *   evict: if non-zero and kv->W > 0, the window's oldest row (position
+ *     T - W, ring row kv->win_offset of win_k and win_v) is packed into row
+ *     T - W of the INT4 planes in the hq_quantize_kv format (K in rows, V in
+ *     TILE16, fp16 {s, z}; bit-exact with hq_quantize_kv_pair). This step
+ *     reads only INT4 rows [0, T - W), so the row is ready for the next step,
+ *     after which the caller advances the window (T + 1, win_offset + 1 mod W)
+ *     and writes the new token into the freed ring row. Requires kv->t_cap >=
+ *     T - W + 1. The INT4 planes are written through the descriptor's
+ *     pointers, which must therefore address writable memory.
+ * The upkeep runs in extra workgroups of the merge launch, after every split
+ * has read the cache. Errors as hq_decode_attn, plus HQ_ERR_INVALID_ARG for
+ * a bad R, step < 0 or a too small t_cap; nothing is enqueued on error.
+ */
+hq_status hq_decode_step(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                         float sm_scale, int n_splits, float *out, float *lse, void *ws,
+                         size_t ws_bytes, void *q_acc, int R, int64_t step, int evict, void *stream);
+
 size_t hq_decode_workspace_size(const hq_hybrid_kv *kv, int Hq, int n_splits);
 
 /* The split count hq_decode_attn uses for n_splits == 0. */

@@ -90,6 +90,26 @@ def test_decode_rejects_null_and_dtype_and_workspace():
     assert _decode(kv, n_splits=-1) == hq.HQ_ERR_INVALID_ARG
 
 
+def _step(kv, q_acc=FAKE, R=64, step=0, evict=1, ws_bytes=1 << 40):
+    return hq.lib().hq_decode_step(FAKE, hq.HQ_BF16, 8, ctypes.byref(kv) if kv is not None else None,
+                                   0.0, 0, FAKE, None, FAKE, ws_bytes, q_acc, R, step, evict, None)
+
+
+def test_decode_step_rejects():
+    # T - W = 872 needs t_cap >= 873 for the eviction: 896 is enough, 872 is not
+    assert _step(_kv(t_cap=864)) == hq.HQ_ERR_INVALID_ARG             # also < T - W
+    assert _step(_kv(T=1024, W=128, t_cap=896)) == hq.HQ_ERR_INVALID_ARG   # T - W = 896: no room
+    assert "t_cap" in hq.hq_last_error()
+    assert _step(_kv(), R=0) == hq.HQ_ERR_INVALID_ARG
+    assert _step(_kv(), R=2000) == hq.HQ_ERR_INVALID_ARG
+    assert _step(_kv(), step=-1) == hq.HQ_ERR_INVALID_ARG
+    assert _step(_kv(), q_acc=FAKE + 4) == hq.HQ_ERR_INVALID_ARG      # misaligned ring
+    assert _step(None) == hq.HQ_ERR_INVALID_ARG
+    assert _step(_kv(), ws_bytes=1) == hq.HQ_ERR_WORKSPACE
+    # without eviction the t_cap rule is that of hq_decode_attn
+    assert _step(_kv(T=1024, W=128, t_cap=896), evict=0, ws_bytes=1) == hq.HQ_ERR_WORKSPACE
+
+
 def test_workspace_sizes():
     kv = _kv()
     s0 = hq.hq_decode_workspace_size(kv, 8, 0)
