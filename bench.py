@@ -2,14 +2,15 @@
 
 One step = one steady-state decode step of one attention layer over its
 hybrid KV cache:
-  1. hq_detect_vlines: the step's queries go into the 64-slot ring; every
-     64th step (step mod 64 == 63) the Q_acc . K^T column scores and the
-     top-k run, and the new VL set is installed (hq_vl_bitmap +
-     hq_gather_rows of the VL keys and values);
-  2. hq_quantize_kv_pair: the token leaving the window is packed into INT4
-     (keys and values in one launch);
-  3. hq_decode_attn: attention over INT4 + VL + window with the split-K
-     LSE merge.
+  1. hq_decode_step: attention over INT4 + VL + window with the split-K LSE
+     merge; in the same launches the step's queries go into the detector's
+     64-slot ring and the window's oldest token is packed into INT4;
+  2. every 64th step (step mod 64 == 63) hq_detect_vlines scores the ring
+     (Q_acc . K^T column sums, top-k) and the new VL set is installed for the
+     next step (hq_vl_bitmap + hq_gather_rows of the VL keys and values).
+With --separate-upkeep the upkeep runs as its own calls before the
+attention (hq_detect_vlines with the new queries, hq_quantize_kv_pair, then
+hq_decode_attn), four launches per step instead of two.
 Steps rotate over `--copies` independent layer caches (>= 1 GB in total) so
 that the 256 MB Infinity Cache cannot hold the working set: every step reads
 its cache from HBM as it would in a model with many layers. All inputs are
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--separate-upkeep", action="store_true",
+                    help="queries to the ring and the eviction as separate calls (hq_decode_attn)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MB (counter calibration)")
     return ap.parse_args()
@@ -121,7 +124,8 @@ def main():
         Kc = K0 if c == 0 else K0.clone()
         Vc = V0 if c == 0 else V0.clone()
         qa = q_hist.clone()
-        cache = hq.HybridCache(B, Hkv, D, T, W, k, dt)
+        # one spare INT4 row: the window's oldest token is packed into row T - W
+        cache = hq.HybridCache(B, Hkv, D, T, W, k, dt, t_cap=(nq + 1 + 31) // 32 * 32)
         cache.quantize(Kc, Vc)
         hq.hq_detect_vlines(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method, idx_new, None, det_ws)
         cache.set_vl(Kc, Vc, idx_new)
@@ -140,21 +144,31 @@ def main():
 
     n_heads = B * Hkv
 
+    def install(c, cache, Kc, Vc):
+        hq.hq_vl_bitmap(idx_new, n_heads, k, cache.t_cap, cache.vl_bits)
+        hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
+        hq.hq_gather_rows(Vc, n_heads, T, D, idx_new, k, cache.vl_v)
+
     def step(s: int):
         c = s % copies
         cache, Kc, Vc = caches[c], Ks[c], Vs[c]
         qn = q_steps[s % q_steps.shape[0]]
-        ran = hq.hq_detect_vlines(qn, qaccs[c], B, Hq, Hkv, D, R, s, False, Kc, T, nq, k, method,
-                                  idx_new, None, det_ws)
-        if ran:
-            hq.hq_vl_bitmap(idx_new, n_heads, k, cache.t_cap, cache.vl_bits)
-            hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
-            hq.hq_gather_rows(Vc, n_heads, T, D, idx_new, k, cache.vl_v)
-        # the token leaving the window goes to INT4 (static context: last INT4 row)
-        hq.hq_quantize_kv_pair(Kc[:, :, nq - 1:], Vc[:, :, nq - 1:], n_heads, 1, D, T * D, D,
-                               cache.k_codes, cache.k_sz, cache.v_codes, cache.v_sz,
-                               cache.t_cap, nq - 1)
-        hq.hq_decode_attn(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
+        if args.separate_upkeep:
+            ran = hq.hq_detect_vlines(qn, qaccs[c], B, Hq, Hkv, D, R, s, False, Kc, T, nq, k, method,
+                                      idx_new, None, det_ws)
+            if ran:
+                install(c, cache, Kc, Vc)
+            # the token leaving the window (position T - W) goes to INT4 row T - W
+            hq.hq_quantize_kv_pair(Kc[:, :, nq:], Vc[:, :, nq:], n_heads, 1, D, T * D, D,
+                                   cache.k_codes, cache.k_sz, cache.v_codes, cache.v_sz,
+                                   cache.t_cap, nq)
+            hq.hq_decode_attn(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
+            return
+        hq.hq_decode_step(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c],
+                          q_acc=qaccs[c], R=R, step=s, evict=True)
+        if hq.hq_detect_vlines(None, qaccs[c], B, Hq, Hkv, D, R, s, False, Kc, T, nq, k, method,
+                               idx_new, None, det_ws):
+            install(c, cache, Kc, Vc)
 
     # ------------------------------------------------------------ timed steps
     for s in range(args.warmup):
@@ -253,6 +267,8 @@ def main():
             "layer_copies_rotated": copies, "detect_method": args.detect_method,
             "decode_splits": hq.hq_decode_auto_splits(descs[0], Hq) if args.splits == 0 else args.splits,
             "detect_every": R, "detections_in_timed_steps": n_detect,
+            "step_calls": ("hq_detect_vlines(q) + hq_quantize_kv_pair + hq_decode_attn" if args.separate_upkeep
+                           else "hq_decode_step (+ hq_detect_vlines every 64th step)"),
         },
         "roofline": {
             "kernel": "decode_kernel (hq_decode_attn)",
