@@ -86,7 +86,7 @@ struct DecodeParams {
   float cs;                 // sm_scale * log2(e)
   // per-step upkeep (hq_decode_step), run by extra blocks of the merge launch
   int merge_blocks;         // blocks of the merge itself
-  int up_q;                 // 1: one block copies q into the detector's query ring
+  int up_q;                 // blocks that copy q into the detector's query ring (0: none)
   uint8_t *q_ring;          // [B][Hq][R][D] of the query dtype
   int R, ring_slot;
   int evict;                // 1: pack the window's oldest row into INT4 row T - W
@@ -1213,7 +1213,8 @@ constexpr int kMergeSlice = 32;
 // Per-step upkeep of hq_decode_step. It runs in the merge launch, after every
 // split has read the cache, so writing INT4 row T - W (outside this step's
 // INT4 range [0, T - W)) cannot race with them.
-//  * block 0 (if up_q): q [B][Hq][D] into slot ring_slot of q_ring;
+//  * the first up_q blocks: q [B][Hq][D] into slot ring_slot of q_ring, one
+//    16-byte chunk per thread;
 //  * the next blocks (if evict): the window's oldest row (position T - W, ring
 //    row win_offset) of every (b, KV head) packed like hq_quantize_kv_pair:
 //    four lanes (a DPP quad) per 32-channel group, K in rows, V in TILE16.
@@ -1223,8 +1224,8 @@ __device__ void upkeep(const DecodeParams &P, int ub) {
   constexpr int NG = D / 32;
   if (ub < P.up_q) {
     constexpr int CH = D * EB / 16;                         // 16-byte chunks per q row
-    const int rows = P.B * P.Hq;
-    for (int c = threadIdx.x; c < rows * CH; c += kThreads) {
+    const int c = ub * kThreads + static_cast<int>(threadIdx.x);
+    if (c < P.B * P.Hq * CH) {
       const int r = c / CH, cc = c % CH;
       const uint4 v = reinterpret_cast<const uint4 *>(P.q)[c];
       reinterpret_cast<uint4 *>(P.q_ring + (static_cast<int64_t>(r) * P.R + P.ring_slot) * (D * EB))[cc] = v;
@@ -1599,7 +1600,9 @@ hq_status decode_common(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid
   const float scale = sm_scale == 0.f ? 1.0f / sqrtf(static_cast<float>(kv->D)) : sm_scale;
   P.cs = scale * kLog2e;
   P.merge_blocks = pl.units * pl.HB * (kv->D / kMergeSlice);
-  P.up_q = up.q_ring ? 1 : 0;
+  P.up_q = up.q_ring ? static_cast<int>(ceil_div(static_cast<int64_t>(kv->B) * Hq * kv->D *
+                                                    (q_dtype == HQ_F32 ? 4 : 2) / 16, kThreads))
+                     : 0;
   P.q_ring = static_cast<uint8_t *>(up.q_ring);
   P.R = up.R;
   P.ring_slot = up.slot;
