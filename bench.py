@@ -210,6 +210,9 @@ def main():
     torch.cuda.synchronize()
     det_us = d0.elapsed_time(d1) * 1e3 / n_det
 
+    # ------------------------------------------------------------ HBM read ceiling, same run
+    stream_gbs = stream_read_ceiling(torch, hq, dev, stream)
+
     if args.calib_copy_mb:
         a = torch.empty(args.calib_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
         b_ = torch.empty_like(a)
@@ -282,6 +285,8 @@ def main():
             "traffic_over_algorithmic": (round(traffic / dec_bytes, 4) if traffic else None),
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "avg_launch_us": round(dec_us, 3),
+            "stream_read_gbs": round(stream_gbs, 1),
+            "frac_of_stream_read": round(achieved / stream_gbs, 4),
         },
         "detector": {"us_per_detection": round(det_us, 2), "method": args.detect_method,
                      "overhead_vs_64_decode_kernels": round(det_us / (64 * dec_us), 4)},
@@ -290,6 +295,25 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def stream_read_ceiling(torch, hq, dev, stream, gib: int = 2, reps: int = 10) -> float:
+    """GB/s of hq_stream_read (one sequential non-temporal read) over a
+    buffer of `gib` GiB, far beyond the 256 MB Infinity Cache."""
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(hq.hq_stream_read_sink_bytes() // 4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        hq.hq_stream_read(buf, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        hq.hq_stream_read(buf, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = reps * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    return gbs
 
 
 def main_prefill(args):

@@ -79,6 +79,8 @@ _SIGS = {
                                       ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_void_p]),
     "hq_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HybridKV), ctypes.c_int, ctypes.c_int]),
+    "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "hq_stream_read_sink_bytes": (ctypes.c_size_t, []),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
     "hq_prefill_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
@@ -213,6 +215,15 @@ def hq_decode_attn(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, stream
     _check(lib().hq_decode_attn(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
                                 n_splits, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream)))
+
+
+def hq_stream_read(buf, sink, stream=None):
+    """One sequential read of the whole tensor `buf` (measurement utility)."""
+    _check(lib().hq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def hq_stream_read_sink_bytes() -> int:
+    return int(lib().hq_stream_read_sink_bytes())
 
 
 def hq_decode_step(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, q_acc=None, R=64, step=0,

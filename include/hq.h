@@ -300,6 +300,19 @@ hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype 
  * out of range). */
 size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D, int k_vl);
 
+/*
+ * hq_stream_read -- measurement utility (not part of the method): reads
+ * `bytes` of device memory at buf once, sequentially, in 16-byte
+ * non-temporal loads from 2048 workgroups, and writes nothing in practice
+ * (sink is only a guard against the loads being removed: it must hold
+ * hq_stream_read_sink_bytes() bytes). Timed over a buffer far larger than
+ * the 256 MB Infinity Cache it gives the HBM read ceiling that the decode
+ * bandwidth is compared with. buf, bytes 16-byte aligned; HQ_ERR_INVALID_ARG
+ * otherwise.
+ */
+hq_status hq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+size_t hq_stream_read_sink_bytes(void);
+
 const char *hq_status_string(hq_status s);
 const char *hq_last_error(void);
 int hq_abi_version(void);
