@@ -220,7 +220,10 @@ size_t hq_detect_workspace_size(int B, int Hkv, int64_t cand_end, int k_top);
  * ws: at least hq_decode_workspace_size(kv, Hq, n_splits) bytes (no
  * initialisation needed). Calls that share a workspace and run concurrently
  * on different streams race; calls on one stream do not.
- * Requires Hq % Hkv == 0 and G in {1, 2, 4, 8, 16}.
+ * Requires Hq % Hkv == 0 and G in {1, 2, 4, 8, 16}. With D == 128 and
+ * G a multiple of 4, the INT4 keys are dotted with the queries in fp16:
+ * bf16 queries must then satisfy |q| < 65504 (magnitudes below 2^-17 round
+ * to the fp16 subnormal grid, absolute error below 2^-25).
  */
 hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
                          float sm_scale, int n_splits, float *out, float *lse, void *ws,
