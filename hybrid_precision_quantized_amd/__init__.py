@@ -21,6 +21,7 @@ HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP = ra
 HQ_F32, HQ_BF16, HQ_F16 = 0, 1, 2
 HQ_LAYOUT_ROWS, HQ_LAYOUT_TILE16 = 0, 1
 HQ_DETECT_MATMUL, HQ_DETECT_QSUM = 0, 1
+HQ_KV_DROP_INT4 = 1
 
 _DT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: HQ_F16}
 
@@ -41,7 +42,7 @@ class HybridKV(ctypes.Structure):
         ("vl_bits", ctypes.c_void_p),
         ("vl_k", ctypes.c_void_p), ("vl_v", ctypes.c_void_p),
         ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
-        ("win_offset", ctypes.c_int), ("hp_dtype", ctypes.c_int),
+        ("win_offset", ctypes.c_int), ("hp_dtype", ctypes.c_int), ("flags", ctypes.c_int),
     ]
 
 

@@ -40,6 +40,7 @@ class HybridCache:
         self.win_k = torch.zeros((B, Hkv, max(W, 1), D), dtype=hp_dtype, device=dev)
         self.win_v = torch.zeros_like(self.win_k)
         self.win_offset = 0
+        self.flags = 0
         self._n = n
 
     # ------------------------------------------------------------ building
@@ -92,6 +93,7 @@ class HybridCache:
         d.win_k, d.win_v = self.win_k.data_ptr(), self.win_v.data_ptr()
         d.win_offset = self.win_offset
         d.hp_dtype = _HP[self.hp_dtype]
+        d.flags = self.flags
         return d
 
     def nbytes_algorithmic(self) -> int:

@@ -1393,12 +1393,14 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
   const int step = 64 / (kv->D / 32);                         // positions per wave step
   const int64_t gran = static_cast<int64_t>(kWaves) * step;   // INT4 split granularity (64 or 128)
   pl.nq = kv->T - kv->W;
+  // positions of the INT4 pass (none when the INT4 set is dropped)
+  const int64_t nq_att = (kv->flags & HQ_KV_DROP_INT4) ? 0 : pl.nq;
   const int64_t nfp = static_cast<int64_t>(kv->k) + kv->W;
   // Splits are sized by cost, not bytes: a 16-bit row costs about twice an
   // INT4 position (fp32 P . V products and 3.2x the bytes, against the
   // unpacking of the codes).
   constexpr double kFpRowCost = 2.0;
-  const double cost_q = static_cast<double>(pl.nq);
+  const double cost_q = static_cast<double>(nq_att);
   const double cost_fp = kFpRowCost * static_cast<double>(nfp);
   int S = n_splits;
   if (S <= 0) {
@@ -1408,7 +1410,7 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
     const int target_blocks = steps_per_wave >= 128.0 ? 2048 : 512;
     S = static_cast<int>(ceil_div(target_blocks, pl.units));
     // at least ~4 wave steps of work per wave
-    const int64_t max_s = ceil_div(pl.nq + nfp, 16LL * step);
+    const int64_t max_s = ceil_div(nq_att + nfp, 16LL * step);
     if (S > max_s) S = static_cast<int>(max_s > 0 ? max_s : 1);
     if (S > kMaxSplits) S = kMaxSplits;
     if (S < 1) S = 1;
@@ -1422,19 +1424,19 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
     if (s_fp > mx) s_fp = static_cast<int>(mx);
   }
   int s_q = 0;
-  if (pl.nq > 0) {
+  if (nq_att > 0) {
     s_q = S - s_fp;
     if (s_q < 1) s_q = 1;
     // the VL bitmap and the ranges: at most 2^20 positions per split
-    const int64_t mn = ceil_div(pl.nq, 1LL << 20);
+    const int64_t mn = ceil_div(nq_att, 1LL << 20);
     if (s_q < mn) s_q = static_cast<int>(mn);
-    const int64_t mx = ceil_div(pl.nq, gran);
+    const int64_t mx = ceil_div(nq_att, gran);
     if (s_q > mx) s_q = static_cast<int>(mx);
   }
   // INT4 splits start at multiples of gran (a multiple of 64): the kernel
   // reads the VL bits of a chunk from one aligned bitmap word
-  pl.len_q = s_q > 0 ? ceil_div(ceil_div(pl.nq, s_q), gran) * gran : 0;
-  pl.S_q = s_q > 0 ? static_cast<int>(ceil_div(pl.nq, pl.len_q)) : 0;
+  pl.len_q = s_q > 0 ? ceil_div(ceil_div(nq_att, s_q), gran) * gran : 0;
+  pl.S_q = s_q > 0 ? static_cast<int>(ceil_div(nq_att, pl.len_q)) : 0;
   // the 16-bit splits divided between the VL rows and the window rows
   int s_win = 0, s_vl = 0;
   if (s_fp > 0) {
@@ -1486,7 +1488,9 @@ hq_status validate(const void *q, int q_dtype, int Hq, const hq_hybrid_kv *kv, f
   if (kv->W > 0 && (kv->win_offset < 0 || kv->win_offset >= kv->W))
     return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: win_offset out of range");
   if (!q || !out) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null q or out");
-  if (kv->T - kv->W > 0 && (!kv->k_codes || !kv->v_codes || !kv->k_sz || !kv->v_sz || !kv->vl_bits))
+  if (kv->flags & ~HQ_KV_DROP_INT4) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: unknown flags");
+  if (kv->T - kv->W > 0 && !(kv->flags & HQ_KV_DROP_INT4) &&
+      (!kv->k_codes || !kv->v_codes || !kv->k_sz || !kv->v_sz || !kv->vl_bits))
     return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null INT4 plane or VL bitmap");
   if (kv->k > 0 && (!kv->vl_k || !kv->vl_v)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null VL rows");
   if (kv->W > 0 && (!kv->win_k || !kv->win_v)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null window rows");

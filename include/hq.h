@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 1
+#define HQ_ABI_VERSION 2
 
 typedef enum {
   HQ_OK = 0,
@@ -106,7 +106,17 @@ typedef struct {
                                  T - W + i sits in row (win_offset + i) % W */
   int win_offset;             /* 0 <= win_offset < W (0 when W == 0) */
   hq_dtype hp_dtype;          /* dtype of the 16-bit rows: HQ_BF16, HQ_F16 or HQ_F32 */
+  int flags;                  /* 0, or HQ_KV_DROP_INT4 */
 } hq_hybrid_kv;
+
+/* hq_hybrid_kv.flags. HQ_KV_DROP_INT4 leaves the INT4 positions out of the
+ * softmax: attention over the VL rows and the window only, the sparse
+ * baseline that discards the long tail which the hybrid cache keeps in 4 bits
+ * [MR, Improvements and Ablation Studies: Table 12 compares keeping the
+ * low-precision long tail with dropping it]. The INT4 planes and the VL
+ * bitmap are then not read (they may be null). With k == 0 it is attention
+ * over the window alone. */
+#define HQ_KV_DROP_INT4 1
 
 /*
  * hq_quantize_kv -- pack rows into INT4 codes plus fp16 scale/zero

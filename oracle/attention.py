@@ -114,6 +114,19 @@ def decode_head(q: np.ndarray, K_hp: np.ndarray, V_hp: np.ndarray,
     return attention(q, Kt, Vt, sm_scale)
 
 
+def decode_sparse_head(q: np.ndarray, K_hp: np.ndarray, V_hp: np.ndarray,
+                       vl_idx: np.ndarray, W: int, sm_scale: float | None = None):
+    """The sparse baseline of the ablation ([MR] "Improvements and Ablation
+    Studies", Table 12: dropping the long tail that the hybrid cache keeps in
+    low precision): one softmax over the VL and window positions only, the
+    quantized set Qs left out. q [G][D], K_hp, V_hp [T][D]. Returns
+    (o [G][D], lse [G])."""
+    T = K_hp.shape[0]
+    vl, win, _ = hybrid_sets(T, W, vl_idx)
+    keep = vl | win
+    return attention(q, np.asarray(K_hp)[keep], np.asarray(V_hp)[keep], sm_scale)
+
+
 def decode(q: np.ndarray, K_hp: np.ndarray, V_hp: np.ndarray,
            k_packed: np.ndarray, k_sz: np.ndarray,
            v_packed: np.ndarray, v_sz: np.ndarray,

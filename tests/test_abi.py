@@ -37,7 +37,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_strings():
-    assert hq.hq_abi_version() == 1
+    assert hq.hq_abi_version() == 2
     assert hq.hq_status_string(0) == "ok"
     assert "workspace" in hq.hq_status_string(3)
 
@@ -108,6 +108,16 @@ def test_decode_step_rejects():
     assert _step(_kv(), ws_bytes=1) == hq.HQ_ERR_WORKSPACE
     # without eviction the t_cap rule is that of hq_decode_attn
     assert _step(_kv(T=1024, W=128, t_cap=896), evict=0, ws_bytes=1) == hq.HQ_ERR_WORKSPACE
+
+
+def test_decode_flags():
+    assert _decode(_kv(flags=2)) == hq.HQ_ERR_INVALID_ARG                  # unknown flag
+    assert "flags" in hq.hq_last_error()
+    # dropping the INT4 set: the planes and the bitmap may be null (the call
+    # then gets as far as the workspace check)
+    kv = _kv(flags=hq.HQ_KV_DROP_INT4, k_codes=None, v_codes=None, k_sz=None, v_sz=None, vl_bits=None)
+    assert _decode(kv, ws_bytes=1) == hq.HQ_ERR_WORKSPACE
+    assert _decode(_kv(k_codes=None), ws_bytes=1) == hq.HQ_ERR_INVALID_ARG
 
 
 def test_workspace_sizes():

@@ -213,3 +213,39 @@ def test_decode_qwen128k_sampled():
         sl = slice(h * w.G, (h + 1) * w.G)
         ro[b, sl], rl[b, sl] = attention.decode_head(q[b, sl], Kh, Vh, kp, ks, vp, vs, vl[b, h], w.W)
     _check(got, (ro, rl), units=units, G=w.G)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,T,W,k,dtype", [
+    (2, 8, 2, 128, 1000, 64, 30, "bf16"),
+    (1, 8, 2, 128, 1000, 64, 0, "bf16"),          # window only
+    (1, 8, 2, 64, 999, 33, 17, "f32"),
+    (1, 32, 8, 128, 32768, 128, 1638, "bf16"),    # the Llama-shaped workload (two units checked)
+])
+def test_decode_drop_int4(B, Hq, Hkv, D, T, W, k, dtype):
+    """HQ_KV_DROP_INT4: attention over the VL and window rows only, against the
+    oracle's sparse baseline."""
+    say(f"drop-int4 B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} W={W} k={k} {dtype}")
+    w = _workload(B, Hq, Hkv, D, T, W, k, dtype, 7000 + T + k)
+    K, V = synth.all_keys(w), synth.all_values(w)
+    q = synth.all_queries(w)
+    vl = _vl_random(w)
+    dt = TORCH_DT[dtype]
+    cache = hq.HybridCache(B, Hkv, D, T, W, k, dt)
+    cache.build(to_dev(K, dtype), to_dev(V, dtype), torch.from_numpy(vl).cuda() if k else None)
+    cache.flags = hq.HQ_KV_DROP_INT4
+    kv = cache.descriptor()
+    ws = torch.full((hq.hq_decode_workspace_size(kv, Hq, 0),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    hq.hq_decode_attn(to_dev(q, dtype), Hq, kv, 0.0, 0, out, lse, ws)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    if T > 10000:
+        units = [(0, 0), (0, Hkv - 1)]
+    ro = np.full((B, Hq, D), np.nan)
+    rl = np.full((B, Hq), np.nan)
+    for b, h in units:
+        sl = slice(h * G, (h + 1) * G)
+        ro[b, sl], rl[b, sl] = attention.decode_sparse_head(q[b, sl], K[b, h], V[b, h], vl[b, h], W)
+    _check((out.cpu().numpy(), lse.cpu().numpy()), (ro, rl), units=units, G=G)

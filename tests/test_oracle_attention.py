@@ -202,3 +202,53 @@ def test_set_validation():
     vl, win, qs = attention.hybrid_sets(10, 3, np.array([0, 4]))
     assert vl.sum() == 2 and win.sum() == 3 and qs.sum() == 5
     assert not np.any(vl & win) and not np.any(vl & qs) and not np.any(win & qs)
+
+
+def test_sparse_baseline_window_only_is_sdpa_over_the_window():
+    """k = 0: the sparse baseline is attention over the last W rows (a
+    library routine, float64)."""
+    rng = np.random.default_rng(21)
+    T, D, W = 150, 64, 24
+    q, K, V, _, _, _, _, _ = _case(rng, T, D, W=W, k=0)
+    o, lse = attention.decode_sparse_head(q, K, V, np.zeros(0, np.int32), W)
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None, :, None, :],
+        torch.from_numpy(K[T - W:].astype(np.float64))[None, None].expand(1, q.shape[0], W, D),
+        torch.from_numpy(V[T - W:].astype(np.float64))[None, None].expand(1, q.shape[0], W, D))
+    assert np.max(np.abs(o - t[0, :, 0].numpy())) < 1e-12
+    lg = (q.astype(np.float64) @ K[T - W:].astype(np.float64).T) / math.sqrt(D)
+    assert np.max(np.abs(lse - np.log(np.exp(lg).sum(1)))) < 1e-12
+
+
+def test_sparse_baseline_brute_force_and_merge_identity():
+    """Scalar brute force over the VL and window positions; and merging the
+    sparse state with the state of the quantized set alone gives the hybrid
+    step (the sets are disjoint and cover [0, T))."""
+    rng = np.random.default_rng(22)
+    T, D, W, k = 40, 32, 6, 5
+    q, K, V, kp, ks, vp, vs, vl = _case(rng, T, D, G=2, W=W, k=k)
+    o, lse = attention.decode_sparse_head(q, K, V, vl, W)
+    keep = sorted(set(int(j) for j in vl) | set(range(T - W, T)))
+    for g in range(q.shape[0]):
+        lg = [sum(float(q[g, d]) * float(K[j, d]) for d in range(D)) / math.sqrt(D) for j in keep]
+        m = max(lg)
+        e = [math.exp(x - m) for x in lg]
+        L = sum(e)
+        for d in range(D):
+            ref = sum(e[i] * float(V[j, d]) for i, j in enumerate(keep)) / L
+            assert abs(o[g, d] - ref) < 1e-12
+        assert abs(lse[g] - (m + math.log(L))) < 1e-12
+    # merge identity with the quantized set
+    _, _, qs = attention.hybrid_sets(T, W, vl)
+    Kq = quant.dequantize_rows(kp, ks)[qs[:T - W]]
+    Vq = quant.dequantize_rows(vp, vs)[qs[:T - W]]
+    scale = 1.0 / math.sqrt(D)
+    sk = K[np.array(keep)].astype(np.float64)
+    sv = V[np.array(keep)].astype(np.float64)
+    oh, lh = attention.decode_head(q, K, V, kp, ks, vp, vs, vl, W)
+    for g in range(q.shape[0]):
+        st_s = attention.softmax_state(scale * (sk @ q[g].astype(np.float64))[None], sv)
+        st_q = attention.softmax_state(scale * (Kq @ q[g].astype(np.float64))[None], Vq)
+        m, L, om = attention.lse_merge([st_s, st_q])
+        assert np.max(np.abs(om[0] - oh[g])) < 1e-12
+        assert abs(m[0] + math.log(L[0]) - lh[g]) < 1e-12
