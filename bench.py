@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--ablation", action="store_true",
+                    help="decode settings of the ablation (hybrid, sparse, window only, strict K4V4, "
+                         "all 16-bit): bytes, time and error against exact attention")
     ap.add_argument("--separate-upkeep", action="store_true",
                     help="queries to the ring and the eviction as separate calls (hq_decode_attn)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -90,6 +93,8 @@ def main():
         sys.exit(1)
     if args.workload == "prefill32k":
         return main_prefill(args)
+    if args.ablation:
+        return main_ablation(args)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     w = synth.WORKLOADS[args.workload]
@@ -293,6 +298,114 @@ def main():
         "step_bytes": int(step_bytes),
         "setup_s": round(t_setup, 1),
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def main_ablation(args):
+    """Decode-step ablation on one workload ([MR] "Improvements and Ablation
+    Studies": Table 12, keeping the low-precision long tail against dropping
+    it; Table 14, memory overhead against strict K4V4). Settings, all on the
+    same synthetic layer and the same detected VL set:
+      hybrid      INT4 majority + VL + window (the method);
+      sparse      VL + window only (HQ_KV_DROP_INT4);
+      window      the window only;
+      k4v4        every position INT4 (k = W = 0);
+      bf16        every position 16-bit (W = T), i.e. plain attention.
+    For each: the algorithmic bytes of one hq_decode_attn call, its time
+    (HIP events, caches rotated past the Infinity Cache), the bytes held in
+    the cache for the layer, and the output error against exact attention
+    (fp32 on the GPU over the 16-bit keys and values)."""
+    import torch
+    import hybrid_precision_quantized_amd as hq
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS[args.workload]
+    B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
+    G = Hq // Hkv
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    hp = 2
+
+    def to_dev(x32):
+        return torch.from_numpy(synth.f32_to_bf16_bits(x32).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    K = torch.empty((B, Hkv, T, D), dtype=dt, device=dev)
+    V = torch.empty_like(K)
+    for b in range(B):
+        K[b].copy_(to_dev(np.stack([synth.keys(w, b, h) for h in range(Hkv)])))
+        V[b].copy_(to_dev(np.stack([synth.values(w, b, h) for h in range(Hkv)])))
+    q = to_dev(synth.all_queries(w))
+    q_hist = to_dev(synth.all_query_histories(w))
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
+    det_ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, T - W, k), dtype=torch.uint8, device=dev)
+    hq.hq_detect_vlines(None, q_hist, B, Hq, Hkv, D, 64, 0, True, K, T, T - W, k, hq.HQ_DETECT_MATMUL,
+                        idx, None, det_ws)
+
+    # exact attention, fp32
+    qf = q.float().view(B, Hkv, G, D)
+    Kf = K.float()
+    lg = torch.matmul(qf, Kf.transpose(-1, -2).contiguous()) / np.sqrt(D)
+    exact = torch.matmul(torch.softmax(lg, dim=-1), V.float()).view(B, Hq, D)
+    del Kf, lg
+    rms = float(exact.pow(2).mean().sqrt())
+
+    settings = [("hybrid", k, W, 0), ("sparse", k, W, hq.HQ_KV_DROP_INT4),
+                ("window", 0, W, hq.HQ_KV_DROP_INT4), ("k4v4", 0, 0, 0), ("bf16", 0, T, 0)]
+    rows = []
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    for name, kk, ww, flags in settings:
+        nq = T - ww
+        units = B * Hkv
+        int4_pos = 0 if flags else nq - kk
+        dec_bytes = (units * (int4_pos * (D + (D // 32) * 8) + (kk + ww) * 2 * D * hp
+                              + (0 if flags else (nq + 31) // 32 * 4))
+                     + B * Hq * D * hp + B * Hq * D * 4 + B * Hq * 4)
+        held = units * ((0 if flags else nq * (D + (D // 32) * 8)) + (kk + ww) * 2 * D * hp)
+        per_copy = max(held, 1)
+        copies = max(1, min(24, int(np.ceil(1.2e9 / per_copy))))
+        caches = []
+        for _ in range(copies):
+            c = hq.HybridCache(B, Hkv, D, T, ww, kk, dt)
+            c.build(K, V, idx[:, :, :kk].contiguous() if kk else None)
+            c.flags = flags
+            caches.append(c)
+        descs = [c.descriptor() for c in caches]
+        ws = torch.zeros(hq.hq_decode_workspace_size(descs[0], Hq, 0), dtype=torch.uint8, device=dev)
+        hq.hq_decode_attn(q, Hq, descs[0], 0.0, 0, out, lse, ws)
+        torch.cuda.synchronize()
+        err = (out - exact).abs()
+        max_rel = float(err.max()) / rms
+        l2 = float(torch.linalg.vector_norm(out - exact) / torch.linalg.vector_norm(exact))
+        for i in range(10):
+            hq.hq_decode_attn(q, Hq, descs[i % copies], 0.0, 0, out, lse, ws)
+        n = 100
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            hq.hq_decode_attn(q, Hq, descs[i % copies], 0.0, 0, out, lse, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        rows.append({"setting": name, "k": kk, "W": ww, "drop_int4": bool(flags),
+                     "algorithmic_bytes": int(dec_bytes), "us_per_call": round(us, 2),
+                     "gbs": round(dec_bytes / (us * 1e-6) / 1e9, 1), "cache_bytes": int(held),
+                     "max_abs_err_over_rms": round(max_rel, 5), "rel_l2_err": round(l2, 6)})
+        del caches, descs, ws
+        torch.cuda.empty_cache()
+    k4 = next(r for r in rows if r["setting"] == "k4v4")["cache_bytes"]
+    for r in rows:
+        r["cache_vs_k4v4"] = round(r["cache_bytes"] / k4 - 1.0, 4)
+    line = {
+        "metric": "decode ablation: bytes, us per hq_decode_attn call and error against exact attention",
+        "n_gpus": 1, "data": "synthetic (seeded; shapes of the named model's attention layer)",
+        "config": {"workload": f"{args.workload}: B {B}, {Hq} q / {Hkv} kv heads, head_dim {D}, context {T}, "
+                               f"window {W}, VL budget {k} (detected from a 64-step query history)"},
+        "exact_reference": "fp32 softmax(q K^T / sqrt(D)) V over the bf16 keys and values",
+        "rows": rows,
     }
     print(json.dumps(line), flush=True)
 
