@@ -52,7 +52,9 @@ def parse():
                     choices=["llama32k", "qwen128k", "glm32k", "prefill32k"],
                     help="decode workloads, or prefill32k: the causal hybrid prefill of a 32K prompt")
     ap.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0 = auto, >= 1 GB)")
-    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum"])
+    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum", "cache"],
+                    help="matmul: Q_acc K^T on MFMA; qsum: summed queries, GEMV; cache: summed "
+                         "queries against the INT4 key cache (hq_detect_vlines_cache)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -103,6 +105,7 @@ def main():
     R = 64
     nq = T - W
     method = hq.HQ_DETECT_MATMUL if args.detect_method == "matmul" else hq.HQ_DETECT_QSUM
+    from_cache = args.detect_method == "cache"
 
     # ------------------------------------------------------------ inputs
     t_setup = time.time()
@@ -132,7 +135,11 @@ def main():
         # one spare INT4 row: the window's oldest token is packed into row T - W
         cache = hq.HybridCache(B, Hkv, D, T, W, k, dt, t_cap=(nq + 1 + 31) // 32 * 32)
         cache.quantize(Kc, Vc)
-        hq.hq_detect_vlines(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method, idx_new, None, det_ws)
+        if from_cache:
+            hq.hq_detect_vlines_cache(None, qa, Hq, R, 0, True, cache.descriptor(), nq, k, idx_new, None, det_ws)
+        else:
+            hq.hq_detect_vlines(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method, idx_new, None,
+                                det_ws)
         cache.set_vl(Kc, Vc, idx_new)
         cache.set_window(Kc, Vc)
         caches.append(cache)
@@ -149,6 +156,13 @@ def main():
 
     n_heads = B * Hkv
 
+    def detect(s, c, force, q_new=None):
+        if from_cache:
+            return hq.hq_detect_vlines_cache(q_new, qaccs[c], Hq, R, s, force, descs[c], nq, k, idx_new, None,
+                                             det_ws)
+        return hq.hq_detect_vlines(q_new, qaccs[c], B, Hq, Hkv, D, R, s, force, Ks[c], T, nq, k, method,
+                                   idx_new, None, det_ws)
+
     def install(c, cache, Kc, Vc):
         hq.hq_vl_bitmap(idx_new, n_heads, k, cache.t_cap, cache.vl_bits)
         hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
@@ -159,9 +173,7 @@ def main():
         cache, Kc, Vc = caches[c], Ks[c], Vs[c]
         qn = q_steps[s % q_steps.shape[0]]
         if args.separate_upkeep:
-            ran = hq.hq_detect_vlines(qn, qaccs[c], B, Hq, Hkv, D, R, s, False, Kc, T, nq, k, method,
-                                      idx_new, None, det_ws)
-            if ran:
+            if detect(s, c, False, qn):
                 install(c, cache, Kc, Vc)
             # the token leaving the window (position T - W) goes to INT4 row T - W
             hq.hq_quantize_kv_pair(Kc[:, :, nq:], Vc[:, :, nq:], n_heads, 1, D, T * D, D,
@@ -171,8 +183,7 @@ def main():
             return
         hq.hq_decode_step(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c],
                           q_acc=qaccs[c], R=R, step=s, evict=True)
-        if hq.hq_detect_vlines(None, qaccs[c], B, Hq, Hkv, D, R, s, False, Kc, T, nq, k, method,
-                               idx_new, None, det_ws):
+        if detect(s, c, False):
             install(c, cache, Kc, Vc)
 
     # ------------------------------------------------------------ timed steps
@@ -209,8 +220,7 @@ def main():
     n_det = 20
     d0.record(stream)
     for i in range(n_det):
-        c = i % copies
-        hq.hq_detect_vlines(None, qaccs[c], B, Hq, Hkv, D, R, 0, True, Ks[c], T, nq, k, method, idx_new, None, det_ws)
+        detect(0, i % copies, True)
     d1.record(stream)
     torch.cuda.synchronize()
     det_us = d0.elapsed_time(d1) * 1e3 / n_det

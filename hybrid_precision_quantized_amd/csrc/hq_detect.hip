@@ -31,6 +31,12 @@
 namespace hq {
 namespace {
 
+template <int DT>
+__device__ __forceinline__ float load_half(uint32_t h) {
+  if constexpr (DT == HQ_BF16) return bf16_to_f32(h);
+  else return f16_to_f32(h);
+}
+
 // ---------------------------------------------------------------- accumulate
 __global__ __launch_bounds__(256) void acc_kernel(const uint8_t *__restrict__ q_new,
                                                   uint8_t *__restrict__ q_acc, int rows, int row_bytes,
@@ -165,29 +171,50 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
 // ---------------------------------------------------------------- QSUM form
 // One block per unit: qs[d] = sum over the unit's rows of q_acc[row][d] in
 // fp64, rows split over 8 row phases and combined in fixed order.
+// Summed query rows of one unit (b, KV head): qs[d] = sum over the G * R rows
+// of q_acc[b][h G + i][r][d], in fp64. D / 8 threads per row, 8 channels each
+// (one 16-byte load of 16-bit values), 1024 / (D / 8) row groups striding
+// over the rows; the groups' sums meet in LDS and are added in group order.
 template <int DT>
 __global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_acc, int Hq, int Hkv,
                                                     int R, int D, double *__restrict__ qs) {
-  __shared__ double part[8][128];
+  __shared__ double part[1024 * 8];
   const int unit = blockIdx.x;
   const int G = Hq / Hkv;
   const int b = unit / Hkv;
   const int h = unit % Hkv;
   const int M = G * R;
-  const int d = threadIdx.x % 128;
-  const int ph = threadIdx.x / 128;
+  const int lpr = D / 8;                       // threads per row
+  const int ng = 1024 / lpr;                   // row groups
+  const int sub = threadIdx.x % lpr;
+  const int rg = threadIdx.x / lpr;
   const int64_t base = (static_cast<int64_t>(b) * Hq + h * G) * R * D;
-  double s = 0.0;
-  if (d < D) {
-    for (int r = ph; r < M; r += 8) s += static_cast<double>(load_as_f32<DT>(q_acc, base + static_cast<int64_t>(r) * D + d));
-  }
-  part[ph][d] = s;
-  __syncthreads();
-  if (ph == 0 && d < D) {
-    double t = 0.0;
+  double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int r = rg; r < M; r += ng) {
+    const int64_t off = base + static_cast<int64_t>(r) * D + sub * 8;
+    if constexpr (DT == HQ_F32) {
+      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q_acc) + off);
+      const float4 x0 = p[0], x1 = p[1];
+      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-    for (int p = 0; p < 8; ++p) t += part[p][d];
-    qs[static_cast<int64_t>(unit) * D + d] = t;
+      for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(v[e]);
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q_acc) + off);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[2 * e] += static_cast<double>(load_half<DT>(w[e] & 0xFFFFu));
+        s[2 * e + 1] += static_cast<double>(load_half<DT>(w[e] >> 16));
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg * D + sub * 8 + e] = s[e];
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < D) {
+    double t = 0.0;
+    for (int g2 = 0; g2 < ng; ++g2) t += part[g2 * D + threadIdx.x];
+    qs[static_cast<int64_t>(unit) * D + threadIdx.x] = t;
   }
 }
 
@@ -517,6 +544,50 @@ DetWs det_ws(int B, int Hkv, int64_t cand_end) {
   return L;
 }
 
+// Scores from the INT4 cache: c_j = qsum . k_hat_j with k_hat = s c + z
+// (fp16 s and z per 32-channel group, codes in the row layout). As in
+// gemv_kernel, D / 8 lanes per key row, 8 channels each (4 code bytes and the
+// group's {s, z} word): 80 bytes per key at D = 128 instead of 256. Every
+// product and sum is in fp64, where s c + z is exact.
+template <int D>
+__global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restrict__ codes,
+                                                        const uint32_t *__restrict__ sz,
+                                                        const double *__restrict__ qs, int64_t t_cap,
+                                                        int64_t cand_end, int chunks_per_unit,
+                                                        int64_t *__restrict__ scores) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  constexpr int CHUNK = 256;
+  const int unit = blockIdx.x / chunks_per_unit;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x % chunks_per_unit) * CHUNK;
+  const int sub = threadIdx.x % LPR;
+  const int rowi = threadIdx.x / LPR;
+  const int g = sub / 4;                    // the lane's 32-channel group
+  double qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = qs[static_cast<int64_t>(unit) * D + sub * 8 + e];
+  for (int64_t r = r0 + rowi; r < r0 + CHUNK; r += RPB) {
+    const bool ok = r < cand_end;
+    double acc = 0.0;
+    if (ok) {
+      const int64_t row = static_cast<int64_t>(unit) * t_cap + r;
+      const uint32_t cw = reinterpret_cast<const uint32_t *>(codes + row * (D / 2))[sub];
+      const uint32_t w = sz[row * (D / 32) + g];
+      const double s = static_cast<double>(f16_to_f32(w & 0xFFFFu));
+      const double z = static_cast<double>(f16_to_f32(w >> 16));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double kh = s * static_cast<double>((cw >> (4 * e)) & 0xFu) + z;
+        acc = fma(qv[e], kh, acc);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (ok && sub == 0)
+      scores[static_cast<int64_t>(unit) * cand_end + r] = __double2ll_rn(acc * 65536.0);
+  }
+}
+
 }  // namespace
 }  // namespace hq
 
@@ -620,6 +691,85 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
     else
       hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
     hq_status s = check_launch("hq_detect_vlines (top-k)");
+    if (s != HQ_OK) return s;
+  }
+  if (ran) *ran = 1;
+  clear_error();
+  return HQ_OK;
+}
+
+extern "C" hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_dtype dtype, int Hq, int R,
+                                            int64_t step, int force, const hq_hybrid_kv *kv,
+                                            int64_t cand_end, int k_top, int32_t *idx_out,
+                                            int64_t *score_out, int *ran, void *ws, size_t ws_bytes,
+                                            void *stream) {
+  if (ran) *ran = 0;
+  if (!kv) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: null descriptor");
+  const int B = kv->B, Hkv = kv->Hkv, D = kv->D;
+  if (!dtype_ok(dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: bad dtype");
+  if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv)
+    return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: bad head counts");
+  if (D != 64 && D != 128) return fail(HQ_ERR_UNSUPPORTED, "hq_detect_vlines_cache: D must be 64 or 128");
+  if (kv->group != 32) return fail(HQ_ERR_UNSUPPORTED, "hq_detect_vlines_cache: group must be 32");
+  if (R < 1 || R > 1024) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: need 1 <= R <= 1024");
+  if (step < 0) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: step < 0");
+  if (k_top < 0 || cand_end < k_top || cand_end > kv->t_cap || cand_end > kv->T)
+    return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: need 0 <= k_top <= cand_end <= min(t_cap, T)");
+  if (cand_end > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_detect_vlines_cache: cand_end too large");
+  if (!q_acc) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: null q_acc");
+  const int eb = dtype_bytes(dtype);
+  const int slot = static_cast<int>(step % R);
+  hipStream_t st = as_stream(stream);
+  const bool detect = force || slot == R - 1;
+  const DetWs L = det_ws(B, Hkv, cand_end);
+  if (detect) {
+    if (!kv->k_codes || !kv->k_sz || (k_top > 0 && !idx_out))
+      return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: null INT4 key plane or idx_out");
+    if (!ws || ws_bytes < L.total)
+      return fail(HQ_ERR_WORKSPACE, "hq_detect_vlines_cache: workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+    if (reinterpret_cast<uintptr_t>(kv->k_codes) % 16 || reinterpret_cast<uintptr_t>(kv->k_sz) % 4 ||
+        reinterpret_cast<uintptr_t>(q_acc) % 16)
+      return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: misaligned k planes or q_acc");
+  }
+  if (q_new) {
+    if (reinterpret_cast<uintptr_t>(q_new) % 16)
+      return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_cache: q_new must be 16-byte aligned");
+    const int rows = B * Hq;
+    const int row_bytes = D * eb;
+    const int64_t threads = static_cast<int64_t>(rows) * (row_bytes / 16);
+    hipLaunchKernelGGL(acc_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(q_new), static_cast<uint8_t *>(q_acc), rows, row_bytes, R,
+                       slot);
+    hq_status s = check_launch("hq_detect_vlines_cache (accumulate)");
+    if (s != HQ_OK) return s;
+  }
+  if (!detect) { clear_error(); return HQ_OK; }
+  int64_t *scores = score_out ? score_out : reinterpret_cast<int64_t *>(static_cast<uint8_t *>(ws) + L.scores);
+  const int units = B * Hkv;
+  if (cand_end > 0) {
+    double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
+    switch (dtype) {
+      case HQ_F32: hipLaunchKernelGGL(qsum_kernel<HQ_F32>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+      case HQ_BF16: hipLaunchKernelGGL(qsum_kernel<HQ_BF16>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+      default: hipLaunchKernelGGL(qsum_kernel<HQ_F16>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+    }
+    const int cpu = static_cast<int>((cand_end + 255) / 256);
+    const dim3 grid(static_cast<unsigned>(units * cpu));
+    const uint32_t *szw = reinterpret_cast<const uint32_t *>(kv->k_sz);
+    if (D == 128)
+      hipLaunchKernelGGL((gemv_int4_kernel<128>), grid, dim3(256), 0, st, kv->k_codes, szw, qs, kv->t_cap, cand_end, cpu, scores);
+    else
+      hipLaunchKernelGGL((gemv_int4_kernel<64>), grid, dim3(256), 0, st, kv->k_codes, szw, qs, kv->t_cap, cand_end, cpu, scores);
+    hq_status s = check_launch("hq_detect_vlines_cache (scores)");
+    if (s != HQ_OK) return s;
+  }
+  if (k_top > 0) {
+    uint32_t *gkeys = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + L.keys);
+    if (cand_end <= kLdsKeys)
+      hipLaunchKernelGGL((topk_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    else
+      hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    hq_status s = check_launch("hq_detect_vlines_cache (top-k)");
     if (s != HQ_OK) return s;
   }
   if (ran) *ran = 1;

@@ -212,6 +212,28 @@ hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype dtype, int B
                            hq_detect_method method, int32_t *idx_out, int64_t *score_out,
                            int *ran, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * hq_detect_vlines_cache -- the detector scored from the INT4 key cache
+ * instead of the 16-bit keys (a detector variant: the same column scores of
+ * summed queries, over the dequantized keys k_hat = c * s + z that the decode
+ * already holds, 80 bytes per key at D = 128 instead of 256). Accumulate and
+ * cadence exactly as hq_detect_vlines; on detection, for every (b, h):
+ *   c_j = (sum over r < R and the group's query heads of q_acc[b][i][r]) .
+ *         k_hat[b][h][j], j in [0, cand_end),
+ * the query sum and every product and sum in fp64 (exact when the queries
+ * are multiples of 2^-4 and the partial sums stay within 2^53 units of their
+ * quantum), then top-k as hq_detect_vlines; score_out in units of 2^-16
+ * rounded to nearest even. B, Hkv, D, t_cap and the key planes (k_codes in
+ * HQ_LAYOUT_ROWS, k_sz) come from kv; cand_end <= min(kv->t_cap, kv->T).
+ * Requires ws_bytes >= hq_detect_workspace_size(kv->B, kv->Hkv, cand_end,
+ * k_top); errors as hq_detect_vlines, nothing enqueued on error.
+ */
+hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_dtype dtype, int Hq, int R,
+                                 int64_t step, int force, const hq_hybrid_kv *kv,
+                                 int64_t cand_end, int k_top, int32_t *idx_out,
+                                 int64_t *score_out, int *ran, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 size_t hq_detect_workspace_size(int B, int Hkv, int64_t cand_end, int k_top);
 
 /*

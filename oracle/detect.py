@@ -24,6 +24,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import quant
+
 SCORE_FRAC_BITS = 16
 
 
@@ -88,4 +90,51 @@ def detect(q_acc: np.ndarray, K: np.ndarray, cand_end: int, k: int, require_exac
                 if not (on_grid(rows) and on_grid(Kh) and exact_bound_ok(rows, Kh)):
                     raise ValueError("exact scores need grid inputs within the magnitude bound")
             idx[b, h], sc[b, h] = detect_head(rows, Kh, cand_end, k)
+    return idx, sc
+
+
+def cache_scores(q_rows: np.ndarray, k_packed: np.ndarray, k_sz: np.ndarray, group: int = 32):
+    """Detector variant scored from the INT4 key cache: c_j = (sum_rows q) .
+    k_hat_j, k_hat = c * s + z. Exact integer arithmetic: the summed query in
+    units of 2**-4 (every q must be a multiple of 2**-4) and k_hat in units of
+    2**-24 (fp16 s and z are multiples of 2**-24), so c_j is an integer in
+    units of 2**-28. Returns (int64 units of 2**-16 rounded half to even,
+    ok) where ok says every |partial sum| stays below 2**53 units, the
+    condition under which a float64 evaluation in any order is exact."""
+    Q = np.asarray(q_rows, dtype=np.float64)
+    if not on_grid(Q):
+        raise ValueError("exact cache scores need queries on the 2**-4 grid")
+    qs = np.rint(Q * 16.0).astype(np.int64).sum(axis=0)                 # [D], units 2**-4
+    codes = quant.unpack_nibbles(k_packed).astype(np.int64)              # [n][D]
+    s, z = quant.split_scale_zero(k_sz)                                  # [n][D/group] fp16
+    s24 = np.rint(s.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    z24 = np.rint(z.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    kh = codes * np.repeat(s24, group, axis=1) + np.repeat(z24, group, axis=1)   # units 2**-24
+    terms_abs = np.abs(kh) @ np.abs(qs)
+    ok = bool(terms_abs.max(initial=0) < 2 ** 53)
+    x = kh @ qs                                                          # units 2**-28
+    # to units of 2**-16: divide by 2**12, round half to even
+    qd, r = np.divmod(x, 4096)
+    up = (r > 2048) | ((r == 2048) & (qd % 2 == 1))
+    return (qd + up).astype(np.int64), ok
+
+
+def detect_cache(q_acc: np.ndarray, k_packed: np.ndarray, k_sz: np.ndarray, cand_end: int, k: int,
+                 require_exact: bool = True):
+    """The detector scored from the INT4 key cache. q_acc [B][Hq][R][D];
+    k_packed [B][Hkv][>=cand_end][D/2]; k_sz [B][Hkv][>=cand_end][D/32][2].
+    Returns (idx int32 [B][Hkv][k], scores int64 [B][Hkv][cand_end])."""
+    B, Hq, R, D = q_acc.shape
+    Hkv = k_packed.shape[1]
+    G = Hq // Hkv
+    idx = np.empty((B, Hkv, k), dtype=np.int32)
+    sc = np.empty((B, Hkv, cand_end), dtype=np.int64)
+    for b in range(B):
+        for h in range(Hkv):
+            rows = q_acc[b, h * G:(h + 1) * G].reshape(G * R, D)
+            units, ok = cache_scores(rows, k_packed[b, h, :cand_end], k_sz[b, h, :cand_end])
+            if require_exact and not ok:
+                raise ValueError("cache scores exceed the exact float64 range")
+            sc[b, h] = units
+            idx[b, h] = top_k(units, k)
     return idx, sc

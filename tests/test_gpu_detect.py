@@ -9,7 +9,7 @@ import torch
 
 import hybrid_precision_quantized_amd as hq
 import synth
-from oracle import detect
+from oracle import detect, quant
 from tests.gpu_util import TORCH_DT, say, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -95,3 +95,68 @@ def test_detect_full_workload(name, method):
     got_idx, got_sc = _run(q, K, ce, w.k, method, w.dtype)
     assert np.array_equal(got_sc, want_sc)
     assert np.array_equal(got_idx, want_idx)
+
+
+def _run_cache(q_acc, K, cand_end, k_top, dtype, T, W):
+    """hq_detect_vlines_cache over a cache whose INT4 planes were written by
+    hq_quantize_kv from K (positions [0, T - W))."""
+    B, Hq, R, D = q_acc.shape
+    Hkv = K.shape[1]
+    dt = TORCH_DT[dtype]
+    kd = to_dev(K, dtype)
+    cache = hq.HybridCache(B, Hkv, D, T, W, 0, dt)
+    cache.quantize(kd, kd)
+    kv = cache.descriptor()
+    qd = to_dev(q_acc, dtype)
+    idx = torch.full((B, Hkv, max(k_top, 1)), -1, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, Hkv, max(cand_end, 1)), dtype=torch.int64, device="cuda")
+    ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, cand_end, k_top), dtype=torch.uint8, device="cuda")
+    ran = hq.hq_detect_vlines_cache(None, qd, Hq, R, 0, True, kv, cand_end, k_top, idx, sc, ws)
+    torch.cuda.synchronize()
+    assert ran
+    return idx.cpu().numpy()[..., :k_top], sc.cpu().numpy()[..., :cand_end]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,R,T,W,k_top,dtype,spread", [
+    (2, 8, 2, 128, 64, 3000, 100, 145, "bf16", 3.0),
+    (1, 6, 2, 64, 33, 777, 77, 35, "bf16", 1.0),
+    (1, 8, 1, 128, 64, 2048, 128, 1920, "f16", 1.0),     # k_top == cand_end
+    (1, 8, 2, 128, 16, 40128, 128, 2000, "bf16", 2.0),   # keys beyond the LDS-resident size
+    (1, 4, 1, 128, 2, 5000, 100, 3000, "bf16", 0.0625),  # many equal scores
+])
+def test_detect_cache_small(B, Hq, Hkv, D, R, T, W, k_top, dtype, spread):
+    """Scores from the INT4 key cache: bit-exact int64 scores and index sets
+    against the oracle's exact integer evaluation."""
+    say(f"detect cache B={B} Hq={Hq} Hkv={Hkv} D={D} R={R} T={T} W={W} k={k_top} {dtype}")
+    rng = np.random.default_rng(T + R)
+    q = np.rint(rng.standard_normal((B, Hq, R, D)) * spread * 16) / 16
+    K = rng.standard_normal((B, Hkv, T, D)) * spread
+    if dtype == "bf16":
+        q, K = synth.round_dtype(q, "bf16"), synth.round_dtype(K, "bf16")
+    else:
+        q = q.astype(np.float16).astype(np.float32)
+        K = K.astype(np.float16).astype(np.float32)
+    ce = T - W
+    kp, ks = quant.quantize_rows(K[:, :, :ce])
+    want_idx, want_sc = detect.detect_cache(q, kp, ks, ce, k_top)
+    got_idx, got_sc = _run_cache(q, K, ce, k_top, dtype, T, W)
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+
+
+@pytest.mark.parametrize("name", ["glm32k", "llama32k"])
+def test_detect_cache_full_workload(name):
+    w = synth.WORKLOADS[name]
+    say(f"detect cache full workload {name}")
+    K = synth.all_keys(w)
+    q = synth.all_query_histories(w)
+    ce = w.T - w.W
+    kp, ks = quant.quantize_rows(K[:, :, :ce])
+    want_idx, want_sc = detect.detect_cache(q, kp, ks, ce, w.k)
+    got_idx, got_sc = _run_cache(q, K, ce, w.k, w.dtype, w.T, w.W)
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+    # how many of the 16-bit detector's lines the cache form keeps
+    idx16, _ = detect.detect(q, K, ce, w.k)
+    overlap = np.mean([len(np.intersect1d(got_idx[0, h], idx16[0, h])) / w.k for h in range(w.Hkv)])
+    say(f"   overlap with the 16-bit detector's set: {overlap:.3f}")

@@ -108,3 +108,45 @@ def test_rejects_non_grid_in_exact_mode():
         detect.detect(q, K, 8, 2)
     idx, _ = detect.detect(q, K, 8, 2, require_exact=False)
     assert idx.tolist() == [[[0, 1]]]
+
+
+def test_cache_scores_brute_force_fractions():
+    """The INT4-cache scores against exact rationals: sum over rows and
+    channels of q * (c * s + z), rounded to units of 2**-16 half to even."""
+    from oracle import quant
+    rng = np.random.default_rng(31)
+    Q = _grid(rng, (5, 64))
+    K = rng.standard_normal((9, 64)).astype(np.float32) * 3
+    kp, ks = quant.quantize_rows(K)
+    units, ok = detect.cache_scores(Q, kp, ks)
+    assert ok
+    codes = quant.unpack_nibbles(kp)
+    s, z = quant.split_scale_zero(ks)
+    for j in range(9):
+        c = Fraction(0)
+        for d in range(64):
+            kh = Fraction(int(codes[j, d])) * Fraction(float(s[j, d // 32])) + Fraction(float(z[j, d // 32]))
+            c += sum(Fraction(float(Q[r, d])) for r in range(5)) * kh
+        x = c * (1 << 16)
+        fl = x.numerator // x.denominator
+        rem = x - fl
+        want = fl + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1) else 0)
+        assert int(units[j]) == want
+
+
+def test_cache_scores_equal_fp64_scores_of_dequantized_keys():
+    """On grid queries the exact cache scores equal the float64 column scores
+    of the dequantized rows (a different route: matmul then column sums)."""
+    from oracle import quant
+    rng = np.random.default_rng(32)
+    Q = _grid(rng, (64, 128), scale=1.0)
+    K = (rng.standard_normal((500, 128)) * np.where(rng.random(128) < 0.03, 10, 1)).astype(np.float32)
+    kp, ks = quant.quantize_rows(K)
+    units, ok = detect.cache_scores(Q, kp, ks)
+    assert ok
+    ref = detect.to_units(detect.column_scores(Q, quant.dequantize_rows(kp, ks)))
+    assert np.array_equal(units, ref)
+    idx, _ = detect.detect_cache(Q[None, None], kp[None, None], ks[None, None], 500, 25)
+    assert np.array_equal(idx[0, 0], detect.top_k(ref, 25))
+    with pytest.raises(ValueError):
+        detect.cache_scores(Q + 1e-3, kp, ks)
