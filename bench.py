@@ -52,9 +52,10 @@ def parse():
                     choices=["llama32k", "qwen128k", "glm32k", "prefill32k"],
                     help="decode workloads, or prefill32k: the causal hybrid prefill of a 32K prompt")
     ap.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0 = auto, >= 1 GB)")
-    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum", "cache"],
+    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum", "cache", "mass"],
                     help="matmul: Q_acc K^T on MFMA; qsum: summed queries, GEMV; cache: summed "
-                         "queries against the INT4 key cache (hq_detect_vlines_cache)")
+                         "queries against the INT4 key cache (hq_detect_vlines_cache); mass: "
+                         "attention-mass scores (hq_detect_vlines_mass)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,6 +107,7 @@ def main():
     nq = T - W
     method = hq.HQ_DETECT_MATMUL if args.detect_method == "matmul" else hq.HQ_DETECT_QSUM
     from_cache = args.detect_method == "cache"
+    by_mass = args.detect_method == "mass"
 
     # ------------------------------------------------------------ inputs
     t_setup = time.time()
@@ -127,7 +129,8 @@ def main():
     copies = args.copies or max(1, int(np.ceil(1.2e9 / layer_bytes)))
     caches, Ks, Vs, qaccs = [], [], [], []
     idx_new = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
-    det_ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, nq, k), dtype=torch.uint8, device=dev)
+    det_ws = torch.zeros(hq.hq_detect_mass_workspace_size(B, Hq, Hkv, R, T, nq) if by_mass
+                         else hq.hq_detect_workspace_size(B, Hkv, nq, k), dtype=torch.uint8, device=dev)
     for c in range(copies):
         Kc = K0 if c == 0 else K0.clone()
         Vc = V0 if c == 0 else V0.clone()
@@ -137,6 +140,8 @@ def main():
         cache.quantize(Kc, Vc)
         if from_cache:
             hq.hq_detect_vlines_cache(None, qa, Hq, R, 0, True, cache.descriptor(), nq, k, idx_new, None, det_ws)
+        elif by_mass:
+            hq.hq_detect_vlines_mass(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, idx_new, None, det_ws)
         else:
             hq.hq_detect_vlines(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method, idx_new, None,
                                 det_ws)
@@ -160,6 +165,9 @@ def main():
         if from_cache:
             return hq.hq_detect_vlines_cache(q_new, qaccs[c], Hq, R, s, force, descs[c], nq, k, idx_new, None,
                                              det_ws)
+        if by_mass:
+            return hq.hq_detect_vlines_mass(q_new, qaccs[c], B, Hq, Hkv, D, R, s, force, Ks[c], T, nq, k,
+                                            idx_new, None, det_ws)
         return hq.hq_detect_vlines(q_new, qaccs[c], B, Hq, Hkv, D, R, s, force, Ks[c], T, nq, k, method,
                                    idx_new, None, det_ws)
 

@@ -75,6 +75,14 @@ _SIGS = {
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int),
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "hq_detect_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
+    "hq_detect_vlines_mass": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.POINTER(ctypes.c_int), ctypes.c_void_p,
+                                             ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_detect_mass_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_int64, ctypes.c_int64]),
     "hq_decode_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -216,6 +224,23 @@ def hq_detect_vlines_cache(q_new, q_acc, Hq, R, step, force, kv: HybridKV, cand_
     _check(lib().hq_detect_vlines_cache(_ptr(q_new), _ptr(q_acc), _dt(q_acc), Hq, R, step, int(force),
                                         ctypes.byref(kv), cand_end, k_top, _ptr(idx_out), _ptr(score_out),
                                         ctypes.byref(ran), _ptr(ws), ws_bytes, _stream(stream)))
+    return bool(ran.value)
+
+
+def hq_detect_mass_workspace_size(B, Hq, Hkv, R, k_rows, cand_end) -> int:
+    return int(lib().hq_detect_mass_workspace_size(B, Hq, Hkv, R, k_rows, cand_end))
+
+
+def hq_detect_vlines_mass(q_new, q_acc, B, Hq, Hkv, D, R, step, force, k, k_rows, cand_end, k_top,
+                          idx_out, score_out=None, ws=None, sm_scale=0.0, stream=None) -> bool:
+    """The detector scored by attention mass (see include/hq.h). Returns True
+    if detection was enqueued."""
+    ran = ctypes.c_int(0)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hq_detect_vlines_mass(_ptr(q_new), _ptr(q_acc), _dt(q_acc), B, Hq, Hkv, D, R, step,
+                                       int(force), _ptr(k), k_rows, cand_end, k_top, float(sm_scale),
+                                       _ptr(idx_out), _ptr(score_out), ctypes.byref(ran), _ptr(ws),
+                                       ws_bytes, _stream(stream)))
     return bool(ran.value)
 
 

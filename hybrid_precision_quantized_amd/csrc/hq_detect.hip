@@ -588,6 +588,205 @@ __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restric
   }
 }
 
+// ---------------------------------------------------------------- attention-mass form
+// Scores c_j = sum over the unit's query rows rho of softmax_rho(l)_j, the
+// attention probability row rho gives key j, l = sm_scale q_rho . k over all
+// k_rows keys. Three kernels, each on the column-sum layout above (4 waves,
+// two 32-key tiles per wave with their K fragments in registers, the query
+// rows staged through LDS 128 at a time):
+//  1. mass_stats: per (row, block) partial max (raw logit units) and sum of
+//     2^(cs (l - m)) over the block's 256 keys, from S^T = K Q^T (lane = row,
+//     registers = keys);
+//  2. mass_merge: per row, the partials merged into cs * m and 1 / L;
+//  3. mass_cols: per candidate key, sum over rows of 2^(cs l - cs m) / L
+//     from S = Q K^T (lane = key, registers = rows), in a fixed order.
+// The exponentials make these scores approximate (fp32), not exact.
+constexpr float kNegInfF = -__builtin_huge_valf();
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void mass_stats_kernel(const uint16_t *__restrict__ q_acc,
+                                                         const uint16_t *__restrict__ k, int Hq, int Hkv,
+                                                         int R, int64_t k_rows, int blocks_per_unit,
+                                                         float cs, float2 *__restrict__ part) {
+  constexpr int KC = D / 16, ROWV = D / 8, PER_T = kStageRows * ROWV / 256;
+  __shared__ uint16_t qs[kStageRows][D + kRowPad];
+  __shared__ float2 wpart[4][kStageRows];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int unit = blockIdx.x / blocks_per_unit;
+  const int cb = blockIdx.x % blocks_per_unit;
+  const int G = Hq / Hkv, b = unit / Hkv, h = unit % Hkv, M = G * R;
+  const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
+  uint4 kf[2][KC];
+  int64_t key0[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    key0[t] = (static_cast<int64_t>(cb) * 8 + wave * 2 + t) * 32;     // first key of the tile
+    const int64_t kr = key0[t] + (lane & 31);
+    const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (kr < k_rows ? kr : 0)) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      kf[t][kc] = kr < k_rows ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8)
+                              : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int stages = (M + kStageRows - 1) / kStageRows;
+  for (int st = 0; st < stages; ++st) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      const int grow = st * kStageRows + row;
+      *reinterpret_cast<uint4 *>(&qs[row][c8 * 8]) =
+          grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
+                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < kStageRows / 32; ++sub) {
+      const uint16_t *qrow = &qs[sub * 32 + (lane & 31)][half * 8];
+      float m = kNegInfF, l = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          acc = mfma32<DT>(kf[t][kc], *reinterpret_cast<const uint4 *>(qrow + kc * 16), acc);
+        // lane: row sub * 32 + lane % 32; register r: key key0 + 8 (r / 4) + 4 half + r % 4
+        float tm = kNegInfF;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = key0[t] + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= k_rows) acc[r] = kNegInfF;
+          tm = fmaxf(tm, acc[r]);
+        }
+        const float mn = fmaxf(m, tm);
+        if (mn != kNegInfF) {
+          float sum = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f((acc[r] - mn) * cs);
+          l = l * __builtin_amdgcn_exp2f((m - mn) * cs) + sum;
+          m = mn;
+        }
+      }
+      // the two halves hold the same row (the other 16 keys of each tile)
+      const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+      const float mm = fmaxf(m, mo);
+      const float ll = mm == kNegInfF ? 0.f
+                                      : l * __builtin_amdgcn_exp2f((m - mm) * cs) +
+                                            lo * __builtin_amdgcn_exp2f((mo - mm) * cs);
+      if (half == 0) wpart[wave][sub * 32 + lane] = make_float2(mm, ll);
+    }
+    __syncthreads();
+    // merge the 4 waves (fixed order) and write this block's partial per row
+    if (threadIdx.x < kStageRows) {
+      const int row = st * kStageRows + threadIdx.x;
+      float mm = kNegInfF;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mm = fmaxf(mm, wpart[w][threadIdx.x].x);
+      float ll = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float2 v = wpart[w][threadIdx.x];
+        if (v.x != kNegInfF) ll += v.y * __builtin_amdgcn_exp2f((v.x - mm) * cs);
+      }
+      if (row < M) part[(static_cast<int64_t>(unit) * M + row) * blocks_per_unit + cb] = make_float2(mm, ll);
+    }
+    __syncthreads();
+  }
+}
+
+// per (unit, row): stats = (cs * m, 1 / L) of the row's softmax over all keys;
+// the logits above are raw q . k, so cs = sm_scale * log2(e)
+__global__ __launch_bounds__(256) void mass_merge_kernel(const float2 *__restrict__ part, int rows_total,
+                                                         int nblk, float cs, float2 *__restrict__ stats) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows_total) return;
+  const float2 *p = part + static_cast<int64_t>(r) * nblk;
+  float mm = kNegInfF;
+  for (int i = 0; i < nblk; ++i) mm = fmaxf(mm, p[i].x);
+  double L = 0.0;
+  for (int i = 0; i < nblk; ++i)
+    if (p[i].x != kNegInfF) L += static_cast<double>(p[i].y) * exp2(static_cast<double>(cs) * (p[i].x - mm));
+  stats[r] = make_float2(cs * mm, L > 0.0 ? static_cast<float>(1.0 / L) : 0.f);
+}
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void mass_cols_kernel(const uint16_t *__restrict__ q_acc,
+                                                        const uint16_t *__restrict__ k, int Hq, int Hkv, int R,
+                                                        int64_t k_rows, int64_t cand_end, int blocks_per_unit,
+                                                        float cs, const float2 *__restrict__ stats,
+                                                        int64_t *__restrict__ scores) {
+  constexpr int KC = D / 16, ROWV = D / 8, PER_T = kStageRows * ROWV / 256;
+  __shared__ uint16_t qs[kStageRows][D + kRowPad];
+  __shared__ float2 rs[kStageRows];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int unit = blockIdx.x / blocks_per_unit;
+  const int cb = blockIdx.x % blocks_per_unit;
+  const int G = Hq / Hkv, b = unit / Hkv, h = unit % Hkv, M = G * R;
+  const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
+  uint4 kf[2][KC];
+  int64_t col[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    col[t] = (static_cast<int64_t>(cb) * 8 + wave * 2 + t) * 32 + (lane & 31);
+    const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col[t] < cand_end ? col[t] : 0)) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      kf[t][kc] = col[t] < cand_end ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float cols[2] = {0.f, 0.f};
+  const int stages = (M + kStageRows - 1) / kStageRows;
+  for (int st = 0; st < stages; ++st) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      const int grow = st * kStageRows + row;
+      *reinterpret_cast<uint4 *>(&qs[row][c8 * 8]) =
+          grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
+                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (threadIdx.x < kStageRows) {
+      const int grow = st * kStageRows + threadIdx.x;
+      rs[threadIdx.x] = grow < M ? stats[static_cast<int64_t>(unit) * M + grow] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < kStageRows / 32; ++sub) {
+      const uint16_t *arow = &qs[sub * 32 + (lane & 31)][half * 8];
+      f32x16 acc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * 16);
+        acc[0] = mfma32<DT>(a, kf[0][kc], acc[0]);
+        acc[1] = mfma32<DT>(a, kf[1][kc], acc[1]);
+      }
+      // lane: key col; register r: row sub * 32 + 8 (r / 4) + 4 half + r % 4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float2 st2 = rs[sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          cols[t] += __builtin_amdgcn_exp2f(fmaf(acc[t][r], cs, -st2.x)) * st2.y;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float c = cols[t] + __shfl_xor(cols[t], 32, 64);
+    if (half == 0 && col[t] < cand_end)
+      scores[static_cast<int64_t>(unit) * cand_end + col[t]] =
+          __double2ll_rn(static_cast<double>(c) * 1099511627776.0);   // units of 2^-40
+  }
+}
+
 }  // namespace
 }  // namespace hq
 
@@ -770,6 +969,118 @@ extern "C" hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_d
     else
       hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
     hq_status s = check_launch("hq_detect_vlines_cache (top-k)");
+    if (s != HQ_OK) return s;
+  }
+  if (ran) *ran = 1;
+  clear_error();
+  return HQ_OK;
+}
+
+namespace hq {
+namespace {
+struct MassWs {
+  size_t scores, part, stats, keys, total;
+  int nblk;
+};
+MassWs mass_ws(int B, int Hq, int Hkv, int R, int64_t k_rows, int64_t cand_end) {
+  MassWs L{};
+  const int64_t units = static_cast<int64_t>(B) * Hkv;
+  const int64_t M = static_cast<int64_t>(Hq / Hkv) * R;
+  L.nblk = static_cast<int>((k_rows + 255) / 256);
+  L.scores = 0;
+  L.part = align_up(static_cast<size_t>(units) * cand_end * sizeof(int64_t), 256);
+  L.stats = align_up(L.part + static_cast<size_t>(units) * M * L.nblk * sizeof(float2), 256);
+  L.keys = align_up(L.stats + static_cast<size_t>(units) * M * sizeof(float2), 256);
+  L.total = L.keys + (cand_end > kLdsKeys ? static_cast<size_t>(units) * cand_end * 4 : 0);
+  return L;
+}
+}  // namespace
+}  // namespace hq
+
+extern "C" size_t hq_detect_mass_workspace_size(int B, int Hq, int Hkv, int R, int64_t k_rows,
+                                                int64_t cand_end) {
+  if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv || R < 1 || k_rows < 1 || cand_end < 0) return 0;
+  return mass_ws(B, Hq, Hkv, R, k_rows, cand_end).total;
+}
+
+extern "C" hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dtype dtype, int B, int Hq,
+                                           int Hkv, int D, int R, int64_t step, int force, const void *k,
+                                           int64_t k_rows, int64_t cand_end, int k_top, float sm_scale,
+                                           int32_t *idx_out, int64_t *score_out, int *ran, void *ws,
+                                           size_t ws_bytes, void *stream) {
+  if (ran) *ran = 0;
+  if (dtype != HQ_BF16 && dtype != HQ_F16)
+    return fail(HQ_ERR_UNSUPPORTED, "hq_detect_vlines_mass: dtype must be HQ_BF16 or HQ_F16");
+  if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: bad head counts");
+  if (D != 64 && D != 128) return fail(HQ_ERR_UNSUPPORTED, "hq_detect_vlines_mass: D must be 64 or 128");
+  if (R < 1 || R > 1024) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: need 1 <= R <= 1024");
+  if (step < 0) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: step < 0");
+  if (k_top < 0 || cand_end < k_top || k_rows < cand_end || k_rows < 1)
+    return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: need 0 <= k_top <= cand_end <= k_rows, k_rows >= 1");
+  if (k_rows > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_detect_vlines_mass: k_rows too large");
+  if (!q_acc) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: null q_acc");
+  const int eb = dtype_bytes(dtype);
+  const int slot = static_cast<int>(step % R);
+  hipStream_t st = as_stream(stream);
+  const bool detect = force || slot == R - 1;
+  const MassWs L = mass_ws(B, Hq, Hkv, R, k_rows, cand_end);
+  if (detect) {
+    if (!k || (k_top > 0 && !idx_out)) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: null k or idx_out");
+    if (!ws || ws_bytes < L.total)
+      return fail(HQ_ERR_WORKSPACE, "hq_detect_vlines_mass: workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+    if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(q_acc) % 16)
+      return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: k and q_acc must be 16-byte aligned");
+  }
+  if (q_new) {
+    if (reinterpret_cast<uintptr_t>(q_new) % 16)
+      return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines_mass: q_new must be 16-byte aligned");
+    const int rows = B * Hq;
+    const int row_bytes = D * eb;
+    const int64_t threads = static_cast<int64_t>(rows) * (row_bytes / 16);
+    hipLaunchKernelGGL(acc_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(q_new), static_cast<uint8_t *>(q_acc), rows, row_bytes, R,
+                       slot);
+    hq_status s = check_launch("hq_detect_vlines_mass (accumulate)");
+    if (s != HQ_OK) return s;
+  }
+  if (!detect) { clear_error(); return HQ_OK; }
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  int64_t *scores = score_out ? score_out : reinterpret_cast<int64_t *>(w8 + L.scores);
+  float2 *part = reinterpret_cast<float2 *>(w8 + L.part);
+  float2 *stats = reinterpret_cast<float2 *>(w8 + L.stats);
+  const int units = B * Hkv;
+  const int M = (Hq / Hkv) * R;
+  const float cs = (sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(D))) * 1.4426950408889634f;
+  const uint16_t *qa = static_cast<const uint16_t *>(q_acc);
+  const uint16_t *kk = static_cast<const uint16_t *>(k);
+  if (cand_end > 0) {
+    const int nb1 = L.nblk;
+    const int nb3 = static_cast<int>((cand_end + 255) / 256);
+#define HQ_MASS(DD, TT)                                                                                  \
+  do {                                                                                                   \
+    hipLaunchKernelGGL((mass_stats_kernel<DD, TT>), dim3(units * nb1), dim3(256), 0, st, qa, kk, Hq, Hkv, \
+                       R, k_rows, nb1, cs, part);                                                        \
+    hipLaunchKernelGGL(mass_merge_kernel, dim3((units * M + 255) / 256), dim3(256), 0, st, part,          \
+                       units * M, nb1, cs, stats);                                                       \
+    hipLaunchKernelGGL((mass_cols_kernel<DD, TT>), dim3(units * nb3), dim3(256), 0, st, qa, kk, Hq, Hkv,  \
+                       R, k_rows, cand_end, nb3, cs, stats, scores);                                      \
+  } while (0)
+    if (D == 128) {
+      if (dtype == HQ_BF16) HQ_MASS(128, HQ_BF16); else HQ_MASS(128, HQ_F16);
+    } else {
+      if (dtype == HQ_BF16) HQ_MASS(64, HQ_BF16); else HQ_MASS(64, HQ_F16);
+    }
+#undef HQ_MASS
+    hq_status s = check_launch("hq_detect_vlines_mass (scores)");
+    if (s != HQ_OK) return s;
+  }
+  if (k_top > 0) {
+    uint32_t *gkeys = reinterpret_cast<uint32_t *>(w8 + L.keys);
+    if (cand_end <= kLdsKeys)
+      hipLaunchKernelGGL((topk_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    else
+      hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    hq_status s = check_launch("hq_detect_vlines_mass (top-k)");
     if (s != HQ_OK) return s;
   }
   if (ran) *ran = 1;

@@ -234,6 +234,32 @@ hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_dtype dtype,
                                  int64_t *score_out, int *ran, void *ws, size_t ws_bytes,
                                  void *stream);
 
+/*
+ * hq_detect_vlines_mass -- the detector scored by attention mass (a detector
+ * variant: the pages measure how much of the attention mass the vertical
+ * lines cover [AFS, What to Watch For: about 5 % of the tokens hold 50-85 %
+ * of it]). Accumulate and cadence exactly as hq_detect_vlines; on detection,
+ * for every (b, h) and every accumulated query row rho of the group:
+ *   p_rho,j = softmax over all k_rows keys of sm_scale q_rho . k_j,
+ *   c_j = sum over rho of p_rho,j for candidates j in [0, cand_end),
+ * then top-k as hq_detect_vlines (ties to the lower position). sm_scale <= 0
+ * means 1/sqrt(D). The logits come from bf16/fp16 MFMA with fp32
+ * accumulation and the exponentials are fp32, so the scores are
+ * approximations of the exact masses (not bit-reproducible against a
+ * reference, but deterministic run to run). score_out (optional) receives
+ * c_j in int64 units of 2^-40. Requires dtype HQ_BF16 or HQ_F16, D in {64,
+ * 128}, 0 <= k_top <= cand_end <= k_rows, 1 <= R <= 1024, ws_bytes >=
+ * hq_detect_mass_workspace_size(B, Hq, Hkv, R, k_rows, cand_end); errors as
+ * hq_detect_vlines, nothing enqueued on error.
+ */
+hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dtype dtype, int B, int Hq,
+                                int Hkv, int D, int R, int64_t step, int force, const void *k,
+                                int64_t k_rows, int64_t cand_end, int k_top, float sm_scale,
+                                int32_t *idx_out, int64_t *score_out, int *ran, void *ws,
+                                size_t ws_bytes, void *stream);
+size_t hq_detect_mass_workspace_size(int B, int Hq, int Hkv, int R, int64_t k_rows,
+                                     int64_t cand_end);
+
 size_t hq_detect_workspace_size(int B, int Hkv, int64_t cand_end, int k_top);
 
 /*

@@ -138,3 +138,34 @@ def detect_cache(q_acc: np.ndarray, k_packed: np.ndarray, k_sz: np.ndarray, cand
             sc[b, h] = units
             idx[b, h] = top_k(units, k)
     return idx, sc
+
+
+def mass_scores(q_rows: np.ndarray, K: np.ndarray, cand_end: int, sm_scale: float | None = None) -> np.ndarray:
+    """Detector variant scored by attention mass ([AFS] "What to Watch For":
+    the vertical lines are the few tokens holding most of the attention
+    mass): p_rho = softmax over all rows of K of sm_scale * q_rho . K^T, and
+    c_j = sum over rho of p_rho,j for j in [0, cand_end). float64 [cand_end]."""
+    Q = np.asarray(q_rows, dtype=np.float64)
+    Kf = np.asarray(K, dtype=np.float64)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(Q.shape[1])
+    L = sm_scale * (Q @ Kf.T)                            # [rows][n]
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    return P[:, :cand_end].sum(axis=0)
+
+
+def detect_mass(q_acc: np.ndarray, K: np.ndarray, cand_end: int, k: int, sm_scale: float | None = None):
+    """q_acc [B][Hq][R][D], K [B][Hkv][k_rows][D] (the softmax runs over all
+    k_rows keys). Returns (idx int32 [B][Hkv][k], scores float64 [B][Hkv][cand_end])."""
+    B, Hq, R, D = q_acc.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    idx = np.empty((B, Hkv, k), dtype=np.int32)
+    sc = np.empty((B, Hkv, cand_end), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            rows = q_acc[b, h * G:(h + 1) * G].reshape(G * R, D)
+            sc[b, h] = mass_scores(rows, K[b, h], cand_end, sm_scale)
+            idx[b, h] = top_k(sc[b, h], k)
+    return idx, sc

@@ -160,3 +160,80 @@ def test_detect_cache_full_workload(name):
     idx16, _ = detect.detect(q, K, ce, w.k)
     overlap = np.mean([len(np.intersect1d(got_idx[0, h], idx16[0, h])) / w.k for h in range(w.Hkv)])
     say(f"   overlap with the 16-bit detector's set: {overlap:.3f}")
+
+
+def _run_mass(q_acc, K, cand_end, k_top, dtype):
+    B, Hq, R, D = q_acc.shape
+    Hkv, k_rows = K.shape[1], K.shape[2]
+    qd = to_dev(q_acc, dtype)
+    kd = to_dev(K, dtype)
+    idx = torch.full((B, Hkv, max(k_top, 1)), -1, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, Hkv, max(cand_end, 1)), dtype=torch.int64, device="cuda")
+    ws = torch.full((hq.hq_detect_mass_workspace_size(B, Hq, Hkv, R, k_rows, cand_end),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
+    ran = hq.hq_detect_vlines_mass(None, qd, B, Hq, Hkv, D, R, 0, True, kd, k_rows, cand_end, k_top,
+                                   idx, sc, ws)
+    torch.cuda.synchronize()
+    assert ran
+    return idx.cpu().numpy()[..., :k_top], sc.cpu().numpy()[..., :cand_end]
+
+
+def _check_mass(got_idx, got_units, want_idx, want_sc, k_top, rel=1e-4):
+    """Scores within rel of the unit's largest oracle score; index sets equal
+    except for positions whose oracle score lies within that tolerance of the
+    k-th largest (near ties the fp32 evaluation may order either way)."""
+    got_sc = got_units.astype(np.float64) / float(1 << 40)
+    B, Hkv, _ = want_sc.shape
+    for b in range(B):
+        for h in range(Hkv):
+            tol = rel * max(float(want_sc[b, h].max()), 1e-30)
+            err = float(np.max(np.abs(got_sc[b, h] - want_sc[b, h])))
+            assert err <= tol, (b, h, err, tol)
+            if k_top == 0:
+                continue
+            tau = np.sort(want_sc[b, h])[::-1][k_top - 1]
+            diff = np.setxor1d(got_idx[b, h], want_idx[b, h])
+            assert np.all(np.abs(want_sc[b, h][diff] - tau) <= 2 * tol), (b, h, diff)
+            assert np.all(np.diff(got_idx[b, h]) > 0)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,R,n,ce,k_top,dtype", [
+    (2, 8, 2, 128, 64, 3000, 2900, 145, "bf16"),
+    (1, 6, 2, 64, 33, 777, 700, 35, "bf16"),
+    (1, 8, 1, 128, 64, 2048, 1920, 1920, "f16"),    # k_top == cand_end
+    (1, 4, 2, 128, 5, 300, 1, 1, "bf16"),           # single candidate, few rows
+])
+def test_detect_mass_small(B, Hq, Hkv, D, R, n, ce, k_top, dtype):
+    """Attention-mass scores against the oracle's float64 softmax masses."""
+    say(f"detect mass B={B} Hq={Hq} Hkv={Hkv} D={D} R={R} n={n} ce={ce} k={k_top} {dtype}")
+    rng = np.random.default_rng(n + 3 * R)
+    q = rng.standard_normal((B, Hq, R, D)) * 2
+    K = rng.standard_normal((B, Hkv, n, D))
+    if dtype == "bf16":
+        q, K = synth.round_dtype(q, "bf16"), synth.round_dtype(K, "bf16")
+    else:
+        q = q.astype(np.float16).astype(np.float32)
+        K = K.astype(np.float16).astype(np.float32)
+    want_idx, want_sc = detect.detect_mass(q, K, ce, k_top)
+    got_idx, got_units = _run_mass(q, K, ce, k_top, dtype)
+    _check_mass(got_idx, got_units, want_idx, want_sc, k_top)
+    again_idx, again_units = _run_mass(q, K, ce, k_top, dtype)
+    assert np.array_equal(again_units, got_units) and np.array_equal(again_idx, got_idx)
+
+
+@pytest.mark.parametrize("name", ["glm32k", "llama32k"])
+def test_detect_mass_full_workload(name):
+    w = synth.WORKLOADS[name]
+    say(f"detect mass full workload {name}")
+    K = synth.all_keys(w)
+    q = synth.all_query_histories(w)
+    ce = w.T - w.W
+    want_idx, want_sc = detect.detect_mass(q, K, ce, w.k)
+    got_idx, got_units = _run_mass(q, K, ce, w.k, w.dtype)
+    _check_mass(got_idx, got_units, want_idx, want_sc, w.k)
+    # the mass the chosen set covers, and how it compares with the logit-sum set
+    G = w.Hq // w.Hkv
+    idx16, _ = detect.detect(q, K, ce, w.k)
+    cover = np.mean([want_sc[0, h][got_idx[0, h]].sum() / (G * w.R) for h in range(w.Hkv)])
+    cover16 = np.mean([want_sc[0, h][idx16[0, h]].sum() / (G * w.R) for h in range(w.Hkv)])
+    say(f"   attention mass covered: mass set {cover:.3f}, logit-sum set {cover16:.3f}")

@@ -150,3 +150,33 @@ def test_cache_scores_equal_fp64_scores_of_dequantized_keys():
     assert np.array_equal(idx[0, 0], detect.top_k(ref, 25))
     with pytest.raises(ValueError):
         detect.cache_scores(Q + 1e-3, kp, ks)
+
+
+def test_mass_scores_closed_forms_and_brute_force():
+    """Attention-mass scores: every row's probabilities sum to one, so over
+    all keys the scores sum to the number of rows; a single key gets every
+    row's whole mass; a key shift common to all keys leaves the masses
+    unchanged (softmax shift invariance); scalar brute force on a tiny case."""
+    import math
+    rng = np.random.default_rng(41)
+    Q = rng.standard_normal((12, 16))
+    K = rng.standard_normal((30, 16))
+    c = detect.mass_scores(Q, K, 30)
+    assert abs(c.sum() - 12) < 1e-12
+    assert abs(detect.mass_scores(Q, K[:1], 1)[0] - 12) < 1e-12
+    shift = rng.standard_normal(16)
+    # a common shift of the keys moves every logit of a row by the same amount
+    c2 = detect.mass_scores(Q, K + shift, 30)
+    assert np.max(np.abs(c2 - c)) < 1e-12
+    scale = 1 / math.sqrt(16)
+    for j in range(0, 30, 7):
+        tot = 0.0
+        for r in range(12):
+            lg = [scale * sum(Q[r, d] * K[i, d] for d in range(16)) for i in range(30)]
+            m = max(lg)
+            den = sum(math.exp(x - m) for x in lg)
+            tot += math.exp(lg[j] - m) / den
+        assert abs(c[j] - tot) < 1e-12
+    idx, sc = detect.detect_mass(Q[None, None], K[None, None], 25, 5)
+    assert np.array_equal(idx[0, 0], detect.top_k(sc[0, 0], 5))
+    assert np.max(np.abs(sc[0, 0] - c[:25])) < 1e-15
