@@ -697,18 +697,24 @@ __global__ __launch_bounds__(256) void mass_stats_kernel(const uint16_t *__restr
 }
 
 // per (unit, row): stats = (cs * m, 1 / L) of the row's softmax over all keys;
-// the logits above are raw q . k, so cs = sm_scale * log2(e)
+// the logits above are raw q . k, so cs = sm_scale * log2(e). One wave per
+// row: lanes stride over the row's partials, then a fixed-order wave reduction.
 __global__ __launch_bounds__(256) void mass_merge_kernel(const float2 *__restrict__ part, int rows_total,
                                                          int nblk, float cs, float2 *__restrict__ stats) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows_total) return;
+  const int r = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows_total) return;                              // wave-uniform
   const float2 *p = part + static_cast<int64_t>(r) * nblk;
   float mm = kNegInfF;
-  for (int i = 0; i < nblk; ++i) mm = fmaxf(mm, p[i].x);
-  double L = 0.0;
-  for (int i = 0; i < nblk; ++i)
-    if (p[i].x != kNegInfF) L += static_cast<double>(p[i].y) * exp2(static_cast<double>(cs) * (p[i].x - mm));
-  stats[r] = make_float2(cs * mm, L > 0.0 ? static_cast<float>(1.0 / L) : 0.f);
+  for (int i = lane; i < nblk; i += 64) mm = fmaxf(mm, p[i].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
+  float L = 0.f;
+  for (int i = lane; i < nblk; i += 64)
+    if (p[i].x != kNegInfF) L += p[i].y * __builtin_amdgcn_exp2f(cs * (p[i].x - mm));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+  if (lane == 0) stats[r] = make_float2(cs * mm, L > 0.f ? 1.0f / L : 0.f);
 }
 
 template <int D, int DT>
@@ -783,7 +789,7 @@ __global__ __launch_bounds__(256) void mass_cols_kernel(const uint16_t *__restri
     const float c = cols[t] + __shfl_xor(cols[t], 32, 64);
     if (half == 0 && col[t] < cand_end)
       scores[static_cast<int64_t>(unit) * cand_end + col[t]] =
-          __double2ll_rn(static_cast<double>(c) * 1099511627776.0);   // units of 2^-40
+          __double2ll_rn(static_cast<double>(c) * 4194304.0);   // units of 2^-22
   }
 }
 
@@ -1060,7 +1066,7 @@ extern "C" hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dt
   do {                                                                                                   \
     hipLaunchKernelGGL((mass_stats_kernel<DD, TT>), dim3(units * nb1), dim3(256), 0, st, qa, kk, Hq, Hkv, \
                        R, k_rows, nb1, cs, part);                                                        \
-    hipLaunchKernelGGL(mass_merge_kernel, dim3((units * M + 255) / 256), dim3(256), 0, st, part,          \
+    hipLaunchKernelGGL(mass_merge_kernel, dim3((units * M + 3) / 4), dim3(256), 0, st, part,              \
                        units * M, nb1, cs, stats);                                                       \
     hipLaunchKernelGGL((mass_cols_kernel<DD, TT>), dim3(units * nb3), dim3(256), 0, st, qa, kk, Hq, Hkv,  \
                        R, k_rows, cand_end, nb3, cs, stats, scores);                                      \

@@ -247,7 +247,8 @@ hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_dtype dtype,
  * accumulation and the exponentials are fp32, so the scores are
  * approximations of the exact masses (not bit-reproducible against a
  * reference, but deterministic run to run). score_out (optional) receives
- * c_j in int64 units of 2^-40. Requires dtype HQ_BF16 or HQ_F16, D in {64,
+ * c_j in int64 units of 2^-22 (so that up to 1024 query rows the score range
+ * fits the top-k's 32-bit keys without refinement). Requires dtype HQ_BF16 or HQ_F16, D in {64,
  * 128}, 0 <= k_top <= cand_end <= k_rows, 1 <= R <= 1024, ws_bytes >=
  * hq_detect_mass_workspace_size(B, Hq, Hkv, R, k_rows, cand_end); errors as
  * hq_detect_vlines, nothing enqueued on error.

@@ -182,7 +182,7 @@ def _check_mass(got_idx, got_units, want_idx, want_sc, k_top, rel=1e-4):
     """Scores within rel of the unit's largest oracle score; index sets equal
     except for positions whose oracle score lies within that tolerance of the
     k-th largest (near ties the fp32 evaluation may order either way)."""
-    got_sc = got_units.astype(np.float64) / float(1 << 40)
+    got_sc = got_units.astype(np.float64) / float(1 << 22)
     B, Hkv, _ = want_sc.shape
     for b in range(B):
         for h in range(Hkv):
