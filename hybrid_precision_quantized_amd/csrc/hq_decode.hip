@@ -524,66 +524,111 @@ __device__ void int4_split(const DecodeParams &P, SharedMem &sm, int b, int h, i
 
 // ---------------------------------------------------------------- INT4 pass, D = 128, 4 heads
 // Specialisation of the INT4 pass for the common shape (head_dim 128, a GQA
-// chunk of 4 query heads, 16-bit queries). Lane (slot, g) keeps its four
-// per-head partial dots in a lane-dependent order -- register j holds head
-// g ^ j -- so two DPP exchanges (xor 2, then xor 1) leave the full logit of
-// head g in lane g of the token with three adds and no selects. The mask, the
-// max test, the subtraction and the exponential then run once per lane, and
-// the other heads' probabilities reach the P . V weights through DPP
-// broadcasts fused into the multiplies.
+// chunk of 4 query heads, 16-bit queries). Both products run on the matrix
+// cores with v_mfma_f32_4x4x4_16b_f16: sixteen independent 4x4 blocks per
+// instruction, each lane feeding one row of A and one column of B of its
+// block (lane 4 blk + i) and receiving that column of D in four registers
+// (rows 0..3).
 //
-// Key codes become fp16 pairs at two nibble positions without shifts: the
-// low nibble of each byte under the magic 1024 (ulp 1, so 1024 + c) and the
-// high nibble in place under the magic 64 (ulp 1/16 at bits 4-7, so 64 + c);
-// one shift by 8 serves the other two nibbles. The queries are rounded to
-// fp16 once (exact for bf16 magnitudes in [2^-17, 65504]; the fast path
-// requires |q| < 65504), and each dot chain starts from minus its offset,
-// -(1024 sum of the even channels + 64 sum of the odd ones), so the chain
-// ends at q . c itself.
-__device__ __forceinline__ float dot2_f16_from(uint32_t a, uint32_t b, float c) {
-  // the VOP3P form: the accumulator input need not be the destination
-  float d;
-  asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
+// Q . K: block blk = 4 g + tq computes, for key group g and the four tokens
+// 4 tq .. 4 tq + 3 of the chunk, the four heads' group dots: A rows are the
+// heads' query channels of group g, B columns the tokens' key codes. Lane
+// (token t = lane % 16, group g = lane / 16) loads its own 32 codes, so every
+// lane's D holds the four heads of its (token, group). Eight instructions
+// cover the 32 channels of a group. Key codes become fp16 pairs without
+// shifts at two nibble positions: the low nibble of each byte under the
+// magic 1024 (ulp 1, so 1024 + c) and the high nibble in place under the
+// magic 64 (ulp 1/16 at bits 4-7, so 64 + c); one shift by 8 serves the
+// other two nibbles. The queries are rounded to fp16 once (exact for bf16
+// magnitudes in [2^-17, 65504]; the fast path requires |q| < 65504) and the
+// accumulation starts from minus the offsets, -(1024 sum of the low-nibble
+// channels + 64 sum of the others), so it ends at q . c. The group scale and
+// zero point are applied per (token, group) on the vector unit, and three
+// permlane swaps with three adds sum the four groups (rows of 16 lanes) so
+// that lane (t, h = lane / 16) holds the logit of head h for token t.
+//
+// P . V: block blk computes, for 4 value channels of one group, the four
+// heads' sums over 4 tokens: A rows are the heads' weights p s of the
+// tokens (written to LDS by the softmax lanes, 2 reads per lane), B columns
+// the channels' centred codes from the TILE16 tiles. Lane l's D is then the
+// four heads of channel 2l (even set) or 2l + 1 (odd set): the accumulator
+// layout of the 16-bit pass.
+typedef _Float16 h4x __attribute__((ext_vector_type(4)));
+typedef float f4x __attribute__((ext_vector_type(4)));
+typedef uint32_t u2x __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f4x mfma4x4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4x c) {
+  const u2x a = {a0, a1}, bb = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4x, a), __builtin_bit_cast(h4x, bb), c, 0, 0, 0);
 }
-template <int CTRL>
-__device__ __forceinline__ float dpp_mul(float a, float b) {   // dpp(a) * b
-  return dpp_f<CTRL>(a) * b;
+// In-place row swaps between two registers (rows of 16 lanes): 32-swap
+// exchanges rows 2,3 of x with rows 0,1 of y, 16-swap the odd rows of x with
+// the even rows of y. Written as inline asm with both operands tied: the
+// compiler's builtins for these instructions fold swap(x, x) to (x, x) and
+// take both results from one register. The compiler does not see inside the
+// asm, so it carries its own wait states: two before (a vector write of
+// either operand just before) and two after (a read of the results).
+__device__ __forceinline__ void permlane32_swap(float &x, float &y) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void permlane16_swap(float &x, float &y) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+// x of rows 0 + 2 and 1 + 3 in rows 0, 1; y of rows 0 + 2 and 1 + 3 in rows 2, 3
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+  permlane32_swap(x, y);
+  return x + y;
+}
+// x of rows 0 + 1 in row 0, y of rows 0 + 1 in row 1, x of rows 2 + 3 in row 2, y in row 3
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+  permlane16_swap(x, y);
+  return x + y;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kRowRor + 8>(v));
+  v = fmaxf(v, dpp_f<kRowRor + 4>(v));
+  v = fmaxf(v, dpp_f<kRowRor + 2>(v));
+  return fmaxf(v, dpp_f<kRowRor + 1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kRowRor + 8>(v);
+  v += dpp_f<kRowRor + 4>(v);
+  v += dpp_f<kRowRor + 2>(v);
+  return v + dpp_f<kRowRor + 1>(v);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 constexpr int kQuadBcast[4] = {0x00, 0x55, 0xAA, 0xFF};        // quad_perm [h,h,h,h]
 
 template <int QT>
 __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int h, int i0,
                                    int64_t r0, int64_t r1, WaveState<4> &st) {
-  constexpr int D = 128, HB = 4, LPT = 4, SLOTS = 16, CP = 64;
+  constexpr int D = 128, SLOTS = 16, CP = 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
-  const int slot = lane >> 2;
-  const int g = lane & 3;
-  const int cp = lane;                 // P.V lane: channel pair
-  const int gp = cp >> 4;
+  const int t = lane & 15;             // token of the chunk
+  const int row = lane >> 4;           // key group (loads, Q . K), head (softmax)
+  const int hq = lane & 3;             // head of this lane's A row in Q . K and P . V
   const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
 
-  // raw query channels of this lane's group for head g ^ j, loaded before the
-  // ring so that their wait does not cover the ring's loads
-  uint32_t qraw[4][16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    load_q32<QT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32, qraw[j]);
+  // raw query channels of head hq, group `row`, loaded before the ring so
+  // that their wait does not cover the ring's loads
+  uint32_t qraw[16];
+  load_q32<QT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + hq) * D + row * 32, qraw);
   __builtin_amdgcn_sched_barrier(0);
 
   const uint32_t vmagic = 0x64006400u;
-  float zl[4] = {0.f, 0.f, 0.f, 0.f};   // sum p_h (z + 8 s) of this lane's group, head h
-  float lown = 0.f;                      // sum of p of head g (this lane's head)
-  // running max of head g; starts finite, so p = 2^(l - m) needs no guard
-  // (a live logit above it always takes the rescale first)
+  float zl[4] = {0.f, 0.f, 0.f, 0.f};   // sum p_h (z + 8 s) of group `row`, head h
+  float lown = 0.f;                      // sum of p of head `row`
+  // running max of head `row`; starts finite, so p = 2^(l - m) needs no
+  // guard (a live logit above it always takes the rescale first)
   float mown = -__FLT_MAX__;
 
   // Each chunk gets its own buffer views, built in SGPRs from wave-uniform
   // offsets: the per-lane offsets below never change, so the loads need no
   // vector address arithmetic, and a view past the end of the split is empty
   // (its loads return 0). Splits start at multiples of 64 positions, so the
-  // VL bits of chunk c sit in word c / 2 at bit 16 (c % 2) + slot, and c % 2
+  // VL bits of chunk c sit in word c / 2 at bit 16 (c % 2) + t, and c % 2
   // equals wave % 2 for every chunk of this wave.
   const uint32_t n = static_cast<uint32_t>(r1 - r0);
   const int64_t row0 = head * P.t_cap + r0;
@@ -594,10 +639,10 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
   const uint8_t *bb = reinterpret_cast<const uint8_t *>(P.vl_bits + head * P.bits_words + (r0 >> 5));
   const uint32_t nk = n * (D / 2), ns = n * (D / 8), nv = ((n + 15) / 16) * (CP * 16);
   const uint32_t nb = ((n + 31) >> 5) * 4;
-  const uint32_t lo_k = slot * (D / 2) + g * 16;
-  const uint32_t lo_s = slot * (D / 8) + g * 4;
-  const uint32_t lo_v = cp * 16;
-  const uint32_t bitpos = (wave & 1) * 16 + slot;
+  const uint32_t lo_k = t * (D / 2) + row * 16;
+  const uint32_t lo_s = t * (D / 8) + row * 4;
+  const uint32_t lo_v = lane * 16;
+  const uint32_t bitpos = (wave & 1) * 16 + t;
 
   auto issue = [&](uint32_t c, Int4Loads<D> &L) {
     const uint32_t os = c * (SLOTS * D / 8);
@@ -616,18 +661,16 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
     issue(wave + jr * kWaves, ring[jr]);
     __builtin_amdgcn_sched_barrier(0);   // keep the ring's issue order: waits are counts
   }
-  // fp16 query pairs (register j: head g ^ j) while the ring's first loads fly
-  uint32_t qp[4][4][4];
-  float cqs[4];          // cs * sum of the group's query channels, head g ^ j
-  float nof[4];          // minus the chain offset, head g ^ j
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t (&raw)[16] = qraw[j];
+  // fp16 query pairs in the order of the unpacked code pairs, while the
+  // ring's first loads fly: qa[w][m] = channels (8w + m, 8w + m + 4)
+  uint32_t qa[4][4];
+  float nf, cq;
+  {
     uint32_t hb[32];
     float se = 0.f, so = 0.f;
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
-      const uint32_t bits = (raw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+      const uint32_t bits = (qraw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
       _Float16 q16;
       if constexpr (QT == HQ_BF16) q16 = static_cast<_Float16>(bf16_to_f32(bits));
       else q16 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits));
@@ -638,102 +681,113 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) qp[j][w][m] = hb[8 * w + m] | (hb[8 * w + m + 4] << 16);
-    cqs[j] = P.cs * (se + so);
-    nof[j] = -fmaf(1024.f, se, 64.f * so);
+      for (int m = 0; m < 4; ++m) qa[w][m] = hb[8 * w + m] | (hb[8 * w + m + 4] << 16);
+    cq = P.cs * (se + so);
+    nf = -fmaf(1024.f, se, 64.f * so);
   }
-  _Float16 *psh = reinterpret_cast<_Float16 *>(&sm.ps[wave][0]);
+  // per head i of this lane's group (the quad's lane i holds head i)
+  f4x nofv;
+  float cqv[4];
+  nofv[0] = dpp_f<kQuadBcast[0]>(nf); cqv[0] = dpp_f<kQuadBcast[0]>(cq);
+  nofv[1] = dpp_f<kQuadBcast[1]>(nf); cqv[1] = dpp_f<kQuadBcast[1]>(cq);
+  nofv[2] = dpp_f<kQuadBcast[2]>(nf); cqv[2] = dpp_f<kQuadBcast[2]>(cq);
+  nofv[3] = dpp_f<kQuadBcast[3]>(nf); cqv[3] = dpp_f<kQuadBcast[3]>(cq);
+
+  f4x ae, ao;
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    ae[hh] = st.acc_e[hh];
+    ao[hh] = st.acc_o[hh];
+  }
+  // nibble masks in SGPRs and fp16 magics in VGPRs, opaque to constant
+  // folding, so that each code pair is one v_and_or_b32
+  uint32_t m_lo, m_hi, mg1024, mg64;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(m_lo));
+  asm("s_mov_b32 %0, 0xf000f0" : "=s"(m_hi));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(mg1024));
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(mg64));
+  uint16_t *psw = reinterpret_cast<uint16_t *>(&sm.ps[wave][0]);   // [head][group][16 tokens]
+  const uint4 *pws = reinterpret_cast<const uint4 *>(psw + (hq * 4 + row) * 16);
   // one wave step over chunk c held in `cur`
   auto step = [&](const uint32_t c, const Int4Loads<D> &cur) {
-
-    // ---- q . c over this lane's group, head g ^ j in part[j] (each chain
-    // starts at minus its magic offset)
-    float part[4];
+    // ---- q . c of the 4 heads over this lane's (token, group)
     const uint32_t w[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+    f4x d = nofv;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
+      // plain expressions (v_and_or_b32 with the registers above), not
+      // inline asm: the compiler must see these vector writes to keep the
+      // wait states before the MFMA that reads them
       const uint32_t w8 = w[ww] >> 8;
-      const uint32_t x0 = and_or(w[ww], 0x000F000Fu, 0x64006400u);   // channels 8ww, 8ww + 4
-      const uint32_t x1 = and_or(w[ww], 0x00F000F0u, 0x54005400u);   // 8ww + 1, 8ww + 5
-      const uint32_t x2 = and_or(w8, 0x000F000Fu, 0x64006400u);      // 8ww + 2, 8ww + 6
-      const uint32_t x3 = and_or(w8, 0x00F000F0u, 0x54005400u);      // 8ww + 3, 8ww + 7
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        part[j] = ww == 0 ? dot2_f16_from(qp[j][0][0], x0, nof[j]) : dot2_f16(qp[j][ww][0], x0, part[j]);
-        part[j] = dot2_f16(qp[j][ww][1], x1, part[j]);
-        part[j] = dot2_f16(qp[j][ww][2], x2, part[j]);
-        part[j] = dot2_f16(qp[j][ww][3], x3, part[j]);
-      }
+      const uint32_t x0 = (w[ww] & m_lo) | mg1024;   // channels 8ww, 8ww + 4
+      const uint32_t x1 = (w[ww] & m_hi) | mg64;     // 8ww + 1, 8ww + 5
+      const uint32_t x2 = (w8 & m_lo) | mg1024;      // 8ww + 2, 8ww + 6
+      const uint32_t x3 = (w8 & m_hi) | mg64;        // 8ww + 3, 8ww + 7
+      d = mfma4x4(qa[ww][0], qa[ww][1], x0, x1, d);
+      d = mfma4x4(qa[ww][2], qa[ww][3], x2, x3, d);
     }
     // scaled group partials: cs (s q.c + z sum q) = (cs s) q.c + (cs sum q) z
     const float ssc = lo_f16(cur.ks) * P.cs;
     const float zk = hi_f16(cur.ks);
+    float part[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) part[j] = fmaf(ssc, part[j], cqs[j] * zk);
-    // quad reduce-scatter: lane g ends with head g summed over the 4 groups
-    const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
-    const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
-    const float lgv = y0 + dpp_f<kQuadXor1>(y1);
-    const bool live = (slot < n - c * SLOTS) && !((cur.bits >> bitpos) & 1u);
+    for (int i = 0; i < 4; ++i) part[i] = fmaf(ssc, d[i], cqv[i] * zk);
+    // sum over the 4 groups: lane (t, h) ends with head h
+    const float lgv = swap16_sum(swap32_sum(part[0], part[2]), swap32_sum(part[1], part[3]));
+    const bool live = (t < n - c * SLOTS) && !((cur.bits >> bitpos) & 1u);
     const float lg = live ? lgv : kNegInf;
 
     if (__builtin_expect(__ballot(lg > mown) != 0, 0)) {
-      // slow path: new wave max of head g; rescale every running quantity
-      const float mx = slots_max<LPT>(lg);
-      const float mn = fmaxf(mown, mx);
-      const float alpha = fast_exp2(mown - mn);          // of head g
+      // slow path: new wave max of head `row`; rescale every running quantity
+      const float mn = fmaxf(mown, row16_max(lg));
+      const float alpha = fast_exp2(mown - mn);          // of head `row`
       mown = mn;
       lown *= alpha;
-      zl[0] = dpp_mul<kQuadBcast[0]>(alpha, zl[0]);
-      zl[1] = dpp_mul<kQuadBcast[1]>(alpha, zl[1]);
-      zl[2] = dpp_mul<kQuadBcast[2]>(alpha, zl[2]);
-      zl[3] = dpp_mul<kQuadBcast[3]>(alpha, zl[3]);
-      // the P.V lanes hold channels of every head: alpha of head hh from lane hh
-      const float a0 = __shfl(alpha, 0, 64), a1 = __shfl(alpha, 1, 64);
-      const float a2 = __shfl(alpha, 2, 64), a3 = __shfl(alpha, 3, 64);
-      st.acc_e[0] *= a0; st.acc_o[0] *= a0;
-      st.acc_e[1] *= a1; st.acc_o[1] *= a1;
-      st.acc_e[2] *= a2; st.acc_o[2] *= a2;
-      st.acc_e[3] *= a3; st.acc_o[3] *= a3;
+      const float a0 = readlane_f(alpha, 0), a1 = readlane_f(alpha, 16);
+      const float a2 = readlane_f(alpha, 32), a3 = readlane_f(alpha, 48);
+      zl[0] *= a0; ae[0] *= a0; ao[0] *= a0;
+      zl[1] *= a1; ae[1] *= a1; ao[1] *= a1;
+      zl[2] *= a2; ae[2] *= a2; ao[2] *= a2;
+      zl[3] *= a3; ae[3] *= a3; ao[3] *= a3;
     }
     const float p = fast_exp2(lg - mown);
     lown += p;
-    // V scale and the zero point of the centred codes, z + 8 s; zero for
-    // masked tokens (their planes may hold anything, NaN included)
+    // the 4 heads' p of token t in every row: after the 32-swap x holds the
+    // p of row r % 2 and y that of row 2 + r % 2; the 16-swaps spread each
+    float ph[4];
+    float x = p, y = p;
+    permlane32_swap(x, y);
+    ph[0] = x; ph[1] = x;
+    permlane16_swap(ph[0], ph[1]);
+    ph[2] = y; ph[3] = y;
+    permlane16_swap(ph[2], ph[3]);
+    // V scale and the zero point of the centred codes, z + 8 s, of group
+    // `row`; zero for masked tokens (their planes may hold anything)
     const uint32_t vsw = live ? cur.vs : 0u;
     const float sv = lo_f16(vsw);
     const float zv = fmaf(8.f, sv, hi_f16(vsw));
-    const float ps0 = dpp_mul<kQuadBcast[0]>(p, sv);
-    const float ps1 = dpp_mul<kQuadBcast[1]>(p, sv);
-    const float ps2 = dpp_mul<kQuadBcast[2]>(p, sv);
-    const float ps3 = dpp_mul<kQuadBcast[3]>(p, sv);
-    zl[0] = fmaf(dpp_f<kQuadBcast[0]>(p), zv, zl[0]);
-    zl[1] = fmaf(dpp_f<kQuadBcast[1]>(p), zv, zl[1]);
-    zl[2] = fmaf(dpp_f<kQuadBcast[2]>(p), zv, zl[2]);
-    zl[3] = fmaf(dpp_f<kQuadBcast[3]>(p), zv, zl[3]);
-    const uint32_t ps01 = pack_f16_rne(ps0, ps1), ps23 = pack_f16_rne(ps2, ps3);
-    uint16_t *psw = reinterpret_cast<uint16_t *>(psh);
-    psw[(0 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps01);
-    psw[(1 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps01 >> 16);
-    psw[(2 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps23);
-    psw[(3 * LPT + g) * 32 + slot] = static_cast<uint16_t>(ps23 >> 16);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) zl[hh] = fmaf(ph[hh], zv, zl[hh]);
+    const uint32_t w01 = pack_f16_rne(ph[0] * sv, ph[1] * sv), w23 = pack_f16_rne(ph[2] * sv, ph[3] * sv);
+    psw[(0 * 4 + row) * 16 + t] = static_cast<uint16_t>(w01);
+    psw[(1 * 4 + row) * 16 + t] = static_cast<uint16_t>(w01 >> 16);
+    psw[(2 * 4 + row) * 16 + t] = static_cast<uint16_t>(w23);
+    psw[(3 * 4 + row) * 16 + t] = static_cast<uint16_t>(w23 >> 16);
     wave_sync();
 
     // ---- p . v (v never dequantized: sum (p s)(c - 8), zero point later)
     const uint32_t vw[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
     uint32_t e[8], o[8];
     unpack_v_tile(vw, vmagic, e, o);
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(&sm.ps[wave][(hh * LPT + gp) * 16]);
-      const uint4 pa = src[0], pb = src[1];
-      const uint32_t pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        st.acc_e[hh] = dot2_f16(pr[i], e[i], st.acc_e[hh]);
-        st.acc_o[hh] = dot2_f16(pr[i], o[i], st.acc_o[hh]);
-      }
-    }
+    const uint4 pa = pws[0], pb = pws[1];     // head hq, group row, tokens 0..7 / 8..15
+    ae = mfma4x4(pa.x, pa.y, e[0], e[1], ae);
+    ao = mfma4x4(pa.x, pa.y, o[0], o[1], ao);
+    ae = mfma4x4(pa.z, pa.w, e[2], e[3], ae);
+    ao = mfma4x4(pa.z, pa.w, o[2], o[3], ao);
+    ae = mfma4x4(pb.x, pb.y, e[4], e[5], ae);
+    ao = mfma4x4(pb.x, pb.y, o[4], o[5], ao);
+    ae = mfma4x4(pb.z, pb.w, e[6], e[7], ae);
+    ao = mfma4x4(pb.z, pb.w, o[6], o[7], ao);
   };
   // full groups of NPF steps: every refill is issued unconditionally (past
   // the split the buffer loads return 0), so each wait for the oldest ring
@@ -755,22 +809,23 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
       step(cb + jr * kWaves, ring[jr]);
     }
 
-  // ---- per-(head, group) zero-point sums, folded into the accumulators; the
-  // wave state of head hh lives in lane hh's quad position
+  // ---- per-(head, group) zero-point sums, folded into the accumulators;
+  // the softmax state of head hh lives in row hh
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    const float z = xor_sum<LPT>(zl[hh]);
-    if (slot == 0) sm.zo[wave][hh][g] = z;
+  for (int hh = 0; hh < 4; ++hh) {
+    const float z = row16_sum(zl[hh]);
+    if (t == 0) sm.zo[wave][hh][row] = z;
   }
-  const float lsum = xor_sum<LPT>(lown);                 // head g, over the slots
+  const float lsum = row16_sum(lown);                   // head `row`, over the tokens
   wave_sync();
+  const int gp = lane >> 4;                              // group of channels 2 lane, 2 lane + 1
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
+  for (int hh = 0; hh < 4; ++hh) {
     const float z = sm.zo[wave][hh][gp];
-    st.acc_e[hh] = st.acc_e[hh] + z;
-    st.acc_o[hh] = st.acc_o[hh] * 0.0625f + z;
-    st.m[hh] = __shfl(mown, hh, 64);
-    st.l[hh] = __shfl(lsum, hh, 64);
+    st.acc_e[hh] = ae[hh] + z;
+    st.acc_o[hh] = ao[hh] * 0.0625f + z;
+    st.m[hh] = readlane_f(mown, 16 * hh);
+    st.l[hh] = readlane_f(lsum, 16 * hh);
   }
 }
 
@@ -1108,7 +1163,7 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
 
 // ---------------------------------------------------------------- the kernel
 template <int D, int HB, int QT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams P) {
   __shared__ SharedMem sm;
   constexpr int CP = D / 2;
   // XCD-aware numbering: hardware block id -> (xcd, index on that xcd)
