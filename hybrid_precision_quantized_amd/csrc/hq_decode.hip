@@ -264,6 +264,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t view(const uint8_t *base, uint
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// non-temporal: the codes are streamed once per step
+__device__ __forceinline__ u32x4 bload16nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -646,11 +650,11 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
 
   auto issue = [&](uint32_t c, Int4Loads<D> &L) {
     const uint32_t os = c * (SLOTS * D / 8);
-    L.kc = bload16(view(kb, nk, c * (SLOTS * D / 2)), lo_k);
+    L.kc = bload16nt(view(kb, nk, c * (SLOTS * D / 2)), lo_k);
     L.ks = bload4(view(ksb, ns, os), lo_s);
     L.vs = bload4(view(vsb, ns, os), lo_s);
     L.bits = bload4(view(bb, nb, (c >> 1) * 4), 0);
-    L.vc = bload16(view(vb, nv, c * (CP * 16)), lo_v);
+    L.vc = bload16nt(view(vb, nv, c * (CP * 16)), lo_v);
   };
 
   constexpr int NPF = 6;
@@ -1459,10 +1463,12 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
   const double cost_fp = kFpRowCost * static_cast<double>(nfp);
   int S = n_splits;
   if (S <= 0) {
-    // one generation of 512 blocks fills the chip; long contexts get four,
+    // one generation of 512 blocks fills the chip; long contexts get six,
     // so that blocks finishing early are replaced and the tail stays short
+    // (at 16 x 128K tokens, 8 KV heads: 533 us with 2048 blocks, 503 with
+    // 3072, 505 with 4096)
     const double steps_per_wave = (cost_q + cost_fp) / step * pl.units / (512.0 * kWaves);
-    const int target_blocks = steps_per_wave >= 128.0 ? 2048 : 512;
+    const int target_blocks = steps_per_wave >= 128.0 ? 3072 : 512;
     S = static_cast<int>(ceil_div(target_blocks, pl.units));
     // at least ~4 wave steps of work per wave
     const int64_t max_s = ceil_div(nq_att + nfp, 16LL * step);
@@ -1470,17 +1476,26 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
     if (S > kMaxSplits) S = kMaxSplits;
     if (S < 1) S = 1;
   }
-  // 16-bit splits: rounded up, so that none costs more than an average split
-  int s_fp = 0;
-  if (nfp > 0) {
-    s_fp = static_cast<int>(std::ceil(cost_fp / (cost_q + cost_fp) * S - 1e-9));
-    if (s_fp < 1) s_fp = 1;
-    const int64_t mx = ceil_div(nfp, step);
-    if (s_fp > mx) s_fp = static_cast<int>(mx);
+  // 16-bit splits: the VL rows and the window rows are rounded up each on
+  // their own, so that no 16-bit split costs more than an average split (a
+  // long VL split would otherwise be the launch's tail)
+  const double avg = (cost_q + cost_fp) / S;
+  int s_vl = 0, s_win = 0;
+  if (kv->k > 0) {
+    s_vl = static_cast<int>(std::ceil(kFpRowCost * kv->k / avg - 1e-9));
+    const int64_t mx = ceil_div(kv->k, step);
+    if (s_vl > mx) s_vl = static_cast<int>(mx);
+    if (s_vl < 1) s_vl = 1;
+  }
+  if (kv->W > 0) {
+    s_win = static_cast<int>(std::ceil(kFpRowCost * kv->W / avg - 1e-9));
+    const int64_t mx = ceil_div(kv->W, step);
+    if (s_win > mx) s_win = static_cast<int>(mx);
+    if (s_win < 1) s_win = 1;
   }
   int s_q = 0;
   if (nq_att > 0) {
-    s_q = S - s_fp;
+    s_q = S - s_vl - s_win;
     if (s_q < 1) s_q = 1;
     // the VL bitmap and the ranges: at most 2^20 positions per split
     const int64_t mn = ceil_div(nq_att, 1LL << 20);
@@ -1492,16 +1507,6 @@ Plan make_plan(const hq_hybrid_kv *kv, int Hq, int n_splits) {
   // reads the VL bits of a chunk from one aligned bitmap word
   pl.len_q = s_q > 0 ? ceil_div(ceil_div(nq_att, s_q), gran) * gran : 0;
   pl.S_q = s_q > 0 ? static_cast<int>(ceil_div(nq_att, pl.len_q)) : 0;
-  // the 16-bit splits divided between the VL rows and the window rows
-  int s_win = 0, s_vl = 0;
-  if (s_fp > 0) {
-    if (kv->W > 0) {
-      s_win = static_cast<int>(static_cast<double>(s_fp) * kv->W / nfp + 0.5);
-      if (s_win < 1) s_win = 1;
-    }
-    s_vl = kv->k > 0 ? s_fp - s_win : 0;
-    if (kv->k > 0 && s_vl < 1) s_vl = 1;
-  }
   pl.len_vl = s_vl > 0 ? static_cast<int>(ceil_div(ceil_div(kv->k, s_vl), step) * step) : 0;
   pl.S_vl = s_vl > 0 ? static_cast<int>(ceil_div(kv->k, pl.len_vl)) : 0;
   pl.len_win = s_win > 0 ? static_cast<int>(ceil_div(ceil_div(kv->W, s_win), step) * step) : 0;
