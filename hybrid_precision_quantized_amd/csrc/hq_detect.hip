@@ -21,11 +21,17 @@
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
-//  * topk_kernel     one workgroup per unit: radix select (8-bit digits,
-//    one histogram per wave so the waves never contend) on the 32-bit key
-//    (score - min) >> shift (held in LDS), refinement of the boundary bucket
-//    on the bits the shift dropped, then an index cut for equal scores and an
-//    in-order compaction, so the output is ascending by position.
+//  * top-k           three launches. topk_range: many blocks per unit, each
+//    the min and max of a chunk of the scores. topk_keys: the same blocks
+//    reduce the unit's partial ranges, write the 32-bit keys
+//    1 + (score - min) >> shift and a histogram of the keys' top 11 bits per
+//    block. topk_select: one workgroup per unit sums the block histograms
+//    into the first digit. A boundary bucket of at most 1024 keys is ranked
+//    directly by (score, position); a larger one goes through the remaining
+//    two digits (11 and 10 bits), a refinement on the bits the shift dropped
+//    and a cut of equal scores by position. The keys sit in LDS up to 32768
+//    candidates and are streamed beyond; the output is compacted in order,
+//    ascending by position.
 #include "hq_common.h"
 
 namespace hq {
@@ -270,13 +276,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, c
 }
 
 // ---------------------------------------------------------------- top-k
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int kTopkThreads = 1024;
-constexpr int kLdsKeys = 33792;          // keys kept in LDS up to this many candidates
-// LDS slot of key j: one padding word per 32 keys, so both the strided passes
-// (consecutive j across lanes) and the per-thread runs of the compaction
-// (j = t * per + i, 33 * t mod 64 distinct) are free of bank conflicts
-__device__ __forceinline__ int64_t pad_slot(int64_t j) { return j + (j >> 5); }
-constexpr int kLdsKeySlots = kLdsKeys + kLdsKeys / 32;
+constexpr int kRun = 32;                       // positions per thread per batch
+constexpr int kDigitBits = 11;                 // three passes over a 32-bit key
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kHists = kTopkThreads / 128;     // one histogram per two waves
+// per-unit stride of the streamed keys (a multiple of 4: 16-byte loads)
+__host__ __device__ inline int64_t key_stride(int64_t n) { return (n + 3) & ~3LL; }
 
 // exclusive scan of one int per thread over the block; *total gets the sum
 __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) {
@@ -289,14 +296,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) 
   }
   if (lane == 63) sh[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
-      const int t = sh[i];
-      sh[i] = run;
-      run += t;
+  if (threadIdx.x < 64) {                       // scan of the 16 wave totals by the first wave
+    const int t = threadIdx.x < kTopkThreads / 64 ? sh[threadIdx.x] : 0;
+    int x = t;
+#pragma unroll
+    for (int m = 1; m < kTopkThreads / 64; m <<= 1) {
+      const int y = __shfl_up(x, m, 64);
+      if (static_cast<int>(threadIdx.x) >= m) x += y;
     }
-    sh[kTopkThreads / 64] = run;
+    if (threadIdx.x < kTopkThreads / 64) sh[threadIdx.x] = x - t;
+    if (threadIdx.x == kTopkThreads / 64 - 1) sh[kTopkThreads / 64] = x;
   }
   __syncthreads();
   const int pre = sh[w] + inc - v;
@@ -305,161 +314,415 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) 
   return pre;
 }
 
-constexpr int kDigitBits = 8;            // radix digits of 8 bits, 256 bins
-constexpr int kBins = 1 << kDigitBits;
+constexpr int kSmallBucket = kTopkThreads;     // boundary buckets up to this size are ranked directly
+constexpr int64_t kLdsKeys = 32768;            // keys kept in LDS up to this many candidates
+// LDS slot of key j: one padding word per 32 keys, so the per-thread runs
+// (j = t * 32 + i, 33 t mod 64 distinct) are free of bank conflicts
+__device__ __forceinline__ int64_t pad_slot(int64_t j) { return j + (j >> 5); }
+constexpr int kLdsKeySlots = static_cast<int>(kLdsKeys + kLdsKeys / 32);
+// LK: the keys live in LDS, sharing the space of the radix histograms, which
+// only the large-bucket path uses (and it streams the keys from memory)
+template <bool LK>
 struct TopkShared {
-  uint32_t whist[kTopkThreads / 64][kBins];   // one histogram per wave: no cross-wave contention
+  union {
+    uint32_t whist[kHists][kBins];
+    uint32_t lkeys[LK ? kLdsKeySlots : 1];
+  } u;
   uint32_t hist[kBins];
   int scan[kTopkThreads / 64 + 2];
   int sel[4];
   unsigned long long mm[2 * kTopkThreads / 64];
+  long long bsc[kSmallBucket];                 // the boundary bucket: scores and positions
+  int bpos[kSmallBucket];
+  int rank[kSmallBucket];
+  int bcnt;
 };
 
-__device__ __forceinline__ void clear_whist(TopkShared &sh) {
-  uint32_t *h = &sh.whist[0][0];
-  for (int i = threadIdx.x; i < (kTopkThreads / 64) * kBins; i += kTopkThreads) h[i] = 0u;
+template <class SH>
+__device__ __forceinline__ void clear_whist(SH &sh) {
+  uint32_t *h = &sh.u.whist[0][0];
+  for (int i = threadIdx.x; i < kHists * kBins; i += kTopkThreads) h[i] = 0u;
 }
-// sum the per-wave histograms into sh.hist
-__device__ __forceinline__ void reduce_whist(TopkShared &sh) {
+// sum the histograms into sh.hist
+template <class SH>
+__device__ __forceinline__ void reduce_whist(SH &sh) {
   for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
     uint32_t t = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkThreads / 64; ++w) t += sh.whist[w][b];
+    for (int w = 0; w < kHists; ++w) t += sh.u.whist[w][b];
     sh.hist[b] = t;
+  }
+}
+// Adds the lanes with `match` to bin d. The lanes that share the first
+// matching lane's bin add with one atomic (scores pile into few bins when
+// they are skewed, and same-address LDS atomics serialise); the others add
+// their own. Called by the whole wave.
+__device__ __forceinline__ void hist_add(uint32_t *wh, bool match, uint32_t d) {
+  const unsigned long long act = __ballot(match);
+  if (act == 0) return;
+  const int first = static_cast<int>(__builtin_ctzll(act));
+  const uint32_t lead = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(d), first));
+  const bool same = match && d == lead;
+  const unsigned long long sm = __ballot(same);
+  if (same) {
+    if ((threadIdx.x & 63) == first) atomicAdd(&wh[lead], static_cast<uint32_t>(__popcll(sm)));
+  } else if (match) {
+    atomicAdd(&wh[d], 1u);
   }
 }
 
 // Digit search after a histogram pass: the digit (bins in descending order)
 // holding the k_rem-th largest; returns it, *k_rem becomes the rank inside
-// the digit and *cnt the digit's population.
-__device__ int find_digit(int nb, int *k_rem, int *cnt, TopkShared &sh) {
-  const int dhi = nb - 1 - 2 * static_cast<int>(threadIdx.x);
-  const int dlo = dhi - 1;
-  const int chi = dhi >= 0 ? static_cast<int>(sh.hist[dhi]) : 0;
-  const int clo = dlo >= 0 ? static_cast<int>(sh.hist[dlo]) : 0;
-  int tot;
-  const int above = block_exclusive_scan(chi + clo, sh.scan, &tot);
-  const int kr = *k_rem;
-  if (dhi >= 0 && above < kr && kr <= above + chi) {
-    sh.sel[0] = dhi; sh.sel[1] = kr - above; sh.sel[2] = chi;
-  } else if (dlo >= 0 && above + chi < kr && kr <= above + chi + clo) {
-    sh.sel[0] = dlo; sh.sel[1] = kr - above - chi; sh.sel[2] = clo;
+// the digit and *cnt the digit's population. The first wave searches (lane
+// l holds the l-th group of bins from the top) and publishes the result
+// behind one barrier; sel is written again only behind later barriers.
+template <class SH>
+__device__ int find_digit(int nb, int *k_rem, int *cnt, SH &sh) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (nb + 63) / 64;
+    const int hi = nb - per * lane > 0 ? nb - per * lane : 0;          // bins [lo, hi)
+    const int lo = hi - per > 0 ? hi - per : 0;
+    int s = 0;
+    if (per == kBins / 64 && lo == hi - per) {       // the 2048-bin digit: every read issued at once
+      uint32_t v[kBins / 64];
+#pragma unroll
+      for (int i = 0; i < kBins / 64; ++i) v[i] = sh.hist[lo + i];
+#pragma unroll
+      for (int i = 0; i < kBins / 64; ++i) s += static_cast<int>(v[i]);
+    } else {
+      for (int b = hi - 1; b >= lo; --b) s += static_cast<int>(sh.hist[b]);
+    }
+    int inc = s;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int y = __shfl_up(inc, m, 64);
+      if (lane >= m) inc += y;
+    }
+    const int kr = *k_rem;
+    int acc = inc - s;                                                  // above this lane's bins
+    if (acc < kr && kr <= inc) {
+      for (int b = hi - 1; b >= lo; --b) {
+        const int c = static_cast<int>(sh.hist[b]);
+        if (acc < kr && kr <= acc + c) {
+          sh.sel[0] = b;
+          sh.sel[1] = kr - acc;
+          sh.sel[2] = c;
+        }
+        acc += c;
+      }
+    }
   }
   __syncthreads();
-  const int d = sh.sel[0];
   *k_rem = sh.sel[1];
   *cnt = sh.sel[2];
-  __syncthreads();
-  return d;
+  return sh.sel[0];
 }
 
-// One workgroup per (b, h). Keys (score - min) >> shift live in LDS (or, past
-// kLdsKeys candidates, in the workspace); scores are read from global memory
-// in the two key-building passes (8 independent loads per thread per step)
-// and again only for members of the boundary bucket.
-template <bool IN_LDS>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__restrict__ scores,
-                                                            uint32_t *__restrict__ gkeys, int64_t n,
-                                                            int k_top, int32_t *__restrict__ idx_out) {
-  __shared__ TopkShared sh;
-  __shared__ uint32_t lkeys[IN_LDS ? kLdsKeySlots : 1];
-  const int unit = blockIdx.x;
-  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
-  uint32_t *gk = gkeys + static_cast<int64_t>(unit) * n;
-  int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
-  if (k_top == 0) return;
-  constexpr int U = 8;
-  const int64_t stride = static_cast<int64_t>(kTopkThreads) * U;
+// Chunking of a unit's candidates over the blocks of the first two launches.
+constexpr int kTkBlock = 256;
+constexpr int kTkMaxBlocks = 32;
+struct TopkChunks {
+  int nbu;        // blocks per unit
+  int64_t ch;     // candidates per block (a multiple of 4)
+};
+__host__ __device__ inline TopkChunks topk_chunks(int64_t n) {
+  int64_t nbu = (n + 1023) / 1024;
+  if (nbu > kTkMaxBlocks) nbu = kTkMaxBlocks;
+  if (nbu < 1) nbu = 1;
+  TopkChunks c;
+  c.nbu = static_cast<int>(nbu);
+  c.ch = (((n + nbu - 1) / nbu) + 3) & ~3LL;
+  return c;
+}
+// workspace of the top-k: partial ranges, block histograms, keys
+struct TopkWs {
+  size_t mm, hist, keys, total;
+};
+TopkWs topk_ws(int64_t units, int64_t n) {
+  const TopkChunks c = topk_chunks(n);
+  TopkWs L{};
+  L.mm = 0;
+  L.hist = align_up(static_cast<size_t>(units) * c.nbu * 2 * sizeof(unsigned long long), 256);
+  L.keys = align_up(L.hist + static_cast<size_t>(units) * c.nbu * kBins * sizeof(uint32_t), 256);
+  L.total = align_up(L.keys + static_cast<size_t>(units) * key_stride(n) * sizeof(uint32_t), 256);
+  return L;
+}
 
-  // 1. range of the scores
-  unsigned long long mn = ~0ull, mx = 0;
-  for (int64_t j0 = threadIdx.x; j0 < n; j0 += stride) {
-    long long w[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int64_t j = j0 + static_cast<int64_t>(i) * kTopkThreads;
-      w[i] = j < n ? sc[j] : sc[j0];
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const unsigned long long u = static_cast<unsigned long long>(w[i]) ^ 0x8000000000000000ull;
-      mn = u < mn ? u : mn;
-      mx = u > mx ? u : mx;
-    }
-  }
+__device__ __forceinline__ unsigned long long ordered(long long v) {
+  return static_cast<unsigned long long>(v) ^ 0x8000000000000000ull;
+}
+// min and max over a 256-thread block, into *mn / *mx of thread 0
+__device__ __forceinline__ void block_minmax(unsigned long long &mn, unsigned long long &mx,
+                                             unsigned long long *red) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
     const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
     mn = a < mn ? a : mn;
     mx = c > mx ? c : mx;
   }
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    sh.mm[threadIdx.x >> 6] = mn;
-    sh.mm[kTopkThreads / 64 + (threadIdx.x >> 6)] = mx;
+    red[2 * w] = mn;
+    red[2 * w + 1] = mx;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 1; i < kTopkThreads / 64; ++i) {
-      mn = sh.mm[i] < mn ? sh.mm[i] : mn;
-      mx = sh.mm[kTopkThreads / 64 + i] > mx ? sh.mm[kTopkThreads / 64 + i] : mx;
+    for (int i = 1; i < static_cast<int>(blockDim.x) / 64; ++i) {
+      mn = red[2 * i] < mn ? red[2 * i] : mn;
+      mx = red[2 * i + 1] > mx ? red[2 * i + 1] : mx;
     }
-    sh.mm[0] = mn;
-    sh.mm[1] = mx;
+  }
+}
+// the unit's range from its nbu partials, by the first wave (every block
+// and every launch reduces them in the same way)
+__device__ __forceinline__ void unit_range(const unsigned long long *mm, int nbu, unsigned long long &base,
+                                           int &shift, unsigned long long *red) {
+  if (threadIdx.x < 64) {
+    unsigned long long mn = ~0ull, mx = 0;
+    for (int i = threadIdx.x; i < nbu; i += 64) {
+      mn = mm[2 * i] < mn ? mm[2 * i] : mn;
+      mx = mm[2 * i + 1] > mx ? mm[2 * i + 1] : mx;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    if (threadIdx.x == 0) {
+      red[0] = mn;
+      red[1] = mx;
+    }
   }
   __syncthreads();
-  const unsigned long long base = sh.mm[0];
-  const unsigned long long range = sh.mm[1] - base;
-  __syncthreads();
+  base = red[0];
+  const unsigned long long range = red[1] - red[0];
+  // keys 1 + (score - min) >> shift fit 32 bits; key 0 marks no position
   const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
-  const int shift = nbits > 32 ? nbits - 32 : 0;
-  auto off = [&](long long sv) -> unsigned long long {
-    return (static_cast<unsigned long long>(sv) ^ 0x8000000000000000ull) - base;
-  };
+  shift = nbits > 31 ? nbits - 31 : 0;
+  __syncthreads();
+}
 
-  // 2. keys
-  for (int64_t j0 = threadIdx.x; j0 < n; j0 += stride) {
-    long long w[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int64_t j = j0 + static_cast<int64_t>(i) * kTopkThreads;
-      w[i] = j < n ? sc[j] : 0;
+// 1. per (unit, block): min and max of the chunk's scores
+__global__ __launch_bounds__(kTkBlock) void topk_range_kernel(const int64_t *__restrict__ scores, int64_t n,
+                                                              int nbu, int64_t ch,
+                                                              unsigned long long *__restrict__ mm) {
+  __shared__ unsigned long long red[2 * kTkBlock / 64];
+  const int unit = blockIdx.x / nbu, blk = blockIdx.x % nbu;
+  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
+  const int64_t c0 = blk * ch;
+  const int64_t c1 = c0 + ch < n ? c0 + ch : n;
+  unsigned long long mn = ~0ull, mx = 0;
+  for (int64_t j = c0 + threadIdx.x; j < c1; j += kTkBlock) {
+    const unsigned long long u = ordered(sc[j]);
+    mn = u < mn ? u : mn;
+    mx = u > mx ? u : mx;
+  }
+  block_minmax(mn, mx, red);
+  if (threadIdx.x == 0) {
+    mm[2 * (static_cast<int64_t>(unit) * nbu + blk)] = mn;
+    mm[2 * (static_cast<int64_t>(unit) * nbu + blk) + 1] = mx;
+  }
+}
+
+// 2. per (unit, block): the chunk's keys and the histogram of their top 11 bits
+__global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__restrict__ scores, int64_t n,
+                                                             int nbu, int64_t ch,
+                                                             const unsigned long long *__restrict__ mm,
+                                                             uint32_t *__restrict__ keys,
+                                                             uint32_t *__restrict__ bhist) {
+  __shared__ uint32_t h[kTkBlock / 64][kBins];
+  __shared__ unsigned long long red[2];
+  const int unit = blockIdx.x / nbu, blk = blockIdx.x % nbu;
+  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
+  uint32_t *kk = keys + static_cast<int64_t>(unit) * key_stride(n);
+  for (int i = threadIdx.x; i < (kTkBlock / 64) * kBins; i += kTkBlock) (&h[0][0])[i] = 0u;
+  unsigned long long base;
+  int shift;
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * nbu, nbu, base, shift, red);
+  const int64_t c0 = blk * ch;
+  const int64_t c1 = c0 + ch < n ? c0 + ch : n;
+  uint32_t *wh = h[threadIdx.x >> 6];
+  for (int64_t jb = c0; jb < c0 + ch; jb += kTkBlock) {     // same trip count in every thread
+    const int64_t j = jb + threadIdx.x;
+    const bool ok = j < c1;
+    uint32_t key = 0;
+    if (ok) {
+      key = 1u + static_cast<uint32_t>((ordered(sc[j]) - base) >> shift);
+      kk[j] = key;
     }
+    hist_add(wh, ok, key >> 21);
+  }
+  __syncthreads();
+  uint32_t *bh = bhist + (static_cast<int64_t>(unit) * nbu + blk) * kBins;
+  for (int b = threadIdx.x; b < kBins; b += kTkBlock) bh[b] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+}
+
+// 3. One workgroup per unit. Thread t owns positions [t P, t P + P), P a
+// multiple of 4. LK (n <= kLdsKeys): the keys are loaded once into LDS;
+// otherwise every pass streams them from the workspace in batches of kRun
+// with 16-byte loads. The first digit comes from the block histograms. When
+// its bucket holds at most kSmallBucket keys, the bucket's (score, position)
+// pairs are collected and the k_rem-th of them is found by ranking; the
+// selection is then a predicate on (digit, score, position), counted, scanned
+// and written in order. Larger buckets take the radix path below.
+template <bool LK>
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t *__restrict__ scores,
+                                                                   uint32_t *__restrict__ keys,
+                                                                   const uint32_t *__restrict__ bhist,
+                                                                   const unsigned long long *__restrict__ mm,
+                                                                   int64_t n, int nbu, int k_top,
+                                                                   int32_t *__restrict__ idx_out) {
+  __shared__ TopkShared<LK> sh;
+  const int unit = blockIdx.x;
+  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
+  const int64_t nst = key_stride(n);
+  uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
+  int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
+  if (k_top == 0) return;
+  uint32_t *wh = sh.u.whist[threadIdx.x >> 7];
+  const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // wave-uniform
+  const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
+  const int64_t j1 = j0 + P < n ? j0 + P : n;
+
+  // the first digit from the block histograms (every load in flight at
+  // once) and, LK, the thread's keys into LDS
+  {
+    const uint32_t *bh = bhist + static_cast<int64_t>(unit) * nbu * kBins;
+    for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
+      uint32_t v[kTkMaxBlocks];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int64_t j = j0 + static_cast<int64_t>(i) * kTopkThreads;
-      if (j < n) {
-        const uint32_t key = static_cast<uint32_t>(off(w[i]) >> shift);
-        if constexpr (IN_LDS) lkeys[pad_slot(j)] = key; else gk[j] = key;
+      for (int blk = 0; blk < kTkMaxBlocks; ++blk) v[blk] = blk < nbu ? bh[static_cast<int64_t>(blk) * kBins + b] : 0u;
+      uint32_t t = 0;
+#pragma unroll
+      for (int blk = 0; blk < kTkMaxBlocks; ++blk) t += v[blk];
+      sh.hist[b] = t;
+    }
+  }
+  if constexpr (LK) {
+#pragma unroll
+    for (int i = 0; i < kRun / 4; ++i) {
+      const int64_t j = j0 + 4 * i;                                   // j0: a multiple of 4
+      if (j < j1) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(gk + j);
+        sh.u.lkeys[pad_slot(j)] = v.x;
+        if (j + 1 < j1) sh.u.lkeys[pad_slot(j + 1)] = v.y;
+        if (j + 2 < j1) sh.u.lkeys[pad_slot(j + 2)] = v.z;
+        if (j + 3 < j1) sh.u.lkeys[pad_slot(j + 3)] = v.w;
       }
     }
   }
+  if (threadIdx.x == 0) sh.bcnt = 0;
+  if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
   __syncthreads();
-  auto key_at = [&](int64_t j) -> uint32_t {
-    if constexpr (IN_LDS) return lkeys[pad_slot(j)]; else return gk[j];
+  int k_rem = k_top, eq = 0;
+  uint32_t prefix = static_cast<uint32_t>(find_digit(kBins, &k_rem, &eq, sh)) << 21;
+  uint32_t pmask = 0x7FFu << 21;
+
+  // visit(j, key, valid) streamed from the workspace, batch by batch; the
+  // trip count is the same for every thread (P is uniform), so the body may
+  // use wave-wide operations
+  auto for_own_ws = [&](auto &&visit) {
+#pragma unroll 1
+    for (int64_t c0 = 0; c0 < P; c0 += kRun) {
+      const int64_t b0 = threadIdx.x * P + c0;          // a multiple of 4
+      uint32_t kv[kRun];
+#pragma unroll
+      for (int i = 0; i < kRun / 4; ++i) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (b0 + 4 * i < nst) v = *reinterpret_cast<const uint4 *>(gk + b0 + 4 * i);
+        kv[4 * i] = v.x; kv[4 * i + 1] = v.y; kv[4 * i + 2] = v.z; kv[4 * i + 3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < kRun; ++i) visit(b0 + i, kv[i], b0 + i < j1);
+    }
+  };
+  // the fast path's visits: from LDS (no wave-wide operations in the body)
+  auto for_own = [&](auto &&visit) {
+    if constexpr (LK) {
+#pragma unroll 4
+      for (int64_t j = j0; j < j1; ++j) visit(j, sh.u.lkeys[pad_slot(j)], true);
+    } else {
+      for_own_ws(visit);
+    }
   };
 
-  // 3. radix select on the keys: four 8-bit digits
-  int k_rem = k_top, eq = 0;
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t *wh = sh.whist[threadIdx.x >> 6];
-  for (int sft = 24; sft >= 0; sft -= kDigitBits) {
+  if (eq <= kSmallBucket) {                     // eq: from LDS, uniform
+    const uint32_t d1 = prefix >> 21;
+    for_own([&](int64_t j, uint32_t key, bool ok) {
+      if (ok && (key >> 21) == d1) {
+        const int slot = atomicAdd(&sh.bcnt, 1);
+        sh.bsc[slot] = sc[j];
+        sh.bpos[slot] = static_cast<int>(j);
+      }
+    });
+    __syncthreads();
+    // rank of each member in the order (score descending, position
+    // ascending): parts = 1024 / eq threads share a member's comparisons
+    {
+      const int parts = kTopkThreads / eq;
+      const int e = static_cast<int>(threadIdx.x) / parts;
+      const int part = static_cast<int>(threadIdx.x) % parts;
+      if (e < eq) {
+        const long long ms = sh.bsc[e];
+        const int mp = sh.bpos[e];
+        int r = 0;
+        for (int i = part; i < eq; i += parts) {
+          const long long si = sh.bsc[i];
+          r += (si > ms) || (si == ms && sh.bpos[i] < mp);
+        }
+        if (r) atomicAdd(&sh.rank[e], r);
+      }
+    }
+    __syncthreads();
+    // each member's decision goes into its key: all ones (above every real
+    // key, at most 2^31) to take it, 0 to drop it; the passes below then need
+    // no scores
+    if (static_cast<int>(threadIdx.x) < eq) {
+      const uint32_t mark = sh.rank[threadIdx.x] < k_rem ? 0xFFFFFFFFu : 0u;
+      const int64_t j = sh.bpos[threadIdx.x];
+      if constexpr (LK) sh.u.lkeys[pad_slot(j)] = mark;
+      else gk[j] = mark;
+    }
+    if constexpr (!LK) __threadfence_block();
+    __syncthreads();
+    auto take_it = [&](int64_t, uint32_t key) -> bool { return key == 0xFFFFFFFFu || (key >> 21) > d1; };
+    int cnt = 0;
+    for_own([&](int64_t j, uint32_t key, bool ok) { cnt += ok && take_it(j, key); });
+    int tot;
+    int pos = block_exclusive_scan(cnt, sh.scan, &tot);
+    for_own([&](int64_t j, uint32_t key, bool ok) {
+      if (ok && take_it(j, key) && pos < k_top) out[pos++] = static_cast<int32_t>(j);
+    });
+    return;
+  }
+
+  unsigned long long base;
+  int shift;
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * nbu, nbu, base, shift, sh.mm);
+  auto off = [&](long long sv) -> unsigned long long { return ordered(sv) - base; };
+
+  // the other two digits: bits 10..20, then 0..9
+#pragma unroll 1
+  for (int ps = 0; ps < 2; ++ps) {
+    const int sft = ps == 0 ? 10 : 0;
+    const int nbt = ps == 0 ? 11 : 10;
+    const uint32_t dm = (1u << nbt) - 1u;
     clear_whist(sh);
     __syncthreads();
-#pragma unroll 4
-    for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-      const uint32_t key = key_at(j);
-      if ((key & pmask) == prefix) atomicAdd(&wh[(key >> sft) & (kBins - 1)], 1u);
-    }
+    for_own_ws([&](int64_t, uint32_t key, bool ok) {
+      hist_add(wh, ok && (key & pmask) == prefix, (key >> sft) & dm);
+    });
     __syncthreads();
     reduce_whist(sh);
     __syncthreads();
-    const int d = find_digit(kBins, &k_rem, &eq, sh);
+    const int d = find_digit(1 << nbt, &k_rem, &eq, sh);
     prefix |= static_cast<uint32_t>(d) << sft;
-    pmask |= static_cast<uint32_t>(kBins - 1) << sft;
+    pmask |= dm << sft;
   }
-  const uint32_t kappa = prefix;   // key of the k_top-th largest
+  const uint32_t kappa = prefix;   // key of the k_top-th largest (>= 1)
   int take = k_rem;                // taken among key == kappa
-
   // 4. members of the kappa bucket differ only in the low `shift` bits:
   //    select on those bits when the bucket is not taken whole
   const bool refine = eq > take && shift > 0;
@@ -472,12 +735,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__res
       const int sh2 = top - bits;
       clear_whist(sh);
       __syncthreads();
-      for (int64_t j = threadIdx.x; j < n; j += kTopkThreads) {
-        if (key_at(j) == kappa) {
+      for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+        bool m = false;
+        uint32_t d = 0;
+        if (ok && key == kappa) {
           const unsigned long long lo = off(sc[j]) & lbits;
-          if ((lo & lowmask) == lowpre) atomicAdd(&wh[(lo >> sh2) & ((1u << bits) - 1u)], 1u);
+          m = (lo & lowmask) == lowpre;
+          d = static_cast<uint32_t>(lo >> sh2) & ((1u << bits) - 1u);
         }
-      }
+        hist_add(wh, m, d);
+      });
       __syncthreads();
       reduce_whist(sh);
       __syncthreads();
@@ -490,7 +757,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__res
   }
   // every candidate above the threshold is taken; of those equal to it, the
   // first `take` by position
-  const unsigned long long tau = (static_cast<unsigned long long>(kappa) << shift) + low;
+  const unsigned long long tau = (static_cast<unsigned long long>(kappa - 1u) << shift) + low;
   auto is_tie = [&](int64_t j, uint32_t key) -> bool {
     if (key != kappa) return false;
     return refine ? (off(sc[j]) == tau) : true;
@@ -500,38 +767,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const int64_t *__res
     return refine && off(sc[j]) > tau;
   };
 
-  // 5. in-order compaction over contiguous per-thread runs
-  const int64_t per = (n + kTopkThreads - 1) / kTopkThreads;
-  const int64_t j0 = threadIdx.x * per < n ? threadIdx.x * per : n;
-  const int64_t j1 = (j0 + per) < n ? (j0 + per) : n;
+  // 5. in-order compaction over the contiguous runs
   int ties = 0, sure = 0;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t key = key_at(j);
-    ties += is_tie(j, key);
-    sure += is_sure(j, key);
-  }
+  for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+    if (ok) {
+      ties += is_tie(j, key);
+      sure += is_sure(j, key);
+    }
+  });
   int tot;
   const int tie_before = block_exclusive_scan(ties, sh.scan, &tot);
   int sel = sure;
   {
     int r = tie_before;
-    for (int64_t j = j0; j < j1; ++j)
-      if (is_tie(j, key_at(j))) { sel += (r < take); ++r; }
+    for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+      if (ok && is_tie(j, key)) { sel += (r < take); ++r; }
+    });
   }
   int pos = block_exclusive_scan(sel, sh.scan, &tot);
   {
     int r = tie_before;
-    for (int64_t j = j0; j < j1; ++j) {
-      const uint32_t key = key_at(j);
+    for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+      if (!ok) return;
       bool sj = is_sure(j, key);
       if (is_tie(j, key)) { sj = r < take; ++r; }
       if (sj && pos < k_top) out[pos++] = static_cast<int32_t>(j);
-    }
+    });
   }
 }
 
+void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, int64_t n, int k_top,
+                 int32_t *idx_out) {
+  const TopkChunks c = topk_chunks(n);
+  const TopkWs L = topk_ws(units, n);
+  uint8_t *w8 = static_cast<uint8_t *>(tws);
+  unsigned long long *mm = reinterpret_cast<unsigned long long *>(w8 + L.mm);
+  uint32_t *bh = reinterpret_cast<uint32_t *>(w8 + L.hist);
+  uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + L.keys);
+  const unsigned nb = static_cast<unsigned>(units) * c.nbu;
+  hipLaunchKernelGGL(topk_range_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, mm);
+  hipLaunchKernelGGL(topk_keys_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, mm, keys, bh);
+  if (n <= kLdsKeys)
+    hipLaunchKernelGGL((topk_select_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm, n,
+                       c.nbu, k_top, idx_out);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm,
+                       n, c.nbu, k_top, idx_out);
+}
+
 // ---------------------------------------------------------------- workspace
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct DetWs {
   size_t scores, qs, keys, total;
 };
@@ -540,7 +824,7 @@ DetWs det_ws(int B, int Hkv, int64_t cand_end) {
   L.scores = 0;
   L.qs = align_up(static_cast<size_t>(B) * Hkv * cand_end * sizeof(int64_t), 256);
   L.keys = align_up(L.qs + static_cast<size_t>(B) * Hkv * 128 * sizeof(double), 256);
-  L.total = L.keys + (cand_end > kLdsKeys ? static_cast<size_t>(B) * Hkv * cand_end * 4 : 0);
+  L.total = L.keys + topk_ws(static_cast<int64_t>(B) * Hkv, cand_end).total;
   return L;
 }
 
@@ -830,8 +1114,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
   if (detect) {
     if (!k || (k_top > 0 && !idx_out)) return fail(HQ_ERR_INVALID_ARG, "hq_detect_vlines: null k or idx_out");
     const DetWs L = det_ws(B, Hkv, cand_end);
-    const bool need_ws = score_out == nullptr || method == HQ_DETECT_QSUM || cand_end > kLdsKeys;
-    const size_t need = need_ws ? L.total : 0;
+    const size_t need = L.total;
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(HQ_ERR_WORKSPACE, "hq_detect_vlines: workspace needs %zu bytes, got %zu", need, ws_bytes);
     if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(q_acc) % 16)
@@ -890,11 +1173,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
     if (s != HQ_OK) return s;
   }
   if (k_top > 0) {
-    uint32_t *gkeys = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + L.keys);
-    if (cand_end <= kLdsKeys)
-      hipLaunchKernelGGL((topk_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
-    else
-      hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    launch_topk(st, units, scores, static_cast<uint8_t *>(ws) + L.keys, cand_end, k_top, idx_out);
     hq_status s = check_launch("hq_detect_vlines (top-k)");
     if (s != HQ_OK) return s;
   }
@@ -969,11 +1248,7 @@ extern "C" hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_d
     if (s != HQ_OK) return s;
   }
   if (k_top > 0) {
-    uint32_t *gkeys = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + L.keys);
-    if (cand_end <= kLdsKeys)
-      hipLaunchKernelGGL((topk_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
-    else
-      hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    launch_topk(st, units, scores, static_cast<uint8_t *>(ws) + L.keys, cand_end, k_top, idx_out);
     hq_status s = check_launch("hq_detect_vlines_cache (top-k)");
     if (s != HQ_OK) return s;
   }
@@ -997,7 +1272,7 @@ MassWs mass_ws(int B, int Hq, int Hkv, int R, int64_t k_rows, int64_t cand_end) 
   L.part = align_up(static_cast<size_t>(units) * cand_end * sizeof(int64_t), 256);
   L.stats = align_up(L.part + static_cast<size_t>(units) * M * L.nblk * sizeof(float2), 256);
   L.keys = align_up(L.stats + static_cast<size_t>(units) * M * sizeof(float2), 256);
-  L.total = L.keys + (cand_end > kLdsKeys ? static_cast<size_t>(units) * cand_end * 4 : 0);
+  L.total = L.keys + topk_ws(units, cand_end).total;
   return L;
 }
 }  // namespace
@@ -1081,11 +1356,7 @@ extern "C" hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dt
     if (s != HQ_OK) return s;
   }
   if (k_top > 0) {
-    uint32_t *gkeys = reinterpret_cast<uint32_t *>(w8 + L.keys);
-    if (cand_end <= kLdsKeys)
-      hipLaunchKernelGGL((topk_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
-    else
-      hipLaunchKernelGGL((topk_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, gkeys, cand_end, k_top, idx_out);
+    launch_topk(st, units, scores, w8 + L.keys, cand_end, k_top, idx_out);
     hq_status s = check_launch("hq_detect_vlines_mass (top-k)");
     if (s != HQ_OK) return s;
   }
