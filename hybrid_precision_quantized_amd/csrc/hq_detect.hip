@@ -21,9 +21,9 @@
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
-//  * top-k           three launches. topk_range: many blocks per unit, each
-//    the min and max of a chunk of the scores. topk_keys: the same blocks
-//    reduce the unit's partial ranges, write the 32-bit keys
+//  * top-k           every score kernel also writes the min and max of the
+//    256 scores each of its blocks produced. topk_keys: many blocks per
+//    unit reduce the unit's partial ranges, write the 32-bit keys
 //    1 + (score - min) >> shift and a histogram of the keys' top 11 bits per
 //    block. topk_select: one workgroup per unit sums the block histograms
 //    into the first digit. A boundary bucket of at most 1024 keys is ranked
@@ -41,6 +41,36 @@ template <int DT>
 __device__ __forceinline__ float load_half(uint32_t h) {
   if constexpr (DT == HQ_BF16) return bf16_to_f32(h);
   else return f16_to_f32(h);
+}
+
+// Range of the scores a 256-thread block wrote, as order-preserving
+// unsigned values (score ^ sign bit): the top-k reduces these partials
+// instead of reading every score once more. Every thread of the block calls.
+__device__ __forceinline__ unsigned long long ordered_score(long long v) {
+  return static_cast<unsigned long long>(v) ^ 0x8000000000000000ull;
+}
+__device__ __forceinline__ void block_range_out(unsigned long long mn, unsigned long long mx,
+                                                unsigned long long *dst) {
+  __shared__ unsigned long long red[8];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+    mn = a < mn ? a : mn;
+    mx = c > mx ? c : mx;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * (threadIdx.x >> 6)] = mn;
+    red[2 * (threadIdx.x >> 6) + 1] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && dst) {
+    for (int i = 1; i < static_cast<int>(blockDim.x) / 64; ++i) {
+      mn = red[2 * i] < mn ? red[2 * i] : mn;
+      mx = red[2 * i + 1] > mx ? red[2 * i + 1] : mx;
+    }
+    dst[0] = mn;
+    dst[1] = mx;
+  }
 }
 
 // ---------------------------------------------------------------- accumulate
@@ -85,7 +115,8 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
                                                           const uint16_t *__restrict__ k, int Hq,
                                                           int Hkv, int R, int64_t k_rows,
                                                           int64_t cand_end, int tiles_per_unit,
-                                                          int64_t *__restrict__ scores) {
+                                                          int64_t *__restrict__ scores,
+                                                          unsigned long long *__restrict__ mm) {
   constexpr int KC = D / 16;                       // k-chunks of 16
   constexpr int ROWV = D / 8;                      // uint4 per row
   constexpr int PER_T = kStageRows * ROWV / 256;   // uint4 per thread per stage
@@ -164,14 +195,21 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
     __syncthreads();
   }
   // column = lane & 31; this lane holds 16 of the 32 row residues
+  unsigned long long mn = ~0ull, mx = 0;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     long long s = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += __double2ll_rn(static_cast<double>(acc[t][i]) * 65536.0);
     const long long other = __shfl_xor(s, 32, 64);
-    if (half == 0 && col_ok[t]) scores[static_cast<int64_t>(unit) * cand_end + col[t]] = s + other;
+    if (half == 0 && col_ok[t]) {
+      scores[static_cast<int64_t>(unit) * cand_end + col[t]] = s + other;
+      const unsigned long long u = ordered_score(s + other);
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
   }
+  block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * blocks_per_unit + cb) : nullptr);
 }
 
 // ---------------------------------------------------------------- QSUM form
@@ -228,7 +266,8 @@ __global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_a
 template <int D, int DT>
 __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, const double *__restrict__ qs,
                                                    int64_t k_rows, int64_t cand_end, int chunks_per_unit,
-                                                   int64_t *__restrict__ scores) {
+                                                   int64_t *__restrict__ scores,
+                                                   unsigned long long *__restrict__ mm) {
   constexpr int LPR = D / 8;                // lanes per row
   constexpr int RPB = 256 / LPR;            // rows per block step
   constexpr int CHUNK = 256;                // rows per block
@@ -239,6 +278,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, c
   double qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = qs[static_cast<int64_t>(unit) * D + sub * 8 + e];
+  unsigned long long mn = ~0ull, mx = 0;
   for (int64_t r = r0 + rowi; r < r0 + CHUNK; r += RPB) {
     const bool ok = r < cand_end;
     double acc = 0.0;
@@ -270,9 +310,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, c
     }
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (ok && sub == 0)
-      scores[static_cast<int64_t>(unit) * cand_end + r] = __double2ll_rn(acc * 65536.0);
+    if (ok && sub == 0) {
+      const long long v = __double2ll_rn(acc * 65536.0);
+      scores[static_cast<int64_t>(unit) * cand_end + r] = v;
+      const unsigned long long u = ordered_score(v);
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
   }
+  block_range_out(mn, mx, mm ? mm + 2 * static_cast<int64_t>(blockIdx.x) : nullptr);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -435,6 +481,9 @@ __host__ __device__ inline TopkChunks topk_chunks(int64_t n) {
   c.ch = (((n + nbu - 1) / nbu) + 3) & ~3LL;
   return c;
 }
+// Partial score ranges per unit: one per 256 candidates, written by the
+// score kernels (every one of them covers 256 candidates per block).
+__host__ __device__ inline int topk_partials(int64_t n) { return static_cast<int>((n + 255) / 256); }
 // workspace of the top-k: partial ranges, block histograms, keys
 struct TopkWs {
   size_t mm, hist, keys, total;
@@ -443,10 +492,14 @@ TopkWs topk_ws(int64_t units, int64_t n) {
   const TopkChunks c = topk_chunks(n);
   TopkWs L{};
   L.mm = 0;
-  L.hist = align_up(static_cast<size_t>(units) * c.nbu * 2 * sizeof(unsigned long long), 256);
+  L.hist = align_up(static_cast<size_t>(units) * topk_partials(n) * 2 * sizeof(unsigned long long), 256);
   L.keys = align_up(L.hist + static_cast<size_t>(units) * c.nbu * kBins * sizeof(uint32_t), 256);
   L.total = align_up(L.keys + static_cast<size_t>(units) * key_stride(n) * sizeof(uint32_t), 256);
   return L;
+}
+// where the score kernels put their partial ranges
+unsigned long long *topk_mm(void *tws, int64_t units, int64_t n) {
+  return reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(tws) + topk_ws(units, n).mm);
 }
 
 __device__ __forceinline__ unsigned long long ordered(long long v) {
@@ -504,31 +557,9 @@ __device__ __forceinline__ void unit_range(const unsigned long long *mm, int nbu
   __syncthreads();
 }
 
-// 1. per (unit, block): min and max of the chunk's scores
-__global__ __launch_bounds__(kTkBlock) void topk_range_kernel(const int64_t *__restrict__ scores, int64_t n,
-                                                              int nbu, int64_t ch,
-                                                              unsigned long long *__restrict__ mm) {
-  __shared__ unsigned long long red[2 * kTkBlock / 64];
-  const int unit = blockIdx.x / nbu, blk = blockIdx.x % nbu;
-  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
-  const int64_t c0 = blk * ch;
-  const int64_t c1 = c0 + ch < n ? c0 + ch : n;
-  unsigned long long mn = ~0ull, mx = 0;
-  for (int64_t j = c0 + threadIdx.x; j < c1; j += kTkBlock) {
-    const unsigned long long u = ordered(sc[j]);
-    mn = u < mn ? u : mn;
-    mx = u > mx ? u : mx;
-  }
-  block_minmax(mn, mx, red);
-  if (threadIdx.x == 0) {
-    mm[2 * (static_cast<int64_t>(unit) * nbu + blk)] = mn;
-    mm[2 * (static_cast<int64_t>(unit) * nbu + blk) + 1] = mx;
-  }
-}
-
-// 2. per (unit, block): the chunk's keys and the histogram of their top 11 bits
+// 1. per (unit, block): the chunk's keys and the histogram of their top 11 bits
 __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__restrict__ scores, int64_t n,
-                                                             int nbu, int64_t ch,
+                                                             int nbu, int64_t ch, int np,
                                                              const unsigned long long *__restrict__ mm,
                                                              uint32_t *__restrict__ keys,
                                                              uint32_t *__restrict__ bhist) {
@@ -540,7 +571,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
   for (int i = threadIdx.x; i < (kTkBlock / 64) * kBins; i += kTkBlock) (&h[0][0])[i] = 0u;
   unsigned long long base;
   int shift;
-  unit_range(mm + 2 * static_cast<int64_t>(unit) * nbu, nbu, base, shift, red);
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, red);
   const int64_t c0 = blk * ch;
   const int64_t c1 = c0 + ch < n ? c0 + ch : n;
   uint32_t *wh = h[threadIdx.x >> 6];
@@ -559,7 +590,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
   for (int b = threadIdx.x; b < kBins; b += kTkBlock) bh[b] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
 }
 
-// 3. One workgroup per unit. Thread t owns positions [t P, t P + P), P a
+// 2. One workgroup per unit. Thread t owns positions [t P, t P + P), P a
 // multiple of 4. LK (n <= kLdsKeys): the keys are loaded once into LDS;
 // otherwise every pass streams them from the workspace in batches of kRun
 // with 16-byte loads. The first digit comes from the block histograms. When
@@ -572,7 +603,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
                                                                    uint32_t *__restrict__ keys,
                                                                    const uint32_t *__restrict__ bhist,
                                                                    const unsigned long long *__restrict__ mm,
-                                                                   int64_t n, int nbu, int k_top,
+                                                                   int64_t n, int nbu, int np, int k_top,
                                                                    int32_t *__restrict__ idx_out) {
   __shared__ TopkShared<LK> sh;
   const int unit = blockIdx.x;
@@ -700,7 +731,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
 
   unsigned long long base;
   int shift;
-  unit_range(mm + 2 * static_cast<int64_t>(unit) * nbu, nbu, base, shift, sh.mm);
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, sh.mm);
   auto off = [&](long long sv) -> unsigned long long { return ordered(sv) - base; };
 
   // the other two digits: bits 10..20, then 0..9
@@ -796,6 +827,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
   }
 }
 
+// The score kernels have written their partial ranges to topk_mm(tws, units, n).
 void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, int64_t n, int k_top,
                  int32_t *idx_out) {
   const TopkChunks c = topk_chunks(n);
@@ -804,15 +836,15 @@ void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, in
   unsigned long long *mm = reinterpret_cast<unsigned long long *>(w8 + L.mm);
   uint32_t *bh = reinterpret_cast<uint32_t *>(w8 + L.hist);
   uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + L.keys);
+  const int np = topk_partials(n);
   const unsigned nb = static_cast<unsigned>(units) * c.nbu;
-  hipLaunchKernelGGL(topk_range_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, mm);
-  hipLaunchKernelGGL(topk_keys_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, mm, keys, bh);
+  hipLaunchKernelGGL(topk_keys_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, np, mm, keys, bh);
   if (n <= kLdsKeys)
     hipLaunchKernelGGL((topk_select_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm, n,
-                       c.nbu, k_top, idx_out);
+                       c.nbu, np, k_top, idx_out);
   else
     hipLaunchKernelGGL((topk_select_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm,
-                       n, c.nbu, k_top, idx_out);
+                       n, c.nbu, np, k_top, idx_out);
 }
 
 // ---------------------------------------------------------------- workspace
@@ -838,7 +870,8 @@ __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restric
                                                         const uint32_t *__restrict__ sz,
                                                         const double *__restrict__ qs, int64_t t_cap,
                                                         int64_t cand_end, int chunks_per_unit,
-                                                        int64_t *__restrict__ scores) {
+                                                        int64_t *__restrict__ scores,
+                                                        unsigned long long *__restrict__ mm) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
   constexpr int CHUNK = 256;
@@ -850,6 +883,7 @@ __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restric
   double qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = qs[static_cast<int64_t>(unit) * D + sub * 8 + e];
+  unsigned long long mn = ~0ull, mx = 0;
   for (int64_t r = r0 + rowi; r < r0 + CHUNK; r += RPB) {
     const bool ok = r < cand_end;
     double acc = 0.0;
@@ -867,9 +901,15 @@ __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restric
     }
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (ok && sub == 0)
-      scores[static_cast<int64_t>(unit) * cand_end + r] = __double2ll_rn(acc * 65536.0);
+    if (ok && sub == 0) {
+      const long long v = __double2ll_rn(acc * 65536.0);
+      scores[static_cast<int64_t>(unit) * cand_end + r] = v;
+      const unsigned long long u = ordered_score(v);
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
   }
+  block_range_out(mn, mx, mm ? mm + 2 * static_cast<int64_t>(blockIdx.x) : nullptr);
 }
 
 // ---------------------------------------------------------------- attention-mass form
@@ -1006,7 +1046,8 @@ __global__ __launch_bounds__(256) void mass_cols_kernel(const uint16_t *__restri
                                                         const uint16_t *__restrict__ k, int Hq, int Hkv, int R,
                                                         int64_t k_rows, int64_t cand_end, int blocks_per_unit,
                                                         float cs, const float2 *__restrict__ stats,
-                                                        int64_t *__restrict__ scores) {
+                                                        int64_t *__restrict__ scores,
+                                                        unsigned long long *__restrict__ mm) {
   constexpr int KC = D / 16, ROWV = D / 8, PER_T = kStageRows * ROWV / 256;
   __shared__ uint16_t qs[kStageRows][D + kRowPad];
   __shared__ float2 rs[kStageRows];
@@ -1068,13 +1109,19 @@ __global__ __launch_bounds__(256) void mass_cols_kernel(const uint16_t *__restri
     }
     __syncthreads();
   }
+  unsigned long long mn = ~0ull, mx = 0;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float c = cols[t] + __shfl_xor(cols[t], 32, 64);
-    if (half == 0 && col[t] < cand_end)
-      scores[static_cast<int64_t>(unit) * cand_end + col[t]] =
-          __double2ll_rn(static_cast<double>(c) * 4194304.0);   // units of 2^-22
+    if (half == 0 && col[t] < cand_end) {
+      const long long v = __double2ll_rn(static_cast<double>(c) * 4194304.0);   // units of 2^-22
+      scores[static_cast<int64_t>(unit) * cand_end + col[t]] = v;
+      const unsigned long long u = ordered_score(v);
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
   }
+  block_range_out(mn, mx, mm ? mm + 2 * static_cast<int64_t>(blockIdx.x) : nullptr);
 }
 
 }  // namespace
@@ -1135,6 +1182,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
   const DetWs L = det_ws(B, Hkv, cand_end);
   int64_t *scores = score_out ? score_out : reinterpret_cast<int64_t *>(static_cast<uint8_t *>(ws) + L.scores);
   const int units = B * Hkv;
+  unsigned long long *tmm = k_top > 0 ? topk_mm(static_cast<uint8_t *>(ws) + L.keys, units, cand_end) : nullptr;
   if (cand_end > 0) {
     if (method == HQ_DETECT_MATMUL) {
       const int tiles = static_cast<int>((cand_end + 31) / 32);
@@ -1143,14 +1191,14 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
       const uint16_t *kk = static_cast<const uint16_t *>(k);
       if (D == 128) {
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores);
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores);
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       } else {
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores);
+          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores);
+          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       }
     } else {
       double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
@@ -1161,7 +1209,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
       }
       const int cpu = static_cast<int>((cand_end + 255) / 256);
       const dim3 grid(static_cast<unsigned>(units * cpu));
-#define HQ_GEMV(DD, TT) hipLaunchKernelGGL((gemv_kernel<DD, TT>), grid, dim3(256), 0, st, k, qs, k_rows, cand_end, cpu, scores)
+#define HQ_GEMV(DD, TT) hipLaunchKernelGGL((gemv_kernel<DD, TT>), grid, dim3(256), 0, st, k, qs, k_rows, cand_end, cpu, scores, tmm)
       if (D == 128) {
         if (dtype == HQ_F32) HQ_GEMV(128, HQ_F32); else if (dtype == HQ_BF16) HQ_GEMV(128, HQ_BF16); else HQ_GEMV(128, HQ_F16);
       } else {
@@ -1230,6 +1278,7 @@ extern "C" hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_d
   if (!detect) { clear_error(); return HQ_OK; }
   int64_t *scores = score_out ? score_out : reinterpret_cast<int64_t *>(static_cast<uint8_t *>(ws) + L.scores);
   const int units = B * Hkv;
+  unsigned long long *tmm = k_top > 0 ? topk_mm(static_cast<uint8_t *>(ws) + L.keys, units, cand_end) : nullptr;
   if (cand_end > 0) {
     double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
     switch (dtype) {
@@ -1241,9 +1290,9 @@ extern "C" hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_d
     const dim3 grid(static_cast<unsigned>(units * cpu));
     const uint32_t *szw = reinterpret_cast<const uint32_t *>(kv->k_sz);
     if (D == 128)
-      hipLaunchKernelGGL((gemv_int4_kernel<128>), grid, dim3(256), 0, st, kv->k_codes, szw, qs, kv->t_cap, cand_end, cpu, scores);
+      hipLaunchKernelGGL((gemv_int4_kernel<128>), grid, dim3(256), 0, st, kv->k_codes, szw, qs, kv->t_cap, cand_end, cpu, scores, tmm);
     else
-      hipLaunchKernelGGL((gemv_int4_kernel<64>), grid, dim3(256), 0, st, kv->k_codes, szw, qs, kv->t_cap, cand_end, cpu, scores);
+      hipLaunchKernelGGL((gemv_int4_kernel<64>), grid, dim3(256), 0, st, kv->k_codes, szw, qs, kv->t_cap, cand_end, cpu, scores, tmm);
     hq_status s = check_launch("hq_detect_vlines_cache (scores)");
     if (s != HQ_OK) return s;
   }
@@ -1330,6 +1379,7 @@ extern "C" hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dt
   float2 *part = reinterpret_cast<float2 *>(w8 + L.part);
   float2 *stats = reinterpret_cast<float2 *>(w8 + L.stats);
   const int units = B * Hkv;
+  unsigned long long *tmm = k_top > 0 ? topk_mm(w8 + L.keys, units, cand_end) : nullptr;
   const int M = (Hq / Hkv) * R;
   const float cs = (sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(D))) * 1.4426950408889634f;
   const uint16_t *qa = static_cast<const uint16_t *>(q_acc);
@@ -1344,7 +1394,7 @@ extern "C" hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dt
     hipLaunchKernelGGL(mass_merge_kernel, dim3((units * M + 3) / 4), dim3(256), 0, st, part,              \
                        units * M, nb1, cs, stats);                                                       \
     hipLaunchKernelGGL((mass_cols_kernel<DD, TT>), dim3(units * nb3), dim3(256), 0, st, qa, kk, Hq, Hkv,  \
-                       R, k_rows, cand_end, nb3, cs, stats, scores);                                      \
+                       R, k_rows, cand_end, nb3, cs, stats, scores, tmm);                                 \
   } while (0)
     if (D == 128) {
       if (dtype == HQ_BF16) HQ_MASS(128, HQ_BF16); else HQ_MASS(128, HQ_F16);
