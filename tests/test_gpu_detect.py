@@ -3,6 +3,8 @@ accumulation, exact int64 column scores and bit-exact index sets (both the
 MFMA matmul form and the summed-query form), on tie-heavy small cases and
 on the full GLM-4-9B-shaped (32 q / 2 kv heads, 32K) and
 Llama-3.1-8B-shaped (32 q / 8 kv heads, 32K) workloads."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -237,3 +239,63 @@ def test_detect_mass_full_workload(name):
     cover = np.mean([want_sc[0, h][got_idx[0, h]].sum() / (G * w.R) for h in range(w.Hkv)])
     cover16 = np.mean([want_sc[0, h][idx16[0, h]].sum() / (G * w.R) for h in range(w.Hkv)])
     say(f"   attention mass covered: mass set {cover:.3f}, logit-sum set {cover16:.3f}")
+
+
+def _pattern_case(values, k_top, method):
+    """Scores equal to (rows) * values[j] exactly: every query row is the
+    first unit vector and key j carries values[j] in channel 0, so the score
+    pattern (ties, skew, bucket sizes) is set by `values` alone."""
+    n = len(values)
+    B, Hq, Hkv, D, R = 1, 4, 1, 64, 2
+    q = np.zeros((B, Hq, R, D), np.float32)
+    q[..., 0] = 1.0
+    K = np.zeros((B, Hkv, n, D), np.float32)
+    K[0, 0, :, 0] = values
+    # the other channels meet zero query entries; on the 2^-4 grid so the
+    # oracle's exactness check holds
+    K[0, 0, :, 1:] = np.rint(np.random.default_rng(n).standard_normal((n, D - 1)) * 16) / 16
+    want_idx, want_sc = detect.detect(q, K, n, k_top)
+    got_idx, got_sc = _run(q, K, n, k_top, method, "bf16")
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+
+
+def _grid_values(rng, n, lo, hi):
+    return np.rint(rng.uniform(lo, hi, n) * 16).astype(np.float32) / 16
+
+
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("case", ["ties_small_bucket", "ties_large_bucket", "k_is_n", "k_is_1",
+                                  "all_equal", "threshold_in_lowest_bin", "threshold_in_top_bin"])
+def test_topk_score_patterns(method, case):
+    """Edge cases of the top-k's two paths: a boundary bucket of at most 1024
+    keys is ranked directly, a larger one goes through the remaining radix
+    digits; ties at the threshold go to the lower positions either way."""
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    n = 6000
+    v = _grid_values(rng, n, -8.0, 8.0)
+    k_top = 300
+    if case == "ties_small_bucket":       # 700 equal scores straddle the cut
+        tie = rng.choice(n, 700, replace=False)
+        v[v > 6.0] = 5.0
+        v[tie] = 6.0
+        k_top = 350
+    elif case == "ties_large_bucket":     # 2000 equal scores straddle the cut
+        tie = rng.choice(n, 2000, replace=False)
+        v[v > 6.0] = 5.0
+        v[tie] = 6.0
+        k_top = 1500
+    elif case == "k_is_n":
+        k_top = n
+    elif case == "k_is_1":
+        k_top = 1
+    elif case == "all_equal":
+        v[:] = 2.5
+        k_top = 37
+    elif case == "threshold_in_lowest_bin":   # almost everything selected
+        k_top = n - 3
+    elif case == "threshold_in_top_bin":      # only the largest few
+        v[rng.choice(n, 5, replace=False)] = 7.9375
+        k_top = 3
+    say(f"top-k pattern {case} method={method} n={n} k={k_top}")
+    _pattern_case(v, k_top, method)
