@@ -263,6 +263,102 @@ __global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_a
 }
 
 // 256 threads; lanes in groups of D/8 per key row (8 channels per lane).
+// The same column sums with the unit's query rows resident: all M <= 256
+// rows are staged into LDS once, then the block walks `gpb` groups of 256
+// columns (8 tiles of 32, two per wave), loading the next group's K
+// fragments into a second register set while the matrix core works on the
+// current one. Q is read from L2 once per gpb groups instead of once per
+// group, and the K stream overlaps the MFMAs. Each group writes its scores
+// and its score range (one partial per 256 candidates, as the top-k expects).
+constexpr int kResRows = 256;
+template <int D, int DT>
+__global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t *__restrict__ q_acc,
+                                                                 const uint16_t *__restrict__ k, int Hq,
+                                                                 int Hkv, int R, int64_t k_rows,
+                                                                 int64_t cand_end, int groups, int gpb,
+                                                                 int64_t *__restrict__ scores,
+                                                                 unsigned long long *__restrict__ mm) {
+  constexpr int KC = D / 16;
+  constexpr int ROWV = D / 8;
+  __shared__ uint16_t qs[kResRows][D + kRowPad];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int bpu = (groups + gpb - 1) / gpb;                   // blocks per unit
+  const int unit = blockIdx.x / bpu;
+  const int g0 = (blockIdx.x % bpu) * gpb;
+  const int g1 = g0 + gpb < groups ? g0 + gpb : groups;
+  const int G = Hq / Hkv;
+  const int b = unit / Hkv;
+  const int h = unit % Hkv;
+  const int M = G * R;                                        // <= kResRows
+  const int subs = (M + 31) / 32;
+  const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
+  const uint16_t *kunit = k + static_cast<int64_t>(unit) * k_rows * D;
+
+  // K fragments of group g: this lane's column of tiles (wave*2 + t) of the group
+  auto load_frag = [&](int g, uint4 (&kf)[2][KC]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t col = (static_cast<int64_t>(g) * 8 + wave * 2 + t) * 32 + (lane & 31);
+      const bool ok = col < cand_end;
+      const uint16_t *krow = kunit + (ok ? col : 0) * D;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[t][kc] = ok ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 kfa[2][KC], kfb[2][KC];
+  if (g0 < g1) load_frag(g0, kfa);
+  // all query rows into LDS (zero past M)
+  for (int idx = threadIdx.x; idx < kResRows * ROWV; idx += 256) {
+    const int row = idx / ROWV, c8 = idx % ROWV;
+    *reinterpret_cast<uint4 *>(&qs[row][c8 * 8]) =
+        row < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(row) * D + c8 * 8)
+                : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+
+  auto group = [&](int g, const uint4 (&kf)[2][KC], uint4 (&next)[2][KC]) {
+    if (g + 1 < g1) load_frag(g + 1, next);
+    f32x16 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+    for (int sub = 0; sub < subs; ++sub) {
+      const uint16_t *arow = &qs[sub * 32 + (lane & 31)][half * 8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * 16);
+        acc[0] = mfma32<DT>(a, kf[0][kc], acc[0]);
+        acc[1] = mfma32<DT>(a, kf[1][kc], acc[1]);
+      }
+    }
+    // column = lane & 31; this lane holds 16 of the 32 row residues
+    unsigned long long mn = ~0ull, mx = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t col = (static_cast<int64_t>(g) * 8 + wave * 2 + t) * 32 + (lane & 31);
+      long long sv = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv += __double2ll_rn(static_cast<double>(acc[t][i]) * 65536.0);
+      const long long other = __shfl_xor(sv, 32, 64);
+      if (half == 0 && col < cand_end) {
+        scores[static_cast<int64_t>(unit) * cand_end + col] = sv + other;
+        const unsigned long long u = ordered_score(sv + other);
+        mn = u < mn ? u : mn;
+        mx = u > mx ? u : mx;
+      }
+    }
+    block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * groups + g) : nullptr);
+  };
+  for (int g = g0; g < g1; g += 2) {
+    group(g, kfa, kfb);
+    if (g + 1 < g1) group(g + 1, kfb, kfa);
+  }
+}
+
 template <int D, int DT>
 __global__ __launch_bounds__(256) void gemv_kernel(const void *__restrict__ k, const double *__restrict__ qs,
                                                    int64_t k_rows, int64_t cand_end, int chunks_per_unit,
@@ -1189,7 +1285,20 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
       const int blocks = units * ((tiles + 7) / 8);
       const uint16_t *qa = static_cast<const uint16_t *>(q_acc);
       const uint16_t *kk = static_cast<const uint16_t *>(k);
-      if (D == 128) {
+      const int groups = (tiles + 7) / 8;                    // 256-column groups per unit
+      // groups per block: about two blocks per CU over the launch, at most
+      // 16. The resident form pays off once a block walks 4 or more groups
+      // (16 x 128K: column sums 1291 -> 1148 us); with 2 groups per block
+      // (1 x 32K, 8 KV heads) its longer blocks lose (28.9 -> 31.1 us).
+      int gpb = static_cast<int>((static_cast<int64_t>(units) * groups) / 512);
+      gpb = gpb < 1 ? 1 : (gpb > 16 ? 16 : gpb);
+      if (D == 128 && (Hq / Hkv) * R <= kResRows && gpb >= 4) {
+        const int rblocks = units * ((groups + gpb - 1) / gpb);
+        if (dtype == HQ_BF16)
+          hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_BF16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
+        else
+          hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_F16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
+      } else if (D == 128) {
         if (dtype == HQ_BF16)
           hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else

@@ -299,3 +299,20 @@ def test_topk_score_patterns(method, case):
         k_top = 3
     say(f"top-k pattern {case} method={method} n={n} k={k_top}")
     _pattern_case(v, k_top, method)
+
+
+@pytest.mark.parametrize("method", METHODS)
+def test_detect_many_units_long_rows(method):
+    """Enough (unit, 256-column group) pairs that the matmul form walks 4
+    groups per block with the query rows resident in LDS (the long-context
+    layout): 8 sequences x 8 KV heads, 32 query heads, 64 steps, 8064
+    candidates. Scores and sets bit-exact against the oracle."""
+    B, Hq, Hkv, D, R, n, ce, k_top = 8, 32, 8, 128, 64, 8192, 8064, 403
+    rng = np.random.default_rng(77)
+    q = synth.round_dtype(np.rint(rng.standard_normal((B, Hq, R, D)) * 16) / 16, "bf16")
+    K = synth.round_dtype(np.rint(rng.standard_normal((B, Hkv, n, D)) * 16) / 16, "bf16")
+    say(f"detect method={method} B={B} Hq={Hq} Hkv={Hkv} n={n} ce={ce} k={k_top} (resident rows)")
+    want_idx, want_sc = detect.detect(q, K, ce, k_top)
+    got_idx, got_sc = _run(q, K, ce, k_top, method, "bf16")
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
