@@ -66,12 +66,23 @@ __device__ __forceinline__ uint32_t encode_quarter(const float (&v)[8], _Float16
   z16 = static_cast<_Float16>(mn + 0.0f);
   const float s = static_cast<float>(s16);
   const float z = static_cast<float>(z16);
+  // Fast path: q' = (x - z) * rcp(s) is within 2^-18 of the correctly rounded
+  // quotient for |q| <= 16 (v_rcp_f32 is good to 1 ulp, the product adds half
+  // an ulp; |q| <= 15 (1 + 2^-11) here since s and z are the group's rounded
+  // range and minimum). Rounding q' to an integer then agrees with rounding
+  // the correctly rounded quotient unless q' lies within 2^-16 of a
+  // half-integer; only those elements (exact ties among them) take the IEEE
+  // divide. NaN inputs fail the test and take the divide too.
+  const float rs = __builtin_amdgcn_rcpf(s);
   uint32_t packed = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t c = 0;
     if (s != 0.0f) {
-      float t = __builtin_rintf((v[i] - z) / s);
+      const float d = v[i] - z;
+      const float qf = d * rs;
+      float t = __builtin_rintf(qf);
+      if (!(0.5f - fabsf(qf - t) > 0x1p-16f)) t = __builtin_rintf(d / s);
       t = fminf(fmaxf(t, 0.0f), 15.0f);
       c = static_cast<uint32_t>(t);
     }

@@ -87,6 +87,52 @@ __global__ __launch_bounds__(256) void quantize_kernel(
                                codes, sz, dst_head_rows, dst_row0);
 }
 
+// Values in TILE16, whole tiles only: one wave per (head, tile, 32-channel
+// group). Lane (row rr of the tile, quarter q) encodes as quantize_quarter
+// does; the codes then pass through LDS so that each tile row (one channel
+// pair over the tile's 16 rows, in slot order) leaves as a single 16-byte
+// store instead of 16 single-byte stores from different lanes.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_tiles_kernel(
+    const void *__restrict__ x, int n_heads, int64_t n_tiles, int D, int64_t x_head_stride,
+    int64_t x_row_stride, uint8_t *__restrict__ codes, uint16_t *__restrict__ sz,
+    int64_t dst_head_rows, int64_t dst_row0, int64_t tile0) {
+  __shared__ __align__(16) uint8_t tb[4][16][16];        // [wave][channel pair of the group][slot]
+  const int ng = D / kGroup;
+  const int wave = static_cast<int>(threadIdx.x >> 6);
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;   // (head, tile, group)
+  if (wid >= static_cast<int64_t>(n_heads) * n_tiles * ng) return;   // wave-uniform
+  const int g = static_cast<int>(wid % ng);
+  const int64_t ht = wid / ng;
+  const int64_t u = tile0 + ht % n_tiles;
+  const int64_t h = ht / n_tiles;
+  const int rr = lane >> 2, q = lane & 3;
+  const int64_t row = u * 16 + rr;
+  const int64_t src = h * x_head_stride + (row - dst_row0) * x_row_stride + g * kGroup + q * 8;
+  float v[8];
+  load8<DT>(x, src, v);
+  _Float16 s16, z16;
+  const uint32_t packed = encode_quarter(v, s16, z16);
+  // each run of 4 rows is stored in the order 0, 2, 1, 3
+  const int slot16 = (rr & ~3) | ((rr & 1) << 1) | ((rr >> 1) & 1);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) tb[wave][q * 4 + jj][slot16] = static_cast<uint8_t>((packed >> (8 * jj)) & 0xFFu);
+  if (q == 0) {
+    const uint32_t szw = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+    reinterpret_cast<uint32_t *>(sz)[(h * dst_head_rows + row) * ng + g] = szw;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < 16) {
+    const uint4 t = *reinterpret_cast<const uint4 *>(&tb[wave][lane][0]);
+    uint8_t *tile = codes + (h * (dst_head_rows / 16) + u) * (D / 2) * 16;
+    *reinterpret_cast<uint4 *>(tile + (g * 16 + lane) * 16) = t;
+  }
+}
+
 // Keys (row layout) and values (16-token tiles) of the same rows in one launch:
 // the first half of the threads packs K, the second half V.
 template <int DT>
@@ -134,10 +180,31 @@ void launch_quantize_dt(int layout, dim3 grid, hipStream_t st, const void *x, in
   if (layout == HQ_LAYOUT_ROWS) {
     hipLaunchKernelGGL((quantize_kernel<DT, HQ_LAYOUT_ROWS>), grid, dim3(256), 0, st, x,
                        n_heads, n_rows, D, xh, xr, codes, sz, dhr, d0);
-  } else {
+    return;
+  }
+  // TILE16: whole tiles through the tile kernel, the partial tiles at either
+  // end (rows [d0, a) and [b, d0 + n_rows)) through the per-byte kernel
+  const int64_t end = d0 + n_rows;
+  const int64_t a = (d0 + 15) / 16 * 16, b = end / 16 * 16;
+  if (b <= a) {
     hipLaunchKernelGGL((quantize_kernel<DT, HQ_LAYOUT_TILE16>), grid, dim3(256), 0, st, x,
                        n_heads, n_rows, D, xh, xr, codes, sz, dhr, d0);
+    return;
   }
+  const int eb = DT == HQ_F32 ? 4 : 2;
+  auto piece = [&](int64_t r0, int64_t r1) {         // rows [r0, r1) by the per-byte kernel
+    if (r1 <= r0) return;
+    const int64_t threads = 4 * static_cast<int64_t>(n_heads) * (r1 - r0) * (D / kGroup);
+    const void *xs = static_cast<const uint8_t *>(x) + (r0 - d0) * xr * eb;
+    hipLaunchKernelGGL((quantize_kernel<DT, HQ_LAYOUT_TILE16>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, st, xs, n_heads, r1 - r0, D, xh, xr, codes, sz, dhr, r0);
+  };
+  piece(d0, a);
+  piece(b, end);
+  const int64_t n_tiles = (b - a) / 16;
+  const int64_t waves = static_cast<int64_t>(n_heads) * n_tiles * (D / kGroup);
+  hipLaunchKernelGGL((quantize_tiles_kernel<DT>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st,
+                     x, n_heads, n_tiles, D, xh, xr, codes, sz, dhr, d0, a / 16);
 }
 
 }  // namespace
