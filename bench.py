@@ -267,7 +267,7 @@ def main():
         try:
             tr = json.load(open(TRAFFIC_FILE))
             rec = tr.get(args.workload)
-            if rec and rec.get("source_hash") == source_hash("hq_decode.hip", "hq_common.h") \
+            if rec and rec.get("source_hash") == source_hash("hq_decode.hip", "hq_common.h", "hq_int4.h") \
                     and rec.get("splits", 0) == args.splits:
                 traffic = rec["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
