@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--ablation", action="store_true",
                     help="decode settings of the ablation (hybrid, sparse, window only, strict K4V4, "
                          "all 16-bit): bytes, time and error against exact attention")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps in one HIP graph and time its replay")
     ap.add_argument("--separate-upkeep", action="store_true",
                     help="queries to the ring and the eviction as separate calls (hq_decode_attn)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -176,7 +178,7 @@ def main():
         hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
         hq.hq_gather_rows(Vc, n_heads, T, D, idx_new, k, cache.vl_v)
 
-    sh = stream.cuda_stream          # the launch stream's handle, looked up once
+    launch_stream = stream           # the stream the step's calls go to
 
     def step(s: int):
         c = s % copies
@@ -192,7 +194,7 @@ def main():
             hq.hq_decode_attn(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
             return
         hq.hq_decode_step(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c],
-                          q_acc=qaccs[c], R=R, step=s, evict=True, stream=sh)
+                          q_acc=qaccs[c], R=R, step=s, evict=True, stream=launch_stream.cuda_stream)
         # the queries went into the ring with the step; the detector has work
         # only on the ring's last slot, so the loop calls it there alone
         if s % R == R - 1 and detect(s, c, False):
@@ -205,10 +207,27 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     base = args.warmup
+    if args.graph:
+        # the same steps captured once; the replay is the timed region (the
+        # library only enqueues kernels, so every call is capturable)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        launch_stream = cap
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for s in range(base, base + args.steps):
+                    step(s)
+        launch_stream = stream
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
     e0.record(stream)
     h0 = time.perf_counter()
-    for s in range(base, base + args.steps):
-        step(s)
+    if args.graph:
+        graph.replay()
+    else:
+        for s in range(base, base + args.steps):
+            step(s)
     h1 = time.perf_counter()
     e1.record(stream)
     torch.cuda.synchronize()
@@ -301,6 +320,7 @@ def main():
             "layer_copies_rotated": copies, "detect_method": args.detect_method,
             "decode_splits": hq.hq_decode_auto_splits(descs[0], Hq) if args.splits == 0 else args.splits,
             "detect_every": R, "detections_in_timed_steps": n_detect,
+            "timed_as": "one HIP graph replay of the steps" if args.graph else "stream launches per step",
             "step_calls": ("hq_detect_vlines(q) + hq_quantize_kv_pair + hq_decode_attn" if args.separate_upkeep
                            else "hq_decode_step (+ hq_detect_vlines every 64th step)"),
         },
