@@ -29,9 +29,11 @@
 //    into the first digit. A boundary bucket of at most 1024 keys is ranked
 //    directly by (score, position); a larger one goes through the remaining
 //    two digits (11 and 10 bits), a refinement on the bits the shift dropped
-//    and a cut of equal scores by position. The keys sit in LDS up to 32768
-//    candidates and are streamed beyond; the output is compacted in order,
-//    ascending by position.
+//    and a cut of equal scores by position; the output is compacted in
+//    order, ascending by position. Up to 32768 candidates per unit one
+//    launch does both (topk_small): each thread keeps the keys of its 32
+//    positions in registers, and the range and the first histogram are
+//    built inside the workgroup.
 #include "hq_common.h"
 
 namespace hq {
@@ -268,9 +270,12 @@ __global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_a
 // columns (8 tiles of 32, two per wave), loading the next group's K
 // fragments into a second register set while the matrix core works on the
 // current one. Q is read from L2 once per gpb groups instead of once per
-// group, and the K stream overlaps the MFMAs. Each group writes its scores
-// and its score range (one partial per 256 candidates, as the top-k expects).
+// group, and the K stream overlaps the MFMAs. Each group writes its scores;
+// its score range (one partial per 256 candidates, as the top-k expects)
+// goes per wave into LDS and is reduced over the waves after the last group,
+// so the waves of a block meet at no barrier between groups.
 constexpr int kResRows = 256;
+constexpr int kResMaxGroups = 16;                 // groups per block at most
 template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t *__restrict__ q_acc,
                                                                  const uint16_t *__restrict__ k, int Hq,
@@ -281,6 +286,7 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
   constexpr int KC = D / 16;
   constexpr int ROWV = D / 8;
   __shared__ uint16_t qs[kResRows][D + kRowPad];
+  __shared__ unsigned long long rng[kResMaxGroups][4][2];     // [group in block][wave] {min, max}
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
@@ -351,11 +357,33 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
         mx = u > mx ? u : mx;
       }
     }
-    block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * groups + g) : nullptr);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    if (lane == 0) {
+      rng[g - g0][wave][0] = mn;
+      rng[g - g0][wave][1] = mx;
+    }
   };
   for (int g = g0; g < g1; g += 2) {
     group(g, kfa, kfb);
     if (g + 1 < g1) group(g + 1, kfb, kfa);
+  }
+  __syncthreads();
+  const int gi = static_cast<int>(threadIdx.x);
+  if (mm && gi < g1 - g0) {
+    unsigned long long mn = rng[gi][0][0], mx = rng[gi][0][1];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      mn = rng[gi][w][0] < mn ? rng[gi][w][0] : mn;
+      mx = rng[gi][w][1] > mx ? rng[gi][w][1] : mx;
+    }
+    unsigned long long *dst = mm + 2 * (static_cast<int64_t>(unit) * groups + g0 + gi);
+    dst[0] = mn;
+    dst[1] = mx;
   }
 }
 
@@ -457,19 +485,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) 
 }
 
 constexpr int kSmallBucket = kTopkThreads;     // boundary buckets up to this size are ranked directly
-constexpr int64_t kLdsKeys = 32768;            // keys kept in LDS up to this many candidates
-// LDS slot of key j: one padding word per 32 keys, so the per-thread runs
-// (j = t * 32 + i, 33 t mod 64 distinct) are free of bank conflicts
-__device__ __forceinline__ int64_t pad_slot(int64_t j) { return j + (j >> 5); }
-constexpr int kLdsKeySlots = static_cast<int>(kLdsKeys + kLdsKeys / 32);
-// LK: the keys live in LDS, sharing the space of the radix histograms, which
-// only the large-bucket path uses (and it streams the keys from memory)
-template <bool LK>
 struct TopkShared {
-  union {
-    uint32_t whist[kHists][kBins];
-    uint32_t lkeys[LK ? kLdsKeySlots : 1];
-  } u;
+  uint32_t whist[kHists][kBins];
   uint32_t hist[kBins];
   int scan[kTopkThreads / 64 + 2];
   int sel[4];
@@ -478,11 +495,13 @@ struct TopkShared {
   int bpos[kSmallBucket];
   int rank[kSmallBucket];
   int bcnt;
+  unsigned long long rbase;                    // the unit's key base and shift
+  int rshift;
 };
 
 template <class SH>
 __device__ __forceinline__ void clear_whist(SH &sh) {
-  uint32_t *h = &sh.u.whist[0][0];
+  uint32_t *h = &sh.whist[0][0];
   for (int i = threadIdx.x; i < kHists * kBins; i += kTopkThreads) h[i] = 0u;
 }
 // sum the histograms into sh.hist
@@ -491,7 +510,7 @@ __device__ __forceinline__ void reduce_whist(SH &sh) {
   for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
     uint32_t t = 0;
 #pragma unroll
-    for (int w = 0; w < kHists; ++w) t += sh.u.whist[w][b];
+    for (int w = 0; w < kHists; ++w) t += sh.whist[w][b];
     sh.hist[b] = t;
   }
 }
@@ -520,21 +539,19 @@ __device__ __forceinline__ void hist_add(uint32_t *wh, bool match, uint32_t d) {
 // behind one barrier; sel is written again only behind later barriers.
 template <class SH>
 __device__ int find_digit(int nb, int *k_rem, int *cnt, SH &sh) {
+  constexpr int kPer = kBins / 64;                 // bins per lane at most
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (nb + 63) / 64;
     const int hi = nb - per * lane > 0 ? nb - per * lane : 0;          // bins [lo, hi)
     const int lo = hi - per > 0 ? hi - per : 0;
+    const int nv = hi - lo;
+    uint32_t v[kPer];                              // every read issued at once
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = i < nv ? sh.hist[lo + i] : 0u;
     int s = 0;
-    if (per == kBins / 64 && lo == hi - per) {       // the 2048-bin digit: every read issued at once
-      uint32_t v[kBins / 64];
 #pragma unroll
-      for (int i = 0; i < kBins / 64; ++i) v[i] = sh.hist[lo + i];
-#pragma unroll
-      for (int i = 0; i < kBins / 64; ++i) s += static_cast<int>(v[i]);
-    } else {
-      for (int b = hi - 1; b >= lo; --b) s += static_cast<int>(sh.hist[b]);
-    }
+    for (int i = 0; i < kPer; ++i) s += static_cast<int>(v[i]);
     int inc = s;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -543,16 +560,21 @@ __device__ int find_digit(int nb, int *k_rem, int *cnt, SH &sh) {
     }
     const int kr = *k_rem;
     int acc = inc - s;                                                  // above this lane's bins
-    if (acc < kr && kr <= inc) {
-      for (int b = hi - 1; b >= lo; --b) {
-        const int c = static_cast<int>(sh.hist[b]);
+    if (acc < kr && kr <= inc) {                   // one lane: walk its bins from the top
+      int bsel = 0, rsel = 0, csel = 0;
+#pragma unroll
+      for (int i = kPer - 1; i >= 0; --i) {
+        const int c = static_cast<int>(v[i]);
         if (acc < kr && kr <= acc + c) {
-          sh.sel[0] = b;
-          sh.sel[1] = kr - acc;
-          sh.sel[2] = c;
+          bsel = lo + i;
+          rsel = kr - acc;
+          csel = c;
         }
         acc += c;
       }
+      sh.sel[0] = bsel;
+      sh.sel[1] = rsel;
+      sh.sel[2] = csel;
     }
   }
   __syncthreads();
@@ -686,151 +708,40 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
   for (int b = threadIdx.x; b < kBins; b += kTkBlock) bh[b] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
 }
 
-// 2. One workgroup per unit. Thread t owns positions [t P, t P + P), P a
-// multiple of 4. LK (n <= kLdsKeys): the keys are loaded once into LDS;
-// otherwise every pass streams them from the workspace in batches of kRun
-// with 16-byte loads. The first digit comes from the block histograms. When
-// its bucket holds at most kSmallBucket keys, the bucket's (score, position)
-// pairs are collected and the k_rem-th of them is found by ranking; the
-// selection is then a predicate on (digit, score, position), counted, scanned
-// and written in order. Larger buckets take the radix path below.
-template <bool LK>
-__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t *__restrict__ scores,
-                                                                   uint32_t *__restrict__ keys,
-                                                                   const uint32_t *__restrict__ bhist,
-                                                                   const unsigned long long *__restrict__ mm,
-                                                                   int64_t n, int nbu, int np, int k_top,
-                                                                   int32_t *__restrict__ idx_out) {
-  __shared__ TopkShared<LK> sh;
-  const int unit = blockIdx.x;
-  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
-  const int64_t nst = key_stride(n);
-  uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
-  int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
-  if (k_top == 0) return;
-  uint32_t *wh = sh.u.whist[threadIdx.x >> 7];
-  const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // wave-uniform
-  const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
-  const int64_t j1 = j0 + P < n ? j0 + P : n;
-
-  // the first digit from the block histograms (every load in flight at
-  // once) and, LK, the thread's keys into LDS
-  {
-    const uint32_t *bh = bhist + static_cast<int64_t>(unit) * nbu * kBins;
-    for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
-      uint32_t v[kTkMaxBlocks];
-#pragma unroll
-      for (int blk = 0; blk < kTkMaxBlocks; ++blk) v[blk] = blk < nbu ? bh[static_cast<int64_t>(blk) * kBins + b] : 0u;
-      uint32_t t = 0;
-#pragma unroll
-      for (int blk = 0; blk < kTkMaxBlocks; ++blk) t += v[blk];
-      sh.hist[b] = t;
-    }
-  }
-  if constexpr (LK) {
+// Visits the thread's positions [t P, t P + P) of a unit's keys, streamed
+// from the workspace in batches of kRun with 16-byte loads: visit(j, key,
+// valid). The trip count is the same for every thread (P is uniform), so the
+// body may use wave-wide operations.
+template <class F>
+__device__ __forceinline__ void for_own_ws(const uint32_t *gk, int64_t nst, int64_t P, int64_t j1, F &&visit) {
+#pragma unroll 1
+  for (int64_t c0 = 0; c0 < P; c0 += kRun) {
+    const int64_t b0 = threadIdx.x * P + c0;          // a multiple of 4
+    uint32_t kv[kRun];
 #pragma unroll
     for (int i = 0; i < kRun / 4; ++i) {
-      const int64_t j = j0 + 4 * i;                                   // j0: a multiple of 4
-      if (j < j1) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(gk + j);
-        sh.u.lkeys[pad_slot(j)] = v.x;
-        if (j + 1 < j1) sh.u.lkeys[pad_slot(j + 1)] = v.y;
-        if (j + 2 < j1) sh.u.lkeys[pad_slot(j + 2)] = v.z;
-        if (j + 3 < j1) sh.u.lkeys[pad_slot(j + 3)] = v.w;
-      }
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (b0 + 4 * i < nst) v = *reinterpret_cast<const uint4 *>(gk + b0 + 4 * i);
+      kv[4 * i] = v.x; kv[4 * i + 1] = v.y; kv[4 * i + 2] = v.z; kv[4 * i + 3] = v.w;
     }
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) visit(b0 + i, kv[i], b0 + i < j1);
   }
-  if (threadIdx.x == 0) sh.bcnt = 0;
-  if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
-  __syncthreads();
-  int k_rem = k_top, eq = 0;
-  uint32_t prefix = static_cast<uint32_t>(find_digit(kBins, &k_rem, &eq, sh)) << 21;
+}
+
+// The radix path after the first digit (prefix = that digit << 21): the
+// other two digits (bits 10..20, then 0..9) over the streamed keys; then,
+// when the threshold key's bucket is not taken whole, a selection on the low
+// `shift` bits of the scores that the keys dropped; then the in-order
+// compaction: every candidate above the threshold, and of those equal to it
+// the first `take` by position.
+__device__ void topk_radix(TopkShared &sh, const int64_t *sc, const uint32_t *gk, int64_t nst, int64_t P,
+                           int64_t j1, unsigned long long base, int shift, uint32_t prefix, int k_rem, int eq,
+                           int k_top, int32_t *out) {
+  uint32_t *wh = sh.whist[threadIdx.x >> 7];
   uint32_t pmask = 0x7FFu << 21;
-
-  // visit(j, key, valid) streamed from the workspace, batch by batch; the
-  // trip count is the same for every thread (P is uniform), so the body may
-  // use wave-wide operations
-  auto for_own_ws = [&](auto &&visit) {
-#pragma unroll 1
-    for (int64_t c0 = 0; c0 < P; c0 += kRun) {
-      const int64_t b0 = threadIdx.x * P + c0;          // a multiple of 4
-      uint32_t kv[kRun];
-#pragma unroll
-      for (int i = 0; i < kRun / 4; ++i) {
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (b0 + 4 * i < nst) v = *reinterpret_cast<const uint4 *>(gk + b0 + 4 * i);
-        kv[4 * i] = v.x; kv[4 * i + 1] = v.y; kv[4 * i + 2] = v.z; kv[4 * i + 3] = v.w;
-      }
-#pragma unroll
-      for (int i = 0; i < kRun; ++i) visit(b0 + i, kv[i], b0 + i < j1);
-    }
-  };
-  // the fast path's visits: from LDS (no wave-wide operations in the body)
-  auto for_own = [&](auto &&visit) {
-    if constexpr (LK) {
-#pragma unroll 4
-      for (int64_t j = j0; j < j1; ++j) visit(j, sh.u.lkeys[pad_slot(j)], true);
-    } else {
-      for_own_ws(visit);
-    }
-  };
-
-  if (eq <= kSmallBucket) {                     // eq: from LDS, uniform
-    const uint32_t d1 = prefix >> 21;
-    for_own([&](int64_t j, uint32_t key, bool ok) {
-      if (ok && (key >> 21) == d1) {
-        const int slot = atomicAdd(&sh.bcnt, 1);
-        sh.bsc[slot] = sc[j];
-        sh.bpos[slot] = static_cast<int>(j);
-      }
-    });
-    __syncthreads();
-    // rank of each member in the order (score descending, position
-    // ascending): parts = 1024 / eq threads share a member's comparisons
-    {
-      const int parts = kTopkThreads / eq;
-      const int e = static_cast<int>(threadIdx.x) / parts;
-      const int part = static_cast<int>(threadIdx.x) % parts;
-      if (e < eq) {
-        const long long ms = sh.bsc[e];
-        const int mp = sh.bpos[e];
-        int r = 0;
-        for (int i = part; i < eq; i += parts) {
-          const long long si = sh.bsc[i];
-          r += (si > ms) || (si == ms && sh.bpos[i] < mp);
-        }
-        if (r) atomicAdd(&sh.rank[e], r);
-      }
-    }
-    __syncthreads();
-    // each member's decision goes into its key: all ones (above every real
-    // key, at most 2^31) to take it, 0 to drop it; the passes below then need
-    // no scores
-    if (static_cast<int>(threadIdx.x) < eq) {
-      const uint32_t mark = sh.rank[threadIdx.x] < k_rem ? 0xFFFFFFFFu : 0u;
-      const int64_t j = sh.bpos[threadIdx.x];
-      if constexpr (LK) sh.u.lkeys[pad_slot(j)] = mark;
-      else gk[j] = mark;
-    }
-    if constexpr (!LK) __threadfence_block();
-    __syncthreads();
-    auto take_it = [&](int64_t, uint32_t key) -> bool { return key == 0xFFFFFFFFu || (key >> 21) > d1; };
-    int cnt = 0;
-    for_own([&](int64_t j, uint32_t key, bool ok) { cnt += ok && take_it(j, key); });
-    int tot;
-    int pos = block_exclusive_scan(cnt, sh.scan, &tot);
-    for_own([&](int64_t j, uint32_t key, bool ok) {
-      if (ok && take_it(j, key) && pos < k_top) out[pos++] = static_cast<int32_t>(j);
-    });
-    return;
-  }
-
-  unsigned long long base;
-  int shift;
-  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, sh.mm);
   auto off = [&](long long sv) -> unsigned long long { return ordered(sv) - base; };
-
-  // the other two digits: bits 10..20, then 0..9
+  auto for_own = [&](auto &&visit) { for_own_ws(gk, nst, P, j1, visit); };
 #pragma unroll 1
   for (int ps = 0; ps < 2; ++ps) {
     const int sft = ps == 0 ? 10 : 0;
@@ -838,7 +749,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
     const uint32_t dm = (1u << nbt) - 1u;
     clear_whist(sh);
     __syncthreads();
-    for_own_ws([&](int64_t, uint32_t key, bool ok) {
+    for_own([&](int64_t, uint32_t key, bool ok) {
       hist_add(wh, ok && (key & pmask) == prefix, (key >> sft) & dm);
     });
     __syncthreads();
@@ -850,8 +761,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
   }
   const uint32_t kappa = prefix;   // key of the k_top-th largest (>= 1)
   int take = k_rem;                // taken among key == kappa
-  // 4. members of the kappa bucket differ only in the low `shift` bits:
-  //    select on those bits when the bucket is not taken whole
+  // members of the kappa bucket differ only in the low `shift` bits: select
+  // on those bits when the bucket is not taken whole
   const bool refine = eq > take && shift > 0;
   unsigned long long low = 0;
   if (refine) {
@@ -862,7 +773,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
       const int sh2 = top - bits;
       clear_whist(sh);
       __syncthreads();
-      for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+      for_own([&](int64_t j, uint32_t key, bool ok) {
         bool m = false;
         uint32_t d = 0;
         if (ok && key == kappa) {
@@ -882,8 +793,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
     }
     low = lowpre;
   }
-  // every candidate above the threshold is taken; of those equal to it, the
-  // first `take` by position
   const unsigned long long tau = (static_cast<unsigned long long>(kappa - 1u) << shift) + low;
   auto is_tie = [&](int64_t j, uint32_t key) -> bool {
     if (key != kappa) return false;
@@ -893,10 +802,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
     if (key != kappa) return key > kappa;
     return refine && off(sc[j]) > tau;
   };
-
-  // 5. in-order compaction over the contiguous runs
   int ties = 0, sure = 0;
-  for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+  for_own([&](int64_t j, uint32_t key, bool ok) {
     if (ok) {
       ties += is_tie(j, key);
       sure += is_sure(j, key);
@@ -907,20 +814,255 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
   int sel = sure;
   {
     int r = tie_before;
-    for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+    for_own([&](int64_t j, uint32_t key, bool ok) {
       if (ok && is_tie(j, key)) { sel += (r < take); ++r; }
     });
   }
   int pos = block_exclusive_scan(sel, sh.scan, &tot);
   {
     int r = tie_before;
-    for_own_ws([&](int64_t j, uint32_t key, bool ok) {
+    for_own([&](int64_t j, uint32_t key, bool ok) {
       if (!ok) return;
       bool sj = is_sure(j, key);
       if (is_tie(j, key)) { sj = r < take; ++r; }
       if (sj && pos < k_top) out[pos++] = static_cast<int32_t>(j);
     });
   }
+}
+
+// Ranks the boundary bucket's eq members (sh.bsc, sh.bpos; sh.rank zeroed)
+// in the order (score descending, position ascending): parts = 1024 / eq
+// threads share a member's comparisons. Ends behind a barrier.
+__device__ __forceinline__ void rank_bucket(TopkShared &sh, int eq) {
+  const int parts = kTopkThreads / eq;
+  const int e = static_cast<int>(threadIdx.x) / parts;
+  const int part = static_cast<int>(threadIdx.x) % parts;
+  if (e < eq) {
+    const long long ms = sh.bsc[e];
+    const int mp = sh.bpos[e];
+    int r = 0;
+    for (int i = part; i < eq; i += parts) {
+      const long long si = sh.bsc[i];
+      r += (si > ms) || (si == ms && sh.bpos[i] < mp);
+    }
+    if (r) atomicAdd(&sh.rank[e], r);
+  }
+  __syncthreads();
+}
+
+// 2. Units with more than kSmallN candidates: one workgroup per unit; thread
+// t owns positions [t P, t P + P), P a multiple of 4, and streams their keys
+// from the workspace. The first digit comes from the block histograms. When
+// its bucket holds at most kSmallBucket keys, the bucket's (score, position)
+// pairs are collected and ranked; the selection is then a predicate on
+// (digit, score, position), counted, scanned and written in order. Larger
+// buckets take the radix path.
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t *__restrict__ scores,
+                                                                   uint32_t *__restrict__ keys,
+                                                                   const uint32_t *__restrict__ bhist,
+                                                                   const unsigned long long *__restrict__ mm,
+                                                                   int64_t n, int nbu, int np, int k_top,
+                                                                   int32_t *__restrict__ idx_out) {
+  __shared__ TopkShared sh;
+  const int unit = blockIdx.x;
+  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
+  const int64_t nst = key_stride(n);
+  uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
+  int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
+  if (k_top == 0) return;
+  const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // wave-uniform
+  const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
+  const int64_t j1 = j0 + P < n ? j0 + P : n;
+
+  // the first digit from the block histograms (every load in flight at once)
+  {
+    const uint32_t *bh = bhist + static_cast<int64_t>(unit) * nbu * kBins;
+    for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
+      uint32_t v[kTkMaxBlocks];
+#pragma unroll
+      for (int blk = 0; blk < kTkMaxBlocks; ++blk) v[blk] = blk < nbu ? bh[static_cast<int64_t>(blk) * kBins + b] : 0u;
+      uint32_t t = 0;
+#pragma unroll
+      for (int blk = 0; blk < kTkMaxBlocks; ++blk) t += v[blk];
+      sh.hist[b] = t;
+    }
+  }
+  if (threadIdx.x == 0) sh.bcnt = 0;
+  if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
+  __syncthreads();
+  int k_rem = k_top, eq = 0;
+  const uint32_t d1 = static_cast<uint32_t>(find_digit(kBins, &k_rem, &eq, sh));
+
+  if (eq <= kSmallBucket) {                     // eq: from LDS, uniform
+    for_own_ws(gk, nst, P, j1, [&](int64_t j, uint32_t key, bool ok) {
+      if (ok && (key >> 21) == d1) {
+        const int slot = atomicAdd(&sh.bcnt, 1);
+        sh.bsc[slot] = sc[j];
+        sh.bpos[slot] = static_cast<int>(j);
+      }
+    });
+    __syncthreads();
+    rank_bucket(sh, eq);
+    // each member's decision goes into its key: all ones (above every real
+    // key, at most 2^31) to take it, 0 to drop it; the passes below then need
+    // no scores
+    if (static_cast<int>(threadIdx.x) < eq) {
+      const uint32_t mark = sh.rank[threadIdx.x] < k_rem ? 0xFFFFFFFFu : 0u;
+      gk[sh.bpos[threadIdx.x]] = mark;
+    }
+    __threadfence_block();
+    __syncthreads();
+    auto take_it = [&](uint32_t key) -> bool { return key == 0xFFFFFFFFu || (key >> 21) > d1; };
+    int cnt = 0;
+    for_own_ws(gk, nst, P, j1, [&](int64_t, uint32_t key, bool ok) { cnt += ok && take_it(key); });
+    int tot;
+    int pos = block_exclusive_scan(cnt, sh.scan, &tot);
+    for_own_ws(gk, nst, P, j1, [&](int64_t j, uint32_t key, bool ok) {
+      if (ok && take_it(key) && pos < k_top) out[pos++] = static_cast<int32_t>(j);
+    });
+    return;
+  }
+  unsigned long long base;
+  int shift;
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, sh.mm);
+  topk_radix(sh, sc, gk, nst, P, j1, base, shift, d1 << 21, k_rem, eq, k_top, out);
+}
+
+// 1 + 2 in one launch for units with at most kSmallN candidates: one
+// workgroup per unit; thread t loads the scores of its positions [t P, t P +
+// P), P <= kSmallP. The unit's range is a block min / max of the scores
+// (equal to the reduction of the score kernels' partial ranges); the keys
+// then stay in registers and their top-11-bit histogram is built in LDS. A
+// boundary bucket of at most kSmallBucket keys is collected with its scores
+// and ranked by (score, position); a member's key register then holds its
+// slot in the bucket, and the selection (digit above, or a member ranked
+// below k_rem) is counted, scanned and written in order. A larger bucket
+// writes the keys to the workspace and takes the radix path.
+constexpr int kSmallP = 32;
+constexpr int64_t kSmallN = static_cast<int64_t>(kTopkThreads) * kSmallP;
+// A copy of x that the compiler cannot relate to x, so that the per-position
+// values built on it in one phase are not merged with those of another phase
+// (which would keep 32 of them live, or spilled, in between).
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+__global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t *__restrict__ scores,
+                                                                  uint32_t *__restrict__ keys, int64_t n,
+                                                                  int k_top, int32_t *__restrict__ idx_out) {
+  __shared__ TopkShared sh;
+  const int unit = blockIdx.x;
+  if (k_top == 0) return;
+  const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
+  const int64_t nst = key_stride(n);
+  uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
+  int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // <= kSmallP
+  const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
+  const int64_t j1 = j0 + P < n ? j0 + P : n;
+  const int nown = static_cast<int>(j1 - j0);                             // valid: i < nown
+
+  // key[i] of position j0 + i; 0 (no position) for i >= nown. The scores
+  // come through a buffer resource over the unit's n scores: loads past the
+  // end return 0 and need no per-position mask.
+  uint32_t key[kSmallP];
+  {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int64_t *>(sc), static_cast<short>(0), static_cast<int>(n * 8), 0x00020000);
+    const uint32_t vo = opaque_v(static_cast<uint32_t>(j0) * 8u);
+    const uint32_t vmask = nown >= 32 ? 0xFFFFFFFFu : (1u << nown) - 1u;
+    unsigned long long u[kSmallP];
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i)
+      u[i] = ordered(__builtin_bit_cast(long long, __builtin_amdgcn_raw_buffer_load_b64(rs, vo + 8u * i, 0, 0)));
+    unsigned long long mn = ~0ull, mx = 0;
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i) {
+      const bool ok = (vmask >> i) & 1u;
+      mn = ok && u[i] < mn ? u[i] : mn;
+      mx = ok && u[i] > mx ? u[i] : mx;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    if (lane == 0) {
+      sh.mm[2 * wave] = mn;
+      sh.mm[2 * wave + 1] = mx;
+    }
+    clear_whist(sh);
+    if (threadIdx.x == 0) sh.bcnt = 0;
+    if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+      mn = sh.mm[2 * w] < mn ? sh.mm[2 * w] : mn;
+      mx = sh.mm[2 * w + 1] > mx ? sh.mm[2 * w + 1] : mx;
+    }
+    // keys 1 + (score - min) >> shift fit 32 bits (at most 2^31)
+    const unsigned long long range = mx - mn;
+    const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
+    const int shift = nbits > 31 ? nbits - 31 : 0;
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i)
+      key[i] = (1u + static_cast<uint32_t>((u[i] - mn) >> shift)) & (0u - ((vmask >> i) & 1u));
+    if (threadIdx.x == 0) {                                   // for the radix path
+      sh.rbase = mn;
+      sh.rshift = shift;
+    }
+  }
+  uint32_t *wh = sh.whist[threadIdx.x >> 7];
+#pragma unroll
+  for (int i = 0; i < kSmallP; ++i) hist_add(wh, key[i] != 0u, key[i] >> 21);
+  __syncthreads();
+  const unsigned long long base = sh.rbase;
+  const int shift = sh.rshift;
+  reduce_whist(sh);
+  __syncthreads();
+  int k_rem = k_top, eq = 0;
+  const uint32_t d1 = static_cast<uint32_t>(find_digit(kBins, &k_rem, &eq, sh));
+
+  if (eq <= kSmallBucket) {                     // eq: from LDS, uniform
+    uint32_t memb = 0;                          // bit i: position j0 + i is in the bucket
+    const uint32_t jc = opaque_v(static_cast<uint32_t>(j0));
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i) {
+      if (key[i] != 0u && (key[i] >> 21) == d1) {
+        const int slot = atomicAdd(&sh.bcnt, 1);
+        sh.bsc[slot] = sc[jc + i];
+        sh.bpos[slot] = static_cast<int>(jc + i);
+        key[i] = static_cast<uint32_t>(slot);
+        memb |= 1u << i;
+      }
+    }
+    __syncthreads();
+    rank_bucket(sh, eq);
+    // a position outside the range has key 0: digit 0 <= d1, never a member
+    auto take = [&](int i) -> bool {
+      return ((memb >> i) & 1u) ? sh.rank[key[i]] < k_rem : (key[i] >> 21) > d1;
+    };
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i) cnt += take(i);
+    int tot;
+    int pos = block_exclusive_scan(cnt, sh.scan, &tot);
+    const uint32_t jw = opaque_v(static_cast<uint32_t>(j0));
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i)
+      if (take(i) && pos < k_top) out[pos++] = static_cast<int32_t>(jw + i);
+    return;
+  }
+  // a crowded first digit: the keys into the workspace, then the radix path
+#pragma unroll
+  for (int i = 0; i < kSmallP; ++i)
+    if (key[i] != 0u) gk[j0 + i] = key[i];
+  __threadfence_block();
+  __syncthreads();
+  topk_radix(sh, sc, gk, nst, P, j1, base, shift, d1 << 21, k_rem, eq, k_top, out);
 }
 
 // The score kernels have written their partial ranges to topk_mm(tws, units, n).
@@ -933,14 +1075,14 @@ void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, in
   uint32_t *bh = reinterpret_cast<uint32_t *>(w8 + L.hist);
   uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + L.keys);
   const int np = topk_partials(n);
+  if (n <= kSmallN) {
+    hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, keys, n, k_top, idx_out);
+    return;
+  }
   const unsigned nb = static_cast<unsigned>(units) * c.nbu;
   hipLaunchKernelGGL(topk_keys_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, np, mm, keys, bh);
-  if (n <= kLdsKeys)
-    hipLaunchKernelGGL((topk_select_kernel<true>), dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm, n,
-                       c.nbu, np, k_top, idx_out);
-  else
-    hipLaunchKernelGGL((topk_select_kernel<false>), dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm,
-                       n, c.nbu, np, k_top, idx_out);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm, n, c.nbu, np,
+                     k_top, idx_out);
 }
 
 // ---------------------------------------------------------------- workspace
@@ -1291,7 +1433,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
       // (16 x 128K: column sums 1291 -> 1148 us); with 2 groups per block
       // (1 x 32K, 8 KV heads) its longer blocks lose (28.9 -> 31.1 us).
       int gpb = static_cast<int>((static_cast<int64_t>(units) * groups) / 512);
-      gpb = gpb < 1 ? 1 : (gpb > 16 ? 16 : gpb);
+      gpb = gpb < 1 ? 1 : (gpb > kResMaxGroups ? kResMaxGroups : gpb);
       if (D == 128 && (Hq / Hkv) * R <= kResRows && gpb >= 4) {
         const int rblocks = units * ((groups + gpb - 1) / gpb);
         if (dtype == HQ_BF16)
