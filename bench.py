@@ -19,8 +19,11 @@ seeded synthetic tensors already resident in HBM when timing starts.
 Prints one JSON line (rank 0). `value` is the algorithmic HBM bytes of a
 step divided by the measured step time (GB/s); `ms_per_step` is the step
 time. `roofline` is the decode kernel alone, timed per launch with HIP
-events on the launch stream. `cpu_baseline` is the CPU oracle on a bounded
-sample of the same step.
+events on the launch stream (mean, and p10 / p50 / p90), beside the HBM read
+ceiling (a 2 GiB sequential read), the time of a plain read of the call's
+own bytes at the same size, and the median of launches that reuse one cache
+copy ("warm": what the Infinity Cache can hold may come from it).
+`cpu_baseline` is the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -247,6 +250,7 @@ def main():
     torch.cuda.synchronize()
     durs = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])   # us
     dec_us = float(np.mean(durs))
+    dec_pct = np.percentile(durs, [10, 50, 90])
 
     # ------------------------------------------------------------ detector alone (amortized share)
     d0 = torch.cuda.Event(enable_timing=True)
@@ -261,6 +265,16 @@ def main():
 
     # ------------------------------------------------------------ HBM read ceiling, same run
     stream_gbs = stream_read_ceiling(torch, hq, dev, stream)
+
+    # ------------------------------------------------------------ warm launches (after the rest)
+    # one copy every launch, so that a cache smaller than the 256 MB Infinity
+    # Cache may be served from it (labelled, never the roofline figure)
+    for i in range(args.kernel_launches):
+        starts[i].record(stream)
+        hq.hq_decode_attn(q_steps[i % q_steps.shape[0]], Hq, descs[0], 0.0, args.splits, out, lse, dec_ws[0])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    warm_us = float(np.median([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]))
 
     if args.calib_copy_mb:
         a = torch.empty(args.calib_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -280,6 +294,9 @@ def main():
     step_bytes = dec_bytes + evict_bytes + acc_bytes + (det_bytes + gather_bytes) * n_detect / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_us * 1e-6) / 1e9
+    # the same read at this size: a plain sequential read of dec_bytes,
+    # rotated past the Infinity Cache and event-timed per launch like the call
+    same_us = stream_read_same_bytes_us(torch, hq, dev, stream, dec_bytes, args.kernel_launches)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -336,8 +353,12 @@ def main():
             "traffic_over_algorithmic": (round(traffic / dec_bytes, 4) if traffic else None),
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "avg_launch_us": round(dec_us, 3),
+            "launch_us_p10_p50_p90": [round(float(x), 3) for x in dec_pct],
+            "warm_launch_us_median": round(warm_us, 3),
             "stream_read_gbs": round(stream_gbs, 1),
             "frac_of_stream_read": round(achieved / stream_gbs, 4),
+            "stream_read_same_bytes_us": round(same_us, 3),
+            "frac_of_stream_read_same_bytes": round(same_us / dec_us, 4),
         },
         "detector": {"us_per_detection": round(det_us, 2), "method": args.detect_method,
                      "overhead_vs_64_decode_kernels": round(det_us / (64 * dec_us), 4)},
@@ -473,6 +494,30 @@ def stream_read_ceiling(torch, hq, dev, stream, gib: int = 2, reps: int = 10) ->
     gbs = reps * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del buf, sink
     return gbs
+
+
+def stream_read_same_bytes_us(torch, hq, dev, stream, nbytes: int, launches: int) -> float:
+    """Mean event-timed duration (us) of one hq_stream_read of `nbytes`, the
+    launches rotating over slices of a buffer of >= 1 GiB, so that every read
+    comes from HBM: the time a plain read of that many bytes takes at that
+    size, launch and ramp included."""
+    nb = (int(nbytes) + 255) // 256 * 256
+    n = max(2, -(-(1 << 30) // nb))
+    buf = torch.ones(n * nb, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(hq.hq_stream_read_sink_bytes() // 4, dtype=torch.int32, device=dev)
+    views = [buf[i * nb:i * nb + int(nbytes) // 16 * 16] for i in range(n)]
+    for i in range(n):
+        hq.hq_stream_read(views[i], sink)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    for i in range(launches):
+        starts[i].record(stream)
+        hq.hq_stream_read(views[i % n], sink)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)]))
+    del views, buf, sink
+    return us
 
 
 def main_prefill(args):

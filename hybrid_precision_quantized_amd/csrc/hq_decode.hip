@@ -86,6 +86,7 @@ struct DecodeParams {
   float cs;                 // sm_scale * log2(e)
   // per-step upkeep (hq_decode_step), run by extra blocks of the merge launch
   int merge_blocks;         // blocks of the merge itself
+  int merge_per_xcd;        // ceil(merge_blocks / 8): the merge part of the grid is 8 times this
   int up_q;                 // blocks that copy q into the detector's query ring (0: none)
   uint8_t *q_ring;          // [B][Hq][R][D] of the query dtype
   int R, ring_slot;
@@ -1329,10 +1330,16 @@ __device__ void upkeep(const DecodeParams &P, int ub) {
 
 template <int D, int HB, int QT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
-  if (static_cast<int>(blockIdx.x) >= P.merge_blocks) {    // block-uniform
-    upkeep<D, QT>(P, static_cast<int>(blockIdx.x) - P.merge_blocks);
+  // XCD-aware numbering as in the split kernel: merge block m runs on the XCD
+  // whose L2 the unit's splits wrote their partials through
+  const int hw = blockIdx.x;
+  const int mgrid = kNumXcd * P.merge_per_xcd;
+  if (hw >= mgrid) {                                         // block-uniform
+    upkeep<D, QT>(P, hw - mgrid);
     return;
   }
+  const int mb = (hw % kNumXcd) * P.merge_per_xcd + hw / kNumXcd;
+  if (mb >= P.merge_blocks) return;
   constexpr int NSL = D / kMergeSlice;            // slices per head
   constexpr int F4 = kMergeSlice / 4;             // float4 per slice row
   constexpr int SG = kThreads / F4;               // split groups
@@ -1341,8 +1348,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
   static_assert(kMaxSplits % SG == 0 && kMaxSplits % 64 == 0, "split tiling");
   __shared__ float sw[kMaxSplits];
   __shared__ float4 red[SG][F4];
-  const int sl = blockIdx.x % NSL;
-  const int qh = blockIdx.x / NSL;
+  const int sl = mb % NSL;
+  const int qh = mb / NSL;
   const int unit = qh / HB;
   const int hh = qh % HB;
   const int hc = unit % P.nhc;
@@ -1569,7 +1576,7 @@ void launch_qt(dim3 grid, dim3 mgrid, hipStream_t st, const DecodeParams &P) {
 }
 template <int D, int HB>
 void launch_hb(int qdt, dim3 grid, hipStream_t st, const DecodeParams &P) {
-  const dim3 mgrid(static_cast<unsigned>(P.merge_blocks + P.up_q) +
+  const dim3 mgrid(static_cast<unsigned>(kNumXcd * P.merge_per_xcd + P.up_q) +
                    (P.evict ? static_cast<unsigned>((8 * P.B * P.Hkv * (D / 32) + kThreads - 1) / kThreads) : 0u));
   switch (qdt) {
     case HQ_F32: launch_qt<D, HB, HQ_F32>(grid, mgrid, st, P); break;
@@ -1664,6 +1671,7 @@ hq_status decode_common(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid
   const float scale = sm_scale == 0.f ? 1.0f / sqrtf(static_cast<float>(kv->D)) : sm_scale;
   P.cs = scale * kLog2e;
   P.merge_blocks = pl.units * pl.HB * (kv->D / kMergeSlice);
+  P.merge_per_xcd = static_cast<int>(ceil_div(P.merge_blocks, kNumXcd));
   P.up_q = up.q_ring ? static_cast<int>(ceil_div(static_cast<int64_t>(kv->B) * Hq * kv->D *
                                                     (q_dtype == HQ_F32 ? 4 : 2) / 16, kThreads))
                      : 0;
