@@ -495,8 +495,6 @@ struct TopkShared {
   int bpos[kSmallBucket];
   int rank[kSmallBucket];
   int bcnt;
-  unsigned long long rbase;                    // the unit's key base and shift
-  int rshift;
 };
 
 template <class SH>
@@ -930,13 +928,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
 
 // 1 + 2 in one launch for units with at most kSmallN candidates: one
 // workgroup per unit; thread t loads the scores of its positions [t P, t P +
-// P), P <= kSmallP. The unit's range is a block min / max of the scores
-// (equal to the reduction of the score kernels' partial ranges); the keys
-// then stay in registers and their top-11-bit histogram is built in LDS. A
+// P), P <= kSmallP. The unit's range comes from the score kernels' partial
+// ranges; the keys then stay in registers and their top-11-bit histogram is
+// built in LDS. A
 // boundary bucket of at most kSmallBucket keys is collected with its scores
 // and ranked by (score, position); a member's key register then holds its
 // slot in the bucket, and the selection (digit above, or a member ranked
-// below k_rem) is counted, scanned and written in order. A larger bucket
+// below k_rem) becomes a bit mask per thread, whose population is scanned
+// and whose set bits are written in order. A larger bucket
 // writes the keys to the workspace and takes the radix path.
 constexpr int kSmallP = 32;
 constexpr int64_t kSmallN = static_cast<int64_t>(kTopkThreads) * kSmallP;
@@ -949,8 +948,9 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
   return r;
 }
 __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t *__restrict__ scores,
+                                                                  const unsigned long long *__restrict__ mm,
                                                                   uint32_t *__restrict__ keys, int64_t n,
-                                                                  int k_top, int32_t *__restrict__ idx_out) {
+                                                                  int np, int k_top, int32_t *__restrict__ idx_out) {
   __shared__ TopkShared sh;
   const int unit = blockIdx.x;
   if (k_top == 0) return;
@@ -958,69 +958,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
   const int64_t nst = key_stride(n);
   uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
   int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // <= kSmallP
   const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
   const int64_t j1 = j0 + P < n ? j0 + P : n;
   const int nown = static_cast<int>(j1 - j0);                             // valid: i < nown
 
   // key[i] of position j0 + i; 0 (no position) for i >= nown. The scores
-  // come through a buffer resource over the unit's n scores: loads past the
-  // end return 0 and need no per-position mask.
+  // come through a buffer resource over the unit's n scores (loads past the
+  // end return 0 and need no per-position mask); the range is the reduction
+  // of the score kernels' np partial ranges, by the first wave.
   uint32_t key[kSmallP];
+  unsigned long long base;
+  int shift;
   {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int64_t *>(sc), static_cast<short>(0), static_cast<int>(n * 8), 0x00020000);
     const uint32_t vo = opaque_v(static_cast<uint32_t>(j0) * 8u);
-    const uint32_t vmask = nown >= 32 ? 0xFFFFFFFFu : (1u << nown) - 1u;
     unsigned long long u[kSmallP];
 #pragma unroll
     for (int i = 0; i < kSmallP; ++i)
       u[i] = ordered(__builtin_bit_cast(long long, __builtin_amdgcn_raw_buffer_load_b64(rs, vo + 8u * i, 0, 0)));
-    unsigned long long mn = ~0ull, mx = 0;
-#pragma unroll
-    for (int i = 0; i < kSmallP; ++i) {
-      const bool ok = (vmask >> i) & 1u;
-      mn = ok && u[i] < mn ? u[i] : mn;
-      mx = ok && u[i] > mx ? u[i] : mx;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
-      mn = a < mn ? a : mn;
-      mx = c > mx ? c : mx;
-    }
-    if (lane == 0) {
-      sh.mm[2 * wave] = mn;
-      sh.mm[2 * wave + 1] = mx;
-    }
     clear_whist(sh);
     if (threadIdx.x == 0) sh.bcnt = 0;
     if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-      mn = sh.mm[2 * w] < mn ? sh.mm[2 * w] : mn;
-      mx = sh.mm[2 * w + 1] > mx ? sh.mm[2 * w + 1] : mx;
-    }
-    // keys 1 + (score - min) >> shift fit 32 bits (at most 2^31)
-    const unsigned long long range = mx - mn;
-    const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
-    const int shift = nbits > 31 ? nbits - 31 : 0;
+    unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, sh.mm);   // ends behind a barrier
+    const uint32_t vmask = nown >= 32 ? 0xFFFFFFFFu : (1u << nown) - 1u;
 #pragma unroll
     for (int i = 0; i < kSmallP; ++i)
-      key[i] = (1u + static_cast<uint32_t>((u[i] - mn) >> shift)) & (0u - ((vmask >> i) & 1u));
-    if (threadIdx.x == 0) {                                   // for the radix path
-      sh.rbase = mn;
-      sh.rshift = shift;
-    }
+      key[i] = (1u + static_cast<uint32_t>((u[i] - base) >> shift)) & (0u - ((vmask >> i) & 1u));
   }
   uint32_t *wh = sh.whist[threadIdx.x >> 7];
 #pragma unroll
   for (int i = 0; i < kSmallP; ++i) hist_add(wh, key[i] != 0u, key[i] >> 21);
   __syncthreads();
-  const unsigned long long base = sh.rbase;
-  const int shift = sh.rshift;
   reduce_whist(sh);
   __syncthreads();
   int k_rem = k_top, eq = 0;
@@ -1045,15 +1015,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
     auto take = [&](int i) -> bool {
       return ((memb >> i) & 1u) ? sh.rank[key[i]] < k_rem : (key[i] >> 21) > d1;
     };
-    int cnt = 0;
+    uint32_t tmask = 0;                         // bit i: position j0 + i is taken
 #pragma unroll
-    for (int i = 0; i < kSmallP; ++i) cnt += take(i);
+    for (int i = 0; i < kSmallP; ++i) tmask |= static_cast<uint32_t>(take(i)) << i;
     int tot;
-    int pos = block_exclusive_scan(cnt, sh.scan, &tot);
+    int pos = block_exclusive_scan(__popc(tmask), sh.scan, &tot);
     const uint32_t jw = opaque_v(static_cast<uint32_t>(j0));
-#pragma unroll
-    for (int i = 0; i < kSmallP; ++i)
-      if (take(i) && pos < k_top) out[pos++] = static_cast<int32_t>(jw + i);
+    for (; tmask != 0u && pos < k_top; tmask &= tmask - 1u)
+      out[pos++] = static_cast<int32_t>(jw + static_cast<uint32_t>(__builtin_ctz(tmask)));
     return;
   }
   // a crowded first digit: the keys into the workspace, then the radix path
@@ -1076,7 +1045,8 @@ void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, in
   uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + L.keys);
   const int np = topk_partials(n);
   if (n <= kSmallN) {
-    hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, keys, n, k_top, idx_out);
+    hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, mm, keys, n, np, k_top,
+                       idx_out);
     return;
   }
   const unsigned nb = static_cast<unsigned>(units) * c.nbu;
