@@ -1035,8 +1035,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
 }
 
 // The score kernels have written their partial ranges to topk_mm(tws, units, n).
+// skewed: scores whose first digit is crowded (the attention mass), which
+// always take the radix path; they keep the two launches, whose keys and
+// first histogram come from many workgroups.
 void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, int64_t n, int k_top,
-                 int32_t *idx_out) {
+                 int32_t *idx_out, bool skewed = false) {
   const TopkChunks c = topk_chunks(n);
   const TopkWs L = topk_ws(units, n);
   uint8_t *w8 = static_cast<uint8_t *>(tws);
@@ -1044,7 +1047,7 @@ void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, in
   uint32_t *bh = reinterpret_cast<uint32_t *>(w8 + L.hist);
   uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + L.keys);
   const int np = topk_partials(n);
-  if (n <= kSmallN) {
+  if (n <= kSmallN && !skewed) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, mm, keys, n, np, k_top,
                        idx_out);
     return;
@@ -1627,7 +1630,7 @@ extern "C" hq_status hq_detect_vlines_mass(const void *q_new, void *q_acc, hq_dt
     if (s != HQ_OK) return s;
   }
   if (k_top > 0) {
-    launch_topk(st, units, scores, w8 + L.keys, cand_end, k_top, idx_out);
+    launch_topk(st, units, scores, w8 + L.keys, cand_end, k_top, idx_out, /*skewed=*/true);
     hq_status s = check_launch("hq_detect_vlines_mass (top-k)");
     if (s != HQ_OK) return s;
   }
