@@ -107,6 +107,8 @@ CASES = [
     (1, 4, 2, 128, 300, 10, 290, "bf16"),      # every non-window position VL
     (1, 4, 1, 128, 1, 1, 0, "bf16"),           # one token
     (1, 4, 1, 64, 33, 0, 1, "bf16"),
+    (1, 3, 3, 64, 500, 16, 10, "bf16"),        # G = 1, D = 64: 6 merge blocks, a ragged XCD grid
+    (1, 2, 1, 64, 257, 8, 3, "f16"),           # G = 2: 4 merge blocks
 ]
 
 

@@ -36,6 +36,7 @@ def _planes(cache):
     (1, 8, 8, 128, 517, 16, 10, "f16", 15, 0, 64, True),      # row T - W = 501: mid-tile, odd slot
     (1, 8, 2, 128, 200, 0, 5, "bf16", 0, 5, 64, True),       # W = 0: nothing to evict
     (1, 8, 2, 128, 700, 64, 20, "bf16", 9, 11, 16, False),   # ring only
+    (1, 3, 3, 64, 400, 16, 6, "bf16", 3, 63, 64, True),      # 6 merge blocks, upkeep after a ragged XCD grid
 ])
 def test_decode_step(B, Hq, Hkv, D, T, W, k, dtype, win_offset, step, R, evict):
     say(f"decode_step B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} W={W} k={k} {dtype} off={win_offset} "
