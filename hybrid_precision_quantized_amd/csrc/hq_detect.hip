@@ -104,16 +104,17 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
   }
 }
 
-// Grid: units * ceil(tiles / 8) blocks of 4 waves; wave w of block cb owns the
-// 32-token column tiles 8 cb + 2 w and 8 cb + 2 w + 1 with their K fragments
-// in registers. The unit's query rows are staged through LDS 128 rows at a
-// time (double buffered; rows padded by 16 bytes so the 32 lanes reading 32
-// consecutive rows hit different banks) and every A fragment feeds the MFMAs
-// of both tiles.
+// Grid: units * ceil(tiles / (4 TPW)) blocks of 4 waves; wave w of block cb
+// owns the TPW 32-token column tiles 4 TPW cb + TPW w + t with their K
+// fragments in registers. The unit's query rows are staged through LDS 128
+// rows at a time (double buffered; rows padded by 16 bytes so the 32 lanes
+// reading 32 consecutive rows hit different banks) and every A fragment feeds
+// the MFMAs of all TPW tiles. TPW = 4 halves the LDS reads and the query
+// staging per column; it is used when the grid still has two blocks per CU.
 constexpr int kStageRows = 128;
 constexpr int kRowPad = 8;        // halves
-template <int D, int DT>
-__global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__restrict__ q_acc,
+template <int D, int DT, int TPW>
+__global__ __launch_bounds__(256, 2) void mfma_colsum_kernel(const uint16_t *__restrict__ q_acc,
                                                           const uint16_t *__restrict__ k, int Hq,
                                                           int Hkv, int R, int64_t k_rows,
                                                           int64_t cand_end, int tiles_per_unit,
@@ -122,10 +123,13 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
   constexpr int KC = D / 16;                       // k-chunks of 16
   constexpr int ROWV = D / 8;                      // uint4 per row
   constexpr int PER_T = kStageRows * ROWV / 256;   // uint4 per thread per stage
+  constexpr int TPB = 4 * TPW;                     // tiles per block
+  constexpr int GPB = TPB / 8;                     // 256-candidate groups (score partials) per block
   __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
+  __shared__ unsigned long long rng[4][2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int blocks_per_unit = (tiles_per_unit + 7) / 8;
+  const int blocks_per_unit = (tiles_per_unit + TPB - 1) / TPB;
   const int unit = blockIdx.x / blocks_per_unit;              // b * Hkv + h
   const int cb = blockIdx.x % blocks_per_unit;
   const int G = Hq / Hkv;
@@ -135,12 +139,12 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
   const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
   const int half = lane >> 5;
 
-  uint4 bfrag[2][KC];
-  int64_t col[2];
-  bool col_ok[2];
+  uint4 bfrag[TPW][KC];
+  int64_t col[TPW];
+  bool col_ok[TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tile = cb * 8 + wave * 2 + t;
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = cb * TPB + wave * TPW + t;
     col[t] = static_cast<int64_t>(tile) * 32 + (lane & 31);
     col_ok[t] = col[t] < cand_end;
     const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
@@ -170,9 +174,9 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
     }
   };
 
-  f32x16 acc[2];
+  f32x16 acc[TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
 
@@ -189,8 +193,8 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * 16);
-        acc[0] = mfma32<DT>(a, bfrag[0][kc], acc[0]);
-        acc[1] = mfma32<DT>(a, bfrag[1][kc], acc[1]);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t] = mfma32<DT>(a, bfrag[t][kc], acc[t]);
       }
     }
     if (st + 1 < stages) store_stage((st + 1) & 1);
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
   // column = lane & 31; this lane holds 16 of the 32 row residues
   unsigned long long mn = ~0ull, mx = 0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     long long s = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += __double2ll_rn(static_cast<double>(acc[t][i]) * 65536.0);
@@ -211,7 +215,31 @@ __global__ __launch_bounds__(256) void mfma_colsum_kernel(const uint16_t *__rest
       mx = u > mx ? u : mx;
     }
   }
-  block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * blocks_per_unit + cb) : nullptr);
+  if constexpr (GPB == 1) {
+    block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * blocks_per_unit + cb) : nullptr);
+  } else {
+    // one partial per 256 candidates: waves 2 g and 2 g + 1 cover group g
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    if (lane == 0) {
+      rng[wave][0] = mn;
+      rng[wave][1] = mx;
+    }
+    __syncthreads();
+    const int np = static_cast<int>((cand_end + 255) / 256);   // the top-k's partial count
+    const int g = static_cast<int>(threadIdx.x);
+    if (mm && g < GPB && cb * GPB + g < np) {
+      const unsigned long long a0 = rng[2 * g][0], a1 = rng[2 * g + 1][0];
+      const unsigned long long c0 = rng[2 * g][1], c1 = rng[2 * g + 1][1];
+      unsigned long long *dst = mm + 2 * (static_cast<int64_t>(unit) * np + cb * GPB + g);
+      dst[0] = a0 < a1 ? a0 : a1;
+      dst[1] = c0 > c1 ? c0 : c1;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- QSUM form
@@ -1413,16 +1441,23 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
           hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_BF16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
         else
           hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_F16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
+      } else if (D == 128 && units * ((tiles + 15) / 16) >= 512) {
+        // four tiles per wave while the grid keeps two blocks per CU
+        const int blocks4 = units * ((tiles + 15) / 16);
+        if (dtype == HQ_BF16)
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16, 4>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+        else
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16, 4>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       } else if (D == 128) {
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       } else {
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       }
     } else {
       double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
