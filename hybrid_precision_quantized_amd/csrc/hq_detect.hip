@@ -13,11 +13,12 @@
 // Kernels:
 //  * acc_kernel      copies this step's queries into the ring slot.
 //  * mfma_colsum     (HQ_DETECT_MATMUL) bf16/fp16 MFMA 32x32x16: each wave
-//    owns two 32-token column tiles with their K fragments in registers and
-//    runs over all rows of the unit (staged through LDS) in 32-row chunks,
-//    accumulating every chunk into the same accumulator (so rows congruent
-//    mod 32 are summed by the matrix core itself); the 32 row sums of a
-//    column are then converted to int64 units of 2^-16 and added exactly.
+//    owns two or four 32-token column tiles with their K fragments in
+//    registers and runs over all rows of the unit (staged through LDS) in
+//    32-row chunks, accumulating every chunk into the same accumulator (so
+//    rows congruent mod 32 are summed by the matrix core itself); the 32 row
+//    sums of a column are then converted to int64 units of 2^-16 and added
+//    exactly.
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
