@@ -17,8 +17,8 @@
 //    registers and runs over all rows of the unit (staged through LDS) in
 //    32-row chunks, accumulating every chunk into the same accumulator (so
 //    rows congruent mod 32 are summed by the matrix core itself); the 32 row
-//    sums of a column are then converted to int64 units of 2^-16 and added
-//    exactly.
+//    sums of a column are then added in fp64 (exactly on the 2^-4 grid) and
+//    rounded once to int64 units of 2^-16.
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
@@ -103,6 +103,19 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+}
+
+// Score of one column in int64 units of 2^-16 from its 32 fp32 row residues,
+// 16 in each half of the wave: summed in fp64, then rounded once. The sum is
+// exact whenever the residues need fewer than 53 bits together, as on the
+// 2^-4 input grid (multiples of 2^-8 below 2^16), where it equals the sum of
+// the residues each converted exactly.
+__device__ __forceinline__ long long column_score(const f32x16 &a) {
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += static_cast<double>(a[i]);
+  s += __shfl_xor(s, 32, 64);
+  return __double2ll_rn(s * 65536.0);
 }
 
 // Grid: units * ceil(tiles / (4 TPW)) blocks of 4 waves; wave w of block cb
@@ -205,13 +218,10 @@ __global__ __launch_bounds__(256, 2) void mfma_colsum_kernel(const uint16_t *__r
   unsigned long long mn = ~0ull, mx = 0;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    long long s = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s += __double2ll_rn(static_cast<double>(acc[t][i]) * 65536.0);
-    const long long other = __shfl_xor(s, 32, 64);
+    const long long v = column_score(acc[t]);
     if (half == 0 && col_ok[t]) {
-      scores[static_cast<int64_t>(unit) * cand_end + col[t]] = s + other;
-      const unsigned long long u = ordered_score(s + other);
+      scores[static_cast<int64_t>(unit) * cand_end + col[t]] = v;
+      const unsigned long long u = ordered_score(v);
       mn = u < mn ? u : mn;
       mx = u > mx ? u : mx;
     }
@@ -375,13 +385,10 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int64_t col = (static_cast<int64_t>(g) * 8 + wave * 2 + t) * 32 + (lane & 31);
-      long long sv = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv += __double2ll_rn(static_cast<double>(acc[t][i]) * 65536.0);
-      const long long other = __shfl_xor(sv, 32, 64);
+      const long long v = column_score(acc[t]);
       if (half == 0 && col < cand_end) {
-        scores[static_cast<int64_t>(unit) * cand_end + col] = sv + other;
-        const unsigned long long u = ordered_score(sv + other);
+        scores[static_cast<int64_t>(unit) * cand_end + col] = v;
+        const unsigned long long u = ordered_score(v);
         mn = u < mn ? u : mn;
         mx = u > mx ? u : mx;
       }
