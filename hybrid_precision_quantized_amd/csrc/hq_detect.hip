@@ -13,12 +13,14 @@
 // Kernels:
 //  * acc_kernel      copies this step's queries into the ring slot.
 //  * mfma_colsum     (HQ_DETECT_MATMUL) bf16/fp16 MFMA 32x32x16: each wave
-//    owns two or four 32-token column tiles with their K fragments in
-//    registers and runs over all rows of the unit (staged through LDS) in
-//    32-row chunks, accumulating every chunk into the same accumulator (so
-//    rows congruent mod 32 are summed by the matrix core itself); the 32 row
-//    sums of a column are then added in fp64 (exactly on the 2^-4 grid) and
-//    rounded once to int64 units of 2^-16.
+//    owns two 32-token column tiles with their K fragments in registers and
+//    runs over all rows of the unit (staged through LDS) in 32-row chunks,
+//    accumulating every chunk into the same accumulator (so rows congruent
+//    mod 32 are summed by the matrix core itself); the 32 row sums of a
+//    column are then added in fp64 (exactly on the 2^-4 grid) and rounded
+//    once to int64 units of 2^-16. mfma16_colsum is the 16x16x32 form (eight
+//    16-column tiles per wave) for grids with two blocks per CU, and
+//    colsum_resident keeps the query rows in LDS for long contexts.
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).
@@ -118,16 +120,15 @@ __device__ __forceinline__ long long column_score(const f32x16 &a) {
   return __double2ll_rn(s * 65536.0);
 }
 
-// Grid: units * ceil(tiles / (4 TPW)) blocks of 4 waves; wave w of block cb
-// owns the TPW 32-token column tiles 4 TPW cb + TPW w + t with their K
-// fragments in registers. The unit's query rows are staged through LDS 128
-// rows at a time (double buffered; rows padded by 16 bytes so the 32 lanes
-// reading 32 consecutive rows hit different banks) and every A fragment feeds
-// the MFMAs of all TPW tiles. TPW = 4 halves the LDS reads and the query
-// staging per column; it is used when the grid still has two blocks per CU.
+// Grid: units * ceil(tiles / 8) blocks of 4 waves; wave w of block cb owns the
+// 32-token column tiles 8 cb + 2 w and 8 cb + 2 w + 1 with their K fragments
+// in registers. The unit's query rows are staged through LDS 128 rows at a
+// time (double buffered; rows padded by 16 bytes so the 32 lanes reading 32
+// consecutive rows hit different banks) and every A fragment feeds the MFMAs
+// of both tiles.
 constexpr int kStageRows = 128;
 constexpr int kRowPad = 8;        // halves
-template <int D, int DT, int TPW>
+template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void mfma_colsum_kernel(const uint16_t *__restrict__ q_acc,
                                                           const uint16_t *__restrict__ k, int Hq,
                                                           int Hkv, int R, int64_t k_rows,
@@ -137,10 +138,9 @@ __global__ __launch_bounds__(256, 2) void mfma_colsum_kernel(const uint16_t *__r
   constexpr int KC = D / 16;                       // k-chunks of 16
   constexpr int ROWV = D / 8;                      // uint4 per row
   constexpr int PER_T = kStageRows * ROWV / 256;   // uint4 per thread per stage
-  constexpr int TPB = 4 * TPW;                     // tiles per block
-  constexpr int GPB = TPB / 8;                     // 256-candidate groups (score partials) per block
+  constexpr int TPW = 2;                           // tiles per wave
+  constexpr int TPB = 4 * TPW;                     // tiles per block: one 256-candidate score partial
   __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
-  __shared__ unsigned long long rng[4][2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int blocks_per_unit = (tiles_per_unit + TPB - 1) / TPB;
@@ -226,30 +226,150 @@ __global__ __launch_bounds__(256, 2) void mfma_colsum_kernel(const uint16_t *__r
       mx = u > mx ? u : mx;
     }
   }
-  if constexpr (GPB == 1) {
-    block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * blocks_per_unit + cb) : nullptr);
+  block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * blocks_per_unit + cb) : nullptr);
+}
+
+// The 16x16x32 form of the same column sums (D = 128), for grids with two
+// blocks per CU: wave w of block cb owns the eight 16-column tiles 32 cb + 8 w
+// + t (128 columns, 512 per block). MFMA kc covers channels 32 kc + 8 g .. +
+// 7 for lane group g = lane / 16, the same order in both operands, so one K
+// load reads 64 contiguous bytes of each of 16 rows (the 32x32 operand layout
+// reads 32 bytes of each of 32 rows, which stalls the texture path). A lane
+// ends with 4 of a column's 16 row residues; the column sums them with the
+// other three lane groups in fp64.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  if constexpr (DT == HQ_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   } else {
-    // one partial per 256 candidates: waves 2 g and 2 g + 1 cover group g
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+template <int DT>
+__global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *__restrict__ q_acc,
+                                                            const uint16_t *__restrict__ k, int Hq,
+                                                            int Hkv, int R, int64_t k_rows,
+                                                            int64_t cand_end,
+                                                            int64_t *__restrict__ scores,
+                                                            unsigned long long *__restrict__ mm) {
+  constexpr int D = 128;
+  constexpr int KC = D / 32;                       // MFMAs per 16x16 tile and row chunk
+  constexpr int NT = 8;                            // 16-column tiles per wave
+  constexpr int ROWV = D / 8;
+  constexpr int PER_T = kStageRows * ROWV / 256;
+  __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
+  __shared__ unsigned long long rng[4][2];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4;                        // lane group: channels 8 g4 .. 8 g4 + 7 of each 32
+  const int c16 = lane & 15;                       // column of the tile (B), row of the chunk (A)
+  const int blocks_per_unit = static_cast<int>((cand_end + 511) / 512);
+  const int unit = blockIdx.x / blocks_per_unit;
+  const int cb = blockIdx.x % blocks_per_unit;
+  const int G = Hq / Hkv;
+  const int b = unit / Hkv;
+  const int h = unit % Hkv;
+  const int M = G * R;
+  const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
+
+  uint4 bfrag[NT][KC];
+  int64_t col[NT];
+  bool col_ok[NT];
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
-      mn = a < mn ? a : mn;
-      mx = c > mx ? c : mx;
+  for (int t = 0; t < NT; ++t) {
+    col[t] = static_cast<int64_t>(cb) * 512 + (wave * NT + t) * 16 + c16;
+    col_ok[t] = col[t] < cand_end;
+    const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      bfrag[t][kc] = col_ok[t] ? *reinterpret_cast<const uint4 *>(krow + 32 * kc + 8 * g4)
+                               : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  uint4 buf[PER_T];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      const int grow = st * kStageRows + row;
+      buf[e] = grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (lane == 0) {
-      rng[wave][0] = mn;
-      rng[wave][1] = mx;
+  };
+  auto store_stage = [&](int slot) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      *reinterpret_cast<uint4 *>(&qs[slot][row][c8 * 8]) = buf[e];
     }
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int stages = (M + kStageRows - 1) / kStageRows;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < stages; ++st) {
+    if (st + 1 < stages) load_stage(st + 1);
+    const int slot = st & 1;
+#pragma unroll
+    for (int sub = 0; sub < kStageRows / 16; ++sub) {
+      const uint16_t *arow = &qs[slot][sub * 16 + c16][8 * g4];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(arow + 32 * kc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma16<DT>(a, bfrag[t][kc], acc[t]);
+      }
+    }
+    if (st + 1 < stages) store_stage((st + 1) & 1);
     __syncthreads();
-    const int np = static_cast<int>((cand_end + 255) / 256);   // the top-k's partial count
-    const int g = static_cast<int>(threadIdx.x);
-    if (mm && g < GPB && cb * GPB + g < np) {
-      const unsigned long long a0 = rng[2 * g][0], a1 = rng[2 * g + 1][0];
-      const unsigned long long c0 = rng[2 * g][1], c1 = rng[2 * g + 1][1];
-      unsigned long long *dst = mm + 2 * (static_cast<int64_t>(unit) * np + cb * GPB + g);
-      dst[0] = a0 < a1 ? a0 : a1;
-      dst[1] = c0 > c1 ? c0 : c1;
+  }
+  // column c16 of tile t: this lane holds row residues 4 g4 .. 4 g4 + 3 (mod 16)
+  unsigned long long mn = ~0ull, mx = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    double sd = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sd += static_cast<double>(acc[t][j]);
+    sd += __shfl_xor(sd, 16, 64);
+    sd += __shfl_xor(sd, 32, 64);
+    const long long v = __double2ll_rn(sd * 65536.0);
+    if (g4 == 0 && col_ok[t]) {
+      scores[static_cast<int64_t>(unit) * cand_end + col[t]] = v;
+      const unsigned long long u = ordered_score(v);
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
     }
+  }
+  // one partial per 256 candidates: waves 2 g and 2 g + 1 cover group g
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+    mn = a < mn ? a : mn;
+    mx = c > mx ? c : mx;
+  }
+  if (lane == 0) {
+    rng[wave][0] = mn;
+    rng[wave][1] = mx;
+  }
+  __syncthreads();
+  const int np = static_cast<int>((cand_end + 255) / 256);   // the top-k's partial count
+  const int gi = static_cast<int>(threadIdx.x);
+  if (mm && gi < 2 && cb * 2 + gi < np) {
+    const unsigned long long a0 = rng[2 * gi][0], a1 = rng[2 * gi + 1][0];
+    const unsigned long long c0 = rng[2 * gi][1], c1 = rng[2 * gi + 1][1];
+    unsigned long long *dst = mm + 2 * (static_cast<int64_t>(unit) * np + cb * 2 + gi);
+    dst[0] = a0 < a1 ? a0 : a1;
+    dst[1] = c0 > c1 ? c0 : c1;
   }
 }
 
@@ -1450,22 +1570,22 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
         else
           hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_F16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
       } else if (D == 128 && units * ((tiles + 15) / 16) >= 512) {
-        // four tiles per wave while the grid keeps two blocks per CU
+        // 512 columns per block while the grid keeps two blocks per CU
         const int blocks4 = units * ((tiles + 15) / 16);
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16, 4>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma16_colsum_kernel<HQ_BF16>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16, 4>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma16_colsum_kernel<HQ_F16>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm);
       } else if (D == 128) {
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       } else {
         if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
         else
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16, 2>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       }
     } else {
       double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
