@@ -426,7 +426,8 @@ __global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_a
 // 256 threads; lanes in groups of D/8 per key row (8 channels per lane).
 // The same column sums with the unit's query rows resident: all M <= 256
 // rows are staged into LDS once, then the block walks `gpb` groups of 256
-// columns (8 tiles of 32, two per wave), loading the next group's K
+// columns (16 tiles of 16, four per wave, on the 16x16x32 MFMA with the
+// channel order of mfma16_colsum), loading the next group's K
 // fragments into a second register set while the matrix core works on the
 // current one. Q is read from L2 once per gpb groups instead of once per
 // group, and the K stream overlaps the MFMAs. Each group writes its scores;
@@ -442,13 +443,15 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
                                                                  int64_t cand_end, int groups, int gpb,
                                                                  int64_t *__restrict__ scores,
                                                                  unsigned long long *__restrict__ mm) {
-  constexpr int KC = D / 16;
+  constexpr int KC = D / 32;                       // 16x16x32 MFMAs per tile and row chunk
+  constexpr int NT = 4;                            // 16-column tiles per wave and group
   constexpr int ROWV = D / 8;
   __shared__ uint16_t qs[kResRows][D + kRowPad];
   __shared__ unsigned long long rng[kResMaxGroups][4][2];     // [group in block][wave] {min, max}
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
+  const int g4 = lane >> 4;                        // lane group: channels 8 g4 .. + 7 of each 32
+  const int c16 = lane & 15;                       // column of a tile (B), row of a chunk (A)
   const int bpu = (groups + gpb - 1) / gpb;                   // blocks per unit
   const int unit = blockIdx.x / bpu;
   const int g0 = (blockIdx.x % bpu) * gpb;
@@ -457,23 +460,24 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
   const int b = unit / Hkv;
   const int h = unit % Hkv;
   const int M = G * R;                                        // <= kResRows
-  const int subs = (M + 31) / 32;
+  const int subs = (M + 15) / 16;
   const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
   const uint16_t *kunit = k + static_cast<int64_t>(unit) * k_rows * D;
 
-  // K fragments of group g: this lane's column of tiles (wave*2 + t) of the group
-  auto load_frag = [&](int g, uint4 (&kf)[2][KC]) {
+  // K fragments of group g: this lane's column of tiles 4 wave + t of the
+  // group, channels 32 kc + 8 g4 .. + 7 (64 contiguous bytes per row and kc)
+  auto load_frag = [&](int g, uint4 (&kf)[NT][KC]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t col = (static_cast<int64_t>(g) * 8 + wave * 2 + t) * 32 + (lane & 31);
+    for (int t = 0; t < NT; ++t) {
+      const int64_t col = static_cast<int64_t>(g) * 256 + (wave * NT + t) * 16 + c16;
       const bool ok = col < cand_end;
       const uint16_t *krow = kunit + (ok ? col : 0) * D;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        kf[t][kc] = ok ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8) : make_uint4(0u, 0u, 0u, 0u);
+        kf[t][kc] = ok ? *reinterpret_cast<const uint4 *>(krow + 32 * kc + 8 * g4) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  uint4 kfa[2][KC], kfb[2][KC];
+  uint4 kfa[NT][KC], kfb[NT][KC];
   if (g0 < g1) load_frag(g0, kfa);
   // all query rows into LDS (zero past M)
   for (int idx = threadIdx.x; idx < kResRows * ROWV; idx += 256) {
@@ -484,29 +488,32 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
   }
   __syncthreads();
 
-  auto group = [&](int g, const uint4 (&kf)[2][KC], uint4 (&next)[2][KC]) {
+  auto group = [&](int g, const uint4 (&kf)[NT][KC], uint4 (&next)[NT][KC]) {
     if (g + 1 < g1) load_frag(g + 1, next);
-    f32x16 acc[2];
+    f32x4 acc[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sub = 0; sub < subs; ++sub) {
-      const uint16_t *arow = &qs[sub * 32 + (lane & 31)][half * 8];
+      const uint16_t *arow = &qs[sub * 16 + c16][8 * g4];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * 16);
-        acc[0] = mfma32<DT>(a, kf[0][kc], acc[0]);
-        acc[1] = mfma32<DT>(a, kf[1][kc], acc[1]);
+        const uint4 a = *reinterpret_cast<const uint4 *>(arow + 32 * kc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma16<DT>(a, kf[t][kc], acc[t]);
       }
     }
-    // column = lane & 31; this lane holds 16 of the 32 row residues
+    // column c16 of tile t: this lane holds row residues 4 g4 .. 4 g4 + 3 (mod 16)
     unsigned long long mn = ~0ull, mx = 0;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t col = (static_cast<int64_t>(g) * 8 + wave * 2 + t) * 32 + (lane & 31);
-      const long long v = column_score(acc[t]);
-      if (half == 0 && col < cand_end) {
+    for (int t = 0; t < NT; ++t) {
+      const int64_t col = static_cast<int64_t>(g) * 256 + (wave * NT + t) * 16 + c16;
+      double sd = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sd += static_cast<double>(acc[t][j]);
+      sd += __shfl_xor(sd, 16, 64);
+      sd += __shfl_xor(sd, 32, 64);
+      const long long v = __double2ll_rn(sd * 65536.0);
+      if (g4 == 0 && col < cand_end) {
         scores[static_cast<int64_t>(unit) * cand_end + col] = v;
         const unsigned long long u = ordered_score(v);
         mn = u < mn ? u : mn;
