@@ -107,136 +107,22 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
   }
 }
 
-// Score of one column in int64 units of 2^-16 from its 32 fp32 row residues,
-// 16 in each half of the wave: summed in fp64, then rounded once. The sum is
-// exact whenever the residues need fewer than 53 bits together, as on the
-// 2^-4 input grid (multiples of 2^-8 below 2^16), where it equals the sum of
-// the residues each converted exactly.
-__device__ __forceinline__ long long column_score(const f32x16 &a) {
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s += static_cast<double>(a[i]);
-  s += __shfl_xor(s, 32, 64);
-  return __double2ll_rn(s * 65536.0);
-}
 
-// Grid: units * ceil(tiles / 8) blocks of 4 waves; wave w of block cb owns the
-// 32-token column tiles 8 cb + 2 w and 8 cb + 2 w + 1 with their K fragments
-// in registers. The unit's query rows are staged through LDS 128 rows at a
-// time (double buffered; rows padded by 16 bytes so the 32 lanes reading 32
-// consecutive rows hit different banks) and every A fragment feeds the MFMAs
-// of both tiles.
 constexpr int kStageRows = 128;
 constexpr int kRowPad = 8;        // halves
-template <int D, int DT>
-__global__ __launch_bounds__(256, 2) void mfma_colsum_kernel(const uint16_t *__restrict__ q_acc,
-                                                          const uint16_t *__restrict__ k, int Hq,
-                                                          int Hkv, int R, int64_t k_rows,
-                                                          int64_t cand_end, int tiles_per_unit,
-                                                          int64_t *__restrict__ scores,
-                                                          unsigned long long *__restrict__ mm) {
-  constexpr int KC = D / 16;                       // k-chunks of 16
-  constexpr int ROWV = D / 8;                      // uint4 per row
-  constexpr int PER_T = kStageRows * ROWV / 256;   // uint4 per thread per stage
-  constexpr int TPW = 2;                           // tiles per wave
-  constexpr int TPB = 4 * TPW;                     // tiles per block: one 256-candidate score partial
-  __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int blocks_per_unit = (tiles_per_unit + TPB - 1) / TPB;
-  const int unit = blockIdx.x / blocks_per_unit;              // b * Hkv + h
-  const int cb = blockIdx.x % blocks_per_unit;
-  const int G = Hq / Hkv;
-  const int b = unit / Hkv;
-  const int h = unit % Hkv;
-  const int M = G * R;                                        // rows of this unit
-  const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
-  const int half = lane >> 5;
 
-  uint4 bfrag[TPW][KC];
-  int64_t col[TPW];
-  bool col_ok[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = cb * TPB + wave * TPW + t;
-    col[t] = static_cast<int64_t>(tile) * 32 + (lane & 31);
-    col_ok[t] = col[t] < cand_end;
-    const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      bfrag[t][kc] = col_ok[t] ? *reinterpret_cast<const uint4 *>(krow + kc * 16 + half * 8)
-                               : make_uint4(0u, 0u, 0u, 0u);
-  }
-
-  uint4 buf[PER_T];
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int e = 0; e < PER_T; ++e) {
-      const int idx = e * 256 + threadIdx.x;
-      const int row = idx / ROWV, c8 = idx % ROWV;
-      const int grow = st * kStageRows + row;
-      buf[e] = grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
-                        : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_stage = [&](int slot) {
-#pragma unroll
-    for (int e = 0; e < PER_T; ++e) {
-      const int idx = e * 256 + threadIdx.x;
-      const int row = idx / ROWV, c8 = idx % ROWV;
-      *reinterpret_cast<uint4 *>(&qs[slot][row][c8 * 8]) = buf[e];
-    }
-  };
-
-  f32x16 acc[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-
-  const int stages = (M + kStageRows - 1) / kStageRows;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int st = 0; st < stages; ++st) {
-    if (st + 1 < stages) load_stage(st + 1);
-    const int slot = st & 1;
-#pragma unroll
-    for (int sub = 0; sub < kStageRows / 32; ++sub) {
-      const uint16_t *arow = &qs[slot][sub * 32 + (lane & 31)][half * 8];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(arow + kc * 16);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = mfma32<DT>(a, bfrag[t][kc], acc[t]);
-      }
-    }
-    if (st + 1 < stages) store_stage((st + 1) & 1);
-    __syncthreads();
-  }
-  // column = lane & 31; this lane holds 16 of the 32 row residues
-  unsigned long long mn = ~0ull, mx = 0;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const long long v = column_score(acc[t]);
-    if (half == 0 && col_ok[t]) {
-      scores[static_cast<int64_t>(unit) * cand_end + col[t]] = v;
-      const unsigned long long u = ordered_score(v);
-      mn = u < mn ? u : mn;
-      mx = u > mx ? u : mx;
-    }
-  }
-  block_range_out(mn, mx, mm ? mm + 2 * (static_cast<int64_t>(unit) * blocks_per_unit + cb) : nullptr);
-}
-
-// The 16x16x32 form of the same column sums (D = 128), for grids with two
-// blocks per CU: wave w of block cb owns the eight 16-column tiles 32 cb + 8 w
-// + t (128 columns, 512 per block). MFMA kc covers channels 32 kc + 8 g .. +
-// 7 for lane group g = lane / 16, the same order in both operands, so one K
-// load reads 64 contiguous bytes of each of 16 rows (the 32x32 operand layout
-// reads 32 bytes of each of 32 rows, which stalls the texture path). A lane
-// ends with 4 of a column's 16 row residues; the column sums them with the
-// other three lane groups in fp64.
+// Grid: units * ceil(n / (64 NT)) blocks of 4 waves on the 16x16x32 MFMA;
+// wave w of block cb owns the NT 16-column tiles 4 NT cb + NT w + t with their
+// K fragments in registers (NT = 8 while the grid keeps two blocks per CU,
+// else 4). MFMA kc covers channels 32 kc + 8 g .. + 7 for lane group g = lane
+// / 16, the same order in both operands, so one K load reads 64 contiguous
+// bytes of each of 16 rows (the 32x32 operand layout reads 32 bytes of each
+// of 32 rows, which stalled the texture path). The unit's query rows are
+// staged through LDS 128 rows at a time (double buffered; rows padded by 16
+// bytes) and every A fragment feeds all NT tiles; rows congruent mod 16 are
+// summed by the matrix core itself. A lane ends with 4 of a column's 16 row
+// residues; the column sums them with the other three lane groups in fp64
+// (exact on the 2^-4 grid) and rounds once to int64 units of 2^-16.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
@@ -248,16 +134,18 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 }
-template <int DT>
+template <int D, int DT, int NT>
 __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *__restrict__ q_acc,
                                                             const uint16_t *__restrict__ k, int Hq,
                                                             int Hkv, int R, int64_t k_rows,
                                                             int64_t cand_end,
                                                             int64_t *__restrict__ scores,
                                                             unsigned long long *__restrict__ mm) {
-  constexpr int D = 128;
   constexpr int KC = D / 32;                       // MFMAs per 16x16 tile and row chunk
-  constexpr int NT = 8;                            // 16-column tiles per wave
+  constexpr int CPB = 64 * NT;                     // columns per block
+  constexpr int GPB = CPB / 256;                   // 256-candidate score partials per block
+  constexpr int WPG = 4 / GPB;                     // waves per partial
+  static_assert(NT == 4 || NT == 8, "tiles per wave");
   constexpr int ROWV = D / 8;
   constexpr int PER_T = kStageRows * ROWV / 256;
   __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
@@ -266,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   const int wave = threadIdx.x >> 6;
   const int g4 = lane >> 4;                        // lane group: channels 8 g4 .. 8 g4 + 7 of each 32
   const int c16 = lane & 15;                       // column of the tile (B), row of the chunk (A)
-  const int blocks_per_unit = static_cast<int>((cand_end + 511) / 512);
+  const int blocks_per_unit = static_cast<int>((cand_end + CPB - 1) / CPB);
   const int unit = blockIdx.x / blocks_per_unit;
   const int cb = blockIdx.x % blocks_per_unit;
   const int G = Hq / Hkv;
@@ -280,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   bool col_ok[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    col[t] = static_cast<int64_t>(cb) * 512 + (wave * NT + t) * 16 + c16;
+    col[t] = static_cast<int64_t>(cb) * CPB + (wave * NT + t) * 16 + c16;
     col_ok[t] = col[t] < cand_end;
     const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
 #pragma unroll
@@ -350,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
       mx = u > mx ? u : mx;
     }
   }
-  // one partial per 256 candidates: waves 2 g and 2 g + 1 cover group g
+  // one partial per 256 candidates: waves WPG g .. WPG g + WPG - 1 cover group g
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
     const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
@@ -364,12 +252,16 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   __syncthreads();
   const int np = static_cast<int>((cand_end + 255) / 256);   // the top-k's partial count
   const int gi = static_cast<int>(threadIdx.x);
-  if (mm && gi < 2 && cb * 2 + gi < np) {
-    const unsigned long long a0 = rng[2 * gi][0], a1 = rng[2 * gi + 1][0];
-    const unsigned long long c0 = rng[2 * gi][1], c1 = rng[2 * gi + 1][1];
-    unsigned long long *dst = mm + 2 * (static_cast<int64_t>(unit) * np + cb * 2 + gi);
-    dst[0] = a0 < a1 ? a0 : a1;
-    dst[1] = c0 > c1 ? c0 : c1;
+  if (mm && gi < GPB && cb * GPB + gi < np) {
+    unsigned long long a0 = rng[WPG * gi][0], c0 = rng[WPG * gi][1];
+#pragma unroll
+    for (int w = 1; w < WPG; ++w) {
+      a0 = rng[WPG * gi + w][0] < a0 ? rng[WPG * gi + w][0] : a0;
+      c0 = rng[WPG * gi + w][1] > c0 ? rng[WPG * gi + w][1] : c0;
+    }
+    unsigned long long *dst = mm + 2 * (static_cast<int64_t>(unit) * np + cb * GPB + gi);
+    dst[0] = a0;
+    dst[1] = c0;
   }
 }
 
@@ -1560,7 +1452,6 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
   if (cand_end > 0) {
     if (method == HQ_DETECT_MATMUL) {
       const int tiles = static_cast<int>((cand_end + 31) / 32);
-      const int blocks = units * ((tiles + 7) / 8);
       const uint16_t *qa = static_cast<const uint16_t *>(q_acc);
       const uint16_t *kk = static_cast<const uint16_t *>(k);
       const int groups = (tiles + 7) / 8;                    // 256-column groups per unit
@@ -1576,23 +1467,21 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
           hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_BF16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
         else
           hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_F16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
-      } else if (D == 128 && units * ((tiles + 15) / 16) >= 512) {
-        // 512 columns per block while the grid keeps two blocks per CU
-        const int blocks4 = units * ((tiles + 15) / 16);
-        if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma16_colsum_kernel<HQ_BF16>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm);
-        else
-          hipLaunchKernelGGL((mfma16_colsum_kernel<HQ_F16>), dim3(blocks4), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm);
-      } else if (D == 128) {
-        if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
-        else
-          hipLaunchKernelGGL((mfma_colsum_kernel<128, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
       } else {
-        if (dtype == HQ_BF16)
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_BF16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
-        else
-          hipLaunchKernelGGL((mfma_colsum_kernel<64, HQ_F16>), dim3(blocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, tiles, scores, tmm);
+        // the 16x16x32 form: 512 columns per block while the grid keeps two
+        // blocks per CU, else 256
+        const bool wide = static_cast<int64_t>(units) * ((cand_end + 511) / 512) >= 512;
+        const int cpb = wide ? 512 : 256;
+        const dim3 grid(static_cast<unsigned>(units * ((cand_end + cpb - 1) / cpb)));
+#define HQ_C16(DD, TT, NN) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm)
+        if (D == 128) {
+          if (dtype == HQ_BF16) { if (wide) HQ_C16(128, HQ_BF16, 8); else HQ_C16(128, HQ_BF16, 4); }
+          else { if (wide) HQ_C16(128, HQ_F16, 8); else HQ_C16(128, HQ_F16, 4); }
+        } else {
+          if (dtype == HQ_BF16) { if (wide) HQ_C16(64, HQ_BF16, 8); else HQ_C16(64, HQ_BF16, 4); }
+          else { if (wide) HQ_C16(64, HQ_F16, 8); else HQ_C16(64, HQ_F16, 4); }
+        }
+#undef HQ_C16
       }
     } else {
       double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
