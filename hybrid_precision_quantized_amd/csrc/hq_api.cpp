@@ -34,7 +34,7 @@ hq_status check_launch(const char *what) {
 }  // namespace hq
 
 extern "C" const char *hq_status_string(hq_status s) {
-  switch (s) {
+  switch (static_cast<int>(s)) {
     case HQ_OK: return "ok";
     case HQ_ERR_INVALID_ARG: return "invalid argument";
     case HQ_ERR_UNSUPPORTED: return "unsupported shape or dtype";

@@ -1561,6 +1561,13 @@ hq_status validate(const void *q, int q_dtype, int Hq, const hq_hybrid_kv *kv, f
     return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null INT4 plane or VL bitmap");
   if (kv->k > 0 && (!kv->vl_k || !kv->vl_v)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null VL rows");
   if (kv->W > 0 && (!kv->win_k || !kv->win_v)) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null window rows");
+  // dropping the INT4 set with no VL and no window rows leaves nothing to attend to
+  if ((kv->flags & HQ_KV_DROP_INT4) && kv->k == 0 && kv->W == 0)
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: HQ_KV_DROP_INT4 with k == 0 and W == 0 is an empty softmax");
+  // the scale planes and the bitmap are read as 32-bit words
+  if ((reinterpret_cast<uintptr_t>(kv->k_sz) | reinterpret_cast<uintptr_t>(kv->v_sz) |
+       reinterpret_cast<uintptr_t>(kv->vl_bits)) % 4)
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: k_sz, v_sz and vl_bits must be 4-byte aligned");
   const uintptr_t al = reinterpret_cast<uintptr_t>(kv->k_codes) | reinterpret_cast<uintptr_t>(kv->v_codes) |
                        reinterpret_cast<uintptr_t>(kv->vl_k) | reinterpret_cast<uintptr_t>(kv->vl_v) |
                        reinterpret_cast<uintptr_t>(kv->win_k) | reinterpret_cast<uintptr_t>(kv->win_v) |

@@ -12,15 +12,16 @@
 //
 // Kernels:
 //  * acc_kernel      copies this step's queries into the ring slot.
-//  * mfma_colsum     (HQ_DETECT_MATMUL) bf16/fp16 MFMA 32x32x16: each wave
-//    owns two 32-token column tiles with their K fragments in registers and
-//    runs over all rows of the unit (staged through LDS) in 32-row chunks,
-//    accumulating every chunk into the same accumulator (so rows congruent
-//    mod 32 are summed by the matrix core itself); the 32 row sums of a
-//    column are then added in fp64 (exactly on the 2^-4 grid) and rounded
-//    once to int64 units of 2^-16. mfma16_colsum is the 16x16x32 form (eight
-//    16-column tiles per wave) for grids with two blocks per CU, and
-//    colsum_resident keeps the query rows in LDS for long contexts.
+//  * mfma16_colsum   (HQ_DETECT_MATMUL) bf16/fp16 MFMA 16x16x32: each wave
+//    keeps the K fragments of 4 or 8 16-column tiles in registers and runs
+//    over all rows of the unit (staged through LDS, 128 rows at a time) in
+//    16-row chunks, accumulating every chunk into the same accumulator, so
+//    the rows congruent mod 16 (rows numbered head * R + slot) are summed in
+//    fp32 by the matrix core itself. The 16 residue sums of a column are then
+//    added in fp64 and the total is rounded once to int64 units of 2^-16.
+//    On the 2^-4 input grid, with every residue's absolute sum below 2^16,
+//    each fp32 partial is exact and so is the score. colsum_resident is the
+//    same arithmetic with the query rows resident in LDS for long contexts.
 //  * qsum / gemv     (HQ_DETECT_QSUM) the same scores through linearity:
 //    sum the unit's query rows in fp64, then one fp64 dot per key row
 //    (HBM-bound: K is read once).

@@ -57,22 +57,37 @@ extern "C" {
 
 #define HQ_ABI_VERSION 2
 
+/* Each enum below carries two range markers (never returned or accepted) so
+ * that every int is a representable value of the type: a caller passing an
+ * unknown value gets HQ_ERR_INVALID_ARG (or "unknown status") instead of
+ * undefined behaviour in the library. */
 typedef enum {
   HQ_OK = 0,
   HQ_ERR_INVALID_ARG = 1,   /* a null pointer, a size or range out of bounds */
   HQ_ERR_UNSUPPORTED = 2,   /* a valid but unimplemented shape or dtype */
   HQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-  HQ_ERR_HIP = 4            /* the HIP runtime reported an error */
+  HQ_ERR_HIP = 4,           /* the HIP runtime reported an error */
+  HQ_STATUS_RANGE_LO_ = -2147483647 - 1,
+  HQ_STATUS_RANGE_HI_ = 2147483647
 } hq_status;
 
-typedef enum { HQ_F32 = 0, HQ_BF16 = 1, HQ_F16 = 2 } hq_dtype;
+typedef enum {
+  HQ_F32 = 0, HQ_BF16 = 1, HQ_F16 = 2,
+  HQ_DTYPE_RANGE_LO_ = -2147483647 - 1, HQ_DTYPE_RANGE_HI_ = 2147483647
+} hq_dtype;
 
-typedef enum { HQ_LAYOUT_ROWS = 0, HQ_LAYOUT_TILE16 = 1 } hq_code_layout;
+typedef enum {
+  HQ_LAYOUT_ROWS = 0, HQ_LAYOUT_TILE16 = 1,
+  HQ_LAYOUT_RANGE_LO_ = -2147483647 - 1, HQ_LAYOUT_RANGE_HI_ = 2147483647
+} hq_code_layout;
 
 /* Detector forms: the pages' matrix multiplication (MFMA) followed by
  * column sums, or the same scores through the sum of the query rows followed
  * by one matrix-vector product (equal by linearity). */
-typedef enum { HQ_DETECT_MATMUL = 0, HQ_DETECT_QSUM = 1 } hq_detect_method;
+typedef enum {
+  HQ_DETECT_MATMUL = 0, HQ_DETECT_QSUM = 1,
+  HQ_DETECT_RANGE_LO_ = -2147483647 - 1, HQ_DETECT_RANGE_HI_ = 2147483647
+} hq_detect_method;
 
 /*
  * One layer's hybrid KV cache for a decode step [AFS, How It Works: the
@@ -196,12 +211,18 @@ hq_status hq_vl_bitmap(const int32_t *vl_idx, int n_heads, int k, int64_t t_cap,
  * `dtype` (HQ_BF16 or HQ_F16; HQ_F32 only with HQ_DETECT_QSUM).
  * score_out (optional) [B][Hkv][cand_end] int64 receives c_j in units of
  * 2^-16 (rounded to nearest even). With HQ_DETECT_MATMUL the product is formed
- * by bf16/fp16 MFMA with fp32 accumulation: for each residue rho mod 32 the
- * rows congruent to rho are accumulated in fp32, and the 32 sums are added in
- * int64; when every input is a multiple of 2^-4 and every partial sum stays
- * below 2^16 in magnitude the scores are exact. With HQ_DETECT_QSUM the query
- * rows are summed in fp64 and multiplied with each key in fp64 (exact for the
- * same inputs).
+ * by bf16/fp16 MFMA with fp32 accumulation. The unit's rows are numbered
+ * rho = i * R + r (query head i of the group, ring slot r); for each residue
+ * rho mod 16 the rows congruent to it are accumulated by the matrix core in
+ * fp32, the 16 residue sums of a column are added in fp64 and the total is
+ * rounded once to the units. When every input is a multiple of 2^-4 and, for
+ * every column j and residue, the sum over its rows and channels of
+ * |q[rho][d] k[j][d]| stays below 2^16, every fp32 partial is exact and so
+ * are the scores. Otherwise each residue sum carries the fp32 rounding of its
+ * accumulation chain: at most 2 n 2^-24 times that absolute sum, n = (G R /
+ * 16) D products per residue. With HQ_DETECT_QSUM the query rows are summed in
+ * fp64 and multiplied with each key in fp64 (exact for grid inputs within the
+ * fp64 range).
  * *ran (host, optional) is set to 1 when detection was enqueued, else 0.
  * Requires 0 <= k_top <= cand_end <= k_rows, 1 <= R <= 1024, D in {64, 128},
  * Hq % Hkv == 0, ws_bytes >= hq_detect_workspace_size(...).
@@ -279,7 +300,9 @@ size_t hq_detect_workspace_size(int B, int Hkv, int64_t cand_end, int k_top);
  * ws: at least hq_decode_workspace_size(kv, Hq, n_splits) bytes (no
  * initialisation needed). Calls that share a workspace and run concurrently
  * on different streams race; calls on one stream do not.
- * Requires Hq % Hkv == 0 and G in {1, 2, 4, 8, 16}. With D == 128 and
+ * Requires Hq % Hkv == 0 and G in {1, 2, 4, 8, 16}; k_sz, v_sz and vl_bits
+ * 4-byte aligned, the other buffers 16-byte aligned; with HQ_KV_DROP_INT4,
+ * k + W >= 1 (an empty softmax is rejected). With D == 128 and
  * G a multiple of 4, the INT4 keys are dotted with the queries in fp16:
  * bf16 queries must then satisfy |q| < 65504 (magnitudes below 2^-17 round
  * to the fp16 subnormal grid, absolute error below 2^-25).

@@ -76,3 +76,56 @@ def upload_kv(w: synth.Workload, n: int | None = None):
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     rms = float(np.sqrt(np.mean(np.square(ref))))
     return float(np.max(np.abs(got - ref))) / rms
+
+
+# ------------------------------------------------ matrix-core detector bounds
+# The MFMA detector groups a unit's rows rho = i * R + r (query head i of the
+# group, ring slot r) by rho mod 16 and accumulates each group in fp32 (the
+# library header states this arithmetic). These helpers restate its
+# consequences on the host, from the inputs alone.
+N_RESIDUES = 16
+
+
+def residue_abs_sums(q_acc: np.ndarray, K: np.ndarray, b: int, h: int, cand_end: int) -> np.ndarray:
+    """[cand_end][16]: for column j and residue r, the sum over the rows
+    rho = r mod 16 of the unit and all channels of |q[rho][d] k[j][d]|."""
+    B, Hq, R, D = q_acc.shape
+    G = Hq // K.shape[1]
+    rows = np.abs(q_acc[b, h * G:(h + 1) * G].reshape(G * R, D).astype(np.float64))
+    res = np.zeros((N_RESIDUES, D))
+    for r in range(N_RESIDUES):
+        res[r] = rows[r::N_RESIDUES].sum(axis=0)
+    return np.abs(K[b, h, :cand_end].astype(np.float64)) @ res.T
+
+
+def matmul_exact_precondition(q_acc: np.ndarray, K: np.ndarray, cand_end: int) -> float:
+    """Largest residue absolute sum over all units and columns. Below 2^16
+    (with grid inputs) every fp32 partial of the MFMA form is exact."""
+    worst = 0.0
+    for b in range(q_acc.shape[0]):
+        for h in range(K.shape[1]):
+            if cand_end:
+                worst = max(worst, float(residue_abs_sums(q_acc, K, b, h, cand_end).max()))
+    return worst
+
+
+def matmul_score_bound_units(q_acc: np.ndarray, K: np.ndarray, cand_end: int) -> np.ndarray:
+    """[B][Hkv][cand_end] bound, in score units of 2^-16, on |GPU - exact| for
+    the MFMA form on inputs off the grid: each residue's fp32 chain of
+    n = (G R / 16) D products (each exact in fp32) is off by at most
+    2 n 2^-24 times its absolute sum (a factor 2 over round-to-nearest, so
+    that truncating adds are covered too); the fp64 sum of the 16 residues
+    adds at most 16 2^-53 of the total; the final rounding to units half a
+    unit. One unit of slack."""
+    B, Hq, R, D = q_acc.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    n = (G * R + N_RESIDUES - 1) // N_RESIDUES * D
+    out = np.zeros((B, Hkv, cand_end))
+    for b in range(B):
+        for h in range(Hkv):
+            s = residue_abs_sums(q_acc, K, b, h, cand_end)            # [n][16]
+            tot = s.sum(axis=1)
+            err = 2.0 * n * 2.0 ** -24 * tot + 16 * 2.0 ** -53 * tot
+            out[b, h] = np.ceil(err * 65536.0) + 1.5
+    return out

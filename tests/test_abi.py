@@ -182,3 +182,156 @@ def test_detect_rejects_and_accumulate_only_path():
     assert call(step=63, wsb=16) == hq.HQ_ERR_WORKSPACE
     # no q_new and not the last slot: nothing to do, nothing enqueued
     assert call(step=5) == hq.HQ_OK and ran.value == 0
+
+
+def test_decode_rejects_empty_softmax_and_misaligned_words():
+    # dropping the INT4 set with no VL rows and no window leaves nothing to attend to
+    kv = _kv(flags=hq.HQ_KV_DROP_INT4, T=800, k=0, W=0, win_offset=0)
+    assert _decode(kv) == hq.HQ_ERR_INVALID_ARG
+    assert "empty" in hq.hq_last_error()
+    # the scale planes and the VL bitmap are read as 32-bit words
+    for f in ("k_sz", "v_sz", "vl_bits"):
+        assert _decode(_kv(**{f: FAKE + 2})) == hq.HQ_ERR_INVALID_ARG, f
+        assert "4-byte" in hq.hq_last_error()
+    assert _decode(_kv(k_sz=FAKE + 4), ws_bytes=1) == hq.HQ_ERR_WORKSPACE   # 4-byte aligned is enough
+
+
+def test_quantize_pair_rejects():
+    L = hq.lib()
+    ok = dict(xk=FAKE, xv=FAKE, dt=hq.HQ_BF16, nh=2, nr=10, D=128, g=32, xh=1280, xr=128,
+              kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, dhr=64, d0=0)
+
+    def call(**o):
+        a = dict(ok, **o)
+        return L.hq_quantize_kv_pair(a["xk"], a["xv"], a["dt"], a["nh"], a["nr"], a["D"], a["g"], a["xh"],
+                                     a["xr"], a["kc"], a["ks"], a["vc"], a["vs"], a["dhr"], a["d0"], None)
+    assert call(dt=5) == hq.HQ_ERR_INVALID_ARG
+    assert call(g=64) == hq.HQ_ERR_UNSUPPORTED
+    assert call(D=256) == hq.HQ_ERR_UNSUPPORTED
+    assert call(nr=-1) == hq.HQ_ERR_INVALID_ARG
+    assert call(d0=60) == hq.HQ_ERR_INVALID_ARG          # rows past dst_head_rows
+    assert call(dhr=72) == hq.HQ_ERR_INVALID_ARG         # not a multiple of 16 (TILE16 values)
+    assert call(xv=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(vs=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(xr=100) == hq.HQ_ERR_INVALID_ARG         # rows not 16-byte aligned
+    assert call(ks=FAKE + 2) == hq.HQ_ERR_INVALID_ARG    # scale plane not 4-byte aligned
+    assert call(nr=0) == hq.HQ_OK                        # empty: no-op
+
+
+def test_prefill_rejects():
+    L = hq.lib()
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, dt=hq.HQ_BF16, B=1, Hq=8, Hkv=2, T=1000, D=128, g=32, W=128,
+              vl=FAKE, kvl=50, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+
+    def call(**o):
+        a = dict(ok, **o)
+        return L.hq_prefill_attn(a["q"], a["k"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["T"], a["D"],
+                                 a["g"], a["W"], a["vl"], a["kvl"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"],
+                                 None)
+    assert call(dt=hq.HQ_F32) == hq.HQ_ERR_UNSUPPORTED
+    assert call(D=64) == hq.HQ_ERR_UNSUPPORTED
+    assert call(g=16) == hq.HQ_ERR_UNSUPPORTED
+    assert call(T=0) == hq.HQ_ERR_INVALID_ARG
+    assert call(Hq=7) == hq.HQ_ERR_INVALID_ARG
+    assert call(W=-1) == hq.HQ_ERR_INVALID_ARG
+    assert call(kvl=1001) == hq.HQ_ERR_INVALID_ARG        # more VL columns than positions
+    assert call(q=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(out=FAKE + 8) == hq.HQ_ERR_INVALID_ARG    # misaligned
+    need = hq.hq_prefill_workspace_size(1, 8, 2, 1000, 128, 50)
+    assert need > 0
+    assert call(wsb=need - 1) == hq.HQ_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == hq.HQ_ERR_INVALID_ARG    # workspace not 256-byte aligned
+
+
+def test_detect_cache_and_mass_reject():
+    L = hq.lib()
+    ran = ctypes.c_int(7)
+    kv = _kv()
+
+    def cache(**o):
+        a = dict(q_new=None, q_acc=FAKE, dt=hq.HQ_BF16, Hq=8, R=64, step=63, force=0, kv=kv, ce=800,
+                 kt=40, idx=FAKE, sc=None, ws=FAKE, wsb=1 << 30)
+        a.update(o)
+        return L.hq_detect_vlines_cache(a["q_new"], a["q_acc"], a["dt"], a["Hq"], a["R"], a["step"], a["force"],
+                                        ctypes.byref(a["kv"]) if a["kv"] is not None else None, a["ce"],
+                                        a["kt"], a["idx"], a["sc"], ctypes.byref(ran), a["ws"], a["wsb"], None)
+    assert cache(kv=None) == hq.HQ_ERR_INVALID_ARG
+    assert cache(dt=9) == hq.HQ_ERR_INVALID_ARG
+    assert cache(Hq=7) == hq.HQ_ERR_INVALID_ARG
+    assert cache(kv=_kv(D=96)) == hq.HQ_ERR_UNSUPPORTED
+    assert cache(R=0) == hq.HQ_ERR_INVALID_ARG
+    assert cache(step=-1) == hq.HQ_ERR_INVALID_ARG
+    assert cache(ce=1001) == hq.HQ_ERR_INVALID_ARG       # beyond T
+    assert cache(kt=801) == hq.HQ_ERR_INVALID_ARG        # k_top > cand_end
+    assert cache(q_acc=None) == hq.HQ_ERR_INVALID_ARG
+    assert cache(wsb=8) == hq.HQ_ERR_WORKSPACE
+    assert cache(step=5) == hq.HQ_OK and ran.value == 0  # not the ring's last slot: nothing to do
+
+    def mass(**o):
+        a = dict(q_new=None, q_acc=FAKE, dt=hq.HQ_BF16, B=1, Hq=32, Hkv=2, D=128, R=64, step=63, force=0,
+                 k=FAKE, k_rows=1000, ce=900, kt=45, idx=FAKE, sc=None, ws=FAKE, wsb=1 << 30)
+        a.update(o)
+        return L.hq_detect_vlines_mass(a["q_new"], a["q_acc"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                       a["R"], a["step"], a["force"], a["k"], a["k_rows"], a["ce"], a["kt"], 0.0,
+                                       a["idx"], a["sc"], ctypes.byref(ran), a["ws"], a["wsb"], None)
+    assert mass(dt=hq.HQ_F32) == hq.HQ_ERR_UNSUPPORTED
+    assert mass(Hq=31) == hq.HQ_ERR_INVALID_ARG
+    assert mass(D=96) == hq.HQ_ERR_UNSUPPORTED
+    assert mass(R=2000) == hq.HQ_ERR_INVALID_ARG
+    assert mass(ce=1001) == hq.HQ_ERR_INVALID_ARG
+    assert mass(kt=901) == hq.HQ_ERR_INVALID_ARG
+    assert mass(k=None) == hq.HQ_ERR_INVALID_ARG
+    assert mass(wsb=8) == hq.HQ_ERR_WORKSPACE
+    assert mass(k=FAKE + 8) == hq.HQ_ERR_INVALID_ARG     # misaligned keys
+    assert mass(step=5) == hq.HQ_OK and ran.value == 0
+
+
+def test_stream_read_rejects():
+    L = hq.lib()
+    assert L.hq_stream_read(None, 4096, FAKE, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_stream_read(FAKE, 4096, None, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_stream_read(FAKE + 8, 4096, FAKE, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_stream_read(FAKE, 4100, FAKE, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_stream_read(FAKE, 0, FAKE, None) == hq.HQ_OK
+    assert hq.lib().hq_stream_read_sink_bytes() > 0
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+import hybrid_precision_quantized_amd as hq
+L = hq.lib()
+F = 0x100000
+kv = hq.HybridKV()
+kv.B, kv.Hkv, kv.D, kv.group, kv.T, kv.W, kv.k, kv.t_cap = 1, 2, 128, 32, 1000, 128, 40, 896
+for f in ("k_codes", "v_codes", "k_sz", "v_sz", "vl_bits", "vl_k", "vl_v", "win_k", "win_v"):
+    setattr(kv, f, F)
+kv.hp_dtype = hq.HQ_BF16
+calls = {
+    "hq_decode_attn": lambda: L.hq_decode_attn(F, hq.HQ_BF16, 8, ctypes.byref(kv), 0.0, 0, F, None, F, 1 << 40, None),
+    "hq_quantize_kv": lambda: L.hq_quantize_kv(F, hq.HQ_BF16, 2, 10, 128, 32, 2560, 128, F, F, 0, 64, 0, None),
+    "hq_gather_rows": lambda: L.hq_gather_rows(F, hq.HQ_BF16, 2, 100, 128, F, 5, F, None),
+    "hq_vl_bitmap": lambda: L.hq_vl_bitmap(F, 2, 5, 128, F, None),
+    "hq_stream_read": lambda: L.hq_stream_read(F, 4096, F, None),
+}
+for name, fn in calls.items():
+    s = fn()
+    msg = hq.hq_last_error()
+    print(name, s, msg)
+    assert s == hq.HQ_ERR_HIP, (name, s)
+    assert msg, name
+print("NO_DEVICE_OK")
+"""
+
+
+def test_no_device_reports_hip_error():
+    """Without a GPU every valid call fails with HQ_ERR_HIP and a message
+    instead of crashing. Run in a child process (no HIP state leaks into this
+    one) and only where no device is visible: on a GPU machine the same calls
+    would launch kernels on the fake addresses."""
+    import sys
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: this check runs only where none is")
+    r = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT], capture_output=True, text=True,
+                       cwd=ROOT, timeout=300)
+    assert r.returncode == 0 and "NO_DEVICE_OK" in r.stdout, r.stdout + r.stderr

@@ -15,7 +15,7 @@ import torch
 import hybrid_precision_quantized_amd as hq
 import synth
 from oracle import attention, detect, quant
-from tests.gpu_util import TORCH_DT, rel_err, say, tile16_slot, to_dev, upload_kv
+from tests.gpu_util import TORCH_DT, rel_err, say, tile16_codes, tile16_slot, to_dev, upload_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -171,6 +171,36 @@ def _vl_detected(w):
     return K, vl
 
 
+def _check_planes(cache, kp, ks, vp, vs, units, nq):
+    """INT4 planes written by hq_quantize_kv against the oracle quantizer,
+    bit for bit: key codes (rows), value codes (TILE16, compared as logical
+    rows) and both fp16 {scale, zero} planes, for the listed (b, h) units."""
+    kc = cache.k_codes
+    ksz = cache.k_sz
+    vsz = cache.v_sz
+    for i, (b, h) in enumerate(units):
+        assert np.array_equal(kc[b, h, :nq].cpu().numpy(), kp[i]), ("k codes", b, h)
+        assert np.array_equal(ksz[b, h, :nq].cpu().numpy().view(np.uint16), ks[i]), ("k s/z", b, h)
+        assert np.array_equal(vsz[b, h, :nq].cpu().numpy().view(np.uint16), vs[i]), ("v s/z", b, h)
+        vrows = tile16_codes(cache.v_codes[b, h])[:nq]
+        assert np.array_equal(vrows, vp[i]), ("v codes", b, h)
+
+
+def test_quantize_full_llama32k_planes():
+    """Every INT4 code and fp16 scale/zero of the Llama-shaped 32K layer
+    (8 KV heads x 32640 rows, K and V) bit-exact against the oracle."""
+    w = synth.WORKLOADS["llama32k"]
+    say("quantize full llama32k planes")
+    K, V = synth.all_keys(w), synth.all_values(w)
+    nq = w.T - w.W
+    cache = hq.HybridCache(w.B, w.Hkv, w.D, w.T, w.W, w.k, TORCH_DT[w.dtype])
+    cache.quantize(to_dev(K, w.dtype), to_dev(V, w.dtype))
+    torch.cuda.synchronize()
+    kp, ks = quant.quantize_rows(K[0, :, :nq])
+    vp, vs = quant.quantize_rows(V[0, :, :nq])
+    _check_planes(cache, kp, ks, vp, vs, [(0, h) for h in range(w.Hkv)], nq)
+
+
 @pytest.mark.parametrize("name", ["llama32k", "glm32k"])
 def test_decode_full_workload(name):
     w = synth.WORKLOADS[name]
@@ -207,14 +237,19 @@ def test_decode_qwen128k_sampled():
     say("decode qwen128k (oracle)")
     ro = np.full((w.B, w.Hq, w.D), np.nan)
     rl = np.full((w.B, w.Hq), np.nan)
+    planes = ([], [], [], [])
     for b, h in units:
         Kh = synth.keys(w, b, h)
         Vh = synth.values(w, b, h)
         kp, ks = quant.quantize_rows(Kh[:w.T - w.W])
         vp, vs = quant.quantize_rows(Vh[:w.T - w.W])
+        for lst, x in zip(planes, (kp, ks, vp, vs)):
+            lst.append(x)
         sl = slice(h * w.G, (h + 1) * w.G)
         ro[b, sl], rl[b, sl] = attention.decode_head(q[b, sl], Kh, Vh, kp, ks, vp, vs, vl[b, h], w.W)
     _check(got, (ro, rl), units=units, G=w.G)
+    say("decode qwen128k (INT4 planes of the sampled units, bit for bit)")
+    _check_planes(cache, *planes, units, w.T - w.W)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,D,T,W,k,dtype", [
@@ -251,3 +286,44 @@ def test_decode_drop_int4(B, Hq, Hkv, D, T, W, k, dtype):
         sl = slice(h * G, (h + 1) * G)
         ro[b, sl], rl[b, sl] = attention.decode_sparse_head(q[b, sl], K[b, h], V[b, h], vl[b, h], W)
     _check((out.cpu().numpy(), lse.cpu().numpy()), (ro, rl), units=units, G=G)
+
+
+OFF_GRID = [
+    # B, Hq, Hkv, D, T, W, k, dtype, what
+    (1, 8, 2, 128, 3000, 128, 100, "bf16", "plain"),    # G = 4, D = 128: the matrix-core INT4 pass
+    (1, 8, 2, 128, 2500, 64, 70, "f16", "plain"),
+    (1, 32, 2, 128, 2049, 128, 90, "bf16", "plain"),    # G = 16
+    (2, 16, 8, 64, 1500, 32, 40, "bf16", "plain"),      # G = 2, D = 64
+    (1, 8, 8, 128, 777, 16, 5, "f16", "plain"),         # G = 1
+    (1, 8, 2, 128, 3000, 128, 100, "bf16", "tiny_q"),   # half the channels of q below 2^-17
+    (1, 8, 2, 128, 3000, 128, 100, "f16", "tiny_q"),
+    (1, 8, 2, 128, 3000, 128, 100, "bf16", "huge_q"),   # |q| up to ~6.5e4, keys scaled by 2^-14
+    (1, 8, 2, 128, 3000, 128, 100, "f16", "huge_q"),
+]
+
+
+@pytest.mark.parametrize("case", OFF_GRID, ids=[str(c) for c in OFF_GRID])
+def test_decode_off_grid(case):
+    """Plain bf16 / fp16 draws (no 2^-4 grid) for K and q, and queries at
+    the ends of the fp16 range the D = 128 INT4 pass converts them to: tiny
+    magnitudes (the fp16 subnormal grid, absolute error below 2^-25) and
+    magnitudes near 6.5e4 (the largest the fast path admits) with keys
+    scaled so that the logits stay of order one."""
+    B, Hq, Hkv, D, T, W, k, dtype, what = case
+    seed = zlib.crc32(str(case).encode()) % 10000 + 20000
+    w = synth.Workload(f"offgrid{seed}", seed, B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, W=W, k=k, dtype=dtype,
+                       grid=False, n_plant=max(1, int(0.02 * T)))
+    say(f"decode off-grid {case}")
+    K, V, q = synth.all_keys(w), synth.all_values(w), synth.all_queries(w)
+    assert not detect.on_grid(K) and not detect.on_grid(q)
+    if what == "tiny_q":
+        q = q.copy()
+        q[..., 1::2] = synth.round_dtype(q[..., 1::2].astype(np.float64) * 2.0 ** -20, dtype)
+        assert np.all(np.abs(q[..., 1::2]) < 2.0 ** -17)
+    elif what == "huge_q":
+        q = synth.round_dtype(np.clip(q.astype(np.float64) * 15000.0, -65000.0, 65000.0), dtype)
+        K = synth.round_dtype(K.astype(np.float64) * 2.0 ** -14, dtype)
+        assert 6.0e4 < np.abs(q).max() < 65504.0
+    vl = _vl_random(w)
+    got = _gpu_decode(w, K, V, q, vl)
+    _check(got, _oracle(w, K, V, q, vl))

@@ -12,15 +12,22 @@ import torch
 import hybrid_precision_quantized_amd as hq
 import synth
 from oracle import detect, quant
-from tests.gpu_util import TORCH_DT, say, to_dev
+from tests.gpu_util import (TORCH_DT, matmul_exact_precondition, matmul_score_bound_units, say,
+                            to_dev)
 
 pytestmark = pytest.mark.gpu
 
 METHODS = [hq.HQ_DETECT_MATMUL, hq.HQ_DETECT_QSUM]
 
 
-def _run(q_acc, K, cand_end, k_top, method, dtype):
+def _run(q_acc, K, cand_end, k_top, method, dtype, exact=True):
     B, Hq, R, D = q_acc.shape
+    if exact and method == hq.HQ_DETECT_MATMUL:
+        # the matrix-core form is exact on grid inputs only while every
+        # residue's absolute sum stays below 2^16 (its fp32 partials exact)
+        worst = matmul_exact_precondition(q_acc, K, cand_end)
+        assert worst < 2.0 ** 16, f"inputs outside the exact range of the MFMA form: {worst}"
+
     Hkv, k_rows = K.shape[1], K.shape[2]
     qd = to_dev(q_acc, dtype)
     kd = to_dev(K, dtype)
@@ -316,3 +323,56 @@ def test_detect_many_units_long_rows(method):
     got_idx, got_sc = _run(q, K, ce, k_top, method, "bf16")
     assert np.array_equal(got_sc, want_sc)
     assert np.array_equal(got_idx, want_idx)
+
+
+def _check_near_ties(got_idx, got_sc, want_idx, want_sc, bound, k_top):
+    """Scores within their bound of the exact ones; the index sets equal
+    except for positions whose exact score lies within twice the bound of the
+    k-th largest exact score (there the fp32 rounding may order either way);
+    every returned set ascending and of the right size."""
+    B, Hkv, _ = want_sc.shape
+    worst = 0.0
+    n_swapped = 0
+    for b in range(B):
+        for h in range(Hkv):
+            err = np.abs(got_sc[b, h] - want_sc[b, h]).astype(np.float64)
+            assert np.all(err <= bound[b, h]), (b, h, float((err - bound[b, h]).max()))
+            worst = max(worst, float((err / bound[b, h]).max()))
+            if k_top == 0:
+                continue
+            assert len(got_idx[b, h]) == k_top and np.all(np.diff(got_idx[b, h]) > 0)
+            tau = np.sort(want_sc[b, h])[::-1][k_top - 1]
+            diff = np.setxor1d(got_idx[b, h], want_idx[b, h])
+            n_swapped += len(diff)
+            assert np.all(np.abs(want_sc[b, h][diff] - tau) <= 2 * bound[b, h][diff]), (b, h, diff)
+    say(f"   max |err| / bound = {worst:.2e}; positions swapped at the cut: {n_swapped}")
+
+
+@pytest.mark.parametrize("case", ["glm32k", "llama32k", "small_f16", "small_g1"])
+def test_detect_matmul_off_grid(case):
+    """The MFMA form on plain bf16/fp16 inputs (no 2^-4 grid): queries
+    N(0, 1) + 7 u and keys with outlier channels and planted lines, as the
+    GLM-4-9B-shaped detector workload draws them. The exact scores are the
+    oracle's float64 ones; the GPU's differ by the fp32 rounding of each
+    residue chain, bounded from the inputs, and the sets may differ only at
+    near ties of the k-th score."""
+    if case in ("glm32k", "llama32k"):
+        w = synth.WORKLOADS[case].replace(grid=False)
+    elif case == "small_f16":
+        w = synth.Workload("offgrid_f16", 4711, B=2, Hq=8, Hkv=2, D=128, T=3000, W=100, k=150,
+                           dtype="f16", grid=False)
+    else:
+        w = synth.Workload("offgrid_g1", 4712, B=1, Hq=4, Hkv=4, D=64, T=2000, W=64, k=90,
+                           dtype="bf16", grid=False, R=33)
+    say(f"detect matmul off-grid {case}")
+    K = synth.all_keys(w)
+    q = synth.all_query_histories(w)
+    assert not detect.on_grid(q) and not detect.on_grid(K)
+    ce = w.T - w.W
+    want_idx, want_sc = detect.detect(q, K, ce, w.k, require_exact=False)
+    got_idx, got_sc = _run(q, K, ce, w.k, hq.HQ_DETECT_MATMUL, w.dtype, exact=False)
+    bound = matmul_score_bound_units(q, K, ce)
+    _check_near_ties(got_idx, got_sc, want_idx, want_sc, bound, w.k)
+    # and run to run the same bits
+    again_idx, again_sc = _run(q, K, ce, w.k, hq.HQ_DETECT_MATMUL, w.dtype, exact=False)
+    assert np.array_equal(again_sc, got_sc) and np.array_equal(again_idx, got_idx)
