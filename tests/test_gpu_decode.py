@@ -321,7 +321,9 @@ def test_decode_off_grid(case):
         q[..., 1::2] = synth.round_dtype(q[..., 1::2].astype(np.float64) * 2.0 ** -20, dtype)
         assert np.all(np.abs(q[..., 1::2]) < 2.0 ** -17)
     elif what == "huge_q":
-        q = synth.round_dtype(np.clip(q.astype(np.float64) * 15000.0, -65000.0, 65000.0), dtype)
+        q = np.clip(q.astype(np.float64) * 15000.0, -65000.0, 65000.0)
+        q[..., 5] = 65000.0 * np.where(np.arange(Hq) % 2, 1.0, -1.0)   # one channel at the top of the range
+        q = synth.round_dtype(q, dtype)
         K = synth.round_dtype(K.astype(np.float64) * 2.0 ** -14, dtype)
         assert 6.0e4 < np.abs(q).max() < 65504.0
     vl = _vl_random(w)
