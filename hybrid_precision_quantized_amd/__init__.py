@@ -93,6 +93,9 @@ _SIGS = {
                                       ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_void_p]),
     "hq_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HybridKV), ctypes.c_int, ctypes.c_int]),
+    "hq_decode_attn_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                              ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_stream_read_sink_bytes": (ctypes.c_size_t, []),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
@@ -258,6 +261,16 @@ def hq_decode_attn(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, ws, stream
     _check(lib().hq_decode_attn(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
                                 n_splits, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream)))
+
+
+def hq_decode_attn_noalloc(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, stream=None):
+    """hq_decode_attn with the split partials in the library's fixed device
+    array instead of a workspace (for callers that cannot allocate)."""
+    _check(lib().hq_decode_attn_noalloc(_ptr(q), _dt(q), Hq, ctypes.byref(kv), float(sm_scale),
+                                        n_splits, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+HQ_DECODE_SCRATCH_BYTES = 16 << 20
 
 
 def hq_stream_read(buf, sink, stream=None):

@@ -47,6 +47,7 @@
 #include <math.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "hq_common.h"
 #include "hq_int4.h"
@@ -1705,6 +1706,65 @@ extern "C" hq_status hq_decode_attn(const void *q, hq_dtype q_dtype, int Hq, con
                                     stream);
   if (s != HQ_OK) return s;
   return check_launch("hq_decode_attn");
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// The split partials of hq_decode_attn live in a fixed device array instead
+// of a caller's workspace, for callers that cannot allocate. Each device the
+// library runs on holds its own copy of the array until the process ends.
+// In host code the array's name is only a stand-in: its device address is
+// looked up once per device with hipGetSymbolAddress (under a lock, with
+// that device current) and only that address is handed to the kernels.
+namespace hq {
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;       // HQ_DECODE_SCRATCH_BYTES
+static_assert(kScratchBytes == HQ_DECODE_SCRATCH_BYTES, "header and library agree on the scratch size");
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hq_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HQ_ERR_HIP, "hq_decode_attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HQ_ERR_HIP, "hq_decode_attn_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HQ_OK;
+}
+}  // namespace
+}  // namespace hq
+
+extern "C" hq_status hq_decode_attn_noalloc(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                                            float sm_scale, int n_splits, float *out, float *lse, void *stream) {
+  // every host-checkable precondition first, so that a rejected call touches no device
+  const hq_status v = validate(q, q_dtype, Hq, kv, out);
+  if (v != HQ_OK) return v;
+  if (n_splits < 0) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn_noalloc: n_splits < 0");
+  const Plan pl = make_plan(kv, Hq, n_splits);
+  if (pl.S > kMaxSplits)
+    return fail(HQ_ERR_UNSUPPORTED, "hq_decode_attn_noalloc: %d splits exceed the maximum %d", pl.S, kMaxSplits);
+  const size_t need = ws_layout(kv, Hq, pl).total;
+  if (need > kScratchBytes)
+    return fail(HQ_ERR_WORKSPACE,
+                "hq_decode_attn_noalloc: these sizes need %zu bytes of split partials, above the fixed %zu "
+                "(use fewer splits or hq_decode_attn with a workspace)", need, kScratchBytes);
+  void *ws = nullptr;
+  const hq_status s = scratch_for_current_device(&ws);
+  if (s != HQ_OK) return s;
+  const hq_status r = decode_common(q, q_dtype, Hq, kv, sm_scale, n_splits, out, lse, ws, kScratchBytes, Upkeep{},
+                                    stream);
+  if (r != HQ_OK) return r;
+  return check_launch("hq_decode_attn_noalloc");
 }
 
 extern "C" hq_status hq_decode_step(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,

@@ -341,6 +341,30 @@ hq_status hq_decode_step(const void *q, hq_dtype q_dtype, int Hq, const hq_hybri
 
 size_t hq_decode_workspace_size(const hq_hybrid_kv *kv, int Hq, int n_splits);
 
+/*
+ * hq_decode_attn_noalloc -- hq_decode_attn without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same arguments,
+ * results and errors as hq_decode_attn (bitwise the same outputs for the
+ * same inputs and n_splits); the split partials go to a fixed device array
+ * of HQ_DECODE_SCRATCH_BYTES inside the library instead of `ws`. It calls
+ * no allocation routine. Each GPU it runs on holds its own copy of that
+ * array until the process ends; the first call on a device looks up the
+ * array's address there. Limits and sharing:
+ *  - HQ_ERR_WORKSPACE (nothing enqueued, no device touched) when the split
+ *    partials of these sizes would exceed HQ_DECODE_SCRATCH_BYTES, i.e. when
+ *    hq_decode_workspace_size(kv, Hq, n_splits) > HQ_DECODE_SCRATCH_BYTES
+ *    (16 sequences x 32 query heads at the automatic split count need about
+ *    6 MB);
+ *  - every call on one GPU shares that GPU's array, and each call overwrites
+ *    it before reading it (nothing needs clearing), so calls that overlap in
+ *    time on one GPU (different streams, or host threads without ordering)
+ *    race; calls on one stream do not.
+ */
+#define HQ_DECODE_SCRATCH_BYTES (16u << 20)
+hq_status hq_decode_attn_noalloc(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid_kv *kv,
+                                 float sm_scale, int n_splits, float *out, float *lse, void *stream);
+
 /* The split count hq_decode_attn uses for n_splits == 0. */
 int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
 

@@ -335,3 +335,20 @@ def test_no_device_reports_hip_error():
     r = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT], capture_output=True, text=True,
                        cwd=ROOT, timeout=300)
     assert r.returncode == 0 and "NO_DEVICE_OK" in r.stdout, r.stdout + r.stderr
+
+
+def test_decode_noalloc_rejects_before_touching_a_device():
+    L = hq.lib()
+
+    def call(kv, Hq=8, n_splits=0, q=FAKE, out=FAKE):
+        return L.hq_decode_attn_noalloc(q, hq.HQ_BF16, Hq, ctypes.byref(kv) if kv is not None else None,
+                                        0.0, n_splits, out, None, None)
+    assert call(None) == hq.HQ_ERR_INVALID_ARG
+    assert call(_kv(D=96)) == hq.HQ_ERR_UNSUPPORTED
+    assert call(_kv(), q=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(_kv(), n_splits=-1) == hq.HQ_ERR_INVALID_ARG
+    # more split partials than the fixed array holds: 16 x 32 heads x 256 splits
+    big = _kv(B=16, Hkv=8, T=4096, W=128, k=100, t_cap=4096)
+    assert hq.hq_decode_workspace_size(big, 32, 256) > hq.HQ_DECODE_SCRATCH_BYTES
+    assert call(big, Hq=32, n_splits=256) == hq.HQ_ERR_WORKSPACE
+    assert "fixed" in hq.hq_last_error()
