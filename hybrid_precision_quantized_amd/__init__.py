@@ -43,6 +43,7 @@ class HybridKV(ctypes.Structure):
         ("vl_k", ctypes.c_void_p), ("vl_v", ctypes.c_void_p),
         ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
         ("win_offset", ctypes.c_int), ("hp_dtype", ctypes.c_int), ("flags", ctypes.c_int),
+        ("win_cap", ctypes.c_int),
     ]
 
 
@@ -96,6 +97,9 @@ _SIGS = {
     "hq_decode_attn_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "hq_vl_update": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_stream_read_sink_bytes": (ctypes.c_size_t, []),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
@@ -273,6 +277,15 @@ def hq_decode_attn_noalloc(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, st
 HQ_DECODE_SCRATCH_BYTES = 16 << 20
 
 
+def hq_vl_update(kv: HybridKV, vl_idx, p0, scores, score_stride, k_new, new_idx, new_vl_k, new_vl_v,
+                 vl_bits, stream=None):
+    """Apply a re-detection to a rolling cache: the k_new best of the current
+    VL set and the positions [p0, T - W) still in the ring (see include/hq.h)."""
+    _check(lib().hq_vl_update(ctypes.byref(kv), _ptr(vl_idx), int(p0), _ptr(scores), int(score_stride),
+                              int(k_new), _ptr(new_idx), _ptr(new_vl_k), _ptr(new_vl_v), _ptr(vl_bits),
+                              _stream(stream)))
+
+
 def hq_stream_read(buf, sink, stream=None):
     """One sequential read of the whole tensor `buf` (measurement utility)."""
     _check(lib().hq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
@@ -320,4 +333,4 @@ def hq_abi_version() -> int:
     return int(lib().hq_abi_version())
 
 
-from .cache import HybridCache  # noqa: E402,F401
+from .cache import HybridCache, RollingCache  # noqa: E402,F401

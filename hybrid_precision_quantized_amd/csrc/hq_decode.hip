@@ -77,6 +77,7 @@ struct DecodeParams {
   int64_t nq;               // T - W
   int64_t bits_words;       // words per head of vl_bits
   int k, W, win_offset;
+  int win_cap;              // rows of the window ring (>= W)
   int B, Hkv, Hq, G, nhc;   // nhc = head chunks per KV head
   int S_q, S_vl, S_win, S;  // splits per unit: INT4, VL rows, window rows
   int64_t len_q;            // positions per INT4 split (multiple of 64)
@@ -845,9 +846,9 @@ __device__ __forceinline__ int64_t fp_row(const DecodeParams &P, int64_t head, i
   rr = rr < r1 ? rr : r1 - 1;
   *in_vl = rr < P.k;
   if (rr < P.k) return (head * P.k + rr) * D;
-  int wi = P.win_offset + static_cast<int>(rr - P.k);     // < 2 W
-  wi -= (wi >= P.W) ? P.W : 0;
-  return (head * P.W + wi) * D;
+  int wi = P.win_offset + static_cast<int>(rr - P.k);     // < win_cap + W <= 2 win_cap
+  wi -= (wi >= P.win_cap) ? P.win_cap : 0;
+  return (head * P.win_cap + wi) * D;
 }
 
 template <int HT>
@@ -1048,15 +1049,15 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
     vbase = static_cast<const uint8_t *>(P.vl_v) + (head * P.k + r0) * RB;
     kbytes = n * RB;
   } else {
-    // the head's ring of W rows; list row k + w is ring row (win_offset + w) mod W
-    kbase = static_cast<const uint8_t *>(P.win_k) + head * P.W * RB;
-    vbase = static_cast<const uint8_t *>(P.win_v) + head * P.W * RB;
-    kbytes = static_cast<uint32_t>(P.W) * RB;
-    wrow0 = P.win_offset + static_cast<int>(r0 - P.k);      // ring row of the split's first row, < 2 W
+    // the head's ring of win_cap rows; list row k + w is ring row (win_offset + w) mod win_cap
+    kbase = static_cast<const uint8_t *>(P.win_k) + head * P.win_cap * RB;
+    vbase = static_cast<const uint8_t *>(P.win_v) + head * P.win_cap * RB;
+    kbytes = static_cast<uint32_t>(P.win_cap) * RB;
+    wrow0 = P.win_offset + static_cast<int>(r0 - P.k);      // ring row of the split's first row, < win_cap + W
   }
-  auto ring_row = [&](int w) {                                // w < 3 W
-    w -= (w >= P.W) ? P.W : 0;
-    w -= (w >= P.W) ? P.W : 0;
+  auto ring_row = [&](int w) {                                // w < win_cap + 2 W <= 3 win_cap
+    w -= (w >= P.win_cap) ? P.win_cap : 0;
+    w -= (w >= P.win_cap) ? P.win_cap : 0;
     return w;
   };
 
@@ -1304,7 +1305,7 @@ __device__ void upkeep(const DecodeParams &P, int ub) {
   const int64_t hd = item / NG;                             // b * Hkv + h
   const void *src = is_v ? P.win_v : P.win_k;
   float v[8];
-  load8<QT>(src, (hd * P.W + P.win_offset) * D + g * 32 + qq * 8, v);
+  load8<QT>(src, (hd * P.win_cap + P.win_offset) * D + g * 32 + qq * 8, v);
   _Float16 s16, z16;
   const uint32_t packed = encode_quarter(v, s16, z16);
   const int64_t row = P.nq;                                 // position T - W
@@ -1536,6 +1537,9 @@ WsLayout ws_layout(const hq_hybrid_kv *kv, int Hq, const Plan &pl) {
   return L;
 }
 
+// rows of the window ring: win_cap, or W when win_cap is 0
+int ring_rows(const hq_hybrid_kv *kv) { return kv->win_cap > 0 ? kv->win_cap : kv->W; }
+
 hq_status validate(const void *q, int q_dtype, int Hq, const hq_hybrid_kv *kv, float *out) {
   if (!kv) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null descriptor");
   if (kv->B < 1 || kv->Hkv < 1 || Hq < 1) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: B, Hkv, Hq must be >= 1");
@@ -1553,7 +1557,9 @@ hq_status validate(const void *q, int q_dtype, int Hq, const hq_hybrid_kv *kv, f
   if (kv->k < 0 || kv->k > kv->T - kv->W) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: need 0 <= k <= T - W");
   if (kv->t_cap < kv->T - kv->W || kv->t_cap % 32 != 0)
     return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: t_cap must be >= T - W and a multiple of 32");
-  if (kv->W > 0 && (kv->win_offset < 0 || kv->win_offset >= kv->W))
+  if (kv->win_cap != 0 && kv->win_cap < kv->W)
+    return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: win_cap must be 0 or >= W");
+  if (kv->W > 0 && (kv->win_offset < 0 || kv->win_offset >= ring_rows(kv)))
     return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: win_offset out of range");
   if (!q || !out) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: null q or out");
   if (kv->flags & ~HQ_KV_DROP_INT4) return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: unknown flags");
@@ -1660,6 +1666,7 @@ hq_status decode_common(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid
   P.k = kv->k;
   P.W = kv->W;
   P.win_offset = kv->win_offset;
+  P.win_cap = ring_rows(kv);
   P.B = kv->B;
   P.Hkv = kv->Hkv;
   P.Hq = Hq;

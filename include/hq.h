@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 2
+#define HQ_ABI_VERSION 3
 
 /* Each enum below carries two range markers (never returned or accepted) so
  * that every int is a representable value of the type: a caller passing an
@@ -117,11 +117,16 @@ typedef struct {
                                  iff position t is a VL position */
   const void *vl_k, *vl_v;    /* [B][Hkv][k][D] hp_dtype, VL rows in ascending
                                  position order */
-  const void *win_k, *win_v;  /* [B][Hkv][W][D] hp_dtype, ring buffer: position
-                                 T - W + i sits in row (win_offset + i) % W */
-  int win_offset;             /* 0 <= win_offset < W (0 when W == 0) */
+  const void *win_k, *win_v;  /* [B][Hkv][C][D] hp_dtype, ring buffer of C = win_cap
+                                 rows (C = W when win_cap == 0): position T - W + i
+                                 sits in row (win_offset + i) % C */
+  int win_offset;             /* 0 <= win_offset < C (0 when W == 0) */
   hq_dtype hp_dtype;          /* dtype of the 16-bit rows: HQ_BF16, HQ_F16 or HQ_F32 */
   int flags;                  /* 0, or HQ_KV_DROP_INT4 */
+  int win_cap;                /* 0, or the ring's row count C >= W. With C > W the
+                                 ring also keeps the 16-bit rows of the C - W positions
+                                 that left the window last, [T - C, T - W) (those
+                                 >= 0), which hq_vl_update can promote */
 } hq_hybrid_kv;
 
 /* hq_hybrid_kv.flags. HQ_KV_DROP_INT4 leaves the INT4 positions out of the
@@ -367,6 +372,38 @@ hq_status hq_decode_attn_noalloc(const void *q, hq_dtype q_dtype, int Hq, const 
 
 /* The split count hq_decode_attn uses for n_splits == 0. */
 int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
+
+/*
+ * hq_vl_update -- apply a re-detection to a rolling hybrid cache [WPN, body
+ * paragraph 4: the detector runs every 64 tokens; AFS, How It Works, items
+ * 1-2: only the vertical-line tokens and a recent window are kept in 16 bits,
+ * the rest in 4 bits]. A decode-time cache holds 16-bit rows only for its
+ * VL set and its window ring, so a position can be promoted only while its
+ * 16-bit row still exists (a reading of the pages, which say nothing on it).
+ * For every (b, h) the candidates are the current VL positions
+ * vl_idx[b][h][0..kv->k) (ascending, all below p0: not checked on the
+ * device) and the positions [p0, T - W) that left the window since the last
+ * update, whose rows are still in the ring (kv->win_cap > W). The new set is
+ * the k_new candidates with the largest scores[b][h][position] (int64, rows
+ * of score_stride >= T - W entries, e.g. the score_out of a detector call
+ * over cand_end = T - W), equal scores to the lower position:
+ *   new_idx [B][Hkv][k_new] ascending;
+ *   new_vl_k, new_vl_v [B][Hkv][k_new][D] (kv->hp_dtype): the 16-bit rows of
+ *     the new set, copied from kv->vl_k / kv->vl_v or from the ring;
+ *   vl_bits [B][Hkv][t_cap/32] (may be kv->vl_bits), updated in place: the
+ *     bits of dropped VL positions cleared (they fall back to their INT4
+ *     rows, which exist for every position), those of promoted ones set.
+ * The ring must hold every position of [T - C, T) (C = ring rows) when the
+ * call runs. Afterwards the caller uses new_idx / new_vl_k / new_vl_v with
+ * k = k_new, and passes p0 = T - W at the next update.
+ * Requires max(0, T - C) <= p0 <= T - W, 0 <= k_new <= kv->k + (T - W - p0),
+ * at most 8192 candidates per head (else HQ_ERR_UNSUPPORTED), D in {64, 128},
+ * 16-byte aligned rows, new buffers not overlapping the old ones or the ring
+ * (HQ_ERR_INVALID_ARG otherwise). No workspace; nothing enqueued on error.
+ */
+hq_status hq_vl_update(const hq_hybrid_kv *kv, const int32_t *vl_idx, int64_t p0, const int64_t *scores,
+                       int64_t score_stride, int k_new, int32_t *new_idx, void *new_vl_k, void *new_vl_v,
+                       uint32_t *vl_bits, void *stream);
 
 /*
  * hq_prefill_attn -- causal hybrid-precision prefill attention [AFS, The

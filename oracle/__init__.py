@@ -26,6 +26,8 @@ token sets; raw-logit column scores; lower index wins score ties).
 
 Modules: ``quant`` (INT4 encode/decode), ``attention`` (hybrid decode
 attention and the LSE merge), ``detect`` (vertical-line detector),
-``prefill`` (hybrid prefill operator).
+``prefill`` (hybrid prefill operator), ``lifecycle`` (the rolling cache over
+many decode steps: re-detection every R steps among the positions that still
+have 16-bit rows).
 """
-from . import quant, attention, detect, prefill  # noqa: F401
+from . import quant, attention, detect, prefill, lifecycle  # noqa: F401

@@ -37,7 +37,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_strings():
-    assert hq.hq_abi_version() == 2
+    assert hq.hq_abi_version() == 3
     assert hq.hq_status_string(0) == "ok"
     assert "workspace" in hq.hq_status_string(3)
 

@@ -13,7 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "hybrid_precision_quantized_amd", "csrc")
 SOURCES = ["hq_api.cpp", "hq_quantize.hip", "hq_decode.hip", "hq_detect.hip", "hq_prefill.hip",
-           "hq_stream.hip"]
+           "hq_stream.hip", "hq_lifecycle.hip"]
 
 
 def _hipcc():
