@@ -1,30 +1,33 @@
 """Benchmark of the HyQuant decode hot path on one MI355X.
 
 One step = one steady-state decode step of one attention layer over its
-hybrid KV cache:
+rolling hybrid KV cache (16-bit rows only for the VL set and a window ring
+of W + 64 rows, everything else INT4):
   1. hq_decode_step: attention over INT4 + VL + window with the split-K LSE
      merge; in the same launches the step's queries go into the detector's
      64-slot ring and the window's oldest token is packed into INT4;
-  2. every 64th step (step mod 64 == 63) hq_detect_vlines scores the ring
-     (Q_acc . K^T column sums, top-k) and the new VL set is installed for the
-     next step (hq_vl_bitmap + hq_gather_rows of the VL keys and values).
-With --separate-upkeep the upkeep runs as its own calls before the
-attention (hq_detect_vlines with the new queries, hq_quantize_kv_pair, then
-hq_decode_attn), four launches per step instead of two.
-Steps rotate over `--copies` independent layer caches (>= 1 GB in total) so
-that the 256 MB Infinity Cache cannot hold the working set: every step reads
-its cache from HBM as it would in a model with many layers. All inputs are
-seeded synthetic tensors already resident in HBM when timing starts.
+  2. every 64th step a re-detection: column scores of every position from
+     the INT4 keys and the 64 accumulated steps (hq_detect_vlines_cache),
+     then hq_vl_update re-chooses the VL set among the current one and the
+     ring rows behind the window. It is timed on its own and 1/64 of it is
+     added to the step time, so that any --steps includes its share.
+The decode steps rotate over `--copies` independent layer caches (>= 1 GB of
+decode-read bytes in total) so that the 256 MB Infinity Cache cannot hold
+the working set: every step reads its cache from HBM as it would in a model
+with many layers. All inputs are seeded synthetic tensors already resident
+in HBM when timing starts; the 16-bit source rows a prefill would leave are
+freed once the caches are built.
 
 Prints one JSON line (rank 0). `value` is the algorithmic HBM bytes of a
-step divided by the measured step time (GB/s); `ms_per_step` is the step
-time. `roofline` is the decode call alone (split kernel + merge kernel),
-timed with HIP events on the launch stream around back-to-back calls (and,
-for the spread, per call: p10 / p50 / p90), beside the HBM read
-ceiling (a 2 GiB sequential read), the time of a plain read of the call's
-own bytes at the same size, and the median of launches that reuse one cache
-copy ("warm": what the Infinity Cache can hold may come from it).
-`cpu_baseline` is the CPU oracle on a bounded sample of the same step.
+step divided by the step time (GB/s); `ms_per_step` is the step time.
+`roofline` is the decode call alone (split kernel + merge kernel), timed
+with HIP events on the launch stream around back-to-back calls (and, for the
+spread, per call: p10 / p50 / p90), beside the HBM read ceiling (a 2 GiB
+sequential read), the time of a plain read of the call's own bytes at the
+same size, and the median of launches that reuse one cache copy ("warm").
+`long_context` (default workload only) is the 16 x 128K workload in the
+same run. `cpu_baseline` is the CPU oracle on a bounded sample of the same
+step, in a process pool.
 """
 from __future__ import annotations
 
@@ -56,21 +59,22 @@ def parse():
                     choices=["llama32k", "qwen128k", "glm32k", "prefill32k"],
                     help="decode workloads, or prefill32k: the causal hybrid prefill of a 32K prompt")
     ap.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0 = auto, >= 1 GB)")
-    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum", "cache", "mass"],
-                    help="matmul: Q_acc K^T on MFMA; qsum: summed queries, GEMV; cache: summed "
-                         "queries against the INT4 key cache (hq_detect_vlines_cache); mass: "
-                         "attention-mass scores (hq_detect_vlines_mass)")
+    ap.add_argument("--detect-method", default="matmul", choices=["matmul", "qsum", "mass"],
+                    help="the detector over the full 16-bit keys reported beside the re-detection "
+                         "(matmul: Q_acc K^T on MFMA; qsum: summed queries, GEMV; mass: attention-mass "
+                         "scores)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="budget of the CPU baseline; its 128K sample is skipped beyond it")
     ap.add_argument("--ablation", action="store_true",
                     help="decode settings of the ablation (hybrid, sparse, window only, strict K4V4, "
                          "all 16-bit): bytes, time and error against exact attention")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in one HIP graph and time its replay")
-    ap.add_argument("--separate-upkeep", action="store_true",
-                    help="queries to the ring and the eviction as separate calls (hq_decode_attn)")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the 16 x 128K entry of the default workload's line")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MB (counter calibration)")
     return ap.parse_args()
@@ -87,9 +91,9 @@ def source_hash(*names) -> str:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(decode attention shards by KV head or batch with no communication; "
-              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path here (decode attention "
+              "would shard by KV head or by sequence with no communication, one GPU's share being "
+              "this same kernel at its own shape). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -104,19 +108,21 @@ def main():
         return main_prefill(args)
     if args.ablation:
         return main_ablation(args)
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
-    w = synth.WORKLOADS[args.workload]
+    return main_decode(args, torch, hq, synth)
+
+
+def build_rolling_caches(torch, hq, synth, w, copies, dev):
+    """`copies` independent rolling caches of one layer at context T, in the
+    state a prefill leaves them: INT4 planes for [0, T - W), the VL set from
+    the pages' detector (Q_acc K^T column sums, top-k) over the prompt's last
+    R queries and the 16-bit keys, the VL rows, and a ring of W + R rows
+    holding positions [T - W - R, T). The 16-bit source rows are freed
+    afterwards: the caches hold nothing else. Returns (caches, K source kept
+    for the detector measurement or None, q_steps, idx)."""
     dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
     R = 64
     nq = T - W
-    method = hq.HQ_DETECT_MATMUL if args.detect_method == "matmul" else hq.HQ_DETECT_QSUM
-    from_cache = args.detect_method == "cache"
-    by_mass = args.detect_method == "mass"
-
-    # ------------------------------------------------------------ inputs
-    t_setup = time.time()
 
     def to_dev(x32):
         if w.dtype == "bf16":
@@ -126,85 +132,80 @@ def main():
     K0 = torch.empty((B, Hkv, T, D), dtype=dt, device=dev)
     V0 = torch.empty_like(K0)
     for b in range(B):
-        K0[b].copy_(to_dev(np.stack([synth.keys(w, b, h) for h in range(Hkv)])))
-        V0[b].copy_(to_dev(np.stack([synth.values(w, b, h) for h in range(Hkv)])))
+        K0[b].copy_(to_dev(np.stack(synth._parallel(lambda h: synth.keys(w, b, h), [(h,) for h in range(Hkv)]))))
+        V0[b].copy_(to_dev(np.stack(synth._parallel(lambda h: synth.values(w, b, h), [(h,) for h in range(Hkv)]))))
     q_steps = to_dev(np.stack([synth.all_queries(w.replace(seed=w.seed + 17 * s)) for s in range(4)]))
     q_hist = to_dev(synth.all_query_histories(w))
-
-    layer_bytes = (2 * K0.numel() * K0.element_size()) + 2 * B * Hkv * T * (D // 2 + D // 16)
-    copies = args.copies or max(1, int(np.ceil(1.2e9 / layer_bytes)))
-    caches, Ks, Vs, qaccs = [], [], [], []
-    idx_new = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
-    det_ws = torch.zeros(hq.hq_detect_mass_workspace_size(B, Hq, Hkv, R, T, nq) if by_mass
-                         else hq.hq_detect_workspace_size(B, Hkv, nq, k), dtype=torch.uint8, device=dev)
+    # the set at the end of prefill: the pages' detector over the full 16-bit keys
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
+    ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, nq, k), dtype=torch.uint8, device=dev)
+    hq.hq_detect_vlines(None, q_hist, B, Hq, Hkv, D, R, 0, True, K0, T, nq, k, hq.HQ_DETECT_MATMUL, idx, None, ws)
+    caches = []
+    t_cap = (nq + 1 + 31) // 32 * 32              # one spare row: the step packs position T - W
     for c in range(copies):
-        Kc = K0 if c == 0 else K0.clone()
-        Vc = V0 if c == 0 else V0.clone()
-        qa = q_hist.clone()
-        # one spare INT4 row: the window's oldest token is packed into row T - W
-        cache = hq.HybridCache(B, Hkv, D, T, W, k, dt, t_cap=(nq + 1 + 31) // 32 * 32)
-        cache.quantize(Kc, Vc)
-        if from_cache:
-            hq.hq_detect_vlines_cache(None, qa, Hq, R, 0, True, cache.descriptor(), nq, k, idx_new, None, det_ws)
-        elif by_mass:
-            hq.hq_detect_vlines_mass(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, idx_new, None, det_ws)
-        else:
-            hq.hq_detect_vlines(None, qa, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method, idx_new, None,
-                                det_ws)
-        cache.set_vl(Kc, Vc, idx_new)
-        cache.set_window(Kc, Vc)
-        caches.append(cache)
-        Ks.append(Kc)
-        Vs.append(Vc)
-        qaccs.append(qa)
+        rc = hq.RollingCache(B, Hkv, D, T, W, k, dt, Hq, R=R, t_cap=t_cap, device=dev)
+        rc.build(K0, V0, idx)
+        rc.q_acc.copy_(q_hist)
+        # the context is held at T: every update treats the R ring rows behind
+        # the window as the positions that left it since the previous one
+        rc.p0 = nq - R
+        caches.append(rc)
+    torch.cuda.synchronize()
+    del V0
+    return caches, K0, q_steps, idx
+
+
+def main_decode(args, torch, hq, synth):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS[args.workload]
+    B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
+    R = 64
+    nq = T - W
+    hp = 2 if w.dtype in ("bf16", "f16") else 4
+    units = B * Hkv
+
+    # ------------------------------------------------------------ bytes
+    # one decode call: INT4 codes and scales of the non-VL quantized
+    # positions, 16-bit VL and window rows, the VL bitmap, q in, O and lse out
+    dec_bytes = (units * ((nq - k) * (D + (D // 32) * 8) + (k + W) * 2 * D * hp + (nq + 31) // 32 * 4)
+                 + B * Hq * D * hp + B * Hq * D * 4 + B * Hq * 4)
+    # the step's upkeep: the window's oldest row read and packed, q into the ring
+    evict_bytes = 2 * units * (D * hp + D // 2 + (D // 32) * 4)
+    acc_bytes = 2 * B * Hq * D * hp
+    # a re-detection: summed ring queries, the INT4 key codes and scales of
+    # [0, T - W), the candidates' scores, and the VL rows rewritten (old
+    # rows and ring rows read, new rows written, K and V)
+    det_bytes = (B * Hq * R * D * hp + units * nq * (D // 2 + (D // 32) * 4) + units * nq * 8
+                 + units * (k + R) * 8 + units * (2 * k + R) * 2 * D * hp + units * (k + k) * 4)
+
+    t_setup = time.time()
+    copies = args.copies or max(1, int(np.ceil(1.05e9 / dec_bytes)))
+    caches, K0, q_steps, idx0 = build_rolling_caches(torch, hq, synth, w, copies, dev)
     descs = [c.descriptor() for c in caches]
-    dec_ws = [torch.zeros(hq.hq_decode_workspace_size(d, Hq, args.splits), dtype=torch.uint8, device=dev)
-              for d in descs]
+    ws_bytes = max(hq.hq_decode_workspace_size(d, Hq, args.splits) for d in descs)
+    dec_ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    resident = caches[0].resident_bytes()
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
-    n_heads = B * Hkv
-
-    def detect(s, c, force, q_new=None):
-        if from_cache:
-            return hq.hq_detect_vlines_cache(q_new, qaccs[c], Hq, R, s, force, descs[c], nq, k, idx_new, None,
-                                             det_ws)
-        if by_mass:
-            return hq.hq_detect_vlines_mass(q_new, qaccs[c], B, Hq, Hkv, D, R, s, force, Ks[c], T, nq, k,
-                                            idx_new, None, det_ws)
-        return hq.hq_detect_vlines(q_new, qaccs[c], B, Hq, Hkv, D, R, s, force, Ks[c], T, nq, k, method,
-                                   idx_new, None, det_ws)
-
-    def install(c, cache, Kc, Vc):
-        hq.hq_vl_bitmap(idx_new, n_heads, k, cache.t_cap, cache.vl_bits)
-        hq.hq_gather_rows(Kc, n_heads, T, D, idx_new, k, cache.vl_k)
-        hq.hq_gather_rows(Vc, n_heads, T, D, idx_new, k, cache.vl_v)
-
-    launch_stream = stream           # the stream the step's calls go to
+    launch_stream = stream
+    nqs = q_steps.shape[0]
 
     def step(s: int):
         c = s % copies
-        cache, Kc, Vc = caches[c], Ks[c], Vs[c]
-        qn = q_steps[s % q_steps.shape[0]]
-        if args.separate_upkeep:
-            if detect(s, c, False, qn):
-                install(c, cache, Kc, Vc)
-            # the token leaving the window (position T - W) goes to INT4 row T - W
-            hq.hq_quantize_kv_pair(Kc[:, :, nq:], Vc[:, :, nq:], n_heads, 1, D, T * D, D,
-                                   cache.k_codes, cache.k_sz, cache.v_codes, cache.v_sz,
-                                   cache.t_cap, nq)
-            hq.hq_decode_attn(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
-            return
-        hq.hq_decode_step(qn, Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c],
-                          q_acc=qaccs[c], R=R, step=s, evict=True, stream=launch_stream.cuda_stream)
-        # the queries went into the ring with the step; the detector has work
-        # only on the ring's last slot, so the loop calls it there alone
-        if s % R == R - 1 and detect(s, c, False):
-            install(c, cache, Kc, Vc)
+        hq.hq_decode_step(q_steps[s % nqs], Hq, descs[c], 0.0, args.splits, out, lse, dec_ws,
+                          q_acc=caches[c].q_acc, R=R, step=s, evict=True, stream=launch_stream.cuda_stream)
 
-    # ------------------------------------------------------------ timed steps
+    def redetect(c: int):
+        rc = caches[c]
+        rc.p0 = nq - R
+        rc.redetect()
+        descs[c] = rc.descriptor()
+
+    # ------------------------------------------------------------ timed decode steps
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -212,8 +213,6 @@ def main():
     e1 = torch.cuda.Event(enable_timing=True)
     base = args.warmup
     if args.graph:
-        # the same steps captured once; the replay is the timed region (the
-        # library only enqueues kernels, so every call is capturable)
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
@@ -235,81 +234,37 @@ def main():
     h1 = time.perf_counter()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    host_us_per_step = (h1 - h0) * 1e6 / args.steps     # enqueue cost of the timed loop
-    ms_per_step = ms_total / args.steps
-    n_detect = sum(1 for s in range(base, base + args.steps) if s % R == R - 1)
+    step_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    host_us_per_step = (h1 - h0) * 1e6 / args.steps
 
-    # ------------------------------------------------------------ decode kernels alone
-    # hq_decode_attn (split kernel + merge kernel) back to back, one event pair
-    # around all the calls: the mean call time without per-call event packets
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for i in range(args.kernel_launches):
-        hq.hq_decode_attn(q_steps[i % q_steps.shape[0]], Hq, descs[i % copies], 0.0, args.splits, out, lse,
-                          dec_ws[i % copies])
-    c1.record(stream)
+    # ------------------------------------------------------------ re-detection (every R steps)
+    n_det = max(8, min(2 * copies, 40))
+    for c in range(min(copies, 4)):
+        redetect(c)
     torch.cuda.synchronize()
-    dec_us = c0.elapsed_time(c1) * 1e3 / args.kernel_launches
-    # the spread: every call bracketed by its own events (which add their own time)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_launches)]
-    for i in range(args.kernel_launches):
-        c = i % copies
-        starts[i].record(stream)
-        hq.hq_decode_attn(q_steps[i % q_steps.shape[0]], Hq, descs[c], 0.0, args.splits, out, lse, dec_ws[c])
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    durs = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])   # us
-    dec_pct = np.percentile(durs, [10, 50, 90])
-
-    # ------------------------------------------------------------ detector alone (amortized share)
     d0 = torch.cuda.Event(enable_timing=True)
     d1 = torch.cuda.Event(enable_timing=True)
-    n_det = 20
     d0.record(stream)
     for i in range(n_det):
-        detect(0, i % copies, True)
+        redetect(i % copies)
     d1.record(stream)
     torch.cuda.synchronize()
     det_us = d0.elapsed_time(d1) * 1e3 / n_det
+    # the pages' matrix-multiplication detector on the full 16-bit keys (the
+    # prefill-end detection; the detector workload of the GLM-4-9B shape)
+    mm_us = detector_matmul_us(torch, hq, w, K0, caches[0].q_acc, args.detect_method, dev, stream)
+    del K0
 
-    # ------------------------------------------------------------ HBM read ceiling, same run
-    stream_gbs = stream_read_ceiling(torch, hq, dev, stream)
+    us_per_step = step_us + det_us / R
+    step_bytes = dec_bytes + evict_bytes + acc_bytes + det_bytes / R
+    value = step_bytes / (us_per_step * 1e-6) / 1e9
 
-    # ------------------------------------------------------------ warm launches (after the rest)
-    # one copy every launch, so that a cache smaller than the 256 MB Infinity
-    # Cache may be served from it (labelled, never the roofline figure)
-    for i in range(args.kernel_launches):
-        starts[i].record(stream)
-        hq.hq_decode_attn(q_steps[i % q_steps.shape[0]], Hq, descs[0], 0.0, args.splits, out, lse, dec_ws[0])
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    warm_us = float(np.median([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]))
-
-    if args.calib_copy_mb:
-        a = torch.empty(args.calib_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        b_ = torch.empty_like(a)
-        b_.copy_(a)
-        torch.cuda.synchronize()
-
-    # ------------------------------------------------------------ bytes
-    hp = K0.element_size()
-    units = B * Hkv
-    dec_bytes = (units * ((nq - k) * (D + (D // 32) * 8) + (k + W) * 2 * D * hp + (T - W + 31) // 32 * 4)
-                 + B * Hq * D * hp + B * Hq * D * 4 + B * Hq * 4)
-    det_bytes = units * nq * D * hp + B * Hq * R * D * hp + units * k * 4
-    gather_bytes = 2 * units * k * D * hp * 2 + units * (caches[0].t_cap // 32) * 4
-    evict_bytes = 2 * units * (D * hp + D // 2 + (D // 32) * 4)
-    acc_bytes = 2 * B * Hq * D * hp
-    step_bytes = dec_bytes + evict_bytes + acc_bytes + (det_bytes + gather_bytes) * n_detect / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # ------------------------------------------------------------ decode call alone
+    dec_us, dec_pct, warm_us = time_decode_calls(torch, hq, caches, descs, q_steps, Hq, out, lse, dec_ws,
+                                                 args.splits, args.kernel_launches, stream)
     achieved = dec_bytes / (dec_us * 1e-6) / 1e9
-    # the same read at this size: a plain sequential read of dec_bytes,
-    # rotated past the Infinity Cache and event-timed per launch like the call
+    stream_gbs = stream_read_ceiling(torch, hq, dev, stream)
     same_us = stream_read_same_bytes_us(torch, hq, dev, stream, dec_bytes, args.kernel_launches)
-
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -320,11 +275,18 @@ def main():
                 traffic = rec["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
+    auto_s = hq.hq_decode_auto_splits(descs[0], Hq) if args.splits == 0 else args.splits
+    del caches, descs, dec_ws
+    torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ CPU oracle baseline
+    # ------------------------------------------------------------ the 128K workload, same line
+    long_ctx = None
+    if args.workload == "llama32k" and not args.no_long_context:
+        long_ctx = long_context_entry(torch, hq, synth, dev, stream, args)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds, step_bytes)
+        cpu = cpu_baseline(w, args.cpu_seconds, step_bytes, us_per_step)
 
     line = {
         "metric": METRIC,
@@ -333,28 +295,34 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "us_per_step": round(ms_per_step * 1e3, 3),
+        "ms_per_step": round(us_per_step * 1e-3, 6),
+        "us_per_step": round(us_per_step, 3),
+        "us_per_step_parts": {"decode_step": round(step_us, 3), "redetection_share": round(det_us / R, 3)},
         "host_enqueue_us_per_step": round(host_us_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4+bf16 (fp32 accumulate)" if w.dtype == "bf16" else f"int4+{w.dtype}",
+        "dtype": ("int4 k/v (codes as fp16) + bf16 rows; q fp16 in the int4 pass, p*s fp16, fp32 accumulate"
+                  if w.dtype == "bf16" else f"int4 k/v + {w.dtype} rows, fp32 accumulate"),
         "data": "synthetic (seeded; shapes of the named model's attention layer, random-init values)",
         "config": {
             "workload": f"{args.workload}: one decode step of one attention layer, B {B}, "
                         f"{Hq} q / {Hkv} kv heads, head_dim {D}, context {T}, window {W}, "
-                        f"VL budget {k}, INT4 group 32 with fp16 scale/zero",
+                        f"VL budget {k}, INT4 group 32 with fp16 scale/zero; rolling cache (16-bit rows: "
+                        f"VL set + a ring of W + {R}), re-detection every {R} steps",
             "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
-            "layer_copies_rotated": copies, "detect_method": args.detect_method,
-            "decode_splits": hq.hq_decode_auto_splits(descs[0], Hq) if args.splits == 0 else args.splits,
-            "detect_every": R, "detections_in_timed_steps": n_detect,
-            "timed_as": "one HIP graph replay of the steps" if args.graph else "stream launches per step",
-            "step_calls": ("hq_detect_vlines(q) + hq_quantize_kv_pair + hq_decode_attn" if args.separate_upkeep
-                           else "hq_decode_step (+ hq_detect_vlines every 64th step)"),
+            "layer_copies_rotated": copies,
+            "decode_read_bytes_rotated": int(copies * dec_bytes),
+            "decode_splits": auto_s,
+            "timed_as": ("the decode steps as one HIP graph replay" if args.graph else
+                         "exactly `steps` decode steps (hq_decode_step: attention + the step's upkeep) on "
+                         "the stream, plus 1/64 of a re-detection timed separately "
+                         "(hq_detect_vlines_cache scores + hq_vl_update)"),
+            "layer_resident_bytes": int(resident),
+            "layer_resident_vs_k4v4": round(resident / (units * nq * 2 * (D // 2 + (D // 32) * 4)) - 1.0, 4),
         },
         "roofline": {
-            "kernel": "decode_kernel (hq_decode_attn)",
+            "kernel": "decode_kernel + merge_kernel (hq_decode_attn)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
@@ -365,8 +333,8 @@ def main():
             "traffic_over_algorithmic": (round(traffic / dec_bytes, 4) if traffic else None),
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "avg_launch_us": round(dec_us, 3),
-            "avg_launch_us_timed_as": "one event pair around back-to-back hq_decode_attn calls "
-                                      "(split kernel + merge kernel each)",
+            "avg_launch_us_timed_as": "one HIP event pair on the launch stream around back-to-back "
+                                      "hq_decode_attn calls (split kernel + merge kernel each), caches rotated",
             "bracketed_call_us_p10_p50_p90": [round(float(x), 3) for x in dec_pct],
             "warm_launch_us_median": round(warm_us, 3),
             "stream_read_gbs": round(stream_gbs, 1),
@@ -374,13 +342,155 @@ def main():
             "stream_read_same_bytes_us": round(same_us, 3),
             "frac_of_stream_read_same_bytes": round(same_us / dec_us, 4),
         },
-        "detector": {"us_per_detection": round(det_us, 2), "method": args.detect_method,
-                     "overhead_vs_64_decode_kernels": round(det_us / (64 * dec_us), 4)},
+        "detector": {
+            "us_per_redetection": round(det_us, 2),
+            "redetection": "scores from the INT4 keys (hq_detect_vlines_cache, k_top 0) + hq_vl_update",
+            "redetection_bytes": int(det_bytes),
+            "overhead_vs_64_decode_steps": round(det_us / (R * step_us), 4),
+            "matmul_us_per_detection": round(mm_us, 2),
+            "matmul_method": args.detect_method,
+            "matmul_overhead_vs_64_decode_steps": round(mm_us / (R * step_us), 4),
+        },
         "step_bytes": int(step_bytes),
         "setup_s": round(t_setup, 1),
-        "cpu_baseline": cpu,
     }
+    if long_ctx is not None:
+        line["long_context"] = long_ctx
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
+
+
+def time_decode_calls(torch, hq, caches, descs, q_steps, Hq, out, lse, ws, splits, launches, stream):
+    """hq_decode_attn alone: one event pair around back-to-back calls over
+    the rotated caches (mean), each call bracketed by its own events (p10,
+    p50, p90: the events add their own time), and the median of calls that
+    reuse one cache ("warm": what fits the Infinity Cache may come from it)."""
+    copies = len(caches)
+    nqs = q_steps.shape[0]
+    for i in range(min(launches, 2 * copies)):
+        hq.hq_decode_attn(q_steps[i % nqs], Hq, descs[i % copies], 0.0, splits, out, lse, ws)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(launches):
+        hq.hq_decode_attn(q_steps[i % nqs], Hq, descs[i % copies], 0.0, splits, out, lse, ws)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    mean_us = c0.elapsed_time(c1) * 1e3 / launches
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    for i in range(launches):
+        starts[i].record(stream)
+        hq.hq_decode_attn(q_steps[i % nqs], Hq, descs[i % copies], 0.0, splits, out, lse, ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    pct = np.percentile([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)], [10, 50, 90])
+    for i in range(launches):
+        starts[i].record(stream)
+        hq.hq_decode_attn(q_steps[i % nqs], Hq, descs[0], 0.0, splits, out, lse, ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    warm = float(np.median([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)]))
+    return mean_us, pct, warm
+
+
+def detector_matmul_us(torch, hq, w, K0, q_acc, method_name, dev, stream):
+    """The detector over the full 16-bit keys (what runs at the end of
+    prefill, and the GLM-4-9B-shaped detector workload): mean of repeated
+    detections, the keys rotated over copies past the Infinity Cache when
+    they are smaller than 1 GB."""
+    B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
+    R = 64
+    nq = T - W
+    kb = K0.numel() * K0.element_size()
+    n_k = max(1, min(16, int(np.ceil(1.05e9 / kb))))
+    Ks = [K0] + [K0.clone() for _ in range(n_k - 1)]
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
+    if method_name == "mass":
+        ws = torch.zeros(hq.hq_detect_mass_workspace_size(B, Hq, Hkv, R, T, nq), dtype=torch.uint8, device=dev)
+        fn = lambda Kc: hq.hq_detect_vlines_mass(None, q_acc, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, idx,
+                                                 None, ws)
+    else:
+        method = hq.HQ_DETECT_QSUM if method_name == "qsum" else hq.HQ_DETECT_MATMUL
+        ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, nq, k), dtype=torch.uint8, device=dev)
+        fn = lambda Kc: hq.hq_detect_vlines(None, q_acc, B, Hq, Hkv, D, R, 0, True, Kc, T, nq, k, method,
+                                            idx, None, ws)
+    for Kc in Ks:
+        fn(Kc)
+    torch.cuda.synchronize()
+    n = 20
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(Ks[i % n_k])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    del Ks
+    return us
+
+
+def long_context_entry(torch, hq, synth, dev, stream, args):
+    """The 16 x 128K workload (Qwen3-8B-style GQA) in the same run: one
+    rolling cache (3 GB of decode-read bytes, beyond the Infinity Cache by
+    itself), the decode call and step time, and one re-detection."""
+    w = synth.WORKLOADS["qwen128k"]
+    B, Hq, Hkv, D, T, W, k = w.B, w.Hq, w.Hkv, w.D, w.T, w.W, w.k
+    R = 64
+    nq = T - W
+    units = B * Hkv
+    t0 = time.time()
+    caches, K0, q_steps, _ = build_rolling_caches(torch, hq, synth, w, 1, dev)
+    del K0
+    torch.cuda.empty_cache()
+    rc = caches[0]
+    desc = rc.descriptor()
+    dec_bytes = (units * ((nq - k) * (D + (D // 32) * 8) + (k + W) * 2 * D * 2 + (nq + 31) // 32 * 4)
+                 + B * Hq * D * 2 + B * Hq * D * 4 + B * Hq * 4)
+    ws = torch.zeros(hq.hq_decode_workspace_size(desc, Hq, 0), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    setup_s = time.time() - t0
+    n = 20
+    for i in range(3):
+        hq.hq_decode_step(q_steps[i % 4], Hq, desc, 0.0, 0, out, lse, ws, q_acc=rc.q_acc, R=R, step=i, evict=True)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        hq.hq_decode_step(q_steps[i % 4], Hq, desc, 0.0, 0, out, lse, ws, q_acc=rc.q_acc, R=R, step=i, evict=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / n
+    e0.record(stream)
+    for i in range(n):
+        hq.hq_decode_attn(q_steps[i % 4], Hq, desc, 0.0, 0, out, lse, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_us = e0.elapsed_time(e1) * 1e3 / n
+    rc.p0 = nq - R
+    rc.redetect()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(3):
+        rc.p0 = nq - R
+        rc.redetect()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    det_us = e0.elapsed_time(e1) * 1e3 / 3
+    achieved = dec_bytes / (call_us * 1e-6) / 1e9
+    return {"workload": f"qwen128k: B {B}, {Hq} q / {Hkv} kv heads, head_dim {D}, context {T}, window {W}, "
+                        f"VL budget {k}",
+            "us_per_step": round(step_us + det_us / R, 2),
+            "decode_call_us": round(call_us, 2), "decode_step_us": round(step_us, 2),
+            "us_per_redetection": round(det_us, 1),
+            "achieved_gbs": round(achieved, 1), "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+            "decode_splits": hq.hq_decode_auto_splits(desc, Hq), "setup_s": round(setup_s, 1),
+            "timed_as": "one HIP event pair around 20 back-to-back calls; 3 GB per call, no rotation needed"}
 
 
 def main_ablation(args):
@@ -444,7 +554,13 @@ def main_ablation(args):
         dec_bytes = (units * (int4_pos * (D + (D // 32) * 8) + (kk + ww) * 2 * D * hp
                               + (0 if flags else (nq + 31) // 32 * 4))
                      + B * Hq * D * hp + B * Hq * D * 4 + B * Hq * 4)
-        held = units * ((0 if flags else nq * (D + (D // 32) * 8)) + (kk + ww) * 2 * D * hp)
+        # what the layer holds in a rolling cache: the INT4 planes, the VL
+        # rows with their index list and bitmap, and the window ring, which
+        # keeps 64 more rows (the positions that left the window since the
+        # last re-detection) whenever there is a VL set to maintain
+        ring = ww + (64 if kk > 0 and ww > 0 else 0)
+        held = units * ((0 if flags else nq * (D + (D // 32) * 8) + (nq + 31) // 32 * 4)
+                        + (kk + ring) * 2 * D * hp + kk * 4)
         per_copy = max(held, 1)
         copies = max(1, min(24, int(np.ceil(1.2e9 / per_copy))))
         caches = []
@@ -679,59 +795,116 @@ def cpu_baseline_prefill(w, seconds: float, flops: float):
                       f"scaled to all {w.T} rows x {w.Hq} heads"}
 
 
-def cpu_baseline(w, seconds: float, step_bytes: float):
-    """The CPU oracle (unchanged) on a bounded sample of the same step: the
-    decode of whole (b, KV head) units over their cache, plus the amortized
-    detector share, repeated until `seconds` of work; scaled to one step."""
-    import synth
-    from oracle import attention, detect, quant
+def _cpu_worker_init():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
-        threads = 1
+        pass
+
+
+def _cpu_decode_unit(task):
+    """One (b, KV head) unit of a decode step on one core: its inputs
+    regenerated from the seeded streams and quantized (not timed), then the
+    oracle decode of the unit's query heads (timed)."""
+    name, T_over, b, h = task
+    import synth
+    from oracle import attention, quant
+    w = synth.WORKLOADS[name]
+    if T_over:
+        w = w.replace(T=T_over, k=int(0.05 * T_over))
     nq = w.T - w.W
+    K = synth.keys(w, b, h)
+    V = synth.values(w, b, h)
+    kp, ks = quant.quantize_rows(K[:nq])
+    vp, vs = quant.quantize_rows(V[:nq])
+    vl = synth.random_vl_index(w, b, h)
+    q = np.stack([synth.query(w, b, i) for i in range(h * w.G, (h + 1) * w.G)])
+    t0 = time.perf_counter()
+    attention.decode_head(q, K, V, kp, ks, vp, vs, vl, w.W)
+    return time.perf_counter() - t0
+
+
+def _cpu_detect_unit(task):
+    """One (b, KV head) unit of the detector (the pages' matmul + column
+    sums + top-k over the 16-bit keys, exact grid inputs) on one core."""
+    name, b, h = task
+    import synth
+    from oracle import detect
+    w = synth.WORKLOADS[name]
+    K = synth.keys(w, b, h)
+    rows = np.stack([synth.query_history(w, b, i) for i in range(h * w.G, (h + 1) * w.G)]).reshape(-1, w.D)
+    t0 = time.perf_counter()
+    detect.detect_head(rows, K, w.T - w.W, w.k)
+    return time.perf_counter() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, seconds: float, step_bytes: float, gpu_us_per_step: float):
+    """The CPU oracle (unchanged) on bounded samples, in a process pool of
+    single-threaded workers (one (b, KV head) unit per task, BLAS limited to
+    one thread per worker; at most 15 workers):
+      * the benchmarked step: all its decode units at once, plus 1/64 of the
+        detector over one unit per worker; the wall time is the step time;
+      * the same units one after another on one core (the single-core time);
+      * the tiny fp32 step, the GLM-4-9B-shaped detection, and a 16 x 128K
+        step extrapolated from a sample of its units (stated)."""
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    # fresh interpreters (spawn): the workers hold no GPU state; 15 of them
+    # plus this process stay within the host share of one GPU
+    workers = max(1, min(15, os.cpu_count() or 1))
     units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
-    prep = []
-    for (b, h) in units[:4]:
-        K = synth.keys(w, b, h)
-        V = synth.values(w, b, h)
-        kp, ks = quant.quantize_rows(K[:nq])
-        vp, vs = quant.quantize_rows(V[:nq])
-        vl = synth.random_vl_index(w, b, h)
-        q = np.stack([synth.query(w, b, i) for i in range(h * w.G, (h + 1) * w.G)])
-        qh = np.stack([synth.query_history(w, b, i) for i in range(h * w.G, (h + 1) * w.G)]).reshape(-1, w.D)
-        prep.append((q, K, V, kp, ks, vp, vs, vl, qh))
-    t0 = time.time()
-    n_units = 0
-    n_det = 0
-    while time.time() - t0 < seconds:
-        q, K, V, kp, ks, vp, vs, vl, qh = prep[n_units % len(prep)]
-        attention.decode_head(q, K, V, kp, ks, vp, vs, vl, w.W)
-        n_units += 1
-        if n_units % 16 == 0:
-            detect.detect_head(qh, K, nq, w.k)
-            n_det += 1
-        if n_units >= 200:
-            break
-    el = time.time() - t0
-    # per unit: decode + detect share (the detector runs once per 64 steps)
-    t_det_share = 0.0
-    per_unit = el / max(n_units, 1)
-    if n_det:
-        # separate the two: time one detection alone
-        q, K, V, kp, ks, vp, vs, vl, qh = prep[0]
-        t1 = time.time()
-        detect.detect_head(qh, K, nq, w.k)
-        t_det = time.time() - t1
-        per_unit = (el - n_det * t_det) / n_units
-        t_det_share = t_det / 64
-    s_per_step = (per_unit + t_det_share) * len(units)
-    return {"value": round(step_bytes / s_per_step / 1e9, 3), "unit": "GB/s",
-            "us_per_step": round(s_per_step * 1e6, 1), "cores": threads, "kind": "oracle",
-            "sample": f"{n_units} (b, kv-head) decode units of the {w.name} step over prebuilt INT4 "
-                      f"caches (+{n_det} detections), {el:.1f} s, scaled to all {len(units)} units "
-                      f"and the detector's 1/64 share"}
+    t_all = time.time()
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(workers, mp_context=ctx, initializer=_cpu_worker_init) as ex:
+        # warm the workers' imports
+        list(ex.map(_cpu_decode_unit, [("tiny", 0, 0, 0)] * workers))
+        t0 = time.perf_counter()
+        dec = list(ex.map(_cpu_decode_unit, [(w.name, 0, b, h) for b, h in units]))
+        wall_dec = time.perf_counter() - t0
+        det_units = units[:max(1, min(len(units), workers))]
+        t0 = time.perf_counter()
+        det = list(ex.map(_cpu_detect_unit, [(w.name, b, h) for b, h in det_units]))
+        wall_det = time.perf_counter() - t0
+        tiny = list(ex.map(_cpu_decode_unit, [("tiny", 0, 0, 0)]))[0]
+        glm = list(ex.map(_cpu_detect_unit, [("glm32k", 0, h) for h in range(2)]))
+        extra = {"tiny_step_s": round(tiny, 4), "glm32k_detection_s": round(max(glm), 3)}
+        if time.time() - t_all < seconds and w.name != "qwen128k":
+            synth_units = [(b, h) for b in (0, 15) for h in (0, 7)][:max(1, min(4, workers))]
+            qs = list(ex.map(_cpu_decode_unit, [("qwen128k", 0, b, h) for b, h in synth_units]))
+            per_unit = float(np.mean(qs))
+            n_units = 16 * 8
+            extra["qwen128k_step_s_extrapolated"] = round(per_unit * n_units / workers, 3)
+            extra["qwen128k_sample"] = (f"{len(qs)} of {n_units} units timed ({per_unit:.3f} s each on one "
+                                        f"core), x {n_units} / {workers} workers")
+    # step time with the pool: the units' timed oracle work spread over the
+    # workers (never below the longest unit), plus 1/64 of one detection of
+    # every unit spread the same way
+    det_all = float(np.mean(det)) * len(units)
+    s_per_step = max(sum(dec) / workers, max(dec)) + max(det_all / workers, max(det)) / 64
+    single = sum(dec) + det_all / 64
+    return {"value": round(step_bytes / s_per_step / 1e9, 4), "unit": "GB/s",
+            "us_per_step": round(s_per_step * 1e6, 1),
+            "single_core_us_per_step": round(single * 1e6, 1),
+            "gpu_over_cpu": round(s_per_step * 1e6 / gpu_us_per_step, 1),
+            "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"the {w.name} step's {len(units)} (b, kv-head) decode units in a pool of {workers} "
+                      f"single-threaded processes (oracle time per unit {min(dec):.3f}-{max(dec):.3f} s; "
+                      f"pool wall {wall_dec:.2f} s incl. regenerating inputs), the detector over "
+                      f"{len(det_units)} units ({float(np.mean(det)):.3f} s each) x 1/64 per step; inputs "
+                      f"regenerated and quantized outside the timed part",
+            **extra}
 
 
 if __name__ == "__main__":

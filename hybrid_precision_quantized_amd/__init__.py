@@ -98,8 +98,7 @@ _SIGS = {
                                               ctypes.POINTER(HybridKV), ctypes.c_float, ctypes.c_int,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_vl_update": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                    ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                    ctypes.c_int64, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_stream_read_sink_bytes": (ctypes.c_size_t, []),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
@@ -277,12 +276,11 @@ def hq_decode_attn_noalloc(q, Hq, kv: HybridKV, sm_scale, n_splits, out, lse, st
 HQ_DECODE_SCRATCH_BYTES = 16 << 20
 
 
-def hq_vl_update(kv: HybridKV, vl_idx, p0, scores, score_stride, k_new, new_idx, new_vl_k, new_vl_v,
-                 vl_bits, stream=None):
-    """Apply a re-detection to a rolling cache: the k_new best of the current
-    VL set and the positions [p0, T - W) still in the ring (see include/hq.h)."""
+def hq_vl_update(kv: HybridKV, vl_idx, p0, scores, score_stride, stream=None):
+    """Apply a re-detection to a rolling cache in place: the k best of the
+    current VL set and the positions [p0, T - W) still in the ring (see
+    include/hq.h)."""
     _check(lib().hq_vl_update(ctypes.byref(kv), _ptr(vl_idx), int(p0), _ptr(scores), int(score_stride),
-                              int(k_new), _ptr(new_idx), _ptr(new_vl_k), _ptr(new_vl_v), _ptr(vl_bits),
                               _stream(stream)))
 
 

@@ -144,7 +144,6 @@ class RollingCache(HybridCache):
         self.p0 = T0 - W
         self.q_acc = torch.zeros((B, Hq, R, D), dtype=hp_dtype, device=dev)
         self.scores = torch.zeros((B, Hkv, self.t_cap), dtype=torch.int64, device=dev)
-        self._spare = (torch.zeros_like(self.vl_idx), torch.zeros_like(self.vl_k), torch.zeros_like(self.vl_v))
         self.det_ws = torch.zeros(hq_detect_workspace_size(B, Hkv, self.t_cap, 0), dtype=torch.uint8, device=dev)
 
     def decode_step(self, q, out, lse, ws, n_splits=0, stream=None):
@@ -176,21 +175,15 @@ class RollingCache(HybridCache):
         cand_end = self.T - self.W
         kv = self.descriptor()
         sc = self.scores.view(-1)[:self.B * self.Hkv * cand_end]
-        hq_detect_vlines_cache(None, self.q_acc, self.Hq, self.R, self.step_no - 1, True, kv, cand_end, 0,
+        hq_detect_vlines_cache(None, self.q_acc, self.Hq, self.R, max(self.step_no - 1, 0), True, kv, cand_end, 0,
                                None, sc, self.det_ws, stream=stream)
-        if self.k == 0:
-            return
-        n_idx, n_k, n_v = self._spare
-        hq_vl_update(kv, self.vl_idx, self.p0, sc, cand_end, self.k, n_idx, n_k, n_v, self.vl_bits,
-                     stream=stream)
-        self._spare = (self.vl_idx, self.vl_k, self.vl_v)
-        self.vl_idx, self.vl_k, self.vl_v = n_idx, n_k, n_v
+        hq_vl_update(kv, self.vl_idx, self.p0, sc, cand_end, stream=stream)
         self.p0 = cand_end
 
     def resident_bytes(self) -> int:
         """Device bytes this layer's cache holds: INT4 planes and scales at
-        capacity, VL bitmap, VL rows and index list (both buffers), the window
-        ring, the detector's query ring and score buffer."""
+        capacity, VL bitmap, VL rows and index list, the window ring, the
+        detector's query ring and score buffer."""
         ts = (self.k_codes, self.v_codes, self.k_sz, self.v_sz, self.vl_bits, self.vl_idx, self.vl_k,
-              self.vl_v, self.win_k, self.win_v, self.q_acc, self.scores, *self._spare)
+              self.vl_v, self.win_k, self.win_v, self.q_acc, self.scores)
         return int(sum(t.numel() * t.element_size() for t in ts))

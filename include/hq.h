@@ -115,8 +115,10 @@ typedef struct {
   const uint16_t *v_sz;       /* [B][Hkv][t_cap][D/group][2] fp16 {s, z} */
   const uint32_t *vl_bits;    /* [B][Hkv][t_cap/32]: bit t%32 of word t/32 set
                                  iff position t is a VL position */
-  const void *vl_k, *vl_v;    /* [B][Hkv][k][D] hp_dtype, VL rows in ascending
-                                 position order */
+  const void *vl_k, *vl_v;    /* [B][Hkv][k][D] hp_dtype, the VL rows (ascending
+                                 position order as gathered from a detector's list,
+                                 any order after hq_vl_update: the attention reads
+                                 them as a set) */
   const void *win_k, *win_v;  /* [B][Hkv][C][D] hp_dtype, ring buffer of C = win_cap
                                  rows (C = W when win_cap == 0): position T - W + i
                                  sits in row (win_offset + i) % C */
@@ -374,36 +376,35 @@ hq_status hq_decode_attn_noalloc(const void *q, hq_dtype q_dtype, int Hq, const 
 int hq_decode_auto_splits(const hq_hybrid_kv *kv, int Hq);
 
 /*
- * hq_vl_update -- apply a re-detection to a rolling hybrid cache [WPN, body
- * paragraph 4: the detector runs every 64 tokens; AFS, How It Works, items
- * 1-2: only the vertical-line tokens and a recent window are kept in 16 bits,
- * the rest in 4 bits]. A decode-time cache holds 16-bit rows only for its
- * VL set and its window ring, so a position can be promoted only while its
- * 16-bit row still exists (a reading of the pages, which say nothing on it).
- * For every (b, h) the candidates are the current VL positions
- * vl_idx[b][h][0..kv->k) (ascending, all below p0: not checked on the
- * device) and the positions [p0, T - W) that left the window since the last
- * update, whose rows are still in the ring (kv->win_cap > W). The new set is
- * the k_new candidates with the largest scores[b][h][position] (int64, rows
- * of score_stride >= T - W entries, e.g. the score_out of a detector call
- * over cand_end = T - W), equal scores to the lower position:
- *   new_idx [B][Hkv][k_new] ascending;
- *   new_vl_k, new_vl_v [B][Hkv][k_new][D] (kv->hp_dtype): the 16-bit rows of
- *     the new set, copied from kv->vl_k / kv->vl_v or from the ring;
- *   vl_bits [B][Hkv][t_cap/32] (may be kv->vl_bits), updated in place: the
- *     bits of dropped VL positions cleared (they fall back to their INT4
- *     rows, which exist for every position), those of promoted ones set.
- * The ring must hold every position of [T - C, T) (C = ring rows) when the
- * call runs. Afterwards the caller uses new_idx / new_vl_k / new_vl_v with
- * k = k_new, and passes p0 = T - W at the next update.
- * Requires max(0, T - C) <= p0 <= T - W, 0 <= k_new <= kv->k + (T - W - p0),
- * at most 8192 candidates per head (else HQ_ERR_UNSUPPORTED), D in {64, 128},
- * 16-byte aligned rows, new buffers not overlapping the old ones or the ring
- * (HQ_ERR_INVALID_ARG otherwise). No workspace; nothing enqueued on error.
+ * hq_vl_update -- apply a re-detection to a rolling hybrid cache, in place
+ * [WPN, body paragraph 4: the detector runs every 64 tokens; AFS, How It
+ * Works, items 1-2: only the vertical-line tokens and a recent window are kept
+ * in 16 bits, the rest in 4 bits]. A decode-time cache holds 16-bit rows only
+ * for its VL set and its window ring, so a position can be promoted only
+ * while its 16-bit row still exists (a reading of the pages, which say
+ * nothing on it). For every (b, h) the candidates are the current VL
+ * positions vl_idx[b][h][0..kv->k) (VL row i holds position vl_idx[b][h][i];
+ * distinct, all below p0: not checked on the device) and the positions
+ * [p0, T - W) that left the window since the last update, whose rows are
+ * still in the ring (kv->win_cap > W). The new set is the kv->k candidates
+ * with the largest scores[b][h][position] (int64, rows of score_stride >=
+ * T - W entries, e.g. the score_out of a detector call over cand_end = T - W),
+ * equal scores to the lower position. The VL rows keep their slots: the
+ * slot of each dropped position (taken in slot order) receives a promoted
+ * one (in position order), so vl_idx, the rows kv->vl_k / kv->vl_v and the
+ * bitmap kv->vl_bits are updated through the descriptor's pointers, which
+ * must address writable memory; only promoted rows are copied (from the
+ * ring). Dropped positions fall back to their INT4 rows, which exist for
+ * every position. The ring rows of [p0, T - W) must still hold those
+ * positions (each is overwritten C positions later, C = ring rows). The
+ * caller passes p0 = T - W at the next update.
+ * Requires max(0, T - C) <= p0 <= T - W, T - W - p0 <= 1024 and at most
+ * 8192 candidates per head (else HQ_ERR_UNSUPPORTED), D in {64, 128},
+ * 16-byte aligned rows (HQ_ERR_INVALID_ARG otherwise). k == 0 or p0 == T - W
+ * is a no-op. No workspace; nothing enqueued on error.
  */
-hq_status hq_vl_update(const hq_hybrid_kv *kv, const int32_t *vl_idx, int64_t p0, const int64_t *scores,
-                       int64_t score_stride, int k_new, int32_t *new_idx, void *new_vl_k, void *new_vl_v,
-                       uint32_t *vl_bits, void *stream);
+hq_status hq_vl_update(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, const int64_t *scores,
+                       int64_t score_stride, void *stream);
 
 /*
  * hq_prefill_attn -- causal hybrid-precision prefill attention [AFS, The

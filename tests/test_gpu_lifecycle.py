@@ -54,7 +54,7 @@ def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, d
         rc.advance(Kd[:, :, T0 + s], Vd[:, :, T0 + s])
         if rc.due():
             rc.redetect()
-            got_sets.append((s, rc.vl_idx[..., :k].cpu().numpy().copy()))
+            got_sets.append((s, np.sort(rc.vl_idx[..., :k].cpu().numpy(), axis=-1)))
     torch.cuda.synchronize()
     say(f"  worst step max|err|/rms = {worst:.3e}")
     assert [s for s, _ in got_sets] == [s for s, _ in sets]
@@ -70,9 +70,12 @@ def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, d
     for b in range(B):
         for h in range(Hkv):
             assert np.array_equal(tile16_codes(rc.v_codes[b, h])[:nq], vp[b, h])
+            # the rows keep their slots across updates: slot i holds position vl_idx[i]
+            slots = rc.vl_idx[b, h, :k].cpu().numpy()
+            assert np.array_equal(np.sort(slots), final[b, h])
             rows_k = rc.vl_k[b, h, :k].float().cpu().numpy()
             rows_v = rc.vl_v[b, h, :k].float().cpu().numpy()
-            assert np.array_equal(rows_k, K[b, h, final[b, h]]) and np.array_equal(rows_v, V[b, h, final[b, h]])
+            assert np.array_equal(rows_k, K[b, h, slots]) and np.array_equal(rows_v, V[b, h, slots])
             bits = rc.vl_bits[b, h].cpu().numpy().view(np.uint32)
             want = np.zeros_like(bits)
             for p in final[b, h]:
