@@ -288,21 +288,42 @@ __global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_a
   const int rg = threadIdx.x / lpr;
   const int64_t base = (static_cast<int64_t>(b) * Hq + h * G) * R * D;
   double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  for (int r = rg; r < M; r += ng) {
-    const int64_t off = base + static_cast<int64_t>(r) * D + sub * 8;
+  // four rows per group in flight at a time (loads first, then the sums)
+  constexpr int NB = 4;
+  for (int r = rg; r < M; r += NB * ng) {
     if constexpr (DT == HQ_F32) {
-      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q_acc) + off);
-      const float4 x0 = p[0], x1 = p[1];
-      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float4 x[NB][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(v[e]);
+      for (int j = 0; j < NB; ++j) {
+        const int rr = r + j * ng;
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q_acc) + base +
+                                                           static_cast<int64_t>(rr < M ? rr : r) * D + sub * 8);
+        x[j][0] = rr < M ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[j][1] = rr < M ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const float v[8] = {x[j][0].x, x[j][0].y, x[j][0].z, x[j][0].w, x[j][1].x, x[j][1].y, x[j][1].z, x[j][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(v[e]);
+      }
     } else {
-      const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q_acc) + off);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      uint4 u[NB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[2 * e] += static_cast<double>(load_half<DT>(w[e] & 0xFFFFu));
-        s[2 * e + 1] += static_cast<double>(load_half<DT>(w[e] >> 16));
+      for (int j = 0; j < NB; ++j) {
+        const int rr = r + j * ng;
+        u[j] = rr < M ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q_acc) + base +
+                                                         static_cast<int64_t>(rr) * D + sub * 8)
+                      : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[2 * e] += static_cast<double>(load_half<DT>(w[e] & 0xFFFFu));
+          s[2 * e + 1] += static_cast<double>(load_half<DT>(w[e] >> 16));
+        }
       }
     }
   }
@@ -1128,10 +1149,15 @@ DetWs det_ws(int B, int Hkv, int64_t cand_end) {
 }
 
 // Scores from the INT4 cache: c_j = qsum . k_hat_j with k_hat = s c + z
-// (fp16 s and z per 32-channel group, codes in the row layout). As in
-// gemv_kernel, D / 8 lanes per key row, 8 channels each (4 code bytes and the
-// group's {s, z} word): 80 bytes per key at D = 128 instead of 256. Every
-// product and sum is in fp64, where s c + z is exact.
+// (fp16 s and z per 32-channel group, codes in the row layout), evaluated
+// per group as s (sum_e q_e c_e) + z (sum_e q_e): lane (row, group g) holds
+// the group's 32 summed query channels in fp64, loads its 16 code bytes and
+// {s, z} word, and the D / 32 lanes of a row add their group terms. A block
+// takes 256 rows; every lane issues the loads of all its rows first (one
+// row per pass of 256 / (D / 32) rows), then computes, so the block waits
+// for one round of loads instead of one per row. Every product and sum is
+// in fp64: exact for queries on the 2^-4 grid within the fp64 range (the
+// products are multiples of 2^-28), whatever the order.
 template <int D>
 __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restrict__ codes,
                                                         const uint32_t *__restrict__ sz,
@@ -1139,37 +1165,51 @@ __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restric
                                                         int64_t cand_end, int chunks_per_unit,
                                                         int64_t *__restrict__ scores,
                                                         unsigned long long *__restrict__ mm) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
+  constexpr int NG = D / 32;                // lanes per row, one group each
+  constexpr int RPP = 256 / NG;             // rows per pass of the block
   constexpr int CHUNK = 256;
+  constexpr int NP = CHUNK / RPP;           // passes
   const int unit = blockIdx.x / chunks_per_unit;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x % chunks_per_unit) * CHUNK;
-  const int sub = threadIdx.x % LPR;
-  const int rowi = threadIdx.x / LPR;
-  const int g = sub / 4;                    // the lane's 32-channel group
-  double qv[8];
+  const int g = threadIdx.x % NG;
+  const int rowi = threadIdx.x / NG;
+  uint4 cw[NP];
+  uint32_t w[NP];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qv[e] = qs[static_cast<int64_t>(unit) * D + sub * 8 + e];
-  unsigned long long mn = ~0ull, mx = 0;
-  for (int64_t r = r0 + rowi; r < r0 + CHUNK; r += RPB) {
-    const bool ok = r < cand_end;
-    double acc = 0.0;
-    if (ok) {
+  for (int p = 0; p < NP; ++p) {
+    const int64_t r = r0 + rowi + p * RPP;
+    if (r < cand_end) {
       const int64_t row = static_cast<int64_t>(unit) * t_cap + r;
-      const uint32_t cw = reinterpret_cast<const uint32_t *>(codes + row * (D / 2))[sub];
-      const uint32_t w = sz[row * (D / 32) + g];
-      const double s = static_cast<double>(f16_to_f32(w & 0xFFFFu));
-      const double z = static_cast<double>(f16_to_f32(w >> 16));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double kh = s * static_cast<double>((cw >> (4 * e)) & 0xFu) + z;
-        acc = fma(qv[e], kh, acc);
-      }
+      cw[p] = *reinterpret_cast<const uint4 *>(codes + row * (D / 2) + g * 16);
+      w[p] = sz[row * NG + g];
+    } else {
+      cw[p] = make_uint4(0u, 0u, 0u, 0u);
+      w[p] = 0u;
     }
+  }
+  double qv[32];
+  double qsum = 0.0;
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (ok && sub == 0) {
-      const long long v = __double2ll_rn(acc * 65536.0);
+  for (int e = 0; e < 32; ++e) {
+    qv[e] = qs[static_cast<int64_t>(unit) * D + g * 32 + e];
+    qsum += qv[e];
+  }
+  unsigned long long mn = ~0ull, mx = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t r = r0 + rowi + p * RPP;
+    const uint32_t word[4] = {cw[p].x, cw[p].y, cw[p].z, cw[p].w};
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      acc = fma(qv[e], static_cast<double>((word[e >> 3] >> (4 * (e & 7))) & 0xFu), acc);
+    const double s = static_cast<double>(f16_to_f32(w[p] & 0xFFFFu));
+    const double z = static_cast<double>(f16_to_f32(w[p] >> 16));
+    double part = fma(s, acc, z * qsum);
+#pragma unroll
+    for (int m = 1; m < NG; m <<= 1) part += __shfl_xor(part, m, 64);
+    if (r < cand_end && g == 0) {
+      const long long v = __double2ll_rn(part * 65536.0);
       scores[static_cast<int64_t>(unit) * cand_end + r] = v;
       const unsigned long long u = ordered_score(v);
       mn = u < mn ? u : mn;

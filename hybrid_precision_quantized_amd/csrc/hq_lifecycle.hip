@@ -16,10 +16,13 @@
 //
 // Kernel: one workgroup of 1024 threads per (sequence, KV head), in place.
 //  * The n <= 8192 candidates (the current VL rows in slot order, then the
-//    recent range) are loaded with their scores as order-preserving 64-bit
-//    keys and sorted in LDS by a bitonic network, best first (larger key,
-//    then lower position); padding entries sort last. The first k sorted
-//    entries are kept.
+//    recent range) are loaded into LDS with their scores as order-preserving
+//    64-bit keys. The k best (larger score, then lower position) are found
+//    by a radix select over the 96-bit rank key (score key, then inverted
+//    position), most significant byte first: per pass a 256-bin histogram of
+//    the candidates still tied with the threshold, one wave's scan for the
+//    digit where the count from the top reaches what is still needed, and
+//    the candidates above it taken. No sort: a dozen passes at most.
 //  * The VL rows keep their slots: the slot of every dropped VL position is
 //    refilled with a promoted one (the j-th freed slot in slot order takes
 //    the j-th promoted position in position order, both found with one
@@ -51,66 +54,99 @@ __device__ __forceinline__ unsigned long long order_key(long long v) {
   return static_cast<unsigned long long>(v) ^ 0x8000000000000000ull;
 }
 
+// Digit d (0 = most significant) of a candidate's 96-bit rank key: the
+// 64-bit order-preserving score key, then 2^32 - 1 - position (a lower
+// position ranks higher). Keys are distinct because positions are.
+__device__ __forceinline__ uint32_t rank_digit(unsigned long long key, int32_t pos, int d) {
+  if (d < 8) return static_cast<uint32_t>(key >> (8 * (7 - d))) & 0xFFu;
+  const uint32_t inv = 0xFFFFFFFFu - static_cast<uint32_t>(pos);
+  return (inv >> (8 * (11 - d))) & 0xFFu;
+}
+
 __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
   __shared__ unsigned long long key[kMaxCand];
   __shared__ int32_t pos[kMaxCand];         // candidate index -> position
-  __shared__ uint16_t id[kMaxCand];         // sorted slot -> candidate index
   __shared__ uint8_t taken[kMaxCand];
+  __shared__ uint8_t alive[kMaxCand];       // still tied with the threshold's digits so far
   __shared__ uint16_t freed[kMaxMoved];     // j-th freed VL slot
   __shared__ int32_t prom[kMaxMoved];       // j-th promoted position
   __shared__ int scan[kUpdThreads];
+  __shared__ int hist[256];
+  __shared__ int sel_digit, sel_need, sel_count;
   __shared__ int n_freed_sh;
   const int64_t unit = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int k = P.k;
   const int n = k + static_cast<int>(P.nq - P.p0);
-  int npow = 2;
-  while (npow < n) npow <<= 1;
   int32_t *ui = P.idx + unit * k;
 
   // ---- candidates and their keys
-  for (int i = tid; i < npow; i += kUpdThreads) {
-    if (i < n) {
-      const int64_t p = i < k ? static_cast<int64_t>(ui[i]) : P.p0 + (i - k);
-      pos[i] = static_cast<int32_t>(p);
-      key[i] = order_key(P.scores[unit * P.stride + p]);
-      id[i] = static_cast<uint16_t>(i);
-    } else {
-      key[i] = 0ull;
-      id[i] = 0xFFFFu;
-    }
+  for (int i = tid; i < n; i += kUpdThreads) {
+    const int64_t p = i < k ? static_cast<int64_t>(ui[i]) : P.p0 + (i - k);
+    pos[i] = static_cast<int32_t>(p);
+    key[i] = order_key(P.scores[unit * P.stride + p]);
     taken[i] = 0;
+    alive[i] = 1;
   }
+  int need = k;                             // still to take among the alive candidates
   __syncthreads();
 
-  // ---- bitonic sort, best first: larger key, then lower position
-  auto better = [&](int a, int b) {
-    const unsigned long long ka = key[a], kb = key[b];
-    if (ka != kb) return ka > kb;
-    const int ia = id[a], ib = id[b];
-    if (ia == 0xFFFF || ib == 0xFFFF) return ia < ib;        // padding last
-    return pos[ia] < pos[ib];
-  };
-  for (int size = 2; size <= npow; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (npow >> 1); i += kUpdThreads) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        if (up ? better(hi, lo) : better(lo, hi)) {
-          const unsigned long long tk = key[lo];
-          key[lo] = key[hi];
-          key[hi] = tk;
-          const uint16_t ti = id[lo];
-          id[lo] = id[hi];
-          id[hi] = ti;
+  // ---- radix select of the k best, most significant byte first: each pass
+  // counts the alive candidates per digit, finds the digit b* at which the
+  // count from the top reaches `need`, takes the alive candidates above it
+  // and keeps those equal to it alive. Ends when the digit's whole bucket is
+  // needed (or after the last digit, where one candidate is left).
+  for (int d = 0; d < 12 && need > 0; ++d) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kUpdThreads)
+      if (alive[i]) atomicAdd(&hist[rank_digit(key[i], pos[i], d)], 1);
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds the bins 255 - 4l .. 252 - 4l (descending)
+      int c[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[255 - (4 * lane + j)];
+        tot += c[j];
+      }
+      int incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      int cum = incl - tot;                 // alive candidates in the bins above this lane's
+      if (cum < need && need <= incl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= need) {
+            sel_digit = 255 - (4 * lane + j);
+            sel_need = need - cum;
+            sel_count = c[j];
+            break;
+          }
+          cum += c[j];
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
+    const uint32_t bstar = static_cast<uint32_t>(sel_digit);
+    const bool whole = sel_need == sel_count;   // the bucket is needed entirely
+    for (int i = tid; i < n; i += kUpdThreads) {
+      if (!alive[i]) continue;
+      const uint32_t dg = rank_digit(key[i], pos[i], d);
+      if (dg > bstar || (dg == bstar && whole)) {
+        taken[i] = 1;
+        alive[i] = 0;
+      } else if (dg < bstar) {
+        alive[i] = 0;
+      }
+    }
+    need = whole ? 0 : sel_need;
+    __syncthreads();
   }
-  for (int r = tid; r < k; r += kUpdThreads) taken[id[r]] = 1;
-  __syncthreads();
 
   // ---- flags: a freed slot (VL candidate not kept) or a promoted position
   // (recent candidate kept); one block scan ranks both in candidate order.

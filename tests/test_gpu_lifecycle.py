@@ -82,3 +82,59 @@ def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, d
                 want[p >> 5] |= np.uint32(1) << np.uint32(p & 31)
             assert np.array_equal(bits, want)
     say(f"  resident bytes of the rolling cache: {rc.resident_bytes()}")
+
+
+@pytest.mark.parametrize("k,n_st,spread,seed", [
+    (35, 64, 3, 1),          # many equal scores: the position decides
+    (5, 64, 1000, 2),        # more recent candidates than VL slots
+    (1638, 64, 1 << 40, 3),  # the Llama-shaped budget, scores over a wide range (negative too)
+    (8000, 64, 7, 4),        # close to the candidate limit, heavy ties
+    (300, 1, 2, 5),          # one position left the window
+])
+def test_vl_update_ties_and_sizes(k, n_st, spread, seed):
+    """hq_vl_update alone on constructed scores, against the oracle's update
+    rule: the new set (compared as a set), the rows of every slot (kept
+    slots untouched, freed ones holding the promoted ring rows) and the
+    bitmap, bit for bit."""
+    B, Hkv, D, W, R = 1, 2, 128, 32, 64
+    C = W + R
+    T = k + 3 * R + W + 200
+    nq = T - W
+    p0 = nq - n_st
+    say(f"vl_update k={k} n_st={n_st} spread={spread}")
+    rng = np.random.default_rng(seed)
+    cache = hq.HybridCache(B, Hkv, D, T, W, k, torch.bfloat16, win_cap=C)
+    # VL slots in no particular order, all below p0; rows and ring rows random
+    old = np.stack([rng.permutation(rng.choice(p0, k, replace=False)) for _ in range(Hkv)])[None].astype(np.int32)
+    cache.vl_idx.copy_(torch.from_numpy(old))
+    cache.vl_k.copy_(torch.randn(cache.vl_k.shape, device="cuda").to(torch.bfloat16))
+    cache.vl_v.copy_(torch.randn(cache.vl_v.shape, device="cuda").to(torch.bfloat16))
+    cache.win_k.copy_(torch.randn(cache.win_k.shape, device="cuda").to(torch.bfloat16))
+    cache.win_v.copy_(torch.randn(cache.win_v.shape, device="cuda").to(torch.bfloat16))
+    cache.win_offset = int(rng.integers(C))
+    hq.hq_vl_bitmap(cache.vl_idx, Hkv, k, cache.t_cap, cache.vl_bits)
+    scores = rng.integers(-spread, spread + 1, (B, Hkv, nq), dtype=np.int64)
+    sc = torch.from_numpy(scores).cuda()
+    vl_k0, vl_v0 = cache.vl_k.float().cpu().numpy(), cache.vl_v.float().cpu().numpy()
+    ring_k, ring_v = cache.win_k.float().cpu().numpy(), cache.win_v.float().cpu().numpy()
+    hq.hq_vl_update(cache.descriptor(), cache.vl_idx, p0, sc, nq)
+    torch.cuda.synchronize()
+    got = cache.vl_idx.cpu().numpy()
+    gk, gv = cache.vl_k.float().cpu().numpy(), cache.vl_v.float().cpu().numpy()
+    bits = cache.vl_bits.cpu().numpy().view(np.uint32)
+    for h in range(Hkv):
+        want = lifecycle.select(scores[0, h], np.sort(old[0, h]), p0, nq, k)
+        assert np.array_equal(np.sort(got[0, h]), want), h
+        for slot in range(k):
+            p = got[0, h, slot]
+            if p == old[0, h, slot]:
+                src_k, src_v = vl_k0[0, h, slot], vl_v0[0, h, slot]          # kept: untouched
+            else:
+                assert p0 <= p < nq                                          # promoted from the ring
+                row = (cache.win_offset + (p - nq)) % C
+                src_k, src_v = ring_k[0, h, row], ring_v[0, h, row]
+            assert np.array_equal(gk[0, h, slot], src_k) and np.array_equal(gv[0, h, slot], src_v)
+        wb = np.zeros_like(bits[0, h])
+        for p in want:
+            wb[p >> 5] |= np.uint32(1) << np.uint32(p & 31)
+        assert np.array_equal(bits[0, h], wb)
