@@ -660,7 +660,7 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
     L.vc = bload16nt(view(vb, nv, c * (CP * 16)), lo_v);
   };
 
-  constexpr int NPF = 6;
+  constexpr int NPF = 3;
   const uint32_t nsteps = (n + SLOTS - 1) / SLOTS;
   Int4Loads<D> ring[NPF];
 #pragma unroll
@@ -1008,35 +1008,66 @@ __device__ void fp_split(const DecodeParams &P, SharedMem &sm, int b, int h, int
 
 // ---------------------------------------------------------------- 16-bit pass, D = 128, 4 heads
 // Specialisation of the 16-bit pass for head_dim 128, a chunk of 4 query
-// heads and 16-bit rows. A split holds either VL rows (a contiguous block of
-// vl_k / vl_v) or window rows (the ring), never both, so the chunk type is
-// wave-uniform. Lane (slot, g) dots its row's 32 channels of group g with the
-// query of head g ^ j in register j; the quad reduce-scatter of the INT4 pass
-// then leaves head g's logit in lane g, so one exponential per lane suffices.
-// P . V: lane cp accumulates channels (2cp, 2cp+1) of all 4 heads over the 16
-// rows, weights read back from LDS in fp32 (these rows carry the largest
-// attention weights, so the weights are not rounded).
+// heads and 16-bit rows, on the matrix cores with the lane layout of the
+// INT4 pass (v_mfma_f32_4x4x4_16b_bf16 or _f16, sixteen 4x4x4 blocks). A
+// split holds either VL rows (a contiguous block of vl_k / vl_v) or window
+// rows (the ring), never both, so the chunk type is wave-uniform.
+//  * Q . K: lane (token t = lane % 16, group g = lane / 16) loads the 32
+//    channels of group g of its row (64 bytes) and is column t of block
+//    4 g + t / 4; its A row is head lane % 4's query channels of group g in
+//    the rows' own 16-bit type. MFMA j covers channels 4 j .. 4 j + 3 of the
+//    group, eight of them the whole group; the permlane sums of the INT4
+//    pass then give lane (t, h = lane / 16) the logit of head h for token t.
+//  * Softmax as in the INT4 pass (one exponential per lane).
+//  * P . V: the four heads' p (fp16, relative rounding 2^-12, as the INT4
+//    pass's p s) go through LDS in the INT4 pass's layout; lane cp loads
+//    channel pair cp of the chunk's 16 rows (one dword per row) and turns
+//    them into fp16 token pairs (bf16 values convert exactly for magnitudes
+//    in [2^-14, 65504]; smaller ones round to the fp16 subnormal grid,
+//    absolute error below 2^-25), the B operand of the INT4 pass's P . V
+//    MFMAs. No zero point: the rows are the values themselves.
 struct FpRing {
   u32x4 k[4];                 // 32 key channels of this lane's (row, group)
   uint32_t v[16];             // value channel pair cp of the chunk's 16 rows
 };
 
-template <int HT, bool WIN>
+template <int QT>
+__device__ __forceinline__ f4x mfma4x4_16b(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4x c) {
+  if constexpr (QT == HQ_BF16) {
+    typedef short s4x __attribute__((ext_vector_type(4)));
+    const u2x a = {a0, a1}, bb = {b0, b1};
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s4x, a), __builtin_bit_cast(s4x, bb), c, 0, 0,
+                                                   0);
+  } else {
+    return mfma4x4(a0, a1, b0, b1, c);
+  }
+}
+// two 16-bit values (low halves of x and y, or high halves) as an fp16 pair
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t pair_f16(uint32_t x, uint32_t y) {
+  if constexpr (QT == HQ_F16) {
+    return HI ? __builtin_amdgcn_perm(y, x, 0x07060302u) : __builtin_amdgcn_perm(y, x, 0x05040100u);
+  } else {
+    const float fx = __uint_as_float(HI ? (x & 0xFFFF0000u) : (x << 16));
+    const float fy = __uint_as_float(HI ? (y & 0xFFFF0000u) : (y << 16));
+    return pack_f16_rne(fx, fy);
+  }
+}
+
+template <int QT, bool WIN>
 __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int h, int i0,
                                 int64_t r0, int64_t r1, WaveState<4> &st) {
-  constexpr int D = 128, LPT = 4, SLOTS = 16, RB = D * 2;   // RB: bytes per row
+  constexpr int D = 128, SLOTS = 16, RB = D * 2;   // RB: bytes per row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot = lane >> 2;
-  const int g = lane & 3;
-  const int cp = lane;
+  const int t = lane & 15;             // row of the chunk
+  const int row = lane >> 4;           // key group (loads, Q . K), head (softmax)
+  const int hq = lane & 3;             // head of this lane's A row
   const int64_t head = static_cast<int64_t>(b) * P.Hkv + h;
 
-  // natural query pairs (q[2i], q[2i+1]) of group g, head g ^ j in register j
-  uint32_t qn[4][16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    load_q32<HT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + (g ^ j)) * D + g * 32, qn[j]);
+  // query channels of head hq, group `row`, natural pairs (2c, 2c + 1)
+  uint32_t qw[16];
+  load_q32<QT>(P.q, (static_cast<int64_t>(b) * P.Hq + i0 + hq) * D + row * 32, qw);
   __builtin_amdgcn_sched_barrier(0);
 
   const uint32_t n = static_cast<uint32_t>(r1 - r0);
@@ -1060,26 +1091,25 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
     w -= (w >= P.win_cap) ? P.win_cap : 0;
     return w;
   };
-
   auto issue = [&](uint32_t c, FpRing &L) {
     const uint32_t f = c * SLOTS;                              // first row of the chunk in the split
     if constexpr (!WIN) {
       const __amdgpu_buffer_rsrc_t rk = view(kbase, kbytes, f * RB);
       const __amdgpu_buffer_rsrc_t rv = view(vbase, kbytes, f * RB);
-      const uint32_t ko = slot * RB + g * 64;
+      const uint32_t ko = t * RB + row * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i) L.k[i] = bload16(rk, ko + 16 * i);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) L.v[r] = bload4(rv, cp * 4 + r * RB);
+      for (int r = 0; r < 16; ++r) L.v[r] = bload4(rv, lane * 4 + r * RB);
     } else {
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, kbytes);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, kbytes);
-      const uint32_t ko = static_cast<uint32_t>(ring_row(wrow0 + static_cast<int>(f) + slot)) * RB + g * 64;
+      const uint32_t ko = static_cast<uint32_t>(ring_row(wrow0 + static_cast<int>(f) + t)) * RB + row * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i) L.k[i] = bload16(rk, ko + 16 * i);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        L.v[r] = bload4(rv, cp * 4 + static_cast<uint32_t>(ring_row(wrow0 + static_cast<int>(f) + r)) * RB);
+        L.v[r] = bload4(rv, lane * 4 + static_cast<uint32_t>(ring_row(wrow0 + static_cast<int>(f) + r)) * RB);
     }
   };
 
@@ -1091,57 +1121,71 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
     issue(wave + jr * kWaves, ring[jr]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  float mown = -__FLT_MAX__;            // running max of head g (finite: see the INT4 pass)
+  float mown = -__FLT_MAX__;            // running max of head `row` (finite: see the INT4 pass)
   float lown = 0.f;
-  float *pw = &sm.p[wave][0];           // [head][32] fp32 weights of the chunk
+  f4x ae = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+  uint16_t *psw = reinterpret_cast<uint16_t *>(&sm.ps[wave][0]);   // [head][group][16 rows]
+  const uint4 *pws = reinterpret_cast<const uint4 *>(psw + (hq * 4 + row) * 16);
 
   auto step = [&](const uint32_t c, const FpRing &cur) {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- q . k of the 4 heads over this lane's (row, group)
     const uint32_t kw[16] = {cur.k[0].x, cur.k[0].y, cur.k[0].z, cur.k[0].w,
                              cur.k[1].x, cur.k[1].y, cur.k[1].z, cur.k[1].w,
                              cur.k[2].x, cur.k[2].y, cur.k[2].z, cur.k[2].w,
                              cur.k[3].x, cur.k[3].y, cur.k[3].z, cur.k[3].w};
+    f4x d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
+    for (int j = 0; j < 8; ++j) d = mfma4x4_16b<QT>(qw[2 * j], qw[2 * j + 1], kw[2 * j], kw[2 * j + 1], d);
+    float part[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[j] = dot2_q<HT>(qn[j][e], kw[e], part[j]);
-    const float y0 = part[0] + dpp_f<kQuadXor2>(part[2]);
-    const float y1 = part[1] + dpp_f<kQuadXor2>(part[3]);
-    const float lgv = (y0 + dpp_f<kQuadXor1>(y1)) * P.cs;
-    const bool live = slot < n - c * SLOTS;
+    for (int i = 0; i < 4; ++i) part[i] = d[i] * P.cs;
+    const float lgv = swap16_sum(swap32_sum(part[0], part[2]), swap32_sum(part[1], part[3]));
+    const bool live = t < n - c * SLOTS;
     const float lg = live ? lgv : kNegInf;
     if (__builtin_expect(__ballot(lg > mown) != 0, 0)) {
-      const float mx = slots_max<LPT>(lg);
-      const float mn = fmaxf(mown, mx);
-      const float alpha = fast_exp2(mown - mn);
+      const float mn = fmaxf(mown, row16_max(lg));
+      const float alpha = fast_exp2(mown - mn);          // of head `row`
       mown = mn;
       lown *= alpha;
-      const float a0 = __shfl(alpha, 0, 64), a1 = __shfl(alpha, 1, 64);
-      const float a2 = __shfl(alpha, 2, 64), a3 = __shfl(alpha, 3, 64);
-      st.acc_e[0] *= a0; st.acc_o[0] *= a0;
-      st.acc_e[1] *= a1; st.acc_o[1] *= a1;
-      st.acc_e[2] *= a2; st.acc_o[2] *= a2;
-      st.acc_e[3] *= a3; st.acc_o[3] *= a3;
+      const float a0 = readlane_f(alpha, 0), a1 = readlane_f(alpha, 16);
+      const float a2 = readlane_f(alpha, 32), a3 = readlane_f(alpha, 48);
+      ae[0] *= a0; ao[0] *= a0;
+      ae[1] *= a1; ao[1] *= a1;
+      ae[2] *= a2; ao[2] *= a2;
+      ae[3] *= a3; ao[3] *= a3;
     }
     const float p = fast_exp2(lg - mown);
     lown += p;
-    pw[g * 32 + slot] = p;
+    float ph[4];
+    float x = p, y = p;
+    permlane32_swap(x, y);
+    ph[0] = x; ph[1] = x;
+    permlane16_swap(ph[0], ph[1]);
+    ph[2] = y; ph[3] = y;
+    permlane16_swap(ph[2], ph[3]);
+    const uint32_t w01 = pack_f16_rne(ph[0], ph[1]), w23 = pack_f16_rne(ph[2], ph[3]);
+    psw[(0 * 4 + row) * 16 + t] = static_cast<uint16_t>(w01);
+    psw[(1 * 4 + row) * 16 + t] = static_cast<uint16_t>(w01 >> 16);
+    psw[(2 * 4 + row) * 16 + t] = static_cast<uint16_t>(w23);
+    psw[(3 * 4 + row) * 16 + t] = static_cast<uint16_t>(w23 >> 16);
     wave_sync();
+
+    // ---- p . v: fp16 token pairs of this lane's channel pair
+    uint32_t e[8], o[8];
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const float4 *pp = reinterpret_cast<const float4 *>(pw + hh * 32);
-      float pr[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 f4 = pp[i];
-        pr[4 * i] = f4.x; pr[4 * i + 1] = f4.y; pr[4 * i + 2] = f4.z; pr[4 * i + 3] = f4.w;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        st.acc_e[hh] = fmaf(pr[r], half_bits_to_f32<HT>(cur.v[r] & 0xFFFFu), st.acc_e[hh]);
-        st.acc_o[hh] = fmaf(pr[r], half_bits_to_f32<HT>(cur.v[r] >> 16), st.acc_o[hh]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      e[i] = pair_f16<QT, false>(cur.v[2 * i], cur.v[2 * i + 1]);
+      o[i] = pair_f16<QT, true>(cur.v[2 * i], cur.v[2 * i + 1]);
     }
+    const uint4 pa = pws[0], pb = pws[1];     // head hq, tokens 0..7 / 8..15
+    ae = mfma4x4(pa.x, pa.y, e[0], e[1], ae);
+    ao = mfma4x4(pa.x, pa.y, o[0], o[1], ao);
+    ae = mfma4x4(pa.z, pa.w, e[2], e[3], ae);
+    ao = mfma4x4(pa.z, pa.w, o[2], o[3], ao);
+    ae = mfma4x4(pb.x, pb.y, e[4], e[5], ae);
+    ao = mfma4x4(pb.x, pb.y, o[4], o[5], ao);
+    ae = mfma4x4(pb.z, pb.w, e[6], e[7], ae);
+    ao = mfma4x4(pb.z, pb.w, o[6], o[7], ao);
     wave_sync();
   };
   uint32_t cb = wave;
@@ -1160,11 +1204,13 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
       step(cb + jr * kWaves, ring[jr]);
     }
 
-  const float lsum = xor_sum<LPT>(lown);
+  const float lsum = row16_sum(lown);                   // head `row`, over the rows
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
-    st.m[hh] = __shfl(mown, hh, 64);
-    st.l[hh] = __shfl(lsum, hh, 64);
+    st.acc_e[hh] = ae[hh];
+    st.acc_o[hh] = ao[hh];
+    st.m[hh] = readlane_f(mown, 16 * hh);
+    st.l[hh] = readlane_f(lsum, 16 * hh);
   }
 }
 
