@@ -9,7 +9,10 @@
 // abstract" (decode fuses KV dequantization with attention). All three sets
 // feed one softmax.
 //
-// Kernel design (gfx950, wave64, VALU only):
+// Kernel design (gfx950, wave64). The points below describe the generic
+// passes (any D, G, fp32 inputs), on the vector unit; for head_dim 128, a
+// chunk of 4 query heads and 16-bit queries both passes run their products
+// on the 4x4x4 matrix cores instead (int4_split_d128_g4, fp_rows_d128_g4).
 //  * One workgroup = 4 waves = one (sequence b, KV head h, head chunk of HB
 //    query heads, split) unit of work. A split is a contiguous range of INT4
 //    positions or of 16-bit rows (VL rows, then window rows).
@@ -41,9 +44,15 @@
 //    last-block merge inside the split kernel needs a device-scope release
 //    per block, which on gfx950 writes back the XCD's L2 each time and costs
 //    far more than one extra launch.)
-//  * Blocks are numbered so that all splits of a unit run on the same XCD
-//    (dispatch is round-robin over the 8 XCDs), keeping the partials of a
-//    unit in one L2 for the merge.
+//  * Blocks are numbered so that all splits of a KV head run on the same XCD
+//    (dispatch is round-robin over the 8 XCDs), keeping the partials in one
+//    L2 for the merge; when the head group has more than one chunk of query
+//    heads (G = 8, 16), the chunks of each split are adjacent, so they run
+//    together and each KV tile comes from HBM once, the other chunks' reads
+//    hitting the L2. (Holding all 16 heads of a group in one workgroup, the
+//    tile shared in registers, measured slower at the GLM-4-9B shape: each
+//    16-token step becomes four times the vector work with too few waves to
+//    cover it.)
 #include <math.h>
 
 #include <cmath>
@@ -1223,10 +1232,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams P) {
   const int hw = blockIdx.x;
   const int lin = (hw % kNumXcd) * P.blocks_per_xcd + hw / kNumXcd;
   if (lin >= P.blocks_used) return;
-  const int unit = lin / P.S;
-  const int split = lin % P.S;
-  const int hc = unit % P.nhc;
-  const int bh = unit / P.nhc;
+  // the head chunks of one KV head are adjacent for each split, so they
+  // run together on one XCD and read each KV tile from HBM once (the other
+  // chunks' reads hit that XCD's L2)
+  const int hc = lin % P.nhc;
+  const int split = (lin / P.nhc) % P.S;
+  const int bh = lin / (P.nhc * P.S);
   const int h = bh % P.Hkv;
   const int b = bh / P.Hkv;
   const int i0 = h * P.G + hc * HB;           // first query head of this block
