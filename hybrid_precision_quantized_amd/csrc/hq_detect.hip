@@ -1155,7 +1155,8 @@ DetWs det_ws(int B, int Hkv, int64_t cand_end) {
 // {s, z} word, and the D / 32 lanes of a row add their group terms. A block
 // takes 256 rows; every lane issues the loads of all its rows first (one
 // row per pass of 256 / (D / 32) rows), then computes, so the block waits
-// for one round of loads instead of one per row. Every product and sum is
+// for one round of loads instead of one per row; the summed query comes
+// through LDS once per block. Every product and sum is
 // in fp64: exact for queries on the 2^-4 grid within the fp64 range (the
 // products are multiples of 2^-28), whatever the order.
 template <int D>
@@ -1187,11 +1188,16 @@ __global__ __launch_bounds__(256) void gemv_int4_kernel(const uint8_t *__restric
       w[p] = 0u;
     }
   }
+  // the unit's summed query, once per block through LDS (lanes of one group
+  // read the same words: broadcasts)
+  __shared__ double qsh[D];
+  if (static_cast<int>(threadIdx.x) < D) qsh[threadIdx.x] = qs[static_cast<int64_t>(unit) * D + threadIdx.x];
+  __syncthreads();
   double qv[32];
   double qsum = 0.0;
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
-    qv[e] = qs[static_cast<int64_t>(unit) * D + g * 32 + e];
+    qv[e] = qsh[g * 32 + e];
     qsum += qv[e];
   }
   unsigned long long mn = ~0ull, mx = 0;

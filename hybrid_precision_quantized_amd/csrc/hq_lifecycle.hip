@@ -73,6 +73,9 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
   __shared__ int scan[kUpdThreads];
   __shared__ int hist[256];
   __shared__ int sel_digit, sel_need, sel_count;
+  __shared__ unsigned long long red_mn[kUpdThreads / 64], red_mx[kUpdThreads / 64];
+  __shared__ uint16_t list[64];             // the candidates still alive, once at most 64
+  __shared__ int n_list, n_alive, first_digit;
   __shared__ int n_freed_sh;
   const int64_t unit = blockIdx.x;
   const int tid = threadIdx.x;
@@ -90,18 +93,63 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     alive[i] = 1;
   }
   int need = k;                             // still to take among the alive candidates
-  __syncthreads();
+  // the bytes every score key shares need no pass: start at the first byte
+  // where the smallest and largest keys differ
+  {
+    unsigned long long mn = ~0ull, mx = 0ull;
+    for (int i = tid; i < n; i += kUpdThreads) {
+      mn = key[i] < mn ? key[i] : mn;
+      mx = key[i] > mx ? key[i] : mx;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    if (lane == 0) {
+      red_mn[tid >> 6] = mn;
+      red_mx[tid >> 6] = mx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < kUpdThreads / 64; ++w) {
+        mn = red_mn[w] < mn ? red_mn[w] : mn;
+        mx = red_mx[w] > mx ? red_mx[w] : mx;
+      }
+      const unsigned long long x = mn ^ mx;
+      first_digit = x ? __clzll(static_cast<long long>(x)) / 8 : 8;    // all keys equal: positions only
+      n_alive = n;
+      n_list = -1;                                                       // no pass has listed survivors
+    }
+    __syncthreads();
+  }
 
   // ---- radix select of the k best, most significant byte first: each pass
   // counts the alive candidates per digit, finds the digit b* at which the
   // count from the top reaches `need`, takes the alive candidates above it
-  // and keeps those equal to it alive. Ends when the digit's whole bucket is
-  // needed (or after the last digit, where one candidate is left).
-  for (int d = 0; d < 12 && need > 0; ++d) {
+  // and keeps those equal to it alive (listing them). When the digit's whole
+  // bucket is needed the selection is complete; when at most 64 candidates
+  // are left alive one wave ranks them directly.
+  for (int d = first_digit; d < 12 && need > 0 && n_alive > 64; ++d) {
     if (tid < 256) hist[tid] = 0;
+    if (tid == 0) n_list = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kUpdThreads)
-      if (alive[i]) atomicAdd(&hist[rank_digit(key[i], pos[i], d)], 1);
+    // skewed scores put many candidates in one bin: the lanes of a wave
+    // that share the digit of the first active lane add with one atomic
+    for (int i0 = 0; i0 < n; i0 += kUpdThreads) {
+      const int i = i0 + tid;
+      const bool act = i < n && alive[i];
+      const int dg = act ? static_cast<int>(rank_digit(key[i], pos[i], d)) : -1;
+      const unsigned long long am = __ballot(act);
+      if (am) {
+        const int lead = __ffsll(static_cast<long long>(am)) - 1;
+        const int d0 = __shfl(dg, lead, 64);
+        const unsigned long long same = __ballot(act && dg == d0);
+        if (lane == lead) atomicAdd(&hist[d0], __popcll(same));
+        else if (act && dg != d0) atomicAdd(&hist[dg], 1);
+      }
+    }
     __syncthreads();
     if (tid < 64) {
       // lane l holds the bins 255 - 4l .. 252 - 4l (descending)
@@ -142,11 +190,33 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
         alive[i] = 0;
       } else if (dg < bstar) {
         alive[i] = 0;
+      } else if (sel_count <= 64) {
+        list[atomicAdd(&n_list, 1)] = static_cast<uint16_t>(i);
       }
     }
     need = whole ? 0 : sel_need;
+    if (tid == 0) n_alive = whole ? 0 : sel_count;
     __syncthreads();
   }
+  // at most 64 candidates left: lane l ranks the l-th of them by (score,
+  // position) against the others; the best `need` are taken
+  if (need > 0 && tid < 64) {
+    // either the last pass listed its survivors, or no pass ran (n <= 64,
+    // every candidate alive)
+    const bool listed = n_list >= 0;
+    const int cnt_alive = listed ? n_list : n;
+    const int i = lane < cnt_alive ? (listed ? static_cast<int>(list[lane]) : lane) : 0;
+    const unsigned long long ki = lane < cnt_alive ? key[i] : 0ull;
+    const int32_t pi = lane < cnt_alive ? pos[i] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < cnt_alive; ++j) {
+      const unsigned long long kj = __shfl(ki, j, 64);
+      const int32_t pj = __shfl(pi, j, 64);
+      rank += (kj > ki || (kj == ki && pj < pi)) ? 1 : 0;
+    }
+    if (lane < cnt_alive && rank < need) taken[i] = 1;
+  }
+  __syncthreads();
 
   // ---- flags: a freed slot (VL candidate not kept) or a promoted position
   // (recent candidate kept); one block scan ranks both in candidate order.
@@ -159,15 +229,27 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     const int i = c0 + e;
     if (i < n) cnt += (i < k) ? !taken[i] : taken[i];
   }
-  scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < kUpdThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  // block exclusive scan: inclusive within each wave, then the wave totals
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  const int excl = scan[tid] - cnt;
+  if (lane == 63) scan[tid >> 6] = incl;
+  __syncthreads();
+  if (tid < 64) {
+    const int wt = tid < kUpdThreads / 64 ? scan[tid] : 0;
+    int wi = wt;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int v = __shfl_up(wi, off, 64);
+      if (lane >= off) wi += v;
+    }
+    if (tid < kUpdThreads / 64) scan[64 + tid] = wi - wt;          // waves before this one
+  }
+  __syncthreads();
+  const int excl = scan[64 + (tid >> 6)] + incl - cnt;
   // the freed count: the exclusive prefix at candidate k (k < n), found by
   // the thread whose run holds candidate k
   if (c0 <= k && k < c0 + kPer) {

@@ -90,6 +90,8 @@ def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, d
     (1638, 64, 1 << 40, 3),  # the Llama-shaped budget, scores over a wide range (negative too)
     (8000, 64, 7, 4),        # close to the candidate limit, heavy ties
     (300, 1, 2, 5),          # one position left the window
+    (20, 30, 3, 6),          # at most 64 candidates: ranked directly
+    (100, 64, 0, 7),         # every score equal: the positions decide alone
 ])
 def test_vl_update_ties_and_sizes(k, n_st, spread, seed):
     """hq_vl_update alone on constructed scores, against the oracle's update
