@@ -75,6 +75,9 @@ def parse():
                     help="time the steps as stream launches instead of one HIP graph replay (the default "
                          "captures exactly `steps` steps in one graph and times its replay, so that the "
                          "host's enqueue rate cannot set the pace)")
+    ap.add_argument("--prefill-form", default="split", choices=["split", "i8"],
+                    help="prefill32k: the quantized Q.K form the step uses (split fp16 planes, or int8 MFMA "
+                         "over the codes); both are timed per call")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the 16 x 128K entry of the default workload's line")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -775,8 +778,10 @@ def main_prefill(args):
         hq.hq_detect_vlines(None, q_last, B, Hq, Hkv, D, R, 0, True, K, T, T - W, k,
                             hq.HQ_DETECT_MATMUL, idx, None, det_ws)
 
-    def prefill():
-        hq.hq_prefill_attn(q, K, V, B, Hq, Hkv, T, D, W, idx, k, 0.0, out, lse, ws)
+    form = args.prefill_form
+
+    def prefill(f=form):
+        hq.hq_prefill_attn(q, K, V, B, Hq, Hkv, T, D, W, idx, k, 0.0, out, lse, ws, form=f)
 
     steps = max(1, min(args.steps, 20))
     warm = max(1, min(args.warmup, 3))
@@ -794,18 +799,27 @@ def main_prefill(args):
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / steps
 
-    # hq_prefill_attn alone, per call (pre-pass + tiling + the attention kernel)
+    # one prefill call alone (pre-pass + tiling + the attention kernel), both
+    # forms of the quantized Q.K
     n_l = max(3, min(args.kernel_launches, 10))
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_l)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_l)]
-    for i in range(n_l):
-        starts[i].record(stream)
-        prefill()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    call_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+
+    def time_calls(f):
+        prefill(f)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_l)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_l)]
+        for i in range(n_l):
+            starts[i].record(stream)
+            prefill(f)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
 
     flops = 2.0 * 2.0 * B * Hq * D * (T * (T + 1) / 2.0)
+    form_ms = {f: time_calls(f) for f in ("split", "i8")}
+    call_ms = form_ms[form]
+    forms = {f: {"entry": "hq_prefill_attn" if f == "split" else "hq_prefill_attn_i8",
+                 "avg_launch_ms": round(ms, 4), "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+             for f, ms in form_ms.items()}
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (call_ms * 1e-3) / 1e12
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_seconds, flops)
@@ -820,7 +834,8 @@ def main_prefill(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 q/k (f16 hi+lo MFMA) + bf16 (fp32 accumulate)",
+        "dtype": ("int4 q/k (f16 hi+lo MFMA) + bf16 (fp32 accumulate)" if form == "split" else
+                  "int4 q/k (int8 MFMA over the codes, fp32 scale epilogue) + bf16 (fp32 accumulate)"),
         "data": "synthetic (seeded; shapes of the named model's attention layer, random-init values)",
         "config": {
             "workload": f"prefill32k: causal prefill of one attention layer, B {B}, {Hq} q / {Hkv} kv heads, "
@@ -829,7 +844,7 @@ def main_prefill(args):
             "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": "prefill_kernel (hq_prefill_attn, timed per call incl. its pre-pass)",
+            "kernel": (f"prefill_kernel ({forms[form]['entry']}, timed per call incl. its pre-pass)"),
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_MFMA_F16_TFLOPS,
@@ -839,6 +854,7 @@ def main_prefill(args):
             "algorithmic_flops_per_launch": int(flops),
             "avg_launch_ms": round(call_ms, 4),
         },
+        "qk_forms": forms,
         "setup_s": round(t_setup, 1),
         "cpu_baseline": cpu,
     }

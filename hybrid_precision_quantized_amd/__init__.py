@@ -107,6 +107,11 @@ _SIGS = {
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                        ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_prefill_attn_i8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "hq_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                     ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
     "hq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -309,14 +314,18 @@ def hq_prefill_workspace_size(B, Hq, Hkv, T, D, k_vl) -> int:
 
 
 def hq_prefill_attn(q, k, v, B, Hq, Hkv, T, D, W, vl_idx, k_vl, sm_scale, out, lse, ws, group=32,
-                    stream=None):
-    """Causal hybrid-precision prefill attention (see include/hq.h)."""
+                    stream=None, form="split"):
+    """Causal hybrid-precision prefill attention (see include/hq.h). form:
+    "split" (hq_prefill_attn, split fp16 planes) or "i8" (hq_prefill_attn_i8,
+    int8 MFMA over the codes)."""
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k and v must share a dtype")
+    if form not in ("split", "i8"):
+        raise ValueError(f"unknown prefill form {form!r}")
+    fn = lib().hq_prefill_attn if form == "split" else lib().hq_prefill_attn_i8
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().hq_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, T, D, group, W,
-                                 _ptr(vl_idx), k_vl, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
-                                 ws_bytes, _stream(stream)))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, T, D, group, W, _ptr(vl_idx), k_vl,
+              float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def hq_status_string(s: int) -> str:

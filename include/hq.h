@@ -432,8 +432,8 @@ hq_status hq_vl_update(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, cons
  * product and V is converted to fp16 (exact for bf16 magnitudes in
  * [2^-17, 65504]; smaller ones round to the fp16 subnormal grid, absolute
  * error below 2^-25; larger ones are a precondition violation).
- * Errors: HQ_ERR_UNSUPPORTED for another dtype, D or group, or more than
- * 5e8 query groups (B * Hq * T * D / 32) in one call; HQ_ERR_INVALID_ARG for
+ * Errors: HQ_ERR_UNSUPPORTED for another dtype, D or group, T >= 2^23, or
+ * more than 5e8 query groups (B * Hq * T * D / 32) in one call; HQ_ERR_INVALID_ARG for
  * sizes < 1, Hq % Hkv != 0, W or k_vl < 0, k_vl > T, null or misaligned
  * pointers; HQ_ERR_WORKSPACE if ws_bytes is too small. Nothing is enqueued
  * on error. The VL positions themselves are not checked on the device.
@@ -443,8 +443,31 @@ hq_status hq_prefill_attn(const void *q, const void *k, const void *v, hq_dtype 
                           float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
                           void *stream);
 
-/* Workspace bytes hq_prefill_attn needs for these sizes (0 if a size is
- * out of range). */
+/*
+ * hq_prefill_attn_i8 -- the same operator as hq_prefill_attn, arguments,
+ * layouts, workspace and errors alike, with the quantized logits computed in
+ * integer form [AFS, The Technical Mechanics, Prefill Stage: the quantized
+ * majority runs on low-precision integer arithmetic]: per 32-channel group,
+ *   q_hat . k_hat = sq sk C + zk (sq Cq + 32 zq) + zq sk Ck,
+ * C the dot product of the two rows' 4-bit codes (an int8 matrix-core
+ * product, exact), Cq and Ck the groups' code sums, (s, z) the fp16 scales
+ * and zeros. Precision: the main term is sq sk C in fp32 (two roundings);
+ * the zero-point terms pass through fp16 hi/lo pairs of
+ * (sq Cq + 32 zq) 2^(a - 6), 2^a a power of two per query row that puts the
+ * row's largest operand just below 2^14, and of sk Ck / 64 (relative 2^-22;
+ * absolute 2^-19 where sk Ck falls below 2^-8); the quantized logits are
+ * within about 2^-21 of the sum of the terms' magnitudes. P . V as in
+ * hq_prefill_attn. Same speed as hq_prefill_attn on gfx950: the group-scale
+ * products per logit load the vector unit as much as the fp16 passes they
+ * replace load the matrix cores.
+ */
+hq_status hq_prefill_attn_i8(const void *q, const void *k, const void *v, hq_dtype dtype, int B, int Hq,
+                             int Hkv, int64_t T, int D, int group, int W, const int32_t *vl_idx, int k_vl,
+                             float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Workspace bytes hq_prefill_attn and hq_prefill_attn_i8 need for these
+ * sizes (0 if a size is out of range). */
 size_t hq_prefill_workspace_size(int B, int Hq, int Hkv, int64_t T, int D, int k_vl);
 
 /*

@@ -138,6 +138,27 @@ int main(void) {
   bad |= expect("prefill workspace", hq_prefill_attn(FAKE, FAKE, FAKE, HQ_BF16, 1, 8, 2, 1000, 128, 32, 128, FAKE,
                                                     50, 0.f, FAKE, NULL, FAKE, 64, NULL), HQ_ERR_WORKSPACE);
 
+  bad |= expect("prefill i8 D", hq_prefill_attn_i8(FAKE, FAKE, FAKE, HQ_BF16, 1, 8, 2, 1000, 64, 32, 128, FAKE, 50,
+                                                  0.f, FAKE, NULL, FAKE, big, NULL), HQ_ERR_UNSUPPORTED);
+  bad |= expect("prefill i8 T", hq_prefill_attn_i8(FAKE, FAKE, FAKE, HQ_BF16, 1, 2, 2, (int64_t)1 << 23, 128, 32, 128,
+                                                  NULL, 0, 0.f, FAKE, NULL, FAKE, big, NULL), HQ_ERR_UNSUPPORTED);
+  bad |= expect("prefill i8 workspace", hq_prefill_attn_i8(FAKE, FAKE, FAKE, HQ_BF16, 1, 8, 2, 1000, 128, 32, 128,
+                                                          FAKE, 50, 0.f, FAKE, NULL, FAKE, 64, NULL),
+                HQ_ERR_WORKSPACE);
+
+  /* rolling-cache VL update (T - W = 872 positions, ring of W rows) */
+  bad |= expect("vl update null kv", hq_vl_update(NULL, FAKE, 800, FAKE, 872, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl update p0 past T - W", hq_vl_update(&kv, FAKE, 873, FAKE, 872, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl update p0 before the ring", hq_vl_update(&kv, FAKE, 700, FAKE, 872, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl update stride", hq_vl_update(&kv, FAKE, 872, FAKE, 871, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl update no-op", hq_vl_update(&kv, FAKE, 872, FAKE, 872, NULL), HQ_OK);
+
+  /* allocation-free decode: rejected before any device is touched */
+  bad |= expect("noalloc null kv", hq_decode_attn_noalloc(FAKE, HQ_BF16, 8, NULL, 0.f, 0, FAKE, NULL, NULL),
+                HQ_ERR_INVALID_ARG);
+  bad |= expect("noalloc Hq", hq_decode_attn_noalloc(FAKE, HQ_BF16, 7, &kv, 0.f, 0, FAKE, NULL, NULL),
+                HQ_ERR_INVALID_ARG);
+
   /* stream read */
   bad |= expect("stream read size", hq_stream_read(FAKE, 4100, FAKE, NULL), HQ_ERR_INVALID_ARG);
   bad |= expect("stream read empty", hq_stream_read(FAKE, 0, FAKE, NULL), HQ_OK);

@@ -218,16 +218,17 @@ def test_quantize_pair_rejects():
     assert call(nr=0) == hq.HQ_OK                        # empty: no-op
 
 
-def test_prefill_rejects():
+@pytest.mark.parametrize("entry", ["hq_prefill_attn", "hq_prefill_attn_i8"])
+def test_prefill_rejects(entry):
     L = hq.lib()
+    fn = getattr(L, entry)
     ok = dict(q=FAKE, k=FAKE, v=FAKE, dt=hq.HQ_BF16, B=1, Hq=8, Hkv=2, T=1000, D=128, g=32, W=128,
               vl=FAKE, kvl=50, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
 
     def call(**o):
         a = dict(ok, **o)
-        return L.hq_prefill_attn(a["q"], a["k"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["T"], a["D"],
-                                 a["g"], a["W"], a["vl"], a["kvl"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"],
-                                 None)
+        return fn(a["q"], a["k"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["T"], a["D"], a["g"], a["W"],
+                  a["vl"], a["kvl"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"], None)
     assert call(dt=hq.HQ_F32) == hq.HQ_ERR_UNSUPPORTED
     assert call(D=64) == hq.HQ_ERR_UNSUPPORTED
     assert call(g=16) == hq.HQ_ERR_UNSUPPORTED
@@ -241,6 +242,8 @@ def test_prefill_rejects():
     assert need > 0
     assert call(wsb=need - 1) == hq.HQ_ERR_WORKSPACE
     assert call(ws=FAKE + 16) == hq.HQ_ERR_INVALID_ARG    # workspace not 256-byte aligned
+    assert call(T=1 << 23, Hq=2, kvl=0) == hq.HQ_ERR_UNSUPPORTED   # one head's planes past 2^31 bytes
+    assert entry in hq.hq_last_error()
 
 
 def test_detect_cache_and_mass_reject():

@@ -1,4 +1,5 @@
-"""GPU parity of hq_prefill_attn against the oracle hybrid prefill operator
+"""GPU parity of hq_prefill_attn (split fp16 planes) and hq_prefill_attn_i8
+(int8 MFMA over the codes) against the oracle hybrid prefill operator
 (oracle/prefill.py): every output row on small prompts (ragged tails,
 windows of 0 / inside / beyond the prompt, with and without vertical lines,
 bf16 and fp16), and sampled rows of the full 32K-token causal prompt with
@@ -27,7 +28,7 @@ def _inputs(w):
     return q, K, V
 
 
-def _run(w, q, K, V, vl):
+def _run(w, q, K, V, vl, form="split"):
     B, Hq, Hkv, T, D = w.B, w.Hq, w.Hkv, w.T, w.D
     k = vl.shape[2]
     qd, kd, vd = to_dev(q, w.dtype), to_dev(K, w.dtype), to_dev(V, w.dtype)
@@ -36,7 +37,7 @@ def _run(w, q, K, V, vl):
     lse = torch.full((B, Hq, T), float("nan"), dtype=torch.float32, device="cuda")
     # the workspace needs no initialisation: start from garbage
     ws = torch.full((hq.hq_prefill_workspace_size(B, Hq, Hkv, T, D, k),), 0xFF, dtype=torch.uint8, device="cuda")
-    hq.hq_prefill_attn(qd, kd, vd, B, Hq, Hkv, T, D, w.W, vld, k, 0.0, out, lse, ws)
+    hq.hq_prefill_attn(qd, kd, vd, B, Hq, Hkv, T, D, w.W, vld, k, 0.0, out, lse, ws, form=form)
     torch.cuda.synchronize()
     return out, lse
 
@@ -75,6 +76,10 @@ def _vl_random(w, k):
     return out
 
 
+FORMS = ("split", "i8")
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("B,Hq,Hkv,T,W,k,dtype", [
     (1, 4, 1, 200, 16, 10, "bf16"),
     (1, 8, 2, 333, 64, 20, "bf16"),
@@ -84,17 +89,56 @@ def _vl_random(w, k):
     (1, 8, 2, 1000, 128, 50, "bf16"),
     (1, 4, 1, 290, 3, 40, "f16"),
 ])
-def test_prefill_small(B, Hq, Hkv, T, W, k, dtype):
+def test_prefill_small(B, Hq, Hkv, T, W, k, dtype, form):
     w = synth.Workload("pf", 3000 + T + W + k, B=B, Hq=Hq, Hkv=Hkv, D=128, T=T, W=W, k=k, dtype=dtype,
                        n_plant=max(1, T // 50))
-    say(f"prefill small B={B} Hq={Hq} Hkv={Hkv} T={T} W={W} k={k} {dtype}")
+    say(f"prefill small B={B} Hq={Hq} Hkv={Hkv} T={T} W={W} k={k} {dtype} {form}")
     q, K, V = _inputs(w)
     vl = _vl_random(w, k)
     rows = np.arange(T)
-    _compare(_run(w, q, K, V, vl), _oracle(w, q, K, V, vl, rows), rows)
+    _compare(_run(w, q, K, V, vl, form), _oracle(w, q, K, V, vl, rows), rows)
 
 
-def test_prefill_32k_sampled():
+@pytest.mark.parametrize("form", FORMS)
+def test_prefill_extremes(form):
+    """Plain (off-grid) rows with groups near the fp16 limit (|x| up to 6e4),
+    groups below 2^-14 and constant groups, bf16: the integer form's zero-point
+    operands (sums over a group, divided by 64) stay in range and the small
+    groups of either form lose nothing that shows. The softmax here is peaked,
+    so the bar is per element and follows from the one rounding the two forms
+    share, P to fp16 for P . V (relative 2^-11 per probability): |out - ref| <=
+    2^-10 sum_j p_j |v_j| + 1e-6, the sum being the oracle's output with |V|
+    for V; lse within 2e-3."""
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, T, D, W, k = 1, 4, 1, 300, 128, 16, 6
+    q = rng.standard_normal((B, Hq, T, D))
+    K = rng.standard_normal((B, Hkv, T, D))
+    V = rng.standard_normal((B, Hkv, T, D))
+    K[:, :, ::7, 0:32] *= 3e4 / 4                     # groups reaching ~ 3e4
+    K[:, :, 3::11, 32:64] = 6.0e4                     # constant groups at the top of the range
+    q[:, :, ::5, 64:96] *= 1e-5                       # groups far below 2^-14
+    q[:, :, 2::9, 96:128] = -2.5                      # constant query groups
+    q *= 1.0 / 3e4                                    # keep the logits O(1)
+    w = synth.Workload("pfx", 1, B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, W=W, k=k, dtype="bf16", n_plant=1)
+    qb, Kb, Vb = (synth.round_dtype(x, "bf16") for x in (q, K, V))
+    vl = np.sort(rng.choice(T, (B, Hkv, k), replace=False), axis=-1).astype(np.int32)
+    rows = np.arange(T)
+    say(f"prefill extremes {form}")
+    out, lse = _run(w, qb, Kb, Vb, vl, form)
+    ref = _oracle(w, qb, Kb, Vb, vl, rows)
+    mag = _oracle(w, qb, Kb, np.abs(Vb), vl, rows)
+    for key in ref:
+        b, i = key
+        o = out[b, i].cpu().numpy()
+        err = np.abs(o - ref[key][0])
+        bound = 2.0 ** -10 * mag[key][0] + 1e-6
+        say(f"   head {i}: max err/bound = {float(np.max(err / bound)):.3f}")
+        assert np.all(np.isfinite(o)) and np.all(err <= bound)
+        assert float(np.max(np.abs(lse[b, i].cpu().numpy() - ref[key][1]))) <= TOL
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_prefill_32k_sampled(form):
     """32K-token causal prompt, 32 query / 8 KV heads; the GPU computes every
     row of every head; the oracle checks sampled rows of KV heads 0 and 5."""
     w = synth.WORKLOADS["prefill32k"]
@@ -103,8 +147,8 @@ def test_prefill_32k_sampled():
     # the VL set: the oracle detector over the last 64 query rows
     qh = q[:, :, w.T - 64:]
     vl, _ = detect.detect(qh, K, w.T - w.W, w.k)
-    say("prefill 32K (run)")
-    got = _run(w, q, K, V, vl)
+    say(f"prefill 32K (run, {form})")
+    got = _run(w, q, K, V, vl, form)
     rows = np.array([0, 1, 2, 127, 128, 129, 255, 4095, 4096, 20011, w.T - 129, w.T - 128, w.T - 1])
     say("prefill 32K (oracle)")
     _compare(got, _oracle(w, q, K, V, vl, rows, kv_heads=(0, 5)), rows)
