@@ -267,74 +267,81 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
 }
 
 // ---------------------------------------------------------------- QSUM form
-// One block per unit: qs[d] = sum over the unit's rows of q_acc[row][d] in
-// fp64, rows split over 8 row phases and combined in fixed order.
 // Summed query rows of one unit (b, KV head): qs[d] = sum over the G * R rows
-// of q_acc[b][h G + i][r][d], in fp64. D / 8 threads per row, 8 channels each
-// (one 16-byte load of 16-bit values), 1024 / (D / 8) row groups striding
-// over the rows; the groups' sums meet in LDS and are added in group order.
+// of q_acc[b][h G + i][r][d], in fp64. One block of 256 threads per (unit,
+// 8-channel slice): thread t loads the slice of rows t, t + 256, ... (one
+// 16-byte load of 16-bit values, or two of fp32, per row; eight rows' loads
+// in flight before their sums), the 64 lanes of a wave combine by butterfly exchanges,
+// and the four waves' sums meet in LDS in wave order. Fixed order throughout
+// (deterministic); exact for queries on the 2^-4 grid within the fp64 range.
 template <int DT>
-__global__ __launch_bounds__(1024) void qsum_kernel(const void *__restrict__ q_acc, int Hq, int Hkv,
-                                                    int R, int D, double *__restrict__ qs) {
-  __shared__ double part[1024 * 8];
-  const int unit = blockIdx.x;
+__global__ __launch_bounds__(256) void qsum_kernel(const void *__restrict__ q_acc, int Hq, int Hkv, int R,
+                                                   int D, double *__restrict__ qs) {
+  constexpr int kBatch = 8;                   // rows per thread in flight
+  __shared__ double part[4][8];
+  const int slices = D / 8;
+  const int unit = blockIdx.x / slices;
+  const int sl = blockIdx.x % slices;
   const int G = Hq / Hkv;
   const int b = unit / Hkv;
   const int h = unit % Hkv;
   const int M = G * R;
-  const int lpr = D / 8;                       // threads per row
-  const int ng = 1024 / lpr;                   // row groups
-  const int sub = threadIdx.x % lpr;
-  const int rg = threadIdx.x / lpr;
-  const int64_t base = (static_cast<int64_t>(b) * Hq + h * G) * R * D;
+  const int t = threadIdx.x;
+  const int64_t base = (static_cast<int64_t>(b) * Hq + h * G) * R * D + sl * 8;
   double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  // four rows per group in flight at a time (loads first, then the sums)
-  constexpr int NB = 4;
-  for (int r = rg; r < M; r += NB * ng) {
+  for (int r0 = t; r0 < M; r0 += 256 * kBatch) {
     if constexpr (DT == HQ_F32) {
-      float4 x[NB][2];
+      float4 x[kBatch][2];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int rr = r + j * ng;
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q_acc) + base +
-                                                           static_cast<int64_t>(rr < M ? rr : r) * D + sub * 8);
-        x[j][0] = rr < M ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-        x[j][1] = rr < M ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < kBatch; ++j) {
+        const int r = r0 + 256 * j;
+        if (r < M) {
+          const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q_acc) + base +
+                                                             static_cast<int64_t>(r) * D);
+          x[j][0] = p[0];
+          x[j][1] = p[1];
+        }
       }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const float v[8] = {x[j][0].x, x[j][0].y, x[j][0].z, x[j][0].w, x[j][1].x, x[j][1].y, x[j][1].z, x[j][1].w};
+      for (int j = 0; j < kBatch; ++j) {
+        if (r0 + 256 * j < M) {
+          const float v[8] = {x[j][0].x, x[j][0].y, x[j][0].z, x[j][0].w,
+                              x[j][1].x, x[j][1].y, x[j][1].z, x[j][1].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(v[e]);
+          for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(v[e]);
+        }
       }
     } else {
-      uint4 u[NB];
+      uint4 u[kBatch];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int rr = r + j * ng;
-        u[j] = rr < M ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q_acc) + base +
-                                                         static_cast<int64_t>(rr) * D + sub * 8)
-                      : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < kBatch; ++j) {
+        const int r = r0 + 256 * j;
+        if (r < M)
+          u[j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q_acc) + base +
+                                                  static_cast<int64_t>(r) * D);
       }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+      for (int j = 0; j < kBatch; ++j) {
+        if (r0 + 256 * j < M) {
+          const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[2 * e] += static_cast<double>(load_half<DT>(w[e] & 0xFFFFu));
-          s[2 * e + 1] += static_cast<double>(load_half<DT>(w[e] >> 16));
+          for (int e = 0; e < 4; ++e) {
+            s[2 * e] += static_cast<double>(load_half<DT>(w[e] & 0xFFFFu));
+            s[2 * e + 1] += static_cast<double>(load_half<DT>(w[e] >> 16));
+          }
         }
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg * D + sub * 8 + e] = s[e];
+  for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += __shfl_xor(s[e], m, 64);
+  if ((t & 63) == 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[t >> 6][e] = s[e];
   __syncthreads();
-  if (static_cast<int>(threadIdx.x) < D) {
-    double t = 0.0;
-    for (int g2 = 0; g2 < ng; ++g2) t += part[g2 * D + threadIdx.x];
-    qs[static_cast<int64_t>(unit) * D + threadIdx.x] = t;
-  }
+  if (t < 8) qs[static_cast<int64_t>(unit) * D + sl * 8 + t] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
 }
 
 // 256 threads; lanes in groups of D/8 per key row (8 channels per lane).
@@ -1533,9 +1540,9 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
     } else {
       double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
       switch (dtype) {
-        case HQ_F32: hipLaunchKernelGGL(qsum_kernel<HQ_F32>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
-        case HQ_BF16: hipLaunchKernelGGL(qsum_kernel<HQ_BF16>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
-        default: hipLaunchKernelGGL(qsum_kernel<HQ_F16>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+        case HQ_F32: hipLaunchKernelGGL(qsum_kernel<HQ_F32>, dim3(units * (D / 8)), dim3(256), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+        case HQ_BF16: hipLaunchKernelGGL(qsum_kernel<HQ_BF16>, dim3(units * (D / 8)), dim3(256), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+        default: hipLaunchKernelGGL(qsum_kernel<HQ_F16>, dim3(units * (D / 8)), dim3(256), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
       }
       const int cpu = static_cast<int>((cand_end + 255) / 256);
       const dim3 grid(static_cast<unsigned>(units * cpu));
@@ -1612,9 +1619,9 @@ extern "C" hq_status hq_detect_vlines_cache(const void *q_new, void *q_acc, hq_d
   if (cand_end > 0) {
     double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
     switch (dtype) {
-      case HQ_F32: hipLaunchKernelGGL(qsum_kernel<HQ_F32>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
-      case HQ_BF16: hipLaunchKernelGGL(qsum_kernel<HQ_BF16>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
-      default: hipLaunchKernelGGL(qsum_kernel<HQ_F16>, dim3(units), dim3(1024), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+      case HQ_F32: hipLaunchKernelGGL(qsum_kernel<HQ_F32>, dim3(units * (D / 8)), dim3(256), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+      case HQ_BF16: hipLaunchKernelGGL(qsum_kernel<HQ_BF16>, dim3(units * (D / 8)), dim3(256), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
+      default: hipLaunchKernelGGL(qsum_kernel<HQ_F16>, dim3(units * (D / 8)), dim3(256), 0, st, q_acc, Hq, Hkv, R, D, qs); break;
     }
     const int cpu = static_cast<int>((cand_end + 255) / 256);
     const dim3 grid(static_cast<unsigned>(units * cpu));

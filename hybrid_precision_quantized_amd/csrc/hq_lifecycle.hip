@@ -18,11 +18,15 @@
 //  * The n <= 8192 candidates (the current VL rows in slot order, then the
 //    recent range) are loaded into LDS with their scores as order-preserving
 //    64-bit keys. The k best (larger score, then lower position) are found
-//    by a radix select over the 96-bit rank key (score key, then inverted
-//    position), most significant byte first: per pass a 256-bin histogram of
-//    the candidates still tied with the threshold, one wave's scan for the
-//    digit where the count from the top reaches what is still needed, and
-//    the candidates above it taken. No sort: a dozen passes at most.
+//    by a radix select over the rank key (score key minus the smallest, then
+//    the inverted position: B + 32 bits, B the width of the score range),
+//    most significant 12 bits first: per pass a 4096-bin histogram of the
+//    candidates still tied with the threshold, one wave's scan for the digit
+//    where the count from the top reaches what is still needed, and the
+//    candidates above it taken. With 4096 bins over the score range the
+//    boundary bin usually holds a few candidates, and once at most 64 are
+//    left one wave ranks them directly: one pass in the common case, a few
+//    for heavy ties.
 //  * The VL rows keep their slots: the slot of every dropped VL position is
 //    refilled with a promoted one (the j-th freed slot in slot order takes
 //    the j-th promoted position in position order, both found with one
@@ -50,17 +54,23 @@ struct UpdParams {
   int k, C, win_offset, row_bytes;
 };
 
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+
 __device__ __forceinline__ unsigned long long order_key(long long v) {
   return static_cast<unsigned long long>(v) ^ 0x8000000000000000ull;
 }
 
-// Digit d (0 = most significant) of a candidate's 96-bit rank key: the
-// 64-bit order-preserving score key, then 2^32 - 1 - position (a lower
-// position ranks higher). Keys are distinct because positions are.
-__device__ __forceinline__ uint32_t rank_digit(unsigned long long key, int32_t pos, int d) {
-  if (d < 8) return static_cast<uint32_t>(key >> (8 * (7 - d))) & 0xFFu;
-  const uint32_t inv = 0xFFFFFFFFu - static_cast<uint32_t>(pos);
-  return (inv >> (8 * (11 - d))) & 0xFFu;
+// Bits [sh, sh + w) (w <= 12) of a candidate's rank key R = hi 2^32 + lo:
+// hi = its score key minus the smallest (fewer than 64 bits), lo = 2^32 - 1 -
+// position (a lower position ranks higher). Keys are distinct because
+// positions are.
+__device__ __forceinline__ uint32_t rank_bits(unsigned long long hi, int32_t pos, int sh, int w) {
+  const uint32_t lo = 0xFFFFFFFFu - static_cast<uint32_t>(pos);
+  const uint32_t mask = (1u << w) - 1u;
+  if (sh >= 32) return static_cast<uint32_t>(hi >> (sh - 32)) & mask;
+  if (sh + w <= 32) return (lo >> sh) & mask;
+  return static_cast<uint32_t>((static_cast<unsigned long long>(lo) >> sh) | (hi << (32 - sh))) & mask;
 }
 
 __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
@@ -71,11 +81,12 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
   __shared__ uint16_t freed[kMaxMoved];     // j-th freed VL slot
   __shared__ int32_t prom[kMaxMoved];       // j-th promoted position
   __shared__ int scan[kUpdThreads];
-  __shared__ int hist[256];
+  __shared__ __align__(16) int hist[kBins];
   __shared__ int sel_digit, sel_need, sel_count;
   __shared__ unsigned long long red_mn[kUpdThreads / 64], red_mx[kUpdThreads / 64];
   __shared__ uint16_t list[64];             // the candidates still alive, once at most 64
-  __shared__ int n_list, n_alive, first_digit;
+  __shared__ int n_list, n_alive, key_bits;
+  __shared__ unsigned long long key_min;
   __shared__ int n_freed_sh;
   const int64_t unit = blockIdx.x;
   const int tid = threadIdx.x;
@@ -84,22 +95,19 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
   const int n = k + static_cast<int>(P.nq - P.p0);
   int32_t *ui = P.idx + unit * k;
 
-  // ---- candidates and their keys
-  for (int i = tid; i < n; i += kUpdThreads) {
-    const int64_t p = i < k ? static_cast<int64_t>(ui[i]) : P.p0 + (i - k);
-    pos[i] = static_cast<int32_t>(p);
-    key[i] = order_key(P.scores[unit * P.stride + p]);
-    taken[i] = 0;
-    alive[i] = 1;
-  }
+  // ---- candidates and their keys, and the range of the score keys
   int need = k;                             // still to take among the alive candidates
-  // the bytes every score key shares need no pass: start at the first byte
-  // where the smallest and largest keys differ
   {
     unsigned long long mn = ~0ull, mx = 0ull;
     for (int i = tid; i < n; i += kUpdThreads) {
-      mn = key[i] < mn ? key[i] : mn;
-      mx = key[i] > mx ? key[i] : mx;
+      const int64_t p = i < k ? static_cast<int64_t>(ui[i]) : P.p0 + (i - k);
+      const unsigned long long kv = order_key(P.scores[unit * P.stride + p]);
+      pos[i] = static_cast<int32_t>(p);
+      key[i] = kv;
+      taken[i] = 0;
+      alive[i] = 1;
+      mn = kv < mn ? kv : mn;
+      mx = kv > mx ? kv : mx;
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -117,22 +125,27 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
         mn = red_mn[w] < mn ? red_mn[w] : mn;
         mx = red_mx[w] > mx ? red_mx[w] : mx;
       }
-      const unsigned long long x = mn ^ mx;
-      first_digit = x ? __clzll(static_cast<long long>(x)) / 8 : 8;    // all keys equal: positions only
+      const unsigned long long x = mx - mn;
+      key_min = mn;
+      key_bits = 32 + (x ? 64 - __clzll(static_cast<long long>(x)) : 0);   // width of the rank keys
       n_alive = n;
-      n_list = -1;                                                       // no pass has listed survivors
+      n_list = -1;                                                           // no pass has listed survivors
     }
     __syncthreads();
   }
+  const unsigned long long kmin = key_min;
 
-  // ---- radix select of the k best, most significant byte first: each pass
-  // counts the alive candidates per digit, finds the digit b* at which the
-  // count from the top reaches `need`, takes the alive candidates above it
-  // and keeps those equal to it alive (listing them). When the digit's whole
-  // bucket is needed the selection is complete; when at most 64 candidates
-  // are left alive one wave ranks them directly.
-  for (int d = first_digit; d < 12 && need > 0 && n_alive > 64; ++d) {
-    if (tid < 256) hist[tid] = 0;
+  // ---- radix select of the k best, most significant 12 bits first: each
+  // pass counts the alive candidates per digit, finds the digit b* at which
+  // the count from the top reaches `need`, takes the alive candidates above
+  // it and keeps those equal to it alive (listing them). When the digit's
+  // whole bucket is needed the selection is complete; when at most 64
+  // candidates are left alive one wave ranks them directly.
+  for (int top = key_bits; top > 0 && need > 0 && n_alive > 64;) {
+    const int w = top < kDigitBits ? top : kDigitBits;
+    const int sh = top - w;
+    top = sh;
+    for (int b = tid; b < kBins; b += kUpdThreads) hist[b] = 0;
     if (tid == 0) n_list = 0;
     __syncthreads();
     // skewed scores put many candidates in one bin: the lanes of a wave
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     for (int i0 = 0; i0 < n; i0 += kUpdThreads) {
       const int i = i0 + tid;
       const bool act = i < n && alive[i];
-      const int dg = act ? static_cast<int>(rank_digit(key[i], pos[i], d)) : -1;
+      const int dg = act ? static_cast<int>(rank_bits(key[i] - kmin, pos[i], sh, w)) : -1;
       const unsigned long long am = __ballot(act);
       if (am) {
         const int lead = __ffsll(static_cast<long long>(am)) - 1;
@@ -152,12 +165,14 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     }
     __syncthreads();
     if (tid < 64) {
-      // lane l holds the bins 255 - 4l .. 252 - 4l (descending)
-      int c[4], tot = 0;
+      // lane l holds the 64 bins kBins - 1 - 64 l down to kBins - 64 (l + 1)
+      constexpr int kPerLane = kBins / 64;
+      const int hi_bin = kBins - 1 - kPerLane * lane;
+      int tot = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - (4 * lane + j)];
-        tot += c[j];
+      for (int j = 0; j < kPerLane; j += 4) {
+        const int4 c4 = *reinterpret_cast<const int4 *>(&hist[hi_bin - j - 3]);
+        tot += c4.x + c4.y + c4.z + c4.w;
       }
       int incl = tot;
 #pragma unroll
@@ -167,15 +182,15 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
       }
       int cum = incl - tot;                 // alive candidates in the bins above this lane's
       if (cum < need && need <= incl) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (cum + c[j] >= need) {
-            sel_digit = 255 - (4 * lane + j);
+        for (int j = 0; j < kPerLane; ++j) {
+          const int c = hist[hi_bin - j];
+          if (cum + c >= need) {
+            sel_digit = hi_bin - j;
             sel_need = need - cum;
-            sel_count = c[j];
+            sel_count = c;
             break;
           }
-          cum += c[j];
+          cum += c;
         }
       }
     }
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     const bool whole = sel_need == sel_count;   // the bucket is needed entirely
     for (int i = tid; i < n; i += kUpdThreads) {
       if (!alive[i]) continue;
-      const uint32_t dg = rank_digit(key[i], pos[i], d);
+      const uint32_t dg = rank_bits(key[i] - kmin, pos[i], sh, w);
       if (dg > bstar || (dg == bstar && whole)) {
         taken[i] = 1;
         alive[i] = 0;
