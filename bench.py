@@ -6,11 +6,12 @@ of W + 64 rows, everything else INT4):
   1. hq_decode_step: attention over INT4 + VL + window with the split-K LSE
      merge; in the same launches the step's queries go into the detector's
      64-slot ring and the window's oldest token is packed into INT4;
-  2. every 64th step a re-detection: column scores of every position from
-     the INT4 keys and the 64 accumulated steps (hq_detect_vlines_cache),
-     then hq_vl_update re-chooses the VL set among the current one and the
-     ring rows behind the window. It is timed on its own and 1/64 of it is
-     added to the step time, so that any --steps includes its share.
+  2. every 64th step a re-detection (hq_vl_redetect, two launches): the 64
+     accumulated steps' summed queries, the column scores of the candidates
+     (the current VL set and the ring rows behind the window, the only
+     positions that can enter the set) from their INT4 keys, and the new VL
+     set written in place. It is timed on its own and 1/64 of it is added to
+     the step time, so that any --steps includes its share.
 The decode steps rotate over `--copies` independent layer caches (>= 1 GB of
 decode-read bytes in total) so that the 256 MB Infinity Cache cannot hold
 the working set: every step reads its cache from HBM as it would in a model
@@ -178,11 +179,12 @@ def main_decode(args, torch, hq, synth):
     # the step's upkeep: the window's oldest row read and packed, q into the ring
     evict_bytes = 2 * units * (D * hp + D // 2 + (D // 32) * 4)
     acc_bytes = 2 * B * Hq * D * hp
-    # a re-detection: summed ring queries, the INT4 key codes and scales of
-    # [0, T - W), the candidates' scores, and the VL rows rewritten (old
-    # rows and ring rows read, new rows written, K and V)
-    det_bytes = (B * Hq * R * D * hp + units * nq * (D // 2 + (D // 32) * 4) + units * nq * 8
-                 + units * (k + R) * 8 + units * (2 * k + R) * 2 * D * hp + units * (k + k) * 4)
+    # a re-detection (hq_vl_redetect): the query ring, the INT4 key codes
+    # and scales of the k + R candidates, the VL index list read, and at most
+    # R promoted rows per head copied from the ring into freed slots (K and V
+    # read and written) with their index entries
+    det_bytes = (B * Hq * R * D * hp + units * (k + R) * (D // 2 + (D // 32) * 4) + units * k * 4
+                 + units * R * 2 * 2 * D * hp + units * R * 4)
 
     t_setup = time.time()
     copies = args.copies or max(1, int(np.ceil(1.05e9 / dec_bytes)))
@@ -321,7 +323,10 @@ def main_decode(args, torch, hq, synth):
     mm_us = detector_matmul_us(torch, hq, w, K0, caches[0].q_acc, args.detect_method, dev, stream)
     del K0
 
-    det_share_us = (det_us_in_cycle if det_us_in_cycle is not None else det_us) / R
+    # the share charged to a step: the re-detection timed alone (a graph of
+    # back-to-back re-detections); the in-cycle difference of two ~1 ms
+    # replays is reported beside it but is too noisy to charge
+    det_share_us = det_us / R
     us_per_step = step_us + det_share_us
     step_bytes = dec_bytes + evict_bytes + acc_bytes + det_bytes / R
     value = step_bytes / (us_per_step * 1e-6) / 1e9
@@ -372,9 +377,7 @@ def main_decode(args, torch, hq, synth):
         "ms_per_step": round(us_per_step * 1e-3, 6),
         "us_per_step": round(us_per_step, 3),
         "us_per_step_parts": {"decode_step": round(step_us, 3), "redetection_share": round(det_share_us, 3),
-                              "redetection_share_from": ("a 64-step cycle with its re-detection minus one "
-                                                         "without, over 64" if det_us_in_cycle is not None
-                                                         else "the re-detection timed alone, over 64")},
+                              "redetection_share_from": "the re-detection timed alone (graph replay), over 64"},
         "host_enqueue_us_per_step": round(host_us_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
@@ -395,8 +398,7 @@ def main_decode(args, torch, hq, synth):
                           "captured in one HIP graph, its replay timed with HIP events" if args.graph else
                           "exactly `steps` decode steps (hq_decode_step: attention + the step's upkeep) "
                           "launched on the stream") +
-                         ", plus 1/64 of a re-detection timed separately (hq_detect_vlines_cache scores + "
-                         "hq_vl_update)"),
+                         ", plus 1/64 of a re-detection timed separately (hq_vl_redetect)"),
             "layer_resident_bytes": int(resident),
             "layer_resident_vs_k4v4": round(resident / (units * nq * 2 * (D // 2 + (D // 32) * 4)) - 1.0, 4),
         },
@@ -428,7 +430,8 @@ def main_decode(args, torch, hq, synth):
             "us_per_redetection_stream_launched": round(det_us_launched, 2),
             "us_per_redetection_in_64_step_cycle": (round(det_us_in_cycle, 2) if det_us_in_cycle is not None
                                                     else None),
-            "redetection": "scores from the INT4 keys (hq_detect_vlines_cache, k_top 0) + hq_vl_update",
+            "redetection": ("hq_vl_redetect: summed ring queries and the candidates' scores from their INT4 "
+                            "keys (many workgroups per head), then the in-place update (one workgroup per head)"),
             "redetection_bytes": int(det_bytes),
             "overhead_vs_64_decode_steps": round(det_share_us / step_us, 4),
             "matmul_us_per_detection": round(mm_us, 2),

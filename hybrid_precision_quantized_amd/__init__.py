@@ -99,6 +99,10 @@ _SIGS = {
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_vl_update": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                     ctypes.c_int64, ctypes.c_void_p]),
+    "hq_vl_redetect": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]),
+    "hq_vl_redetect_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HybridKV)]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "hq_stream_read_sink_bytes": (ctypes.c_size_t, []),
     "hq_decode_auto_splits": (ctypes.c_int, [ctypes.POINTER(HybridKV), ctypes.c_int]),
@@ -287,6 +291,19 @@ def hq_vl_update(kv: HybridKV, vl_idx, p0, scores, score_stride, stream=None):
     include/hq.h)."""
     _check(lib().hq_vl_update(ctypes.byref(kv), _ptr(vl_idx), int(p0), _ptr(scores), int(score_stride),
                               _stream(stream)))
+
+
+def hq_vl_redetect_workspace_size(kv: HybridKV) -> int:
+    return int(lib().hq_vl_redetect_workspace_size(ctypes.byref(kv)))
+
+
+def hq_vl_redetect(kv: HybridKV, vl_idx, p0, q_acc, Hq, R, ws, stream=None):
+    """A whole re-detection: the summed query ring, the column scores of the
+    candidates only (current VL set and [p0, T - W)) from the INT4 keys, and
+    the update of hq_vl_update (see include/hq.h)."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hq_vl_redetect(ctypes.byref(kv), _ptr(vl_idx), int(p0), _ptr(q_acc), _dt(q_acc), int(Hq), int(R),
+                                _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def hq_stream_read(buf, sink, stream=None):

@@ -10,7 +10,7 @@ import torch
 
 from . import (HQ_BF16, HQ_F16, HQ_F32, HQ_LAYOUT_ROWS, HQ_LAYOUT_TILE16, HybridKV, hq_decode_step,
                hq_detect_vlines_cache, hq_detect_workspace_size, hq_gather_rows, hq_quantize_kv,
-               hq_vl_bitmap, hq_vl_update)
+               hq_vl_bitmap, hq_vl_redetect, hq_vl_redetect_workspace_size, hq_vl_update)
 
 _HP = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: HQ_F16}
 
@@ -145,6 +145,7 @@ class RollingCache(HybridCache):
         self.q_acc = torch.zeros((B, Hq, R, D), dtype=hp_dtype, device=dev)
         self.scores = torch.zeros((B, Hkv, self.t_cap), dtype=torch.int64, device=dev)
         self.det_ws = torch.zeros(hq_detect_workspace_size(B, Hkv, self.t_cap, 0), dtype=torch.uint8, device=dev)
+        self.redet_ws = torch.zeros(hq_vl_redetect_workspace_size(self.descriptor()), dtype=torch.uint8, device=dev)
 
     def decode_step(self, q, out, lse, ws, n_splits=0, stream=None):
         """Attention of this step's queries over [0, T); q goes into ring slot
@@ -168,16 +169,22 @@ class RollingCache(HybridCache):
         """True after the step that fills the detector ring's last slot."""
         return self.step_no > 0 and (self.step_no - 1) % self.R == self.R - 1
 
-    def redetect(self, stream=None):
-        """Scores of every position from the INT4 keys and the R accumulated
-        steps, then the new VL set among the current one and the positions
-        that left the window since the last update."""
+    def redetect(self, stream=None, fused=True):
+        """The new VL set among the current one and the positions that left
+        the window since the last update, by their column scores from the
+        INT4 keys and the R accumulated steps: the candidates' scores only,
+        then the update (hq_vl_redetect), or, with fused=False, the detector's
+        scores of every position (hq_detect_vlines_cache) then
+        hq_vl_update."""
         cand_end = self.T - self.W
         kv = self.descriptor()
-        sc = self.scores.view(-1)[:self.B * self.Hkv * cand_end]
-        hq_detect_vlines_cache(None, self.q_acc, self.Hq, self.R, max(self.step_no - 1, 0), True, kv, cand_end, 0,
-                               None, sc, self.det_ws, stream=stream)
-        hq_vl_update(kv, self.vl_idx, self.p0, sc, cand_end, stream=stream)
+        if fused:
+            hq_vl_redetect(kv, self.vl_idx, self.p0, self.q_acc, self.Hq, self.R, self.redet_ws, stream=stream)
+        else:
+            sc = self.scores.view(-1)[:self.B * self.Hkv * cand_end]
+            hq_detect_vlines_cache(None, self.q_acc, self.Hq, self.R, max(self.step_no - 1, 0), True, kv, cand_end,
+                                   0, None, sc, self.det_ws, stream=stream)
+            hq_vl_update(kv, self.vl_idx, self.p0, sc, cand_end, stream=stream)
         self.p0 = cand_end
 
     def resident_bytes(self) -> int:

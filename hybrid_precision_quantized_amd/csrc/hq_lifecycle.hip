@@ -35,6 +35,16 @@
 //    integer atomics (bits of dropped positions cleared, of promoted ones
 //    set). The rows are a set for the attention: their order is irrelevant
 //    to it, and the slot rule makes it deterministic.
+//  * hq_vl_redetect scores only the candidates, the only positions the
+//    update can choose (about k + 64 key rows per head instead of all
+//    T - W), in a kernel of its own with many workgroups per head: each sums
+//    the unit's query ring (fp64, in LDS) and scores 256 candidates per round
+//    (D = 128; 512 at D = 64; up to 8 rounds) from their INT4 key rows, in the INT4-key GEMV's
+//    arithmetic (per 32-channel group s sum_e q_e c_e + z sum_e q_e in fp64,
+//    the groups added by butterfly, rounded once to units of 2^-16), into a
+//    workspace indexed by candidate; the update kernel then reads them by
+//    candidate instead of by position. Scoring in the single update
+//    workgroup of each head made that workgroup's vector unit the bound.
 #include "hq_common.h"
 
 namespace hq {
@@ -46,7 +56,13 @@ constexpr int kMaxMoved = 1024;   // positions that may leave the window between
 
 struct UpdParams {
   int32_t *idx;                  // [units][k] in/out: position of each VL slot
-  const int64_t *scores;         // [units][stride]
+  const int64_t *scores;         // [units][stride], by position, or by candidate when by_cand
+  int64_t *cand_scores;          // scoring kernel: out [units][k + nq - p0]
+  const void *q_acc;             // scoring kernel: query ring [B][Hq][R][D]
+  const uint8_t *k_codes;        //   INT4 key rows [units][t_cap][D / 2]
+  const uint32_t *k_sz;          //   fp16 {s, z} words [units][t_cap][D / 32]
+  int64_t t_cap;
+  int Hq, Hkv, R, by_cand;
   uint8_t *vl_k, *vl_v;          // [units][k][row_bytes] in/out
   const uint8_t *ring_k, *ring_v;// [units][C][row_bytes]
   uint32_t *bits;                // [units][words]
@@ -71,6 +87,142 @@ __device__ __forceinline__ uint32_t rank_bits(unsigned long long hi, int32_t pos
   if (sh >= 32) return static_cast<uint32_t>(hi >> (sh - 32)) & mask;
   if (sh + w <= 32) return (lo >> sh) & mask;
   return static_cast<uint32_t>((static_cast<unsigned long long>(lo) >> sh) | (hi << (32 - sh))) & mask;
+}
+
+template <int DT>
+__device__ __forceinline__ float ring_half(uint32_t h) {
+  if constexpr (DT == HQ_BF16) return bf16_to_f32(h);
+  else return f16_to_f32(h);
+}
+
+// Candidate scores of a re-detection: block (unit, c) scores candidates
+// [c RPB CPR, (c + 1) RPB CPR) of the unit (the VL list, then [p0, T - W)),
+// CPR per round, RPB = rounds rounds (<= kMaxRounds; more rounds per block
+// when there are many heads, so that fewer blocks read each query ring).
+// Lane (candidate, 32-channel group g) reads the candidate's position and
+// issues the loads of its key codes and {s, z} word for every round first;
+// then the block sums the unit's query ring (thread (row group, 8-channel
+// slice) adds its rows, the lanes of a wave sharing a slice combine by
+// butterfly, the waves' sums meet in LDS in wave order), and each lane adds
+// its group terms.
+constexpr int kMaxRounds = 8;
+template <int DT, int D>
+__global__ __launch_bounds__(kUpdThreads) void redetect_scores_kernel(UpdParams P, int rounds) {
+  constexpr int NG = D / 32, CPR = kUpdThreads / NG;     // candidates per round
+  __shared__ double part[kUpdThreads / 64][D];
+  __shared__ double qsh[D];
+  const int k = P.k;
+  const int n = k + static_cast<int>(P.nq - P.p0);
+  const int cpb = CPR * rounds;
+  const int nb = (n + cpb - 1) / cpb;
+  const int64_t unit = blockIdx.x / nb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = tid % NG;
+  const int i0 = static_cast<int>(blockIdx.x % nb) * cpb + tid / NG;
+  uint4 cw[kMaxRounds];
+  uint32_t cz[kMaxRounds];
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    const int i = i0 + CPR * r;
+    cw[r] = make_uint4(0u, 0u, 0u, 0u);
+    cz[r] = 0u;
+    if (r < rounds && i < n) {
+      const int32_t p = i < k ? P.idx[unit * k + i] : static_cast<int32_t>(P.p0 + (i - k));
+      const int64_t row = unit * P.t_cap + p;
+      cw[r] = *reinterpret_cast<const uint4 *>(P.k_codes + row * (D / 2) + g * 16);
+      cz[r] = P.k_sz[row * NG + g];
+    }
+  }
+  {
+    constexpr int LPR = D / 8, RG = kUpdThreads / LPR;
+    constexpr int kRing = DT == HQ_F32 ? 4 : 8;
+    const int G = P.Hq / P.Hkv;
+    const int M = G * P.R;
+    const int64_t b = unit / P.Hkv, h = unit % P.Hkv;
+    const int sub = tid % LPR, rg = tid / LPR;
+    const int64_t base = (b * P.Hq + h * G) * P.R * D + sub * 8;
+    double sq[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int r0 = rg; r0 < M; r0 += RG * kRing) {
+      if constexpr (DT == HQ_F32) {
+        float4 x[kRing][2];
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          const int r = r0 + RG * j;
+          if (r < M) {
+            const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(P.q_acc) + base +
+                                                               static_cast<int64_t>(r) * D);
+            x[j][0] = q[0];
+            x[j][1] = q[1];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          if (r0 + RG * j < M) {
+            const float v[8] = {x[j][0].x, x[j][0].y, x[j][0].z, x[j][0].w, x[j][1].x, x[j][1].y, x[j][1].z, x[j][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq[e] += static_cast<double>(v[e]);
+          }
+        }
+      } else {
+        uint4 u[kRing];
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          const int r = r0 + RG * j;
+          if (r < M)
+            u[j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(P.q_acc) + base +
+                                                    static_cast<int64_t>(r) * D);
+        }
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          if (r0 + RG * j < M) {
+            const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sq[2 * e] += static_cast<double>(ring_half<DT>(w[e] & 0xFFFFu));
+              sq[2 * e + 1] += static_cast<double>(ring_half<DT>(w[e] >> 16));
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq[e] += __shfl_xor(sq[e], m, 64);
+    if (lane < LPR)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[tid >> 6][sub * 8 + e] = sq[e];
+    __syncthreads();
+    if (tid < D) {
+      double t = 0.0;
+      for (int w = 0; w < kUpdThreads / 64; ++w) t += part[w][tid];
+      qsh[tid] = t;
+    }
+    __syncthreads();
+  }
+  double qv[32];
+  double qsum = 0.0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    qv[e] = qsh[g * 32 + e];
+    qsum += qv[e];
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    if (r >= rounds) break;                 // uniform
+    const int i = i0 + CPR * r;
+    const uint32_t word[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) acc = fma(qv[e], static_cast<double>((word[e >> 3] >> (4 * (e & 7))) & 0xFu), acc);
+    const double sc = static_cast<double>(f16_to_f32(cz[r] & 0xFFFFu));
+    const double z = static_cast<double>(f16_to_f32(cz[r] >> 16));
+    double part_g = fma(sc, acc, z * qsum);
+#pragma unroll
+    for (int m = 1; m < NG; m <<= 1) part_g += __shfl_xor(part_g, m, 64);
+    if (i < n && g == 0) P.cand_scores[unit * n + i] = __double2ll_rn(part_g * 65536.0);
+  }
 }
 
 __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
@@ -101,7 +253,7 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     unsigned long long mn = ~0ull, mx = 0ull;
     for (int i = tid; i < n; i += kUpdThreads) {
       const int64_t p = i < k ? static_cast<int64_t>(ui[i]) : P.p0 + (i - k);
-      const unsigned long long kv = order_key(P.scores[unit * P.stride + p]);
+      const unsigned long long kv = order_key(P.scores[unit * P.stride + (P.by_cand ? i : p)]);
       pos[i] = static_cast<int32_t>(p);
       key[i] = kv;
       taken[i] = 0;
@@ -180,18 +332,25 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
         const int v = __shfl_up(incl, off, 64);
         if (lane >= off) incl += v;
       }
-      int cum = incl - tot;                 // alive candidates in the bins above this lane's
-      if (cum < need && need <= incl) {
-        for (int j = 0; j < kPerLane; ++j) {
-          const int c = hist[hi_bin - j];
-          if (cum + c >= need) {
-            sel_digit = hi_bin - j;
-            sel_need = need - cum;
-            sel_count = c;
-            break;
-          }
-          cum += c;
-        }
+      // the lane whose bins reach `need`, then its 64 bins one per lane
+      const int cum = incl - tot;           // alive candidates in the bins above this lane's
+      const unsigned long long hit = __ballot(cum < need && need <= incl);
+      const int L = __ffsll(static_cast<long long>(hit)) - 1;           // exists: the bins hold >= need
+      const int cum_l = __shfl(cum, L, 64);
+      static_assert(kPerLane == 64, "one bin per lane in the second level");
+      const int bin = kBins - 1 - kPerLane * L - lane;
+      const int c = hist[bin];
+      int ci = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(ci, off, 64);
+        if (lane >= off) ci += v;
+      }
+      const int before = cum_l + ci - c;    // alive candidates in the bins above this one
+      if (before < need && need <= before + c) {
+        sel_digit = bin;
+        sel_need = need - before;
+        sel_count = c;
       }
     }
     __syncthreads();
@@ -314,63 +473,147 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
 
 using namespace hq;
 
-extern "C" hq_status hq_vl_update(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, const int64_t *scores,
-                                  int64_t score_stride, void *stream) {
-  if (!kv) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: null descriptor");
-  if (kv->B < 1 || kv->Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: B, Hkv must be >= 1");
-  if (kv->D != 64 && kv->D != 128) return fail(HQ_ERR_UNSUPPORTED, "hq_vl_update: D must be 64 or 128");
-  if (!dtype_ok(kv->hp_dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: bad dtype");
+namespace hq {
+namespace {
+
+// Checks shared by hq_vl_update and hq_vl_redetect; fills the common fields.
+// Returns HQ_OK with *noop set when there is nothing to change.
+hq_status prepare_update(const char *name, const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, UpdParams &P,
+                         bool &noop) {
+  noop = false;
+  if (!kv) return fail(HQ_ERR_INVALID_ARG, "%s: null descriptor", name);
+  if (kv->B < 1 || kv->Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "%s: B, Hkv must be >= 1", name);
+  if (kv->D != 64 && kv->D != 128) return fail(HQ_ERR_UNSUPPORTED, "%s: D must be 64 or 128", name);
+  if (!dtype_ok(kv->hp_dtype)) return fail(HQ_ERR_INVALID_ARG, "%s: bad dtype", name);
   if (kv->T < 1 || kv->W < 0 || kv->W > kv->T || kv->k < 0 || kv->k > kv->T - kv->W)
-    return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: need 0 <= W <= T and 0 <= k <= T - W");
+    return fail(HQ_ERR_INVALID_ARG, "%s: need 0 <= W <= T and 0 <= k <= T - W", name);
   const int64_t C = kv->win_cap > 0 ? kv->win_cap : kv->W;
-  if (C < kv->W) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: win_cap must be 0 or >= W");
+  if (C < kv->W) return fail(HQ_ERR_INVALID_ARG, "%s: win_cap must be 0 or >= W", name);
   if (kv->W > 0 && (kv->win_offset < 0 || kv->win_offset >= C))
-    return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: win_offset out of range");
+    return fail(HQ_ERR_INVALID_ARG, "%s: win_offset out of range", name);
   const int64_t nq = kv->T - kv->W;
   if (p0 > nq || p0 < 0 || p0 < kv->T - C)
     return fail(HQ_ERR_INVALID_ARG,
-                "hq_vl_update: p0 = %lld must lie in [max(0, T - win_cap), T - W] = [%lld, %lld]: only "
+                "%s: p0 = %lld must lie in [max(0, T - win_cap), T - W] = [%lld, %lld]: only "
                 "positions whose 16-bit rows are still in the ring can be promoted",
-                static_cast<long long>(p0), static_cast<long long>(kv->T - C > 0 ? kv->T - C : 0),
+                name, static_cast<long long>(p0), static_cast<long long>(kv->T - C > 0 ? kv->T - C : 0),
                 static_cast<long long>(nq));
   const int64_t n = kv->k + (nq - p0);
   if (nq - p0 > kMaxMoved)
-    return fail(HQ_ERR_UNSUPPORTED, "hq_vl_update: %lld positions left the window since p0, more than %d",
+    return fail(HQ_ERR_UNSUPPORTED, "%s: %lld positions left the window since p0, more than %d", name,
                 static_cast<long long>(nq - p0), kMaxMoved);
   if (n > kMaxCand)
-    return fail(HQ_ERR_UNSUPPORTED, "hq_vl_update: %lld candidates per head exceed %d", static_cast<long long>(n),
+    return fail(HQ_ERR_UNSUPPORTED, "%s: %lld candidates per head exceed %d", name, static_cast<long long>(n),
                 kMaxCand);
   if (kv->t_cap < nq || kv->t_cap % 32 != 0)
-    return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: t_cap must be >= T - W and a multiple of 32");
-  if (score_stride < nq) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: score_stride < T - W");
-  if (kv->k == 0 || nq == p0) { clear_error(); return HQ_OK; }    // nothing to choose from or to change
+    return fail(HQ_ERR_INVALID_ARG, "%s: t_cap must be >= T - W and a multiple of 32", name);
+  if (kv->k == 0 || nq == p0) { noop = true; return HQ_OK; }      // nothing to choose from or to change
   const int64_t units = static_cast<int64_t>(kv->B) * kv->Hkv;
-  const int row_bytes = kv->D * dtype_bytes(kv->hp_dtype);
-  if (!scores || !vl_idx || !kv->vl_bits || !kv->vl_k || !kv->vl_v || !kv->win_k || !kv->win_v)
-    return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: null pointer");
+  if (!vl_idx || !kv->vl_bits || !kv->vl_k || !kv->vl_v || !kv->win_k || !kv->win_v)
+    return fail(HQ_ERR_INVALID_ARG, "%s: null pointer", name);
   const uintptr_t al = reinterpret_cast<uintptr_t>(kv->vl_k) | reinterpret_cast<uintptr_t>(kv->vl_v) |
                        reinterpret_cast<uintptr_t>(kv->win_k) | reinterpret_cast<uintptr_t>(kv->win_v);
-  if (al % 16 || reinterpret_cast<uintptr_t>(kv->vl_bits) % 4 || reinterpret_cast<uintptr_t>(scores) % 8 ||
-      reinterpret_cast<uintptr_t>(vl_idx) % 4)
-    return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: misaligned buffer (rows 16 bytes, words 4, scores 8)");
-  if (units > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_vl_update: too many heads");
-  UpdParams P{};
+  if (al % 16 || reinterpret_cast<uintptr_t>(kv->vl_bits) % 4 || reinterpret_cast<uintptr_t>(vl_idx) % 4)
+    return fail(HQ_ERR_INVALID_ARG, "%s: misaligned buffer (rows 16 bytes, words and indices 4)", name);
+  if (units > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "%s: too many heads", name);
+  P = UpdParams{};
   P.idx = vl_idx;
-  P.scores = scores;
   P.vl_k = static_cast<uint8_t *>(const_cast<void *>(kv->vl_k));
   P.vl_v = static_cast<uint8_t *>(const_cast<void *>(kv->vl_v));
   P.ring_k = static_cast<const uint8_t *>(kv->win_k);
   P.ring_v = static_cast<const uint8_t *>(kv->win_v);
   P.bits = const_cast<uint32_t *>(kv->vl_bits);
-  P.stride = score_stride;
   P.words = kv->t_cap / 32;
   P.p0 = p0;
   P.nq = nq;
   P.k = kv->k;
   P.C = static_cast<int>(C);
   P.win_offset = kv->win_offset;
-  P.row_bytes = row_bytes;
-  hipLaunchKernelGGL(vl_update_kernel, dim3(static_cast<unsigned>(units)), dim3(kUpdThreads), 0,
-                     as_stream(stream), P);
+  P.row_bytes = kv->D * dtype_bytes(kv->hp_dtype);
+  P.t_cap = kv->t_cap;
+  P.Hkv = kv->Hkv;
+  return HQ_OK;
+}
+
+}  // namespace
+}  // namespace hq
+
+extern "C" hq_status hq_vl_update(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, const int64_t *scores,
+                                  int64_t score_stride, void *stream) {
+  UpdParams P;
+  bool noop;
+  hq_status s = prepare_update("hq_vl_update", kv, vl_idx, p0, P, noop);
+  if (s != HQ_OK) return s;
+  if (score_stride < kv->T - kv->W) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: score_stride < T - W");
+  if (noop) { clear_error(); return HQ_OK; }
+  if (!scores) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: null pointer");
+  if (reinterpret_cast<uintptr_t>(scores) % 8) return fail(HQ_ERR_INVALID_ARG, "hq_vl_update: misaligned scores");
+  P.scores = scores;
+  P.stride = score_stride;
+  const int64_t units = static_cast<int64_t>(kv->B) * kv->Hkv;
+  hipLaunchKernelGGL(vl_update_kernel, dim3(static_cast<unsigned>(units)), dim3(kUpdThreads), 0, as_stream(stream),
+                     P);
   return check_launch("hq_vl_update");
+}
+
+extern "C" size_t hq_vl_redetect_workspace_size(const hq_hybrid_kv *kv) {
+  if (!kv || kv->B < 1 || kv->Hkv < 1 || kv->k < 0) return 0;
+  return static_cast<size_t>(kv->B) * kv->Hkv * (static_cast<size_t>(kv->k) + kMaxMoved) * sizeof(int64_t);
+}
+
+extern "C" hq_status hq_vl_redetect(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, const void *q_acc,
+                                    hq_dtype q_dtype, int Hq, int R, void *ws, size_t ws_bytes, void *stream) {
+  UpdParams P;
+  bool noop;
+  hq_status s = prepare_update("hq_vl_redetect", kv, vl_idx, p0, P, noop);
+  if (s != HQ_OK) return s;
+  if (!dtype_ok(q_dtype)) return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: bad query dtype");
+  if (q_dtype != kv->hp_dtype)
+    return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: the query dtype must be the cache's 16-bit dtype");
+  if (Hq < 1 || Hq % kv->Hkv) return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: Hq must be a multiple of Hkv");
+  if (R < 1 || R > 1024) return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: need 1 <= R <= 1024");
+  if (noop) { clear_error(); return HQ_OK; }
+  if (!q_acc || !kv->k_codes || !kv->k_sz) return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: null pointer");
+  if (reinterpret_cast<uintptr_t>(q_acc) % 16 || reinterpret_cast<uintptr_t>(kv->k_codes) % 16 ||
+      reinterpret_cast<uintptr_t>(kv->k_sz) % 4)
+    return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: misaligned buffer (ring and codes 16 bytes, scales 4)");
+  const size_t need = hq_vl_redetect_workspace_size(kv);
+  if (!ws || ws_bytes < need)
+    return fail(HQ_ERR_WORKSPACE, "hq_vl_redetect: workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(HQ_ERR_INVALID_ARG, "hq_vl_redetect: misaligned workspace");
+  const int64_t units = static_cast<int64_t>(kv->B) * kv->Hkv;
+  const int64_t n = kv->k + (P.nq - p0);
+  // candidates per round of a scoring block; rounds per block so that the
+  // grid stays near 512 blocks (each block sums its head's query ring)
+  const int64_t cpr = kUpdThreads / (kv->D / 32);
+  const int64_t per_head = (n + cpr - 1) / cpr;
+  int64_t rounds = (units * per_head + 511) / 512;
+  rounds = rounds < 1 ? 1 : (rounds > kMaxRounds ? kMaxRounds : rounds);
+  const int64_t blocks = units * ((n + cpr * rounds - 1) / (cpr * rounds));
+  if (blocks > 0x7FFFFFFFLL) return fail(HQ_ERR_UNSUPPORTED, "hq_vl_redetect: too many heads");
+  P.q_acc = q_acc;
+  P.k_codes = static_cast<const uint8_t *>(kv->k_codes);
+  P.k_sz = reinterpret_cast<const uint32_t *>(kv->k_sz);
+  P.Hq = Hq;
+  P.R = R;
+  P.cand_scores = static_cast<int64_t *>(ws);
+  hipStream_t st = as_stream(stream);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kUpdThreads);
+  const int nr = static_cast<int>(rounds);
+#define HQ_RD(DT_)                                                                                      \
+  do {                                                                                                  \
+    if (kv->D == 128) hipLaunchKernelGGL((redetect_scores_kernel<DT_, 128>), grid, block, 0, st, P, nr); \
+    else hipLaunchKernelGGL((redetect_scores_kernel<DT_, 64>), grid, block, 0, st, P, nr);               \
+  } while (0)
+  if (q_dtype == HQ_F32) HQ_RD(HQ_F32);
+  else if (q_dtype == HQ_BF16) HQ_RD(HQ_BF16);
+  else HQ_RD(HQ_F16);
+#undef HQ_RD
+  s = check_launch("hq_vl_redetect (scores)");
+  if (s != HQ_OK) return s;
+  P.scores = P.cand_scores;
+  P.stride = n;
+  P.by_cand = 1;
+  hipLaunchKernelGGL(vl_update_kernel, dim3(static_cast<unsigned>(units)), block, 0, st, P);
+  return check_launch("hq_vl_redetect");
 }

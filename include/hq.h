@@ -407,6 +407,33 @@ hq_status hq_vl_update(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, cons
                        int64_t score_stride, void *stream);
 
 /*
+ * hq_vl_redetect -- a whole re-detection of a rolling hybrid cache [WPN, body
+ * paragraph 4; AFS, How It Works, items 1-2]: the same result as
+ * hq_detect_vlines_cache(NULL, q_acc, q_dtype, Hq, R, 0, 1, kv, T - W, 0,
+ * NULL, scores, ...) followed by hq_vl_update(kv, vl_idx, p0, scores, T - W),
+ * bit for bit where those scores are exact (queries on the 2^-4 grid), but
+ * only the candidates are scored: the current VL positions and [p0, T - W),
+ * the only positions the update can choose, about k + 64 key rows per head
+ * instead of T - W. Per (b, h): the summed query of every ring row of the
+ * group's heads (q_acc [B][Hq][R][D], q_dtype == kv->hp_dtype; fp64), each
+ * candidate's column score from its INT4 key row (per 32-channel group
+ * s sum_e q_e c_e + z sum_e q_e, fp64, rounded once to int64 units of
+ * 2^-16), then the update of hq_vl_update. Two launches on `stream`.
+ * ws: at least hq_vl_redetect_workspace_size(kv) bytes, 8-byte aligned, no
+ * initialisation (the candidates' scores). Requirements and errors as
+ * hq_vl_update, plus Hq a multiple of kv->Hkv, 1 <= R <= 1024, the ring and
+ * the key codes 16-byte aligned, the scale planes 4-byte aligned
+ * (HQ_ERR_INVALID_ARG), HQ_ERR_WORKSPACE for a short workspace. Nothing
+ * enqueued on error.
+ */
+hq_status hq_vl_redetect(const hq_hybrid_kv *kv, int32_t *vl_idx, int64_t p0, const void *q_acc,
+                         hq_dtype q_dtype, int Hq, int R, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes hq_vl_redetect needs for this cache: B Hkv (k + 1024)
+ * int64 (0 for a null or malformed descriptor). */
+size_t hq_vl_redetect_workspace_size(const hq_hybrid_kv *kv);
+
+/*
  * hq_prefill_attn -- causal hybrid-precision prefill attention [AFS, The
  * Technical Mechanics, Prefill Stage: the quantized majority is handled first
  * and the 16-bit vertical lines and local window are overlaid into the

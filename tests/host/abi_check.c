@@ -153,6 +153,16 @@ int main(void) {
   bad |= expect("vl update stride", hq_vl_update(&kv, FAKE, 872, FAKE, 871, NULL), HQ_ERR_INVALID_ARG);
   bad |= expect("vl update no-op", hq_vl_update(&kv, FAKE, 872, FAKE, 872, NULL), HQ_OK);
 
+  bad |= expect("vl redetect null kv", hq_vl_redetect(NULL, FAKE, 800, FAKE, HQ_BF16, 8, 64, FAKE, big, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl redetect p0 past T - W", hq_vl_redetect(&kv, FAKE, 873, FAKE, HQ_BF16, 8, 64, FAKE, big, NULL),
+                HQ_ERR_INVALID_ARG);
+  bad |= expect("vl redetect R", hq_vl_redetect(&kv, FAKE, 872, FAKE, HQ_BF16, 8, 0, FAKE, big, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl redetect dtype", hq_vl_redetect(&kv, FAKE, 872, FAKE, HQ_F16, 8, 64, FAKE, big, NULL), HQ_ERR_INVALID_ARG);
+  bad |= expect("vl redetect workspace size", hq_vl_redetect_workspace_size(&kv) == 2 * (40 + 1024) * 8 ? HQ_OK
+                                                                                                  : HQ_ERR_INVALID_ARG,
+                HQ_OK);
+  bad |= expect("vl redetect no-op", hq_vl_redetect(&kv, FAKE, 872, FAKE, HQ_BF16, 8, 64, FAKE, big, NULL), HQ_OK);
+
   /* allocation-free decode: rejected before any device is touched */
   bad |= expect("noalloc null kv", hq_decode_attn_noalloc(FAKE, HQ_BF16, 8, NULL, 0.f, 0, FAKE, NULL, NULL),
                 HQ_ERR_INVALID_ARG);

@@ -246,6 +246,52 @@ def test_prefill_rejects(entry):
     assert entry in hq.hq_last_error()
 
 
+def test_vl_update_and_redetect_reject():
+    """Both in-place VL updates reject what they cannot do before launching
+    anything: p0 outside [max(0, T - win_cap), T - W] (rows no longer in the
+    ring), too many recent positions or candidates, a bad head dim, the
+    fused form's query arguments; p0 == T - W is a no-op."""
+    L = hq.lib()
+    ok = dict(kv=_kv(win_cap=192), idx=FAKE, p0=808, sc=FAKE, stride=872, q=FAKE, qdt=hq.HQ_BF16, Hq=8, R=64,
+              ws=FAKE, wsb=1 << 30)
+
+    def upd(**o):
+        a = dict(ok, **o)
+        kv = a["kv"]
+        return L.hq_vl_update(ctypes.byref(kv) if kv is not None else None, a["idx"], a["p0"], a["sc"],
+                              a["stride"], None)
+
+    def red(**o):
+        a = dict(ok, **o)
+        kv = a["kv"]
+        return L.hq_vl_redetect(ctypes.byref(kv) if kv is not None else None, a["idx"], a["p0"], a["q"], a["qdt"],
+                                a["Hq"], a["R"], a["ws"], a["wsb"], None)
+    for call in (upd, red):
+        assert call(kv=None) == hq.HQ_ERR_INVALID_ARG
+        assert call(p0=873) == hq.HQ_ERR_INVALID_ARG                  # past T - W
+        assert call(p0=807) == hq.HQ_ERR_INVALID_ARG                  # its row left the ring
+        assert call(kv=_kv(win_cap=192, D=96)) == hq.HQ_ERR_UNSUPPORTED
+        assert call(kv=_kv(T=3000, t_cap=2880, win_cap=3000), p0=100, stride=2872) == hq.HQ_ERR_UNSUPPORTED
+        assert call(kv=_kv(T=10000, t_cap=9888, k=8200, win_cap=192), p0=9808, stride=9872) == \
+            hq.HQ_ERR_UNSUPPORTED                                       # more than 8192 candidates
+        assert call(idx=None) == hq.HQ_ERR_INVALID_ARG
+        assert call(kv=_kv(win_cap=192, vl_k=FAKE + 8)) == hq.HQ_ERR_INVALID_ARG
+        assert call(p0=872) == hq.HQ_OK                                # no position left the window
+    assert upd(stride=871) == hq.HQ_ERR_INVALID_ARG
+    assert upd(sc=None) == hq.HQ_ERR_INVALID_ARG
+    assert red(qdt=hq.HQ_F16) == hq.HQ_ERR_INVALID_ARG                # not the cache's 16-bit dtype
+    assert red(Hq=7) == hq.HQ_ERR_INVALID_ARG
+    assert red(R=0) == hq.HQ_ERR_INVALID_ARG and red(R=1025) == hq.HQ_ERR_INVALID_ARG
+    assert red(q=None) == hq.HQ_ERR_INVALID_ARG
+    assert red(q=FAKE + 8) == hq.HQ_ERR_INVALID_ARG
+    assert red(kv=_kv(win_cap=192, k_codes=None)) == hq.HQ_ERR_INVALID_ARG
+    need = hq.hq_vl_redetect_workspace_size(_kv(win_cap=192))
+    assert need == 2 * (40 + 1024) * 8
+    assert red(wsb=need - 1) == hq.HQ_ERR_WORKSPACE and red(ws=None) == hq.HQ_ERR_WORKSPACE
+    assert red(ws=FAKE + 4) == hq.HQ_ERR_INVALID_ARG
+    assert "hq_vl_redetect" in hq.hq_last_error()
+
+
 def test_detect_cache_and_mass_reject():
     L = hq.lib()
     ran = ctypes.c_int(7)

@@ -1,8 +1,11 @@
 """GPU parity of the rolling hybrid cache over many decode steps against the
 oracle's lifecycle simulation (oracle/lifecycle.py): 130 decode steps
-crossing two re-detections. Each step's attention output within the decode
-bar; every re-detected VL set bit-exact; at the end the INT4 planes written
-by the per-step eviction, the VL rows and the VL bitmap bit-exact."""
+crossing two re-detections, through the fused re-detection (hq_vl_redetect)
+and through the detector's scores then hq_vl_update. Each step's attention
+output within the decode bar; every re-detected VL set bit-exact; at the end
+the INT4 planes written by the per-step eviction, the VL rows and the VL
+bitmap bit-exact. hq_vl_update alone on constructed scores, and
+hq_vl_redetect against the two-call path bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -15,14 +18,15 @@ from tests.gpu_util import TORCH_DT, rel_err, say, tile16_codes, to_dev
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("B,Hq,Hkv,D,T0,W,k,R,n,dtype", [
     (1, 8, 2, 128, 700, 32, 35, 64, 130, "bf16"),     # G = 4: the matrix-core INT4 pass
     (2, 4, 2, 64, 500, 16, 25, 16, 40, "f16"),        # D = 64, G = 2, a short ring (R = 16)
 ])
-def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, dtype):
+def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, dtype, fused):
     w = synth.Workload(f"life{T0}", 9100 + T0, B=B, Hq=Hq, Hkv=Hkv, D=D, T=T0 + n, W=W, k=k, dtype=dtype,
                        R=R, n_plant=max(2, int(0.02 * (T0 + n))))
-    say(f"lifecycle B={B} Hq={Hq} Hkv={Hkv} D={D} T0={T0} W={W} k={k} R={R} steps={n} {dtype}")
+    say(f"lifecycle B={B} Hq={Hq} Hkv={Hkv} D={D} T0={T0} W={W} k={k} R={R} steps={n} {dtype} fused={fused}")
     K, V = synth.all_keys(w), synth.all_values(w)                   # every position's 16-bit rows
     queries = np.stack([synth.all_queries(w.replace(seed=w.seed + 101 * (s + 1))) for s in range(n)])
     assert detect.on_grid(queries)                                   # exact detector scores
@@ -53,7 +57,7 @@ def test_rolling_cache_matches_oracle_lifecycle(B, Hq, Hkv, D, T0, W, k, R, n, d
         assert e <= 2e-3 and np.max(np.abs(l - lses[s])) <= 1e-3, (s, e)
         rc.advance(Kd[:, :, T0 + s], Vd[:, :, T0 + s])
         if rc.due():
-            rc.redetect()
+            rc.redetect(fused=fused)
             got_sets.append((s, np.sort(rc.vl_idx[..., :k].cpu().numpy(), axis=-1)))
     torch.cuda.synchronize()
     say(f"  worst step max|err|/rms = {worst:.3e}")
@@ -140,3 +144,57 @@ def test_vl_update_ties_and_sizes(k, n_st, spread, seed):
         for p in want:
             wb[p >> 5] |= np.uint32(1) << np.uint32(p & 31)
         assert np.array_equal(bits[0, h], wb)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,T,W,k,R,n_st,dtype", [
+    (1, 8, 2, 128, 3000, 32, 100, 64, 64, "bf16"),
+    (2, 32, 2, 128, 5000, 128, 250, 64, 64, "bf16"),   # G = 16, the GLM-4-9B head grouping
+    (1, 4, 4, 64, 2000, 16, 90, 16, 16, "f16"),        # D = 64, G = 1
+    (1, 4, 2, 64, 1500, 16, 50, 8, 5, "f32"),          # fp32 rows, fewer new positions than ring slots
+    (4, 32, 8, 128, 6300, 32, 5000, 64, 64, "bf16"),   # 32 heads x 5064 candidates: two rounds per scoring block
+])
+def test_vl_redetect_matches_detector_then_update(B, Hq, Hkv, D, T, W, k, R, n_st, dtype):
+    """hq_vl_redetect (summed ring and candidate scores, then the update)
+    against hq_detect_vlines_cache over every position then hq_vl_update, on
+    two copies of the same cache: the index lists, the VL rows and the bitmap
+    bit for bit; and the new set against the oracle's update rule over the
+    oracle's INT4-key scores (queries on the 2^-4 grid: exact scores)."""
+    say(f"vl_redetect B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} W={W} k={k} R={R} n_st={n_st} {dtype}")
+    rng = np.random.default_rng(T + k)
+    nq = T - W
+    p0 = nq - n_st
+    grid = lambda shape, sc=1.0: np.rint(rng.standard_normal(shape) * sc * 16) / 16
+    K = grid((B, Hkv, T, D)).astype(np.float32)
+    V = grid((B, Hkv, T, D)).astype(np.float32)
+    qring = grid((B, Hq, R, D)).astype(np.float32)
+    vl = np.stack([np.stack([np.sort(rng.choice(p0, k, replace=False)) for _ in range(Hkv)])
+                   for _ in range(B)]).astype(np.int32)
+    dt = TORCH_DT[dtype]
+    Kd, Vd, qd = to_dev(K, dtype), to_dev(V, dtype), to_dev(qring, dtype)
+    caches = []
+    for _ in range(2):
+        c = hq.HybridCache(B, Hkv, D, T, W, k, dt, win_cap=W + R)
+        c.build(Kd, Vd, torch.from_numpy(vl).cuda())
+        caches.append(c)
+    a, b = caches
+    scores = torch.zeros((B, Hkv, nq), dtype=torch.int64, device="cuda")
+    ws = torch.zeros(hq.hq_detect_workspace_size(B, Hkv, nq, 0), dtype=torch.uint8, device="cuda")
+    hq.hq_detect_vlines_cache(None, qd, Hq, R, R - 1, True, a.descriptor(), nq, 0, None, scores.view(-1), ws)
+    hq.hq_vl_update(a.descriptor(), a.vl_idx, p0, scores, nq)
+    rws = torch.full((hq.hq_vl_redetect_workspace_size(b.descriptor()),), 0xFF, dtype=torch.uint8, device="cuda")
+    hq.hq_vl_redetect(b.descriptor(), b.vl_idx, p0, qd, Hq, R, rws)
+    torch.cuda.synchronize()
+    for name in ("vl_idx", "vl_bits", "vl_k", "vl_v"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert torch.equal(x, y), name
+    # the oracle's rule over the oracle's scores
+    G = Hq // Hkv
+    kp, ks = quant.quantize_rows(K[:, :, :nq])
+    got = b.vl_idx.cpu().numpy()
+    for bb in range(B):
+        for h in range(Hkv):
+            rows = qring[bb, h * G:(h + 1) * G].reshape(G * R, D)
+            units, ok = detect.cache_scores(rows, kp[bb, h], ks[bb, h])
+            assert ok
+            want = lifecycle.select(units, vl[bb, h], p0, nq, k)
+            assert np.array_equal(np.sort(got[bb, h]), want), (bb, h)
