@@ -79,3 +79,50 @@ def test_decode_steps_and_detection_replay_in_a_graph():
         hq.hq_decode_attn(qs[(rep + 1) % 4], Hq, kv, 0.0, 0, scratch_o, scratch_l, ws)
         torch.cuda.synchronize()
     say("   3 replays bitwise equal to the eager run")
+
+
+def test_redetection_replays_in_a_graph():
+    """hq_vl_redetect (candidate scores, then the in-place update) captured
+    in a graph and replayed three times on one rolling cache, with eager work
+    and synchronisations between the replays. The update changes the cache,
+    so every replay is compared with the same call run eagerly on a twin
+    cache in the same state: index list, bitmap and VL rows bit for bit."""
+    B, Hq, Hkv, D, T, W, k, R, dtype = 1, 8, 2, 128, 2000, 32, 60, 64, "bf16"
+    say(f"graph: re-detection, B={B} Hq={Hq} Hkv={Hkv} T={T} W={W} k={k}")
+    rng = np.random.default_rng(77)
+    nq = T - W
+    grid = lambda shape: np.rint(rng.standard_normal(shape) * 16) / 16
+    Kd, Vd = to_dev(grid((B, Hkv, T, D)).astype(np.float32), dtype), to_dev(grid((B, Hkv, T, D)).astype(np.float32), dtype)
+    vl = np.stack([np.sort(rng.choice(nq - R, k, replace=False)) for _ in range(Hkv)])[None].astype(np.int32)
+    caches = []
+    for _ in range(2):
+        c = hq.HybridCache(B, Hkv, D, T, W, k, TORCH_DT[dtype], win_cap=W + R)
+        c.build(Kd, Vd, torch.from_numpy(vl).cuda())
+        caches.append(c)
+    eager, graphed = caches
+    rings = [to_dev(grid((B, Hq, R, D)).astype(np.float32), dtype) for _ in range(3)]
+    ring = rings[0].clone()
+    wse = torch.zeros(hq.hq_vl_redetect_workspace_size(eager.descriptor()), dtype=torch.uint8, device="cuda")
+    wsg = torch.zeros_like(wse)
+    p0 = nq - R
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    kvg = graphed.descriptor()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            hq.hq_vl_redetect(kvg, graphed.vl_idx, p0, ring, Hq, R, wsg, stream=s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ring.copy_(rings[rep])                   # a new query ring for each replay
+        hq.hq_vl_redetect(eager.descriptor(), eager.vl_idx, p0, rings[rep], Hq, R, wse)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name in ("vl_idx", "vl_bits", "vl_k", "vl_v"):
+            assert torch.equal(getattr(graphed, name), getattr(eager, name)), f"replay {rep}: {name}"
+        # eager work between replays
+        wsg.fill_(0xFF)
+        torch.cuda.synchronize()
