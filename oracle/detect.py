@@ -119,6 +119,16 @@ def cache_scores(q_rows: np.ndarray, k_packed: np.ndarray, k_sz: np.ndarray, gro
     return (qd + up).astype(np.int64), ok
 
 
+def cache_scores_float(q_rows: np.ndarray, k_packed: np.ndarray, k_sz: np.ndarray, group: int = 32):
+    """The same column scores for queries off the 2**-4 grid: c_j = (sum_rows
+    q) . k_hat_j in float64 (the summed query, the INT4 round trip
+    k_hat = c * s + z, one matrix-vector product), in units of 2**-16 and
+    not rounded. On the grid it rounds (half to even) to cache_scores."""
+    qs = np.asarray(q_rows, dtype=np.float64).sum(axis=0)
+    kh = quant.dequantize_rows(k_packed, k_sz, group).astype(np.float64)
+    return (kh @ qs) * 65536.0
+
+
 def detect_cache(q_acc: np.ndarray, k_packed: np.ndarray, k_sz: np.ndarray, cand_end: int, k: int,
                  require_exact: bool = True):
     """The detector scored from the INT4 key cache. q_acc [B][Hq][R][D];

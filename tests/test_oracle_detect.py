@@ -152,6 +152,32 @@ def test_cache_scores_equal_fp64_scores_of_dequantized_keys():
         detect.cache_scores(Q + 1e-3, kp, ks)
 
 
+def test_cache_scores_float_rounds_to_the_exact_scores_and_tracks_fractions_off_grid():
+    """The float64 cache scores: on grid queries they round (half to even) to
+    the exact integer scores; off the grid (plain draws) they stay within
+    1e-6 units of 2**-16 of the exact rational value (scalar brute force on a
+    few keys), far below the one-unit rounding of the device's int64 scores."""
+    from oracle import quant
+    rng = np.random.default_rng(33)
+    Qg = _grid(rng, (64, 128), scale=1.0)
+    K = (rng.standard_normal((300, 128)) * np.where(rng.random(128) < 0.03, 10, 1)).astype(np.float32)
+    kp, ks = quant.quantize_rows(K)
+    exact, ok = detect.cache_scores(Qg, kp, ks)
+    assert ok
+    assert np.array_equal(np.rint(detect.cache_scores_float(Qg, kp, ks)).astype(np.int64), exact)
+    Q = rng.standard_normal((6, 64)).astype(np.float32).astype(np.float64)
+    kp2, ks2 = quant.quantize_rows(K[:5, :64])
+    f = detect.cache_scores_float(Q, kp2, ks2)
+    codes = quant.unpack_nibbles(kp2)
+    s, z = quant.split_scale_zero(ks2)
+    for j in range(5):
+        c = Fraction(0)
+        for d in range(64):
+            kh = Fraction(int(codes[j, d])) * Fraction(float(s[j, d // 32])) + Fraction(float(z[j, d // 32]))
+            c += sum(Fraction(float(Q[r, d])) for r in range(6)) * kh
+        assert abs(Fraction(float(f[j])) - c * (1 << 16)) < Fraction(1, 10 ** 6)
+
+
 def test_mass_scores_closed_forms_and_brute_force():
     """Attention-mass scores: every row's probabilities sum to one, so over
     all keys the scores sum to the number of rows; a single key gets every
