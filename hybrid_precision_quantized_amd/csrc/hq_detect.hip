@@ -28,16 +28,19 @@
 //  * top-k           every score kernel also writes the min and max of the
 //    256 scores each of its blocks produced. topk_keys: many blocks per
 //    unit reduce the unit's partial ranges, write the 32-bit keys
-//    1 + (score - min) >> shift and a histogram of the keys' top 11 bits per
-//    block. topk_select: one workgroup per unit sums the block histograms
-//    into the first digit. A boundary bucket of at most 1024 keys is ranked
-//    directly by (score, position); a larger one goes through the remaining
-//    two digits (11 and 10 bits), a refinement on the bits the shift dropped
-//    and a cut of equal scores by position; the output is compacted in
-//    order, ascending by position. Up to 32768 candidates per unit one
-//    launch does both (topk_small): each thread keeps the keys of its 32
-//    positions in registers, and the range and the first histogram are
-//    built inside the workgroup.
+//    1 + (score - min) scaled by a power of two so that the range spans 31
+//    bits, and a histogram of the keys' top 11 bits per block.
+//    topk_select: one workgroup per unit sums the block histograms into the
+//    first digit. A boundary bucket of at most 1024 keys is ranked directly
+//    by (score, position), and the output offset of every block's chunk is
+//    scanned; topk_write then writes each chunk's taken positions in order,
+//    a workgroup per chunk. A larger bucket goes through the remaining two
+//    digits (11 and 10 bits), a refinement on the bits the shift dropped and
+//    a cut of equal scores by position, and its output is compacted by
+//    topk_select itself, ascending by position. Up to 32768 candidates per
+//    unit one launch does all of it (topk_small): each thread keeps the
+//    keys of its 32 positions in registers, and the range and the first
+//    histogram are built inside the workgroup.
 #include "hq_common.h"
 
 namespace hq {
@@ -578,6 +581,7 @@ struct TopkShared {
   long long bsc[kSmallBucket];                 // the boundary bucket: scores and positions
   int bpos[kSmallBucket];
   int rank[kSmallBucket];
+  int cnt[32];                                 // taken positions per chunk (the write launch's offsets)
   int bcnt;
 };
 
@@ -668,6 +672,7 @@ __device__ int find_digit(int nb, int *k_rem, int *cnt, SH &sh) {
 // Chunking of a unit's candidates over the blocks of the first two launches.
 constexpr int kTkBlock = 256;
 constexpr int kTkMaxBlocks = 32;
+static_assert(kTkMaxBlocks <= 32, "TopkShared::cnt and the select kernel's per-chunk sums hold 32 chunks");
 struct TopkChunks {
   int nbu;        // blocks per unit
   int64_t ch;     // candidates per block (a multiple of 4)
@@ -684,9 +689,13 @@ __host__ __device__ inline TopkChunks topk_chunks(int64_t n) {
 // Partial score ranges per unit: one per 256 candidates, written by the
 // score kernels (every one of them covers 256 candidates per block).
 __host__ __device__ inline int topk_partials(int64_t n) { return static_cast<int>((n + 255) / 256); }
-// workspace of the top-k: partial ranges, block histograms, keys
+// Per unit, what the select launch hands the write launch: {mode, first
+// digit, output offset of every chunk}; mode 0: the write launch writes the
+// chunk's taken positions, 1: the select launch has written them.
+constexpr int kCtl = kTkMaxBlocks + 2;
+// workspace of the top-k: partial ranges, block histograms, keys, control
 struct TopkWs {
-  size_t mm, hist, keys, total;
+  size_t mm, hist, keys, ctl, total;
 };
 TopkWs topk_ws(int64_t units, int64_t n) {
   const TopkChunks c = topk_chunks(n);
@@ -694,7 +703,8 @@ TopkWs topk_ws(int64_t units, int64_t n) {
   L.mm = 0;
   L.hist = align_up(static_cast<size_t>(units) * topk_partials(n) * 2 * sizeof(unsigned long long), 256);
   L.keys = align_up(L.hist + static_cast<size_t>(units) * c.nbu * kBins * sizeof(uint32_t), 256);
-  L.total = align_up(L.keys + static_cast<size_t>(units) * key_stride(n) * sizeof(uint32_t), 256);
+  L.ctl = align_up(L.keys + static_cast<size_t>(units) * key_stride(n) * sizeof(uint32_t), 256);
+  L.total = align_up(L.ctl + static_cast<size_t>(units) * kCtl * sizeof(int), 256);
   return L;
 }
 // where the score kernels put their partial ranges
@@ -730,7 +740,7 @@ __device__ __forceinline__ void block_minmax(unsigned long long &mn, unsigned lo
 // the unit's range from its nbu partials, by the first wave (every block
 // and every launch reduces them in the same way)
 __device__ __forceinline__ void unit_range(const unsigned long long *mm, int nbu, unsigned long long &base,
-                                           int &shift, unsigned long long *red) {
+                                           int &shift, int &lsh, unsigned long long *red) {
   if (threadIdx.x < 64) {
     unsigned long long mn = ~0ull, mx = 0;
     for (int i = threadIdx.x; i < nbu; i += 64) {
@@ -751,10 +761,17 @@ __device__ __forceinline__ void unit_range(const unsigned long long *mm, int nbu
   __syncthreads();
   base = red[0];
   const unsigned long long range = red[1] - red[0];
-  // keys 1 + (score - min) >> shift fit 32 bits; key 0 marks no position
+  // keys 1 + (((score - min) >> shift) << lsh): the range spans bits 0..30
+  // whatever its width (a wider one drops its low bits, a narrower one is
+  // moved up so that the first digit splits it as finely as a wide one), the
+  // largest key is at most 2^31, and key 0 marks no position
   const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
   shift = nbits > 31 ? nbits - 31 : 0;
+  lsh = nbits < 31 ? 31 - nbits : 0;
   __syncthreads();
+}
+__device__ __forceinline__ uint32_t score_key(unsigned long long off, int shift, int lsh) {
+  return 1u + (static_cast<uint32_t>(off >> shift) << lsh);
 }
 
 // 1. per (unit, block): the chunk's keys and the histogram of their top 11 bits
@@ -770,8 +787,8 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
   uint32_t *kk = keys + static_cast<int64_t>(unit) * key_stride(n);
   for (int i = threadIdx.x; i < (kTkBlock / 64) * kBins; i += kTkBlock) (&h[0][0])[i] = 0u;
   unsigned long long base;
-  int shift;
-  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, red);
+  int shift, lsh;
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, lsh, red);
   const int64_t c0 = blk * ch;
   const int64_t c1 = c0 + ch < n ? c0 + ch : n;
   uint32_t *wh = h[threadIdx.x >> 6];
@@ -780,7 +797,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
     const bool ok = j < c1;
     uint32_t key = 0;
     if (ok) {
-      key = 1u + static_cast<uint32_t>((ordered(sc[j]) - base) >> shift);
+      key = score_key(ordered(sc[j]) - base, shift, lsh);
       kk[j] = key;
     }
     hist_add(wh, ok, key >> 21);
@@ -932,82 +949,183 @@ __device__ __forceinline__ void rank_bucket(TopkShared &sh, int eq) {
   __syncthreads();
 }
 
-// 2. Units with more than kSmallN candidates: one workgroup per unit; thread
-// t owns positions [t P, t P + P), P a multiple of 4, and streams their keys
-// from the workspace. The first digit comes from the block histograms. When
-// its bucket holds at most kSmallBucket keys, the bucket's (score, position)
-// pairs are collected and ranked; the selection is then a predicate on
-// (digit, score, position), counted, scanned and written in order. Larger
-// buckets take the radix path.
+// 2. One workgroup per unit. The first digit comes from the block
+// histograms (every load in flight at once). When its bucket holds at most
+// kSmallBucket keys, the bucket's (score, position) pairs are collected (a
+// coalesced pass over the keys, any order) and ranked, each member's
+// decision is written into its key (all ones: taken, 0: dropped), and the
+// number of taken positions of every chunk of the keys launch (its keys
+// above the digit, from its histogram, plus its taken members) is scanned
+// into the chunks' output offsets: the write launch then emits the positions
+// in order, a workgroup per chunk. A larger bucket takes the radix path here,
+// which writes the output itself.
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t *__restrict__ scores,
                                                                    uint32_t *__restrict__ keys,
                                                                    const uint32_t *__restrict__ bhist,
                                                                    const unsigned long long *__restrict__ mm,
-                                                                   int64_t n, int nbu, int np, int k_top,
-                                                                   int32_t *__restrict__ idx_out) {
+                                                                   int64_t n, int nbu, int64_t ch, int np,
+                                                                   int k_top, int32_t *__restrict__ idx_out,
+                                                                   int *__restrict__ ctl) {
   __shared__ TopkShared sh;
   const int unit = blockIdx.x;
   const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
   const int64_t nst = key_stride(n);
   uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
   int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
+  int *cu = ctl + static_cast<int64_t>(unit) * kCtl;
   if (k_top == 0) return;
-  const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // wave-uniform
-  const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
-  const int64_t j1 = j0 + P < n ? j0 + P : n;
-
-  // the first digit from the block histograms (every load in flight at once)
-  {
-    const uint32_t *bh = bhist + static_cast<int64_t>(unit) * nbu * kBins;
-    for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
-      uint32_t v[kTkMaxBlocks];
+  const uint32_t *bh = bhist + static_cast<int64_t>(unit) * nbu * kBins;
+  for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
+    uint32_t v[kTkMaxBlocks];
 #pragma unroll
-      for (int blk = 0; blk < kTkMaxBlocks; ++blk) v[blk] = blk < nbu ? bh[static_cast<int64_t>(blk) * kBins + b] : 0u;
-      uint32_t t = 0;
+    for (int blk = 0; blk < kTkMaxBlocks; ++blk) v[blk] = blk < nbu ? bh[static_cast<int64_t>(blk) * kBins + b] : 0u;
+    uint32_t t = 0;
 #pragma unroll
-      for (int blk = 0; blk < kTkMaxBlocks; ++blk) t += v[blk];
-      sh.hist[b] = t;
-    }
+    for (int blk = 0; blk < kTkMaxBlocks; ++blk) t += v[blk];
+    sh.hist[b] = t;
   }
   if (threadIdx.x == 0) sh.bcnt = 0;
   if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
+  if (threadIdx.x < kTkMaxBlocks) sh.cnt[threadIdx.x] = 0;
   __syncthreads();
   int k_rem = k_top, eq = 0;
   const uint32_t d1 = static_cast<uint32_t>(find_digit(kBins, &k_rem, &eq, sh));
 
   if (eq <= kSmallBucket) {                     // eq: from LDS, uniform
-    for_own_ws(gk, nst, P, j1, [&](int64_t j, uint32_t key, bool ok) {
-      if (ok && (key >> 21) == d1) {
-        const int slot = atomicAdd(&sh.bcnt, 1);
-        sh.bsc[slot] = sc[j];
-        sh.bpos[slot] = static_cast<int>(j);
+    constexpr int kBatch = 8;                   // 16-byte key loads in flight per thread
+    const uint4 *g4 = reinterpret_cast<const uint4 *>(gk);
+    const int64_t n4 = nst / 4;
+#pragma unroll 1
+    for (int64_t i0 = 0; i0 < n4; i0 += static_cast<int64_t>(kBatch) * kTopkThreads) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * kTopkThreads + threadIdx.x;
+        v[u] = i < n4 ? g4[i] : make_uint4(0u, 0u, 0u, 0u);
       }
-    });
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t j = 4 * (i0 + static_cast<int64_t>(u) * kTopkThreads + threadIdx.x);
+        const uint32_t kk[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (j + c < n && (kk[c] >> 21) == d1) {
+            const int slot = atomicAdd(&sh.bcnt, 1);
+            sh.bsc[slot] = sc[j + c];
+            sh.bpos[slot] = static_cast<int>(j + c);
+          }
+        }
+      }
+    }
     __syncthreads();
     rank_bucket(sh, eq);
-    // each member's decision goes into its key: all ones (above every real
-    // key, at most 2^31) to take it, 0 to drop it; the passes below then need
-    // no scores
-    if (static_cast<int>(threadIdx.x) < eq) {
-      const uint32_t mark = sh.rank[threadIdx.x] < k_rem ? 0xFFFFFFFFu : 0u;
-      gk[sh.bpos[threadIdx.x]] = mark;
+    // per chunk: its keys above the digit (32 threads sum a chunk's bins
+    // above d1), then its taken members
+    {
+      const int blk = static_cast<int>(threadIdx.x) >> 5, part = threadIdx.x & 31;
+      uint32_t a = 0;
+      if (blk < nbu) {
+        const uint32_t *h = bh + static_cast<int64_t>(blk) * kBins;
+#pragma unroll 8
+        for (int b = static_cast<int>(d1) + 1 + part; b < kBins; b += 32) a += h[b];
+      }
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) a += __shfl_xor(a, m, 64);
+      if (part == 0 && blk < nbu) atomicAdd(&sh.cnt[blk], static_cast<int>(a));
     }
-    __threadfence_block();
+    if (static_cast<int>(threadIdx.x) < eq) {
+      const bool t = sh.rank[threadIdx.x] < k_rem;
+      gk[sh.bpos[threadIdx.x]] = t ? 0xFFFFFFFFu : 0u;
+      if (t) atomicAdd(&sh.cnt[static_cast<int64_t>(sh.bpos[threadIdx.x]) / ch], 1);
+    }
     __syncthreads();
-    auto take_it = [&](uint32_t key) -> bool { return key == 0xFFFFFFFFu || (key >> 21) > d1; };
-    int cnt = 0;
-    for_own_ws(gk, nst, P, j1, [&](int64_t, uint32_t key, bool ok) { cnt += ok && take_it(key); });
-    int tot;
-    int pos = block_exclusive_scan(cnt, sh.scan, &tot);
-    for_own_ws(gk, nst, P, j1, [&](int64_t j, uint32_t key, bool ok) {
-      if (ok && take_it(key) && pos < k_top) out[pos++] = static_cast<int32_t>(j);
-    });
+    if (threadIdx.x < 64) {
+      const int c = static_cast<int>(threadIdx.x) < nbu ? sh.cnt[threadIdx.x] : 0;
+      int inc = c;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int y = __shfl_up(inc, m, 64);
+        if (static_cast<int>(threadIdx.x) >= m) inc += y;
+      }
+      if (threadIdx.x == 0) {
+        cu[0] = 0;
+        cu[1] = static_cast<int>(d1);
+      }
+      if (static_cast<int>(threadIdx.x) < nbu) cu[2 + threadIdx.x] = inc - c;
+    }
     return;
   }
+  if (threadIdx.x == 0) cu[0] = 1;
+  const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // wave-uniform
+  const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
+  const int64_t j1 = j0 + P < n ? j0 + P : n;
+  (void)j0;
   unsigned long long base;
-  int shift;
-  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, sh.mm);
+  int shift, lsh;
+  unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, lsh, sh.mm);
   topk_radix(sh, sc, gk, nst, P, j1, base, shift, d1 << 21, k_rem, eq, k_top, out);
+}
+
+// 3. Per (unit, chunk of the keys launch), when the select launch left the
+// writing to it: thread t tests positions [c0 + t Q, c0 + t Q + Q) (taken:
+// key all ones, or first digit above d1), the block scans the counts, and
+// the taken positions go to out[offset + rank] in ascending order.
+constexpr int kWrThreads = 256;
+constexpr int kWrRun = 16;                     // positions per thread per batch
+__global__ __launch_bounds__(kWrThreads) void topk_write_kernel(const uint32_t *__restrict__ keys,
+                                                                const int *__restrict__ ctl, int64_t n, int nbu,
+                                                                int64_t ch, int k_top,
+                                                                int32_t *__restrict__ idx_out) {
+  __shared__ int scan[kWrThreads / 64 + 1];
+  const int unit = blockIdx.x / nbu, blk = blockIdx.x % nbu;
+  const int *cu = ctl + static_cast<int64_t>(unit) * kCtl;
+  if (k_top == 0 || cu[0] != 0) return;        // uniform over the block
+  const uint32_t d1 = static_cast<uint32_t>(cu[1]);
+  const int off = cu[2 + blk];
+  const uint32_t *gk = keys + static_cast<int64_t>(unit) * key_stride(n);
+  int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
+  const int64_t c0 = static_cast<int64_t>(blk) * ch;
+  const int64_t c1 = c0 + ch < n ? c0 + ch : n;
+  const int64_t Q = ((ch + kWrThreads - 1) / kWrThreads + 3) & ~3LL;       // a multiple of 4
+  const int64_t b0 = c0 + static_cast<int64_t>(threadIdx.x) * Q;
+  // taken bits of positions [b0 + q0, b0 + q0 + kWrRun); c0 and Q are
+  // multiples of 4, so each 16-byte load stays inside the unit's key stride
+  auto taken = [&](int64_t q0) -> uint32_t {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kWrRun / 4; ++i) {
+      const int64_t j = b0 + q0 + 4 * i;
+      if (q0 + 4 * i < Q && j < c1) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(gk + j);
+        const uint32_t kk[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool t = j + c < c1 && (kk[c] == 0xFFFFFFFFu || (kk[c] >> 21) > d1);
+          m |= static_cast<uint32_t>(t) << (4 * i + c);
+        }
+      }
+    }
+    return m;
+  };
+  int cnt = 0;
+  for (int64_t q0 = 0; q0 < Q; q0 += kWrRun) cnt += __popc(taken(q0));
+  // exclusive scan of the counts over the block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = cnt;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int y = __shfl_up(inc, m, 64);
+    if (lane >= m) inc += y;
+  }
+  if (lane == 63) scan[w] = inc;
+  __syncthreads();
+  int pre = inc - cnt;
+  for (int i = 0; i < w; ++i) pre += scan[i];
+  int pos = off + pre;
+  for (int64_t q0 = 0; q0 < Q; q0 += kWrRun) {
+    for (uint32_t m = taken(q0); m != 0u && pos < k_top; m &= m - 1u)
+      out[pos++] = static_cast<int32_t>(b0 + q0 + __builtin_ctz(m));
+  }
 }
 
 // 1 + 2 in one launch for units with at most kSmallN candidates: one
@@ -1023,6 +1141,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
 // writes the keys to the workspace and takes the radix path.
 constexpr int kSmallP = 32;
 constexpr int64_t kSmallN = static_cast<int64_t>(kTopkThreads) * kSmallP;
+// units up to this many candidates take the one-launch kernel; larger ones
+// the keys, select and write launches, which spread the passes over the
+// positions across many compute units
+constexpr int64_t kTopkOneLaunchN = kSmallN;
 // A copy of x that the compiler cannot relate to x, so that the per-position
 // values built on it in one phase are not merged with those of another phase
 // (which would keep 32 of them live, or spilled, in between).
@@ -1053,7 +1175,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
   // of the score kernels' np partial ranges, by the first wave.
   uint32_t key[kSmallP];
   unsigned long long base;
-  int shift;
+  int shift, lsh;
   {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int64_t *>(sc), static_cast<short>(0), static_cast<int>(n * 8), 0x00020000);
@@ -1065,11 +1187,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
     clear_whist(sh);
     if (threadIdx.x == 0) sh.bcnt = 0;
     if (threadIdx.x < kSmallBucket) sh.rank[threadIdx.x] = 0;
-    unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, sh.mm);   // ends behind a barrier
+    unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, lsh, sh.mm);   // ends behind a barrier
     const uint32_t vmask = nown >= 32 ? 0xFFFFFFFFu : (1u << nown) - 1u;
 #pragma unroll
     for (int i = 0; i < kSmallP; ++i)
-      key[i] = (1u + static_cast<uint32_t>((u[i] - base) >> shift)) & (0u - ((vmask >> i) & 1u));
+      key[i] = score_key(u[i] - base, shift, lsh) & (0u - ((vmask >> i) & 1u));
   }
   uint32_t *wh = sh.whist[threadIdx.x >> 7];
 #pragma unroll
@@ -1130,16 +1252,18 @@ void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, in
   unsigned long long *mm = reinterpret_cast<unsigned long long *>(w8 + L.mm);
   uint32_t *bh = reinterpret_cast<uint32_t *>(w8 + L.hist);
   uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + L.keys);
+  int *ctl = reinterpret_cast<int *>(w8 + L.ctl);
   const int np = topk_partials(n);
-  if (n <= kSmallN && !skewed) {
+  if (n <= kTopkOneLaunchN && !skewed) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, mm, keys, n, np, k_top,
                        idx_out);
     return;
   }
   const unsigned nb = static_cast<unsigned>(units) * c.nbu;
   hipLaunchKernelGGL(topk_keys_kernel, dim3(nb), dim3(kTkBlock), 0, st, scores, n, c.nbu, c.ch, np, mm, keys, bh);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm, n, c.nbu, np,
-                     k_top, idx_out);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, keys, bh, mm, n, c.nbu, c.ch,
+                     np, k_top, idx_out, ctl);
+  hipLaunchKernelGGL(topk_write_kernel, dim3(nb), dim3(kWrThreads), 0, st, keys, ctl, n, c.nbu, c.ch, k_top, idx_out);
 }
 
 // ---------------------------------------------------------------- workspace

@@ -51,6 +51,13 @@ def _run(q_acc, K, cand_end, k_top, method, dtype, exact=True):
     (1, 8, 2, 128, 64, 1000, 1, 1, "bf16", 1.0),        # single candidate
     (1, 8, 2, 128, 16, 40000, 39900, 1995, "bf16", 2.0),  # keys beyond the LDS-resident size
     (1, 4, 1, 128, 2, 5000, 4900, 4000, "bf16", 0.0625),  # nearly all scores tied
+    (2, 8, 2, 128, 8, 20000, 16411, 700, "bf16", 2.0),    # 4 units, narrow score range
+    # beyond 32768 candidates: the keys, select and write launches
+    (1, 8, 2, 128, 8, 34000, 32769, 1, "bf16", 1.0),      # one above the one-launch size, k = 1
+    (2, 8, 2, 128, 4, 50000, 49999, 2500, "bf16", 0.5),   # ragged last chunk, 4 units
+    (1, 8, 1, 128, 16, 33300, 33000, 33000, "f16", 1.0),  # k_top == cand_end
+    (1, 8, 2, 128, 8, 34000, 33000, 0, "bf16", 1.0),      # k_top == 0
+    (1, 4, 1, 128, 2, 36000, 35900, 20000, "bf16", 0.0625),  # crowded first digit: the radix path
 ])
 def test_detect_small_exact(method, B, Hq, Hkv, D, R, n, ce, k_top, dtype, spread):
     say(f"detect method={method} B={B} Hq={Hq} Hkv={Hkv} D={D} R={R} n={n} ce={ce} k={k_top} {dtype}")
@@ -64,6 +71,30 @@ def test_detect_small_exact(method, B, Hq, Hkv, D, R, n, ce, k_top, dtype, sprea
         K = K.astype(np.float16).astype(np.float32)
     want_idx, want_sc = detect.detect(q, K, ce, k_top)
     got_idx, got_sc = _run(q, K, ce, k_top, method, dtype)
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+
+
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("n,ce,k_top", [(3000, 2900, 100), (34000, 33900, 1700)])
+def test_detect_wide_range(method, n, ce, k_top):
+    """A few planted columns far above the rest: the score range exceeds 31
+    bits, so the keys drop low bits and the bulk shares a handful of first
+    digits (the radix path with its refinement on the dropped bits), in the
+    one-launch and the three-launch top-k."""
+    B, Hq, Hkv, D, R = 1, 8, 2, 128, 8
+    say(f"detect wide range method={method} n={n} ce={ce} k={k_top}")
+    rng = np.random.default_rng(n + 7)
+    q = synth.round_dtype(np.rint(rng.standard_normal((B, Hq, R, D)) * 16) / 16, "bf16")
+    K = synth.round_dtype(np.rint(rng.standard_normal((B, Hkv, n, D)) * 16) / 16, "bf16")
+    G = Hq // Hkv
+    for h in range(Hkv):
+        qs = q[0, h * G:(h + 1) * G].sum(axis=(0, 1))
+        K[0, h, rng.choice(ce, 30, replace=False)] = 64.0 * np.where(qs >= 0, 1.0, -1.0)
+    want_idx, want_sc = detect.detect(q, K, ce, k_top)
+    span = int((want_sc.max(axis=-1) - want_sc.min(axis=-1)).min())
+    assert span >= 2 ** 31, span                       # wider than the keys: low bits dropped
+    got_idx, got_sc = _run(q, K, ce, k_top, method, "bf16")
     assert np.array_equal(got_sc, want_sc)
     assert np.array_equal(got_idx, want_idx)
 
