@@ -123,7 +123,13 @@ constexpr int kRowPad = 8;        // halves
 // bytes of each of 16 rows (the 32x32 operand layout reads 32 bytes of each
 // of 32 rows, which stalled the texture path). The unit's query rows are
 // staged through LDS 128 rows at a time (double buffered; rows padded by 16
-// bytes) and every A fragment feeds all NT tiles; rows congruent mod 16 are
+// bytes) and every A fragment feeds all NT tiles. RES (at most 256 rows):
+// both slots take every row at once, the row loads are issued before the K
+// loads, and both go through buffer resources that return zeros past the
+// last row and the last candidate, so the loads are branch-free and each
+// wait covers only what it needs (23.6 -> 20.6 us at 1 x 32K, 8 KV heads,
+// against per-load branches and a wait for every K fragment before the
+// first LDS store). Rows congruent mod 16 are
 // summed by the matrix core itself. A lane ends with 4 of a column's 16 row
 // residues; the column sums them with the other three lane groups in fp64
 // (exact on the 2^-4 grid) and rounds once to int64 units of 2^-16.
@@ -138,7 +144,7 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 }
-template <int D, int DT, int NT>
+template <int D, int DT, int NT, bool RES>
 __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *__restrict__ q_acc,
                                                             const uint16_t *__restrict__ k, int Hq,
                                                             int Hkv, int R, int64_t k_rows,
@@ -167,6 +173,45 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   const int M = G * R;
   const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
 
+  uint4 buf[PER_T], buf2[PER_T];
+  // RES reads through buffer resources whose ranges end at the last query
+  // row and the last candidate row: the hardware returns zeros past them,
+  // so the loads are straight-line code and their waits count exactly
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(qrows), static_cast<short>(0), M * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(k + static_cast<int64_t>(unit) * k_rows * D), static_cast<short>(0),
+      static_cast<int>(cand_end * D * 2), 0x00020000);
+  auto load_stage = [&](int st, uint4 *bb) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      const int grow = st * kStageRows + row;
+      if constexpr (RES) {
+        bb[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              qrs, static_cast<uint32_t>((grow * D + c8 * 8) * 2), 0, 0));
+      } else {
+        bb[e] = grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  auto store_stage = [&](int slot, const uint4 *bb) {
+#pragma unroll
+    for (int e = 0; e < PER_T; ++e) {
+      const int idx = e * 256 + threadIdx.x;
+      const int row = idx / ROWV, c8 = idx % ROWV;
+      *reinterpret_cast<uint4 *>(&qs[slot][row][c8 * 8]) = bb[e];
+    }
+  };
+  // The query rows' loads are issued before the K loads, so that storing
+  // them waits for them alone (loads complete in issue order). RES: at most
+  // 2 kStageRows rows, which the two slots hold at once.
+  const int stages = (M + kStageRows - 1) / kStageRows;
+  load_stage(0, buf);
+  if constexpr (RES) load_stage(1, buf2);
+
   uint4 bfrag[NT][KC];
   int64_t col[NT];
   bool col_ok[NT];
@@ -174,56 +219,70 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   for (int t = 0; t < NT; ++t) {
     col[t] = static_cast<int64_t>(cb) * CPB + (wave * NT + t) * 16 + c16;
     col_ok[t] = col[t] < cand_end;
-    const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      bfrag[t][kc] = col_ok[t] ? *reinterpret_cast<const uint4 *>(krow + 32 * kc + 8 * g4)
-                               : make_uint4(0u, 0u, 0u, 0u);
   }
-
-  uint4 buf[PER_T];
-  auto load_stage = [&](int st) {
+  if constexpr (RES) {
+    // tile by tile: the four loads of a tile read whole 256-byte rows in
+    // turn (channel-block order, which lets the first MFMAs start earlier,
+    // measured slower: 20.6 -> 21.5 us at 1 x 32K, 8 KV heads)
 #pragma unroll
-    for (int e = 0; e < PER_T; ++e) {
-      const int idx = e * 256 + threadIdx.x;
-      const int row = idx / ROWV, c8 = idx % ROWV;
-      const int grow = st * kStageRows + row;
-      buf[e] = grow < M ? *reinterpret_cast<const uint4 *>(qrows + static_cast<int64_t>(grow) * D + c8 * 8)
-                        : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_stage = [&](int slot) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int e = 0; e < PER_T; ++e) {
-      const int idx = e * 256 + threadIdx.x;
-      const int row = idx / ROWV, c8 = idx % ROWV;
-      *reinterpret_cast<uint4 *>(&qs[slot][row][c8 * 8]) = buf[e];
+      for (int kc = 0; kc < KC; ++kc)
+        bfrag[t][kc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     krs, static_cast<uint32_t>((col[t] * D + 32 * kc + 8 * g4) * 2),
+                                                     0, 0));
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint16_t *krow = k + (static_cast<int64_t>(unit) * k_rows + (col_ok[t] ? col[t] : 0)) * D;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        bfrag[t][kc] = col_ok[t] ? *reinterpret_cast<const uint4 *>(krow + 32 * kc + 8 * g4)
+                                 : make_uint4(0u, 0u, 0u, 0u);
     }
-  };
+  }
 
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int stages = (M + kStageRows - 1) / kStageRows;
-  load_stage(0);
-  store_stage(0);
+  store_stage(0, buf);
+  if constexpr (RES) store_stage(1, buf2);
   __syncthreads();
-  for (int st = 0; st < stages; ++st) {
-    if (st + 1 < stages) load_stage(st + 1);
-    const int slot = st & 1;
+  if constexpr (RES) {
+    // every row is in LDS: no staging inside the loop. (Splitting the tiles
+    // into parts computed in turn, so that the first part's MFMAs overlap
+    // the later parts' loads, re-reads every A fragment per part and was
+    // slower: 20.6 -> 21.6 us with 2 parts, 23.5 us with 4.)
+    for (int st = 0; st < stages; ++st) {
 #pragma unroll
-    for (int sub = 0; sub < kStageRows / 16; ++sub) {
-      const uint16_t *arow = &qs[slot][sub * 16 + c16][8 * g4];
+      for (int sub = 0; sub < kStageRows / 16; ++sub) {
+        const uint16_t *arow = &qs[st][sub * 16 + c16][8 * g4];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(arow + 32 * kc);
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 a = *reinterpret_cast<const uint4 *>(arow + 32 * kc);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mfma16<DT>(a, bfrag[t][kc], acc[t]);
+          for (int t = 0; t < NT; ++t) acc[t] = mfma16<DT>(a, bfrag[t][kc], acc[t]);
+        }
       }
     }
-    if (st + 1 < stages) store_stage((st + 1) & 1);
-    __syncthreads();
+  } else {
+    for (int st = 0; st < stages; ++st) {
+      if (st + 1 < stages) load_stage(st + 1, buf);
+      const int slot = st & 1;
+#pragma unroll
+      for (int sub = 0; sub < kStageRows / 16; ++sub) {
+        const uint16_t *arow = &qs[slot][sub * 16 + c16][8 * g4];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 a = *reinterpret_cast<const uint4 *>(arow + 32 * kc);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = mfma16<DT>(a, bfrag[t][kc], acc[t]);
+        }
+      }
+      if (st + 1 < stages) store_stage((st + 1) & 1, buf);
+      __syncthreads();
+    }
   }
   // column c16 of tile t: this lane holds row residues 4 g4 .. 4 g4 + 3 (mod 16)
   unsigned long long mn = ~0ull, mx = 0;
@@ -386,19 +445,29 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
   const int M = G * R;                                        // <= kResRows
   const int subs = (M + 15) / 16;
   const uint16_t *qrows = q_acc + (static_cast<int64_t>(b) * Hq + h * G) * R * D;
-  const uint16_t *kunit = k + static_cast<int64_t>(unit) * k_rows * D;
+  // The K fragments are read and the scores written through buffer
+  // resources that end at the unit's last candidate: past it, loads return
+  // zeros and stores are dropped, and the loads and stores are branch-free
+  // (qwen-sized 16 x 128K column sums 1033 -> 1006 us against per-load
+  // branches). The compiler still places waits that cover part of the next
+  // group's prefetch before a group's MFMAs.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(k + static_cast<int64_t>(unit) * k_rows * D), static_cast<short>(0),
+      static_cast<int>(cand_end * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      scores + static_cast<int64_t>(unit) * cand_end, static_cast<short>(0), static_cast<int>(cand_end * 8),
+      0x00020000);
 
   // K fragments of group g: this lane's column of tiles 4 wave + t of the
   // group, channels 32 kc + 8 g4 .. + 7 (64 contiguous bytes per row and kc)
   auto load_frag = [&](int g, uint4 (&kf)[NT][KC]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t col = static_cast<int64_t>(g) * 256 + (wave * NT + t) * 16 + c16;
-      const bool ok = col < cand_end;
-      const uint16_t *krow = kunit + (ok ? col : 0) * D;
+      const uint32_t col = static_cast<uint32_t>(g * 256 + (wave * NT + t) * 16 + c16);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        kf[t][kc] = ok ? *reinterpret_cast<const uint4 *>(krow + 32 * kc + 8 * g4) : make_uint4(0u, 0u, 0u, 0u);
+        kf[t][kc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  krs, (col * D + 32 * kc + 8 * g4) * 2, 0, 0));
     }
   };
   uint4 kfa[NT][KC], kfb[NT][KC];
@@ -437,12 +506,14 @@ __global__ __launch_bounds__(256, 2) void colsum_resident_kernel(const uint16_t 
       sd += __shfl_xor(sd, 16, 64);
       sd += __shfl_xor(sd, 32, 64);
       const long long v = __double2ll_rn(sd * 65536.0);
-      if (g4 == 0 && col < cand_end) {
-        scores[static_cast<int64_t>(unit) * cand_end + col] = v;
-        const unsigned long long u = ordered_score(v);
-        mn = u < mn ? u : mn;
-        mx = u > mx ? u : mx;
-      }
+      // lane group 0 stores; the others aim past the range (dropped)
+      const uint32_t so = g4 == 0 ? static_cast<uint32_t>(col) * 8u : 0x80000000u;
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), srs, so, 0, 0);
+      const bool ok = col < cand_end;
+      const unsigned long long u = ordered_score(v);
+      mn = ok && u < mn ? u : mn;
+      mx = ok && u > mx ? u : mx;
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -1639,7 +1710,9 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
       // (1 x 32K, 8 KV heads) its longer blocks lose (28.9 -> 31.1 us).
       int gpb = static_cast<int>((static_cast<int64_t>(units) * groups) / 512);
       gpb = gpb < 1 ? 1 : (gpb > kResMaxGroups ? kResMaxGroups : gpb);
-      if (D == 128 && (Hq / Hkv) * R <= kResRows && gpb >= 4) {
+      // (the resident kernel addresses a unit's candidate rows and scores
+      // with 32-bit byte offsets)
+      if (D == 128 && (Hq / Hkv) * R <= kResRows && gpb >= 4 && cand_end * D * 2 < (int64_t{1} << 31)) {
         const int rblocks = units * ((groups + gpb - 1) / gpb);
         if (dtype == HQ_BF16)
           hipLaunchKernelGGL((colsum_resident_kernel<128, HQ_BF16>), dim3(rblocks), dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, groups, gpb, scores, tmm);
@@ -1651,15 +1724,19 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
         const bool wide = static_cast<int64_t>(units) * ((cand_end + 511) / 512) >= 512;
         const int cpb = wide ? 512 : 256;
         const dim3 grid(static_cast<unsigned>(units * ((cand_end + cpb - 1) / cpb)));
-#define HQ_C16(DD, TT, NN) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm)
+        // RES: the unit's query rows fit the two LDS slots at once, and its
+        // candidate rows fit a buffer resource's 32-bit byte range
+        const bool res = (Hq / Hkv) * R <= 2 * kStageRows && cand_end * D * 2 < (int64_t{1} << 31);
+#define HQ_C16R(DD, TT, NN) do { if (res) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, true>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
+                                 else hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, false>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); } while (0)
+#define HQ_C16(DD, TT) do { if (wide) HQ_C16R(DD, TT, 8); else HQ_C16R(DD, TT, 4); } while (0)
         if (D == 128) {
-          if (dtype == HQ_BF16) { if (wide) HQ_C16(128, HQ_BF16, 8); else HQ_C16(128, HQ_BF16, 4); }
-          else { if (wide) HQ_C16(128, HQ_F16, 8); else HQ_C16(128, HQ_F16, 4); }
+          if (dtype == HQ_BF16) HQ_C16(128, HQ_BF16); else HQ_C16(128, HQ_F16);
         } else {
-          if (dtype == HQ_BF16) { if (wide) HQ_C16(64, HQ_BF16, 8); else HQ_C16(64, HQ_BF16, 4); }
-          else { if (wide) HQ_C16(64, HQ_F16, 8); else HQ_C16(64, HQ_F16, 4); }
+          if (dtype == HQ_BF16) HQ_C16(64, HQ_BF16); else HQ_C16(64, HQ_F16);
         }
 #undef HQ_C16
+#undef HQ_C16R
       }
     } else {
       double *qs = reinterpret_cast<double *>(static_cast<uint8_t *>(ws) + L.qs);
