@@ -671,24 +671,6 @@ __device__ __forceinline__ void reduce_whist(SH &sh) {
     sh.hist[b] = t;
   }
 }
-// Adds the lanes with `match` to bin d. The lanes that share the first
-// matching lane's bin add with one atomic (scores pile into few bins when
-// they are skewed, and same-address LDS atomics serialise); the others add
-// their own. Called by the whole wave.
-__device__ __forceinline__ void hist_add(uint32_t *wh, bool match, uint32_t d) {
-  const unsigned long long act = __ballot(match);
-  if (act == 0) return;
-  const int first = static_cast<int>(__builtin_ctzll(act));
-  const uint32_t lead = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(d), first));
-  const bool same = match && d == lead;
-  const unsigned long long sm = __ballot(same);
-  if (same) {
-    if ((threadIdx.x & 63) == first) atomicAdd(&wh[lead], static_cast<uint32_t>(__popcll(sm)));
-  } else if (match) {
-    atomicAdd(&wh[d], 1u);
-  }
-}
-
 // Digit search after a histogram pass: the digit (bins in descending order)
 // holding the k_rem-th largest; returns it, *k_rem becomes the rank inside
 // the digit and *cnt the digit's population. The first wave searches (lane
@@ -871,7 +853,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
       key = score_key(ordered(sc[j]) - base, shift, lsh);
       kk[j] = key;
     }
-    hist_add(wh, ok, key >> 21);
+    if (ok) atomicAdd(&wh[key >> 21], 1u);
   }
   __syncthreads();
   uint32_t *bh = bhist + (static_cast<int64_t>(unit) * nbu + blk) * kBins;
@@ -899,15 +881,45 @@ __device__ __forceinline__ void for_own_ws(const uint32_t *gk, int64_t nst, int6
   }
 }
 
+// Visits every position j < n of a unit's keys in the workspace, in no
+// particular order: 16-byte loads, consecutive across the block (coalesced),
+// kBatch of them in flight per thread: visit(j, key).
+template <class F>
+__device__ __forceinline__ void for_all_ws(const uint32_t *gk, int64_t n, F &&visit) {
+  constexpr int kBatch = 8;
+  const uint4 *g4 = reinterpret_cast<const uint4 *>(gk);
+  const int64_t n4 = key_stride(n) / 4;
+#pragma unroll 1
+  for (int64_t i0 = 0; i0 < n4; i0 += static_cast<int64_t>(kBatch) * kTopkThreads) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * kTopkThreads + threadIdx.x;
+      v[u] = i < n4 ? g4[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t j = 4 * (i0 + static_cast<int64_t>(u) * kTopkThreads + threadIdx.x);
+      const uint32_t kk[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j + c < n) visit(j + c, kk[c]);
+    }
+  }
+}
+
 // The radix path after the first digit (prefix = that digit << 21): the
 // other two digits (bits 10..20, then 0..9) over the streamed keys; then,
 // when the threshold key's bucket is not taken whole, a selection on the low
 // `shift` bits of the scores that the keys dropped; then the in-order
 // compaction: every candidate above the threshold, and of those equal to it
 // the first `take` by position.
-__device__ void topk_radix(TopkShared &sh, const int64_t *sc, const uint32_t *gk, int64_t nst, int64_t P,
-                           int64_t j1, unsigned long long base, int shift, uint32_t prefix, int k_rem, int eq,
-                           int k_top, int32_t *out) {
+// The histogram passes stream the keys coalesced (for_all_ws) with one LDS
+// atomic per key; the counts and the compaction walk each thread's own
+// positions in order (for_own_ws).
+__device__ void topk_radix(TopkShared &sh, const int64_t *sc, const uint32_t *gk, int64_t n, int64_t nst,
+                           int64_t P, int64_t j1, unsigned long long base, int shift, uint32_t prefix, int k_rem,
+                           int eq, int k_top, int32_t *out) {
   uint32_t *wh = sh.whist[threadIdx.x >> 7];
   uint32_t pmask = 0x7FFu << 21;
   auto off = [&](long long sv) -> unsigned long long { return ordered(sv) - base; };
@@ -919,8 +931,8 @@ __device__ void topk_radix(TopkShared &sh, const int64_t *sc, const uint32_t *gk
     const uint32_t dm = (1u << nbt) - 1u;
     clear_whist(sh);
     __syncthreads();
-    for_own([&](int64_t, uint32_t key, bool ok) {
-      hist_add(wh, ok && (key & pmask) == prefix, (key >> sft) & dm);
+    for_all_ws(gk, n, [&](int64_t, uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&wh[(key >> sft) & dm], 1u);
     });
     __syncthreads();
     reduce_whist(sh);
@@ -943,15 +955,11 @@ __device__ void topk_radix(TopkShared &sh, const int64_t *sc, const uint32_t *gk
       const int sh2 = top - bits;
       clear_whist(sh);
       __syncthreads();
-      for_own([&](int64_t j, uint32_t key, bool ok) {
-        bool m = false;
-        uint32_t d = 0;
-        if (ok && key == kappa) {
+      for_all_ws(gk, n, [&](int64_t j, uint32_t key) {
+        if (key == kappa) {
           const unsigned long long lo = off(sc[j]) & lbits;
-          m = (lo & lowmask) == lowpre;
-          d = static_cast<uint32_t>(lo >> sh2) & ((1u << bits) - 1u);
+          if ((lo & lowmask) == lowpre) atomicAdd(&wh[static_cast<uint32_t>(lo >> sh2) & ((1u << bits) - 1u)], 1u);
         }
-        hist_add(wh, m, d);
       });
       __syncthreads();
       reduce_whist(sh);
@@ -1134,7 +1142,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
   unsigned long long base;
   int shift, lsh;
   unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, lsh, sh.mm);
-  topk_radix(sh, sc, gk, nst, P, j1, base, shift, d1 << 21, k_rem, eq, k_top, out);
+  topk_radix(sh, sc, gk, n, nst, P, j1, base, shift, d1 << 21, k_rem, eq, k_top, out);
 }
 
 // 3. Per (unit, chunk of the keys launch), when the select launch left the
@@ -1264,9 +1272,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
     for (int i = 0; i < kSmallP; ++i)
       key[i] = score_key(u[i] - base, shift, lsh) & (0u - ((vmask >> i) & 1u));
   }
+  // Plain LDS atomics, one per key: the ballot-merged hist_add costs more
+  // instructions per key than the same-bin collisions it saves, even with a
+  // crowded first digit (1 x 32K, 8 units: top-k 23.8 -> 19.0 us on N(0, 1)
+  // scores, 26.7 -> 22.4 with planted columns, 79 -> 78 with columns that
+  // crowd the bulk into a few first digits).
   uint32_t *wh = sh.whist[threadIdx.x >> 7];
 #pragma unroll
-  for (int i = 0; i < kSmallP; ++i) hist_add(wh, key[i] != 0u, key[i] >> 21);
+  for (int i = 0; i < kSmallP; ++i)
+    if (key[i] != 0u) atomicAdd(&wh[key[i] >> 21], 1u);
   __syncthreads();
   reduce_whist(sh);
   __syncthreads();
@@ -1302,13 +1316,57 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
       out[pos++] = static_cast<int32_t>(jw + static_cast<uint32_t>(__builtin_ctz(tmask)));
     return;
   }
-  // a crowded first digit: the keys into the workspace, then the radix path
+  // A crowded first digit: the other two digits (bits 10..20, then 0..9)
+  // from the keys in registers, giving the key kappa of the k_top-th largest
+  // and the number `take` of keys equal to kappa that are taken.
+  const int k_rem1 = k_rem, eq1 = eq;           // after the first digit
+  uint32_t prefix = d1 << 21, pmask = 0x7FFu << 21;
+#pragma unroll 1
+  for (int ps = 0; ps < 2; ++ps) {
+    const int sft = ps == 0 ? 10 : 0;
+    const int nbt = ps == 0 ? 11 : 10;
+    const uint32_t dm = (1u << nbt) - 1u;
+    clear_whist(sh);
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kSmallP; ++i)
-    if (key[i] != 0u) gk[j0 + i] = key[i];
-  __threadfence_block();
-  __syncthreads();
-  topk_radix(sh, sc, gk, nst, P, j1, base, shift, d1 << 21, k_rem, eq, k_top, out);
+    for (int i = 0; i < kSmallP; ++i)
+      if (key[i] != 0u && (key[i] & pmask) == prefix) atomicAdd(&wh[(key[i] >> sft) & dm], 1u);
+    __syncthreads();
+    reduce_whist(sh);
+    __syncthreads();
+    const int d = find_digit(1 << nbt, &k_rem, &eq, sh);
+    prefix |= static_cast<uint32_t>(d) << sft;
+    pmask |= dm << sft;
+  }
+  const uint32_t kappa = prefix;
+  const int take = k_rem;
+  if (eq > take && shift > 0) {
+    // keys equal to kappa that the shift made equal and that are not all
+    // taken: the workspace radix path refines on the dropped bits
+#pragma unroll
+    for (int i = 0; i < kSmallP; ++i)
+      if (key[i] != 0u) gk[j0 + i] = key[i];
+    __threadfence_block();
+    __syncthreads();
+    topk_radix(sh, sc, gk, n, nst, P, j1, base, shift, d1 << 21, k_rem1, eq1, k_top, out);
+    return;
+  }
+  // keys above kappa are taken; keys equal to kappa are equal scores (or all
+  // taken), of which the first `take` by position are taken
+  uint32_t sure = 0, tie = 0;
+#pragma unroll
+  for (int i = 0; i < kSmallP; ++i) {
+    sure |= static_cast<uint32_t>(key[i] > kappa) << i;
+    tie |= static_cast<uint32_t>(key[i] == kappa) << i;
+  }
+  int tot;
+  const int tie_before = block_exclusive_scan(__popc(tie), sh.scan, &tot);
+  uint32_t tmask = sure;
+  for (int r = tie_before; tie != 0u && r < take; ++r, tie &= tie - 1u) tmask |= tie & (0u - tie);
+  int pos = block_exclusive_scan(__popc(tmask), sh.scan, &tot);
+  const uint32_t jw = opaque_v(static_cast<uint32_t>(j0));
+  for (; tmask != 0u && pos < k_top; tmask &= tmask - 1u)
+    out[pos++] = static_cast<int32_t>(jw + static_cast<uint32_t>(__builtin_ctz(tmask)));
 }
 
 // The score kernels have written their partial ranges to topk_mm(tws, units, n).

@@ -99,6 +99,36 @@ def test_detect_wide_range(method, n, ce, k_top):
     assert np.array_equal(got_idx, want_idx)
 
 
+@pytest.mark.parametrize("n", [3000, 34000])
+def test_detect_refine_on_dropped_bits(n):
+    """Scores wider than the 32-bit keys by about 10 bits (QSUM form, exact
+    in fp64), with k_top placed where the k-th and the (k+1)-th largest
+    scores share a key: the top-k must refine on the bits the keys dropped,
+    in the one-launch and the three-launch paths."""
+    B, Hq, Hkv, D, R = 1, 4, 1, 128, 8
+    say(f"detect refine n={n}")
+    rng = np.random.default_rng(n + 11)
+    q = synth.round_dtype(np.rint(rng.standard_normal((B, Hq, R, D)) * 16) / 16, "bf16")
+    K = synth.round_dtype(np.rint(rng.standard_normal((B, Hkv, n, D)) * 16) / 16, "bf16")
+    ce = n - 50
+    qs = q[0].sum(axis=(0, 1))
+    K[0, 0, rng.choice(ce, 20, replace=False)] = 32768.0 * np.where(qs >= 0, 1.0, -1.0)
+    _, sc = detect.detect(q, K, ce, 0)
+    v = sc[0, 0].astype(object)
+    lo, hi = min(v), max(v)
+    nbits = int(hi - lo).bit_length()
+    assert nbits > 38, nbits                            # keys drop nbits - 31 low bits
+    shift = nbits - 31
+    order = sorted(range(ce), key=lambda j: (-v[j], j))
+    keys = [(v[j] - lo) >> shift for j in order]
+    cut = next(i for i in range(30, ce - 1) if keys[i] == keys[i + 1] and v[order[i]] != v[order[i + 1]])
+    k_top = cut + 1                                     # the k-th and (k+1)-th share a key, scores differ
+    want_idx, want_sc = detect.detect(q, K, ce, k_top)
+    got_idx, got_sc = _run(q, K, ce, k_top, hq.HQ_DETECT_QSUM, "bf16")
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+
+
 def test_accumulate_ring_and_cadence():
     say("detect accumulate ring")
     B, Hq, Hkv, D, R, n, ce, kt = 1, 4, 2, 128, 8, 300, 280, 14
