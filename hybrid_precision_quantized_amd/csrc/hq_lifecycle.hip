@@ -300,21 +300,9 @@ __global__ __launch_bounds__(kUpdThreads) void vl_update_kernel(UpdParams P) {
     for (int b = tid; b < kBins; b += kUpdThreads) hist[b] = 0;
     if (tid == 0) n_list = 0;
     __syncthreads();
-    // skewed scores put many candidates in one bin: the lanes of a wave
-    // that share the digit of the first active lane add with one atomic
-    for (int i0 = 0; i0 < n; i0 += kUpdThreads) {
-      const int i = i0 + tid;
-      const bool act = i < n && alive[i];
-      const int dg = act ? static_cast<int>(rank_bits(key[i] - kmin, pos[i], sh, w)) : -1;
-      const unsigned long long am = __ballot(act);
-      if (am) {
-        const int lead = __ffsll(static_cast<long long>(am)) - 1;
-        const int d0 = __shfl(dg, lead, 64);
-        const unsigned long long same = __ballot(act && dg == d0);
-        if (lane == lead) atomicAdd(&hist[d0], __popcll(same));
-        else if (act && dg != d0) atomicAdd(&hist[dg], 1);
-      }
-    }
+    // one plain LDS atomic per alive candidate
+    for (int i = tid; i < n; i += kUpdThreads)
+      if (alive[i]) atomicAdd(&hist[rank_bits(key[i] - kmin, pos[i], sh, w)], 1);
     __syncthreads();
     if (tid < 64) {
       // lane l holds the 64 bins kBins - 1 - 64 l down to kBins - 64 (l + 1)
