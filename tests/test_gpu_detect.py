@@ -167,6 +167,42 @@ def test_detect_full_workload(name, method):
     assert np.array_equal(got_idx, want_idx)
 
 
+def test_detect_qwen128k_sampled():
+    """Batch 16 x 128K context, MATMUL form: the GPU scores and selects for
+    every (b, KV head) (the resident column-sum kernel and the keys, select
+    and write launches of the top-k); the oracle checks KV heads 0 and 7 of
+    sequence 0 and KV head 3 of sequence 15 (int64 scores and index sets,
+    exact)."""
+    w = synth.WORKLOADS["qwen128k"]
+    say("detect qwen128k (upload)")
+    dt = TORCH_DT[w.dtype]
+    Kd = torch.empty((w.B, w.Hkv, w.T, w.D), dtype=dt, device="cuda")
+    for b in range(w.B):
+        kb = np.stack(synth._parallel(lambda h: synth.keys(w, b, h), [(h,) for h in range(w.Hkv)]))
+        Kd[b].copy_(to_dev(kb, w.dtype))
+    q = synth.all_query_histories(w)
+    ce = w.T - w.W
+    idx = torch.full((w.B, w.Hkv, w.k), -1, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((w.B, w.Hkv, ce), dtype=torch.int64, device="cuda")
+    ws = torch.zeros(hq.hq_detect_workspace_size(w.B, w.Hkv, ce, w.k), dtype=torch.uint8, device="cuda")
+    say("detect qwen128k (run)")
+    ran = hq.hq_detect_vlines(None, to_dev(q, w.dtype), w.B, w.Hq, w.Hkv, w.D, w.R, 0, True, Kd, w.T, ce, w.k,
+                              hq.HQ_DETECT_MATMUL, idx, sc, ws)
+    torch.cuda.synchronize()
+    assert ran
+    del Kd
+    got_idx, got_sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for b, h in [(0, 0), (0, 7), (15, 3)]:
+        say(f"detect qwen128k (oracle b={b} h={h})")
+        qh = q[b:b + 1, h * w.G:(h + 1) * w.G]
+        Kh = synth.keys(w, b, h)[None, None]
+        worst = matmul_exact_precondition(qh, Kh, ce)
+        assert worst < 2.0 ** 16, f"inputs outside the exact range of the MFMA form: {worst}"
+        want_idx, want_sc = detect.detect(qh, Kh, ce, w.k)
+        assert np.array_equal(got_sc[b, h], want_sc[0, 0]), (b, h)
+        assert np.array_equal(got_idx[b, h], want_idx[0, 0]), (b, h)
+
+
 def _run_cache(q_acc, K, cand_end, k_top, dtype, T, W):
     """hq_detect_vlines_cache over a cache whose INT4 planes were written by
     hq_quantize_kv from K (positions [0, T - W))."""
