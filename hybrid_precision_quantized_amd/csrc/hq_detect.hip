@@ -1207,17 +1207,18 @@ __global__ __launch_bounds__(kWrThreads) void topk_write_kernel(const uint32_t *
   }
 }
 
-// 1 + 2 in one launch for units with at most kSmallN candidates: one
-// workgroup per unit; thread t loads the scores of its positions [t P, t P +
-// P), P <= kSmallP. The unit's range comes from the score kernels' partial
-// ranges; the keys then stay in registers and their top-11-bit histogram is
-// built in LDS. A
-// boundary bucket of at most kSmallBucket keys is collected with its scores
-// and ranked by (score, position); a member's key register then holds its
-// slot in the bucket, and the selection (digit above, or a member ranked
-// below k_rem) becomes a bit mask per thread, whose population is scanned
-// and whose set bits are written in order. A larger bucket
-// writes the keys to the workspace and takes the radix path.
+// The whole top-k in one launch for units with at most kSmallN candidates:
+// one workgroup per unit; thread t loads the scores of its positions [t P,
+// t P + P), P <= kSmallP. The unit's range comes from the score kernels'
+// partial ranges; the keys then stay in registers and their top-11-bit
+// histogram is built in LDS. A boundary bucket of at most kSmallBucket keys
+// is collected with its scores and ranked by (score, position); a member's
+// key register then holds its slot in the bucket, and the selection (digit
+// above, or a member ranked below k_rem) becomes a bit mask per thread,
+// whose population is scanned and whose set bits are written in order. A
+// larger bucket takes the next two digits from the registers, and refines
+// on the score bits the keys dropped when it must (members' scores
+// reloaded); the workspace is not used.
 constexpr int kSmallP = 32;
 constexpr int64_t kSmallN = static_cast<int64_t>(kTopkThreads) * kSmallP;
 // units up to this many candidates take the one-launch kernel; larger ones
@@ -1234,14 +1235,12 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
 }
 __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t *__restrict__ scores,
                                                                   const unsigned long long *__restrict__ mm,
-                                                                  uint32_t *__restrict__ keys, int64_t n,
-                                                                  int np, int k_top, int32_t *__restrict__ idx_out) {
+                                                                  int64_t n, int np, int k_top,
+                                                                  int32_t *__restrict__ idx_out) {
   __shared__ TopkShared sh;
   const int unit = blockIdx.x;
   if (k_top == 0) return;
   const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
-  const int64_t nst = key_stride(n);
-  uint32_t *gk = keys + static_cast<int64_t>(unit) * nst;
   int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
   const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // <= kSmallP
   const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
@@ -1412,8 +1411,7 @@ void launch_topk(hipStream_t st, int units, const int64_t *scores, void *tws, in
   int *ctl = reinterpret_cast<int *>(w8 + L.ctl);
   const int np = topk_partials(n);
   if (n <= kTopkOneLaunchN && !skewed) {
-    hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, mm, keys, n, np, k_top,
-                       idx_out);
+    hipLaunchKernelGGL(topk_small_kernel, dim3(units), dim3(kTopkThreads), 0, st, scores, mm, n, np, k_top, idx_out);
     return;
   }
   const unsigned nb = static_cast<unsigned>(units) * c.nbu;
