@@ -722,7 +722,7 @@ __device__ int find_digit(int nb, int *k_rem, int *cnt, SH &sh) {
   return sh.sel[0];
 }
 
-// Chunking of a unit's candidates over the blocks of the first two launches.
+// Chunking of a unit's candidates over the blocks of the keys and write launches.
 constexpr int kTkBlock = 256;
 constexpr int kTkMaxBlocks = 32;
 static_assert(kTkMaxBlocks <= 32, "TopkShared::cnt and the select kernel's per-chunk sums hold 32 chunks");
@@ -1271,7 +1271,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_small_kernel(const int64_t 
     for (int i = 0; i < kSmallP; ++i)
       key[i] = score_key(u[i] - base, shift, lsh) & (0u - ((vmask >> i) & 1u));
   }
-  // Plain LDS atomics, one per key: the ballot-merged hist_add costs more
+  // Plain LDS atomics, one per key: a ballot-merged update (one atomic for
+  // the lanes that share the first active lane's bin) costs more
   // instructions per key than the same-bin collisions it saves, even with a
   // crowded first digit (1 x 32K, 8 units: top-k 23.8 -> 19.0 us on N(0, 1)
   // scores, 26.7 -> 22.4 with planted columns, 79 -> 78 with columns that
