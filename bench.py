@@ -627,7 +627,9 @@ def main_ablation(args):
       k4v4        every position INT4 (k = W = 0);
       bf16        every position 16-bit (W = T), i.e. plain attention.
     For each: the algorithmic bytes of one hq_decode_attn call, its time
-    (HIP events, caches rotated past the Infinity Cache), the bytes held in
+    (HIP events around 100 calls replayed from a HIP graph, caches rotated
+    past the Infinity Cache; the same calls launched one by one are
+    reported beside it), the bytes held in
     the cache for the layer, and the output error against exact attention
     (fp32 on the GPU over the 16-bit keys and values)."""
     import torch
@@ -709,9 +711,14 @@ def main_ablation(args):
             hq.hq_decode_attn(q, Hq, descs[i % copies], 0.0, 0, out, lse, ws)
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n
+        us_stream = e0.elapsed_time(e1) * 1e3 / n
+        # the same calls replayed from a HIP graph: the GPU's time per call
+        # without the host's launch cost (which bounds the small settings when
+        # the calls are launched one by one)
+        us = graph_decode_calls_us(torch, hq, caches, descs, q[None], Hq, out, lse, ws, 0, n, stream, None)
         rows.append({"setting": name, "k": kk, "W": ww, "drop_int4": bool(flags),
                      "algorithmic_bytes": int(dec_bytes), "us_per_call": round(us, 2),
+                     "us_per_call_stream_launched": round(us_stream, 2),
                      "gbs": round(dec_bytes / (us * 1e-6) / 1e9, 1), "cache_bytes": int(held),
                      "max_abs_err_over_rms": round(max_rel, 5), "rel_l2_err": round(l2, 6)})
         del caches, descs, ws
