@@ -123,6 +123,46 @@ def test_decode_small(case):
     _check(got, _oracle(w, K, V, q, vl))
 
 
+def _random_cases(n, seed):
+    """n decode configurations drawn from a fixed seed: batch 1-3, 1-8 KV
+    heads, GQA group 1-16, D 64 or 128, contexts 1-2600 with every window
+    and VL budget from 0 up, fp32 / bf16 / fp16, automatic or forced split
+    counts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        if Hkv * G > 64:
+            continue
+        D = int(rng.choice([64, 128]))
+        T = int(rng.integers(1, 2600))
+        W = int(rng.choice([0, 1, 16, 128, T, int(rng.integers(0, T + 1))]))
+        W = min(W, T)
+        k = int(rng.integers(0, min(T - W, 200) + 1))
+        dtype = str(rng.choice(["f32", "bf16", "f16"]))
+        splits = int(rng.choice([0, 0, 1, 3, 17]))
+        cases.append((int(rng.integers(1, 4)), Hkv * G, Hkv, D, T, W, k, dtype, splits))
+    return cases
+
+
+RANDOM_CASES = _random_cases(14, 2024)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[str(c) for c in RANDOM_CASES])
+def test_decode_random_shapes(case):
+    """Seeded random shapes (including empty windows and VL sets, windows
+    covering the whole context and forced split counts) against the
+    oracle."""
+    B, Hq, Hkv, D, T, W, k, dtype, splits = case
+    w = _workload(B, Hq, Hkv, D, T, W, k, dtype, seed=zlib.crc32(str(case).encode()) % 10000 + 20000)
+    say(f"decode random {case}")
+    K, V, q = synth.all_keys(w), synth.all_values(w), synth.all_queries(w)
+    vl = _vl_random(w)
+    got = _gpu_decode(w, K, V, q, vl, n_splits=splits)
+    _check(got, _oracle(w, K, V, q, vl))
+
+
 def test_decode_tiny_workload_with_detected_lines():
     w = synth.WORKLOADS["tiny"]
     say("decode tiny workload")

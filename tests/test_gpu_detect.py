@@ -129,6 +129,51 @@ def test_detect_refine_on_dropped_bits(n):
     assert np.array_equal(got_idx, want_idx)
 
 
+def _random_detect_cases(n, seed):
+    """n detector configurations drawn from a fixed seed: batch 1-2, 1-4 KV
+    heads, group 1-8, D 64 or 128, 1-64 ring slots, 1-36000 candidates
+    (both sides of the one-launch top-k limit), k from 0 to all, score
+    spreads from heavy ties to wide ranges, bf16 or fp16."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128]))
+        R = int(rng.choice([1, 5, 16, 64]))
+        ce = int(rng.choice([int(rng.integers(1, 3000)), int(rng.integers(3000, 36000))]))
+        n_rows = ce + int(rng.integers(0, 200))
+        k = int(rng.choice([0, 1, ce, int(rng.integers(0, ce + 1)), max(1, ce // 20)]))
+        spread = float(rng.choice([0.0625, 0.25, 1.0, 2.0]))
+        dtype = str(rng.choice(["bf16", "f16"]))
+        cases.append((int(rng.integers(1, 3)), Hkv * G, Hkv, D, R, n_rows, ce, k, dtype, spread))
+    return cases
+
+
+RANDOM_DETECT = _random_detect_cases(12, 77)
+
+
+@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("case", RANDOM_DETECT, ids=[str(c) for c in RANDOM_DETECT])
+def test_detect_random_shapes(method, case):
+    """Seeded random shapes on the 2^-4 grid: int64 scores and index sets
+    bit for bit against the oracle."""
+    B, Hq, Hkv, D, R, n, ce, k_top, dtype, spread = case
+    say(f"detect random method={method} {case}")
+    rng = np.random.default_rng(zlib.crc32(str(case).encode()))
+    q = np.rint(rng.standard_normal((B, Hq, R, D)) * spread * 16) / 16
+    K = np.rint(rng.standard_normal((B, Hkv, n, D)) * spread * 16) / 16
+    if dtype == "bf16":
+        q, K = synth.round_dtype(q, "bf16"), synth.round_dtype(K, "bf16")
+    else:
+        q = q.astype(np.float16).astype(np.float32)
+        K = K.astype(np.float16).astype(np.float32)
+    want_idx, want_sc = detect.detect(q, K, ce, k_top)
+    got_idx, got_sc = _run(q, K, ce, k_top, method, dtype)
+    assert np.array_equal(got_sc, want_sc)
+    assert np.array_equal(got_idx, want_idx)
+
+
 def test_accumulate_ring_and_cadence():
     say("detect accumulate ring")
     B, Hq, Hkv, D, R, n, ce, kt = 1, 4, 2, 128, 8, 300, 280, 14
