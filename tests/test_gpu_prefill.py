@@ -99,6 +99,39 @@ def test_prefill_small(B, Hq, Hkv, T, W, k, dtype, form):
     _compare(_run(w, q, K, V, vl, form), _oracle(w, q, K, V, vl, rows), rows)
 
 
+def _random_prefill_cases(n, seed):
+    """n prompts drawn from a fixed seed: batch 1-2, 1-4 KV heads, group 1-8,
+    1-1200 tokens (ragged against the 32-key and 128-query tiles), windows
+    from 0 to beyond the prompt, 0-60 vertical lines, bf16 or fp16."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        T = int(rng.integers(1, 1200))
+        W = int(rng.choice([0, 1, 31, 32, 33, 128, int(rng.integers(0, T + 2))]))
+        k = int(rng.integers(0, min(T, 60) + 1))
+        cases.append((int(rng.integers(1, 3)), Hkv * G, Hkv, T, W, k, str(rng.choice(["bf16", "f16"]))))
+    return cases
+
+
+RANDOM_PREFILL = _random_prefill_cases(8, 31)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("case", RANDOM_PREFILL, ids=[str(c) for c in RANDOM_PREFILL])
+def test_prefill_random_shapes(case, form):
+    """Seeded random prompts, every output row against the oracle."""
+    B, Hq, Hkv, T, W, k, dtype = case
+    w = synth.Workload("pfr", 5000 + T + 7 * W + 13 * k, B=B, Hq=Hq, Hkv=Hkv, D=128, T=T, W=W, k=k,
+                       dtype=dtype, n_plant=max(1, T // 50))
+    say(f"prefill random {case} {form}")
+    q, K, V = _inputs(w)
+    vl = _vl_random(w, k)
+    rows = np.arange(T)
+    _compare(_run(w, q, K, V, vl, form), _oracle(w, q, K, V, vl, rows), rows)
+
+
 @pytest.mark.parametrize("form", FORMS)
 def test_prefill_extremes(form):
     """Plain (off-grid) rows with groups near the fp16 limit (|x| up to 6e4),
