@@ -253,7 +253,10 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
     // every row is in LDS: no staging inside the loop. (Splitting the tiles
     // into parts computed in turn, so that the first part's MFMAs overlap
     // the later parts' loads, re-reads every A fragment per part and was
-    // slower: 20.6 -> 21.6 us with 2 parts, 23.5 us with 4.)
+    // slower: 20.6 -> 21.6 us with 2 parts, 23.5 us with 4. Issuing a
+    // part's K loads only once the previous part's had landed, so that the
+    // first parts arrive first chip-wide, measured 20.2-20.5 us with 1, 2
+    // and 4 parts alike.)
     for (int st = 0; st < stages; ++st) {
 #pragma unroll
       for (int sub = 0; sub < kStageRows / 16; ++sub) {
