@@ -113,12 +113,18 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
 
 
 constexpr int kStageRows = 128;
+constexpr bool kResWide8 = true;   // 512-column resident blocks as 8 waves of 4 tiles (else 4 of 8)
 constexpr int kRowPad = 8;        // halves
 
-// Grid: units * ceil(n / (64 NT)) blocks of 4 waves on the 16x16x32 MFMA;
-// wave w of block cb owns the NT 16-column tiles 4 NT cb + NT w + t with their
-// K fragments in registers (NT = 8 while the grid keeps two blocks per CU,
-// else 4). MFMA kc covers channels 32 kc + 8 g .. + 7 for lane group g = lane
+// Grid: units * ceil(n / (16 NT WPB)) blocks of WPB waves on the 16x16x32
+// MFMA; wave w of block cb owns the NT 16-column tiles WPB NT cb + NT w + t
+// with their K fragments in registers (512 columns per block while the grid
+// keeps two blocks per CU, else 256; resident 512-column blocks run as 8
+// waves of 4 tiles, four waves per SIMD, so that waves whose K landed early
+// run their MFMAs while others still load: 20.4 -> 19.3 us at 1 x 32K, 8 KV
+// heads, against 4 waves of 8 tiles, whose per-wave stamps showed each wave
+// loading for ~8 us, then 5.6 us of MFMAs, then 1.5 us of epilogue, in
+// lockstep across the chip). MFMA kc covers channels 32 kc + 8 g .. + 7 for lane group g = lane
 // / 16, the same order in both operands, so one K load reads 64 contiguous
 // bytes of each of 16 rows (the 32x32 operand layout reads 32 bytes of each
 // of 32 rows, which stalled the texture path). The unit's query rows are
@@ -144,22 +150,24 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 }
-template <int D, int DT, int NT, bool RES>
-__global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *__restrict__ q_acc,
+template <int D, int DT, int NT, bool RES, int WPB>
+__global__ __launch_bounds__(64 * WPB, WPB / 2) void mfma16_colsum_kernel(const uint16_t *__restrict__ q_acc,
                                                             const uint16_t *__restrict__ k, int Hq,
                                                             int Hkv, int R, int64_t k_rows,
                                                             int64_t cand_end,
                                                             int64_t *__restrict__ scores,
                                                             unsigned long long *__restrict__ mm) {
   constexpr int KC = D / 32;                       // MFMAs per 16x16 tile and row chunk
-  constexpr int CPB = 64 * NT;                     // columns per block
+  constexpr int NTH = 64 * WPB;                    // threads per block
+  constexpr int CPB = 16 * NT * WPB;               // columns per block
   constexpr int GPB = CPB / 256;                   // 256-candidate score partials per block
-  constexpr int WPG = 4 / GPB;                     // waves per partial
+  constexpr int WPG = WPB / GPB;                   // waves per partial
   static_assert(NT == 4 || NT == 8, "tiles per wave");
+  static_assert(WPB == 4 || WPB == 8, "waves per block");
   constexpr int ROWV = D / 8;
-  constexpr int PER_T = kStageRows * ROWV / 256;
+  constexpr int PER_T = kStageRows * ROWV / NTH;
   __shared__ uint16_t qs[2][kStageRows][D + kRowPad];
-  __shared__ unsigned long long rng[4][2];
+  __shared__ unsigned long long rng[WPB][2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g4 = lane >> 4;                        // lane group: channels 8 g4 .. 8 g4 + 7 of each 32
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   auto load_stage = [&](int st, uint4 *bb) {
 #pragma unroll
     for (int e = 0; e < PER_T; ++e) {
-      const int idx = e * 256 + threadIdx.x;
+      const int idx = e * NTH + threadIdx.x;
       const int row = idx / ROWV, c8 = idx % ROWV;
       const int grow = st * kStageRows + row;
       if constexpr (RES) {
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void mfma16_colsum_kernel(const uint16_t *_
   auto store_stage = [&](int slot, const uint4 *bb) {
 #pragma unroll
     for (int e = 0; e < PER_T; ++e) {
-      const int idx = e * 256 + threadIdx.x;
+      const int idx = e * NTH + threadIdx.x;
       const int row = idx / ROWV, c8 = idx % ROWV;
       *reinterpret_cast<uint4 *>(&qs[slot][row][c8 * 8]) = bb[e];
     }
@@ -1815,9 +1823,10 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
         // RES: the unit's query rows fit the two LDS slots at once, and its
         // candidate rows fit a buffer resource's 32-bit byte range
         const bool res = (Hq / Hkv) * R <= 2 * kStageRows && cand_end * D * 2 < (int64_t{1} << 31);
-#define HQ_C16R(DD, TT, NN) do { if (res) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, true>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
-                                 else hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, false>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); } while (0)
-#define HQ_C16(DD, TT) do { if (wide) HQ_C16R(DD, TT, 8); else HQ_C16R(DD, TT, 4); } while (0)
+#define HQ_C16R(DD, TT, NN) do { if (res) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, true, 4>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
+                                 else hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, false, 4>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); } while (0)
+#define HQ_C16(DD, TT) do { if (wide && res && kResWide8) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, 4, true, 8>), grid, dim3(512), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
+                            else if (wide) HQ_C16R(DD, TT, 8); else HQ_C16R(DD, TT, 4); } while (0)
         if (D == 128) {
           if (dtype == HQ_BF16) HQ_C16(128, HQ_BF16); else HQ_C16(128, HQ_F16);
         } else {
