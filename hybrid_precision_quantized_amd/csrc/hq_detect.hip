@@ -801,22 +801,59 @@ __device__ __forceinline__ void block_minmax(unsigned long long &mn, unsigned lo
     }
   }
 }
+// The unit's key parameters from its score range [mn, mx]: keys 1 + (((score
+// - mn) >> shift) << lsh), so the range spans bits 0..30 whatever its width
+// (a wider one drops its low bits, a narrower one is moved up so that the
+// first digit splits it as finely as a wide one), the largest key is at most
+// 2^31, and key 0 marks no position.
+__device__ __forceinline__ void key_params(unsigned long long mn, unsigned long long mx, int &shift, int &lsh) {
+  const unsigned long long range = mx - mn;
+  const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
+  shift = nbits > 31 ? nbits - 31 : 0;
+  lsh = nbits < 31 ? 31 - nbits : 0;
+}
+// Min and max over the nbu partial ranges {mn, mx} at mm, by one wave: the
+// partials come through a buffer resource in batches of kRangeBatch per
+// lane, every load of a batch in flight at once (a loop with a load and a
+// use per step waits for every load issued before it, the caller's too).
+// Every lane ends with the result; the reduction order is fixed.
+constexpr int kRangeBatch = 8;
+__device__ __forceinline__ void wave_range(const unsigned long long *mm, int nbu, unsigned long long &mn,
+                                           unsigned long long &mx) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned long long *>(mm), static_cast<short>(0), nbu * 16, 0x00020000);
+  mn = ~0ull;
+  mx = 0;
+  for (int i0 = 0; i0 < nbu; i0 += 64 * kRangeBatch) {
+    uint4 v[kRangeBatch];
+#pragma unroll
+    for (int e = 0; e < kRangeBatch; ++e)
+      v[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, static_cast<uint32_t>(i0 + e * 64 + lane) * 16u, 0, 0));
+#pragma unroll
+    for (int e = 0; e < kRangeBatch; ++e) {
+      const bool ok = i0 + e * 64 + lane < nbu;
+      const unsigned long long a = ok ? (static_cast<unsigned long long>(v[e].y) << 32 | v[e].x) : ~0ull;
+      const unsigned long long c = ok ? (static_cast<unsigned long long>(v[e].w) << 32 | v[e].z) : 0ull;
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
+    mn = a < mn ? a : mn;
+    mx = c > mx ? c : mx;
+  }
+}
 // the unit's range from its nbu partials, by the first wave (every block
 // and every launch reduces them in the same way)
 __device__ __forceinline__ void unit_range(const unsigned long long *mm, int nbu, unsigned long long &base,
                                            int &shift, int &lsh, unsigned long long *red) {
   if (threadIdx.x < 64) {
-    unsigned long long mn = ~0ull, mx = 0;
-    for (int i = threadIdx.x; i < nbu; i += 64) {
-      mn = mm[2 * i] < mn ? mm[2 * i] : mn;
-      mx = mm[2 * i + 1] > mx ? mm[2 * i + 1] : mx;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
-      mn = a < mn ? a : mn;
-      mx = c > mx ? c : mx;
-    }
+    unsigned long long mn, mx;
+    wave_range(mm, nbu, mn, mx);
     if (threadIdx.x == 0) {
       red[0] = mn;
       red[1] = mx;
@@ -824,14 +861,7 @@ __device__ __forceinline__ void unit_range(const unsigned long long *mm, int nbu
   }
   __syncthreads();
   base = red[0];
-  const unsigned long long range = red[1] - red[0];
-  // keys 1 + (((score - min) >> shift) << lsh): the range spans bits 0..30
-  // whatever its width (a wider one drops its low bits, a narrower one is
-  // moved up so that the first digit splits it as finely as a wide one), the
-  // largest key is at most 2^31, and key 0 marks no position
-  const int nbits = range == 0 ? 0 : 64 - __clzll(static_cast<long long>(range));
-  shift = nbits > 31 ? nbits - 31 : 0;
-  lsh = nbits < 31 ? 31 - nbits : 0;
+  key_params(red[0], red[1], shift, lsh);
   __syncthreads();
 }
 __device__ __forceinline__ uint32_t score_key(unsigned long long off, int shift, int lsh) {
@@ -850,21 +880,39 @@ __global__ __launch_bounds__(kTkBlock) void topk_keys_kernel(const int64_t *__re
   const int64_t *sc = scores + static_cast<int64_t>(unit) * n;
   uint32_t *kk = keys + static_cast<int64_t>(unit) * key_stride(n);
   for (int i = threadIdx.x; i < (kTkBlock / 64) * kBins; i += kTkBlock) (&h[0][0])[i] = 0u;
+  const int64_t c0 = blk * ch;
+  const int64_t c1 = c0 + ch < n ? c0 + ch : n;
+  const int cn = static_cast<int>(c1 > c0 ? c1 - c0 : 0);           // this chunk's candidates
+  // The chunk's scores come through a buffer resource, kKeysBatch per
+  // thread in flight at once (loads past the chunk return 0 and are not
+  // used); the first batch flies while the range is reduced. (One guarded
+  // load per step waited for each load in turn.)
+  constexpr int kKeysBatch = 8;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int64_t *>(sc + c0), static_cast<short>(0), cn * 8, 0x00020000);
+  unsigned long long v[kKeysBatch];
+  auto load_batch = [&](int q0) {
+#pragma unroll
+    for (int e = 0; e < kKeysBatch; ++e)
+      v[e] = __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(
+                                    rs, static_cast<uint32_t>(q0 + e * kTkBlock + threadIdx.x) * 8u, 0, 0));
+  };
+  load_batch(0);
   unsigned long long base;
   int shift, lsh;
   unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, lsh, red);
-  const int64_t c0 = blk * ch;
-  const int64_t c1 = c0 + ch < n ? c0 + ch : n;
   uint32_t *wh = h[threadIdx.x >> 6];
-  for (int64_t jb = c0; jb < c0 + ch; jb += kTkBlock) {     // same trip count in every thread
-    const int64_t j = jb + threadIdx.x;
-    const bool ok = j < c1;
-    uint32_t key = 0;
-    if (ok) {
-      key = score_key(ordered(sc[j]) - base, shift, lsh);
-      kk[j] = key;
+  for (int q0 = 0; q0 < cn; q0 += kKeysBatch * kTkBlock) {         // same trip count in every thread
+#pragma unroll
+    for (int e = 0; e < kKeysBatch; ++e) {
+      const int q = q0 + e * kTkBlock + static_cast<int>(threadIdx.x);
+      const uint32_t key = score_key(ordered(static_cast<long long>(v[e])) - base, shift, lsh);
+      if (q < cn) {
+        kk[c0 + q] = key;
+        atomicAdd(&wh[key >> 21], 1u);
+      }
     }
-    if (ok) atomicAdd(&wh[key >> 21], 1u);
+    load_batch(q0 + kKeysBatch * kTkBlock);
   }
   __syncthreads();
   uint32_t *bh = bhist + (static_cast<int64_t>(unit) * nbu + blk) * kBins;
