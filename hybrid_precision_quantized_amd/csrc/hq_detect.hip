@@ -1217,36 +1217,61 @@ __global__ __launch_bounds__(kWrThreads) void topk_write_kernel(const uint32_t *
   __shared__ int scan[kWrThreads / 64 + 1];
   const int unit = blockIdx.x / nbu, blk = blockIdx.x % nbu;
   const int *cu = ctl + static_cast<int64_t>(unit) * kCtl;
-  if (k_top == 0 || cu[0] != 0) return;        // uniform over the block
-  const uint32_t d1 = static_cast<uint32_t>(cu[1]);
-  const int off = cu[2 + blk];
+  if (k_top == 0) return;
   const uint32_t *gk = keys + static_cast<int64_t>(unit) * key_stride(n);
   int32_t *out = idx_out + static_cast<int64_t>(unit) * k_top;
   const int64_t c0 = static_cast<int64_t>(blk) * ch;
   const int64_t c1 = c0 + ch < n ? c0 + ch : n;
   const int64_t Q = ((ch + kWrThreads - 1) / kWrThreads + 3) & ~3LL;       // a multiple of 4
   const int64_t b0 = c0 + static_cast<int64_t>(threadIdx.x) * Q;
-  // taken bits of positions [b0 + q0, b0 + q0 + kWrRun); c0 and Q are
-  // multiples of 4, so each 16-byte load stays inside the unit's key stride
-  auto taken = [&](int64_t q0) -> uint32_t {
+  // taken bits of positions [b0 + q0, b0 + q0 + kWrRun): the chunk's keys
+  // come through a buffer resource over whole 16-byte groups (c0 is a
+  // multiple of 4 and the unit's key stride too, so the groups stay inside
+  // it); loads past it return 0 and keys past c1 are masked, so the loads
+  // are branch-free and all in flight at once
+  const int cn = static_cast<int>(c1 > c0 ? c1 - c0 : 0);
+  const __amdgpu_buffer_rsrc_t ks = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(gk + c0), static_cast<short>(0), ((cn + 3) & ~3) * 4, 0x00020000);
+  const uint32_t t0 = static_cast<uint32_t>(threadIdx.x) * static_cast<uint32_t>(Q);
+  auto load_run = [&](int64_t q0, uint4 *v) {
+#pragma unroll
+    for (int i = 0; i < kWrRun / 4; ++i)
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ks, (t0 + static_cast<uint32_t>(q0) + 4u * i) * 4u, 0, 0));
+  };
+  auto run_bits = [&](int64_t q0, const uint4 *v, uint32_t d1) -> uint32_t {
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < kWrRun / 4; ++i) {
-      const int64_t j = b0 + q0 + 4 * i;
-      if (q0 + 4 * i < Q && j < c1) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(gk + j);
-        const uint32_t kk[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t kk[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bool t = j + c < c1 && (kk[c] == 0xFFFFFFFFu || (kk[c] >> 21) > d1);
-          m |= static_cast<uint32_t>(t) << (4 * i + c);
-        }
+      for (int c = 0; c < 4; ++c) {
+        const int64_t q = q0 + 4 * i + c;
+        const bool t = q < Q && t0 + q < cn && (kk[c] == 0xFFFFFFFFu || (kk[c] >> 21) > d1);
+        m |= static_cast<uint32_t>(t) << (4 * i + c);
       }
     }
     return m;
   };
-  int cnt = 0;
-  for (int64_t q0 = 0; q0 < Q; q0 += kWrRun) cnt += __popc(taken(q0));
+  auto taken = [&](int64_t q0, uint32_t d1) -> uint32_t {
+    uint4 v[kWrRun / 4];
+    load_run(q0, v);
+    return run_bits(q0, v, d1);
+  };
+  // the first run's keys are in flight while the select launch's control
+  // words are read (no early return, which the compiler would hoist above
+  // the loads; a block whose unit the select launch wrote itself writes
+  // nothing), and its bits stay in a register for the write pass (at most
+  // one run per thread unless a chunk exceeds kWrThreads kWrRun keys)
+  uint4 v0[kWrRun / 4];
+  load_run(0, v0);
+  const bool mine = cu[0] == 0;                // uniform over the block
+  const uint32_t d1 = static_cast<uint32_t>(cu[1]);
+  const int off = cu[2 + blk];
+  const uint32_t bits0 = run_bits(0, v0, d1);
+  const uint32_t m0 = mine ? bits0 : 0u;
+  int cnt = __popc(m0);
+  for (int64_t q0 = kWrRun; mine && q0 < Q; q0 += kWrRun) cnt += __popc(taken(q0, d1));
   // exclusive scan of the counts over the block
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int inc = cnt;
@@ -1260,8 +1285,10 @@ __global__ __launch_bounds__(kWrThreads) void topk_write_kernel(const uint32_t *
   int pre = inc - cnt;
   for (int i = 0; i < w; ++i) pre += scan[i];
   int pos = off + pre;
-  for (int64_t q0 = 0; q0 < Q; q0 += kWrRun) {
-    for (uint32_t m = taken(q0); m != 0u && pos < k_top; m &= m - 1u)
+  for (uint32_t m = m0; m != 0u && pos < k_top; m &= m - 1u)
+    out[pos++] = static_cast<int32_t>(b0 + __builtin_ctz(m));
+  for (int64_t q0 = kWrRun; mine && q0 < Q; q0 += kWrRun) {
+    for (uint32_t m = taken(q0, d1); m != 0u && pos < k_top; m &= m - 1u)
       out[pos++] = static_cast<int32_t>(b0 + q0 + __builtin_ctz(m));
   }
 }
