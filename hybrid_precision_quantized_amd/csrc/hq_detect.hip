@@ -779,28 +779,6 @@ unsigned long long *topk_mm(void *tws, int64_t units, int64_t n) {
 __device__ __forceinline__ unsigned long long ordered(long long v) {
   return static_cast<unsigned long long>(v) ^ 0x8000000000000000ull;
 }
-// min and max over a 256-thread block, into *mn / *mx of thread 0
-__device__ __forceinline__ void block_minmax(unsigned long long &mn, unsigned long long &mx,
-                                             unsigned long long *red) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const unsigned long long a = __shfl_xor(mn, m, 64), c = __shfl_xor(mx, m, 64);
-    mn = a < mn ? a : mn;
-    mx = c > mx ? c : mx;
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    red[2 * w] = mn;
-    red[2 * w + 1] = mx;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < static_cast<int>(blockDim.x) / 64; ++i) {
-      mn = red[2 * i] < mn ? red[2 * i] : mn;
-      mx = red[2 * i + 1] > mx ? red[2 * i + 1] : mx;
-    }
-  }
-}
 // The unit's key parameters from its score range [mn, mx]: keys 1 + (((score
 // - mn) >> shift) << lsh), so the range spans bits 0..30 whatever its width
 // (a wider one drops its low bits, a narrower one is moved up so that the
@@ -1197,7 +1175,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const int64_t
   const int64_t P = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3LL;   // wave-uniform
   const int64_t j0 = threadIdx.x * P < n ? threadIdx.x * P : n;
   const int64_t j1 = j0 + P < n ? j0 + P : n;
-  (void)j0;
   unsigned long long base;
   int shift, lsh;
   unit_range(mm + 2 * static_cast<int64_t>(unit) * np, np, base, shift, lsh, sh.mm);

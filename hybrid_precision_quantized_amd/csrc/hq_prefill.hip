@@ -372,7 +372,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams P) {
   const int64_t qi = q0 + wave * 32 + (lane & 31);           // this lane's query position
   const bool q_ok = qi < P.T;
   const int64_t qrow = (static_cast<int64_t>(b) * P.Hq + qh) * P.T + (q_ok ? qi : P.T - 1);
-  const int64_t krow0 = bh * P.T;                            // first K row of the KV head
   const int64_t qlast = (q0 + kBM - 1 < P.T - 1) ? q0 + kBM - 1 : P.T - 1;
 
   // running max of the raw logits; starts finite (the rescale runs before any
