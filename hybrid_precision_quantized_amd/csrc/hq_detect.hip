@@ -114,6 +114,7 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
 
 constexpr int kStageRows = 128;
 constexpr bool kResWide8 = true;   // 512-column resident blocks as 8 waves of 4 tiles (else 4 of 8)
+constexpr bool kStagedNarrow8 = true;   // 256-column staged blocks as 8 waves of 2 tiles (else 4 of 4)
 constexpr int kRowPad = 8;        // halves
 
 // Grid: units * ceil(n / (16 NT WPB)) blocks of WPB waves on the 16x16x32
@@ -124,7 +125,9 @@ constexpr int kRowPad = 8;        // halves
 // run their MFMAs while others still load: 20.4 -> 19.3 us at 1 x 32K, 8 KV
 // heads, against 4 waves of 8 tiles, whose per-wave stamps showed each wave
 // loading for ~8 us, then 5.6 us of MFMAs, then 1.5 us of epilogue, in
-// lockstep across the chip). MFMA kc covers channels 32 kc + 8 g .. + 7 for lane group g = lane
+// lockstep across the chip; staged 256-column blocks likewise run as 8 waves
+// of 2 tiles, two waves per SIMD instead of one: 20.6-21.1 -> 19.3 us at
+// 1 x 32K, 2 KV heads, 1024 rows). MFMA kc covers channels 32 kc + 8 g .. + 7 for lane group g = lane
 // / 16, the same order in both operands, so one K load reads 64 contiguous
 // bytes of each of 16 rows (the 32x32 operand layout reads 32 bytes of each
 // of 32 rows, which stalled the texture path). The unit's query rows are
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(64 * WPB, WPB / 2) void mfma16_colsum_kernel(const 
   constexpr int CPB = 16 * NT * WPB;               // columns per block
   constexpr int GPB = CPB / 256;                   // 256-candidate score partials per block
   constexpr int WPG = WPB / GPB;                   // waves per partial
-  static_assert(NT == 4 || NT == 8, "tiles per wave");
+  static_assert(NT == 2 || NT == 4 || NT == 8, "tiles per wave");
   static_assert(WPB == 4 || WPB == 8, "waves per block");
   constexpr int ROWV = D / 8;
   constexpr int PER_T = kStageRows * ROWV / NTH;
@@ -1878,6 +1881,7 @@ extern "C" hq_status hq_detect_vlines(const void *q_new, void *q_acc, hq_dtype d
 #define HQ_C16R(DD, TT, NN) do { if (res) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, true, 4>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
                                  else hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, NN, false, 4>), grid, dim3(256), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); } while (0)
 #define HQ_C16(DD, TT) do { if (wide && res && kResWide8) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, 4, true, 8>), grid, dim3(512), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
+                            else if (!wide && !res && kStagedNarrow8) hipLaunchKernelGGL((mfma16_colsum_kernel<DD, TT, 2, false, 8>), grid, dim3(512), 0, st, qa, kk, Hq, Hkv, R, k_rows, cand_end, scores, tmm); \
                             else if (wide) HQ_C16R(DD, TT, 8); else HQ_C16R(DD, TT, 4); } while (0)
         if (D == 128) {
           if (dtype == HQ_BF16) HQ_C16(128, HQ_BF16); else HQ_C16(128, HQ_F16);
