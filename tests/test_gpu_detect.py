@@ -58,6 +58,10 @@ def _run(q_acc, K, cand_end, k_top, method, dtype, exact=True):
     (1, 8, 1, 128, 16, 33300, 33000, 33000, "f16", 1.0),  # k_top == cand_end
     (1, 8, 2, 128, 8, 34000, 33000, 0, "bf16", 1.0),      # k_top == 0
     (1, 4, 1, 128, 2, 36000, 35900, 20000, "bf16", 0.0625),  # crowded first digit: the radix path
+    # the eight-wave column-sum blocks at D = 64: 512 staged rows in 256-column
+    # blocks, and 256 resident rows in 512-column blocks (16 units x 32 blocks)
+    (1, 8, 1, 64, 64, 5000, 4900, 245, "bf16", 1.0),
+    (2, 32, 8, 64, 64, 16500, 16384, 819, "f16", 0.5),
 ])
 def test_detect_small_exact(method, B, Hq, Hkv, D, R, n, ce, k_top, dtype, spread):
     say(f"detect method={method} B={B} Hq={Hq} Hkv={Hkv} D={D} R={R} n={n} ce={ce} k={k_top} {dtype}")
