@@ -375,8 +375,8 @@ print("NO_DEVICE_OK")
 def test_no_device_reports_hip_error():
     """Without a GPU every valid call fails with HQ_ERR_HIP and a message
     instead of crashing. Run in a child process (no HIP state leaks into this
-    one) and only where no device is visible: on a GPU machine the same calls
-    would launch kernels on the fake addresses."""
+    one) and only where no device is visible: with a GPU present the same
+    calls would launch kernels on the fake addresses."""
     import sys
     import torch
     if torch.cuda.device_count() > 0:
