@@ -58,6 +58,7 @@ def _run(q_acc, K, cand_end, k_top, method, dtype, exact=True):
     (1, 8, 1, 128, 16, 33300, 33000, 33000, "f16", 1.0),  # k_top == cand_end
     (1, 8, 2, 128, 8, 34000, 33000, 0, "bf16", 1.0),      # k_top == 0
     (1, 4, 1, 128, 2, 36000, 35900, 20000, "bf16", 0.0625),  # crowded first digit: the radix path
+    (1, 4, 1, 128, 2, 140100, 140000, 7000, "bf16", 1.0),  # chunks over 4096 keys: two runs per write thread
     # the eight-wave column-sum blocks at D = 64: 512 staged rows in 256-column
     # blocks, and 256 resident rows in 512-column blocks (16 units x 32 blocks)
     (1, 8, 1, 64, 64, 5000, 4900, 245, "bf16", 1.0),
