@@ -94,6 +94,7 @@ struct DecodeParams {
   int units;                // B * Hkv * nhc
   int blocks_used;          // units * S
   int blocks_per_xcd;
+  int upx;                  // whole units per XCD when the grid splits evenly into them, else 0
   float cs;                 // sm_scale * log2(e)
   // per-step upkeep (hq_decode_step), run by extra blocks of the merge launch
   int merge_blocks;         // blocks of the merge itself
@@ -1235,9 +1236,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams P) {
   // the head chunks of one KV head are adjacent for each split, so they
   // run together on one XCD and read each KV tile from HBM once (the other
   // chunks' reads hit that XCD's L2)
-  const int hc = lin % P.nhc;
-  const int split = (lin / P.nhc) % P.S;
-  const int bh = lin / (P.nhc * P.S);
+  int hc, split, bh;
+  if (P.upx > 0) {
+    // each XCD holds whole units: it runs all their INT4 splits first, then
+    // the VL splits, then the window splits, so that the shorter 16-bit
+    // blocks are the last ones dispatched and fill the tail
+    const int x = lin / P.blocks_per_xcd;
+    const int li = lin - x * P.blocks_per_xcd;
+    const int nq4 = P.upx * P.nhc * P.S_q, nvl = P.upx * P.nhc * P.S_vl;
+    int r, s0, ns;
+    if (li < nq4) {
+      r = li, s0 = 0, ns = P.S_q;
+    } else if (li < nq4 + nvl) {
+      r = li - nq4, s0 = P.S_q, ns = P.S_vl;
+    } else {
+      r = li - nq4 - nvl, s0 = P.S_q + P.S_vl, ns = P.S_win;
+    }
+    hc = r % P.nhc;
+    split = s0 + (r / P.nhc) % ns;
+    bh = x * P.upx + r / (P.nhc * ns);
+  } else {
+    hc = lin % P.nhc;
+    split = (lin / P.nhc) % P.S;
+    bh = lin / (P.nhc * P.S);
+  }
   const int h = bh % P.Hkv;
   const int b = bh / P.Hkv;
   const int i0 = h * P.G + hc * HB;           // first query head of this block
@@ -1328,6 +1350,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeParams P) {
 // the splits t / 8, t / 8 + 32, ..., and the 32 split groups are summed in a
 // fixed order, so the result is deterministic.
 constexpr int kMergeSlice = 32;
+constexpr bool kTypeMajor = true;   // dispatch each XCD's INT4 splits before its 16-bit ones
 
 // Per-step upkeep of hq_decode_step. It runs in the merge launch, after every
 // split has read the cache, so writing INT4 row T - W (outside this step's
@@ -1740,6 +1763,11 @@ hq_status decode_common(const void *q, hq_dtype q_dtype, int Hq, const hq_hybrid
   P.blocks_used = pl.units * pl.S;
   const int blocks = static_cast<int>(ceil_div(P.blocks_used, kNumXcd) * kNumXcd);
   P.blocks_per_xcd = blocks / kNumXcd;
+  {
+    const int per_unit = pl.nhc * pl.S;                     // blocks of one (b, KV head)
+    P.upx = (kTypeMajor && blocks == P.blocks_used && P.blocks_per_xcd % per_unit == 0)
+                ? P.blocks_per_xcd / per_unit : 0;
+  }
   const float scale = sm_scale == 0.f ? 1.0f / sqrtf(static_cast<float>(kv->D)) : sm_scale;
   P.cs = scale * kLog2e;
   P.merge_blocks = pl.units * pl.HB * (kv->D / kMergeSlice);
