@@ -251,3 +251,53 @@ def test_vl_redetect_off_grid(dtype):
             wb[p >> 5] |= np.uint32(1) << np.uint32(p & 31)
         assert np.array_equal(bits, wb)
     say(f"  promoted by the oracle's rule: {changed} positions")
+
+
+def test_rolling_cache_full_llama32k_steps():
+    """The configuration the benchmark times, at its full size: the rolling
+    cache of a Llama-shaped layer (B 1, 32 query / 8 KV heads, D 128, context
+    32768 at step 0, window 128, VL budget 1638, ring of W + 64 rows) built
+    from the prefill-end detection, then three decode steps (hq_decode_step:
+    the step's queries into the ring, the window's oldest row packed into its
+    INT4 row, the automatic 64 splits), the cache advanced after each. Every
+    query head's output and log-sum-exp against the oracle's lifecycle, and
+    the three packed INT4 rows of every KV head bit for bit."""
+    base = synth.WORKLOADS["llama32k"]
+    n = 3
+    w = base.replace(name="llama32k+3", T=base.T + n)
+    B, Hq, Hkv, D, W, k, R = w.B, w.Hq, w.Hkv, w.D, w.W, w.k, 64
+    T0 = base.T
+    say("rolling cache, Llama shape at 32K: inputs and the oracle's three steps ...")
+    K, V = synth.all_keys(w), synth.all_values(w)
+    queries = np.stack([synth.all_queries(w.replace(seed=w.seed + 101 * (s + 1))) for s in range(n)])
+    vl0, _ = detect.detect(synth.all_query_histories(w), K[:, :, :T0], T0 - W, k)
+    outs, lses, sets, _ = lifecycle.simulate(K, V, queries, T0, W, R, k, vl0)
+    assert not sets                                                   # no update within three steps
+    dt = TORCH_DT[w.dtype]
+    Kd, Vd = to_dev(K, w.dtype), to_dev(V, w.dtype)
+    t_cap = ((T0 + n - W + 1) + 31) // 32 * 32
+    rc = hq.RollingCache(B, Hkv, D, T0, W, k, dt, Hq, R=R, t_cap=t_cap)
+    rc.build(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous(), torch.from_numpy(vl0).cuda())
+    assert hq.hq_decode_auto_splits(rc.descriptor(), Hq) == 64
+    ws = torch.full((hq.hq_decode_workspace_size(rc.descriptor(), Hq, 0),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    for s in range(n):
+        say(f"  step {s}")
+        rc.decode_step(to_dev(queries[s], w.dtype), out, lse, ws)
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        e = rel_err(o, outs[s])
+        assert e <= 2e-3 and np.max(np.abs(l - lses[s])) <= 1e-3, (s, e)
+        rc.advance(Kd[:, :, T0 + s], Vd[:, :, T0 + s])
+    torch.cuda.synchronize()
+    # the rows the three steps packed: positions T0 - W .. T0 - W + 2
+    r0, r1 = T0 - W, T0 - W + n
+    kp, ks = quant.quantize_rows(K[:, :, r0:r1])
+    vp, vs = quant.quantize_rows(V[:, :, r0:r1])
+    assert np.array_equal(rc.k_codes[:, :, r0:r1].cpu().numpy(), kp)
+    assert np.array_equal(rc.k_sz[:, :, r0:r1].cpu().numpy().view(np.uint16), ks)
+    assert np.array_equal(rc.v_sz[:, :, r0:r1].cpu().numpy().view(np.uint16), vs)
+    for b in range(B):
+        for h in range(Hkv):
+            assert np.array_equal(tile16_codes(rc.v_codes[b, h])[r0:r1], vp[b, h])
