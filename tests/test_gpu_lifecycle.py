@@ -253,21 +253,23 @@ def test_vl_redetect_off_grid(dtype):
     say(f"  promoted by the oracle's rule: {changed} positions")
 
 
-def test_rolling_cache_full_llama32k_steps():
+@pytest.mark.parametrize("name", ["llama32k", "glm32k"])
+def test_rolling_cache_full_size_steps(name):
     """The configuration the benchmark times, at its full size: the rolling
     cache of a Llama-shaped layer (B 1, 32 query / 8 KV heads, D 128, context
-    32768 at step 0, window 128, VL budget 1638, ring of W + 64 rows) built
-    from the prefill-end detection, then three decode steps (hq_decode_step:
-    the step's queries into the ring, the window's oldest row packed into its
-    INT4 row, the automatic 64 splits), the cache advanced after each. Every
-    query head's output and log-sum-exp against the oracle's lifecycle, and
-    the three packed INT4 rows of every KV head bit for bit."""
-    base = synth.WORKLOADS["llama32k"]
+    32768 at step 0, window 128, VL budget 1638, ring of W + 64 rows), or of
+    the GLM-4-9B head grouping (32 / 2), built from the prefill-end detection,
+    then three decode steps (hq_decode_step: the step's queries into the
+    ring, the window's oldest row packed into its INT4 row, the automatic 64
+    splits), the cache advanced after each. Every query head's output and
+    log-sum-exp against the oracle's lifecycle, and the three packed INT4
+    rows of every KV head bit for bit."""
+    base = synth.WORKLOADS[name]
     n = 3
-    w = base.replace(name="llama32k+3", T=base.T + n)
+    w = base.replace(name=f"{name}+3", T=base.T + n)
     B, Hq, Hkv, D, W, k, R = w.B, w.Hq, w.Hkv, w.D, w.W, w.k, 64
     T0 = base.T
-    say("rolling cache, Llama shape at 32K: inputs and the oracle's three steps ...")
+    say(f"rolling cache, {name}: inputs and the oracle's three steps ...")
     K, V = synth.all_keys(w), synth.all_values(w)
     queries = np.stack([synth.all_queries(w.replace(seed=w.seed + 101 * (s + 1))) for s in range(n)])
     vl0, _ = detect.detect(synth.all_query_histories(w), K[:, :, :T0], T0 - W, k)
