@@ -1811,7 +1811,7 @@ namespace hq {
 namespace {
 constexpr size_t kScratchBytes = size_t(16) << 20;       // HQ_DECODE_SCRATCH_BYTES
 static_assert(kScratchBytes == HQ_DECODE_SCRATCH_BYTES, "header and library agree on the scratch size");
-__device__ __align__(256) uint8_t scratch[kScratchBytes];
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
