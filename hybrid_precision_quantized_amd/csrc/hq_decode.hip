@@ -670,7 +670,9 @@ __device__ void int4_split_d128_g4(const DecodeParams &P, SharedMem &sm, int b, 
     L.vc = bload16nt(view(vb, nv, c * (CP * 16)), lo_v);
   };
 
-  constexpr int NPF = 3;
+  // a 2-deep ring: one chunk's loads in flight while the wave works on the
+  // other (deeper rings measured slower at every shape)
+  constexpr int NPF = 2;
   const uint32_t nsteps = (n + SLOTS - 1) / SLOTS;
   Int4Loads<D> ring[NPF];
 #pragma unroll
