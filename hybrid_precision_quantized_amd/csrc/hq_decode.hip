@@ -1125,7 +1125,9 @@ __device__ void fp_rows_d128_g4(const DecodeParams &P, SharedMem &sm, int b, int
     }
   };
 
-  constexpr int NPF = 2;
+  // no prefetch ring: each wave issues the next chunk's loads after its
+  // current chunk (the other waves on the SIMD cover the wait)
+  constexpr int NPF = 1;
   const uint32_t nsteps = (n + SLOTS - 1) / SLOTS;
   FpRing ring[NPF];
 #pragma unroll
